@@ -1,0 +1,64 @@
+"""Exact-rational brute force of the projection, for tiny inputs.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Decodes IEEE bit
+patterns into ``fractions.Fraction`` from the format definition (sign,
+biased exponent, fraction field; bias 127 for both bf16 and binary32, 7 and
+23 fraction bits) and sums the products with no rounding at all.  It is an
+independent check of ``oracle.c``'s fp64 loop: for K <= 8 bf16 inputs every
+partial sum is exact in double too, so the two must agree exactly.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+
+def decode(bits: int, frac_bits: int) -> Fraction:
+    """Value of an IEEE pattern with an 8-bit exponent (bias 127) and
+    ``frac_bits`` fraction bits (7 for bf16, 23 for binary32).  Infinities
+    and NaNs are rejected (they have no rational value)."""
+    total = 1 + 8 + frac_bits
+    bits = int(bits) & ((1 << total) - 1)
+    sign = -1 if (bits >> (total - 1)) & 1 else 1
+    exp = (bits >> frac_bits) & 0xFF
+    frac = bits & ((1 << frac_bits) - 1)
+    if exp == 0xFF:
+        raise ValueError("inf/nan has no rational value")
+    if exp == 0:  # subnormal: 0.frac * 2^(1-127)
+        mant = Fraction(frac, 1 << frac_bits)
+        e = 1 - 127
+    else:
+        mant = 1 + Fraction(frac, 1 << frac_bits)
+        e = exp - 127
+    scale = Fraction(2) ** e
+    return sign * mant * scale
+
+
+def decode_bf16(bits: int) -> Fraction:
+    return decode(bits, 7)
+
+
+def decode_f32(bits: int) -> Fraction:
+    return decode(bits, 23)
+
+
+def linear_exact(x_rows, w_rows, frac_bits: int):
+    """``x_rows``: list of M lists of K patterns; ``w_rows``: N lists of K
+    patterns.  Returns (y, S) as M x N lists of Fractions."""
+    xs = [[decode(b, frac_bits) for b in row] for row in x_rows]
+    ws = [[decode(b, frac_bits) for b in row] for row in w_rows]
+    y, s = [], []
+    for xr in xs:
+        yr, sr = [], []
+        for wr in ws:
+            if len(wr) != len(xr):
+                raise ValueError("row lengths differ")
+            acc = Fraction(0)
+            mag = Fraction(0)
+            for a, b in zip(xr, wr):
+                acc += a * b
+                mag += abs(a * b)
+            yr.append(acc)
+            sr.append(mag)
+        y.append(yr)
+        s.append(sr)
+    return y, s

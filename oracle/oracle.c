@@ -1,0 +1,118 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference of the fused
+ * decode-time hidden-state projection.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or constant with the
+ * HIP library (it decodes bf16 and rounds to bf16 with its own code).
+ *
+ * What it computes (the plain definition the fusion must reach):
+ *   for every projection i, token row m and output row r
+ *     y_i[m][r] = sum_k X[m][k] * W_i[r][k]          (no bias)
+ *     S_i[m][r] = sum_k |X[m][k] * W_i[r][k]|        (error-bound scale)
+ * The fusion of several projections that read the same activations into one
+ * GEMM over the row-concatenated weight returns exactly these per-projection
+ * linear layers, only with fewer launches:
+ *   - "tinygemm2 for the DeepSeek-V4.1 hidden-state projections"
+ *     (TensorRT-LLM PR #20636), Description: wq_a and wkv concatenated into
+ *     one [1792, 5120] weight, the halves returned as dense [1, N] tensors,
+ *     checked against an FP32 F.linear reference (Test Coverage).
+ *   - "Fuse indexer wk + weights_proj into single GEMM in TF32 for DS-V3.2"
+ *     (TensorRT-LLM PR #12055), Description: two FP32 projections, one GEMM.
+ *
+ * Arithmetic: each stored element is decoded to its exact value, each
+ * product is formed in IEEE double (exact: a bf16 x bf16 product has at most
+ * 16 significant bits and an fp32 x fp32 product at most 48, both below 53),
+ * and products are added in double in increasing k.  The only rounding is
+ * the double accumulation, at most K * 2^-53 * S in total.  An FP64
+ * reference is the pattern of the router GEMV commit of "Staircase: GLM-5.2
+ * NVFP4 low-latency decode target for Rubin (TP16)" (TensorRT-LLM PR #20502).
+ *
+ * Build: gcc -O2 -fPIC -shared (no -ffast-math: IEEE semantics are needed).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* Exact value of a bf16 bit pattern: bf16 is the upper half of an IEEE
+ * binary32, so widening is a 16-bit left shift of the pattern. */
+static double bf16_bits_value(uint16_t bits) {
+  uint32_t u = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double f32_bits_value(uint32_t bits) {
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* dtype codes of this file: 0 = bf16 (uint16 patterns), 1 = fp32 (uint32). */
+static double element(int dtype, const void* base, int64_t idx) {
+  if (dtype == 0) return bf16_bits_value(((const uint16_t*)base)[idx]);
+  return f32_bits_value(((const uint32_t*)base)[idx]);
+}
+
+/*
+ * One linear projection: y[m][r] and S[m][r] for m < M, r < N.
+ *   x : M rows, row stride ldx elements (ldx >= K), unit column stride
+ *   w : N rows of K elements, row stride K
+ *   y, s : M x N doubles, row-major
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_linear(int dtype, int64_t M, int64_t N, int64_t K, int64_t ldx,
+                  const void* x, const void* w, double* y, double* s) {
+  if ((dtype != 0 && dtype != 1) || M < 0 || N < 0 || K < 0 || ldx < K)
+    return -1;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t r = 0; r < N; ++r) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double p = element(dtype, x, m * ldx + k) * element(dtype, w, r * K + k);
+        acc += p;
+        mag += fabs(p);
+      }
+      y[m * N + r] = acc;
+      s[m * N + r] = mag;
+    }
+  }
+  return 0;
+}
+
+/*
+ * Round a double to the nearest bf16, ties to even, with IEEE gradual
+ * underflow (bf16 has float's exponent range: normal exponents -126..127,
+ * 7 stored fraction bits, subnormal quantum 2^-133) and overflow to inf.
+ * The reading of "rounded to BF16 once" in the fused-A commit of PR #20502
+ * is IEEE round-to-nearest-even.  Written from the format definition: find
+ * the quantum of the value's binade, divide (exact: a power of two), round to
+ * an integer with nearbyint (ties-to-even in the default rounding mode),
+ * multiply back.
+ */
+uint16_t oracle_round_bf16(double v) {
+  if (isnan(v)) return (uint16_t)0x7fc0;
+  uint16_t sign = signbit(v) ? (uint16_t)0x8000 : (uint16_t)0;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return (uint16_t)(sign | 0x7f80);
+  int e;
+  frexp(a, &e);             /* a = f * 2^e with f in [0.5, 1) */
+  int E = e - 1;            /* a in [2^E, 2^(E+1)) */
+  if (E < -126) E = -126;   /* subnormal range shares the smallest quantum */
+  double q = ldexp(1.0, E - 7);
+  double r = nearbyint(a / q) * q;
+  const double max_finite = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+  if (r > max_finite) return (uint16_t)(sign | 0x7f80);
+  float f = (float)r; /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7fff));
+}
+
+/* Vector form of oracle_round_bf16 for n doubles. */
+void oracle_round_bf16_array(const double* v, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(v[i]);
+}
