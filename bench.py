@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused decode-time hidden-state projection on one MI355X.
+
+Workload (the pages' headline op): DeepSeek-V4.1 wq_a (5120 -> 1280) fused
+with wkv (5120 -> 512), bf16 in/out with fp32 accumulation, one fused call
+per token count M = 1..8 ("tinygemm2 for the DeepSeek-V4.1 hidden-state
+projections", TensorRT-LLM PR #20636, Description: op-level timing under
+CUDA-graph replay with the weights rotated past the cache).
+
+Protocol.  A pool of independent concatenated-weight copies of at least
+1 GiB (four times the 256 MiB Infinity Cache) is built, one plan each;
+consecutive calls use consecutive copies, so every call streams its weights
+from HBM.  One hipGraph per M holds one fused call per copy; a step replays
+the eight graphs (M = 1..8).  W warm-up steps, then K timed steps between
+HIP events on the launch stream, bracketed by device synchronizations.
+
+Reported: ``value`` = algorithmic bytes (W_cat + x + y per call, summed over
+the step) / step time, in GB/s; ``roofline`` for the fused skinny kernel
+against the 8 TB/s HBM peak; per-M microseconds per call for the fused and
+the one-launch-per-projection path; ``cpu_baseline`` = the CPU oracle
+(single thread) on one pass of the same M sweep over one copy.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("µs/call and HBM GB/s (% of peak), fused skinny GEMM M=1..8, "
+          "weights past MALL")
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+K = 5120
+N = (1280, 512)
+MS = (1, 2, 3, 4, 5, 6, 7, 8)
+
+
+def algorithmic_bytes(M: int, K: int, N, esize: int = 2) -> int:
+    n_total = sum(N)
+    return esize * (n_total * K + M * K + M * n_total)
+
+
+def build_pool(P, torch, n_copies, max_M, seed=0):
+    """n_copies independent weight sets U(-1/sqrt(K), 1/sqrt(K)) -> bf16,
+    drawn on the GPU, each concatenated by its own plan."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    a = 1.0 / math.sqrt(K)
+    plans = []
+    for _ in range(n_copies):
+        ws = [((torch.rand(n, K, generator=g, device="cuda") * 2 - 1) * a)
+              .to(torch.bfloat16) for n in N]
+        plans.append(P.FusedProjection(ws, max_M=max(MS)))
+        del ws
+    return plans
+
+
+def capture(torch, fn):
+    fn()  # eager warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, graphs, steps, warmup):
+    """Replays the graphs in order per step; returns (total_ms, per-graph ms
+    summed over the timed steps)."""
+    for _ in range(warmup):
+        for g in graphs:
+            g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
+    per = [0.0] * len(graphs)
+    total = 0.0
+    for _ in range(steps):
+        evs[0].record(stream)
+        for i, g in enumerate(graphs):
+            g.replay()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(len(graphs)):
+            per[i] += evs[i].elapsed_time(evs[i + 1])
+        total += evs[0].elapsed_time(evs[-1])
+    return total, per
+
+
+def cpu_baseline(plan0_weights_cpu, xs_cpu, budget_s=12.0):
+    """The oracle (single-threaded C loop, fp64) on the M = 1..8 sweep over
+    one weight copy, repeated until ``budget_s`` of CPU time is spent."""
+    import oracle
+    import synthetic_inputs as si
+    oracle.build(force=False)
+    wb = [si.bits(w) for w in plan0_weights_cpu]
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        for M in MS:
+            xb = si.bits(xs_cpu[M])
+            for w in wb:
+                oracle.linear(xb, w)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or passes >= 50:
+            break
+    byts = passes * sum(algorithmic_bytes(M, K, N) for M in MS)
+    return {"value": byts / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d pass(es) of the M=1..8 sweep over one [1792, 5120] bf16 "
+                      "weight copy, %.1f s, single-threaded C fp64 loop" % (passes, el),
+            "us_per_call": el / (passes * len(MS)) * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--pool-mib", type=int, default=1024,
+                    help="total size of the rotated weight pool (>= 1024 for past-MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--details", default="", help="write per-M details JSON here")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X with no "
+              "sharding or collectives (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import projection_gemm_sparse_amd as P
+    import synthetic_inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w_bytes = sum(N) * K * 2
+    n_copies = max(2, math.ceil((args.pool_mib << 20) / w_bytes))
+    print("bench: pool of %d weight copies (%.0f MiB), M=%s" %
+          (n_copies, n_copies * w_bytes / 2**20, list(MS)), file=sys.stderr, flush=True)
+    plans = build_pool(P, torch, n_copies, max(MS))
+
+    xs_cpu, xs, outs = {}, {}, {}
+    for M in MS:
+        xc, _ = si.make_case(K, N, "bf16", M, seed=100 + M)
+        xs_cpu[M] = xc
+        xs[M] = xc.to(dev)
+        outs[M] = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
+
+    def fused_calls(M):
+        def run():
+            for p in plans:
+                p.forward(xs[M], out=outs[M])
+        return run
+
+    def separate_calls(M):
+        def run():
+            for p in plans:
+                p.forward_separate(xs[M], out=outs[M])
+        return run
+
+    fused_graphs = [capture(torch, fused_calls(M)) for M in MS]
+    print("bench: graphs captured", file=sys.stderr, flush=True)
+    total_ms, per_ms = time_graphs(torch, fused_graphs, args.steps, args.warmup)
+    sep_graphs = [capture(torch, separate_calls(M)) for M in MS]
+    _, sep_ms = time_graphs(torch, sep_graphs, max(3, args.steps // 4), 1)
+    sep_steps = max(3, args.steps // 4)
+
+    calls = args.steps * n_copies
+    per_m = {}
+    step_bytes = 0
+    for i, M in enumerate(MS):
+        us = per_ms[i] * 1e3 / calls
+        b = algorithmic_bytes(M, K, N)
+        step_bytes += b * n_copies
+        per_m[str(M)] = {
+            "fused_us": round(us, 4),
+            "separate_us": round(sep_ms[i] * 1e3 / (sep_steps * n_copies), 4),
+            "bytes": b,
+            "fused_GBps": round(b / us / 1e3, 1),
+            "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+            "path": P._lib.PATH_NAMES[plans[0].query(M)[0]],
+        }
+    ms_per_step = total_ms / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # sanity check of one call against a plain PyTorch fp32 product (outside
+    # the timed region)
+    M = 4
+    ref_w = plans[0].views
+    ys = plans[0].forward(xs[M])
+    torch.cuda.synchronize()
+    worst = 0.0
+    for y, w in zip(ys, ref_w):
+        ref = xs[M].float() @ w.float().t()
+        s = xs[M].float().abs() @ w.float().abs().t()
+        worst = max(worst, float(((y.float() - ref).abs() / (2 ** -7 * s + 1e-6)).max()))
+    if not worst <= 1.0:
+        print("bench: SANITY FAILURE, |err|/bound = %.3g" % worst, file=sys.stderr)
+        sys.exit(3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        w0 = [v.cpu() for v in plans[0].views]
+        cpu = cpu_baseline(w0, xs_cpu)
+
+    us_all = [per_m[str(M)]["fused_us"] for M in MS]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded U(-1/sqrt(K),1/sqrt(K)) weights, N(0,1) x, bf16)",
+        "config": {
+            "workload": "wq_a+wkv fused [1280,512]x5120 bf16, M=1..8, one fused call "
+                        "per M per weight copy, %d copies rotated (%.2f GiB > 256 MiB MALL), "
+                        "hipGraph replay" % (n_copies, n_copies * w_bytes / 2**30),
+            "K": K, "N": list(N), "M": list(MS), "pool_copies": n_copies,
+            "calls_per_step": n_copies * len(MS),
+        },
+        "us_per_call": {"mean_M1_8": round(sum(us_all) / len(us_all), 4),
+                        "M1": per_m["1"]["fused_us"], "M8": per_m["8"]["fused_us"]},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(value, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+        "per_m": per_m,
+        "context": {"pages_sm107_fused_m1_us": 4.13,
+                    "note": "Vera Rubin figure from the pages, other hardware"},
+    }
+    print(json.dumps(line), flush=True)
+    if args.details:
+        with open(args.details, "w") as fh:
+            json.dump(line, fh, indent=1)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * fusedproj.h -- C ABI of libfusedproj, the fused decode-time hidden-state
+ * projection for MI355X (gfx950).
+ *
+ * The operation.  Several linear projections that read the same activations
+ * x[M, K] (for example DeepSeek-V4.1's wq_a 5120->1280 and wkv 5120->512)
+ * have their weights W_i[N_i, K] copied once into one row-concatenated
+ * buffer W_cat[sum_i N_i, K]; one skinny GEMM y = x . W_cat^T then computes
+ * all of them and each projection's result is returned as its own dense
+ * [M, N_i] tensor:
+ *     y_i[m, r] = sum_k x[m, k] * W_i[r, k]            (no bias)
+ * Sources (TensorRT-LLM pull-request pages):
+ *   "tinygemm2 for the DeepSeek-V4.1 hidden-state projections" (PR #20636),
+ *     Description: the [1792, 5120] concatenation done after weight load,
+ *     the two weights rebound as views into it, reloads writing through the
+ *     views, the fused call returning dense [M, N] halves, and the fallback
+ *     list for inputs the fast path does not serve; Test Coverage: graph
+ *     replay bitwise equal to eager.
+ *   "Fuse indexer wk + weights_proj into single GEMM in TF32 for DS-V3.2"
+ *     (PR #12055), Description: the FP32 variant (computed here with exact
+ *     fp32 FMA, not TF32).
+ *   "Staircase: GLM-5.2 NVFP4 low-latency decode target for Rubin (TP16)"
+ *     (PR #20502), fused-A and dense-MLP commits: fixed-order fp32 sums,
+ *     rounded to bf16 once; a host "supported" query and refusal of shapes
+ *     the kernels do not serve.
+ *
+ * Conventions for every function below.
+ *   - All pointers named w_*, x, y, w_cat and workspace are DEVICE pointers
+ *     (memory the caller allocated on the plan's GPU); N and other arrays
+ *     are HOST pointers.  `stream` is a hipStream_t passed as void*
+ *     (NULL = the device's null stream).
+ *   - Matrices are row-major with unit column stride.  Sizes, offsets and
+ *     strides are int64_t element counts.
+ *   - Every function returns an fp_status.  All argument and shape checks
+ *     happen before any HIP call, so a call that fails validation has no
+ *     side effect.  No exception crosses the ABI.
+ *   - The library never allocates device memory and never synchronizes:
+ *     fp_plan_create and the forward calls only enqueue work on `stream`.
+ *   - Ownership: the caller owns w_cat, workspace, x and every y; a plan
+ *     borrows w_cat and workspace and must be destroyed before they are
+ *     freed.  A plan holds only host state besides those borrowed buffers.
+ *   - Concurrency: the forward calls of one plan use the plan's workspace;
+ *     two calls of the same plan must not run concurrently (on two streams);
+ *     create one plan per stream for that.
+ */
+#ifndef FUSEDPROJ_H
+#define FUSEDPROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fp_plan_s* fp_plan_t;
+
+/* Storage and arithmetic type.  FP_BF16: bf16 inputs and outputs, fp32
+ * accumulation, each output rounded once to bf16 (round to nearest even).
+ * FP_F32: fp32 inputs and outputs with fp32 fused multiply-add. */
+typedef enum { FP_BF16 = 0, FP_F32 = 1 } fp_dtype;
+
+typedef enum {
+  FP_OK = 0,
+  FP_ERR_INVALID_ARG = 1,  /* null/negative/inconsistent argument, stale plan */
+  FP_ERR_UNSUPPORTED = 2,  /* valid request the kernels do not serve (e.g.
+                              misaligned x, M above the plan's max_M): the
+                              caller falls back to its plain linear layers */
+  FP_ERR_HIP = 3,          /* a HIP call failed; see fp_last_hip_error() */
+  FP_ERR_WORKSPACE = 4     /* workspace smaller than fp_workspace_bytes() */
+} fp_status;
+
+/* Kernel paths reported by fp_plan_query. */
+typedef enum {
+  FP_PATH_NONE = 0,        /* M == 0: nothing is launched */
+  FP_PATH_SKINNY = 1,      /* weight-streaming vector-ALU kernel, one launch */
+  FP_PATH_SKINNY_SPLITK = 2, /* same kernel with the K contraction split
+                              across workgroups and a fixed-order finish
+                              inside the same launch */
+  FP_PATH_MFMA = 3         /* MFMA tile kernel (bf16, M above the crossover) */
+} fp_path;
+
+#define FP_MAX_PROJ 16     /* projections per plan */
+#define FP_MAX_M 256       /* largest token count a plan can serve */
+
+/* Bytes of device workspace a plan needs (split-K partial sums and the
+ * self-resetting arrival counters), for dtype `dtype`, contraction length K,
+ * the n_proj row counts N[] and token counts up to max_M.  Returns 0 on an
+ * invalid argument (and for shapes that need no workspace it still returns a
+ * small positive size for the counters). */
+size_t fp_workspace_bytes(int32_t dtype, int64_t K, int32_t n_proj,
+                          const int64_t* N, int64_t max_M);
+
+/* Load-time half ("post_load_weights" of PR #20636, Description).
+ * Records the projection layout and, on `stream`, copies each w_src[i]
+ * (device, [N[i], K] contiguous row-major) into rows off_i .. off_i+N[i]-1 of
+ * w_cat (device, [sum N, K] row-major, 256-byte aligned), where off_0 = 0 and
+ * off_{i+1} = off_i + N[i].  A NULL w_src (or a NULL entry, or an entry equal
+ * to its destination) skips that copy: the caller fills the rows itself,
+ * typically through the views fp_plan_view returns.  The workspace
+ * (device, ws_bytes >= fp_workspace_bytes(...), 256-byte aligned) has its
+ * counters cleared on `stream` by a fill kernel.
+ * Requirements: 1 <= n_proj <= FP_MAX_PROJ, every N[i] >= 1, K >= 1 with
+ * K * sizeof(element) a multiple of 16, 1 <= max_M <= FP_MAX_M.
+ * On success *out receives the plan. */
+fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj,
+                         const int64_t* N, const void* const* w_src,
+                         void* w_cat, void* workspace, size_t ws_bytes,
+                         int64_t max_M, void* stream, fp_plan_t* out);
+
+/* View of projection i inside w_cat: *w_i = w_cat + off_i * K elements,
+ * *row_offset = off_i, *rows = N[i].  Any output pointer may be NULL.
+ * Writing new weights through a view (an in-place checkpoint reload, as in
+ * PR #20636) keeps the fused path valid: no kernel reads a derived copy. */
+fp_status fp_plan_view(fp_plan_t plan, int32_t i, void** w_i,
+                       int64_t* row_offset, int64_t* rows);
+
+/* Frees the plan's host state.  The borrowed buffers are untouched. */
+fp_status fp_plan_destroy(fp_plan_t plan);
+
+/* Host-only predicate (no HIP call): FP_OK if fp_forward serves token count
+ * M with x (device pointer, row stride ldx elements), FP_ERR_UNSUPPORTED if
+ * the kernels do not (M > max_M, x or its row stride not 16-byte aligned,
+ * fp32 with M > 8), FP_ERR_INVALID_ARG for invalid arguments (ldx < K,
+ * M < 0, NULL x with M > 0, stale plan).  The pattern of the dense-MLP
+ * commit of PR #20502: a host query, refusal otherwise. */
+fp_status fp_supported(fp_plan_t plan, int64_t M, const void* x, int64_t ldx);
+
+/* The fused call: one launch computes every projection.
+ * x: device, M rows with row stride ldx >= K elements (x[m, k] at
+ *    x + m*ldx + k), 16-byte aligned rows.
+ * y: host array of n_proj device pointers; y[i] receives the dense
+ *    [M, N_i] result (y_i[m, r] at y[i] + m*N_i + r).  Outputs must not
+ *    overlap each other, x, w_cat or the workspace.
+ * M == 0 returns FP_OK and launches nothing.  Results are deterministic: a
+ * repeat, a graph replay and fp_forward_separate give bitwise equal y. */
+fp_status fp_forward(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
+                     void* stream, void* const* y);
+
+/* The comparison path: one launch per projection, each over its own rows.
+ * w_override: NULL, or a host array of n_proj entries where a non-NULL
+ * entry is a device [N_i, K] weight used instead of the view (a replaced
+ * Parameter that no longer aliases w_cat, PR #20636 Test Coverage).  With
+ * no override the outputs are bitwise equal to fp_forward's. */
+fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx,
+                              fp_plan_t plan, void* stream, void* const* y,
+                              const void* const* w_override);
+
+/* Which kernel fp_forward runs for M, and how many kernel launches
+ * fp_forward and fp_forward_separate make (0 for M == 0).  Any output
+ * pointer may be NULL.  Host-only. */
+fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path,
+                        int32_t* launches_fused, int32_t* launches_separate);
+
+/* Smallest M served by the MFMA tile path (bf16 plans; default: the
+ * measured crossover).  Values below 2 or above FP_MAX_M+1 are rejected.
+ * Changing it changes which kernel (hence which summation order) serves an
+ * M, so results for that M may differ bitwise from before the change. */
+fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
+
+/* Tiling of one token count (benchmarking and testing aid).  Every tiling
+ * the kernels accept gives results within the same error bound; the
+ * summation order, hence the exact bits, depends on path, kparts, chunks and
+ * splits (never on rows/groups), so fused and separate calls of one plan
+ * stay bitwise equal under any tiling.
+ *   path    FP_PATH_SKINNY / FP_PATH_SKINNY_SPLITK (same kernel; the
+ *           splits field decides) or FP_PATH_MFMA (bf16 only)
+ *   kparts  skinny: waves splitting one K slice (P); mfma: PK
+ *   chunks  skinny: 16-byte chunks per lane and row (CJ, 1..2);
+ *           mfma: 128-wide k tiles per wave (KTW: 1, 2 or 4)
+ *   splits  K slices across workgroups (S >= 1), finished in-launch
+ *   rows    skinny: rows per wave (RW, 1..8); mfma: 16-row groups per
+ *           workgroup (GR); 0 = chosen per launch from its row count
+ *   groups  skinny: row groups per workgroup (G); 0 = chosen per launch;
+ *           mfma: ignored */
+typedef struct {
+  int32_t path;
+  int32_t kparts;
+  int32_t chunks;
+  int32_t splits;
+  int32_t rows;
+  int32_t groups;
+} fp_tiling;
+
+/* Override the tiling used for token count M (1 <= M <= the plan's max_M),
+ * or restore the default with t == NULL.  Host-only.  Returns
+ * FP_ERR_UNSUPPORTED for a tiling the kernels cannot run (block larger than
+ * 1024 threads, LDS above 160 KiB, K not covered, no such kernel) and
+ * FP_ERR_WORKSPACE if its split-K partials do not fit the plan's
+ * workspace. */
+fp_status fp_plan_set_tiling(fp_plan_t plan, int64_t M, const fp_tiling* t);
+
+/* The tiling fp_forward would use for M on a launch of n_rows rows (pass
+ * the plan's total rows for the fused call), with rows/groups resolved. */
+fp_status fp_plan_get_tiling(fp_plan_t plan, int64_t M, int64_t n_rows,
+                             fp_tiling* out);
+
+/* Host-only, no plan needed: the tiling a plan of (dtype, K, n_total rows)
+ * uses by default (default crossover, no override) for token count M on a
+ * launch of n_rows rows (1 <= n_rows <= n_total).  FP_ERR_UNSUPPORTED if no
+ * kernel serves M. */
+fp_status fp_default_tiling(int32_t dtype, int64_t K, int64_t n_total, int64_t M,
+                            int64_t n_rows, fp_tiling* out);
+
+/* Static text for a status code. */
+const char* fp_status_str(int32_t status);
+
+/* The hipError_t of the last failing HIP call made by this thread. */
+int32_t fp_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSEDPROJ_H */

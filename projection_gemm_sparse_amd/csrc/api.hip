@@ -1,0 +1,724 @@
+// api.hip -- host side of libfusedproj: plan bookkeeping, argument checks
+// (all before any HIP call), tiling choice and kernel launches.
+//
+// The load-time half follows "tinygemm2 for the DeepSeek-V4.1 hidden-state
+// projections" (TensorRT-LLM PR #20636), Description: the projection weights
+// are copied once into one row-concatenated buffer and each projection gets
+// a view into it; the decode-time half is one launch over all rows with the
+// per-projection outputs written densely.  The host "supported" predicate
+// and the refusal of unserved shapes follow the dense-MLP commit of
+// "Staircase: GLM-5.2 NVFP4 low-latency decode target for Rubin (TP16)"
+// (PR #20502).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
+#include "../../include/fusedproj.h"
+#include "mfma.hpp"
+#include "skinny.hpp"
+
+namespace {
+
+constexpr uint64_t kPlanMagic = 0x66757365'6470726full;  // "fusedpro"
+constexpr size_t kMaxLds = 160 * 1024;
+constexpr int kSkinnyMaxM = 8;      // largest M the skinny kernel serves
+constexpr int kDefaultMfmaMinM = 9; // crossover (smallest M on the MFMA path)
+constexpr int kCus = 256;           // MI355X compute units
+
+thread_local int32_t g_last_hip = 0;
+
+struct Tiling {
+  int path = 0;   // FP_PATH_*
+  int kparts = 0; // P or PK
+  int chunks = 0; // CJ or KTW
+  int splits = 0; // S
+  int rows = 0;   // RW or GR
+  int groups = 0; // G (skinny)
+  int mt = 0;     // skinny MT bucket or mfma MT16
+};
+
+}  // namespace
+
+struct fp_plan_s {
+  uint64_t magic;
+  int32_t dtype;
+  int32_t esize;
+  int64_t K;
+  int64_t kc;  // 16-byte chunks per row
+  int32_t n_proj;
+  int64_t N[FP_MAX_PROJ];
+  int64_t off[FP_MAX_PROJ];
+  int64_t n_total;
+  unsigned char* w_cat;
+  unsigned char* ws;
+  size_t ws_bytes;
+  int64_t max_M;
+  int64_t mfma_min_m;
+  bool has_override[FP_MAX_M + 1];
+  fp_tiling override_t[FP_MAX_M + 1];
+};
+
+namespace {
+
+std::mutex g_mu;
+std::unordered_set<const fp_plan_s*>& live_plans() {
+  static std::unordered_set<const fp_plan_s*> s;
+  return s;
+}
+
+bool plan_ok(const fp_plan_s* p) {
+  if (p == nullptr) return false;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (live_plans().count(p) == 0) return false;
+  return p->magic == kPlanMagic;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int skinny_mt(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+int mfma_mt16(int64_t M) {
+  const int64_t t = ceil_div(M, 16);
+  return t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 16;
+}
+
+int64_t counters_bytes(int64_t n_total) {
+  return ceil_div(n_total * 4, 256) * 256;
+}
+
+// ------------------------------------------------------------------ tilings
+// Plan-level part (summation order): depends on dtype, K, the M bucket and
+// the plan's total rows only.
+void default_skinny_order(int32_t dtype, int64_t kc, int64_t n_total, int mt,
+                          Tiling* t) {
+  (void)mt;
+  // Split K across workgroups only when the rows alone cannot give each CU
+  // work: fewer than two rows per CU.
+  int64_t S = 1;
+  if (n_total < 2 * kCus) S = std::min<int64_t>(ceil_div(2 * kCus, n_total), 8);
+  // the kernel covers at most 16 waves * 64 lanes * 2 chunks per slice
+  S = std::max<int64_t>(S, ceil_div(kc, 16 * 64 * 2));
+  const int64_t per = ceil_div(kc, S);
+  const int64_t CJ = ceil_div(per, 16 * 64);
+  const int64_t P = ceil_div(per, 64 * CJ);
+  t->path = S > 1 ? FP_PATH_SKINNY_SPLITK : FP_PATH_SKINNY;
+  t->kparts = (int)P;
+  t->chunks = (int)CJ;
+  t->splits = (int)S;
+  (void)dtype;
+}
+
+void default_mfma_order(int64_t kc, int mt16, Tiling* t) {
+  const int64_t kt = ceil_div(kc, 16);
+  const int PK = mt16 == 1 ? 4 : 1;
+  const int KTW = 2;
+  t->path = FP_PATH_MFMA;
+  t->kparts = PK;
+  t->chunks = KTW;
+  t->splits = (int)ceil_div(kt, (int64_t)PK * KTW);
+}
+
+// Launch-level part (work per workgroup): may depend on the launch's rows.
+void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t) {
+  const int rw_max = std::min(8, 64 / mt);
+  // rows per workgroup so that the launch has about one workgroup per CU
+  const int64_t target =
+      std::max<int64_t>(1, (n_rows * t->splits + kCus / 2) / kCus);
+  if (t->rows <= 0) t->rows = (int)std::min<int64_t>(rw_max, target);
+  if (t->groups <= 0) {
+    const int max_threads = fp::skinny_max_threads(t->mt, t->rows, t->chunks);
+    int64_t G = std::max<int64_t>(1, ceil_div(target, t->rows));
+    G = std::min<int64_t>(G, std::max(1, max_threads / (64 * t->kparts)));
+    t->groups = (int)G;
+  }
+}
+
+void resolve_mfma_rows(int mt16, Tiling* t) {
+  if (t->rows <= 0) t->rows = mt16 >= 4 ? 8 : (mt16 == 2 ? 4 : 1);
+  t->groups = 1;
+}
+
+size_t skinny_lds(const Tiling& t) {
+  const int V = t.rows * t.mt;
+  int VP = 1;
+  while (VP < V) VP <<= 1;
+  return (size_t)t.groups * t.kparts * VP * 4 + 16;
+}
+
+size_t mfma_lds(const Tiling& t) {
+  const size_t pitch = (size_t)t.kparts * t.chunks * 16 + 1;
+  const size_t xs = (size_t)16 * t.mt * pitch * 16;
+  const size_t red = t.kparts > 1 ? (size_t)t.rows * t.kparts * t.mt * 256 * 4 : 0;
+  return xs + red + 16;
+}
+
+// Partial-sum floats a tiling needs for a launch of n_rows rows and M tokens.
+int64_t partial_floats(const Tiling& t, int64_t n_rows, int64_t M) {
+  return t.splits > 1 ? (int64_t)t.splits * n_rows * M : 0;
+}
+
+bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t) {
+  if (t.splits < 1 || t.kparts < 1 || t.chunks < 1 || t.rows < 1) return false;
+  if (t.path == FP_PATH_MFMA) {
+    if (p->dtype != FP_BF16) return false;
+    if (!(t.chunks == 1 || t.chunks == 2 || t.chunks == 4)) return false;
+    if ((int64_t)t.rows * t.kparts * 64 > fp::mfma_max_threads(t.mt, t.chunks)) return false;
+    if ((int64_t)t.splits * t.kparts * t.chunks * 16 < p->kc) return false;
+    if (mfma_lds(t) > kMaxLds) return false;
+    if (16 * (int64_t)t.mt < M) return false;
+  } else if (t.path == FP_PATH_SKINNY || t.path == FP_PATH_SKINNY_SPLITK) {
+    if (M > kSkinnyMaxM) return false;
+    if (t.chunks > 2 || t.rows > 8 || t.rows * t.mt > 64) return false;
+    if (t.groups < 1) return false;
+    if ((int64_t)t.groups * t.kparts * 64 > fp::skinny_max_threads(t.mt, t.rows, t.chunks))
+      return false;
+    if ((int64_t)t.splits * t.kparts * 64 * t.chunks < p->kc) return false;
+    if (skinny_lds(t) > kMaxLds) return false;
+  } else {
+    return false;
+  }
+  const int64_t need = counters_bytes(p->n_total) + partial_floats(t, n_rows, M) * 4;
+  return (size_t)need <= p->ws_bytes;
+}
+
+// The tiling for (M, launch rows); the summation-order fields come from the
+// plan's default or the user's override for M and never from n_rows.
+bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t) {
+  *t = Tiling();
+  if (M >= 1 && M <= FP_MAX_M && p->has_override[M]) {
+    const fp_tiling& o = p->override_t[M];
+    t->path = o.path;
+    t->kparts = o.kparts;
+    t->chunks = o.chunks;
+    t->splits = o.splits;
+    t->rows = o.rows;
+    t->groups = o.groups;
+    if (t->path == FP_PATH_SKINNY || t->path == FP_PATH_SKINNY_SPLITK) {
+      t->path = t->splits > 1 ? FP_PATH_SKINNY_SPLITK : FP_PATH_SKINNY;
+    }
+  } else {
+    const bool mfma = p->dtype == FP_BF16 && (M >= p->mfma_min_m || M > kSkinnyMaxM);
+    if (mfma) {
+      default_mfma_order(p->kc, mfma_mt16(M), t);
+    } else {
+      if (M > kSkinnyMaxM) return false;
+      default_skinny_order(p->dtype, p->kc, p->n_total, skinny_mt(M), t);
+    }
+  }
+  if (t->path == FP_PATH_MFMA) {
+    t->mt = mfma_mt16(M);
+    resolve_mfma_rows(t->mt, t);
+  } else {
+    t->mt = skinny_mt(M);
+    if (t->kparts < 1) return false;
+    resolve_skinny_rows(n_rows, t->mt, t);
+  }
+  return tiling_valid(p, M, n_rows, *t);
+}
+
+// A host-only stand-in plan with default settings and unlimited workspace,
+// for questions about default tilings.
+void scratch_plan(fp_plan_s* tmp, int32_t dtype, int64_t K, int64_t n_total,
+                  int64_t max_M) {
+  std::memset(tmp, 0, sizeof *tmp);
+  tmp->magic = kPlanMagic;
+  tmp->dtype = dtype;
+  tmp->esize = dtype == FP_BF16 ? 2 : 4;
+  tmp->K = K;
+  tmp->kc = K * tmp->esize / 16;
+  tmp->n_proj = 1;
+  tmp->N[0] = n_total;
+  tmp->n_total = n_total;
+  tmp->max_M = max_M;
+  tmp->mfma_min_m = kDefaultMfmaMinM;
+  tmp->ws_bytes = SIZE_MAX;
+}
+
+size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) {
+  // counters for every possible row block, plus the largest partial buffer
+  // over the default tilings of every M up to max_M (fused launch: all rows)
+  fp_plan_s tmp;
+  scratch_plan(&tmp, dtype, K, n_total, max_M);
+  int64_t most = 0;
+  for (int64_t M = 1; M <= max_M; ++M) {
+    Tiling t;
+    if (!choose_tiling(&tmp, M, n_total, &t)) continue;
+    most = std::max(most, partial_floats(t, n_total, M));
+  }
+  // the MFMA path at every M (a later fp_plan_set_mfma_min_m can move the
+  // crossover down) for bf16
+  if (dtype == FP_BF16) {
+    for (int64_t M = 1; M <= max_M; ++M) {
+      Tiling t;
+      default_mfma_order(tmp.kc, mfma_mt16(M), &t);
+      most = std::max(most, partial_floats(t, n_total, M));
+    }
+  }
+  return (size_t)(counters_bytes(n_total) + most * 4);
+}
+
+// ------------------------------------------------------------------ kernels
+template <int MT, int CJ, bool BF16>
+const void* skinny_fn_rw(int rw) {
+  switch (rw) {
+    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, BF16>);
+    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, BF16>);
+    case 3: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 3, CJ, BF16>);
+    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, BF16>);
+    case 5: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 5, CJ, BF16>);
+    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, BF16>);
+    case 7: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 7, CJ, BF16>);
+    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, BF16>);
+    default: return nullptr;
+  }
+}
+
+template <int MT, bool BF16>
+const void* skinny_fn_cj(int cj, int rw) {
+  if (cj == 1) return skinny_fn_rw<MT, 1, BF16>(rw);
+  if (cj == 2) return skinny_fn_rw<MT, 2, BF16>(rw);
+  return nullptr;
+}
+
+template <bool BF16>
+const void* skinny_fn_mt(int mt, int cj, int rw) {
+  switch (mt) {
+    case 1: return skinny_fn_cj<1, BF16>(cj, rw);
+    case 2: return skinny_fn_cj<2, BF16>(cj, rw);
+    case 4: return skinny_fn_cj<4, BF16>(cj, rw);
+    case 8: return skinny_fn_cj<8, BF16>(cj, rw);
+    default: return nullptr;
+  }
+}
+
+template <int MT16>
+const void* mfma_fn_ktw(int ktw) {
+  switch (ktw) {
+    case 1: return reinterpret_cast<const void*>(&fp::mfma_kernel<MT16, 1>);
+    case 2: return reinterpret_cast<const void*>(&fp::mfma_kernel<MT16, 2>);
+    case 4: return reinterpret_cast<const void*>(&fp::mfma_kernel<MT16, 4>);
+    default: return nullptr;
+  }
+}
+
+const void* mfma_fn(int mt16, int ktw) {
+  switch (mt16) {
+    case 1: return mfma_fn_ktw<1>(ktw);
+    case 2: return mfma_fn_ktw<2>(ktw);
+    case 4: return mfma_fn_ktw<4>(ktw);
+    case 8: return mfma_fn_ktw<8>(ktw);
+    case 16: return mfma_fn_ktw<16>(ktw);
+    default: return nullptr;
+  }
+}
+
+std::mutex g_attr_mu;
+std::unordered_set<const void*>& big_lds_kernels() {
+  static std::unordered_set<const void*> s;
+  return s;
+}
+
+fp_status hip_fail(hipError_t e) {
+  g_last_hip = (int32_t)e;
+  return FP_ERR_HIP;
+}
+
+fp_status launch(const void* fn, int64_t blocks, int threads, size_t lds,
+                 void* arg, hipStream_t stream) {
+  if (fn == nullptr || blocks <= 0) return FP_ERR_UNSUPPORTED;
+  if (lds > 64 * 1024) {
+    std::lock_guard<std::mutex> lk(g_attr_mu);
+    if (big_lds_kernels().count(fn) == 0) {
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds);
+      if (e != hipSuccess) return hip_fail(e);
+      big_lds_kernels().insert(fn);
+    }
+  }
+  // The launch's own return code is checked; hipGetLastError is not used
+  // because it would also report (and clear) errors left by other code.
+  void* args[] = {arg};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3((unsigned)threads),
+                                 args, lds, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return FP_OK;
+}
+
+// One launch over the rows of `rs` with tiling t.
+fp_status run(const fp_plan_s* p, const Tiling& t, const fp::RowSpace& rs,
+              const void* x, int64_t M, int64_t ldx, hipStream_t stream) {
+  float* partial = reinterpret_cast<float*>(p->ws + counters_bytes(p->n_total));
+  uint32_t* counters = reinterpret_cast<uint32_t*>(p->ws);
+  if (t.path == FP_PATH_MFMA) {
+    fp::MfmaArgs a;
+    a.x = static_cast<const unsigned char*>(x);
+    a.ldx_bytes = ldx * p->esize;
+    a.row_bytes = p->K * p->esize;
+    a.M = (int32_t)M;
+    a.kc = (int32_t)p->kc;
+    a.GR = t.rows;
+    a.PK = t.kparts;
+    a.S = t.splits;
+    a.ktw = t.chunks;
+    a.rs = rs;
+    a.partial = partial;
+    a.counters = counters;
+    const int64_t blocks = ceil_div(rs.n_rows, 16 * (int64_t)t.rows) * t.splits;
+    return launch(mfma_fn(t.mt, t.chunks), blocks, t.rows * t.kparts * 64, mfma_lds(t),
+                  &a, stream);
+  }
+  fp::SkinnyArgs a;
+  a.x = static_cast<const unsigned char*>(x);
+  a.ldx_bytes = ldx * p->esize;
+  a.row_bytes = p->K * p->esize;
+  a.M = (int32_t)M;
+  a.kc = (int32_t)p->kc;
+  a.P = t.kparts;
+  a.G = t.groups;
+  a.S = t.splits;
+  a.cps = t.kparts * 64 * t.chunks;
+  a.R = t.groups * t.rows;
+  a.rs = rs;
+  a.partial = partial;
+  a.counters = counters;
+  const int64_t blocks = ceil_div(rs.n_rows, (int64_t)a.R) * t.splits;
+  const void* fn = p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
+                                       : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
+  return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), &a, stream);
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+  return a0 < b1 && b0 < a1;
+}
+
+// Checks shared by fp_supported and the forward calls (host only).
+fp_status check_x(const fp_plan_s* p, int64_t M, const void* x, int64_t ldx) {
+  if (M < 0) return FP_ERR_INVALID_ARG;
+  if (M == 0) return FP_OK;
+  if (x == nullptr || ldx < p->K) return FP_ERR_INVALID_ARG;
+  if (M > p->max_M) return FP_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || (ldx * p->esize) % 16 != 0) return FP_ERR_UNSUPPORTED;
+  if (p->dtype == FP_F32 && M > kSkinnyMaxM) return FP_ERR_UNSUPPORTED;
+  return FP_OK;
+}
+
+fp_status check_outputs(const fp_plan_s* p, int64_t M, const void* x, int64_t ldx,
+                        void* const* y) {
+  if (y == nullptr) return FP_ERR_INVALID_ARG;
+  const uintptr_t xb = reinterpret_cast<uintptr_t>(x);
+  const uintptr_t xe = xb + (uintptr_t)(((M - 1) * ldx + p->K) * p->esize);
+  const uintptr_t wb = reinterpret_cast<uintptr_t>(p->w_cat);
+  const uintptr_t we = wb + (uintptr_t)(p->n_total * p->K * p->esize);
+  const uintptr_t sb = reinterpret_cast<uintptr_t>(p->ws);
+  const uintptr_t se = sb + p->ws_bytes;
+  for (int i = 0; i < p->n_proj; ++i) {
+    if (y[i] == nullptr || !aligned(y[i], (uintptr_t)p->esize)) return FP_ERR_INVALID_ARG;
+    const uintptr_t b = reinterpret_cast<uintptr_t>(y[i]);
+    const uintptr_t e = b + (uintptr_t)(M * p->N[i] * p->esize);
+    if (overlaps(b, e, xb, xe) || overlaps(b, e, wb, we) || overlaps(b, e, sb, se))
+      return FP_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j) {
+      const uintptr_t b2 = reinterpret_cast<uintptr_t>(y[j]);
+      const uintptr_t e2 = b2 + (uintptr_t)(M * p->N[j] * p->esize);
+      if (overlaps(b, e, b2, e2)) return FP_ERR_INVALID_ARG;
+    }
+  }
+  return FP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp_workspace_bytes(int32_t dtype, int64_t K, int32_t n_proj, const int64_t* N,
+                          int64_t max_M) {
+  if ((dtype != FP_BF16 && dtype != FP_F32) || K < 1 || n_proj < 1 ||
+      n_proj > FP_MAX_PROJ || N == nullptr || max_M < 1 || max_M > FP_MAX_M)
+    return 0;
+  const int esize = dtype == FP_BF16 ? 2 : 4;
+  if ((K * esize) % 16 != 0) return 0;
+  int64_t n_total = 0;
+  for (int i = 0; i < n_proj; ++i) {
+    if (N[i] < 1) return 0;
+    n_total += N[i];
+  }
+  return workspace_need(dtype, K, n_total, max_M);
+}
+
+fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t* N,
+                         const void* const* w_src, void* w_cat, void* workspace,
+                         size_t ws_bytes, int64_t max_M, void* stream, fp_plan_t* out) {
+  if (out == nullptr) return FP_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (dtype != FP_BF16 && dtype != FP_F32) return FP_ERR_INVALID_ARG;
+  if (K < 1 || n_proj < 1 || n_proj > FP_MAX_PROJ || N == nullptr) return FP_ERR_INVALID_ARG;
+  if (max_M < 1 || max_M > FP_MAX_M) return FP_ERR_INVALID_ARG;
+  if (w_cat == nullptr || workspace == nullptr) return FP_ERR_INVALID_ARG;
+  const int esize = dtype == FP_BF16 ? 2 : 4;
+  if ((K * esize) % 16 != 0) return FP_ERR_UNSUPPORTED;
+  if (!aligned(w_cat, 256) || !aligned(workspace, 256)) return FP_ERR_UNSUPPORTED;
+  int64_t n_total = 0;
+  for (int i = 0; i < n_proj; ++i) {
+    if (N[i] < 1) return FP_ERR_INVALID_ARG;
+    n_total += N[i];
+  }
+  if (ws_bytes < workspace_need(dtype, K, n_total, max_M)) return FP_ERR_WORKSPACE;
+
+  fp_plan_s* p = new (std::nothrow) fp_plan_s;
+  if (p == nullptr) return FP_ERR_INVALID_ARG;
+  std::memset(p, 0, sizeof *p);
+  p->magic = kPlanMagic;
+  p->dtype = dtype;
+  p->esize = esize;
+  p->K = K;
+  p->kc = K * esize / 16;
+  p->n_proj = n_proj;
+  int64_t off = 0;
+  for (int i = 0; i < n_proj; ++i) {
+    p->N[i] = N[i];
+    p->off[i] = off;
+    off += N[i];
+  }
+  p->n_total = n_total;
+  p->w_cat = static_cast<unsigned char*>(w_cat);
+  p->ws = static_cast<unsigned char*>(workspace);
+  p->ws_bytes = ws_bytes;
+  p->max_M = max_M;
+  p->mfma_min_m = kDefaultMfmaMinM;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // concatenate: W_cat[off_i + r, :] = W_i[r, :]
+  for (int i = 0; i < n_proj && w_src != nullptr; ++i) {
+    unsigned char* dst = p->w_cat + p->off[i] * K * esize;
+    if (w_src[i] == nullptr || w_src[i] == dst) continue;
+    hipError_t e = hipMemcpyAsync(dst, w_src[i], (size_t)(N[i] * K * esize),
+                                  hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e);
+    }
+  }
+  // zero the arrival counters with a kernel (capture-friendly, no memset node)
+  int64_t nc = counters_bytes(n_total) / 4;
+  uint32_t* cptr = reinterpret_cast<uint32_t*>(p->ws);
+  uint32_t zero = 0u;
+  void* fargs[] = {&cptr, &nc, &zero};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fill_u32_kernel),
+                                 dim3((unsigned)ceil_div(nc, 256)), dim3(256), fargs, 0, st);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e);
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    live_plans().insert(p);
+  }
+  *out = p;
+  return FP_OK;
+}
+
+fp_status fp_plan_view(fp_plan_t plan, int32_t i, void** w_i, int64_t* row_offset,
+                       int64_t* rows) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  if (i < 0 || i >= plan->n_proj) return FP_ERR_INVALID_ARG;
+  if (w_i) *w_i = plan->w_cat + plan->off[i] * plan->K * plan->esize;
+  if (row_offset) *row_offset = plan->off[i];
+  if (rows) *rows = plan->N[i];
+  return FP_OK;
+}
+
+fp_status fp_plan_destroy(fp_plan_t plan) {
+  if (plan == nullptr) return FP_ERR_INVALID_ARG;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (live_plans().erase(plan) == 0) return FP_ERR_INVALID_ARG;
+  }
+  plan->magic = 0;
+  delete plan;
+  return FP_OK;
+}
+
+fp_status fp_supported(fp_plan_t plan, int64_t M, const void* x, int64_t ldx) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  fp_status s = check_x(plan, M, x, ldx);
+  if (s != FP_OK || M == 0) return s;
+  Tiling t;
+  if (!choose_tiling(plan, M, plan->n_total, &t)) return FP_ERR_UNSUPPORTED;
+  return FP_OK;
+}
+
+fp_status fp_forward(const void* x, int64_t M, int64_t ldx, fp_plan_t plan, void* stream,
+                     void* const* y) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  fp_status s = check_x(plan, M, x, ldx);
+  if (s != FP_OK) return s;
+  if (M == 0) return FP_OK;
+  s = check_outputs(plan, M, x, ldx, y);
+  if (s != FP_OK) return s;
+  Tiling t;
+  if (!choose_tiling(plan, M, plan->n_total, &t)) return FP_ERR_UNSUPPORTED;
+  fp::RowSpace rs;
+  std::memset(&rs, 0, sizeof rs);
+  rs.w = plan->w_cat;
+  rs.n_seg = plan->n_proj;
+  rs.n_rows = plan->n_total;
+  for (int i = 0; i < plan->n_proj; ++i) {
+    rs.seg[i].y = static_cast<unsigned char*>(y[i]);
+    rs.seg[i].rows = plan->N[i];
+    rs.seg[i].row_begin = plan->off[i];
+  }
+  return run(plan, t, rs, x, M, ldx, static_cast<hipStream_t>(stream));
+}
+
+fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
+                              void* stream, void* const* y,
+                              const void* const* w_override) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  fp_status s = check_x(plan, M, x, ldx);
+  if (s != FP_OK) return s;
+  if (M == 0) return FP_OK;
+  s = check_outputs(plan, M, x, ldx, y);
+  if (s != FP_OK) return s;
+  Tiling ts[FP_MAX_PROJ];
+  for (int i = 0; i < plan->n_proj; ++i) {
+    if (!choose_tiling(plan, M, plan->N[i], &ts[i])) return FP_ERR_UNSUPPORTED;
+    if (w_override != nullptr && w_override[i] != nullptr &&
+        !aligned(w_override[i], 16))
+      return FP_ERR_UNSUPPORTED;
+  }
+  for (int i = 0; i < plan->n_proj; ++i) {
+    fp::RowSpace rs;
+    std::memset(&rs, 0, sizeof rs);
+    rs.n_seg = 1;
+    rs.n_rows = plan->N[i];
+    const unsigned char* w = plan->w_cat + plan->off[i] * plan->K * plan->esize;
+    if (w_override != nullptr && w_override[i] != nullptr)
+      w = static_cast<const unsigned char*>(w_override[i]);
+    rs.w = w;
+    rs.seg[0].y = static_cast<unsigned char*>(y[i]);
+    rs.seg[0].rows = plan->N[i];
+    rs.seg[0].row_begin = 0;
+    s = run(plan, ts[i], rs, x, M, ldx, static_cast<hipStream_t>(stream));
+    if (s != FP_OK) return s;
+  }
+  return FP_OK;
+}
+
+fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path, int32_t* launches_fused,
+                        int32_t* launches_separate) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  if (M < 0) return FP_ERR_INVALID_ARG;
+  if (M == 0) {
+    if (path) *path = FP_PATH_NONE;
+    if (launches_fused) *launches_fused = 0;
+    if (launches_separate) *launches_separate = 0;
+    return FP_OK;
+  }
+  if (M > plan->max_M || (plan->dtype == FP_F32 && M > kSkinnyMaxM)) return FP_ERR_UNSUPPORTED;
+  Tiling t;
+  if (!choose_tiling(plan, M, plan->n_total, &t)) return FP_ERR_UNSUPPORTED;
+  if (path) *path = t.path;
+  if (launches_fused) *launches_fused = 1;
+  if (launches_separate) *launches_separate = plan->n_proj;
+  return FP_OK;
+}
+
+fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  if (min_m < 2 || min_m > FP_MAX_M + 1) return FP_ERR_INVALID_ARG;
+  plan->mfma_min_m = min_m;
+  return FP_OK;
+}
+
+fp_status fp_plan_set_tiling(fp_plan_t plan, int64_t M, const fp_tiling* t) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  if (M < 1 || M > plan->max_M) return FP_ERR_INVALID_ARG;
+  if (t == nullptr) {
+    plan->has_override[M] = false;
+    return FP_OK;
+  }
+  const bool prev = plan->has_override[M];
+  const fp_tiling prev_t = plan->override_t[M];
+  plan->override_t[M] = *t;
+  plan->has_override[M] = true;
+  // must be runnable for the fused launch and for every separate launch
+  Tiling chk;
+  bool ok = choose_tiling(plan, M, plan->n_total, &chk);
+  for (int i = 0; ok && i < plan->n_proj; ++i) ok = choose_tiling(plan, M, plan->N[i], &chk);
+  if (!ok) {
+    // distinguish a workspace shortfall from an unrunnable tiling
+    const size_t saved = plan->ws_bytes;
+    plan->ws_bytes = SIZE_MAX;
+    bool ok_big = choose_tiling(plan, M, plan->n_total, &chk);
+    for (int i = 0; ok_big && i < plan->n_proj; ++i)
+      ok_big = choose_tiling(plan, M, plan->N[i], &chk);
+    plan->ws_bytes = saved;
+    plan->has_override[M] = prev;
+    plan->override_t[M] = prev_t;
+    return ok_big ? FP_ERR_WORKSPACE : FP_ERR_UNSUPPORTED;
+  }
+  return FP_OK;
+}
+
+fp_status fp_plan_get_tiling(fp_plan_t plan, int64_t M, int64_t n_rows, fp_tiling* out) {
+  if (!plan_ok(plan) || out == nullptr) return FP_ERR_INVALID_ARG;
+  if (M < 1 || M > plan->max_M || n_rows < 1 || n_rows > plan->n_total)
+    return FP_ERR_INVALID_ARG;
+  Tiling t;
+  if (!choose_tiling(plan, M, n_rows, &t)) return FP_ERR_UNSUPPORTED;
+  out->path = t.path;
+  out->kparts = t.kparts;
+  out->chunks = t.chunks;
+  out->splits = t.splits;
+  out->rows = t.rows;
+  out->groups = t.groups;
+  return FP_OK;
+}
+
+fp_status fp_default_tiling(int32_t dtype, int64_t K, int64_t n_total, int64_t M,
+                            int64_t n_rows, fp_tiling* out) {
+  if (out == nullptr || (dtype != FP_BF16 && dtype != FP_F32) || K < 1 || n_total < 1)
+    return FP_ERR_INVALID_ARG;
+  const int esize = dtype == FP_BF16 ? 2 : 4;
+  if ((K * esize) % 16 != 0) return FP_ERR_UNSUPPORTED;
+  if (M < 1 || M > FP_MAX_M || n_rows < 1 || n_rows > n_total) return FP_ERR_INVALID_ARG;
+  fp_plan_s tmp;
+  scratch_plan(&tmp, dtype, K, n_total, FP_MAX_M);
+  Tiling t;
+  if (!choose_tiling(&tmp, M, n_rows, &t)) return FP_ERR_UNSUPPORTED;
+  out->path = t.path;
+  out->kparts = t.kparts;
+  out->chunks = t.chunks;
+  out->splits = t.splits;
+  out->rows = t.rows;
+  out->groups = t.groups;
+  return FP_OK;
+}
+
+const char* fp_status_str(int32_t status) {
+  switch (status) {
+    case FP_OK: return "ok";
+    case FP_ERR_INVALID_ARG: return "invalid argument";
+    case FP_ERR_UNSUPPORTED: return "unsupported by the fused kernels";
+    case FP_ERR_HIP: return "HIP error";
+    case FP_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int32_t fp_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

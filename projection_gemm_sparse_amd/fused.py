@@ -1,0 +1,189 @@
+"""Torch-side owner of a fused projection plan.
+
+The load-time half of "tinygemm2 for the DeepSeek-V4.1 hidden-state
+projections" (TensorRT-LLM PR #20636), Description: the projection weights
+that read the same activations are copied once into one row-concatenated
+buffer, and every projection gets a view into it (no second copy is kept);
+checkpoint reloads that write through the views keep the fused path valid,
+while a weight that no longer aliases its view (a replaced Parameter) is
+served by the one-launch-per-projection path with that weight.
+
+Torch only allocates device memory (the concatenated weight, the workspace
+and the outputs) and supplies the stream; every arithmetic step runs in
+libfusedproj's HIP kernels through the C ABI.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+_DTYPES = {torch.bfloat16: L.FP_BF16, torch.float32: L.FP_F32}
+
+
+def _stream_handle(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+class FusedProjection:
+    """Fuses projections ``weights[i]`` ([N_i, K], one dtype, on one GPU).
+
+    ``copy_weights=True`` copies the given tensors into the concatenated
+    buffer; the caller may then rebind its module weights to ``views``.
+    """
+
+    def __init__(self, weights, max_M: int = 8, stream=None, copy_weights: bool = True,
+                 workspace_bytes: int | None = None):
+        if not weights:
+            raise ValueError("at least one projection")
+        w0 = weights[0]
+        if w0.dtype not in _DTYPES:
+            raise TypeError("weights must be bfloat16 or float32, got %s" % w0.dtype)
+        if not w0.is_cuda:
+            raise ValueError("weights must be on a GPU")
+        self.dtype = w0.dtype
+        self.fp_dtype = _DTYPES[w0.dtype]
+        self.device = w0.device
+        self.K = int(w0.shape[1])
+        self.N = [int(w.shape[0]) for w in weights]
+        for w in weights:
+            if w.dtype != self.dtype or w.device != self.device or w.dim() != 2 \
+                    or int(w.shape[1]) != self.K:
+                raise ValueError("all weights must be [N_i, K] of one dtype on one device")
+        self.max_M = int(max_M)
+        self.n_total = sum(self.N)
+        # plan creation under no_grad: the concatenated buffer must not keep
+        # an autograd graph alive (lesson of PR #20502's commit log)
+        with torch.no_grad():
+            self.w_cat = torch.empty(self.n_total, self.K, dtype=self.dtype, device=self.device)
+            self.ws_bytes = L.fp_workspace_bytes(self.fp_dtype, self.K, self.N, self.max_M)
+            if self.ws_bytes == 0:
+                raise L.FusedProjError(L.FP_ERR_INVALID_ARG, "fp_workspace_bytes")
+            if workspace_bytes is not None:
+                # a larger workspace admits tilings with more K splits
+                self.ws_bytes = max(self.ws_bytes, int(workspace_bytes))
+            self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+            src = None
+            if copy_weights:
+                keep = [w.detach().contiguous() for w in weights]  # alive until copied
+                src = [w.data_ptr() for w in keep]
+            st, plan = L.fp_plan_create(self.fp_dtype, self.K, self.N, src,
+                                        self.w_cat.data_ptr(), self.workspace.data_ptr(),
+                                        self.ws_bytes, self.max_M, _stream_handle(stream))
+            L.check(st, "fp_plan_create")
+            if copy_weights:
+                # the copies are stream-ordered; keep the sources alive until done
+                (torch.cuda.current_stream() if stream is None else stream).synchronize()
+                del keep
+        self.plan = plan
+        self.offsets = []
+        self.views = []
+        for i in range(len(self.N)):
+            st, ptr, off, rows = L.fp_plan_view(plan, i)
+            L.check(st, "fp_plan_view")
+            view = self.w_cat.narrow(0, off, rows)
+            assert view.data_ptr() == ptr
+            self.offsets.append(off)
+            self.views.append(view)
+
+    # ----------------------------------------------------------------- guard
+    def aliases_intact(self, weights) -> list:
+        """Per projection: does ``weights[i]`` still alias its view (same
+        storage address, shape and dense strides)?  A replaced Parameter
+        fails this and must go to the separate path with an override."""
+        out = []
+        for w, v in zip(weights, self.views):
+            out.append(w.data_ptr() == v.data_ptr() and tuple(w.shape) == tuple(v.shape)
+                       and w.stride() == v.stride() and w.dtype == v.dtype)
+        return out
+
+    def supported(self, x: torch.Tensor) -> bool:
+        if x.dim() != 2 or x.dtype != self.dtype or x.device != self.device \
+                or x.stride(1) != 1 or int(x.shape[1]) != self.K:
+            return False
+        return L.fp_supported(self.plan, int(x.shape[0]), x.data_ptr(), int(x.stride(0))) == L.FP_OK
+
+    # ---------------------------------------------------------------- calls
+    def _outputs(self, M: int, out):
+        if out is not None:
+            return out
+        return [torch.empty(M, n, dtype=self.dtype, device=self.device) for n in self.N]
+
+    def _check_x(self, x):
+        if x.dim() != 2 or int(x.shape[1]) != self.K or x.stride(1) != 1:
+            raise ValueError("x must be [M, K] with unit column stride")
+        if x.dtype != self.dtype or x.device != self.device:
+            raise ValueError("x dtype/device differ from the plan's")
+
+    def forward(self, x: torch.Tensor, out=None, stream=None):
+        """Fused call: returns one dense [M, N_i] tensor per projection."""
+        self._check_x(x)
+        M = int(x.shape[0])
+        ys = self._outputs(M, out)
+        st = L.fp_forward(x.data_ptr(), M, int(x.stride(0)), self.plan,
+                          _stream_handle(stream), [y.data_ptr() for y in ys])
+        L.check(st, "fp_forward")
+        return ys
+
+    __call__ = forward
+
+    def forward_separate(self, x: torch.Tensor, out=None, w_override=None, stream=None):
+        """One launch per projection; ``w_override[i]`` (a [N_i, K] tensor)
+        replaces projection i's view."""
+        self._check_x(x)
+        M = int(x.shape[0])
+        ys = self._outputs(M, out)
+        ov = None
+        if w_override is not None:
+            ov = []
+            for i, w in enumerate(w_override):
+                if w is None:
+                    ov.append(None)
+                    continue
+                if tuple(w.shape) != (self.N[i], self.K) or not w.is_contiguous() \
+                        or w.dtype != self.dtype or w.device != self.device:
+                    raise ValueError("override %d must be a dense [%d, %d] tensor"
+                                     % (i, self.N[i], self.K))
+                ov.append(w.data_ptr())
+        st = L.fp_forward_separate(x.data_ptr(), M, int(x.stride(0)), self.plan,
+                                   _stream_handle(stream), [y.data_ptr() for y in ys], ov)
+        L.check(st, "fp_forward_separate")
+        return ys
+
+    def forward_modules(self, x: torch.Tensor, weights, out=None, stream=None):
+        """Dispatch as a module would: the fused call while every weight
+        aliases its view, else the separate path with the replaced weights."""
+        intact = self.aliases_intact(weights)
+        if all(intact):
+            return self.forward(x, out=out, stream=stream)
+        ov = [None if ok else w.detach().contiguous() for ok, w in zip(intact, weights)]
+        return self.forward_separate(x, out=out, w_override=ov, stream=stream)
+
+    # ----------------------------------------------------------- tuning/query
+    def query(self, M: int):
+        st, path, lf, ls = L.fp_plan_query(self.plan, M)
+        L.check(st, "fp_plan_query")
+        return path, lf, ls
+
+    def set_tiling(self, M: int, tiling) -> int:
+        return L.fp_plan_set_tiling(self.plan, M, tiling)
+
+    def get_tiling(self, M: int, n_rows: int | None = None):
+        st, t = L.fp_plan_get_tiling(self.plan, M, self.n_total if n_rows is None else n_rows)
+        L.check(st, "fp_plan_get_tiling")
+        return t
+
+    def set_mfma_min_m(self, m: int) -> None:
+        L.check(L.fp_plan_set_mfma_min_m(self.plan, m), "fp_plan_set_mfma_min_m")
+
+    def close(self) -> None:
+        if getattr(self, "plan", None) is not None:
+            L.fp_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,155 @@
+"""Host-side checks of libfusedproj (no GPU needed, no compute call).
+
+The library loads, exports every function include/fusedproj.h declares, and
+every argument check returns its status before any HIP call (fake device
+addresses are never dereferenced because validation fails first).  The
+tiling logic is checked for the property the bitwise guarantees rest on:
+the summation-order fields never depend on the rows of a launch.
+"""
+import ctypes
+
+import pytest
+
+import projection_gemm_sparse_amd as P
+from projection_gemm_sparse_amd import _lib as L
+
+FAKE = 0x7f0000000000  # 256-byte aligned, never dereferenced
+
+
+def test_exports_every_declared_symbol():
+    names = L.header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L._lib, n), n
+        assert n in L._SIGS, "binding lacks %s" % n
+
+
+def test_status_strings():
+    for st in range(5):
+        assert P.fp_status_str(st) and P.fp_status_str(st) != "unknown status"
+    assert P.fp_status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("args", [
+    (2, 5120, [1280, 512], 8),      # bad dtype
+    (0, 0, [1280, 512], 8),         # K < 1
+    (0, 5121, [1280, 512], 8),      # K*2 not a multiple of 16
+    (1, 7170, [128], 8),            # K*4 not a multiple of 16
+    (0, 5120, [], 8),               # no projection
+    (0, 5120, [0, 512], 8),         # empty projection
+    (0, 5120, [1] * 17, 8),         # too many projections
+    (0, 5120, [1280], 0),           # max_M < 1
+    (0, 5120, [1280], 257),         # max_M too large
+])
+def test_workspace_bytes_rejects(args):
+    assert P.fp_workspace_bytes(*args) == 0
+
+
+def test_workspace_bytes_values():
+    # counters (one per possible row block, 256-byte rounded) + partials
+    ws1 = P.fp_workspace_bytes(0, 5120, [1280, 512], 8)
+    assert ws1 >= 1792 * 4
+    ws128 = P.fp_workspace_bytes(0, 5120, [1280, 512], 128)
+    assert ws128 > ws1  # MFMA split-K partials for large M
+    wsf = P.fp_workspace_bytes(1, 7168, [128, 64], 8)
+    st, t = P.fp_default_tiling(1, 7168, 192, 8, 192)
+    assert st == 0 and t[3] > 1  # fp32 indexer shape splits K
+    assert wsf >= 256 + t[3] * 192 * 8 * 4
+
+
+def _create(dtype=0, K=5120, N=(1280, 512), w_cat=FAKE, ws=FAKE, ws_bytes=None, max_M=8):
+    if ws_bytes is None:
+        ws_bytes = P.fp_workspace_bytes(dtype, K, list(N), max_M)
+    return P.fp_plan_create(dtype, K, list(N), None, w_cat, ws, ws_bytes, max_M, 0)
+
+
+def test_plan_create_validation_before_any_hip_call():
+    assert _create(dtype=3)[0] == P.FP_ERR_INVALID_ARG
+    assert _create(K=-1)[0] == P.FP_ERR_INVALID_ARG
+    assert _create(N=(0,))[0] == P.FP_ERR_INVALID_ARG
+    assert _create(max_M=0)[0] == P.FP_ERR_INVALID_ARG
+    assert _create(w_cat=0)[0] == P.FP_ERR_INVALID_ARG
+    assert _create(ws=0)[0] == P.FP_ERR_INVALID_ARG
+    assert _create(K=5124)[0] == P.FP_ERR_UNSUPPORTED          # rows not 16-B aligned
+    assert _create(w_cat=FAKE + 16)[0] == P.FP_ERR_UNSUPPORTED  # w_cat not 256-B aligned
+    assert _create(ws=FAKE + 64)[0] == P.FP_ERR_UNSUPPORTED
+    assert _create(ws_bytes=16)[0] == P.FP_ERR_WORKSPACE
+    # null out pointer
+    N = (ctypes.c_int64 * 1)(1280)
+    assert L._lib.fp_plan_create(0, 5120, 1, N, None, FAKE, FAKE, 1 << 30, 8, None, None) \
+        == P.FP_ERR_INVALID_ARG
+
+
+def test_calls_on_a_stale_or_null_plan():
+    for plan in (0, FAKE, 12345678):
+        assert P.fp_plan_destroy(plan) == P.FP_ERR_INVALID_ARG
+        assert P.fp_supported(plan, 1, FAKE, 5120) == P.FP_ERR_INVALID_ARG
+        assert P.fp_forward(FAKE, 1, 5120, plan, 0, [FAKE, FAKE]) == P.FP_ERR_INVALID_ARG
+        assert P.fp_forward_separate(FAKE, 1, 5120, plan, 0, [FAKE, FAKE]) == P.FP_ERR_INVALID_ARG
+        assert P.fp_plan_view(plan, 0)[0] == P.FP_ERR_INVALID_ARG
+        assert P.fp_plan_query(plan, 1)[0] == P.FP_ERR_INVALID_ARG
+        assert P.fp_plan_set_mfma_min_m(plan, 9) == P.FP_ERR_INVALID_ARG
+        assert P.fp_plan_set_tiling(plan, 1, None) == P.FP_ERR_INVALID_ARG
+        assert P.fp_plan_get_tiling(plan, 1, 1)[0] == P.FP_ERR_INVALID_ARG
+
+
+def test_default_tiling_argument_checks():
+    assert P.fp_default_tiling(0, 5120, 1792, 0, 1792)[0] == P.FP_ERR_INVALID_ARG
+    assert P.fp_default_tiling(0, 5120, 1792, 1, 1793)[0] == P.FP_ERR_INVALID_ARG
+    assert P.fp_default_tiling(0, 5120, 1792, 257, 1792)[0] == P.FP_ERR_INVALID_ARG
+    assert P.fp_default_tiling(5, 5120, 1792, 1, 1792)[0] == P.FP_ERR_INVALID_ARG
+    assert P.fp_default_tiling(0, 5122, 1792, 1, 1792)[0] == P.FP_ERR_UNSUPPORTED
+    # fp32 is served for M <= 8 only
+    assert P.fp_default_tiling(1, 7168, 192, 9, 192)[0] == P.FP_ERR_UNSUPPORTED
+
+
+SHAPES = [(0, 5120, (1280, 512)), (1, 7168, (128, 64)), (0, 6144, (2048, 576, 128)),
+          (0, 4096, (100, 28, 3)), (1, 1024, (5,))]
+
+
+@pytest.mark.parametrize("dtype,K,N", SHAPES)
+def test_summation_order_independent_of_launch_rows(dtype, K, N):
+    """path/kparts/chunks/splits (the summation order) must be the same for
+    the fused launch (all rows) and each separate launch (one projection):
+    that is what makes fused == separate bitwise."""
+    n_total = sum(N)
+    maxm = 8 if dtype == 1 else 256
+    for M in list(range(1, 17)) + [31, 32, 33, 64, 100, 128, 200, 256]:
+        if M > maxm:
+            continue
+        st, fused = P.fp_default_tiling(dtype, K, n_total, M, n_total)
+        assert st == 0, (M, st)
+        for n in N:
+            st, sep = P.fp_default_tiling(dtype, K, n_total, M, n)
+            assert st == 0
+            assert sep[:4] == fused[:4], (M, n, fused, sep)
+
+
+@pytest.mark.parametrize("dtype,K,N", SHAPES)
+def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
+    n_total = sum(N)
+    esize = 2 if dtype == 0 else 4
+    kc = K * esize // 16
+    maxm = 8 if dtype == 1 else 256
+    ws = P.fp_workspace_bytes(dtype, K, list(N), maxm)
+    counters = ((n_total * 4 + 255) // 256) * 256
+    for M in range(1, maxm + 1):
+        st, (path, kp, ch, S, rows, groups) = P.fp_default_tiling(dtype, K, n_total, M, n_total)
+        assert st == 0
+        if path == P.FP_PATH_MFMA:
+            assert S * kp * ch * 16 >= kc
+            assert M > 8 or M >= 9
+        else:
+            assert M <= 8
+            assert S * kp * 64 * ch >= kc
+            assert (S > 1) == (path == P.FP_PATH_SKINNY_SPLITK)
+        if S > 1:
+            assert counters + S * n_total * M * 4 <= ws
+
+
+def test_default_crossover():
+    # skinny kernel up to M = 8, MFMA tiles above
+    for M in range(1, 9):
+        assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] in (1, 2)
+    for M in (9, 16, 32, 64, 128):
+        assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA

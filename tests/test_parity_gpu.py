@@ -1,0 +1,234 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every workload cell is checked element by element against the oracle's
+fp64 result under the acceptance bound (bf16: 2^-7 * S + 1e-6, fp32:
+1e-5 * S + 1e-7, S = sum_k |x_k w_k|); fused and one-launch-per-projection
+outputs must be bitwise equal, and so must repeats.  Integer-valued data
+must be bit exact (every partial sum is an exact integer below 2^24).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+import projection_gemm_sparse_amd as P
+from gpu_util import (BF16, F32, assert_bitwise_equal, assert_matches_oracle, out_bits,
+                      to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def _plan(ws_cpu, max_M=8, workspace_bytes=None):
+    return P.FusedProjection([to_gpu(w) for w in ws_cpu], max_M=max_M,
+                             workspace_bytes=workspace_bytes)
+
+
+def _check_case(fp, x_cpu, ws_cpu, label, rows=None, separate=True):
+    x = to_gpu(x_cpu)
+    if x_cpu.shape[1] != fp.K:
+        x = x[:, :fp.K]
+    ys = fp(x)
+    assert_matches_oracle(ys, x_cpu[:, :fp.K].contiguous(), ws_cpu, rows=rows, label=label)
+    ys2 = fp(x)
+    assert_bitwise_equal(ys, ys2, label + " repeat")
+    if separate:
+        ysep = fp.forward_separate(x)
+        assert_bitwise_equal(ys, ysep, label + " fused vs separate")
+    return ys
+
+
+def test_library_is_the_in_tree_build():
+    import os
+    here = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    assert os.path.dirname(os.path.abspath(P.LIB_PATH)) == os.path.join(
+        here, "projection_gemm_sparse_amd")
+    assert torch.cuda.is_available()
+
+
+# ---- wq_a + wkv, one token (K=5120, [1280, 512], bf16, seed 0)
+def test_wq_a_wkv_m1():
+    x, ws = si.workload_case("wq_a+wkv_m1", 1, 0)
+    fp = _plan(ws)
+    assert fp.query(1) == (P.FP_PATH_SKINNY, 1, 2)
+    _check_case(fp, x, ws, "wq_a+wkv M=1")
+
+
+# ---- M in {2, 4, 8}, seeds 1-3
+@pytest.mark.parametrize("M", [2, 4, 8])
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_wq_a_wkv_m2_8(M, seed):
+    x, ws = si.workload_case("wq_a+wkv_m2_8", M, seed)
+    fp = _plan(ws)
+    _check_case(fp, x, ws, "wq_a+wkv M=%d seed=%d" % (M, seed))
+
+
+# ---- fp32 indexer fusion, split-K (K=7168, [128, 64])
+@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_indexer_fp32_splitk(M, seed):
+    x, ws = si.workload_case("indexer_f32", M, seed)
+    fp = _plan(ws)
+    path, _, _ = fp.query(M)
+    assert path == P.FP_PATH_SKINNY_SPLITK
+    _check_case(fp, x, ws, "indexer fp32 M=%d seed=%d" % (M, seed))
+
+
+# ---- three-way fused-A (K=6144, [2048, 576, 128]), M 1..8
+@pytest.mark.parametrize("M", range(1, 9))
+def test_fused_a_three_way(M):
+    x, ws = si.workload_case("fused_a_3way", M, 0)
+    fp = _plan(ws)
+    _check_case(fp, x, ws, "fused-A M=%d" % M)
+
+
+# ---- crossover sweep, strided x (row stride K + 64); sampled token rows
+#      for large M (the oracle's cost grows with M; rows are independent)
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 9, 16, 32, 64, 128])
+def test_crossover_sweep_strided_x(M):
+    K = 5120
+    x_full, ws = si.workload_case("crossover", M, 0, ldx=K + 64)
+    fp = _plan(ws, max_M=128)
+    x = to_gpu(x_full)[:, :K]
+    assert x.stride(0) == K + 64
+    ys = fp(x)
+    rows = None if M <= 16 else sorted({0, 1, M // 2, M - 2, M - 1} | set(range(3, M, 13)))
+    assert_matches_oracle(ys, x_full[:, :K].contiguous(), ws, rows=rows,
+                          label="crossover M=%d" % M)
+    assert_bitwise_equal(ys, fp.forward_separate(x), "crossover M=%d fused/sep" % M)
+    # contiguous x gives the same bits as the strided view
+    assert_bitwise_equal(ys, fp(x.contiguous()), "crossover M=%d strided/contig" % M)
+
+
+# ---- small shapes: several tiles, ragged tails, odd projection sizes
+@pytest.mark.parametrize("dt", [BF16, F32])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 7, 8, 9, 17, 33])
+def test_ragged_small_shapes(dt, M):
+    if dt == F32 and M > 8:
+        pytest.skip("fp32 is served for M <= 8")
+    K = 136 if dt == BF16 else 132
+    N = (37, 5, 70, 1)
+    x, ws = si.make_case(K, N, "bf16" if dt == BF16 else "f32", M, seed=40 + M,
+                         w_dist="uniform_inv_sqrt_k" if dt == BF16 else "normal_0.02")
+    fp = _plan(ws, max_M=64)
+    _check_case(fp, x, ws, "ragged %s M=%d" % (dt, M))
+
+
+@pytest.mark.parametrize("dt", [BF16, F32])
+@pytest.mark.parametrize("K", [8, 1032, 20480])
+def test_k_extremes(dt, K):
+    if dt == F32:
+        K = K // 2 if K > 8 else 4
+    N = (300, 29)
+    x, ws = si.make_case(K, N, "bf16" if dt == BF16 else "f32", 3, seed=K,
+                         w_dist="uniform_inv_sqrt_k" if dt == BF16 else "normal_0.02")
+    fp = _plan(ws, max_M=16)
+    _check_case(fp, x, ws, "K=%d %s" % (K, dt))
+
+
+# ---- integer data: bit exact on every path
+@pytest.mark.parametrize("dt,K,N,M", [
+    (BF16, 5120, (1280, 512), 1), (BF16, 5120, (1280, 512), 8),
+    (BF16, 5120, (1280, 512), 32), (BF16, 6144, (2048, 576, 128), 5),
+    (F32, 7168, (128, 64), 4), (F32, 7168, (128, 64), 1)])
+def test_integer_data_bit_exact(dt, K, N, M):
+    x, ws = si.make_case(K, N, "bf16" if dt == BF16 else "f32", M, seed=7,
+                         w_dist="int4", x_dist="int4")
+    fp = _plan(ws, max_M=32)
+    ys = fp(to_gpu(x))
+    got = out_bits(ys)
+    xi = x.float().numpy().astype(np.int64)
+    for w, g in zip(ws, got):
+        exact = (xi @ w.float().numpy().astype(np.int64).T).astype(np.float64)
+        if dt == BF16:
+            want = oracle.round_bf16(exact)
+        else:
+            want = exact.astype(np.float32).view(np.uint32)
+        assert np.array_equal(g, want)
+
+
+# ---- every tiling the kernels accept passes; fused == separate under each
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
+def test_tilings_all_pass(M):
+    x, ws = si.workload_case("crossover", M, 3)
+    fp = _plan(ws, max_M=16, workspace_bytes=64 << 20)
+    xg = to_gpu(x)
+    tilings = [
+        (P.FP_PATH_SKINNY, 10, 1, 1, 0, 0),
+        (P.FP_PATH_SKINNY, 5, 2, 1, 0, 0),
+        (P.FP_PATH_SKINNY, 5, 1, 2, 0, 0),
+        (P.FP_PATH_SKINNY, 2, 1, 5, 1, 0),
+        (P.FP_PATH_SKINNY, 4, 2, 2, 0, 2),
+        (P.FP_PATH_SKINNY, 10, 1, 1, 1, 1),
+        (P.FP_PATH_MFMA, 4, 2, 5, 1, 0),
+        (P.FP_PATH_MFMA, 1, 4, 10, 4, 0),
+        (P.FP_PATH_MFMA, 2, 1, 20, 2, 0),
+        (P.FP_PATH_MFMA, 8, 1, 5, 1, 0),
+    ]
+    ran = 0
+    for t in tilings:
+        st = fp.set_tiling(M, t)
+        if st != P.FP_OK:
+            assert st == P.FP_ERR_UNSUPPORTED and t[0] != P.FP_PATH_MFMA and M > 8, (t, st)
+            continue
+        ran += 1
+        ys = fp(xg)
+        assert_matches_oracle(ys, x, ws, label="tiling %s M=%d" % (t, M))
+        assert_bitwise_equal(ys, fp.forward_separate(xg), "tiling %s fused/sep" % (t,))
+    assert ran >= 4
+    fp.set_tiling(M, None)
+
+
+# ---- edge cases
+def test_m_zero_launches_nothing():
+    x, ws = si.workload_case("wq_a+wkv_m1", 1, 0)
+    fp = _plan(ws)
+    sentinel = [torch.full((1, n), 3.0, dtype=BF16, device="cuda") for n in fp.N]
+    x0 = to_gpu(x)[:0]
+    assert P.fp_forward(x0.data_ptr() or 0, 0, fp.K, fp.plan, 0,
+                        [y.data_ptr() for y in sentinel]) == P.FP_OK
+    torch.cuda.synchronize()
+    assert all(bool((y == 3.0).all()) for y in sentinel)
+    assert fp.query(0) == (P.FP_PATH_NONE, 0, 0)
+
+
+def test_max_m_sampled():
+    M = 256
+    x, ws = si.make_case(1024, (300, 77), "bf16", M, seed=5)
+    fp = _plan(ws, max_M=256)
+    ys = fp(to_gpu(x))
+    rows = [0, 1, 100, 127, 128, 200, 254, 255]
+    assert_matches_oracle(ys, x, ws, rows=rows, label="M=256")
+
+
+def test_unsupported_inputs_are_refused_without_launch():
+    x, ws = si.workload_case("wq_a+wkv_m1", 2, 0)
+    fp = _plan(ws, max_M=8)
+    xg = to_gpu(x)
+    outs = [torch.full((2, n), 7.0, dtype=BF16, device="cuda") for n in fp.N]
+    ptrs = [o.data_ptr() for o in outs]
+    # misaligned x (2-byte offset)
+    buf = torch.zeros(2 * 5120 + 8, dtype=BF16, device="cuda")
+    assert P.fp_forward(buf.data_ptr() + 2, 2, 5120, fp.plan, 0, ptrs) == P.FP_ERR_UNSUPPORTED
+    # row stride not a multiple of 16 bytes
+    assert P.fp_forward(xg.data_ptr(), 2, 5121, fp.plan, 0, ptrs) == P.FP_ERR_UNSUPPORTED
+    # ldx < K
+    assert P.fp_forward(xg.data_ptr(), 2, 5000, fp.plan, 0, ptrs) == P.FP_ERR_INVALID_ARG
+    # M above max_M
+    assert P.fp_forward(xg.data_ptr(), 9, 5120, fp.plan, 0, ptrs) == P.FP_ERR_UNSUPPORTED
+    # output overlapping x
+    assert P.fp_forward(xg.data_ptr(), 2, 5120, fp.plan, 0,
+                        [xg.data_ptr(), ptrs[1]]) == P.FP_ERR_INVALID_ARG
+    # outputs overlapping each other
+    assert P.fp_forward(xg.data_ptr(), 2, 5120, fp.plan, 0,
+                        [ptrs[0], ptrs[0]]) == P.FP_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert all(bool((o == 7.0).all()) for o in outs)
+    assert fp.supported(xg) and not fp.supported(to_gpu(si.workload_case("wq_a+wkv_m1", 9, 0)[0]))
+
+
+def test_single_row_projections_and_one_projection():
+    x, ws = si.make_case(5120, (1,), "bf16", 4, seed=9)
+    _check_case(_plan(ws), x, ws, "one row")
+    x, ws = si.make_case(5120, (1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1), "bf16", 3, seed=9)
+    _check_case(_plan(ws), x, ws, "16 single-row projections")
