@@ -160,19 +160,22 @@ fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
 
 /* Tiling of one token count (benchmarking and testing aid).  Every tiling
  * the kernels accept gives results within the same error bound; the
- * summation order, hence the exact bits, depends on path, kparts, chunks and
- * splits (never on rows/groups), so fused and separate calls of one plan
- * stay bitwise equal under any tiling.
+ * summation order, hence the exact bits, depends on path, kparts, chunks,
+ * splits and (mfma) groups -- never on rows or the skinny groups -- so fused
+ * and separate calls of one plan stay bitwise equal under any tiling.
  *   path    FP_PATH_SKINNY / FP_PATH_SKINNY_SPLITK (same kernel; the
  *           splits field decides) or FP_PATH_MFMA (bf16 only)
  *   kparts  skinny: waves splitting one K slice (P); mfma: PK
  *   chunks  skinny: 16-byte chunks per lane and row (CJ, 1..2);
- *           mfma: 128-wide k tiles per wave (KTW: 1, 2 or 4)
+ *           mfma: 128-wide k tiles per wave and K sub-slice (KTW: 1, 2, 4)
  *   splits  K slices across workgroups (S >= 1), finished in-launch
- *   rows    skinny: rows per wave (RW, 1..8); mfma: 16-row groups per
- *           workgroup (GR); 0 = chosen per launch from its row count
+ *   rows    skinny: rows per wave (RW, 1..8); mfma: row groups per
+ *           workgroup (GR, each of 16/Q rows); 0 = chosen per launch from
+ *           its row count
  *   groups  skinny: row groups per workgroup (G); 0 = chosen per launch;
- *           mfma: ignored */
+ *           mfma: Q, the k-slice packing of the 16 MFMA rows (1, 2, 4, 8:
+ *           16/Q weight rows times Q slices of K; Q > 1 serves at most
+ *           16/Q tokens); part of the summation order */
 typedef struct {
   int32_t path;
   int32_t kparts;

@@ -31,6 +31,8 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive preloaded in SGPRs
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 

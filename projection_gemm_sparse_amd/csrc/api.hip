@@ -96,12 +96,11 @@ int64_t counters_bytes(int64_t n_total) {
 void default_skinny_order(int32_t dtype, int64_t kc, int64_t n_total, int mt,
                           Tiling* t) {
   (void)mt;
-  // Split K across workgroups only when the rows alone cannot give each CU
-  // work: fewer than two rows per CU.
-  int64_t S = 1;
-  if (n_total < 2 * kCus) S = std::min<int64_t>(ceil_div(2 * kCus, n_total), 8);
-  // the kernel covers at most 16 waves * 64 lanes * 2 chunks per slice
-  S = std::max<int64_t>(S, ceil_div(kc, 16 * 64 * 2));
+  (void)n_total;
+  // One workgroup covers a whole row whenever it can (16 waves * 64 lanes *
+  // 2 chunks): finishing a K split across workgroups costs three dependent
+  // memory round trips, more than the idle CUs of a short launch lose.
+  const int64_t S = ceil_div(kc, 16 * 64 * 2);
   const int64_t per = ceil_div(kc, S);
   const int64_t CJ = ceil_div(per, 16 * 64);
   const int64_t P = ceil_div(per, 64 * CJ);
@@ -112,34 +111,73 @@ void default_skinny_order(int32_t dtype, int64_t kc, int64_t n_total, int mt,
   (void)dtype;
 }
 
-void default_mfma_order(int64_t kc, int mt16, Tiling* t) {
-  const int64_t kt = ceil_div(kc, 16);
-  const int PK = mt16 == 1 ? 4 : 1;
-  const int KTW = 2;
+// MFMA order fields: Q (k-slice packing, kept in `groups`), PK, KTW, S.
+void default_mfma_order(int64_t kc, int64_t M, Tiling* t) {
+  const int64_t kt = ceil_div(kc, 16);  // 128-wide k tiles
+  int Q, KTW;
+  int64_t PK;
+  if (M <= 4) {
+    Q = 4; KTW = 2;    // 4-row tiles, 4 K sub-slices
+  } else if (M <= 8) {
+    Q = 2; KTW = 2;    // 8-row tiles, 2 K sub-slices
+  } else {
+    Q = 1; KTW = 2;
+  }
+  if (M <= 32) {
+    // up to 10 waves split K inside the workgroup
+    PK = std::min<int64_t>(10, ceil_div(kt, (int64_t)Q * KTW));
+  } else {
+    PK = 1;            // 8 row groups share activations staged in LDS
+  }
   t->path = FP_PATH_MFMA;
-  t->kparts = PK;
+  t->groups = Q;
+  t->kparts = (int)PK;
   t->chunks = KTW;
-  t->splits = (int)ceil_div(kt, (int64_t)PK * KTW);
+  t->splits = (int)ceil_div(kt, PK * Q * KTW);
 }
 
 // Launch-level part (work per workgroup): may depend on the launch's rows.
+// Rows per workgroup R = G * RW are chosen so that every workgroup is
+// resident at once (one round: all weight loads in flight together) and,
+// among those, to minimise the rows of the busiest CU,
+// ceil(ceil(n_rows / R) / CUs) * R (ties: the larger R, fewer workgroups);
+// RW <= min(8, 64 / MT) and G * P waves fit one workgroup.  Without a
+// one-round choice the largest R is taken.
 void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t) {
   const int rw_max = std::min(8, 64 / mt);
-  // rows per workgroup so that the launch has about one workgroup per CU
-  const int64_t target =
-      std::max<int64_t>(1, (n_rows * t->splits + kCus / 2) / kCus);
-  if (t->rows <= 0) t->rows = (int)std::min<int64_t>(rw_max, target);
-  if (t->groups <= 0) {
-    const int max_threads = fp::skinny_max_threads(t->mt, t->rows, t->chunks);
-    int64_t G = std::max<int64_t>(1, ceil_div(target, t->rows));
-    G = std::min<int64_t>(G, std::max(1, max_threads / (64 * t->kparts)));
-    t->groups = (int)G;
+  const int64_t rows = n_rows * t->splits;  // work units: (row, K slice)
+  if (t->rows > 0 && t->groups > 0) return;
+  int best_rw = 1, best_g = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int rw = 1; rw <= rw_max; ++rw) {
+    if (t->rows > 0 && rw != t->rows) continue;
+    const int g_cap = std::max(1, fp::skinny_max_threads(t->mt, rw, t->chunks) / (64 * t->kparts));
+    for (int g = 1; g <= g_cap; ++g) {
+      if (t->groups > 0 && g != t->groups) continue;
+      const int64_t R = (int64_t)rw * g;
+      const int64_t nb = ceil_div(rows, R);
+      // resident workgroups per CU: 32 wave slots; the kernels' register
+      // use (under 100 VGPRs) lets two workgroups of up to 16 waves share
+      // a CU, more are not assumed
+      const int waves = g * t->kparts;
+      const int64_t resident = std::max(1, std::min(2, 32 / waves));
+      const bool one_round = nb <= resident * kCus;
+      const int64_t cost = one_round ? ceil_div(nb, kCus) * R : INT64_MAX / 2 - R;
+      if (cost < best_cost || (cost == best_cost && R > (int64_t)best_rw * best_g)) {
+        best_cost = cost;
+        best_rw = rw;
+        best_g = g;
+      }
+    }
   }
+  t->rows = best_rw;
+  t->groups = best_g;
 }
 
+bool mfma_xlds(const Tiling& t) { return t.groups == 1 && (t.rows > 1 || t.mt >= 4); }
+
 void resolve_mfma_rows(int mt16, Tiling* t) {
-  if (t->rows <= 0) t->rows = mt16 >= 4 ? 8 : (mt16 == 2 ? 4 : 1);
-  t->groups = 1;
+  if (t->rows <= 0) t->rows = mt16 >= 4 ? 8 : 1;
 }
 
 size_t skinny_lds(const Tiling& t) {
@@ -150,10 +188,12 @@ size_t skinny_lds(const Tiling& t) {
 }
 
 size_t mfma_lds(const Tiling& t) {
-  const size_t pitch = (size_t)t.kparts * t.chunks * 16 + 1;
-  const size_t xs = (size_t)16 * t.mt * pitch * 16;
-  const size_t red = t.kparts > 1 ? (size_t)t.rows * t.kparts * t.mt * 256 * 4 : 0;
-  return xs + red + 16;
+  const int Q = t.groups;
+  const size_t pitch = (size_t)t.kparts * Q * t.chunks * 16 + 1;  // Q == 1 when staged
+  const size_t xs = mfma_xlds(t) ? (size_t)16 * t.mt * pitch * 16 : 0;
+  const size_t rt = 16 / Q, mc = Q == 1 ? 16 : 16 / Q;
+  const size_t red = (size_t)t.rows * t.kparts * Q * t.mt * rt * mc * 4;
+  return std::max(xs, red) + 16;  // the reduction reuses the staging space
 }
 
 // Partial-sum floats a tiling needs for a launch of n_rows rows and M tokens.
@@ -163,16 +203,27 @@ int64_t partial_floats(const Tiling& t, int64_t n_rows, int64_t M) {
 
 bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t) {
   if (t.splits < 1 || t.kparts < 1 || t.chunks < 1 || t.rows < 1) return false;
+  // packed into 8- and 16-bit fields of the kernels' scalar arguments
+  if (t.splits > 0x7fff || t.kparts > 0xff || t.rows > 0xff || t.groups > 0xffff) return false;
   if (t.path == FP_PATH_MFMA) {
+    const int Q = t.groups;
     if (p->dtype != FP_BF16) return false;
+    if (!(Q == 1 || Q == 2 || Q == 4 || Q == 8)) return false;
+    if (Q > 1 && (t.mt != 1 || M > 16 / Q)) return false;
     if (!(t.chunks == 1 || t.chunks == 2 || t.chunks == 4)) return false;
-    if ((int64_t)t.rows * t.kparts * 64 > fp::mfma_max_threads(t.mt, t.chunks)) return false;
-    if ((int64_t)t.splits * t.kparts * t.chunks * 16 < p->kc) return false;
+    if (!mfma_xlds(t) && t.mt > 2) return false;
+    if ((int64_t)t.rows * t.kparts * 64 > fp::mfma_max_threads(t.mt, t.chunks, mfma_xlds(t)))
+      return false;
+    if ((int64_t)t.splits * t.kparts * Q * t.chunks * 16 < p->kc) return false;
     if (mfma_lds(t) > kMaxLds) return false;
     if (16 * (int64_t)t.mt < M) return false;
   } else if (t.path == FP_PATH_SKINNY || t.path == FP_PATH_SKINNY_SPLITK) {
     if (M > kSkinnyMaxM) return false;
-    if (t.chunks > 2 || t.rows > 8 || t.rows * t.mt > 64) return false;
+    if (t.rows > 8 || t.rows * t.mt > 64) return false;
+    const bool cj_ok = t.chunks <= 2 || (t.mt <= 2 && t.rows <= 2 &&
+        (t.chunks == 4 || t.chunks == 5 || t.chunks == 6 || t.chunks == 8 ||
+         t.chunks == 10 || t.chunks == 12));
+    if (!cj_ok) return false;
     if (t.groups < 1) return false;
     if ((int64_t)t.groups * t.kparts * 64 > fp::skinny_max_threads(t.mt, t.rows, t.chunks))
       return false;
@@ -200,10 +251,11 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t) {
     if (t->path == FP_PATH_SKINNY || t->path == FP_PATH_SKINNY_SPLITK) {
       t->path = t->splits > 1 ? FP_PATH_SKINNY_SPLITK : FP_PATH_SKINNY;
     }
+    if (t->path == FP_PATH_MFMA && t->groups <= 0) t->groups = 1;
   } else {
     const bool mfma = p->dtype == FP_BF16 && (M >= p->mfma_min_m || M > kSkinnyMaxM);
     if (mfma) {
-      default_mfma_order(p->kc, mfma_mt16(M), t);
+      default_mfma_order(p->kc, M, t);
     } else {
       if (M > kSkinnyMaxM) return false;
       default_skinny_order(p->dtype, p->kc, p->n_total, skinny_mt(M), t);
@@ -254,7 +306,7 @@ size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) 
   if (dtype == FP_BF16) {
     for (int64_t M = 1; M <= max_M; ++M) {
       Tiling t;
-      default_mfma_order(tmp.kc, mfma_mt16(M), &t);
+      default_mfma_order(tmp.kc, M, &t);
       most = std::max(most, partial_floats(t, n_total, M));
     }
   }
@@ -277,10 +329,35 @@ const void* skinny_fn_rw(int rw) {
   }
 }
 
+// Long per-lane chunk runs (a wave covering a whole row) only for one or
+// two rows per wave and at most two tokens.
+template <int MT, int CJ, bool BF16>
+const void* skinny_fn_rw_long(int rw) {
+  switch (rw) {
+    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, BF16>);
+    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, BF16>);
+    default: return nullptr;
+  }
+}
+
 template <int MT, bool BF16>
 const void* skinny_fn_cj(int cj, int rw) {
-  if (cj == 1) return skinny_fn_rw<MT, 1, BF16>(rw);
-  if (cj == 2) return skinny_fn_rw<MT, 2, BF16>(rw);
+  switch (cj) {
+    case 1: return skinny_fn_rw<MT, 1, BF16>(rw);
+    case 2: return skinny_fn_rw<MT, 2, BF16>(rw);
+    default: break;
+  }
+  if constexpr (MT <= 2) {
+    switch (cj) {
+      case 4: return skinny_fn_rw_long<MT, 4, BF16>(rw);
+      case 5: return skinny_fn_rw_long<MT, 5, BF16>(rw);
+      case 6: return skinny_fn_rw_long<MT, 6, BF16>(rw);
+      case 8: return skinny_fn_rw_long<MT, 8, BF16>(rw);
+      case 10: return skinny_fn_rw_long<MT, 10, BF16>(rw);
+      case 12: return skinny_fn_rw_long<MT, 12, BF16>(rw);
+      default: break;
+    }
+  }
   return nullptr;
 }
 
@@ -295,23 +372,35 @@ const void* skinny_fn_mt(int mt, int cj, int rw) {
   }
 }
 
-template <int MT16>
+template <int Q, int MT16, bool XLDS>
 const void* mfma_fn_ktw(int ktw) {
   switch (ktw) {
-    case 1: return reinterpret_cast<const void*>(&fp::mfma_kernel<MT16, 1>);
-    case 2: return reinterpret_cast<const void*>(&fp::mfma_kernel<MT16, 2>);
-    case 4: return reinterpret_cast<const void*>(&fp::mfma_kernel<MT16, 4>);
+    case 1: return reinterpret_cast<const void*>(&fp::mfma_kernel<Q, MT16, 1, XLDS>);
+    case 2: return reinterpret_cast<const void*>(&fp::mfma_kernel<Q, MT16, 2, XLDS>);
+    case 4: return reinterpret_cast<const void*>(&fp::mfma_kernel<Q, MT16, 4, XLDS>);
     default: return nullptr;
   }
 }
 
-const void* mfma_fn(int mt16, int ktw) {
-  switch (mt16) {
-    case 1: return mfma_fn_ktw<1>(ktw);
-    case 2: return mfma_fn_ktw<2>(ktw);
-    case 4: return mfma_fn_ktw<4>(ktw);
-    case 8: return mfma_fn_ktw<8>(ktw);
-    case 16: return mfma_fn_ktw<16>(ktw);
+const void* mfma_fn(const Tiling& t) {
+  const int ktw = t.chunks;
+  if (t.groups == 8) return t.mt == 1 ? mfma_fn_ktw<8, 1, false>(ktw) : nullptr;
+  if (t.groups == 4) return t.mt == 1 ? mfma_fn_ktw<4, 1, false>(ktw) : nullptr;
+  if (t.groups == 2) return t.mt == 1 ? mfma_fn_ktw<2, 1, false>(ktw) : nullptr;
+  if (t.groups != 1) return nullptr;
+  if (mfma_xlds(t)) {
+    switch (t.mt) {
+      case 1: return mfma_fn_ktw<1, 1, true>(ktw);
+      case 2: return mfma_fn_ktw<1, 2, true>(ktw);
+      case 4: return mfma_fn_ktw<1, 4, true>(ktw);
+      case 8: return mfma_fn_ktw<1, 8, true>(ktw);
+      case 16: return mfma_fn_ktw<1, 16, true>(ktw);
+      default: return nullptr;
+    }
+  }
+  switch (t.mt) {
+    case 1: return mfma_fn_ktw<1, 1, false>(ktw);
+    case 2: return mfma_fn_ktw<1, 2, false>(ktw);
     default: return nullptr;
   }
 }
@@ -328,7 +417,7 @@ fp_status hip_fail(hipError_t e) {
 }
 
 fp_status launch(const void* fn, int64_t blocks, int threads, size_t lds,
-                 void* arg, hipStream_t stream) {
+                 void** args, hipStream_t stream) {
   if (fn == nullptr || blocks <= 0) return FP_ERR_UNSUPPORTED;
   if (lds > 64 * 1024) {
     std::lock_guard<std::mutex> lk(g_attr_mu);
@@ -341,54 +430,49 @@ fp_status launch(const void* fn, int64_t blocks, int threads, size_t lds,
   }
   // The launch's own return code is checked; hipGetLastError is not used
   // because it would also report (and clear) errors left by other code.
-  void* args[] = {arg};
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3((unsigned)threads),
                                  args, lds, stream);
   if (e != hipSuccess) return hip_fail(e);
   return FP_OK;
 }
 
-// One launch over the rows of `rs` with tiling t.
+// One launch over the rows of `rs` with tiling t.  The kernels take their
+// hot scalars as leading arguments (preloaded into SGPRs) and the row space
+// and workspace pointers in a trailing struct.
 fp_status run(const fp_plan_s* p, const Tiling& t, const fp::RowSpace& rs,
               const void* x, int64_t M, int64_t ldx, hipStream_t stream) {
+  const unsigned char* w_pre = rs.w;
+  const unsigned char* x_pre = static_cast<const unsigned char*>(x);
+  int64_t ldx_pre = ldx * p->esize;
+  int64_t n_rows_pre = rs.n_rows;
+  int32_t kc_pre = (int32_t)p->kc;
+  int32_t M_pre = (int32_t)M;
   float* partial = reinterpret_cast<float*>(p->ws + counters_bytes(p->n_total));
   uint32_t* counters = reinterpret_cast<uint32_t*>(p->ws);
   if (t.path == FP_PATH_MFMA) {
     fp::MfmaArgs a;
-    a.x = static_cast<const unsigned char*>(x);
-    a.ldx_bytes = ldx * p->esize;
-    a.row_bytes = p->K * p->esize;
-    a.M = (int32_t)M;
-    a.kc = (int32_t)p->kc;
-    a.GR = t.rows;
-    a.PK = t.kparts;
-    a.S = t.splits;
-    a.ktw = t.chunks;
     a.rs = rs;
     a.partial = partial;
     a.counters = counters;
-    const int64_t blocks = ceil_div(rs.n_rows, 16 * (int64_t)t.rows) * t.splits;
-    return launch(mfma_fn(t.mt, t.chunks), blocks, t.rows * t.kparts * 64, mfma_lds(t),
-                  &a, stream);
+    int32_t geo_pre = t.rows | (t.kparts << 8) | (t.chunks << 16);
+    int32_t S_pre = t.splits;
+    void* args[] = {&w_pre, &x_pre, &ldx_pre, &n_rows_pre, &kc_pre, &M_pre, &geo_pre, &S_pre, &a};
+    const int64_t rows_per_block = (16 / t.groups) * (int64_t)t.rows;
+    const int64_t blocks = ceil_div(rs.n_rows, rows_per_block) * t.splits;
+    return launch(mfma_fn(t), blocks, t.rows * t.kparts * 64, mfma_lds(t), args, stream);
   }
   fp::SkinnyArgs a;
-  a.x = static_cast<const unsigned char*>(x);
-  a.ldx_bytes = ldx * p->esize;
-  a.row_bytes = p->K * p->esize;
-  a.M = (int32_t)M;
-  a.kc = (int32_t)p->kc;
-  a.P = t.kparts;
-  a.G = t.groups;
-  a.S = t.splits;
-  a.cps = t.kparts * 64 * t.chunks;
-  a.R = t.groups * t.rows;
   a.rs = rs;
   a.partial = partial;
   a.counters = counters;
-  const int64_t blocks = ceil_div(rs.n_rows, (int64_t)a.R) * t.splits;
+  int32_t P_pre = t.kparts;
+  int32_t GS_pre = t.groups | (t.splits << 16);
+  void* args[] = {&w_pre, &x_pre, &ldx_pre, &n_rows_pre, &kc_pre, &M_pre, &P_pre, &GS_pre, &a};
+  const int64_t R = (int64_t)t.groups * t.rows;
+  const int64_t blocks = ceil_div(rs.n_rows, R) * t.splits;
   const void* fn = p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
                                        : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
-  return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), &a, stream);
+  return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {

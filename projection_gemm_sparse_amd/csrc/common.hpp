@@ -69,18 +69,8 @@ constexpr int skinny_max_threads(int mt, int rw, int cj) {
   return max_threads_for_regs(pow2ceil(rw * mt) + 4 * rw * cj + 4 * mt * cj + 32);
 }
 
-constexpr int mfma_max_threads(int mt16, int ktw) {
-  return max_threads_for_regs(16 * ktw + 4 * mt16 + 32);
-}
-
-// Segment holding launch row `row` (row < n_rows), or -1.
-__device__ __forceinline__ int find_seg(const RowSpace& rs, int64_t row) {
-  if (row < 0 || row >= rs.n_rows) return -1;
-#pragma unroll 1
-  for (int i = 0; i < rs.n_seg; ++i) {
-    if (row < rs.seg[i].row_begin + rs.seg[i].rows) return i;
-  }
-  return -1;
+constexpr int mfma_max_threads(int mt16, int ktw, bool xlds) {
+  return max_threads_for_regs(16 * ktw + 4 * mt16 + (xlds ? 8 : 16 * ktw * mt16) + 24);
 }
 
 __device__ __forceinline__ const unsigned char* row_pointer(
@@ -97,18 +87,65 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Stores output element (launch row `row`, token m) of the segment that
-// owns the row: y_i[m, row - row_begin] of the dense [M, rows] tensor.
+// Output segments of one workgroup.  A workgroup's rows span at most a few
+// segments; the two that hold its first rows are looked up once, early in
+// the kernel, so the kernel-argument reads are not on the epilogue's
+// critical path.  Rows in later segments (workgroups straddling several
+// tiny projections) fall back to a scan of the table.
+struct OutSegs {
+  unsigned char* y0;
+  int64_t b0, n0;
+  unsigned char* y1;
+  int64_t b1, n1;
+};
+
+__device__ __forceinline__ OutSegs find_out_segs(const RowSpace& rs, int64_t first_row) {
+  OutSegs o;
+  o.y0 = nullptr; o.b0 = 0; o.n0 = 0;
+  o.y1 = nullptr; o.b1 = 0; o.n1 = 0;
+  int i = 0;
+  while (i < rs.n_seg && first_row >= rs.seg[i].row_begin + rs.seg[i].rows) ++i;
+  if (i < rs.n_seg) {
+    o.y0 = rs.seg[i].y; o.b0 = rs.seg[i].row_begin; o.n0 = rs.seg[i].rows;
+  }
+  if (i + 1 < rs.n_seg) {
+    o.y1 = rs.seg[i + 1].y; o.b1 = rs.seg[i + 1].row_begin; o.n1 = rs.seg[i + 1].rows;
+  }
+  return o;
+}
+
+// Stores output element (launch row `row`, token m): y_i[m, row - row_begin]
+// of the dense [M, rows] tensor of the segment that holds the row.
 template <bool BF16>
-__device__ __forceinline__ void store_out(const RowSpace& rs, int64_t row,
-                                          int m, float v) {
-  const int i = find_seg(rs, row);
-  if (i < 0) return;
-  const int64_t idx = (int64_t)m * rs.seg[i].rows + (row - rs.seg[i].row_begin);
-  if constexpr (BF16) {
-    reinterpret_cast<uint16_t*>(rs.seg[i].y)[idx] = f32_to_bf16_rne(v);
+__device__ __forceinline__ void store_out(const RowSpace& rs, const OutSegs& os,
+                                          int64_t row, int m, float v) {
+  unsigned char* y = nullptr;
+  int64_t idx = 0;
+  if (row >= os.b0 && row < os.b0 + os.n0) {
+    y = os.y0;
+    idx = (int64_t)m * os.n0 + (row - os.b0);
+  } else if (row >= os.b1 && row < os.b1 + os.n1) {
+    y = os.y1;
+    idx = (int64_t)m * os.n1 + (row - os.b1);
   } else {
-    reinterpret_cast<float*>(rs.seg[i].y)[idx] = v;
+    for (int i = 0; i < rs.n_seg; ++i) {
+      const int64_t b = rs.seg[i].row_begin;
+      const int64_t n = rs.seg[i].rows;
+      if (row >= b && row < b + n) {
+        y = rs.seg[i].y;
+        idx = (int64_t)m * n + (row - b);
+      }
+    }
+  }
+  if (y == nullptr) return;
+  // agent-coherent (sc1) stores: the line is written through instead of
+  // left dirty in this XCD's L2, which shortens the end-of-kernel writeback
+  if constexpr (BF16) {
+    __hip_atomic_store(reinterpret_cast<uint16_t*>(y) + idx, f32_to_bf16_rne(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    __hip_atomic_store(reinterpret_cast<float*>(y) + idx, v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -234,42 +271,58 @@ __device__ __forceinline__ void transpose_reduce(float* v, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K finish inside the same launch.  Each of the S workgroups of row
-// block rb has written its fp32 partial sums to partial[s][row][m]; they
-// arrive on counters[rb].  The last to arrive adds the S partials of each
-// output in slice order s = 0, 1, ..., S-1, stores the result and resets the
-// counter to zero, so the next call (or graph replay) starts from zero
-// without any host action.  Release/acquire fences at agent scope make the
-// partials of every XCD visible to the finishing workgroup.
-// Must be called by every thread of the workgroup (it has barriers).
+// Split-K partial sums and their finish inside the same launch.
+//
+// Each of the S workgroups of row block rb writes its fp32 partial sums to
+// partial[s][row][m] with agent-coherent stores (sc1: written through to the
+// point of coherence shared by all XCDs instead of staying dirty in this
+// XCD's L2), waits until they are acknowledged, and then arrives on
+// counters[rb].  The workgroup that arrives last reads the S partials with
+// agent-coherent loads, adds them in slice order s = 0, 1, ..., S-1, stores
+// the outputs and resets the counter to zero, so the next call (or graph
+// replay) needs no host action.  Because every partial store and load is
+// agent-coherent, no L2 writeback or invalidation (what an agent-scope
+// fence would cost per workgroup) is needed.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_partial(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Must be called by every thread of the workgroup (it has barriers).
 template <bool BF16>
 __device__ __forceinline__ void splitk_finish(const RowSpace& rs,
                                               const float* partial,
                                               uint32_t* counters, int rb,
                                               int S, int64_t row_base,
                                               int64_t R, int M, int* flag) {
-  __threadfence();
+  // this thread's partial stores are complete (vmcnt = 0; expcnt and
+  // lgkmcnt left at their maximum) before the workgroup arrives
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = atomicAdd(counters + rb, 1u);
+    const unsigned old = __hip_atomic_fetch_add(counters + rb, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
     *flag = (old == (unsigned)(S - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (*flag == 0) return;
-  __threadfence();
   const int64_t n_rows = rs.n_rows;
   const int64_t rows_here = (n_rows - row_base) < R ? (n_rows - row_base) : R;
   const int64_t n_fin = rows_here * M;
   const int64_t sstride = n_rows * M;
+  const OutSegs os = find_out_segs(rs, row_base);
   for (int64_t t = threadIdx.x; t < n_fin; t += blockDim.x) {
     const int64_t rr = t / M;
     const int m = (int)(t - rr * M);
     const int64_t row = row_base + rr;
     const float* pp = partial + row * M + m;
-    float sum = pp[0];
-    for (int ss = 1; ss < S; ++ss) sum += pp[ss * sstride];
-    store_out<BF16>(rs, row, m, sum);
+    float sum = load_partial(pp);
+    for (int ss = 1; ss < S; ++ss) sum += load_partial(pp + ss * sstride);
+    store_out<BF16>(rs, os, row, m, sum);
   }
   if (threadIdx.x == 0) {
     __hip_atomic_store(counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -1,176 +1,270 @@
-// mfma.hpp -- MFMA tile kernel for y = x . W^T (bf16 in, fp32 accumulate),
-// used for token counts above the skinny kernel's range.
+// mfma.hpp -- MFMA tile kernel for y = x . W^T (bf16 in, fp32 accumulate).
 //
 // Instruction: v_mfma_f32_16x16x32_bf16, D[16 x 16] += A[16 x 32] . B[32 x 16].
-// A is a 16-row tile of the weight (rows = outputs), B is 16 token rows of x
-// seen as columns, D[i][j] is output row i for token j.  Lane l supplies A's
-// row l%16 and B's column l%16 with eight bf16 values of one k-slot group
-// g = l/16; the sum over the 32 k-slots is independent of which k a slot
-// carries as long as A and B carry the same k in the same slot.  Lane group
-// g of a 128-wide k tile therefore loads the 64 contiguous bytes at
-// k = 32g .. 32g+31 of its row (four 16-byte loads), and step t of the
-// tile feeds the t-th of them: each weight row is read as 256-byte runs, and
-// W_cat is used as stored (plain row-major, no pre-swizzled copy, so writes
-// through the projection views stay valid).
-// D layout: lane l holds D[4*(l/16) + v][l%16], v = 0..3.
+// Lane l supplies A's row l%16 and B's column l%16 with eight bf16 values of
+// k-slot group g = l/16; the product sums over the 32 k-slots, so any k may
+// sit in a slot as long as A and B carry the same k there.  D layout: lane l
+// holds D[4*(l/16) + v][l%16], v = 0..3.
 //
-// Work split.  A workgroup owns 16 * GR rows (GR row groups of one 16-row
-// tile) and one of S slices of K; the PK waves of a row group split the
-// slice into PK parts of KTW consecutive 128-wide k tiles.  All of a wave's
-// weight loads are issued up front.  The activation tile of the slice
-// (all token rows, zero-padded to 16 * MT16) is staged once per workgroup
-// in LDS and shared by every wave.
-// Reduction order: MFMA k-steps in tile order inside a wave, then the PK
-// waves in wave order (LDS), then the S slices in slice order (the
-// last-arriving workgroup, as in the skinny kernel).  It depends only on
-// (K, KTW, PK, S), never on the rows of a launch.
+// K-slice packing.  With few tokens the 16 MFMA columns are mostly idle, so
+// the 16 A rows are filled with RT = 16/Q weight rows times Q sub-slices of
+// the wave's K range, and the 16 B columns with TQ = 16/Q tokens times the
+// same Q sub-slices: A row s*RT + r carries weight row r on sub-slice s, B
+// column s*TQ + m carries token m on sub-slice s.  The useful outputs are
+// the diagonal blocks D[s*RT + r][s*TQ + m]; adding them over s gives row r,
+// token m.  Q = 1 is the ordinary 16-row tile (and may hold several
+// 16-token tiles, MT16 of them); Q = 2, 4, 8 give 8-, 4- and 2-row tiles for
+// up to 8, 4 and 2 tokens, so a launch has enough workgroups without
+// splitting K across workgroups.
+//
+// Loads.  The sub-slices are interleaved at 16-byte granularity: at MFMA
+// step t of k tile kk, the lane of k-slot group g on sub-slice s reads chunk
+//   kk*16Q + 4Q*t + Q*g + s
+// of the wave's range, so the 4Q lanes that carry one weight row read 64Q
+// contiguous bytes per load instruction (256 B at Q = 4).  W_cat is used as
+// stored (no pre-swizzled copy, so writes through the projection views stay
+// valid).  Every weight load of a wave is issued before its first MFMA.
+// Activations come straight from global memory (they are small and stay in
+// L2) unless several row groups of a workgroup share them (large token
+// counts): then the workgroup stages its activation slice in LDS once,
+// issuing all of a thread's staging loads before its first LDS store.
+//
+// Work split.  A workgroup owns GR row groups of RT rows and one of S
+// slices of K; the PK waves of a row group split the slice into PK parts of
+// KTW k tiles of 16Q chunks each.
+// Reduction order: MFMA steps in tile order inside a wave; then, per output,
+// the Q sub-slices and PK waves in a fixed order (sub-slice outer, wave
+// inner) through LDS; then the S slices in slice order (last-arriving
+// workgroup, see splitk_finish).  It depends only on (K, Q, KTW, PK, S).
 #pragma once
 
 #include "common.hpp"
 
 namespace fp {
 
+// Scalar arguments (leading, preloaded into SGPRs at wave launch): w_pre =
+// rs.w, x_pre = activations (M_pre rows, row stride ldx_pre bytes),
+// n_rows_pre = rs.n_rows, kc_pre = 16-byte chunks per row, geo_pre = GR |
+// PK << 8 | ktw << 16 (row groups per workgroup, waves per row group, k
+// tiles per wave), S_pre = K slices across workgroups.
 struct MfmaArgs {
-  const unsigned char* x;  // activations, M rows
-  int64_t ldx_bytes;       // row stride of x in bytes (multiple of 16)
-  int64_t row_bytes;       // K * 2
-  int32_t M;               // token rows, <= 16 * MT16
-  int32_t kc;              // 16-byte chunks per row (8 bf16 each)
-  int32_t GR;              // 16-row groups per workgroup
-  int32_t PK;              // waves per row group (K parts of a slice)
-  int32_t S;               // K slices
-  int32_t ktw;             // 128-wide k tiles per wave (<= KTW)
   RowSpace rs;
   float* partial;          // [S][n_rows][M] when S > 1
   uint32_t* counters;
 };
 
-template <int MT16, int KTW>
-__global__ void __launch_bounds__(mfma_max_threads(MT16, KTW))
-mfma_kernel(const MfmaArgs a) {
+template <int Q, int MT16, int KTW, bool XLDS>
+__global__ void __launch_bounds__(mfma_max_threads(MT16, KTW, XLDS))
+mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __restrict__ x_pre,
+            int64_t ldx_pre, int64_t n_rows_pre, int32_t kc_pre, int32_t M_pre,
+            int32_t geo_pre, int32_t S_pre, const MfmaArgs a) {
+  constexpr int RT = 16 / Q;  // weight rows per row group
+  constexpr int TQ = 16 / Q;  // tokens per sub-slice
+  constexpr int MC = Q == 1 ? 16 : TQ;  // token columns kept per tile
+  constexpr int TILE = RT * MC;         // useful outputs of one sub-slice tile
+  static_assert(Q == 1 || MT16 == 1, "k-slice packing uses one token tile");
+  static_assert(!XLDS || Q == 1, "staged activations only for unpacked tiles");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pk = wave % a.PK;
-  const int gr = wave / a.PK;
-  const int rb = blockIdx.x / a.S;
-  const int s = blockIdx.x - rb * a.S;
-  const int64_t R = 16 * (int64_t)a.GR;
+  const int GRv = geo_pre & 0xff;
+  const int PKv = (geo_pre >> 8) & 0xff;
+  const int ktw = geo_pre >> 16;
+  const int Sv = S_pre;
+  const int Mv = M_pre;
+  const int kc = kc_pre;
+  const int pk = GRv == 1 ? wave : wave % PKv;
+  const int gr = GRv == 1 ? 0 : wave / PKv;
+  const int rb = Sv == 1 ? (int)blockIdx.x : (int)blockIdx.x / Sv;
+  const int s = Sv == 1 ? 0 : (int)blockIdx.x - rb * Sv;
+  const int64_t R = (int64_t)RT * GRv;
   const int64_t row_base = (int64_t)rb * R;
-  const int64_t row0 = row_base + 16 * (int64_t)gr;
+  const int64_t row0 = row_base + (int64_t)RT * gr;
   const int i16 = lane & 15;
   const int g = lane >> 4;
-  const int slice_tiles = a.PK * a.ktw;            // k tiles per slice
-  const int kt_slice0 = s * slice_tiles;           // first tile of the slice
-  const int kt_wave0 = kt_slice0 + pk * a.ktw;     // first tile of the wave
+  const int wave_chunks = 16 * Q * ktw;             // chunks of a wave
+  const int slice_chunks = PKv * wave_chunks;       // chunks of a K slice
+  const int cw0 = s * slice_chunks + pk * wave_chunks;
 
-  // 1. weight loads of the wave: row row0 + i16, tiles kt_wave0 .. +ktw
+  // A lane: weight row (i16 % RT) on sub-slice (i16 / RT)
+  const int a_sub = i16 / RT;
+  const int a_row = i16 - a_sub * RT;
+  // B lane: token (i16 % TQ) on sub-slice (i16 / TQ)
+  const int b_sub = i16 / TQ;
+  const int b_tok = i16 - b_sub * TQ;
+
+  // Weight loads of the wave, all issued before the first MFMA.
   u32x4 wv[KTW][4];
-  {
-    const unsigned char* wrow = row_pointer(a.rs, row0 + i16, a.row_bytes);
+  // Loads are branch-free: out-of-range elements load a clamped valid
+  // address (rows past the end are computed and dropped), and weight chunks
+  // past K or past the wave's tiles are replaced by zero only when consumed,
+  // so the loads form one straight-line sequence consumed in issue order.
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  auto w_chunk = [&](int kk, int t) { return cw0 + kk * 16 * Q + 4 * Q * t + Q * g + a_sub; };
+  auto load_weights = [&]() {
+    const int64_t n_rows_l = n_rows_pre;
+    const int64_t row = row0 + a_row;
+    const u32x4* wrow = reinterpret_cast<const u32x4*>(
+        w_pre + (row < n_rows_l ? row : n_rows_l - 1) * ((int64_t)kc * 16));
 #pragma unroll
     for (int kk = 0; kk < KTW; ++kk) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int c = (kt_wave0 + kk) * 16 + 4 * g + t;
-        if (wrow != nullptr && kk < a.ktw && c < a.kc) {
-          wv[kk][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow) + c);
-        } else {
-          wv[kk][t] = u32x4{0u, 0u, 0u, 0u};
+        const int c = w_chunk(kk, t);
+        wv[kk][t] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  OutSegs os;
+
+  // 1. activations and weights.  Read per wave, the activations (from L2)
+  //    are loaded first so the weights can be consumed as they land; staged
+  //    in LDS, the weight loads go first so they are in flight while the
+  //    workgroup stages its activation slice.
+  u32x4 xv[XLDS ? 1 : MT16][XLDS ? 1 : KTW][4];
+  const int pitch = slice_chunks + 1;  // LDS row pitch in 16-byte units
+  if constexpr (!XLDS) {
+#pragma unroll
+    for (int mt = 0; mt < MT16; ++mt) {
+      const int m = mt * 16 + (Q == 1 ? i16 : b_tok);
+      const int mc = m < Mv ? m : Mv - 1;
+      const u32x4* xrow = reinterpret_cast<const u32x4*>(x_pre + (int64_t)mc * ldx_pre);
+#pragma unroll
+      for (int kk = 0; kk < KTW; ++kk) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int c = cw0 + kk * 16 * Q + 4 * Q * t + Q * g + b_sub;
+          xv[mt][kk][t] = xrow[c < kc ? c : kc - 1];
         }
       }
     }
-  }
-
-  // 2. stage the slice's activation tile: rows 0 .. 16*MT16-1 (zero past M),
-  //    chunks [kt_slice0*16, (kt_slice0 + slice_tiles)*16), row pitch padded
-  //    by 16 bytes to spread LDS banks.
-  const int slice_chunks = slice_tiles * 16;
-  const int pitch = slice_chunks + 1;  // in 16-byte units
-  u32x4* xs = reinterpret_cast<u32x4*>(lds);
-  {
+    load_weights();
+    os = find_out_segs(a.rs, row_base);  // while the loads are in flight
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    load_weights();
+    os = find_out_segs(a.rs, row_base);
+    __builtin_amdgcn_sched_barrier(0);
+    // rows 0 .. 16*MT16-1 (zero past M) of the slice's chunks; each thread
+    // loads up to 8 chunks into registers before storing any of them
+    u32x4* xs = reinterpret_cast<u32x4*>(lds);
     const int total = 16 * MT16 * slice_chunks;
-    for (int e = tid; e < total; e += blockDim.x) {
-      const int m = e / slice_chunks;
-      const int cc = e - m * slice_chunks;
-      const int c = kt_slice0 * 16 + cc;
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (m < a.M && c < a.kc) {
-        val = reinterpret_cast<const u32x4*>(a.x + (int64_t)m * a.ldx_bytes)[c];
+    for (int base = 0; base < total; base += 8 * (int)blockDim.x) {
+      u32x4 st[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int idx = base + e * (int)blockDim.x + tid;
+        st[e] = u32x4{0u, 0u, 0u, 0u};
+        if (idx < total) {
+          const int m = idx / slice_chunks;
+          const int cc = idx - m * slice_chunks;
+          const int c = s * slice_chunks + cc;
+          if (m < Mv && c < kc) {
+            st[e] = reinterpret_cast<const u32x4*>(x_pre + (int64_t)m * ldx_pre)[c];
+          }
+        }
       }
-      xs[m * pitch + cc] = val;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int idx = base + e * (int)blockDim.x + tid;
+        if (idx < total) {
+          const int m = idx / slice_chunks;
+          const int cc = idx - m * slice_chunks;
+          xs[m * pitch + cc] = st[e];
+        }
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
-  // 3. MFMA over the wave's tiles
+  // 2. MFMA steps in tile order
   f32x4 acc[MT16];
 #pragma unroll
   for (int mt = 0; mt < MT16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < KTW; ++kk) {
-    if (kk < a.ktw) {
-      const int cc0 = (pk * a.ktw + kk) * 16 + 4 * g;
+    if (kk < ktw) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const bf16x8 A = u4bf8(wv[kk][t]);
+        // consume the weight loads in issue order (progressive vmcnt waits)
+        __builtin_amdgcn_sched_barrier(0);
+        const bool a_ok = w_chunk(kk, t) < kc;
+        const bf16x8 A = u4bf8(a_ok ? wv[kk][t] : zero4);
 #pragma unroll
         for (int mt = 0; mt < MT16; ++mt) {
-          const bf16x8 B = u4bf8(xs[(mt * 16 + i16) * pitch + cc0 + t]);
+          bf16x8 B;
+          if constexpr (XLDS) {
+            const u32x4* xs = reinterpret_cast<const u32x4*>(lds);
+            const int cc = pk * wave_chunks + kk * 16 + 4 * t + g;
+            B = u4bf8(xs[(mt * 16 + i16) * pitch + cc]);
+          } else {
+            const int m = mt * 16 + (Q == 1 ? i16 : b_tok);
+            const int c = cw0 + kk * 16 * Q + 4 * Q * t + Q * g + b_sub;
+            B = u4bf8((m < Mv && c < kc) ? xv[mt][kk][t] : zero4);
+          }
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[mt], 0, 0, 0);
         }
       }
     }
   }
 
-  // 4. across the PK waves of the row group (LDS, wave order), then store
-  //    or write the slice's partial sums.
-  const int64_t n_rows = a.rs.n_rows;
-  float* red = reinterpret_cast<float*>(lds + (size_t)16 * MT16 * pitch * 16);
-  if (a.PK > 1) {
-    __syncthreads();  // LDS activation tile no longer read after this point
+  // 3. useful outputs to LDS: red[((gr*PK + pk)*Q + sub)*MT16 + mt][r][m];
+  //    it reuses the staged activations' space once every wave is done
+  //    with them
+  if constexpr (XLDS) __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
-    for (int mt = 0; mt < MT16; ++mt) {
+  for (int mt = 0; mt < MT16; ++mt) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        red[(((gr * a.PK + pk) * MT16 + mt) * 4 + v) * 64 + lane] = acc[mt][v];
-      }
-    }
-    __syncthreads();
-    const int n_el = a.GR * MT16 * 256;
-    for (int e = tid; e < n_el; e += blockDim.x) {
-      const int ln = e & 63;
-      const int v = (e >> 6) & 3;
-      const int mt = (e >> 8) % MT16;
-      const int g2 = (e >> 8) / MT16;
-      const float* rp = red + ((g2 * a.PK * MT16 + mt) * 4 + v) * 64 + ln;
-      float sum = rp[0];
-      for (int q = 1; q < a.PK; ++q) sum += rp[q * MT16 * 256];
-      const int64_t row = row_base + 16 * (int64_t)g2 + 4 * (ln >> 4) + v;
-      const int m = mt * 16 + (ln & 15);
-      if (m < a.M && row < n_rows) {
-        if (a.S == 1) store_out<true>(a.rs, row, m, sum);
-        else a.partial[((int64_t)s * n_rows + row) * a.M + m] = sum;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < MT16; ++mt) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t row = row0 + 4 * g + v;
-        const int m = mt * 16 + i16;
-        if (m < a.M && row < n_rows) {
-          if (a.S == 1) store_out<true>(a.rs, row, m, acc[mt][v]);
-          else a.partial[((int64_t)s * n_rows + row) * a.M + m] = acc[mt][v];
-        }
+    for (int v = 0; v < 4; ++v) {
+      const int arow = 4 * g + v;  // D row
+      const int sa = arow / RT;
+      const int sb = i16 / TQ;     // D column i16
+      if (Q == 1 || sa == sb) {
+        const int r = arow - sa * RT;
+        const int m = i16 - sb * TQ;
+        const int slot = ((gr * PKv + pk) * Q + sa) * MT16 + mt;
+        red[slot * TILE + r * MC + m] = acc[mt][v];
       }
     }
   }
-  if (a.S == 1) return;
-  int* flag = reinterpret_cast<int*>(red + (a.PK > 1 ? a.GR * a.PK * MT16 * 256 : 0));
-  splitk_finish<true>(a.rs, a.partial, a.counters, rb, a.S, row_base, R, a.M, flag);
+  __syncthreads();
+
+  // 4. per output: sub-slices, then waves, in fixed order; store or write
+  //    the slice's partial sum
+  const int64_t n_rows = n_rows_pre;
+  const int mcols = MC * MT16;
+  const int n_out = GRv * RT * mcols;
+  for (int o = tid; o < n_out; o += blockDim.x) {
+    const int g2 = o / (RT * mcols);
+    const int rem = o - g2 * (RT * mcols);
+    const int r = rem / mcols;
+    const int mm = rem - r * mcols;
+    const int mt = mm / MC;
+    const int m16 = mm - mt * MC;
+    const int64_t row = row_base + (int64_t)RT * g2 + r;
+    if (mm >= Mv || row >= n_rows) continue;
+    float sum = 0.0f;
+#pragma unroll
+    for (int sub = 0; sub < Q; ++sub) {
+      for (int q = 0; q < PKv; ++q) {
+        const int slot = ((g2 * PKv + q) * Q + sub) * MT16 + mt;
+        const float val = red[slot * TILE + r * MC + m16];
+        sum = (sub == 0 && q == 0) ? val : sum + val;
+      }
+    }
+    if (Sv == 1) {
+      store_out<true>(a.rs, os, row, mm, sum);
+    } else {
+      store_partial(a.partial + ((int64_t)s * n_rows + row) * Mv + mm, sum);
+    }
+  }
+  if (Sv == 1) return;
+  int* flag = reinterpret_cast<int*>(red + (size_t)GRv * PKv * Q * MT16 * TILE);
+  splitk_finish<true>(a.rs, a.partial, a.counters, rb, Sv, row_base, R, Mv, flag);
 }
 
 }  // namespace fp

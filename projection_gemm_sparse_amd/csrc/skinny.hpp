@@ -15,7 +15,8 @@
 //
 // Activations.  Lane l needs x[m, chunk] only for its own chunks; each of
 // them is used by the RW rows of the lane, so x is held in registers (no
-// element of x is needed twice by one row group).
+// element of x is needed twice by one row group).  They are loaded before
+// the weights, so the rows can be multiplied as their loads land.
 //
 // Reduction, in a fixed order that depends only on (K, dtype, P, CJ, S):
 //   1. in each lane, sequentially over its CJ chunks and, inside a chunk,
@@ -38,25 +39,27 @@
 
 namespace fp {
 
+// Scalar arguments (leading, preloaded): w_pre = rs.w, x_pre = activations
+// (M_pre rows, row stride ldx_pre bytes), n_rows_pre = rs.n_rows, kc_pre =
+// 16-byte chunks per row (K * element size / 16), P_pre = waves per row
+// group (K parts of a slice), GS_pre = G | S << 16 (row groups per
+// workgroup, K slices).  A K slice holds P * 64 * CJ chunks; a workgroup
+// owns G * RW rows.
 struct SkinnyArgs {
-  const unsigned char* x;  // activations, M rows
-  int64_t ldx_bytes;       // row stride of x in bytes (multiple of 16)
-  int64_t row_bytes;       // K * element size (multiple of 16)
-  int32_t M;               // token rows, <= MT
-  int32_t kc;              // 16-byte chunks per row
-  int32_t P;               // waves per row group (K parts of a slice)
-  int32_t G;               // row groups per workgroup
-  int32_t S;               // K slices (workgroups per row block)
-  int32_t cps;             // chunks per slice = P * 64 * CJ
-  int32_t R;               // rows per workgroup = G * RW
-  RowSpace rs;             // rows of this launch
+  RowSpace rs;             // rows of this launch and their output segments
   float* partial;          // [S][n_rows][M] when S > 1
   uint32_t* counters;      // one per row block when S > 1, zero between calls
 };
 
+// The fields the kernel needs before its first load are also passed as
+// leading scalar arguments, which the library build preloads into SGPRs at
+// wave launch (-amdgpu-kernarg-preload-count): the loads can issue without
+// waiting for kernel-argument memory reads.
 template <int MT, int RW, int CJ, bool BF16>
 __global__ void __launch_bounds__(skinny_max_threads(MT, RW, CJ))
-skinny_kernel(const SkinnyArgs a) {
+skinny_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __restrict__ x_pre,
+              int64_t ldx_pre, int64_t n_rows_pre, int32_t kc_pre, int32_t M_pre,
+              int32_t P_pre, int32_t GS_pre, const SkinnyArgs a) {
   constexpr int V = RW * MT;        // outputs per lane
   constexpr int VP = pow2ceil(V);   // padded to a power of two
   constexpr int QV = VP >= 64 ? VP / 64 : 1;
@@ -67,60 +70,111 @@ skinny_kernel(const SkinnyArgs a) {
   const int lane = tid & 63;
   // wave index made scalar so that row and slice arithmetic stays in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int p = wave % a.P;
-  const int gq = wave / a.P;
-  const int rb = blockIdx.x / a.S;
-  const int s = blockIdx.x - rb * a.S;
-  const int64_t row_base = (int64_t)rb * a.R;
+  // GS_pre = G | S << 16; the common single-group, unsplit case (GS = 1 | 1
+  // << 16) avoids the integer divisions
+  const int Gv = GS_pre & 0xffff;
+  const int Sv = GS_pre >> 16;
+  const bool simple = GS_pre == (1 | (1 << 16));
+  const int p = simple ? wave : wave % P_pre;
+  const int gq = simple ? 0 : wave / P_pre;
+  const int rb = simple ? (int)blockIdx.x : (int)blockIdx.x / Sv;
+  const int s = simple ? 0 : (int)blockIdx.x - rb * Sv;
+  const int64_t row_base = (int64_t)rb * (Gv * RW);
   const int64_t wrow0 = row_base + (int64_t)gq * RW;
-  const int cbase = s * a.cps + p * (64 * CJ) + lane;
+  const int cbase = s * (P_pre * 64 * CJ) + p * (64 * CJ) + lane;
 
-  // 1. weight stream: every load of the lane issued up front
-  u32x4 wv[RW][CJ];
+  // Loads are branch-free: an out-of-range chunk or row loads a clamped,
+  // always-valid address, and out-of-range chunks are replaced by zero only
+  // when they are consumed (rows past the end are computed and dropped).  The
+  // loads thus form one straight-line sequence, and each row can be consumed
+  // as soon as its own loads have landed.
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  const int64_t n_rows_l = n_rows_pre;
+  const int kc = kc_pre;
+  const int Mv = M_pre;
+  bool c_ok[CJ];
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const unsigned char* wrow = row_pointer(a.rs, wrow0 + r, a.row_bytes);
-#pragma unroll
-    for (int j = 0; j < CJ; ++j) {
-      const int c = cbase + j * 64;
-      if (wrow != nullptr && c < a.kc) {
-        wv[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow) + c);
-      } else {
-        wv[r][j] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  // 2. the lane's activation chunks
+  for (int j = 0; j < CJ; ++j) c_ok[j] = cbase + j * 64 < kc;
+
+  // 1. the lane's activation chunks first: they come from L2/MALL and are
+  //    needed by every row, so loading them ahead of the weights keeps them
+  //    off the tail of the weight stream
   u32x4 xv[MT][CJ];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
+    const int mc = m < Mv ? m : Mv - 1;
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(x_pre + (int64_t)mc * ldx_pre);
 #pragma unroll
     for (int j = 0; j < CJ; ++j) {
       const int c = cbase + j * 64;
-      if (m < a.M && c < a.kc) {
-        xv[m][j] = reinterpret_cast<const u32x4*>(a.x + (int64_t)m * a.ldx_bytes)[c];
-      } else {
-        xv[m][j] = u32x4{0u, 0u, 0u, 0u};
-      }
+      xv[m][j] = xrow[c < kc ? c : kc - 1];
     }
   }
-  // 3. per-lane partial sums, chunk by chunk
+  // 2. weight stream: every load of the lane issued up front, row by row
+  u32x4 wv[RW][CJ];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t row = wrow0 + r;
+    const u32x4* wrow = reinterpret_cast<const u32x4*>(
+        w_pre + (row < n_rows_l ? row : n_rows_l - 1) * ((int64_t)kc * 16));
+#pragma unroll
+    for (int j = 0; j < CJ; ++j) {
+      const int c = cbase + j * 64;
+      wv[r][j] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // output segments of this workgroup, looked up while the loads are in
+  // flight
+  const OutSegs os = find_out_segs(a.rs, row_base);
+  __builtin_amdgcn_sched_barrier(0);
+  // activations past M or past K count as zero
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int j = 0; j < CJ; ++j) xv[m][j] = (m < Mv && c_ok[j]) ? xv[m][j] : zero4;
+  }
+
+  // 3. per-lane partial sums in load order (row by row), so each row is
+  //    consumed as soon as its loads have landed; each output still adds its
+  //    chunks in order j = 0 .. CJ-1
   float v[VP];
 #pragma unroll
   for (int i = 0; i < VP; ++i) v[i] = 0.0f;
 #pragma unroll
-  for (int j = 0; j < CJ; ++j) {
+  for (int r = 0; r < RW; ++r) {
+    // keep the rows in load order: the compiler then waits only for the
+    // loads of row r (vmcnt counts loads in issue order)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
+    for (int j = 0; j < CJ; ++j) {
+      const u32x4 w = c_ok[j] ? wv[r][j] : zero4;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        v[r * MT + m] = dot_chunk<BF16>(wv[r][j], xv[m][j], v[r * MT + m]);
+        v[r * MT + m] = dot_chunk<BF16>(w, xv[m][j], v[r * MT + m]);
       }
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+
   // 4. across the wave
   transpose_reduce<VP>(v, lane);
-  float* red = smem + (gq * a.P + p) * VP;
+  if (P_pre == 1 && Sv == 1) {
+    // the wave holds whole rows: its lanes store the finished sums, no
+    // workgroup barrier
+    if (lane % LSTRIDE == 0) {
+#pragma unroll
+      for (int q = 0; q < QV; ++q) {
+        const int idx = q + QV * (lane / LSTRIDE);
+        const int r = idx / MT;
+        const int m = idx - r * MT;
+        const int64_t row = wrow0 + r;
+        if (idx < V && m < Mv && row < n_rows_l) store_out<BF16>(a.rs, os, row, m, v[q]);
+      }
+    }
+    return;
+  }
+  float* red = smem + (gq * P_pre + p) * VP;
   if (lane % LSTRIDE == 0) {
 #pragma unroll
     for (int q = 0; q < QV; ++q) red[q + QV * (lane / LSTRIDE)] = v[q];
@@ -128,29 +182,36 @@ skinny_kernel(const SkinnyArgs a) {
   __syncthreads();
 
   // 5. across the P waves of each row group, in wave order
-  const int64_t n_rows = a.rs.n_rows;
-  const int n_out = a.G * V;
+  const int64_t n_rows = n_rows_l;
+  const int n_out = Gv * V;
   for (int t = tid; t < n_out; t += blockDim.x) {
     const int g2 = t / V;
     const int idx = t - g2 * V;
     const int r = idx / MT;
     const int m = idx - r * MT;
     const int64_t row = row_base + (int64_t)g2 * RW + r;
-    if (m >= a.M || row >= n_rows) continue;
-    const float* rp = smem + g2 * a.P * VP + idx;
-    float sum = rp[0];
-    for (int pp = 1; pp < a.P; ++pp) sum += rp[pp * VP];
-    if (a.S == 1) {
-      store_out<BF16>(a.rs, row, m, sum);
+    if (m >= Mv || row >= n_rows) continue;
+    // all P wave sums read at once (P <= 16), then added in wave order
+    const float* rp = smem + g2 * P_pre * VP + idx;
+    float w[16];
+#pragma unroll
+    for (int pp = 0; pp < 16; ++pp) w[pp] = pp < P_pre ? rp[pp * VP] : 0.0f;
+    float sum = w[0];
+#pragma unroll
+    for (int pp = 1; pp < 16; ++pp) {
+      if (pp < P_pre) sum += w[pp];
+    }
+    if (Sv == 1) {
+      store_out<BF16>(a.rs, os, row, m, sum);
     } else {
-      a.partial[((int64_t)s * n_rows + row) * a.M + m] = sum;
+      store_partial(a.partial + ((int64_t)s * n_rows + row) * Mv + m, sum);
     }
   }
-  if (a.S == 1) return;
+  if (Sv == 1) return;
 
   // 6. split-K: the last workgroup of the row block adds the S partials
-  splitk_finish<BF16>(a.rs, a.partial, a.counters, rb, a.S, row_base, a.R, a.M,
-                      reinterpret_cast<int*>(smem + a.G * a.P * VP));
+  splitk_finish<BF16>(a.rs, a.partial, a.counters, rb, Sv, row_base, (int64_t)Gv * RW, Mv,
+                      reinterpret_cast<int*>(smem + Gv * P_pre * VP));
 }
 
 }  // namespace fp

@@ -53,8 +53,13 @@ def test_workspace_bytes_values():
     assert ws128 > ws1  # MFMA split-K partials for large M
     wsf = P.fp_workspace_bytes(1, 7168, [128, 64], 8)
     st, t = P.fp_default_tiling(1, 7168, 192, 8, 192)
-    assert st == 0 and t[3] > 1  # fp32 indexer shape splits K
-    assert wsf >= 256 + t[3] * 192 * 8 * 4
+    # the fp32 indexer rows fit one workgroup each: no K split by default
+    assert st == 0 and t[3] == 1 and t[1] * 64 * t[2] >= 7168 * 4 // 16
+    assert wsf >= 256
+    # a K longer than one workgroup covers (16 waves x 64 lanes x 2 chunks)
+    st, t = P.fp_default_tiling(0, 32768, 300, 2, 300)
+    assert st == 0 and t[3] == 2
+    assert P.fp_workspace_bytes(0, 32768, [300], 8) >= 512 + 2 * 300 * 8 * 4
 
 
 def _create(dtype=0, K=5120, N=(1280, 512), w_cat=FAKE, ws=FAKE, ws_bytes=None, max_M=8):

@@ -63,15 +63,20 @@ def test_wq_a_wkv_m2_8(M, seed):
     _check_case(fp, x, ws, "wq_a+wkv M=%d seed=%d" % (M, seed))
 
 
-# ---- fp32 indexer fusion, split-K (K=7168, [128, 64])
+# ---- fp32 indexer fusion (K=7168, [128, 64]): the default tiling (each
+#      row in one workgroup) and forced K splits across workgroups
 @pytest.mark.parametrize("M", [1, 4, 8])
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
-def test_indexer_fp32_splitk(M, seed):
+@pytest.mark.parametrize("tiling", [None, (P.FP_PATH_SKINNY_SPLITK, 7, 1, 4, 0, 0),
+                                    (P.FP_PATH_SKINNY_SPLITK, 2, 2, 7, 1, 3)],
+                         ids=["default", "split4", "split7"])
+def test_indexer_fp32(M, seed, tiling):
     x, ws = si.workload_case("indexer_f32", M, seed)
-    fp = _plan(ws)
-    path, _, _ = fp.query(M)
-    assert path == P.FP_PATH_SKINNY_SPLITK
-    _check_case(fp, x, ws, "indexer fp32 M=%d seed=%d" % (M, seed))
+    fp = _plan(ws, workspace_bytes=1 << 20)
+    if tiling is not None:
+        assert fp.set_tiling(M, tiling) == P.FP_OK
+        assert fp.query(M)[0] == P.FP_PATH_SKINNY_SPLITK
+    _check_case(fp, x, ws, "indexer fp32 M=%d seed=%d tiling=%s" % (M, seed, tiling))
 
 
 # ---- three-way fused-A (K=6144, [2048, 576, 128]), M 1..8
@@ -160,16 +165,28 @@ def test_tilings_all_pass(M):
         (P.FP_PATH_SKINNY, 2, 1, 5, 1, 0),
         (P.FP_PATH_SKINNY, 4, 2, 2, 0, 2),
         (P.FP_PATH_SKINNY, 10, 1, 1, 1, 1),
+        (P.FP_PATH_SKINNY, 1, 10, 1, 1, 7),  # whole rows per wave, no barrier
+        (P.FP_PATH_SKINNY, 1, 10, 1, 2, 3),
+        (P.FP_PATH_SKINNY, 2, 5, 1, 1, 5),
         (P.FP_PATH_MFMA, 4, 2, 5, 1, 0),
         (P.FP_PATH_MFMA, 1, 4, 10, 4, 0),
         (P.FP_PATH_MFMA, 2, 1, 20, 2, 0),
         (P.FP_PATH_MFMA, 8, 1, 5, 1, 0),
+        (P.FP_PATH_MFMA, 10, 4, 1, 1, 1),   # whole K in one workgroup
+        (P.FP_PATH_MFMA, 10, 2, 1, 1, 2),   # 8-row tiles, 2 K sub-slices
+        (P.FP_PATH_MFMA, 5, 2, 1, 2, 4),    # 4-row tiles, 4 K sub-slices
+        (P.FP_PATH_MFMA, 5, 1, 2, 1, 4),    # with a K split
+        (P.FP_PATH_MFMA, 4, 2, 3, 2, 2),    # uneven K coverage
     ]
     ran = 0
     for t in tilings:
         st = fp.set_tiling(M, t)
         if st != P.FP_OK:
-            assert st == P.FP_ERR_UNSUPPORTED and t[0] != P.FP_PATH_MFMA and M > 8, (t, st)
+            # skinny tilings above M = 8 and packed MFMA tiles above 16/Q
+            # tokens are refused
+            assert st == P.FP_ERR_UNSUPPORTED, (t, st)
+            assert ((t[0] != P.FP_PATH_MFMA and (M > 8 or (t[2] > 2 and M > 2)))
+                    or (t[5] > 1 and M > 16 // t[5])), (t, st)
             continue
         ran += 1
         ys = fp(xg)
