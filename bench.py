@@ -128,6 +128,8 @@ def main():
                     help="total size of the rotated weight pool (>= 1024 for past-MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--details", default="", help="write per-M details JSON here")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -166,6 +168,12 @@ def main():
                 p.forward_separate(xs[M], out=outs[M])
         return run
 
+    # per-launch floor of this stack: a graph of tiny one-block kernels
+    tiny = torch.zeros(64, device=dev)
+    floor_graph = capture(torch, lambda: [tiny.add_(1.0) for _ in range(n_copies)])
+    floor_ms, _ = time_graphs(torch, [floor_graph], max(3, args.steps // 4), 1)
+    floor_us = floor_ms * 1e3 / (max(3, args.steps // 4) * n_copies)
+
     fused_graphs = [capture(torch, fused_calls(M)) for M in MS]
     print("bench: graphs captured", file=sys.stderr, flush=True)
     total_ms, per_ms = time_graphs(torch, fused_graphs, args.steps, args.warmup)
@@ -190,6 +198,13 @@ def main():
         }
     ms_per_step = total_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     # sanity check of one call against a plain PyTorch fp32 product (outside
     # the timed region)
@@ -234,6 +249,13 @@ def main():
         },
         "us_per_call": {"mean_M1_8": round(sum(us_all) / len(us_all), 4),
                         "M1": per_m["1"]["fused_us"], "M8": per_m["8"]["fused_us"]},
+        "launch_floor_us": round(floor_us, 4),
+        "kernel_only_estimate": {
+            "note": "per-call time minus the per-launch floor of a graph of tiny kernels",
+            "us_M1": round(per_m["1"]["fused_us"] - floor_us, 4),
+            "GBps_M1_8": round(step_bytes / ((ms_per_step * 1e-3) / 1.0 -
+                                             floor_us * 1e-6 * n_copies * len(MS)) / 1e9, 1),
+        },
         "roofline": {
             "bound": "hbm",
             "achieved": round(value, 2),
