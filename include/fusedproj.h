@@ -77,7 +77,9 @@ typedef enum {
   FP_PATH_SKINNY_SPLITK = 2, /* same kernel with the K contraction split
                               across workgroups and a fixed-order finish
                               inside the same launch */
-  FP_PATH_MFMA = 3         /* MFMA tile kernel (bf16, M above the crossover) */
+  FP_PATH_MFMA = 3,        /* MFMA tile kernel (bf16, M above the crossover) */
+  FP_PATH_MFMA_SMALL = 4   /* matrix-core kernel for few tokens (bf16, M <= 8):
+                              8-row x 2-sub-slice tiles, one launch */
 } fp_path;
 
 #define FP_MAX_PROJ 16     /* projections per plan */
@@ -164,18 +166,22 @@ fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
  * splits and (mfma) groups -- never on rows or the skinny groups -- so fused
  * and separate calls of one plan stay bitwise equal under any tiling.
  *   path    FP_PATH_SKINNY / FP_PATH_SKINNY_SPLITK (same kernel; the
- *           splits field decides) or FP_PATH_MFMA (bf16 only)
- *   kparts  skinny: waves splitting one K slice (P); mfma: PK
+ *           splits field decides), FP_PATH_MFMA_SMALL (bf16, M <= 8) or
+ *           FP_PATH_MFMA (bf16 only)
+ *   kparts  skinny: waves splitting one K slice (P); mfma and mfma-small:
+ *           waves splitting K (PK, at most 16)
  *   chunks  skinny: 16-byte chunks per lane and row (CJ, 1..2);
- *           mfma: 128-wide k tiles per wave and K sub-slice (KTW: 1, 2, 4)
+ *           mfma: 128-wide k tiles per wave and K sub-slice (KTW: 1, 2, 4);
+ *           mfma-small: MFMA steps of 64 k per wave (KT: 4, 8, 16)
  *   splits  K slices across workgroups (S >= 1), finished in-launch
+ *           (mfma-small: 1)
  *   rows    skinny: rows per wave (RW, 1..8); mfma: row groups per
- *           workgroup (GR, each of 16/Q rows); 0 = chosen per launch from
- *           its row count
- *   groups  skinny: row groups per workgroup (G); 0 = chosen per launch;
- *           mfma: Q, the k-slice packing of the 16 MFMA rows (1, 2, 4, 8:
- *           16/Q weight rows times Q slices of K; Q > 1 serves at most
- *           16/Q tokens); part of the summation order */
+ *           workgroup (GR, each of 16/Q rows); mfma-small: rows per tile
+ *           (1..8); 0 = chosen per launch from its row count
+ *   groups  skinny and mfma-small: row groups per workgroup (G); 0 =
+ *           chosen per launch; mfma: Q, the k-slice packing of the 16 MFMA
+ *           rows (1, 2, 4, 8: 16/Q weight rows times Q slices of K; Q > 1
+ *           serves at most 16/Q tokens); part of the summation order */
 typedef struct {
   int32_t path;
   int32_t kparts;

@@ -11,7 +11,7 @@ through torch.  Importing it fails if the library is not built.
 from . import _lib
 from ._lib import (FP_BF16, FP_F32, FP_OK, FP_ERR_INVALID_ARG, FP_ERR_UNSUPPORTED,
                    FP_ERR_HIP, FP_ERR_WORKSPACE, FP_PATH_NONE, FP_PATH_SKINNY,
-                   FP_PATH_SKINNY_SPLITK, FP_PATH_MFMA, FP_MAX_M, FP_MAX_PROJ,
+                   FP_PATH_SKINNY_SPLITK, FP_PATH_MFMA, FP_PATH_MFMA_SMALL, FP_MAX_M, FP_MAX_PROJ,
                    FusedProjError, LIB_PATH, fp_workspace_bytes, fp_plan_create,
                    fp_plan_view, fp_plan_destroy, fp_supported, fp_forward,
                    fp_forward_separate, fp_plan_query, fp_plan_set_mfma_min_m,

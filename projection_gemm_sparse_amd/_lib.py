@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fusedproj.h")
 
 FP_BF16, FP_F32 = 0, 1
 FP_OK, FP_ERR_INVALID_ARG, FP_ERR_UNSUPPORTED, FP_ERR_HIP, FP_ERR_WORKSPACE = range(5)
-FP_PATH_NONE, FP_PATH_SKINNY, FP_PATH_SKINNY_SPLITK, FP_PATH_MFMA = range(4)
+FP_PATH_NONE, FP_PATH_SKINNY, FP_PATH_SKINNY_SPLITK, FP_PATH_MFMA, FP_PATH_MFMA_SMALL = range(5)
 FP_MAX_PROJ = 16
 FP_MAX_M = 256
 
@@ -26,7 +26,8 @@ STATUS_NAMES = {
     FP_ERR_WORKSPACE: "FP_ERR_WORKSPACE",
 }
 PATH_NAMES = {FP_PATH_NONE: "none", FP_PATH_SKINNY: "skinny",
-              FP_PATH_SKINNY_SPLITK: "skinny_splitk", FP_PATH_MFMA: "mfma"}
+              FP_PATH_SKINNY_SPLITK: "skinny_splitk", FP_PATH_MFMA: "mfma",
+              FP_PATH_MFMA_SMALL: "mfma_small"}
 
 
 class FpTiling(ctypes.Structure):

@@ -21,6 +21,7 @@
 #include "../../include/fusedproj.h"
 #include "mfma.hpp"
 #include "skinny.hpp"
+#include "smfma.hpp"
 
 namespace {
 
@@ -28,7 +29,14 @@ constexpr uint64_t kPlanMagic = 0x66757365'6470726full;  // "fusedpro"
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kSkinnyMaxM = 8;      // largest M the skinny kernel serves
 constexpr int kDefaultMfmaMinM = 9; // crossover (smallest M on the MFMA path)
+// Smallest M the small-M matrix-core kernel serves by default (bf16).  It is
+// off by default (above the vector-ALU kernel's range): measured on MI355X
+// at K = 5120 it is slower than the vector-ALU kernel at every M <= 8 (its
+// operand layout spreads each quarter-wave's loads over eight weight rows);
+// it stays selectable through fp_plan_set_tiling.
+constexpr int kDefaultSmallMfmaMinM = kSkinnyMaxM + 1;
 constexpr int kCus = 256;           // MI355X compute units
+constexpr int64_t kMaxRows = (int64_t)1 << 30;  // rows and chunks per row, 32-bit indexing
 
 thread_local int32_t g_last_hip = 0;
 
@@ -59,6 +67,7 @@ struct fp_plan_s {
   size_t ws_bytes;
   int64_t max_M;
   int64_t mfma_min_m;
+  int64_t small_mfma_min_m;
   bool has_override[FP_MAX_M + 1];
   fp_tiling override_t[FP_MAX_M + 1];
 };
@@ -136,6 +145,19 @@ void default_mfma_order(int64_t kc, int64_t M, Tiling* t) {
   t->splits = (int)ceil_div(kt, PK * Q * KTW);
 }
 
+// Small-M matrix-core order fields: PK waves of KT steps (8 chunks each).
+bool default_smfma_order(int64_t kc, Tiling* t) {
+  const int64_t steps = ceil_div(kc, 8);
+  const int KT = steps <= 64 ? 4 : steps <= 128 ? 8 : 16;
+  const int64_t PK = ceil_div(steps, KT);
+  if (PK > fp::kMaxWaveParts) return false;
+  t->path = FP_PATH_MFMA_SMALL;
+  t->kparts = (int)PK;
+  t->chunks = KT;
+  t->splits = 1;
+  return true;
+}
+
 // Launch-level part (work per workgroup): may depend on the launch's rows.
 // Rows per workgroup R = G * RW are chosen so that every workgroup is
 // resident at once (one round: all weight loads in flight together) and,
@@ -174,6 +196,39 @@ void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t) {
   t->groups = best_g;
 }
 
+// Rows per tile (<= 8) and row groups per workgroup of the small-M
+// matrix-core kernel, by the same one-round, least-loaded-CU rule as the
+// skinny kernel.
+void resolve_smfma_rows(int64_t n_rows, Tiling* t) {
+  if (t->rows > 0 && t->groups > 0) return;
+  int best_rt = 1, best_g = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int rt = 1; rt <= 8; ++rt) {
+    if (t->rows > 0 && rt != t->rows) continue;
+    const int g_cap = std::max(1, fp::smfma_max_threads(t->chunks) / (64 * t->kparts));
+    for (int g = 1; g <= g_cap; ++g) {
+      if (t->groups > 0 && g != t->groups) continue;
+      const int64_t R = (int64_t)rt * g;
+      const int64_t nb = ceil_div(n_rows, R);
+      const int waves = g * t->kparts;
+      const int64_t resident = std::max(1, std::min(2, 32 / waves));
+      const bool one_round = nb <= resident * kCus;
+      const int64_t cost = one_round ? ceil_div(nb, kCus) * R : INT64_MAX / 2 - R;
+      if (cost < best_cost || (cost == best_cost && R > (int64_t)best_rt * best_g)) {
+        best_cost = cost;
+        best_rt = rt;
+        best_g = g;
+      }
+    }
+  }
+  t->rows = best_rt;
+  t->groups = best_g;
+}
+
+size_t smfma_lds(const Tiling& t) {
+  return (size_t)t.groups * 2 * 64 * fp::kMaxWaveParts * 4;
+}
+
 bool mfma_xlds(const Tiling& t) { return t.groups == 1 && (t.rows > 1 || t.mt >= 4); }
 
 void resolve_mfma_rows(int mt16, Tiling* t) {
@@ -184,7 +239,7 @@ size_t skinny_lds(const Tiling& t) {
   const int V = t.rows * t.mt;
   int VP = 1;
   while (VP < V) VP <<= 1;
-  return (size_t)t.groups * t.kparts * VP * 4 + 16;
+  return (size_t)t.groups * VP * fp::kMaxWaveParts * 4 + 16;
 }
 
 size_t mfma_lds(const Tiling& t) {
@@ -204,7 +259,7 @@ int64_t partial_floats(const Tiling& t, int64_t n_rows, int64_t M) {
 bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t) {
   if (t.splits < 1 || t.kparts < 1 || t.chunks < 1 || t.rows < 1) return false;
   // packed into 8- and 16-bit fields of the kernels' scalar arguments
-  if (t.splits > 0x7fff || t.kparts > 0xff || t.rows > 0xff || t.groups > 0xffff) return false;
+  if (t.splits > 0x1fff || t.kparts > 0xff || t.rows > 0xff || t.groups > 0xff) return false;
   if (t.path == FP_PATH_MFMA) {
     const int Q = t.groups;
     if (p->dtype != FP_BF16) return false;
@@ -217,8 +272,15 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     if ((int64_t)t.splits * t.kparts * Q * t.chunks * 16 < p->kc) return false;
     if (mfma_lds(t) > kMaxLds) return false;
     if (16 * (int64_t)t.mt < M) return false;
+  } else if (t.path == FP_PATH_MFMA_SMALL) {
+    if (p->dtype != FP_BF16 || M > kSkinnyMaxM) return false;
+    if (!(t.chunks == 4 || t.chunks == 8 || t.chunks == 16)) return false;
+    if (t.splits != 1 || t.kparts > fp::kMaxWaveParts || t.rows > 8 || t.groups < 1) return false;
+    if ((int64_t)t.groups * t.kparts * 64 > fp::smfma_max_threads(t.chunks)) return false;
+    if ((int64_t)t.kparts * t.chunks * 8 < p->kc) return false;
+    if (smfma_lds(t) > kMaxLds) return false;
   } else if (t.path == FP_PATH_SKINNY || t.path == FP_PATH_SKINNY_SPLITK) {
-    if (M > kSkinnyMaxM) return false;
+    if (M > kSkinnyMaxM || t.kparts > fp::kMaxWaveParts) return false;
     if (t.rows > 8 || t.rows * t.mt > 64) return false;
     const bool cj_ok = t.chunks <= 2 || (t.mt <= 2 && t.rows <= 2 &&
         (t.chunks == 4 || t.chunks == 5 || t.chunks == 6 || t.chunks == 8 ||
@@ -254,8 +316,12 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t) {
     if (t->path == FP_PATH_MFMA && t->groups <= 0) t->groups = 1;
   } else {
     const bool mfma = p->dtype == FP_BF16 && (M >= p->mfma_min_m || M > kSkinnyMaxM);
+    const bool small = p->dtype == FP_BF16 && !mfma && M >= p->small_mfma_min_m &&
+                       default_smfma_order(p->kc, t);
     if (mfma) {
       default_mfma_order(p->kc, M, t);
+    } else if (small) {
+      // order fields already set
     } else {
       if (M > kSkinnyMaxM) return false;
       default_skinny_order(p->dtype, p->kc, p->n_total, skinny_mt(M), t);
@@ -264,6 +330,10 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t) {
   if (t->path == FP_PATH_MFMA) {
     t->mt = mfma_mt16(M);
     resolve_mfma_rows(t->mt, t);
+  } else if (t->path == FP_PATH_MFMA_SMALL) {
+    t->mt = 8;
+    if (t->kparts < 1 || t->chunks < 1) return false;
+    resolve_smfma_rows(n_rows, t);
   } else {
     t->mt = skinny_mt(M);
     if (t->kparts < 1) return false;
@@ -287,6 +357,7 @@ void scratch_plan(fp_plan_s* tmp, int32_t dtype, int64_t K, int64_t n_total,
   tmp->n_total = n_total;
   tmp->max_M = max_M;
   tmp->mfma_min_m = kDefaultMfmaMinM;
+  tmp->small_mfma_min_m = kDefaultSmallMfmaMinM;
   tmp->ws_bytes = SIZE_MAX;
 }
 
@@ -436,40 +507,77 @@ fp_status launch(const void* fn, int64_t blocks, int threads, size_t lds,
   return FP_OK;
 }
 
-// One launch over the rows of `rs` with tiling t.  The kernels take their
-// hot scalars as leading arguments (preloaded into SGPRs) and the row space
-// and workspace pointers in a trailing struct.
-fp_status run(const fp_plan_s* p, const Tiling& t, const fp::RowSpace& rs,
+// The rows one launch computes: rows [0, n_rows) of the weight buffer w
+// (row r at w + r * K * esize), split into n_seg output segments; segment i
+// owns rows [begin[i], begin[i+1]) and writes the dense [M, N_i] tensor y[i].
+struct LaunchRows {
+  const unsigned char* w;
+  int n_rows;
+  int n_seg;
+  unsigned char* y[fp::kMaxSeg];
+  int begin[fp::kMaxSeg + 1];
+};
+
+template <int KT>
+const void* smfma_fn_kt() {
+  return reinterpret_cast<const void*>(&fp::smfma_kernel<KT>);
+}
+
+const void* smfma_fn(const Tiling& t) {
+  switch (t.chunks) {
+    case 4: return smfma_fn_kt<4>();
+    case 8: return smfma_fn_kt<8>();
+    case 16: return smfma_fn_kt<16>();
+    default: return nullptr;
+  }
+}
+
+// One launch over `lr` with tiling t.  Every kernel takes the same 14
+// leading argument dwords, all preloaded into SGPRs at wave launch (the
+// hardware limit; a 15th would be read from memory before the first load):
+// w, x, y0, y1, ldx in bytes, n_rows, kc, M, split and one kernel-specific
+// geometry word; then the trailing Tail (output table for more than two
+// segments, split-K workspace).
+fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
               const void* x, int64_t M, int64_t ldx, hipStream_t stream) {
-  const unsigned char* w_pre = rs.w;
-  const unsigned char* x_pre = static_cast<const unsigned char*>(x);
-  int64_t ldx_pre = ldx * p->esize;
-  int64_t n_rows_pre = rs.n_rows;
-  int32_t kc_pre = (int32_t)p->kc;
-  int32_t M_pre = (int32_t)M;
-  float* partial = reinterpret_cast<float*>(p->ws + counters_bytes(p->n_total));
-  uint32_t* counters = reinterpret_cast<uint32_t*>(p->ws);
+  const unsigned char* w_a = lr.w;
+  const unsigned char* x_a = static_cast<const unsigned char*>(x);
+  unsigned char* y0_a = lr.y[0];
+  unsigned char* y1_a = lr.n_seg >= 2 ? lr.y[1] : lr.y[0];
+  uint32_t ldx_a = (uint32_t)(ldx * p->esize);
+  int32_t n_rows_a = lr.n_rows;
+  int32_t kc_a = (int32_t)p->kc;
+  int32_t M_a = (int32_t)M;
+  int32_t split_a = lr.n_seg > 2 ? -1 : (lr.n_seg == 2 ? lr.begin[1] : lr.n_rows);
+  fp::Tail tail;
+  std::memset(&tail, 0, sizeof tail);
+  tail.out.n_seg = lr.n_seg;
+  for (int i = 0; i < fp::kMaxSeg; ++i) {
+    tail.out.y[i] = i < lr.n_seg ? lr.y[i] : nullptr;
+    tail.out.begin[i] = i < lr.n_seg ? lr.begin[i] : lr.n_rows;
+  }
+  tail.out.begin[fp::kMaxSeg] = lr.n_rows;
+  tail.partial = reinterpret_cast<float*>(p->ws + counters_bytes(p->n_total));
+  tail.counters = reinterpret_cast<uint32_t*>(p->ws);
+  int32_t geo_a = 0;
+  void* args[] = {&w_a, &x_a, &y0_a, &y1_a, &ldx_a, &n_rows_a, &kc_a, &M_a, &split_a,
+                  &geo_a, &tail};
+  if (t.path == FP_PATH_MFMA_SMALL) {
+    geo_a = t.rows | (t.kparts << 8) | (t.groups << 16);
+    const int64_t R = (int64_t)t.rows * t.groups;
+    return launch(smfma_fn(t), ceil_div(lr.n_rows, R), t.groups * t.kparts * 64, smfma_lds(t),
+                  args, stream);
+  }
   if (t.path == FP_PATH_MFMA) {
-    fp::MfmaArgs a;
-    a.rs = rs;
-    a.partial = partial;
-    a.counters = counters;
-    int32_t geo_pre = t.rows | (t.kparts << 8) | (t.chunks << 16);
-    int32_t S_pre = t.splits;
-    void* args[] = {&w_pre, &x_pre, &ldx_pre, &n_rows_pre, &kc_pre, &M_pre, &geo_pre, &S_pre, &a};
+    const int ktw_log2 = t.chunks == 4 ? 2 : t.chunks == 2 ? 1 : 0;
+    geo_a = t.rows | (t.kparts << 8) | (ktw_log2 << 16) | (t.splits << 18);
     const int64_t rows_per_block = (16 / t.groups) * (int64_t)t.rows;
-    const int64_t blocks = ceil_div(rs.n_rows, rows_per_block) * t.splits;
+    const int64_t blocks = ceil_div(lr.n_rows, rows_per_block) * t.splits;
     return launch(mfma_fn(t), blocks, t.rows * t.kparts * 64, mfma_lds(t), args, stream);
   }
-  fp::SkinnyArgs a;
-  a.rs = rs;
-  a.partial = partial;
-  a.counters = counters;
-  int32_t P_pre = t.kparts;
-  int32_t GS_pre = t.groups | (t.splits << 16);
-  void* args[] = {&w_pre, &x_pre, &ldx_pre, &n_rows_pre, &kc_pre, &M_pre, &P_pre, &GS_pre, &a};
+  geo_a = t.kparts | (t.groups << 8) | (t.splits << 16);
   const int64_t R = (int64_t)t.groups * t.rows;
-  const int64_t blocks = ceil_div(rs.n_rows, R) * t.splits;
+  const int64_t blocks = ceil_div(lr.n_rows, R) * t.splits;
   const void* fn = p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
                                        : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
   return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
@@ -495,6 +603,7 @@ fp_status check_x(const fp_plan_s* p, int64_t M, const void* x, int64_t ldx) {
   if (x == nullptr || ldx < p->K) return FP_ERR_INVALID_ARG;
   if (M > p->max_M) return FP_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || (ldx * p->esize) % 16 != 0) return FP_ERR_UNSUPPORTED;
+  if (ldx * p->esize > INT32_MAX) return FP_ERR_UNSUPPORTED;  // 32-bit row stride
   if (p->dtype == FP_F32 && M > kSkinnyMaxM) return FP_ERR_UNSUPPORTED;
   return FP_OK;
 }
@@ -559,6 +668,8 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
     if (N[i] < 1) return FP_ERR_INVALID_ARG;
     n_total += N[i];
   }
+  // the kernels index rows and 16-byte chunks with 32-bit integers
+  if (n_total > kMaxRows || K * esize / 16 > kMaxRows) return FP_ERR_UNSUPPORTED;
   if (ws_bytes < workspace_need(dtype, K, n_total, max_M)) return FP_ERR_WORKSPACE;
 
   fp_plan_s* p = new (std::nothrow) fp_plan_s;
@@ -582,6 +693,7 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
   p->ws_bytes = ws_bytes;
   p->max_M = max_M;
   p->mfma_min_m = kDefaultMfmaMinM;
+  p->small_mfma_min_m = kDefaultSmallMfmaMinM;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // concatenate: W_cat[off_i + r, :] = W_i[r, :]
@@ -654,17 +766,17 @@ fp_status fp_forward(const void* x, int64_t M, int64_t ldx, fp_plan_t plan, void
   if (s != FP_OK) return s;
   Tiling t;
   if (!choose_tiling(plan, M, plan->n_total, &t)) return FP_ERR_UNSUPPORTED;
-  fp::RowSpace rs;
-  std::memset(&rs, 0, sizeof rs);
-  rs.w = plan->w_cat;
-  rs.n_seg = plan->n_proj;
-  rs.n_rows = plan->n_total;
+  LaunchRows lr;
+  std::memset(&lr, 0, sizeof lr);
+  lr.w = plan->w_cat;
+  lr.n_seg = plan->n_proj;
+  lr.n_rows = (int)plan->n_total;
   for (int i = 0; i < plan->n_proj; ++i) {
-    rs.seg[i].y = static_cast<unsigned char*>(y[i]);
-    rs.seg[i].rows = plan->N[i];
-    rs.seg[i].row_begin = plan->off[i];
+    lr.y[i] = static_cast<unsigned char*>(y[i]);
+    lr.begin[i] = (int)plan->off[i];
   }
-  return run(plan, t, rs, x, M, ldx, static_cast<hipStream_t>(stream));
+  lr.begin[plan->n_proj] = (int)plan->n_total;
+  return run(plan, t, lr, x, M, ldx, static_cast<hipStream_t>(stream));
 }
 
 fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
@@ -684,18 +796,18 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx, fp_plan_t p
       return FP_ERR_UNSUPPORTED;
   }
   for (int i = 0; i < plan->n_proj; ++i) {
-    fp::RowSpace rs;
-    std::memset(&rs, 0, sizeof rs);
-    rs.n_seg = 1;
-    rs.n_rows = plan->N[i];
+    LaunchRows lr;
+    std::memset(&lr, 0, sizeof lr);
+    lr.n_seg = 1;
+    lr.n_rows = (int)plan->N[i];
     const unsigned char* w = plan->w_cat + plan->off[i] * plan->K * plan->esize;
     if (w_override != nullptr && w_override[i] != nullptr)
       w = static_cast<const unsigned char*>(w_override[i]);
-    rs.w = w;
-    rs.seg[0].y = static_cast<unsigned char*>(y[i]);
-    rs.seg[0].rows = plan->N[i];
-    rs.seg[0].row_begin = 0;
-    s = run(plan, ts[i], rs, x, M, ldx, static_cast<hipStream_t>(stream));
+    lr.w = w;
+    lr.y[0] = static_cast<unsigned char*>(y[i]);
+    lr.begin[0] = 0;
+    lr.begin[1] = (int)plan->N[i];
+    s = run(plan, ts[i], lr, x, M, ldx, static_cast<hipStream_t>(stream));
     if (s != FP_OK) return s;
   }
   return FP_OK;

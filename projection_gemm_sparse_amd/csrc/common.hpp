@@ -22,25 +22,25 @@ __device__ __forceinline__ bf16x2 u2bf2(unsigned u) { return __builtin_bit_cast(
 __device__ __forceinline__ bf16x8 u4bf8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 constexpr int kMaxSeg = 16;
+// Most waves that split one row's K range inside a workgroup.
+constexpr int kMaxWaveParts = 16;
 
-// One projection's slice of a launch's row space: rows
-// [row_begin, row_begin + rows) of the launch write output column
-// (row - row_begin) of the dense [M, rows] tensor y.
-struct Seg {
-  unsigned char* y;
-  int64_t rows;
-  int64_t row_begin;
+// Output table of a launch.  The launch covers rows [0, n_rows) of its
+// weight buffer; projection (segment) i owns rows [begin[i], begin[i+1])
+// and row r of it writes column r - begin[i] of the dense [M, N_i] tensor
+// y[i] (N_i = begin[i+1] - begin[i]).  Unused entries repeat n_rows.
+struct OutTable {
+  unsigned char* y[kMaxSeg];
+  int32_t begin[kMaxSeg + 1];
+  int32_t n_seg;
 };
 
-// The rows one launch computes.  Their weights are contiguous rows of w
-// (row r at w + r * row_bytes): the fused call covers the whole
-// concatenated buffer with one segment per projection, a separate call one
-// projection's rows with a single segment.
-struct RowSpace {
-  const unsigned char* w;
-  int64_t n_rows;
-  int32_t n_seg;
-  Seg seg[kMaxSeg];
+// Trailing kernel argument (not preloaded): the output table for launches
+// with more than two segments, and the split-K workspace.
+struct Tail {
+  OutTable out;
+  float* partial;      // [S][n_rows][M] when S > 1
+  uint32_t* counters;  // one per row block when S > 1, zero between calls
 };
 
 constexpr int pow2ceil(int v) {
@@ -73,12 +73,6 @@ constexpr int mfma_max_threads(int mt16, int ktw, bool xlds) {
   return max_threads_for_regs(16 * ktw + 4 * mt16 + (xlds ? 8 : 16 * ktw * mt16) + 24);
 }
 
-__device__ __forceinline__ const unsigned char* row_pointer(
-    const RowSpace& rs, int64_t row, int64_t row_bytes) {
-  if (row < 0 || row >= rs.n_rows) return nullptr;
-  return rs.w + row * row_bytes;
-}
-
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = f2u(f);
@@ -87,66 +81,107 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Output segments of one workgroup.  A workgroup's rows span at most a few
-// segments; the two that hold its first rows are looked up once, early in
-// the kernel, so the kernel-argument reads are not on the epilogue's
-// critical path.  Rows in later segments (workgroups straddling several
-// tiny projections) fall back to a scan of the table.
-struct OutSegs {
+// Where a workgroup's outputs go.  Two segments are resolved per workgroup
+// before its weights land: rows [b0, b1) write y0 (width b1 - b0) and rows
+// [b1, e1) write y1 (width e1 - b1).  A launch of one or two projections
+// passes y0, y1 and the split row as preloaded kernel arguments (no memory
+// read at all).  A launch of more projections passes split < 0; the
+// workgroup then reads the row boundaries from the output table, picks the
+// segment of its first row and the next one, and reads their pointers --
+// all at its start, pinned there so that the scalar loads are not sunk
+// towards the end of the kernel, where a kernel-argument read would put a
+// memory round trip on the critical path.  Rows past those two segments (a
+// workgroup straddling a projection shorter than itself) are resolved from
+// the table when stored.
+struct OutMap {
   unsigned char* y0;
-  int64_t b0, n0;
   unsigned char* y1;
-  int64_t b1, n1;
+  int b0, b1, e1;
 };
 
-__device__ __forceinline__ OutSegs find_out_segs(const RowSpace& rs, int64_t first_row) {
-  OutSegs o;
-  o.y0 = nullptr; o.b0 = 0; o.n0 = 0;
-  o.y1 = nullptr; o.b1 = 0; o.n1 = 0;
-  int i = 0;
-  while (i < rs.n_seg && first_row >= rs.seg[i].row_begin + rs.seg[i].rows) ++i;
-  if (i < rs.n_seg) {
-    o.y0 = rs.seg[i].y; o.b0 = rs.seg[i].row_begin; o.n0 = rs.seg[i].rows;
+__device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char* y1, int split,
+                                               int n_rows, const OutTable& tab, int first_row) {
+  OutMap o;
+  if (split >= 0) {
+    o.y0 = y0;
+    o.y1 = y1;
+    o.b0 = 0;
+    o.b1 = split;
+    o.e1 = n_rows;
+    return o;
   }
-  if (i + 1 < rs.n_seg) {
-    o.y1 = rs.seg[i + 1].y; o.b1 = rs.seg[i + 1].row_begin; o.n1 = rs.seg[i + 1].rows;
-  }
+  const int n_seg = tab.n_seg;
+  int i0 = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSeg; ++i) i0 = (i < n_seg && first_row >= tab.begin[i]) ? i : i0;
+  const int i1 = i0 + 1 < kMaxSeg ? i0 + 1 : kMaxSeg - 1;
+  const int i2 = i0 + 2 < kMaxSeg ? i0 + 2 : kMaxSeg;
+  o.y0 = tab.y[i0];
+  o.y1 = tab.y[i1];
+  o.b0 = tab.begin[i0];
+  o.b1 = tab.begin[i0 + 1];
+  o.e1 = tab.begin[i2];
+  asm volatile("" : "+s"(o.y0), "+s"(o.y1), "+s"(o.b0), "+s"(o.b1), "+s"(o.e1));
   return o;
 }
 
-// Stores output element (launch row `row`, token m): y_i[m, row - row_begin]
-// of the dense [M, rows] tensor of the segment that holds the row.
+// Stores output element (launch row `row`, token m) rounded once to the
+// output type (bf16: round to nearest even).  Agent-coherent (sc1) stores:
+// the line is written through instead of left dirty in this XCD's L2.
 template <bool BF16>
-__device__ __forceinline__ void store_out(const RowSpace& rs, const OutSegs& os,
-                                          int64_t row, int m, float v) {
-  unsigned char* y = nullptr;
-  int64_t idx = 0;
-  if (row >= os.b0 && row < os.b0 + os.n0) {
-    y = os.y0;
-    idx = (int64_t)m * os.n0 + (row - os.b0);
-  } else if (row >= os.b1 && row < os.b1 + os.n1) {
-    y = os.y1;
-    idx = (int64_t)m * os.n1 + (row - os.b1);
+__device__ __forceinline__ void store_y(const OutMap& o, const OutTable& tab, int row, int m,
+                                        float v) {
+  unsigned char* y;
+  int idx;
+  if (row < o.b1) {
+    y = o.y0;
+    idx = m * (o.b1 - o.b0) + (row - o.b0);
+  } else if (row < o.e1) {
+    y = o.y1;
+    idx = m * (o.e1 - o.b1) + (row - o.b1);
   } else {
-    for (int i = 0; i < rs.n_seg; ++i) {
-      const int64_t b = rs.seg[i].row_begin;
-      const int64_t n = rs.seg[i].rows;
-      if (row >= b && row < b + n) {
-        y = rs.seg[i].y;
-        idx = (int64_t)m * n + (row - b);
+    // a third segment inside the workgroup (more than two projections only)
+    y = nullptr;
+    idx = 0;
+    for (int i = 0; i < tab.n_seg; ++i) {
+      if (row >= tab.begin[i] && row < tab.begin[i + 1]) {
+        y = tab.y[i];
+        idx = m * (tab.begin[i + 1] - tab.begin[i]) + (row - tab.begin[i]);
       }
     }
+    if (y == nullptr) return;
   }
-  if (y == nullptr) return;
-  // agent-coherent (sc1) stores: the line is written through instead of
-  // left dirty in this XCD's L2, which shortens the end-of-kernel writeback
+  // global (not generic) address space: a global_store, no aperture check
+  typedef __attribute__((address_space(1))) uint16_t g_u16;
+  typedef __attribute__((address_space(1))) float g_f32;
   if constexpr (BF16) {
-    __hip_atomic_store(reinterpret_cast<uint16_t*>(y) + idx, f32_to_bf16_rne(v),
+    __hip_atomic_store((g_u16*)(reinterpret_cast<uint16_t*>(y) + idx), f32_to_bf16_rne(v),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    __hip_atomic_store(reinterpret_cast<float*>(y) + idx, v, __ATOMIC_RELAXED,
+    __hip_atomic_store((g_f32*)(reinterpret_cast<float*>(y) + idx), v, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// Sum of the P <= kMaxWaveParts per-wave partial sums of one output, stored
+// contiguously (slot p at q[p]; q 16-byte aligned), added in wave order.
+// The four 16-byte LDS reads are at fixed offsets; slots at and past P are
+// read (never written for this output) and left out by the selects.
+__device__ __forceinline__ float sum_wave_parts(const float* q, int P) {
+  const f32x4* q4 = reinterpret_cast<const f32x4*>(q);
+  const f32x4 a0 = q4[0], a1 = q4[1], a2 = q4[2], a3 = q4[3];
+  float v[kMaxWaveParts];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a0[i];
+    v[4 + i] = a1[i];
+    v[8 + i] = a2[i];
+    v[12 + i] = a3[i];
+  }
+  float sum = v[0];
+#pragma unroll
+  for (int pp = 1; pp < kMaxWaveParts; ++pp) sum = pp < P ? sum + v[pp] : sum;
+  return sum;
 }
 
 // Multiply-accumulate of one 16-byte chunk of a weight row with the same
@@ -284,48 +319,53 @@ __device__ __forceinline__ void transpose_reduce(float* v, int lane) {
 // agent-coherent, no L2 writeback or invalidation (what an agent-scope
 // fence would cost per workgroup) is needed.
 // ---------------------------------------------------------------------------
+typedef __attribute__((address_space(1))) float gf32;
+typedef __attribute__((address_space(1))) uint32_t gu32;
+
 __device__ __forceinline__ void store_partial(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((gf32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float load_partial(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((gf32*)const_cast<float*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Must be called by every thread of the workgroup (it has barriers).
 template <bool BF16>
-__device__ __forceinline__ void splitk_finish(const RowSpace& rs,
+__device__ __forceinline__ void splitk_finish(int n_rows_i,
                                               const float* partial,
                                               uint32_t* counters, int rb,
                                               int S, int64_t row_base,
-                                              int64_t R, int M, int* flag) {
+                                              int64_t R, int M, int nthreads,
+                                              const OutMap& os, const OutTable& tab,
+                                              int* flag) {
   // this thread's partial stores are complete (vmcnt = 0; expcnt and
   // lgkmcnt left at their maximum) before the workgroup arrives
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(counters + rb, 1u, __ATOMIC_RELAXED,
+    const unsigned old = __hip_atomic_fetch_add((gu32*)(counters + rb), 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
     *flag = (old == (unsigned)(S - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (*flag == 0) return;
-  const int64_t n_rows = rs.n_rows;
+  const int64_t n_rows = n_rows_i;
   const int64_t rows_here = (n_rows - row_base) < R ? (n_rows - row_base) : R;
   const int64_t n_fin = rows_here * M;
   const int64_t sstride = n_rows * M;
-  const OutSegs os = find_out_segs(rs, row_base);
-  for (int64_t t = threadIdx.x; t < n_fin; t += blockDim.x) {
+  for (int64_t t = threadIdx.x; t < n_fin; t += nthreads) {
     const int64_t rr = t / M;
     const int m = (int)(t - rr * M);
     const int64_t row = row_base + rr;
     const float* pp = partial + row * M + m;
     float sum = load_partial(pp);
     for (int ss = 1; ss < S; ++ss) sum += load_partial(pp + ss * sstride);
-    store_out<BF16>(rs, os, row, m, sum);
+    store_y<BF16>(os, tab, (int)row, m, sum);
   }
   if (threadIdx.x == 0) {
-    __hip_atomic_store(counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((gu32*)(counters + rb), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -42,22 +42,15 @@
 
 namespace fp {
 
-// Scalar arguments (leading, preloaded into SGPRs at wave launch): w_pre =
-// rs.w, x_pre = activations (M_pre rows, row stride ldx_pre bytes),
-// n_rows_pre = rs.n_rows, kc_pre = 16-byte chunks per row, geo_pre = GR |
-// PK << 8 | ktw << 16 (row groups per workgroup, waves per row group, k
-// tiles per wave), S_pre = K slices across workgroups.
-struct MfmaArgs {
-  RowSpace rs;
-  float* partial;          // [S][n_rows][M] when S > 1
-  uint32_t* counters;
-};
-
+// Leading scalars preloaded into SGPRs (see skinny_kernel for w_pre, x_pre,
+// y0, y1, ldx, n_rows_pre, kc_pre, M_pre, split); geo_pre = GR | PK << 8 |
+// log2(ktw) << 16 | S << 18 (row groups per workgroup, waves per row group,
+// k tiles per wave, K slices across workgroups).
 template <int Q, int MT16, int KTW, bool XLDS>
 __global__ void __launch_bounds__(mfma_max_threads(MT16, KTW, XLDS))
 mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __restrict__ x_pre,
-            int64_t ldx_pre, int64_t n_rows_pre, int32_t kc_pre, int32_t M_pre,
-            int32_t geo_pre, int32_t S_pre, const MfmaArgs a) {
+            unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows_pre,
+            int32_t kc_pre, int32_t M_pre, int32_t split, int32_t geo_pre, const Tail a) {
   constexpr int RT = 16 / Q;  // weight rows per row group
   constexpr int TQ = 16 / Q;  // tokens per sub-slice
   constexpr int MC = Q == 1 ? 16 : TQ;  // token columns kept per tile
@@ -71,8 +64,8 @@ mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __rest
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int GRv = geo_pre & 0xff;
   const int PKv = (geo_pre >> 8) & 0xff;
-  const int ktw = geo_pre >> 16;
-  const int Sv = S_pre;
+  const int ktw = 1 << ((geo_pre >> 16) & 3);
+  const int Sv = geo_pre >> 18;
   const int Mv = M_pre;
   const int kc = kc_pre;
   const int pk = GRv == 1 ? wave : wave % PKv;
@@ -84,6 +77,8 @@ mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __rest
   const int64_t row0 = row_base + (int64_t)RT * gr;
   const int i16 = lane & 15;
   const int g = lane >> 4;
+  const int nthreads = GRv * PKv * 64;
+  const int64_t ldx_pre = ldx;
   const int wave_chunks = 16 * Q * ktw;             // chunks of a wave
   const int slice_chunks = PKv * wave_chunks;       // chunks of a K slice
   const int cw0 = s * slice_chunks + pk * wave_chunks;
@@ -118,7 +113,6 @@ mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __rest
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  OutSegs os;
 
   // 1. activations and weights.  Read per wave, the activations (from L2)
   //    are loaded first so the weights can be consumed as they land; staged
@@ -142,21 +136,19 @@ mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __rest
       }
     }
     load_weights();
-    os = find_out_segs(a.rs, row_base);  // while the loads are in flight
     __builtin_amdgcn_sched_barrier(0);
   } else {
     load_weights();
-    os = find_out_segs(a.rs, row_base);
     __builtin_amdgcn_sched_barrier(0);
     // rows 0 .. 16*MT16-1 (zero past M) of the slice's chunks; each thread
     // loads up to 8 chunks into registers before storing any of them
     u32x4* xs = reinterpret_cast<u32x4*>(lds);
     const int total = 16 * MT16 * slice_chunks;
-    for (int base = 0; base < total; base += 8 * (int)blockDim.x) {
+    for (int base = 0; base < total; base += 8 * nthreads) {
       u32x4 st[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int idx = base + e * (int)blockDim.x + tid;
+        const int idx = base + e * nthreads + tid;
         st[e] = u32x4{0u, 0u, 0u, 0u};
         if (idx < total) {
           const int m = idx / slice_chunks;
@@ -169,7 +161,7 @@ mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __rest
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int idx = base + e * (int)blockDim.x + tid;
+        const int idx = base + e * nthreads + tid;
         if (idx < total) {
           const int m = idx / slice_chunks;
           const int cc = idx - m * slice_chunks;
@@ -179,6 +171,9 @@ mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __rest
     }
     __syncthreads();
   }
+
+  const OutMap os = make_out_map(y0, y1, split, (int)n_rows_pre, a.out, (int)row_base);
+  __builtin_amdgcn_sched_barrier(0);
 
   // 2. MFMA steps in tile order
   f32x4 acc[MT16];
@@ -238,7 +233,7 @@ mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __rest
   const int64_t n_rows = n_rows_pre;
   const int mcols = MC * MT16;
   const int n_out = GRv * RT * mcols;
-  for (int o = tid; o < n_out; o += blockDim.x) {
+  for (int o = tid; o < n_out; o += nthreads) {
     const int g2 = o / (RT * mcols);
     const int rem = o - g2 * (RT * mcols);
     const int r = rem / mcols;
@@ -257,14 +252,15 @@ mfma_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __rest
       }
     }
     if (Sv == 1) {
-      store_out<true>(a.rs, os, row, mm, sum);
+      store_y<true>(os, a.out, (int)row, mm, sum);
     } else {
       store_partial(a.partial + ((int64_t)s * n_rows + row) * Mv + mm, sum);
     }
   }
   if (Sv == 1) return;
   int* flag = reinterpret_cast<int*>(red + (size_t)GRv * PKv * Q * MT16 * TILE);
-  splitk_finish<true>(a.rs, a.partial, a.counters, rb, Sv, row_base, R, Mv, flag);
+  splitk_finish<true>((int)n_rows, a.partial, a.counters, rb, Sv, row_base, R, Mv,
+                      GRv * PKv * 64, os, a.out, flag);
 }
 
 }  // namespace fp

@@ -23,7 +23,9 @@
 //      in element order;
 //   2. across the 64 lanes of the wave by the transpose reduce of
 //      common.hpp (one fixed tree of lane pairings);
-//   3. across the P waves of the row group in LDS, in wave order;
+//   3. across the P waves of the row group in LDS, in wave order (each
+//      output's P wave sums sit in 16 consecutive slots, read as four
+//      16-byte vectors);
 //   4. with S > 1, across the S workgroups of the row block: each writes its
 //      partial sums to the workspace, and the last workgroup to arrive
 //      (arrival counter) adds the S partials in slice order, stores the
@@ -39,49 +41,47 @@
 
 namespace fp {
 
-// Scalar arguments (leading, preloaded): w_pre = rs.w, x_pre = activations
-// (M_pre rows, row stride ldx_pre bytes), n_rows_pre = rs.n_rows, kc_pre =
-// 16-byte chunks per row (K * element size / 16), P_pre = waves per row
-// group (K parts of a slice), GS_pre = G | S << 16 (row groups per
-// workgroup, K slices).  A K slice holds P * 64 * CJ chunks; a workgroup
-// owns G * RW rows.
-struct SkinnyArgs {
-  RowSpace rs;             // rows of this launch and their output segments
-  float* partial;          // [S][n_rows][M] when S > 1
-  uint32_t* counters;      // one per row block when S > 1, zero between calls
-};
-
-// The fields the kernel needs before its first load are also passed as
-// leading scalar arguments, which the library build preloads into SGPRs at
-// wave launch (-amdgpu-kernarg-preload-count): the loads can issue without
-// waiting for kernel-argument memory reads.
+// Kernel arguments.  The leading scalars are preloaded into SGPRs at wave
+// launch (-amdgpu-kernarg-preload-count), so nothing the kernel needs before
+// its stores is read from kernel-argument memory after the loads are issued:
+//   w, x       weights (row stride kc * 16 bytes) and activations (M rows,
+//              row stride ldx bytes)
+//   y0, y1     outputs of the first two segments, split = first row of the
+//              second (split < 0: more than two segments, see OutMap)
+//   kc         16-byte chunks per row (K * element size / 16)
+//   geo        P | G << 8 | S << 16: waves per row group (K parts of a
+//              slice), row groups per workgroup, K slices
+// A K slice holds P * 64 * CJ chunks; a workgroup owns G * RW rows.  The
+// hardware preloads at most 14 argument dwords, exactly these; one more
+// would be read from memory before the first load could issue.
 template <int MT, int RW, int CJ, bool BF16>
 __global__ void __launch_bounds__(skinny_max_threads(MT, RW, CJ))
-skinny_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __restrict__ x_pre,
-              int64_t ldx_pre, int64_t n_rows_pre, int32_t kc_pre, int32_t M_pre,
-              int32_t P_pre, int32_t GS_pre, const SkinnyArgs a) {
+skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
+              unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
+              int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
   constexpr int V = RW * MT;        // outputs per lane
   constexpr int VP = pow2ceil(V);   // padded to a power of two
   constexpr int QV = VP >= 64 ? VP / 64 : 1;
   constexpr int LSTRIDE = VP >= 64 ? 1 : 64 / VP;
 
-  extern __shared__ float smem[];   // [G][P][VP] wave sums, then one flag
+  extern __shared__ float smem[];   // [G][VP][16] wave sums, then one flag
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave index made scalar so that row and slice arithmetic stays in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // GS_pre = G | S << 16; the common single-group, unsplit case (GS = 1 | 1
-  // << 16) avoids the integer divisions
-  const int Gv = GS_pre & 0xffff;
-  const int Sv = GS_pre >> 16;
-  const bool simple = GS_pre == (1 | (1 << 16));
-  const int p = simple ? wave : wave % P_pre;
-  const int gq = simple ? 0 : wave / P_pre;
+  // the common single-group, unsplit case avoids the integer divisions
+  const int P = geo & 0xff;
+  const int Gv = (geo >> 8) & 0xff;
+  const int Sv = geo >> 16;
+  const bool simple = (geo >> 8) == (1 | (1 << 8));
+  const int p = simple ? wave : wave % P;
+  const int gq = simple ? 0 : wave / P;
   const int rb = simple ? (int)blockIdx.x : (int)blockIdx.x / Sv;
   const int s = simple ? 0 : (int)blockIdx.x - rb * Sv;
-  const int64_t row_base = (int64_t)rb * (Gv * RW);
-  const int64_t wrow0 = row_base + (int64_t)gq * RW;
-  const int cbase = s * (P_pre * 64 * CJ) + p * (64 * CJ) + lane;
+  const int row_base = rb * (Gv * RW);
+  const int wrow0 = row_base + gq * RW;
+  const int cbase = s * (P * 64 * CJ) + p * (64 * CJ) + lane;
+  const uint32_t row_bytes = (uint32_t)kc * 16u;
 
   // Loads are branch-free: an out-of-range chunk or row loads a clamped,
   // always-valid address, and out-of-range chunks are replaced by zero only
@@ -89,9 +89,6 @@ skinny_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __re
   // loads thus form one straight-line sequence, and each row can be consumed
   // as soon as its own loads have landed.
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  const int64_t n_rows_l = n_rows_pre;
-  const int kc = kc_pre;
-  const int Mv = M_pre;
   bool c_ok[CJ];
 #pragma unroll
   for (int j = 0; j < CJ; ++j) c_ok[j] = cbase + j * 64 < kc;
@@ -102,8 +99,8 @@ skinny_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __re
   u32x4 xv[MT][CJ];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int mc = m < Mv ? m : Mv - 1;
-    const u32x4* xrow = reinterpret_cast<const u32x4*>(x_pre + (int64_t)mc * ldx_pre);
+    const int mc = m < M ? m : M - 1;
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
 #pragma unroll
     for (int j = 0; j < CJ; ++j) {
       const int c = cbase + j * 64;
@@ -114,9 +111,8 @@ skinny_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __re
   u32x4 wv[RW][CJ];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    const int64_t row = wrow0 + r;
-    const u32x4* wrow = reinterpret_cast<const u32x4*>(
-        w_pre + (row < n_rows_l ? row : n_rows_l - 1) * ((int64_t)kc * 16));
+    const int row = wrow0 + r < n_rows ? wrow0 + r : n_rows - 1;
+    const u32x4* wrow = reinterpret_cast<const u32x4*>(w + (uint64_t)(uint32_t)row * row_bytes);
 #pragma unroll
     for (int j = 0; j < CJ; ++j) {
       const int c = cbase + j * 64;
@@ -124,15 +120,18 @@ skinny_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __re
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // output segments of this workgroup, looked up while the loads are in
-  // flight
-  const OutSegs os = find_out_segs(a.rs, row_base);
+  // where this workgroup's outputs go, and the split-K workspace, resolved
+  // while the loads are in flight
+  const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
+  float* partial = a.partial;
+  uint32_t* counters = a.counters;
+  if (Sv > 1) asm volatile("" : "+s"(partial), "+s"(counters));
   __builtin_amdgcn_sched_barrier(0);
   // activations past M or past K count as zero
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
 #pragma unroll
-    for (int j = 0; j < CJ; ++j) xv[m][j] = (m < Mv && c_ok[j]) ? xv[m][j] : zero4;
+    for (int j = 0; j < CJ; ++j) xv[m][j] = (m < M && c_ok[j]) ? xv[m][j] : zero4;
   }
 
   // 3. per-lane partial sums in load order (row by row), so each row is
@@ -148,10 +147,10 @@ skinny_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __re
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < CJ; ++j) {
-      const u32x4 w = c_ok[j] ? wv[r][j] : zero4;
+      const u32x4 wj = c_ok[j] ? wv[r][j] : zero4;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        v[r * MT + m] = dot_chunk<BF16>(w, xv[m][j], v[r * MT + m]);
+        v[r * MT + m] = dot_chunk<BF16>(wj, xv[m][j], v[r * MT + m]);
       }
     }
   }
@@ -159,7 +158,7 @@ skinny_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __re
 
   // 4. across the wave
   transpose_reduce<VP>(v, lane);
-  if (P_pre == 1 && Sv == 1) {
+  if (P == 1 && Sv == 1) {
     // the wave holds whole rows: its lanes store the finished sums, no
     // workgroup barrier
     if (lane % LSTRIDE == 0) {
@@ -168,50 +167,45 @@ skinny_kernel(const unsigned char* __restrict__ w_pre, const unsigned char* __re
         const int idx = q + QV * (lane / LSTRIDE);
         const int r = idx / MT;
         const int m = idx - r * MT;
-        const int64_t row = wrow0 + r;
-        if (idx < V && m < Mv && row < n_rows_l) store_out<BF16>(a.rs, os, row, m, v[q]);
+        const int row = wrow0 + r;
+        if (idx < V && m < M && row < n_rows) store_y<BF16>(om, a.out, row, m, v[q]);
       }
     }
     return;
   }
-  float* red = smem + (gq * P_pre + p) * VP;
+  // wave sums to LDS, transposed: output idx of row group gq owns 16
+  // consecutive slots, slot p for wave p
+  float* red = smem + gq * VP * kMaxWaveParts + p;
   if (lane % LSTRIDE == 0) {
 #pragma unroll
-    for (int q = 0; q < QV; ++q) red[q + QV * (lane / LSTRIDE)] = v[q];
+    for (int q = 0; q < QV; ++q) red[(q + QV * (lane / LSTRIDE)) * kMaxWaveParts] = v[q];
   }
   __syncthreads();
 
-  // 5. across the P waves of each row group, in wave order
-  const int64_t n_rows = n_rows_l;
+  // 5. across the P waves of each row group, in wave order.  There are at
+  //    most G * V <= G * P * 64 outputs, one per thread.
   const int n_out = Gv * V;
-  for (int t = tid; t < n_out; t += blockDim.x) {
-    const int g2 = t / V;
-    const int idx = t - g2 * V;
+  if (tid < n_out) {
+    const int g2 = tid / V;
+    const int idx = tid - g2 * V;
     const int r = idx / MT;
     const int m = idx - r * MT;
-    const int64_t row = row_base + (int64_t)g2 * RW + r;
-    if (m >= Mv || row >= n_rows) continue;
-    // all P wave sums read at once (P <= 16), then added in wave order
-    const float* rp = smem + g2 * P_pre * VP + idx;
-    float w[16];
-#pragma unroll
-    for (int pp = 0; pp < 16; ++pp) w[pp] = pp < P_pre ? rp[pp * VP] : 0.0f;
-    float sum = w[0];
-#pragma unroll
-    for (int pp = 1; pp < 16; ++pp) {
-      if (pp < P_pre) sum += w[pp];
-    }
-    if (Sv == 1) {
-      store_out<BF16>(a.rs, os, row, m, sum);
-    } else {
-      store_partial(a.partial + ((int64_t)s * n_rows + row) * Mv + m, sum);
+    const int row = row_base + g2 * RW + r;
+    if (m < M && row < n_rows) {
+      const float sum = sum_wave_parts(smem + (g2 * VP + idx) * kMaxWaveParts, P);
+      if (Sv == 1) {
+        store_y<BF16>(om, a.out, row, m, sum);
+      } else {
+        store_partial(partial + ((int64_t)s * n_rows + row) * M + m, sum);
+      }
     }
   }
   if (Sv == 1) return;
 
   // 6. split-K: the last workgroup of the row block adds the S partials
-  splitk_finish<BF16>(a.rs, a.partial, a.counters, rb, Sv, row_base, (int64_t)Gv * RW, Mv,
-                      reinterpret_cast<int*>(smem + Gv * P_pre * VP));
+  splitk_finish<BF16>(n_rows, partial, counters, rb, Sv, row_base, (int64_t)Gv * RW, M,
+                      Gv * P * 64, om, a.out,
+                      reinterpret_cast<int*>(smem + Gv * VP * kMaxWaveParts));
 }
 
 }  // namespace fp

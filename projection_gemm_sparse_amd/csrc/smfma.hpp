@@ -1,0 +1,154 @@
+// smfma.hpp -- matrix-core kernel for y = x . W^T with few tokens (M <= 8),
+// bf16 in, fp32 accumulate, bf16 out.
+//
+// Why matrix cores at M <= 8.  The weight stream is the cost, but once the
+// weights have landed a vector-ALU kernel still has to do 2 * M * K
+// multiply-adds per row and then add the partial sums of its 64 lanes; at
+// M = 8 that arithmetic (v_dot2 plus the cross-lane reduction) takes longer
+// than a microsecond per CU and it all happens after the last weights
+// arrive.  One v_mfma_f32_16x16x32_bf16 does the multiply-adds of a
+// 16 x 32 x 16 block and the reduction over its 32 k-slots in the matrix
+// unit, so the work left after the stream is a handful of instructions.
+//
+// Instruction layout (gfx950): D[16 x 16] += A[16 x 32] . B[32 x 16].  Lane
+// l supplies A's row l%16 and B's column l%16 with eight bf16 values of
+// k-slot group g = l/16 (k-slots 8g .. 8g+7); lane l receives D[4g + v][l%16]
+// for v = 0..3.  The product sums over the 32 k-slots, so any element of K
+// may sit in a k-slot as long as A and B carry the same one there.
+//
+// K-slice packing (two sub-slices).  With at most 8 tokens, half of the 16
+// B columns would be idle, so the tile is 8 weight rows x 2 sub-slices of
+// K: A row s*8 + r is weight row r on sub-slice s, B column s*8 + m is
+// token m on sub-slice s.  The useful outputs are the two diagonal 8 x 8
+// blocks D[s*8 + r][s*8 + m]; their sum over s is row r, token m.  At one
+// MFMA step t of a wave, the lane of k-slot group g on sub-slice s reads the
+// 16-byte chunk
+//     c = c0 + 8t + 2g + s
+// of its row (c0 = first chunk of the wave's K range), so the eight lanes of
+// one weight row read 128 contiguous bytes and the wave-wide load covers 8
+// rows x 128 B; every weight byte is loaded once, non-temporally, as stored
+// (no re-laid-out copy: writes through the projection views stay valid).
+//
+// Work split.  A workgroup owns G row groups of RT <= 8 rows (a tile with
+// RT < 8 leaves its last A rows unused; the 1792-row fused launch uses 7
+// rows per workgroup so that its 256 workgroups cover the 256 CUs once).
+// The PK waves of a row group split K into PK parts of KT steps (8 chunks
+// each).  All of a wave's weight and activation loads are issued before its
+// first MFMA, and the steps consume them in issue order.
+//
+// Reduction order, fixed by (K, PK, KT): MFMA steps in order inside a wave
+// (the matrix unit's own order inside a step); then per output, through
+// LDS, each sub-slice over the PK waves in wave order, then the two
+// sub-slice sums added.  It does
+// not depend on the row's position in the tile, on RT, G or the rows of
+// the launch, so the fused launch and the one-launch-per-projection path are
+// bitwise equal, as are repeats and graph replays.
+#pragma once
+
+#include "common.hpp"
+
+namespace fp {
+
+constexpr int smfma_max_threads(int kt) {
+  return max_threads_for_regs(8 * kt + 24);
+}
+
+// Leading scalars preloaded into SGPRs (see skinny_kernel for w, x, y0,
+// y1, ldx, n_rows, kc, M, split); geo = RT | PK << 8 | G << 16.
+template <int KT>
+__global__ void __launch_bounds__(smfma_max_threads(KT))
+smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
+             unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
+             int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
+  extern __shared__ float smem[];  // [G][2][8][8][16]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int RT = geo & 0xff;
+  const int PK = (geo >> 8) & 0xff;
+  const int Gv = geo >> 16;
+  const int p = Gv == 1 ? wave : wave % PK;
+  const int g2 = Gv == 1 ? 0 : wave / PK;
+  const int row_base = (int)blockIdx.x * (Gv * RT);
+  const int row0 = row_base + g2 * RT;
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const int sub = i16 >> 3;   // sub-slice of this lane's A row and B column
+  const int r8 = i16 & 7;     // A: weight row in the tile; B: token
+  const int c0 = p * (8 * KT) + 2 * g + sub;  // chunk of step 0
+  const uint32_t row_bytes = (uint32_t)kc * 16u;
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+
+  // 1. activations (token r8, clamped to a valid row and zeroed later),
+  //    then the weights (row r8 of the tile, clamped to the launch): all
+  //    loads issued before the first MFMA
+  u32x4 xv[KT];
+  {
+    const int mc = r8 < M ? r8 : M - 1;
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const int c = c0 + 8 * t;
+      xv[t] = xrow[c < kc ? c : kc - 1];
+    }
+  }
+  u32x4 wv[KT];
+  {
+    const int rr = r8 < RT ? row0 + r8 : row0;
+    const int row = rr < n_rows ? rr : n_rows - 1;
+    const u32x4* wrow = reinterpret_cast<const u32x4*>(w + (uint64_t)(uint32_t)row * row_bytes);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const int c = c0 + 8 * t;
+      wv[t] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
+  __builtin_amdgcn_sched_barrier(0);
+  const bool tok_ok = r8 < M;
+
+  // 2. MFMA steps in order; chunks past K contribute zero
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    __builtin_amdgcn_sched_barrier(0);
+    const bool c_ok = c0 + 8 * t < kc;
+    const bf16x8 A = u4bf8(c_ok ? wv[t] : zero4);
+    const bf16x8 B = u4bf8(c_ok && tok_ok ? xv[t] : zero4);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. the diagonal blocks to LDS: lane (i16, g) holds D[4g + v][i16]; the
+  //    D row's sub-slice is (4g + v) / 8 = g / 2, the column's is i16 / 8.
+  //    Layout [G][sub-slice][row][token][16 wave slots]: the PK wave sums of
+  //    one (sub-slice, row, token) are contiguous.
+  if ((g >> 1) == sub) {
+    float* red = smem + ((g2 * 2 + sub) * 64 + r8) * kMaxWaveParts + p;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = (4 * g + v) & 7;
+      red[r * 8 * kMaxWaveParts] = acc[v];
+    }
+  }
+  __syncthreads();
+
+  // 4. one thread per output: each sub-slice over the PK waves in wave
+  //    order, then sub-slice 0 + sub-slice 1
+  const int n_out = Gv * 64;
+  if (tid < n_out) {
+    const int gg = tid >> 6;
+    const int r = (tid >> 3) & 7;
+    const int m = tid & 7;
+    const int row = row_base + gg * RT + r;
+    if (r < RT && m < M && row < n_rows) {
+      const float* q0 = smem + ((gg * 2 + 0) * 64 + r * 8 + m) * kMaxWaveParts;
+      const float* q1 = smem + ((gg * 2 + 1) * 64 + r * 8 + m) * kMaxWaveParts;
+      const float sum = sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK);
+      store_y<true>(om, a.out, row, m, sum);
+    }
+  }
+}
+
+}  // namespace fp

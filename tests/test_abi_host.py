@@ -144,6 +144,10 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
         if path == P.FP_PATH_MFMA:
             assert S * kp * ch * 16 >= kc
             assert M > 8 or M >= 9
+        elif path == P.FP_PATH_MFMA_SMALL:
+            assert dtype == 0 and 2 <= M <= 8
+            assert S == 1 and kp <= 16 and kp * ch * 8 >= kc
+            assert 1 <= rows <= 8 and groups >= 1
         else:
             assert M <= 8
             assert S * kp * 64 * ch >= kc
@@ -153,8 +157,10 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
 
 
 def test_default_crossover():
-    # skinny kernel up to M = 8, MFMA tiles above
+    # vector-ALU kernel up to M = 8 (bf16 and fp32), MFMA tiles above
     for M in range(1, 9):
-        assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] in (1, 2)
+        assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_SKINNY
+    for M in range(1, 9):
+        assert P.fp_default_tiling(1, 7168, 192, M, 192)[1][0] in (1, 2)
     for M in (9, 16, 32, 64, 128):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA

@@ -177,6 +177,10 @@ def test_tilings_all_pass(M):
         (P.FP_PATH_MFMA, 5, 2, 1, 2, 4),    # 4-row tiles, 4 K sub-slices
         (P.FP_PATH_MFMA, 5, 1, 2, 1, 4),    # with a K split
         (P.FP_PATH_MFMA, 4, 2, 3, 2, 2),    # uneven K coverage
+        (P.FP_PATH_MFMA_SMALL, 10, 8, 1, 0, 0),
+        (P.FP_PATH_MFMA_SMALL, 5, 16, 1, 8, 1),
+        (P.FP_PATH_MFMA_SMALL, 5, 16, 1, 3, 2),  # two row groups of 3 rows
+        (P.FP_PATH_MFMA_SMALL, 16, 8, 1, 1, 0),  # more K parts than needed
     ]
     ran = 0
     for t in tilings:
@@ -186,7 +190,7 @@ def test_tilings_all_pass(M):
             # tokens are refused
             assert st == P.FP_ERR_UNSUPPORTED, (t, st)
             assert ((t[0] != P.FP_PATH_MFMA and (M > 8 or (t[2] > 2 and M > 2)))
-                    or (t[5] > 1 and M > 16 // t[5])), (t, st)
+                    or (t[0] == P.FP_PATH_MFMA and t[5] > 1 and M > 16 // t[5])), (t, st)
             continue
         ran += 1
         ys = fp(xg)
@@ -249,3 +253,30 @@ def test_single_row_projections_and_one_projection():
     _check_case(_plan(ws), x, ws, "one row")
     x, ws = si.make_case(5120, (1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1), "bf16", 3, seed=9)
     _check_case(_plan(ws), x, ws, "16 single-row projections")
+
+
+# ---- the small-M matrix-core kernel (opt-in tiling) on every workload shape
+def _small_mfma_tiling(K, esize=2):
+    kc = K * esize // 16
+    steps = -(-kc // 8)
+    kt = 4 if steps <= 64 else 8 if steps <= 128 else 16
+    return (P.FP_PATH_MFMA_SMALL, -(-steps // kt), kt, 1, 0, 0)
+
+
+@pytest.mark.parametrize("case", ["wq_a+wkv", "fused_a_3way", "ragged", "single_rows", "k8"])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+def test_small_mfma_path(case, M):
+    if case == "wq_a+wkv":
+        x, ws = si.workload_case("wq_a+wkv_m2_8", M, 1)
+    elif case == "fused_a_3way":
+        x, ws = si.workload_case("fused_a_3way", M, 0)
+    elif case == "ragged":
+        x, ws = si.make_case(136, (37, 5, 70, 1), "bf16", M, seed=60 + M)
+    elif case == "single_rows":
+        x, ws = si.make_case(1024, (1,) * 16, "bf16", M, seed=61 + M)
+    else:
+        x, ws = si.make_case(8, (300, 29), "bf16", M, seed=62 + M)
+    fp = _plan(ws)
+    assert fp.set_tiling(M, _small_mfma_tiling(fp.K)) == P.FP_OK
+    assert fp.query(M)[0] == P.FP_PATH_MFMA_SMALL
+    _check_case(fp, x, ws, "small-M MFMA %s M=%d" % (case, M))
