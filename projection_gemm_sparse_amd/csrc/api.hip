@@ -19,9 +19,9 @@
 #include <unordered_set>
 
 #include "../../include/fusedproj.h"
-#include "mfma.hpp"
 #include "skinny.hpp"
 #include "smfma.hpp"
+#include "tile.hpp"
 
 namespace {
 
@@ -120,29 +120,87 @@ void default_skinny_order(int32_t dtype, int64_t kc, int64_t n_total, int mt,
   (void)dtype;
 }
 
-// MFMA order fields: Q (k-slice packing, kept in `groups`), PK, KTW, S.
-void default_mfma_order(int64_t kc, int64_t M, Tiling* t) {
-  const int64_t kt = ceil_div(kc, 16);  // 128-wide k tiles
-  int Q, KTW;
-  int64_t PK;
-  if (M <= 4) {
-    Q = 4; KTW = 2;    // 4-row tiles, 4 K sub-slices
-  } else if (M <= 8) {
-    Q = 2; KTW = 2;    // 8-row tiles, 2 K sub-slices
-  } else {
-    Q = 1; KTW = 2;
+// Tile (MFMA) kernel.  The order field is S, the k-step slices across
+// workgroups (chosen from K and the M bucket only); the launch fields are
+// NW, the 16-row tiles per workgroup, and the compiled slice bound (k steps
+// staged in LDS per wave: CS steps per chunk times C chunks).
+constexpr int kTilePers[] = {8, 10, 16, 20, 40};  // compiled slice bounds (k steps)
+constexpr int kTileNws[] = {2, 4, 8};
+
+int tile_per_bound(int64_t per) {
+  for (int b : kTilePers)
+    if (per <= b) return b;
+  return 0;
+}
+
+// Chunking of a compiled register bound: CS steps per chunk, C chunks.
+void tile_chunks(int bound, int* cs, int* c) {
+  *cs = (bound == 8 || bound == 16) ? 4 : 5;
+  *c = bound / *cs;
+}
+
+size_t tile_lds(int mt16, int64_t per, int nw) {
+  const int b = tile_per_bound(per);
+  if (b == 0) return SIZE_MAX;
+  int cs, c;
+  tile_chunks(b, &cs, &c);
+  return (size_t)fp::tile_slots(mt16, (int)per, nw, cs, c) * 16;
+}
+
+// Resident workgroups per CU for a tile launch (LDS and wave slots).
+int64_t tile_resident(int mt16, int64_t per, int nw) {
+  const size_t lds = std::max<size_t>(tile_lds(mt16, per, nw), 16);
+  return std::max<int64_t>(1, std::min<int64_t>((int64_t)(kMaxLds / lds), 16 / nw));
+}
+
+// Best NW for a launch of n_rows rows with S slices (0 if none fits): one
+// round of workgroups, as many busy CUs as possible, then fewer rows per CU.
+// NW for a launch with S slices: four row tiles per workgroup (eight from
+// 128 tokens) when that fits in LDS, else the largest that does (0: none).
+int tile_pick_nw(int mt16, int64_t n_steps, int64_t S, int64_t n_rows) {
+  (void)n_rows;
+  const int64_t per = ceil_div(n_steps, S);
+  const int pref = mt16 >= 8 ? 8 : 4;
+  if (tile_lds(mt16, per, pref) <= kMaxLds) return pref;
+  for (int nw : {8, 4, 2})
+    if (tile_lds(mt16, per, nw) <= kMaxLds) return nw;
+  return 0;
+}
+
+bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
+  (void)n_total;
+  const int mt16 = mfma_mt16(M);
+  const int64_t n_steps = ceil_div(kc, 4);
+  // Measured on MI355X (K = 5120, 1792 rows): four row tiles per workgroup
+  // (eight from 128 tokens), and the fewest slices whose slice fills a
+  // compiled slice bound nearly (no wasted LDS rows) and fits in LDS.  The
+  // choice depends on (K, M bucket) only, so every launch of a plan adds
+  // the same slices in the same order.
+  const int nw = mt16 >= 8 ? 8 : 4;
+  int64_t pick = 0;
+  for (int64_t S = 1; S <= n_steps && S <= 0x1fff; ++S) {
+    const int64_t per = ceil_div(n_steps, S);
+    const int b = tile_per_bound(per);
+    if (b == 0 || per + 2 < b) continue;
+    if (tile_lds(mt16, per, nw) > kMaxLds) continue;
+    pick = S;
+    break;
   }
-  if (M <= 32) {
-    // up to 10 waves split K inside the workgroup
-    PK = std::min<int64_t>(10, ceil_div(kt, (int64_t)Q * KTW));
-  } else {
-    PK = 1;            // 8 row groups share activations staged in LDS
+  if (pick == 0) {
+    // short K or odd shapes: any slice count that fits
+    for (int64_t S = 1; S <= n_steps && S <= 0x1fff && pick == 0; ++S) {
+      const int64_t per = ceil_div(n_steps, S);
+      if (tile_per_bound(per) == 0) continue;
+      for (int w : kTileNws)
+        if (tile_lds(mt16, per, w) <= kMaxLds) pick = S;
+    }
   }
+  if (pick == 0) return false;
   t->path = FP_PATH_MFMA;
-  t->groups = Q;
-  t->kparts = (int)PK;
-  t->chunks = KTW;
-  t->splits = (int)ceil_div(kt, PK * Q * KTW);
+  t->splits = (int)pick;
+  t->kparts = 0;  // NW, per launch
+  t->chunks = 0;  // register bound, per launch
+  return true;
 }
 
 // Small-M matrix-core order fields: PK waves of KT steps (8 chunks each).
@@ -229,12 +287,6 @@ size_t smfma_lds(const Tiling& t) {
   return (size_t)t.groups * 2 * 64 * fp::kMaxWaveParts * 4;
 }
 
-bool mfma_xlds(const Tiling& t) { return t.groups == 1 && (t.rows > 1 || t.mt >= 4); }
-
-void resolve_mfma_rows(int mt16, Tiling* t) {
-  if (t->rows <= 0) t->rows = mt16 >= 4 ? 8 : 1;
-}
-
 size_t skinny_lds(const Tiling& t) {
   const int V = t.rows * t.mt;
   int VP = 1;
@@ -242,18 +294,21 @@ size_t skinny_lds(const Tiling& t) {
   return (size_t)t.groups * VP * fp::kMaxWaveParts * 4 + 16;
 }
 
-size_t mfma_lds(const Tiling& t) {
-  const int Q = t.groups;
-  const size_t pitch = (size_t)t.kparts * Q * t.chunks * 16 + 1;  // Q == 1 when staged
-  const size_t xs = mfma_xlds(t) ? (size_t)16 * t.mt * pitch * 16 : 0;
-  const size_t rt = 16 / Q, mc = Q == 1 ? 16 : 16 / Q;
-  const size_t red = (size_t)t.rows * t.kparts * Q * t.mt * rt * mc * 4;
-  return std::max(xs, red) + 16;  // the reduction reuses the staging space
+void resolve_tile_launch(const fp_plan_s* p, int64_t n_rows, Tiling* t) {
+  const int64_t n_steps = ceil_div(p->kc, 4);
+  const int64_t per = ceil_div(n_steps, std::max(1, t->splits));
+  if (t->kparts <= 0) t->kparts = tile_pick_nw(t->mt, n_steps, t->splits, n_rows);
+  if (t->chunks <= 0) t->chunks = tile_per_bound(per);
+  t->rows = 1;    // unused by the tile kernel
+  t->groups = 1;
 }
 
 // Partial-sum floats a tiling needs for a launch of n_rows rows and M tokens.
 int64_t partial_floats(const Tiling& t, int64_t n_rows, int64_t M) {
-  return t.splits > 1 ? (int64_t)t.splits * n_rows * M : 0;
+  if (t.splits <= 1) return 0;
+  // the tile kernel keeps 16-token-aligned partial rows
+  const int64_t mcols = t.path == FP_PATH_MFMA ? 16 * (int64_t)mfma_mt16(M) : M;
+  return (int64_t)t.splits * n_rows * mcols;
 }
 
 bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t) {
@@ -261,17 +316,17 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
   // packed into 8- and 16-bit fields of the kernels' scalar arguments
   if (t.splits > 0x1fff || t.kparts > 0xff || t.rows > 0xff || t.groups > 0xff) return false;
   if (t.path == FP_PATH_MFMA) {
-    const int Q = t.groups;
     if (p->dtype != FP_BF16) return false;
-    if (!(Q == 1 || Q == 2 || Q == 4 || Q == 8)) return false;
-    if (Q > 1 && (t.mt != 1 || M > 16 / Q)) return false;
-    if (!(t.chunks == 1 || t.chunks == 2 || t.chunks == 4)) return false;
-    if (!mfma_xlds(t) && t.mt > 2) return false;
-    if ((int64_t)t.rows * t.kparts * 64 > fp::mfma_max_threads(t.mt, t.chunks, mfma_xlds(t)))
-      return false;
-    if ((int64_t)t.splits * t.kparts * Q * t.chunks * 16 < p->kc) return false;
-    if (mfma_lds(t) > kMaxLds) return false;
+    const int64_t n_steps = ceil_div(p->kc, 4);
+    const int64_t per = ceil_div(n_steps, t.splits);
+    bool nw_ok = false, per_ok = false;
+    for (int nw : kTileNws) nw_ok = nw_ok || nw == t.kparts;
+    for (int b : kTilePers) per_ok = per_ok || b == t.chunks;
+    if (!nw_ok || !per_ok || per > t.chunks) return false;
+    if (tile_lds(t.mt, per, t.kparts) > kMaxLds) return false;
     if (16 * (int64_t)t.mt < M) return false;
+    // buffer offsets are 32-bit
+    if ((int64_t)t.splits * n_rows * 16 * t.mt * 4 >= ((int64_t)1 << 31)) return false;
   } else if (t.path == FP_PATH_MFMA_SMALL) {
     if (p->dtype != FP_BF16 || M > kSkinnyMaxM) return false;
     if (!(t.chunks == 4 || t.chunks == 8 || t.chunks == 16)) return false;
@@ -313,13 +368,12 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t) {
     if (t->path == FP_PATH_SKINNY || t->path == FP_PATH_SKINNY_SPLITK) {
       t->path = t->splits > 1 ? FP_PATH_SKINNY_SPLITK : FP_PATH_SKINNY;
     }
-    if (t->path == FP_PATH_MFMA && t->groups <= 0) t->groups = 1;
   } else {
     const bool mfma = p->dtype == FP_BF16 && (M >= p->mfma_min_m || M > kSkinnyMaxM);
     const bool small = p->dtype == FP_BF16 && !mfma && M >= p->small_mfma_min_m &&
                        default_smfma_order(p->kc, t);
     if (mfma) {
-      default_mfma_order(p->kc, M, t);
+      if (!default_mfma_order(p->kc, M, p->n_total, t)) return false;
     } else if (small) {
       // order fields already set
     } else {
@@ -329,7 +383,8 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t) {
   }
   if (t->path == FP_PATH_MFMA) {
     t->mt = mfma_mt16(M);
-    resolve_mfma_rows(t->mt, t);
+    if (t->splits < 1) return false;
+    resolve_tile_launch(p, n_rows, t);
   } else if (t->path == FP_PATH_MFMA_SMALL) {
     t->mt = 8;
     if (t->kparts < 1 || t->chunks < 1) return false;
@@ -377,7 +432,7 @@ size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) 
   if (dtype == FP_BF16) {
     for (int64_t M = 1; M <= max_M; ++M) {
       Tiling t;
-      default_mfma_order(tmp.kc, M, &t);
+      if (!default_mfma_order(tmp.kc, M, n_total, &t)) continue;
       most = std::max(most, partial_floats(t, n_total, M));
     }
   }
@@ -443,35 +498,35 @@ const void* skinny_fn_mt(int mt, int cj, int rw) {
   }
 }
 
-template <int Q, int MT16, bool XLDS>
-const void* mfma_fn_ktw(int ktw) {
-  switch (ktw) {
-    case 1: return reinterpret_cast<const void*>(&fp::mfma_kernel<Q, MT16, 1, XLDS>);
-    case 2: return reinterpret_cast<const void*>(&fp::mfma_kernel<Q, MT16, 2, XLDS>);
-    case 4: return reinterpret_cast<const void*>(&fp::mfma_kernel<Q, MT16, 4, XLDS>);
+template <int MT16, int NW>
+const void* tile_fn_per(int per) {
+  switch (per) {
+    case 8: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 4, 2>);
+    case 10: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 5, 2>);
+    case 16: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 4, 4>);
+    case 20: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 5, 4>);
+    case 40: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 5, 8>);
+    default: return nullptr;
+  }
+}
+
+template <int MT16>
+const void* tile_fn_nw(int nw, int per) {
+  switch (nw) {
+    case 2: return tile_fn_per<MT16, 2>(per);
+    case 4: return tile_fn_per<MT16, 4>(per);
+    case 8: return tile_fn_per<MT16, 8>(per);
     default: return nullptr;
   }
 }
 
 const void* mfma_fn(const Tiling& t) {
-  const int ktw = t.chunks;
-  if (t.groups == 8) return t.mt == 1 ? mfma_fn_ktw<8, 1, false>(ktw) : nullptr;
-  if (t.groups == 4) return t.mt == 1 ? mfma_fn_ktw<4, 1, false>(ktw) : nullptr;
-  if (t.groups == 2) return t.mt == 1 ? mfma_fn_ktw<2, 1, false>(ktw) : nullptr;
-  if (t.groups != 1) return nullptr;
-  if (mfma_xlds(t)) {
-    switch (t.mt) {
-      case 1: return mfma_fn_ktw<1, 1, true>(ktw);
-      case 2: return mfma_fn_ktw<1, 2, true>(ktw);
-      case 4: return mfma_fn_ktw<1, 4, true>(ktw);
-      case 8: return mfma_fn_ktw<1, 8, true>(ktw);
-      case 16: return mfma_fn_ktw<1, 16, true>(ktw);
-      default: return nullptr;
-    }
-  }
   switch (t.mt) {
-    case 1: return mfma_fn_ktw<1, 1, false>(ktw);
-    case 2: return mfma_fn_ktw<1, 2, false>(ktw);
+    case 1: return tile_fn_nw<1>(t.kparts, t.chunks);
+    case 2: return tile_fn_nw<2>(t.kparts, t.chunks);
+    case 4: return tile_fn_nw<4>(t.kparts, t.chunks);
+    case 8: return tile_fn_nw<8>(t.kparts, t.chunks);
+    case 16: return tile_fn_nw<16>(t.kparts, t.chunks);
     default: return nullptr;
   }
 }
@@ -569,11 +624,11 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
                   args, stream);
   }
   if (t.path == FP_PATH_MFMA) {
-    const int ktw_log2 = t.chunks == 4 ? 2 : t.chunks == 2 ? 1 : 0;
-    geo_a = t.rows | (t.kparts << 8) | (ktw_log2 << 16) | (t.splits << 18);
-    const int64_t rows_per_block = (16 / t.groups) * (int64_t)t.rows;
-    const int64_t blocks = ceil_div(lr.n_rows, rows_per_block) * t.splits;
-    return launch(mfma_fn(t), blocks, t.rows * t.kparts * 64, mfma_lds(t), args, stream);
+    geo_a = t.splits;
+    const int64_t per = ceil_div(ceil_div(p->kc, 4), t.splits);
+    const int64_t blocks = ceil_div(lr.n_rows, 16 * (int64_t)t.kparts) * t.splits;
+    const size_t lds = std::max<size_t>(tile_lds(t.mt, per, t.kparts), 16);
+    return launch(mfma_fn(t), blocks, t.kparts * 64, lds, args, stream);
   }
   geo_a = t.kparts | (t.groups << 8) | (t.splits << 16);
   const int64_t R = (int64_t)t.groups * t.rows;

@@ -69,9 +69,6 @@ constexpr int skinny_max_threads(int mt, int rw, int cj) {
   return max_threads_for_regs(pow2ceil(rw * mt) + 4 * rw * cj + 4 * mt * cj + 32);
 }
 
-constexpr int mfma_max_threads(int mt16, int ktw, bool xlds) {
-  return max_threads_for_regs(16 * ktw + 4 * mt16 + (xlds ? 8 : 16 * ktw * mt16) + 24);
-}
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

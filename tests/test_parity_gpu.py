@@ -168,15 +168,13 @@ def test_tilings_all_pass(M):
         (P.FP_PATH_SKINNY, 1, 10, 1, 1, 7),  # whole rows per wave, no barrier
         (P.FP_PATH_SKINNY, 1, 10, 1, 2, 3),
         (P.FP_PATH_SKINNY, 2, 5, 1, 1, 5),
-        (P.FP_PATH_MFMA, 4, 2, 5, 1, 0),
-        (P.FP_PATH_MFMA, 1, 4, 10, 4, 0),
-        (P.FP_PATH_MFMA, 2, 1, 20, 2, 0),
-        (P.FP_PATH_MFMA, 8, 1, 5, 1, 0),
-        (P.FP_PATH_MFMA, 10, 4, 1, 1, 1),   # whole K in one workgroup
-        (P.FP_PATH_MFMA, 10, 2, 1, 1, 2),   # 8-row tiles, 2 K sub-slices
-        (P.FP_PATH_MFMA, 5, 2, 1, 2, 4),    # 4-row tiles, 4 K sub-slices
-        (P.FP_PATH_MFMA, 5, 1, 2, 1, 4),    # with a K split
-        (P.FP_PATH_MFMA, 4, 2, 3, 2, 2),    # uneven K coverage
+        (P.FP_PATH_MFMA, 2, 40, 4, 0, 0),   # tile kernel: row tiles, register
+        (P.FP_PATH_MFMA, 4, 20, 8, 0, 0),   # bound of k steps, slices
+        (P.FP_PATH_MFMA, 8, 8, 20, 0, 0),
+        (P.FP_PATH_MFMA, 2, 8, 20, 0, 0),
+        (P.FP_PATH_MFMA, 2, 40, 5, 0, 0),
+        (P.FP_PATH_MFMA, 2, 20, 9, 0, 0),   # uneven slices (160 steps / 9)
+        (P.FP_PATH_MFMA, 2, 8, 160, 0, 0),  # one k step per slice
         (P.FP_PATH_MFMA_SMALL, 10, 8, 1, 0, 0),
         (P.FP_PATH_MFMA_SMALL, 5, 16, 1, 8, 1),
         (P.FP_PATH_MFMA_SMALL, 5, 16, 1, 3, 2),  # two row groups of 3 rows
@@ -190,7 +188,7 @@ def test_tilings_all_pass(M):
             # tokens are refused
             assert st == P.FP_ERR_UNSUPPORTED, (t, st)
             assert ((t[0] != P.FP_PATH_MFMA and (M > 8 or (t[2] > 2 and M > 2)))
-                    or (t[0] == P.FP_PATH_MFMA and t[5] > 1 and M > 16 // t[5])), (t, st)
+                    or (t[0] == P.FP_PATH_MFMA and M <= 8)), (t, st)
             continue
         ran += 1
         ys = fp(xg)
