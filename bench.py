@@ -15,14 +15,25 @@ the eight graphs (M = 1..8).  W warm-up steps, then K timed steps between
 HIP events on the launch stream, bracketed by device synchronizations.
 
 Reported: ``value`` = algorithmic bytes (W_cat + x + y per call, summed over
-the step) / step time, in GB/s; ``roofline`` for the fused skinny kernel
-against the 8 TB/s HBM peak; per-M microseconds per call for the fused and
-the one-launch-per-projection path; ``cpu_baseline`` = the CPU oracle
-(single thread) on one pass of the same M sweep over one copy.
+the step) / step time, in GB/s; ``roofline`` for the dominant kernel (the
+kernel instantiation with the most time in the step): its algorithmic bytes
+per launch over its average launch duration (HIP events over the timed
+region, on the launch stream), against the 8 TB/s HBM peak, with the HBM
+traffic per launch measured by rocprofv3 counters when the recorded
+measurement (profiles/traffic.json) matches the current kernel sources;
+per-M microseconds per call for the fused and the one-launch-per-projection
+path; ``cpu_baseline`` = the CPU oracle (single thread) on a bounded sample
+of the same M sweep over one copy.
+
+``--crossover FILE`` additionally times, per token count M in
+{1, 2, 4, 8, 9, 16, 32, 64, 128}, every kernel path that serves M (vector
+ALU, small-M matrix core, tile) on the same rotated pool and writes the
+table to FILE: the measured crossover that places the MFMA path.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -42,6 +53,41 @@ N = (1280, 512)
 MS = (1, 2, 3, 4, 5, 6, 7, 8)
 
 
+KERNEL_SOURCES = ("projection_gemm_sparse_amd/csrc/common.hpp",
+                  "projection_gemm_sparse_amd/csrc/skinny.hpp",
+                  "projection_gemm_sparse_amd/csrc/smfma.hpp",
+                  "projection_gemm_sparse_amd/csrc/tile.hpp",
+                  "projection_gemm_sparse_amd/csrc/api.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter record,
+    or None when there is none or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_sha256_16") != kernel_sources_digest():
+        return None
+    ent = rec.get("kernels", {}).get(kernel)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def skinny_kernel_name(M: int) -> str:
+    mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
+    return "fp::skinny_kernel<%d, 7, 1, true>" % mt
+
+
 def algorithmic_bytes(M: int, K: int, N, esize: int = 2) -> int:
     n_total = sum(N)
     return esize * (n_total * K + M * K + M * n_total)
@@ -57,7 +103,7 @@ def build_pool(P, torch, n_copies, max_M, seed=0):
     for _ in range(n_copies):
         ws = [((torch.rand(n, K, generator=g, device="cuda") * 2 - 1) * a)
               .to(torch.bfloat16) for n in N]
-        plans.append(P.FusedProjection(ws, max_M=max(MS)))
+        plans.append(P.FusedProjection(ws, max_M=max_M))
         del ws
     return plans
 
@@ -119,6 +165,47 @@ def cpu_baseline(plan0_weights_cpu, xs_cpu, budget_s=12.0):
             "us_per_call": el / (passes * len(MS)) * 1e6}
 
 
+def crossover(path, P, torch, dev, plans, n_copies):
+    """Per token count, every kernel path that serves it, on the rotated
+    pool (plans are made for max_M = 8, so this builds a second pool)."""
+    import synthetic_inputs as si
+    del plans
+    torch.cuda.empty_cache()
+    big = build_pool(P, torch, n_copies, 128)
+    rows = []
+    for M in (1, 2, 4, 8, 9, 16, 32, 64, 128):
+        xc, _ = si.make_case(K, N, "bf16", M, seed=200 + M)
+        x = xc.to(dev)
+        out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
+        cands = [("default", None)]
+        if M <= 8:
+            kc = K * 2 // 16
+            steps = -(-kc // 8)
+            kt = 4 if steps <= 64 else 8 if steps <= 128 else 16
+            cands += [("skinny", (P.FP_PATH_SKINNY, 10, 1, 1, 0, 0)),
+                      ("mfma_small", (P.FP_PATH_MFMA_SMALL, -(-steps // kt), kt, 1, 0, 0))]
+        for name, t in cands:
+            if t is not None and any(p.set_tiling(M, t) for p in big):
+                for p in big:
+                    p.set_tiling(M, None)
+                continue
+            g = capture(torch, lambda: [p.forward(x, out=out) for p in big])
+            ms, _ = time_graphs(torch, [g], 10, 2)
+            us = ms * 1e3 / (10 * n_copies)
+            b = algorithmic_bytes(M, K, N)
+            rows.append({"M": M, "variant": name,
+                         "path": P._lib.PATH_NAMES[big[0].query(M)[0]],
+                         "tiling": list(big[0].get_tiling(M)), "us": round(us, 3),
+                         "GBps": round(b / us / 1e3, 1)})
+            print("bench: crossover %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            for p in big:
+                p.set_tiling(M, None)
+            del g
+    with open(path, "w") as fh:
+        json.dump({"workload": "wq_a+wkv [1280,512]x5120 bf16, %d rotated copies" % n_copies,
+                   "rows": rows}, fh, indent=1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +217,8 @@ def main():
     ap.add_argument("--details", default="", help="write per-M details JSON here")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--crossover", default="",
+                    help="also time every kernel path per M in 1..128 and write the table here")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -188,6 +277,7 @@ def main():
         us = per_ms[i] * 1e3 / calls
         b = algorithmic_bytes(M, K, N)
         step_bytes += b * n_copies
+        tl = plans[0].get_tiling(M)
         per_m[str(M)] = {
             "fused_us": round(us, 4),
             "separate_us": round(sep_ms[i] * 1e3 / (sep_steps * n_copies), 4),
@@ -195,15 +285,20 @@ def main():
             "fused_GBps": round(b / us / 1e3, 1),
             "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
             "path": P._lib.PATH_NAMES[plans[0].query(M)[0]],
+            "tiling": list(tl),
+            "kernel": skinny_kernel_name(M) if tl[0] in (P.FP_PATH_SKINNY,) and tl[4] == 7
+                      and tl[2] == 1 else None,
         }
     ms_per_step = total_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     if args.calib_copy_mib:
-        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        # counter calibration: an elementwise kernel that reads and writes
+        # exactly calib_copy_mib MiB (bf16 negation)
+        src = torch.ones((args.calib_copy_mib << 20) // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
     # sanity check of one call against a plain PyTorch fp32 product (outside
@@ -226,6 +321,32 @@ def main():
         w0 = [v.cpu() for v in plans[0].views]
         cpu = cpu_baseline(w0, xs_cpu)
 
+    # dominant kernel: the instantiation with the most time in the step
+    by_kernel = {}
+    for M in MS:
+        e = per_m[str(M)]
+        k = e["kernel"] or ("%s %s" % (e["path"], e["tiling"]))
+        t_us, b_sum, n = by_kernel.get(k, (0.0, 0, 0))
+        by_kernel[k] = (t_us + e["fused_us"], b_sum + e["bytes"], n + 1)
+    dom = max(by_kernel, key=lambda k: by_kernel[k][0])
+    t_us, b_sum, n_m = by_kernel[dom]
+    achieved = b_sum / t_us / 1e3  # GB/s: bytes per launch / average launch duration
+    traffic = recorded_traffic(dom)
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "launch_us": round(t_us / n_m, 4),
+        "bytes_per_launch": round(b_sum / n_m),
+        "note": "per launch, over the token counts this kernel serves in the step; launch "
+                "duration = timed region / launches (HIP events on the launch stream); "
+                "traffic = HBM bytes per launch from rocprofv3 counters (null if the "
+                "kernel changed since they were taken)",
+    }
     us_all = [per_m[str(M)]["fused_us"] for M in MS]
     line = {
         "metric": METRIC,
@@ -256,19 +377,14 @@ def main():
             "GBps_M1_8": round(step_bytes / ((ms_per_step * 1e-3) / 1.0 -
                                              floor_us * 1e-6 * n_copies * len(MS)) / 1e9, 1),
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(value, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(value / HBM_PEAK_GBS, 4),
-            "traffic": None,
-        },
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "per_m": per_m,
         "context": {"pages_sm107_fused_m1_us": 4.13,
                     "note": "Vera Rubin figure from the pages, other hardware"},
     }
+    if args.crossover:
+        crossover(args.crossover, P, torch, dev, plans, n_copies)
     print(json.dumps(line), flush=True)
     if args.details:
         with open(args.details, "w") as fh:

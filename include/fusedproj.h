@@ -162,26 +162,27 @@ fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
 
 /* Tiling of one token count (benchmarking and testing aid).  Every tiling
  * the kernels accept gives results within the same error bound; the
- * summation order, hence the exact bits, depends on path, kparts, chunks,
- * splits and (mfma) groups -- never on rows or the skinny groups -- so fused
- * and separate calls of one plan stay bitwise equal under any tiling.
+ * summation order, hence the exact bits, depends on path and the order
+ * fields (skinny: kparts, chunks, splits; mfma-small: kparts, chunks;
+ * mfma: splits) -- never on rows, groups or the tile kernel's kparts and
+ * chunks -- so fused and separate calls of one plan stay bitwise equal
+ * under any tiling.
  *   path    FP_PATH_SKINNY / FP_PATH_SKINNY_SPLITK (same kernel; the
  *           splits field decides), FP_PATH_MFMA_SMALL (bf16, M <= 8) or
- *           FP_PATH_MFMA (bf16 only)
- *   kparts  skinny: waves splitting one K slice (P); mfma and mfma-small:
- *           waves splitting K (PK, at most 16)
+ *           FP_PATH_MFMA (the tile kernel, bf16)
+ *   kparts  skinny: waves splitting one K slice (P, <= 16); mfma-small:
+ *           waves splitting K (PK, <= 16); mfma: 16-row tiles per
+ *           workgroup (2, 4 or 8; 0 = chosen per launch)
  *   chunks  skinny: 16-byte chunks per lane and row (CJ, 1..2);
- *           mfma: 128-wide k tiles per wave and K sub-slice (KTW: 1, 2, 4);
- *           mfma-small: MFMA steps of 64 k per wave (KT: 4, 8, 16)
+ *           mfma-small: MFMA steps of 64 k per wave (KT: 4, 8, 16);
+ *           mfma: compiled bound of 32-wide k steps per slice (8, 10, 16,
+ *           20 or 40, at least ceil(ceil(K/32) / splits); 0 = smallest)
  *   splits  K slices across workgroups (S >= 1), finished in-launch
  *           (mfma-small: 1)
- *   rows    skinny: rows per wave (RW, 1..8); mfma: row groups per
- *           workgroup (GR, each of 16/Q rows); mfma-small: rows per tile
- *           (1..8); 0 = chosen per launch from its row count
+ *   rows    skinny: rows per wave (RW, 1..8); mfma-small: rows per tile
+ *           (1..8); 0 = chosen per launch from its row count; mfma: unused
  *   groups  skinny and mfma-small: row groups per workgroup (G); 0 =
- *           chosen per launch; mfma: Q, the k-slice packing of the 16 MFMA
- *           rows (1, 2, 4, 8: 16/Q weight rows times Q slices of K; Q > 1
- *           serves at most 16/Q tokens); part of the summation order */
+ *           chosen per launch; mfma: unused */
 typedef struct {
   int32_t path;
   int32_t kparts;

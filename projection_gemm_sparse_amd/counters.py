@@ -1,0 +1,159 @@
+"""Summaries of rocprofv3 runs of bench.py (kernel trace and HBM counters).
+
+    python -m projection_gemm_sparse_amd.counters --trace DIR --pmc DIR [DIR ...] \\
+        --out-md FILE.md --out-json profiles/traffic.json --command "..."
+
+Reads the CSV files rocprofv3 writes (``*_kernel_stats.csv`` of a
+``--kernel-trace --stats`` run; ``*_counter_collection.csv`` of ``--pmc``
+runs) and writes a markdown table of the library's kernels plus, for the
+skinny and tile kernels, the HBM bytes read and written per launch.
+
+HBM bytes per launch come from the L2-to-fabric request counters
+(TCC_EA0_RDREQ_{32B,64B,128B}_sum, TCC_EA0_WRREQ_{64B,}_sum: bytes = size
+x requests), each divided by the factor the same counters read for the
+elementwise kernel of known size (bf16 negation: reads and writes
+--calib-copy-mib MiB) that bench.py runs with --calib-copy-mib.
+The derived FETCH_SIZE / WRITE_SIZE are summarised too, but FETCH_SIZE
+counts the non-temporal 16-byte loads of these kernels at about half their
+size, so the request counters are the ones used.  The record carries a
+digest of the kernel sources; bench.py reports the traffic only while the
+sources still match it.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import re
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def _short(name: str) -> str:
+    return re.sub(r"\(.*$", "", name).strip()
+
+
+def load_pmc(dirs):
+    """{(kernel, grid): {counter: [values per dispatch]}}"""
+    out = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            with open(path) as fh:
+                for r in csv.DictReader(fh):
+                    key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+                    out.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+    return out
+
+
+def load_stats(d):
+    rows = []
+    for path in glob.glob(os.path.join(d, "*kernel_stats.csv")):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                rows.append({"kernel": _short(r["Name"]), "calls": int(r["Calls"]),
+                             "avg_ns": float(r["AverageNs"]), "min_ns": float(r["MinNs"]),
+                             "max_ns": float(r["MaxNs"])})
+    return rows
+
+
+def med(vals):
+    return statistics.median(vals) if vals else None
+
+
+def hbm_bytes(c):
+    """Read and write bytes per dispatch from the request counters."""
+    rd = None
+    if "TCC_EA0_RDREQ_128B_sum" in c:
+        rd = (128 * med(c["TCC_EA0_RDREQ_128B_sum"]) + 64 * med(c.get("TCC_EA0_RDREQ_64B_sum", [0]))
+              + 32 * med(c.get("TCC_EA0_RDREQ_32B_sum", [0])))
+    wr = None
+    if "TCC_EA0_WRREQ_sum" in c and "TCC_EA0_WRREQ_64B_sum" in c:
+        w64 = med(c["TCC_EA0_WRREQ_64B_sum"])
+        wr = 64 * w64 + 32 * (med(c["TCC_EA0_WRREQ_sum"]) - w64)
+    return rd, wr
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--pmc", nargs="+", required=True)
+    ap.add_argument("--calib-bytes", type=int, required=True,
+                    help="bytes read (and written) by the calibration copy kernel")
+    ap.add_argument("--calib-name", default="neg_kernel",
+                    help="substring of the calibration kernel's name")
+    ap.add_argument("--out-md", required=True)
+    ap.add_argument("--out-json", required=True)
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--title", default="")
+    args = ap.parse_args()
+
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+
+    pmc = load_pmc(args.pmc)
+    calib = None
+    calib_grid = None
+    for (k, grid), c in pmc.items():
+        if args.calib_name in k and (calib_grid is None or grid > calib_grid):
+            calib, calib_grid = c, grid
+    if calib is None:
+        raise SystemExit("no calibration kernel named *%s* in the counter runs" % args.calib_name)
+    crd, cwr = hbm_bytes(calib)
+    f_rd = crd / args.calib_bytes if crd else None
+    f_wr = cwr / args.calib_bytes if cwr else None
+    f_fetch = (med(calib.get("FETCH_SIZE", [])) or 0) * 1024 / args.calib_bytes or None
+    f_write = (med(calib.get("WRITE_SIZE", [])) or 0) * 1024 / args.calib_bytes or None
+
+    stats = {r["kernel"]: r for r in load_stats(args.trace)}
+    lines = ["# %s" % (args.title or "Fused projection kernels: duration and HBM traffic"), "",
+             "Commands (run from /tmp with TMPDIR=/tmp, repository root $R):", "", "```"]
+    lines += args.command + ["```", ""]
+    lines += ["Calibration: the bf16 negation kernel over %d bytes (grid %d) reads as %s read bytes "
+              "and %s written bytes by the request counters (factors %s / %s), FETCH_SIZE "
+              "factor %s, WRITE_SIZE factor %s." % (
+                  args.calib_bytes, calib_grid, crd, cwr,
+                  None if f_rd is None else round(f_rd, 4),
+                  None if f_wr is None else round(f_wr, 4),
+                  None if f_fetch is None else round(f_fetch, 4),
+                  None if f_write is None else round(f_write, 4)), ""]
+    lines += ["| kernel | grid | calls | avg ns (trace) | min ns | HBM read B/launch | "
+              "HBM write B/launch | FETCH_SIZE B (scaled) | WRITE_SIZE B (scaled) |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    rec = {"kernel_sources_sha256_16": bench.kernel_sources_digest(), "kernels": {},
+           "calibration": {"bytes": args.calib_bytes, "read_factor": f_rd, "write_factor": f_wr}}
+    for (k, grid), c in sorted(pmc.items()):
+        if not (k.startswith("void fp::") or k.startswith("fp::")):
+            continue
+        name = k.replace("void ", "")
+        rd, wr = hbm_bytes(c)
+        rd = rd / f_rd if (rd is not None and f_rd) else None
+        wr = wr / f_wr if (wr is not None and f_wr) else None
+        fs = med(c.get("FETCH_SIZE", []))
+        ws = med(c.get("WRITE_SIZE", []))
+        fs = fs * 1024 / f_fetch if (fs is not None and f_fetch) else None
+        ws = ws * 1024 / f_write if (ws is not None and f_write) else None
+        st = stats.get(k) or stats.get(name) or {}
+        lines.append("| `%s` | %d | %s | %s | %s | %s | %s | %s | %s |" % (
+            name, grid, st.get("calls", ""), st.get("avg_ns", ""), st.get("min_ns", ""),
+            None if rd is None else round(rd), None if wr is None else round(wr),
+            None if fs is None else round(fs), None if ws is None else round(ws)))
+        if rd is not None and wr is not None:
+            rec["kernels"][name] = {"grid": grid, "hbm_read_bytes_per_launch": round(rd),
+                                    "hbm_write_bytes_per_launch": round(wr),
+                                    "hbm_bytes_per_launch": round(rd + wr),
+                                    "trace_avg_ns": st.get("avg_ns")}
+    with open(args.out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    with open(args.out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print("wrote", args.out_md, args.out_json)
+
+
+if __name__ == "__main__":
+    main()
