@@ -83,9 +83,17 @@ def recorded_traffic(kernel: str):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-def skinny_kernel_name(M: int) -> str:
-    mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
-    return "fp::skinny_kernel<%d, 7, 1, true>" % mt
+def kernel_name(P, M: int, tiling) -> str:
+    """The kernel instantiation a (resolved) tiling runs, as rocprofv3 names it."""
+    path, kparts, chunks, splits, rows, groups = tiling
+    if path in (P.FP_PATH_SKINNY, P.FP_PATH_SKINNY_SPLITK):
+        mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
+        return "fp::skinny_kernel<%d, %d, %d, true>" % (mt, rows, chunks)
+    if path == P.FP_PATH_MFMA_SMALL:
+        return "fp::smfma_kernel<%d>" % chunks
+    mt16 = next(b for b in (1, 2, 4, 8, 16) if 16 * b >= M)
+    cs = 4 if chunks in (8, 16) else 5
+    return "fp::tile_kernel<%d, %d, %d, %d>" % (mt16, kparts, cs, chunks // cs)
 
 
 def algorithmic_bytes(M: int, K: int, N, esize: int = 2) -> int:
@@ -217,6 +225,9 @@ def main():
     ap.add_argument("--details", default="", help="write per-M details JSON here")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="skip the one-launch-per-projection timing (profiler runs: every "
+                         "dispatch of a kernel is then a fused call)")
     ap.add_argument("--crossover", default="",
                     help="also time every kernel path per M in 1..128 and write the table here")
     args = ap.parse_args()
@@ -266,9 +277,12 @@ def main():
     fused_graphs = [capture(torch, fused_calls(M)) for M in MS]
     print("bench: graphs captured", file=sys.stderr, flush=True)
     total_ms, per_ms = time_graphs(torch, fused_graphs, args.steps, args.warmup)
-    sep_graphs = [capture(torch, separate_calls(M)) for M in MS]
-    _, sep_ms = time_graphs(torch, sep_graphs, max(3, args.steps // 4), 1)
     sep_steps = max(3, args.steps // 4)
+    if args.fused_only:
+        sep_ms = [float("nan")] * len(MS)
+    else:
+        sep_graphs = [capture(torch, separate_calls(M)) for M in MS]
+        _, sep_ms = time_graphs(torch, sep_graphs, sep_steps, 1)
 
     calls = args.steps * n_copies
     per_m = {}
@@ -280,14 +294,14 @@ def main():
         tl = plans[0].get_tiling(M)
         per_m[str(M)] = {
             "fused_us": round(us, 4),
-            "separate_us": round(sep_ms[i] * 1e3 / (sep_steps * n_copies), 4),
+            "separate_us": (None if args.fused_only else
+                            round(sep_ms[i] * 1e3 / (sep_steps * n_copies), 4)),
             "bytes": b,
             "fused_GBps": round(b / us / 1e3, 1),
             "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
             "path": P._lib.PATH_NAMES[plans[0].query(M)[0]],
             "tiling": list(tl),
-            "kernel": skinny_kernel_name(M) if tl[0] in (P.FP_PATH_SKINNY,) and tl[4] == 7
-                      and tl[2] == 1 else None,
+            "kernel": kernel_name(P, M, tl),
         }
     ms_per_step = total_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -325,7 +339,7 @@ def main():
     by_kernel = {}
     for M in MS:
         e = per_m[str(M)]
-        k = e["kernel"] or ("%s %s" % (e["path"], e["tiling"]))
+        k = e["kernel"]
         t_us, b_sum, n = by_kernel.get(k, (0.0, 0, 0))
         by_kernel[k] = (t_us + e["fused_us"], b_sum + e["bytes"], n + 1)
     dom = max(by_kernel, key=lambda k: by_kernel[k][0])

@@ -29,12 +29,13 @@ constexpr uint64_t kPlanMagic = 0x66757365'6470726full;  // "fusedpro"
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kSkinnyMaxM = 8;      // largest M the skinny kernel serves
 constexpr int kDefaultMfmaMinM = 9; // crossover (smallest M on the MFMA path)
-// Smallest M the small-M matrix-core kernel serves by default (bf16).  It is
-// off by default (above the vector-ALU kernel's range): measured on MI355X
-// at K = 5120 it is slower than the vector-ALU kernel at every M <= 8 (its
-// operand layout spreads each quarter-wave's loads over eight weight rows);
-// it stays selectable through fp_plan_set_tiling.
-constexpr int kDefaultSmallMfmaMinM = kSkinnyMaxM + 1;
+// Smallest M the small-M matrix-core kernel serves by default (bf16); the
+// vector-ALU kernel runs below it.  Measured on MI355X at K = 5120, 1792
+// rows: the vector-ALU kernel is faster up to M = 4 (5.52 vs 5.87 us at
+// M = 4), the matrix-core kernel from M = 5 (5.94 vs 6.53 us at M = 5, 6.12
+// vs 6.56 at M = 8), where the vector-ALU kernel's multiply-adds and
+// 64-value lane reduction start to show after the last weights land.
+constexpr int kDefaultSmallMfmaMinM = 5;
 constexpr int kCus = 256;           // MI355X compute units
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // rows and chunks per row, 32-bit indexing
 

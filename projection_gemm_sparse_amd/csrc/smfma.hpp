@@ -21,13 +21,15 @@
 // K: A row s*8 + r is weight row r on sub-slice s, B column s*8 + m is
 // token m on sub-slice s.  The useful outputs are the two diagonal 8 x 8
 // blocks D[s*8 + r][s*8 + m]; their sum over s is row r, token m.  At one
-// MFMA step t of a wave, the lane of k-slot group g on sub-slice s reads the
-// 16-byte chunk
+// MFMA step t of a wave, the lane of k-slot group g on sub-slice s carries
+// the 16-byte chunk
 //     c = c0 + 8t + 2g + s
-// of its row (c0 = first chunk of the wave's K range), so the eight lanes of
-// one weight row read 128 contiguous bytes and the wave-wide load covers 8
-// rows x 128 B; every weight byte is loaded once, non-temporally, as stored
-// (no re-laid-out copy: writes through the projection views stay valid).
+// of its row (c0 = first chunk of the wave's K range), so one step covers
+// 8 rows x 128 contiguous bytes; every weight byte is loaded once,
+// non-temporally, as stored (no re-laid-out copy: writes through the
+// projection views stay valid).  The loads themselves keep each
+// quarter-wave on two rows (2 x 128 contiguous bytes) and a four-dword
+// lane shuffle (ds_bpermute) moves each chunk to its MFMA lane.
 //
 // Work split.  A workgroup owns G row groups of RT <= 8 rows (a tile with
 // RT < 8 leaves its last A rows unused; the 1792-row fused launch uses 7
@@ -75,31 +77,50 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   const int g = lane >> 4;
   const int sub = i16 >> 3;   // sub-slice of this lane's A row and B column
   const int r8 = i16 & 7;     // A: weight row in the tile; B: token
-  const int c0 = p * (8 * KT) + 2 * g + sub;  // chunk of step 0
+  const int cw = p * (8 * KT);        // first chunk of the wave's K range
+  const int c0 = cw + 2 * g + sub;    // chunk of this lane's operands at step 0
   const uint32_t row_bytes = (uint32_t)kc * 16u;
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
 
-  // 1. activations (token r8, clamped to a valid row and zeroed later),
-  //    then the weights (row r8 of the tile, clamped to the launch): all
-  //    loads issued before the first MFMA
+  // Loads use the layout that keeps each quarter-wave on two rows: lane L
+  // reads row (token) rl = 2 (L / 16) + (L / 8) % 2, chunk cl = L % 8 of
+  // the step's eight chunks, so a quarter-wave covers 2 x 128 contiguous
+  // bytes (as the vector-ALU kernel's 1 KiB runs do).  The operand of MFMA
+  // lane (i16, g) -- row i16 % 8, chunk 2g + i16 / 8 -- then sits in lane
+  // 8 (i16 % 8) + 2g + i16 / 8 and is fetched with four ds_bpermute_b32.
+  const int rl = 2 * (lane >> 4) + ((lane >> 3) & 1);
+  const int cl = lane & 7;
+  const int src4 = (8 * (lane & 7) + 2 * (lane >> 4) + ((lane >> 3) & 1)) * 4;
+  auto shuffle = [&](const u32x4& v) {
+    u32x4 o;
+    o.x = (unsigned)__builtin_amdgcn_ds_bpermute(src4, (int)(unsigned)v.x);
+    o.y = (unsigned)__builtin_amdgcn_ds_bpermute(src4, (int)(unsigned)v.y);
+    o.z = (unsigned)__builtin_amdgcn_ds_bpermute(src4, (int)(unsigned)v.z);
+    o.w = (unsigned)__builtin_amdgcn_ds_bpermute(src4, (int)(unsigned)v.w);
+    return o;
+  };
+
+  // 1. activations (token rl, clamped to a valid row; tokens past M are
+  //    zeroed after the shuffle), then the weights (row rl of the tile,
+  //    clamped to the launch): all loads issued before the first MFMA
   u32x4 xv[KT];
   {
-    const int mc = r8 < M ? r8 : M - 1;
+    const int mc = rl < M ? rl : M - 1;
     const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const int c = c0 + 8 * t;
+      const int c = cw + 8 * t + cl;
       xv[t] = xrow[c < kc ? c : kc - 1];
     }
   }
   u32x4 wv[KT];
   {
-    const int rr = r8 < RT ? row0 + r8 : row0;
+    const int rr = rl < RT ? row0 + rl : row0;
     const int row = rr < n_rows ? rr : n_rows - 1;
     const u32x4* wrow = reinterpret_cast<const u32x4*>(w + (uint64_t)(uint32_t)row * row_bytes);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const int c = c0 + 8 * t;
+      const int c = cw + 8 * t + cl;
       wv[t] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
     }
   }
@@ -114,8 +135,10 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   for (int t = 0; t < KT; ++t) {
     __builtin_amdgcn_sched_barrier(0);
     const bool c_ok = c0 + 8 * t < kc;
-    const bf16x8 A = u4bf8(c_ok ? wv[t] : zero4);
-    const bf16x8 B = u4bf8(c_ok && tok_ok ? xv[t] : zero4);
+    const u32x4 wa = shuffle(wv[t]);
+    const u32x4 xb = shuffle(xv[t]);
+    const bf16x8 A = u4bf8(c_ok ? wa : zero4);
+    const bf16x8 B = u4bf8(c_ok && tok_ok ? xb : zero4);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);

@@ -151,7 +151,7 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
             n_steps = -(-kc // 4)
             assert -(-n_steps // S) <= ch
         elif path == P.FP_PATH_MFMA_SMALL:
-            assert dtype == 0 and 2 <= M <= 8
+            assert dtype == 0 and 5 <= M <= 8
             assert S == 1 and kp <= 16 and kp * ch * 8 >= kc
             assert 1 <= rows <= 8 and groups >= 1
         else:
@@ -166,9 +166,12 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
 
 
 def test_default_crossover():
-    # vector-ALU kernel up to M = 8 (bf16 and fp32), MFMA tiles above
-    for M in range(1, 9):
+    # bf16: vector-ALU kernel up to M = 4, small-M matrix-core kernel for
+    # M = 5..8, tile kernel above; fp32: vector-ALU kernel (M <= 8)
+    for M in range(1, 5):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_SKINNY
+    for M in range(5, 9):
+        assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA_SMALL
     for M in range(1, 9):
         assert P.fp_default_tiling(1, 7168, 192, M, 192)[1][0] in (1, 2)
     for M in (9, 16, 32, 64, 128):
