@@ -25,6 +25,23 @@ Sources (TensorRT-LLM pull-request pages):
 * "Staircase: GLM-5.2 NVFP4 low-latency decode target for Rubin (TP16)"
   (PR #20502), router GEMV commit: checked against an FP64 reference.
 
+Epilogues (``oracle.c``), each applied with the pages' rounding points:
+
+* RMSNorm of a projection's bf16 output with a bf16 gain (q_norm over the
+  q_a columns, kv_norm over the kv columns: the consumers of the fused
+  projection in PR #20636, Description)::
+
+      out[m, j] = V[m, j] * G[j] / sqrt(mean_j V[m, j]^2 + eps)
+
+* SwiGLU of row-concatenated gate/up projections, gate and up rounded to
+  bf16 first (dense-MLP commit of PR #20502)::
+
+      h[m, j] = silu(G[m, j]) * U[m, j],   silu(v) = v / (1 + exp(-v))
+
+Their acceptance bounds (``rmsnorm_bound``, ``swiglu_bound``) are derived
+from the GPU's fp32 steps and documented at each function; the router GEMV
+(bf16 operands, fp32 logits, PR #20502) uses the fp32 rule below.
+
 Acceptance rule (error bound) for a GPU result compared with the unrounded
 fp64 ``y``: bf16 outputs within ``2**-7 * S + 1e-6``, fp32 outputs within
 ``1e-5 * S + 1e-7``.  The bf16 bound covers one output rounding (at most
@@ -86,6 +103,13 @@ def _load():
             lib.oracle_round_bf16_array.restype = None
             lib.oracle_round_bf16_array.argtypes = [
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+            lib.oracle_rmsnorm_bf16.restype = ctypes.c_int
+            lib.oracle_rmsnorm_bf16.argtypes = [
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_swiglu_bf16.restype = ctypes.c_int
+            lib.oracle_swiglu_bf16.argtypes = [
+                ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
             _lib = lib
     return _lib
 
@@ -190,3 +214,150 @@ def check_within_bound(y_out_f64: np.ndarray, y: np.ndarray, S: np.ndarray,
     worst = float(ratio[idx])
     ok = bool(np.all(np.isfinite(y_out_f64)) and worst <= 1.0)
     return ok, worst, idx
+
+
+# --------------------------------------------------------------- epilogues
+# Longest chain of fp32 roundings any output's sum goes through in the GPU
+# kernels (sequential adds plus tree levels; the matrix unit's 32-term step
+# counted as 32): the fp32 sum of an output is then within FP32_SUM_DEPTH *
+# 2^-24 * S of the exact sum.  The kernels stay far below it (at most a few
+# hundred); it only enters the epilogue bounds below.
+FP32_SUM_DEPTH = 1024
+_U = 2.0 ** -24
+
+
+def rmsnorm(v_bits: np.ndarray, gamma_bits: np.ndarray, eps: float):
+    """RMSNorm of each row of bf16 ``v_bits`` [M, N] with bf16 gain
+    ``gamma_bits`` [N] (``oracle.c``): returns ``(out, rinv)``, out the
+    unrounded float64 [M, N] result and rinv[m] = 1 / sqrt(mean_j v^2 + eps).
+    ``eps`` should be a value exact in fp32 (the GPU adds it in fp32)."""
+    v = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    g = np.ascontiguousarray(gamma_bits, dtype=np.uint16)
+    if v.ndim != 2 or g.ndim != 1 or g.shape[0] != v.shape[1]:
+        raise ValueError("v must be [M, N] and gamma [N]")
+    M, N = v.shape
+    out = np.zeros((M, N), dtype=np.float64)
+    rinv = np.zeros(M, dtype=np.float64)
+    rc = _load().oracle_rmsnorm_bf16(M, N, v.ctypes.data, g.ctypes.data, float(eps),
+                                     out.ctypes.data, rinv.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_rmsnorm_bf16 rejected its arguments")
+    return out, rinv
+
+
+def swiglu(g_bits: np.ndarray, u_bits: np.ndarray) -> np.ndarray:
+    """silu(G) * U elementwise over bf16 patterns (``oracle.c``), unrounded
+    float64 of the same shape."""
+    g = np.ascontiguousarray(g_bits, dtype=np.uint16)
+    u = np.ascontiguousarray(u_bits, dtype=np.uint16)
+    if g.shape != u.shape:
+        raise ValueError("gate and up shapes differ")
+    h = np.zeros(g.shape, dtype=np.float64)
+    rc = _load().oracle_swiglu_bf16(g.size, g.ctypes.data, u.ctypes.data, h.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_swiglu_bf16 rejected its arguments")
+    return h
+
+
+def fused_rmsnorm(x_bits: np.ndarray, weights: list, gammas: list, eps: float):
+    """The fused projection followed by a per-projection RMSNorm, with the
+    rounding points of the unfused chain: y_i = x . W_i^T (exact), rounded
+    once to bf16, then normalised (gamma_i None: projection left as is).
+    Returns one dict per projection: y, S (exact sum and its scale), yb (the
+    bf16 patterns of y), out (unrounded fp64 normalised result, or y when not
+    normalised), rinv (per token, or None)."""
+    res = []
+    for w, gm in zip(weights, gammas):
+        y, s = linear(x_bits, w)
+        yb = round_bf16(y)
+        if gm is None:
+            res.append({"y": y, "S": s, "yb": yb, "out": y, "rinv": None})
+            continue
+        out, rinv = rmsnorm(yb, gm, eps)
+        res.append({"y": y, "S": s, "yb": yb, "out": out, "rinv": rinv})
+    return res
+
+
+def fused_swiglu(x_bits: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray):
+    """Gate/up + SwiGLU with the pages' rounding points: g = x . Wg^T and
+    u = x . Wu^T (exact), each rounded to bf16, h = silu(g_b) * u_b
+    (unrounded fp64; the GPU rounds it once to bf16).  Returns a dict with
+    g, Sg, u, Su, gb, ub, h."""
+    g, sg = linear(x_bits, w_gate)
+    u, su = linear(x_bits, w_up)
+    gb = round_bf16(g)
+    ub = round_bf16(u)
+    return {"g": g, "Sg": sg, "u": u, "Su": su, "gb": gb, "ub": ub, "h": swiglu(gb, ub)}
+
+
+def _bf16_pair_gap(y, S, exact_sums: bool):
+    """Bound on |a - RNE(y)| for a = RNE(y') with y' an fp32 sum of the same
+    products (|y' - y| <= FP32_SUM_DEPTH * 2^-24 * S): both roundings are
+    within 2^-8 of their argument, so the gap is at most
+    2^-7 |y| + (1 + 2^-8) * D * u * S (+1e-6 for values near zero).  With
+    exact_sums (integer data: every fp32 partial sum exact) the two
+    roundings coincide and the gap is 0."""
+    if exact_sums:
+        return np.zeros_like(np.asarray(y, dtype=np.float64))
+    y = np.abs(np.asarray(y, dtype=np.float64))
+    S = np.asarray(S, dtype=np.float64)
+    return 2.0 ** -7 * y + (1 + 2.0 ** -8) * FP32_SUM_DEPTH * _U * S + 1e-6
+
+
+def rmsnorm_bound(r: dict, gamma_bits: np.ndarray, eps: float, exact_sums: bool = False):
+    """Allowed |out_gpu - out| per element for one normalised projection of
+    ``fused_rmsnorm`` (GPU: bf16 projection output, fp32 sum of squares,
+    rsqrt and products in fp32, one rounding to bf16).  Derived bound:
+      D_j   = gap of the GPU's bf16 projection output to RNE(y_j) (above)
+      dms   = (1/N) sum_j D_j (2|v_j| + D_j) + (N + 4) u (ms + that)
+      er    = 0.5 * d / (1 - d) + 8u,   d = dms / (ms + eps)   (rsqrt)
+      E_j   = |g_j| rinv (D_j + |v_j| er) (1 + 4u)
+      tol_j = E_j + 2^-8 (|out_j| + E_j) + 1e-6                (output rounding)"""
+    v = bf16_bits_to_f64(r["yb"])
+    M, N = v.shape
+    D = _bf16_pair_gap(r["y"], r["S"], exact_sums)
+    ms = np.sum(v * v, axis=1) / N
+    dms = np.sum(D * (2 * np.abs(v) + D), axis=1) / N
+    dms = dms + (N + 4) * _U * (ms + dms)
+    d = dms / (ms + eps)
+    if np.any(d >= 0.5):
+        raise ValueError("perturbation too large for the first-order rsqrt bound")
+    er = 0.5 * d / (1 - d) + 8 * _U
+    gam = np.abs(bf16_bits_to_f64(gamma_bits))[None, :]
+    rinv = r["rinv"][:, None]
+    E = gam * rinv * (D + np.abs(v) * er[:, None]) * (1 + 4 * _U)
+    return E + 2.0 ** -8 * (np.abs(r["out"]) + E) + 1e-6
+
+
+# relative error allowed for the GPU's fp32 silu (fast exp of -g and a
+# reciprocal-based division): the exponent's own rounding grows with |g|
+def _silu_rel(g):
+    return 2.0 ** -20 * (np.abs(g) + 8.0)
+
+
+def swiglu_bound(r: dict, exact_sums: bool = False):
+    """Allowed |h_gpu - h| per element for ``fused_swiglu``'s h.  With Dg,
+    Du the gaps of the GPU's bf16 gate/up values to RNE(g), RNE(u) (above),
+    |silu'| <= 1.1 and a relative error s of the fp32 silu:
+      E   = 1.1 Dg (|u_b| + Du) + |silu(g_b)| Du + s (|silu(g_b)| + 1.1 Dg)(|u_b| + Du)
+      tol = E + 2^-8 (|h| + E) + 1e-6."""
+    Dg = _bf16_pair_gap(r["g"], r["Sg"], exact_sums)
+    Du = _bf16_pair_gap(r["u"], r["Su"], exact_sums)
+    gb = bf16_bits_to_f64(r["gb"])
+    ub = np.abs(bf16_bits_to_f64(r["ub"]))
+    sil = np.abs(swiglu(r["gb"], round_bf16(np.ones(r["gb"].shape))))  # |silu(g_b)|
+    s = _silu_rel(gb)
+    E = 1.1 * Dg * (ub + Du) + sil * Du + s * (sil + 1.1 * Dg) * (ub + Du)
+    return E + 2.0 ** -8 * (np.abs(r["h"]) + E) + 1e-6
+
+
+def check_against(got_f64: np.ndarray, want: np.ndarray, bound: np.ndarray):
+    """``(ok, worst_ratio, index)`` of |got - want| / bound (ok: <= 1, all
+    finite)."""
+    got = np.asarray(got_f64, dtype=np.float64)
+    ratio = np.abs(got - want) / bound
+    if ratio.size == 0:
+        return True, 0.0, None
+    idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    worst = float(ratio[idx])
+    return bool(np.all(np.isfinite(got)) and worst <= 1.0), worst, idx

@@ -116,3 +116,53 @@ uint16_t oracle_round_bf16(double v) {
 void oracle_round_bf16_array(const double* v, uint16_t* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(v[i]);
 }
+
+/*
+ * RMSNorm of each row of a bf16 matrix v[M][N] with a bf16 gain g[N]:
+ *   ms[m]     = (1/N) * sum_j V[m][j]^2
+ *   rinv[m]   = 1 / sqrt(ms[m] + eps)
+ *   out[m][j] = V[m][j] * rinv[m] * G[j]
+ * all in double, V and G the exact values of the stored patterns, no
+ * rounding of the result (callers round with oracle_round_bf16).  The
+ * normalisation that follows the fused projection: q_norm over the q_a
+ * columns and kv_norm over the kv columns ("tinygemm2 for the
+ * DeepSeek-V4.1 hidden-state projections", PR #20636, Description: the
+ * projection's consumers are these RMSNorms), applied to the projection's
+ * bf16 output as the unfused chain would (the GEMM rounds to bf16 once,
+ * the norm reads that).  eps is the caller's value (the pages state none).
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_rmsnorm_bf16(int64_t M, int64_t N, const uint16_t* v, const uint16_t* g,
+                        double eps, double* out, double* rinv) {
+  if (M < 0 || N < 1 || !(eps >= 0.0)) return -1;
+  for (int64_t m = 0; m < M; ++m) {
+    double ss = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+      double a = bf16_bits_value(v[m * N + j]);
+      ss += a * a;
+    }
+    double r = 1.0 / sqrt(ss / (double)N + eps);
+    if (rinv) rinv[m] = r;
+    for (int64_t j = 0; j < N; ++j)
+      out[m * N + j] = bf16_bits_value(v[m * N + j]) * r * bf16_bits_value(g[j]);
+  }
+  return 0;
+}
+
+/*
+ * SwiGLU of bf16 gate and up values, elementwise:
+ *   h = silu(G) * U,   silu(G) = G / (1 + exp(-G))
+ * in double, from the exact values of the stored patterns, unrounded.  The
+ * gate/up + SwiGLU step of the dense-MLP commit of "Staircase: GLM-5.2
+ * NVFP4 low-latency decode target for Rubin (TP16)" (PR #20502): the gate
+ * and up sums are rounded to bf16 before SwiGLU (the callers pass those
+ * rounded values) and h is rounded to bf16 once afterwards.
+ */
+int oracle_swiglu_bf16(int64_t n, const uint16_t* g, const uint16_t* u, double* h) {
+  if (n < 0) return -1;
+  for (int64_t i = 0; i < n; ++i) {
+    double a = bf16_bits_value(g[i]);
+    h[i] = a / (1.0 + exp(-a)) * bf16_bits_value(u[i]);
+  }
+  return 0;
+}

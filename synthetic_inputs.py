@@ -64,7 +64,55 @@ WORKLOADS = {
                           "uniform_inv_sqrt_k",
                           (1, 2, 4, 8, 9, 16, 32, 64, 128), (0,),
                           "M sweep, strided x, reload through views"),
+    # Epilogue workloads.  Router GEMV: GLM-5's 256 expert logits at hidden
+    # 6144 for 1-16 tokens, fp32 output (router commit of PR #20502).
+    "router_f32out": Workload("router_f32out", 6144, (256,), "bf16",
+                              "uniform_inv_sqrt_k", tuple(range(1, 17)), (0, 1),
+                              "bf16 operands, fp32 logits"),
+    # wq_a + wkv with q_norm / kv_norm gains (PR #20636's consumers)
+    "q_kv_norm": Workload("q_kv_norm", 5120, (1280, 512), "bf16",
+                          "uniform_inv_sqrt_k", (1, 2, 3, 4, 5, 6, 7, 8), (0, 1),
+                          "fused projection + RMSNorm per projection"),
+    # dense-MLP gate/up of one TP16 rank: [2 * 768, 6144] (PR #20502)
+    "gate_up_swiglu": Workload("gate_up_swiglu", 6144, (768, 768), "bf16",
+                               "uniform_inv_sqrt_k", (1, 2, 3, 4, 5, 6, 7, 8), (0, 1),
+                               "gate rows over up rows, SwiGLU epilogue"),
 }
+
+
+def draw_gamma(N: int, g: torch.Generator) -> torch.Tensor:
+    """An RMSNorm gain of N entries near 1 (1 + 0.1 * N(0, 1), in bf16), drawn
+    after the weights and x of the same seed."""
+    return (1.0 + 0.1 * torch.randn(int(N), generator=g, dtype=torch.float32)).to(
+        torch.bfloat16)
+
+
+def norm_case(M: int, seed: int, ldx: int | None = None):
+    """x, the two weights and their two gains of the q_kv_norm workload."""
+    w = WORKLOADS["q_kv_norm"]
+    g = _gen(seed)
+    ws = draw_weights(w.K, w.N, w.dtype, w.w_dist, g)
+    x = draw_x(M, w.K, w.dtype, g, ldx=ldx)
+    gammas = [draw_gamma(n, g) for n in w.N]
+    return x, ws, gammas
+
+
+def sparse_int_case(K: int, N, M: int, seed: int, nnz: int = 4, x_den: float = 64.0):
+    """Exact-arithmetic data: x on a 1/x_den grid in [-4, 4], each weight row
+    with nnz integer entries in [-2, 2] at random columns (bf16 exact).  Every
+    fp32 partial sum of a projection is then exact, so the GPU's sums equal
+    the exact ones bit for bit before any rounding."""
+    g = _gen(seed)
+    ws = []
+    for n in N:
+        w = torch.zeros(int(n), K, dtype=torch.float32)
+        for r in range(int(n)):
+            cols = torch.randperm(K, generator=g)[:nnz]
+            w[r, cols] = torch.randint(-2, 3, (nnz,), generator=g).to(torch.float32)
+        ws.append(w.to(torch.bfloat16))
+    lim = int(4 * x_den) - 1
+    x = (torch.randint(-lim, lim + 1, (M, K), generator=g).to(torch.float32) / x_den)
+    return x.to(torch.bfloat16), ws
 
 
 def _gen(seed: int) -> torch.Generator:
