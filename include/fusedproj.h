@@ -148,6 +148,61 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx,
                               fp_plan_t plan, void* stream, void* const* y,
                               const void* const* w_override);
 
+/* ---------------------------------------------------------------------
+ * Epilogues: the step that consumes the projection, applied inside the same
+ * launch.  Both read the projection after its single rounding to bf16, as
+ * the unfused chain (projection, then a second kernel) does, and both give
+ * results bitwise equal to that chain (fp_forward_separate followed by
+ * fp_rmsnorm / fp_swiglu on its outputs).  The fused forms serve bf16 plans
+ * with 1 <= M <= 8 on the unsplit one-launch kernels; other cases return
+ * FP_ERR_UNSUPPORTED with no launch (the caller then runs the unfused
+ * chain).  They stage the bf16 projection in the plan's workspace, so they
+ * share the plan's rule that its calls must not overlap in time.
+ * --------------------------------------------------------------------- */
+
+/* Fused projection + RMSNorm per projection (q_norm over the q_a columns and
+ * kv_norm over the kv columns that consume the fused wq_a/wkv projection in
+ * PR #20636, Description):
+ *     v = bf16(x . W_i^T)                      (the projection, rounded once)
+ *     out_i[m, j] = bf16( v[m, j] * rinv_m * gamma_i[j] ),
+ *     rinv_m = 1 / sqrt( (1/N_i) sum_j v[m, j]^2 + eps )     (fp32 arithmetic)
+ * gamma: host array of n_proj entries; entry i is a device bf16 [N_i] gain
+ *   (16-byte aligned, N_i a multiple of 8, N_i <= 2048) or NULL, in which
+ *   case out_i receives the projection itself.
+ * out: host array of n_proj device pointers, dense [M, N_i] bf16, 16-byte
+ *   aligned where normalised; no overlap with each other, x, w_cat, the
+ *   workspace or a gain.
+ * eps: finite, >= 0. */
+fp_status fp_forward_rmsnorm(const void* x, int64_t M, int64_t ldx,
+                             fp_plan_t plan, void* stream,
+                             const void* const* gamma, float eps,
+                             void* const* out);
+
+/* Fused gate/up projection + SwiGLU (dense-MLP commit of PR #20502): the plan
+ * holds exactly two projections of equal width N (the gate rows, then the
+ * up rows, N a multiple of 8), and
+ *     g = bf16(x . W_gate^T),  u = bf16(x . W_up^T)
+ *     h[m, j] = bf16( g / (1 + exp(-g)) * u )     (fp32 arithmetic)
+ * h: device, dense [M, N] bf16, 16-byte aligned, no overlap with x, w_cat or
+ * the workspace.  FP_ERR_INVALID_ARG if the plan is not such a pair. */
+fp_status fp_forward_swiglu(const void* x, int64_t M, int64_t ldx,
+                            fp_plan_t plan, void* stream, void* h);
+
+/* The unfused second step of the chain: RMSNorm of y (device, dense [M, N]
+ * bf16) with gain gamma (device, bf16 [N]) into out (device, dense [M, N]
+ * bf16; out == y normalises in place, other overlaps are refused), with the
+ * arithmetic of fp_forward_rmsnorm.  All three pointers 16-byte aligned,
+ * N a multiple of 8 and at most 2048.  M == 0 launches nothing. */
+fp_status fp_rmsnorm(const void* y, int64_t M, int64_t N, const void* gamma,
+                     float eps, void* out, void* stream);
+
+/* The unfused second step of the gate/up chain: h = bf16(silu(g) * u)
+ * elementwise over dense [M, N] bf16 tensors g, u, h (device, 16-byte
+ * aligned, N a multiple of 8; h may be g or u, other overlaps are refused),
+ * with the arithmetic of fp_forward_swiglu. */
+fp_status fp_swiglu(const void* g, const void* u, int64_t M, int64_t N,
+                    void* h, void* stream);
+
 /* Which kernel fp_forward runs for M, and how many kernel launches
  * fp_forward and fp_forward_separate make (0 for M == 0).  Any output
  * pointer may be NULL.  Host-only. */

@@ -78,6 +78,10 @@ _SIGS = {
     "fp_supported": (_i32, [_p, _i64, _p, _i64]),
     "fp_forward": (_i32, [_p, _i64, _i64, _p, _p, _P_p]),
     "fp_forward_separate": (_i32, [_p, _i64, _i64, _p, _p, _P_p, _P_p]),
+    "fp_forward_rmsnorm": (_i32, [_p, _i64, _i64, _p, _p, _P_p, ctypes.c_float, _P_p]),
+    "fp_forward_swiglu": (_i32, [_p, _i64, _i64, _p, _p, _p]),
+    "fp_rmsnorm": (_i32, [_p, _i64, _i64, _p, ctypes.c_float, _p, _p]),
+    "fp_swiglu": (_i32, [_p, _p, _i64, _i64, _p, _p]),
     "fp_plan_query": (_i32, [_p, _i64, _P_i32, _P_i32, _P_i32]),
     "fp_plan_set_mfma_min_m": (_i32, [_p, _i64]),
     "fp_plan_set_tiling": (_i32, [_p, _i64, ctypes.POINTER(FpTiling)]),
@@ -145,6 +149,25 @@ def fp_forward_separate(x: int, M: int, ldx: int, plan: int, stream: int, y,
                         w_override=None) -> int:
     ov = None if w_override is None else _ptr_array(w_override)
     return _lib.fp_forward_separate(x, M, ldx, plan, stream, _ptr_array(y), ov)
+
+
+def fp_forward_rmsnorm(x: int, M: int, ldx: int, plan: int, stream: int, gamma, eps: float,
+                       out) -> int:
+    """``gamma``: per projection a device pointer or None (not normalised)."""
+    return _lib.fp_forward_rmsnorm(x, M, ldx, plan, stream, _ptr_array(gamma), float(eps),
+                                   _ptr_array(out))
+
+
+def fp_forward_swiglu(x: int, M: int, ldx: int, plan: int, stream: int, h: int) -> int:
+    return _lib.fp_forward_swiglu(x, M, ldx, plan, stream, h)
+
+
+def fp_rmsnorm(y: int, M: int, N: int, gamma: int, eps: float, out: int, stream: int) -> int:
+    return _lib.fp_rmsnorm(y, M, N, gamma, float(eps), out, stream)
+
+
+def fp_swiglu(g: int, u: int, M: int, N: int, h: int, stream: int) -> int:
+    return _lib.fp_swiglu(g, u, M, N, h, stream)
 
 
 def fp_plan_query(plan: int, M: int):

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -22,6 +23,7 @@
 #include "skinny.hpp"
 #include "smfma.hpp"
 #include "tile.hpp"
+#include "epilogue.hpp"
 
 namespace {
 
@@ -96,8 +98,17 @@ int mfma_mt16(int64_t M) {
   return t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 16;
 }
 
+// Arrival counters: one per row block of a split-K launch (at most n_total)
+// and, at index n_total, the epilogue's.
 int64_t counters_bytes(int64_t n_total) {
-  return ceil_div(n_total * 4, 256) * 256;
+  return ceil_div((n_total + 1) * 4, 256) * 256;
+}
+
+// Staged bf16 projection outputs of an epilogue call: segment i's dense
+// [M, N_i] rows at byte offset kEpiMaxM * off_i * 2 past the counters (the
+// same region as the split-K partials, which an epilogue call never uses).
+int64_t staging_bytes(int32_t dtype, int64_t n_total) {
+  return dtype == FP_BF16 ? (int64_t)fp::kEpiMaxM * n_total * 2 : 0;
 }
 
 // ------------------------------------------------------------------ tilings
@@ -437,6 +448,7 @@ size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) 
       most = std::max(most, partial_floats(t, n_total, M));
     }
   }
+  most = std::max(most, ceil_div(staging_bytes(dtype, n_total), 4));
   return (size_t)(counters_bytes(n_total) + most * 4);
 }
 
@@ -595,7 +607,8 @@ const void* smfma_fn(const Tiling& t) {
 // geometry word; then the trailing Tail (output table for more than two
 // segments, split-K workspace).
 fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
-              const void* x, int64_t M, int64_t ldx, hipStream_t stream) {
+              const void* x, int64_t M, int64_t ldx, hipStream_t stream,
+              const fp::Epi* epi = nullptr) {
   const unsigned char* w_a = lr.w;
   const unsigned char* x_a = static_cast<const unsigned char*>(x);
   unsigned char* y0_a = lr.y[0];
@@ -618,11 +631,22 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   int32_t geo_a = 0;
   void* args[] = {&w_a, &x_a, &y0_a, &y1_a, &ldx_a, &n_rows_a, &kc_a, &M_a, &split_a,
                   &geo_a, &tail};
+  size_t epi_lds = 0;
+  if (epi != nullptr) {
+    // only the unsplit vector-ALU and small-M matrix-core launches finish an
+    // epilogue (checked by the caller)
+    tail.epi = *epi;
+    bool normed[fp::kMaxSeg];
+    for (int i = 0; i < fp::kMaxSeg; ++i) normed[i] = i < lr.n_seg && epi->gamma[i] != nullptr;
+    epi_lds = fp::epi_lds_bytes(epi->mode, (int)M, lr.n_seg, lr.begin, normed);
+  }
   if (t.path == FP_PATH_MFMA_SMALL) {
-    geo_a = t.rows | (t.kparts << 8) | (t.groups << 16);
+    geo_a = t.rows | (t.kparts << 8) | (t.groups << 16) | (epi ? fp::kGeoEpi : 0);
     const int64_t R = (int64_t)t.rows * t.groups;
-    return launch(smfma_fn(t), ceil_div(lr.n_rows, R), t.groups * t.kparts * 64, smfma_lds(t),
-                  args, stream);
+    const int64_t blocks = ceil_div(lr.n_rows, R);
+    tail.epi.n_blocks = (int32_t)blocks;
+    return launch(smfma_fn(t), blocks, t.groups * t.kparts * 64,
+                  std::max(smfma_lds(t), epi_lds), args, stream);
   }
   if (t.path == FP_PATH_MFMA) {
     geo_a = t.splits;
@@ -631,12 +655,14 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
     const size_t lds = std::max<size_t>(tile_lds(t.mt, per, t.kparts), 16);
     return launch(mfma_fn(t), blocks, t.kparts * 64, lds, args, stream);
   }
-  geo_a = t.kparts | (t.groups << 8) | (t.splits << 16);
+  geo_a = t.kparts | (t.groups << 8) | (t.splits << 16) | (epi ? fp::kGeoEpi : 0);
   const int64_t R = (int64_t)t.groups * t.rows;
   const int64_t blocks = ceil_div(lr.n_rows, R) * t.splits;
+  tail.epi.n_blocks = (int32_t)blocks;
   const void* fn = p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
                                        : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
-  return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
+  return launch(fn, blocks, t.groups * t.kparts * 64, std::max(skinny_lds(t), epi_lds), args,
+                stream);
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
@@ -867,6 +893,154 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx, fp_plan_t p
     if (s != FP_OK) return s;
   }
   return FP_OK;
+}
+
+namespace {
+
+// The tiling of an epilogue call: the fused launch must be one unsplit
+// vector-ALU or small-M matrix-core launch (those kernels carry the finish).
+fp_status epi_tiling(const fp_plan_s* p, int64_t M, Tiling* t) {
+  if (!choose_tiling(p, M, p->n_total, t)) return FP_ERR_UNSUPPORTED;
+  if (t->splits != 1 || !(t->path == FP_PATH_SKINNY || t->path == FP_PATH_MFMA_SMALL))
+    return FP_ERR_UNSUPPORTED;
+  return FP_OK;
+}
+
+unsigned char* staging(const fp_plan_s* p, int i) {
+  return p->ws + counters_bytes(p->n_total) + (int64_t)fp::kEpiMaxM * p->off[i] * 2;
+}
+
+bool range_overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return overlaps(a0, a0 + (uintptr_t)a_bytes, b0, b0 + (uintptr_t)b_bytes);
+}
+
+LaunchRows fused_rows(const fp_plan_s* p) {
+  LaunchRows lr;
+  std::memset(&lr, 0, sizeof lr);
+  lr.w = p->w_cat;
+  lr.n_seg = p->n_proj;
+  lr.n_rows = (int)p->n_total;
+  for (int i = 0; i < p->n_proj; ++i) lr.begin[i] = (int)p->off[i];
+  lr.begin[p->n_proj] = (int)p->n_total;
+  return lr;
+}
+
+}  // namespace
+
+fp_status fp_forward_rmsnorm(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
+                             void* stream, const void* const* gamma, float eps,
+                             void* const* out) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  if (gamma == nullptr || out == nullptr) return FP_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !(eps < INFINITY)) return FP_ERR_INVALID_ARG;
+  fp_status s = check_x(plan, M, x, ldx);
+  if (s != FP_OK) return s;
+  if (M == 0) return FP_OK;
+  if (plan->dtype != FP_BF16 || M > fp::kEpiMaxM) return FP_ERR_UNSUPPORTED;
+  s = check_outputs(plan, M, x, ldx, out);
+  if (s != FP_OK) return s;
+  for (int i = 0; i < plan->n_proj; ++i) {
+    if (gamma[i] == nullptr) continue;
+    const int64_t N = plan->N[i];
+    if (N % 8 != 0 || N > fp::kNormMaxN) return FP_ERR_UNSUPPORTED;
+    if (!aligned(out[i], 16) || !aligned(gamma[i], 16)) return FP_ERR_UNSUPPORTED;
+    for (int j = 0; j < plan->n_proj; ++j)
+      if (range_overlaps(gamma[i], N * 2, out[j], M * plan->N[j] * 2)) return FP_ERR_INVALID_ARG;
+  }
+  Tiling t;
+  s = epi_tiling(plan, M, &t);
+  if (s != FP_OK) return s;
+  LaunchRows lr = fused_rows(plan);
+  fp::Epi e;
+  std::memset(&e, 0, sizeof e);
+  bool normed[fp::kMaxSeg] = {};
+  for (int i = 0; i < plan->n_proj; ++i) {
+    normed[i] = gamma[i] != nullptr;
+    lr.y[i] = normed[i] ? staging(plan, i) : static_cast<unsigned char*>(out[i]);
+    e.out[i] = static_cast<unsigned char*>(out[i]);
+    e.gamma[i] = static_cast<const unsigned char*>(gamma[i]);
+  }
+  if (fp::epi_lds_bytes(fp::kEpiRmsNorm, (int)M, lr.n_seg, lr.begin, normed) > kMaxLds)
+    return FP_ERR_UNSUPPORTED;
+  e.counter = reinterpret_cast<uint32_t*>(plan->ws) + plan->n_total;
+  e.mode = fp::kEpiRmsNorm;
+  e.eps = eps;
+  return run(plan, t, lr, x, M, ldx, static_cast<hipStream_t>(stream), &e);
+}
+
+fp_status fp_forward_swiglu(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
+                            void* stream, void* h) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  if (plan->n_proj != 2 || plan->N[0] != plan->N[1]) return FP_ERR_INVALID_ARG;
+  fp_status s = check_x(plan, M, x, ldx);
+  if (s != FP_OK) return s;
+  if (M == 0) return FP_OK;
+  if (h == nullptr) return FP_ERR_INVALID_ARG;
+  const int64_t N = plan->N[0];
+  if (plan->dtype != FP_BF16 || M > fp::kEpiMaxM || N % 8 != 0) return FP_ERR_UNSUPPORTED;
+  if (!aligned(h, 16)) return FP_ERR_UNSUPPORTED;
+  const int64_t hb = M * N * 2;
+  if (range_overlaps(h, hb, x, ((M - 1) * ldx + plan->K) * 2) ||
+      range_overlaps(h, hb, plan->w_cat, plan->n_total * plan->K * 2) ||
+      range_overlaps(h, hb, plan->ws, (int64_t)plan->ws_bytes))
+    return FP_ERR_INVALID_ARG;
+  Tiling t;
+  s = epi_tiling(plan, M, &t);
+  if (s != FP_OK) return s;
+  LaunchRows lr = fused_rows(plan);
+  lr.y[0] = staging(plan, 0);
+  lr.y[1] = staging(plan, 1);
+  if (fp::epi_lds_bytes(fp::kEpiSwiglu, (int)M, lr.n_seg, lr.begin, nullptr) > kMaxLds)
+    return FP_ERR_UNSUPPORTED;
+  fp::Epi e;
+  std::memset(&e, 0, sizeof e);
+  e.out[0] = static_cast<unsigned char*>(h);
+  e.counter = reinterpret_cast<uint32_t*>(plan->ws) + plan->n_total;
+  e.mode = fp::kEpiSwiglu;
+  return run(plan, t, lr, x, M, ldx, static_cast<hipStream_t>(stream), &e);
+}
+
+fp_status fp_rmsnorm(const void* y, int64_t M, int64_t N, const void* gamma, float eps,
+                     void* out, void* stream) {
+  if (M < 0 || N < 1 || !(eps >= 0.0f) || !(eps < INFINITY)) return FP_ERR_INVALID_ARG;
+  if (M == 0) return FP_OK;
+  if (y == nullptr || gamma == nullptr || out == nullptr) return FP_ERR_INVALID_ARG;
+  if (N % 8 != 0 || N > fp::kNormMaxN || M > INT32_MAX) return FP_ERR_UNSUPPORTED;
+  if (!aligned(y, 16) || !aligned(gamma, 16) || !aligned(out, 16)) return FP_ERR_UNSUPPORTED;
+  // in place (out == y) is allowed; any other overlap is not
+  if (out != y && range_overlaps(out, M * N * 2, y, M * N * 2)) return FP_ERR_INVALID_ARG;
+  if (range_overlaps(out, M * N * 2, gamma, N * 2)) return FP_ERR_INVALID_ARG;
+  const unsigned char* y_a = static_cast<const unsigned char*>(y);
+  const unsigned char* g_a = static_cast<const unsigned char*>(gamma);
+  unsigned char* o_a = static_cast<unsigned char*>(out);
+  int32_t n_a = (int32_t)N;
+  float eps_a = eps;
+  void* args[] = {&y_a, &g_a, &o_a, &n_a, &eps_a};
+  return launch(reinterpret_cast<const void*>(&fp::rmsnorm_kernel), M, 64, 0, args,
+                static_cast<hipStream_t>(stream));
+}
+
+fp_status fp_swiglu(const void* g, const void* u, int64_t M, int64_t N, void* h,
+                    void* stream) {
+  if (M < 0 || N < 1) return FP_ERR_INVALID_ARG;
+  if (M == 0) return FP_OK;
+  if (g == nullptr || u == nullptr || h == nullptr) return FP_ERR_INVALID_ARG;
+  if (N % 8 != 0) return FP_ERR_UNSUPPORTED;
+  const int64_t chunks = M * N / 8;
+  if (chunks > INT32_MAX - 256) return FP_ERR_UNSUPPORTED;
+  if (!aligned(g, 16) || !aligned(u, 16) || !aligned(h, 16)) return FP_ERR_UNSUPPORTED;
+  const int64_t b = M * N * 2;
+  // h may replace g or u element for element; any other overlap is not allowed
+  if ((h != g && range_overlaps(h, b, g, b)) || (h != u && range_overlaps(h, b, u, b)))
+    return FP_ERR_INVALID_ARG;
+  const unsigned char* g_a = static_cast<const unsigned char*>(g);
+  const unsigned char* u_a = static_cast<const unsigned char*>(u);
+  unsigned char* h_a = static_cast<unsigned char*>(h);
+  int32_t n_a = (int32_t)chunks;
+  void* args[] = {&g_a, &u_a, &h_a, &n_a};
+  return launch(reinterpret_cast<const void*>(&fp::swiglu_kernel), ceil_div(chunks, 256), 256,
+                0, args, static_cast<hipStream_t>(stream));
 }
 
 fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path, int32_t* launches_fused,

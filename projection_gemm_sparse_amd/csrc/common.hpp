@@ -35,12 +35,37 @@ struct OutTable {
   int32_t n_seg;
 };
 
+// Epilogue applied after the projection inside the same launch (set when
+// the geometry word carries kGeoEpi): the launch's outputs y[i] of the
+// output table are then staging buffers in the workspace, and the last
+// workgroup to finish reads them back and writes the final tensors.
+//   mode     kEpiRmsNorm: out[i] = RMSNorm(y_i) * gamma[i] for every segment
+//            with gamma[i] != nullptr; segments without a gain are written
+//            straight to their final tensor by the projection itself.
+//            kEpiSwiglu: out[0] = silu(y_0) * y_1 (two segments of equal
+//            width: gate rows, then up rows).
+//   counter  arrival counter (zero between calls; reset by the finisher)
+//   n_blocks workgroups of the launch
+constexpr int kEpiRmsNorm = 1;
+constexpr int kEpiSwiglu = 2;
+constexpr int kGeoEpi = 1 << 29;  // geometry-word flag: run the epilogue
+
+struct Epi {
+  unsigned char* out[kMaxSeg];
+  const unsigned char* gamma[kMaxSeg];
+  uint32_t* counter;
+  int32_t n_blocks;
+  int32_t mode;
+  float eps;
+};
+
 // Trailing kernel argument (not preloaded): the output table for launches
-// with more than two segments, and the split-K workspace.
+// with more than two segments, the split-K workspace and the epilogue.
 struct Tail {
   OutTable out;
   float* partial;      // [S][n_rows][M] when S > 1
   uint32_t* counters;  // one per row block when S > 1, zero between calls
+  Epi epi;
 };
 
 constexpr int pow2ceil(int v) {

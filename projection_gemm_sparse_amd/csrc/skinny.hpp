@@ -38,6 +38,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "epilogue.hpp"
 
 namespace fp {
 
@@ -72,8 +73,9 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   // the common single-group, unsplit case avoids the integer divisions
   const int P = geo & 0xff;
   const int Gv = (geo >> 8) & 0xff;
-  const int Sv = geo >> 16;
-  const bool simple = (geo >> 8) == (1 | (1 << 8));
+  const int Sv = (geo >> 16) & 0x1fff;
+  const bool simple = ((geo >> 8) & 0x1fffff) == (1 | (1 << 8));
+  const bool epi = (geo & kGeoEpi) != 0;
   const int p = simple ? wave : wave % P;
   const int gq = simple ? 0 : wave / P;
   const int rb = simple ? (int)blockIdx.x : (int)blockIdx.x / Sv;
@@ -126,6 +128,13 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   float* partial = a.partial;
   uint32_t* counters = a.counters;
   if (Sv > 1) asm volatile("" : "+s"(partial), "+s"(counters));
+  uint32_t* ecounter = nullptr;
+  int eblocks = 0;
+  if (epi) {
+    ecounter = a.epi.counter;
+    eblocks = a.epi.n_blocks;
+    asm volatile("" : "+s"(ecounter), "+s"(eblocks));
+  }
   __builtin_amdgcn_sched_barrier(0);
   // activations past M or past K count as zero
 #pragma unroll
@@ -171,6 +180,8 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
         if (idx < V && m < M && row < n_rows) store_y<BF16>(om, a.out, row, m, v[q]);
       }
     }
+    if (epi) epi_finish(a.out, a.epi, ecounter, eblocks, M, Gv * P * 64,
+                        reinterpret_cast<unsigned char*>(smem));
     return;
   }
   // wave sums to LDS, transposed: output idx of row group gq owns 16
@@ -200,7 +211,11 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
       }
     }
   }
-  if (Sv == 1) return;
+  if (Sv == 1) {
+    if (epi) epi_finish(a.out, a.epi, ecounter, eblocks, M, Gv * P * 64,
+                        reinterpret_cast<unsigned char*>(smem));
+    return;
+  }
 
   // 6. split-K: the last workgroup of the row block adds the S partials
   splitk_finish<BF16>(n_rows, partial, counters, rb, Sv, row_base, (int64_t)Gv * RW, M,

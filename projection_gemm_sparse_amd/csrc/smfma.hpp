@@ -48,6 +48,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "epilogue.hpp"
 
 namespace fp {
 
@@ -68,7 +69,8 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int RT = geo & 0xff;
   const int PK = (geo >> 8) & 0xff;
-  const int Gv = geo >> 16;
+  const int Gv = (geo >> 16) & 0xff;
+  const bool epi = (geo & kGeoEpi) != 0;
   const int p = Gv == 1 ? wave : wave % PK;
   const int g2 = Gv == 1 ? 0 : wave / PK;
   const int row_base = (int)blockIdx.x * (Gv * RT);
@@ -126,6 +128,13 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   }
   __builtin_amdgcn_sched_barrier(0);
   const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
+  uint32_t* ecounter = nullptr;
+  int eblocks = 0;
+  if (epi) {
+    ecounter = a.epi.counter;
+    eblocks = a.epi.n_blocks;
+    asm volatile("" : "+s"(ecounter), "+s"(eblocks));
+  }
   __builtin_amdgcn_sched_barrier(0);
   const bool tok_ok = r8 < M;
 
@@ -172,6 +181,8 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
       store_y<true>(om, a.out, row, m, sum);
     }
   }
+  if (epi) epi_finish(a.out, a.epi, ecounter, eblocks, M, Gv * PK * 64,
+                      reinterpret_cast<unsigned char*>(smem));
 }
 
 }  // namespace fp

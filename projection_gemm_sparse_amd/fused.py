@@ -160,6 +160,69 @@ class FusedProjection:
         ov = [None if ok else w.detach().contiguous() for ok, w in zip(intact, weights)]
         return self.forward_separate(x, out=out, w_override=ov, stream=stream)
 
+    # ------------------------------------------------------------ epilogues
+    def _gains(self, gammas):
+        if len(gammas) != len(self.N):
+            raise ValueError("one gain (or None) per projection")
+        ptrs = []
+        for i, g in enumerate(gammas):
+            if g is None:
+                ptrs.append(None)
+                continue
+            if g.dtype != torch.bfloat16 or g.device != self.device or g.dim() != 1 \
+                    or int(g.shape[0]) != self.N[i] or not g.is_contiguous():
+                raise ValueError("gain %d must be a dense bf16 [%d] tensor" % (i, self.N[i]))
+            ptrs.append(g.data_ptr())
+        return ptrs
+
+    def forward_rmsnorm(self, x: torch.Tensor, gammas, eps: float, out=None, stream=None):
+        """Fused projection + RMSNorm: projection i is normalised with gain
+        ``gammas[i]`` (bf16 [N_i]) or returned as is when that entry is None."""
+        self._check_x(x)
+        M = int(x.shape[0])
+        ys = self._outputs(M, out)
+        st = L.fp_forward_rmsnorm(x.data_ptr(), M, int(x.stride(0)), self.plan,
+                                  _stream_handle(stream), self._gains(gammas), eps,
+                                  [y.data_ptr() for y in ys])
+        L.check(st, "fp_forward_rmsnorm")
+        return ys
+
+    def forward_rmsnorm_separate(self, x: torch.Tensor, gammas, eps: float, stream=None):
+        """The unfused chain: one projection launch per projection, then one
+        RMSNorm launch per normalised projection (in place)."""
+        ptrs = self._gains(gammas)
+        ys = self.forward_separate(x, stream=stream)
+        M = int(x.shape[0])
+        for i, g in enumerate(ptrs):
+            if g is None:
+                continue
+            st = L.fp_rmsnorm(ys[i].data_ptr(), M, self.N[i], g, eps, ys[i].data_ptr(),
+                              _stream_handle(stream))
+            L.check(st, "fp_rmsnorm")
+        return ys
+
+    def forward_swiglu(self, x: torch.Tensor, out=None, stream=None):
+        """Fused gate/up + SwiGLU (a plan of two equal-width projections,
+        gate first): returns h, dense [M, N]."""
+        self._check_x(x)
+        M = int(x.shape[0])
+        h = out if out is not None else torch.empty(M, self.N[0], dtype=self.dtype,
+                                                    device=self.device)
+        st = L.fp_forward_swiglu(x.data_ptr(), M, int(x.stride(0)), self.plan,
+                                 _stream_handle(stream), h.data_ptr())
+        L.check(st, "fp_forward_swiglu")
+        return h
+
+    def forward_swiglu_separate(self, x: torch.Tensor, stream=None):
+        """The unfused chain: gate and up launches, then one SwiGLU launch
+        (written over the gate output)."""
+        g, u = self.forward_separate(x, stream=stream)
+        M = int(x.shape[0])
+        st = L.fp_swiglu(g.data_ptr(), u.data_ptr(), M, self.N[0], g.data_ptr(),
+                         _stream_handle(stream))
+        L.check(st, "fp_swiglu")
+        return g
+
     # ----------------------------------------------------------- tuning/query
     def query(self, M: int):
         st, path, lf, ls = L.fp_plan_query(self.plan, M)

@@ -176,3 +176,37 @@ def test_default_crossover():
         assert P.fp_default_tiling(1, 7168, 192, M, 192)[1][0] in (1, 2)
     for M in (9, 16, 32, 64, 128):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA
+
+
+def test_epilogue_argument_checks_before_any_hip_call():
+    # standalone steps: every refusal happens before a launch
+    assert P.fp_rmsnorm(FAKE, -1, 1280, FAKE, 1e-6, FAKE, 0) == P.FP_ERR_INVALID_ARG
+    assert P.fp_rmsnorm(FAKE, 0, 1280, FAKE, 1e-6, FAKE, 0) == P.FP_OK  # nothing to do
+    assert P.fp_rmsnorm(FAKE, 2, 1280, FAKE, -1.0, FAKE + (1 << 20), 0) == P.FP_ERR_INVALID_ARG
+    assert P.fp_rmsnorm(FAKE, 2, 1280, FAKE, float("inf"), FAKE, 0) == P.FP_ERR_INVALID_ARG
+    assert P.fp_rmsnorm(FAKE, 2, 1284, FAKE + (1 << 24), 1e-6, FAKE + (2 << 24), 0) \
+        == P.FP_ERR_UNSUPPORTED
+    assert P.fp_rmsnorm(FAKE, 2, 4096, FAKE + (1 << 24), 1e-6, FAKE + (2 << 24), 0) \
+        == P.FP_ERR_UNSUPPORTED  # wider than one wave's four chunks per lane
+    assert P.fp_rmsnorm(FAKE + 8, 2, 1280, FAKE + (1 << 24), 1e-6, FAKE + (2 << 24), 0) \
+        == P.FP_ERR_UNSUPPORTED  # misaligned
+    assert P.fp_rmsnorm(FAKE, 2, 1280, FAKE + (1 << 24), 1e-6, FAKE + 16, 0) \
+        == P.FP_ERR_INVALID_ARG  # partial overlap of out and y
+    assert P.fp_swiglu(FAKE, FAKE, -1, 768, FAKE, 0) == P.FP_ERR_INVALID_ARG
+    assert P.fp_swiglu(FAKE, FAKE, 0, 768, FAKE, 0) == P.FP_OK
+    assert P.fp_swiglu(FAKE, FAKE + (1 << 24), 2, 770, FAKE + (2 << 24), 0) \
+        == P.FP_ERR_UNSUPPORTED
+    assert P.fp_swiglu(FAKE, FAKE + (1 << 24), 2, 768, FAKE + 16, 0) == P.FP_ERR_INVALID_ARG
+    # fused forms on a null plan
+    assert P.fp_forward_rmsnorm(FAKE, 1, 5120, None, 0, [None, None], 1e-6,
+                                [FAKE, FAKE]) == P.FP_ERR_INVALID_ARG
+    assert P.fp_forward_swiglu(FAKE, 1, 5120, None, 0, FAKE) == P.FP_ERR_INVALID_ARG
+
+
+def test_workspace_holds_epilogue_staging():
+    # an epilogue call stages M <= 8 bf16 rows of every projection after the
+    # counters (one per row plus the epilogue's, 256-byte rounded)
+    n = 768 + 768
+    ws = P.fp_workspace_bytes(0, 6144, [768, 768], 8)
+    counters = ((n + 1) * 4 + 255) // 256 * 256
+    assert ws >= counters + 8 * n * 2
