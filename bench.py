@@ -214,6 +214,90 @@ def crossover(path, P, torch, dev, plans, n_copies):
                    "rows": rows}, fh, indent=1)
 
 
+def epilogue_cells(P, torch, dev, plans, n_copies, steps, Ms=(1, 2, 4, 8)):
+    """The fused epilogues on rotated pools, next to their unfused chains.
+
+    RMSNorm (q_norm / kv_norm over the wq_a / wkv outputs) on the main pool:
+    fused (the fused projection, then one normalisation launch for both
+    projections) vs the unfused chain (one projection launch per projection,
+    then one RMSNorm launch per projection).  SwiGLU on a pool of gate/up
+    weights [2 x 768, 6144] (past the MALL as well): fused (one launch over
+    gate/up row pairs) vs gate and up launches followed by the SwiGLU
+    launch."""
+    L = P._lib
+    eps = 1e-6
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    gammas = [(1.0 + 0.1 * torch.randn(n, generator=g, device="cuda")).to(torch.bfloat16)
+              for n in N]
+    res = {"rmsnorm": {}, "swiglu": {}}
+    for M in Ms:
+        xc, _ = __import__("synthetic_inputs").make_case(K, N, "bf16", M, seed=300 + M)
+        x = xc.to(dev)
+        outs = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
+
+        def fused():
+            for p in plans:
+                p.forward_rmsnorm(x, gammas, eps, out=outs)
+
+        def chain():
+            s = torch.cuda.current_stream().cuda_stream
+            for p in plans:
+                p.forward_separate(x, out=outs)
+                for i, n in enumerate(N):
+                    L.check(L.fp_rmsnorm(outs[i].data_ptr(), M, n, gammas[i].data_ptr(), eps,
+                                         outs[i].data_ptr(), s), "fp_rmsnorm")
+        gf, gc = capture(torch, fused), capture(torch, chain)
+        (tf, _), (tc, _) = time_graphs(torch, [gf], steps, 2), time_graphs(torch, [gc], steps, 2)
+        b = algorithmic_bytes(M, K, N) + 2 * sum(N)
+        uf, uc = tf * 1e3 / (steps * n_copies), tc * 1e3 / (steps * n_copies)
+        res["rmsnorm"][str(M)] = {"fused_us": round(uf, 4), "unfused_us": round(uc, 4),
+                                  "fused_launches": 2, "unfused_launches": 2 * len(N),
+                                  "fused_GBps": round(b / uf / 1e3, 1), "bytes": b}
+        del gf, gc
+    # gate/up pool
+    Kg, Ng = 6144, (768, 768)
+    wb = sum(Ng) * Kg * 2
+    ng = max(2, math.ceil((1 << 30) / wb))
+    a = 1.0 / math.sqrt(Kg)
+    gplans = []
+    for _ in range(ng):
+        ws = [((torch.rand(n, Kg, generator=g, device="cuda") * 2 - 1) * a).to(torch.bfloat16)
+              for n in Ng]
+        gplans.append(P.FusedProjection(ws, max_M=8))
+        del ws
+    for M in Ms:
+        xc, _ = __import__("synthetic_inputs").make_case(Kg, Ng, "bf16", M, seed=400 + M)
+        x = xc.to(dev)
+        h = torch.empty(M, Ng[0], dtype=torch.bfloat16, device=dev)
+        gu = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in Ng]
+
+        def fused():
+            for p in gplans:
+                p.forward_swiglu(x, out=h)
+
+        def chain():
+            s = torch.cuda.current_stream().cuda_stream
+            for p in gplans:
+                p.forward_separate(x, out=gu)
+                L.check(L.fp_swiglu(gu[0].data_ptr(), gu[1].data_ptr(), M, Ng[0], h.data_ptr(),
+                                    s), "fp_swiglu")
+        gf, gc = capture(torch, fused), capture(torch, chain)
+        (tf, _), (tc, _) = time_graphs(torch, [gf], steps, 2), time_graphs(torch, [gc], steps, 2)
+        b = 2 * (sum(Ng) * Kg + M * Kg + M * Ng[0])
+        uf, uc = tf * 1e3 / (steps * ng), tc * 1e3 / (steps * ng)
+        res["swiglu"][str(M)] = {"fused_us": round(uf, 4), "unfused_us": round(uc, 4),
+                                 "fused_launches": 1, "unfused_launches": 3,
+                                 "fused_GBps": round(b / uf / 1e3, 1), "bytes": b}
+        del gf, gc
+    for p in gplans:
+        p.close()
+    res["note"] = ("us per call on pools rotated past the MALL (rmsnorm: %d wq_a+wkv copies; "
+                   "swiglu: %d gate/up [2x768, 6144] copies); unfused = one projection launch "
+                   "per projection, then the standalone epilogue launch(es)" % (n_copies, ng))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +312,8 @@ def main():
     ap.add_argument("--fused-only", action="store_true",
                     help="skip the one-launch-per-projection timing (profiler runs: every "
                          "dispatch of a kernel is then a fused call)")
+    ap.add_argument("--no-epilogues", action="store_true",
+                    help="skip the fused RMSNorm / SwiGLU epilogue cells")
     ap.add_argument("--crossover", default="",
                     help="also time every kernel path per M in 1..128 and write the table here")
     args = ap.parse_args()
@@ -397,6 +483,9 @@ def main():
         "context": {"pages_sm107_fused_m1_us": 4.13,
                     "note": "Vera Rubin figure from the pages, other hardware"},
     }
+    if not args.no_epilogues and not args.fused_only:
+        line["epilogues"] = epilogue_cells(P, torch, dev, plans, n_copies,
+                                           max(3, args.steps // 4))
     if args.crossover:
         crossover(args.crossover, P, torch, dev, plans, n_copies)
     print(json.dumps(line), flush=True)

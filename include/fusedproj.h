@@ -149,15 +149,12 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx,
                               const void* const* w_override);
 
 /* ---------------------------------------------------------------------
- * Epilogues: the step that consumes the projection, applied inside the same
- * launch.  Both read the projection after its single rounding to bf16, as
- * the unfused chain (projection, then a second kernel) does, and both give
- * results bitwise equal to that chain (fp_forward_separate followed by
- * fp_rmsnorm / fp_swiglu on its outputs).  The fused forms serve bf16 plans
- * with 1 <= M <= 8 on the unsplit one-launch kernels; other cases return
- * FP_ERR_UNSUPPORTED with no launch (the caller then runs the unfused
- * chain).  They stage the bf16 projection in the plan's workspace, so they
- * share the plan's rule that its calls must not overlap in time.
+ * Epilogues: the step that consumes the projection.  Both read the
+ * projection after its single rounding to bf16, as the unfused chain (one
+ * projection launch per projection, then a second kernel) does, and both
+ * give results bitwise equal to that chain (fp_forward_separate followed by
+ * fp_rmsnorm / fp_swiglu on its outputs).  bf16 plans only; other cases
+ * return FP_ERR_UNSUPPORTED with no launch.
  * --------------------------------------------------------------------- */
 
 /* Fused projection + RMSNorm per projection (q_norm over the q_a columns and
@@ -166,6 +163,11 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx,
  *     v = bf16(x . W_i^T)                      (the projection, rounded once)
  *     out_i[m, j] = bf16( v[m, j] * rinv_m * gamma_i[j] ),
  *     rinv_m = 1 / sqrt( (1/N_i) sum_j v[m, j]^2 + eps )     (fp32 arithmetic)
+ * Two launches for any number of projections: the fused projection into
+ * out[], then one normalisation launch over every normalised (projection,
+ * token) row, in place.  (A finish inside the projection launch was measured
+ * slower on MI355X: its cross-workgroup arrival alone costs about a kernel
+ * boundary.)  Serves every M the plan's fused call serves.
  * gamma: host array of n_proj entries; entry i is a device bf16 [N_i] gain
  *   (16-byte aligned, N_i a multiple of 8, N_i <= 2048) or NULL, in which
  *   case out_i receives the projection itself.
@@ -178,13 +180,16 @@ fp_status fp_forward_rmsnorm(const void* x, int64_t M, int64_t ldx,
                              const void* const* gamma, float eps,
                              void* const* out);
 
-/* Fused gate/up projection + SwiGLU (dense-MLP commit of PR #20502): the plan
- * holds exactly two projections of equal width N (the gate rows, then the
- * up rows, N a multiple of 8), and
+/* Fused gate/up projection + SwiGLU (dense-MLP commit of PR #20502), one
+ * launch: the plan holds exactly two projections of equal width N (the gate
+ * rows, then the up rows, N a multiple of 8); the launch takes the rows in
+ * (gate j, up j) pairs so that one workgroup owns both rows of an output
+ * column, and
  *     g = bf16(x . W_gate^T),  u = bf16(x . W_up^T)
  *     h[m, j] = bf16( g / (1 + exp(-g)) * u )     (fp32 arithmetic)
- * h: device, dense [M, N] bf16, 16-byte aligned, no overlap with x, w_cat or
- * the workspace.  FP_ERR_INVALID_ARG if the plan is not such a pair. */
+ * 1 <= M <= 8.  h: device, dense [M, N] bf16, 16-byte aligned, no overlap
+ * with x, w_cat or the workspace.  FP_ERR_INVALID_ARG if the plan is not
+ * such a pair. */
 fp_status fp_forward_swiglu(const void* x, int64_t M, int64_t ldx,
                             fp_plan_t plan, void* stream, void* h);
 

@@ -98,17 +98,8 @@ int mfma_mt16(int64_t M) {
   return t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 16;
 }
 
-// Arrival counters: one per row block of a split-K launch (at most n_total)
-// and, at index n_total, the epilogue's.
 int64_t counters_bytes(int64_t n_total) {
-  return ceil_div((n_total + 1) * 4, 256) * 256;
-}
-
-// Staged bf16 projection outputs of an epilogue call: segment i's dense
-// [M, N_i] rows at byte offset kEpiMaxM * off_i * 2 past the counters (the
-// same region as the split-K partials, which an epilogue call never uses).
-int64_t staging_bytes(int32_t dtype, int64_t n_total) {
-  return dtype == FP_BF16 ? (int64_t)fp::kEpiMaxM * n_total * 2 : 0;
+  return ceil_div(n_total * 4, 256) * 256;
 }
 
 // ------------------------------------------------------------------ tilings
@@ -235,13 +226,13 @@ bool default_smfma_order(int64_t kc, Tiling* t) {
 // ceil(ceil(n_rows / R) / CUs) * R (ties: the larger R, fewer workgroups);
 // RW <= min(8, 64 / MT) and G * P waves fit one workgroup.  Without a
 // one-round choice the largest R is taken.
-void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t) {
+void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs) {
   const int rw_max = std::min(8, 64 / mt);
   const int64_t rows = n_rows * t->splits;  // work units: (row, K slice)
   if (t->rows > 0 && t->groups > 0) return;
-  int best_rw = 1, best_g = 1;
+  int best_rw = pairs ? 2 : 1, best_g = 1;
   int64_t best_cost = INT64_MAX;
-  for (int rw = 1; rw <= rw_max; ++rw) {
+  for (int rw = pairs ? 2 : 1; rw <= rw_max; rw += pairs ? 2 : 1) {
     if (t->rows > 0 && rw != t->rows) continue;
     const int g_cap = std::max(1, fp::skinny_max_threads(t->mt, rw, t->chunks) / (64 * t->kparts));
     for (int g = 1; g <= g_cap; ++g) {
@@ -269,11 +260,11 @@ void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t) {
 // Rows per tile (<= 8) and row groups per workgroup of the small-M
 // matrix-core kernel, by the same one-round, least-loaded-CU rule as the
 // skinny kernel.
-void resolve_smfma_rows(int64_t n_rows, Tiling* t) {
+void resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs) {
   if (t->rows > 0 && t->groups > 0) return;
-  int best_rt = 1, best_g = 1;
+  int best_rt = pairs ? 2 : 1, best_g = 1;
   int64_t best_cost = INT64_MAX;
-  for (int rt = 1; rt <= 8; ++rt) {
+  for (int rt = pairs ? 2 : 1; rt <= 8; rt += pairs ? 2 : 1) {
     if (t->rows > 0 && rt != t->rows) continue;
     const int g_cap = std::max(1, fp::smfma_max_threads(t->chunks) / (64 * t->kparts));
     for (int g = 1; g <= g_cap; ++g) {
@@ -367,7 +358,8 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
 
 // The tiling for (M, launch rows); the summation-order fields come from the
 // plan's default or the user's override for M and never from n_rows.
-bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t) {
+bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
+                   bool pairs = false) {
   *t = Tiling();
   if (M >= 1 && M <= FP_MAX_M && p->has_override[M]) {
     const fp_tiling& o = p->override_t[M];
@@ -400,12 +392,14 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t) {
   } else if (t->path == FP_PATH_MFMA_SMALL) {
     t->mt = 8;
     if (t->kparts < 1 || t->chunks < 1) return false;
-    resolve_smfma_rows(n_rows, t);
+    resolve_smfma_rows(n_rows, t, pairs);
   } else {
     t->mt = skinny_mt(M);
     if (t->kparts < 1) return false;
-    resolve_skinny_rows(n_rows, t->mt, t);
+    resolve_skinny_rows(n_rows, t->mt, t, pairs);
   }
+  // a gate/up launch keeps both rows of a pair in one row group
+  if (pairs && (t->rows % 2 != 0 || t->splits != 1)) return false;
   return tiling_valid(p, M, n_rows, *t);
 }
 
@@ -448,11 +442,42 @@ size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) 
       most = std::max(most, partial_floats(t, n_total, M));
     }
   }
-  most = std::max(most, ceil_div(staging_bytes(dtype, n_total), 4));
   return (size_t)(counters_bytes(n_total) + most * 4);
 }
 
 // ------------------------------------------------------------------ kernels
+// Gate/up launches (PAIRS): bf16, an even number of rows per wave, one or
+// two chunks per lane.
+template <int MT, int CJ>
+const void* skinny_pairs_fn_rw(int rw) {
+  switch (rw) {
+    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, true>);
+    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, true>);
+    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, true, true>);
+    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, true>);
+    default: return nullptr;
+  }
+}
+
+template <int MT>
+const void* skinny_pairs_fn_cj(int cj, int rw) {
+  switch (cj) {
+    case 1: return skinny_pairs_fn_rw<MT, 1>(rw);
+    case 2: return skinny_pairs_fn_rw<MT, 2>(rw);
+    default: return nullptr;
+  }
+}
+
+const void* skinny_pairs_fn(int mt, int cj, int rw) {
+  switch (mt) {
+    case 1: return skinny_pairs_fn_cj<1>(cj, rw);
+    case 2: return skinny_pairs_fn_cj<2>(cj, rw);
+    case 4: return skinny_pairs_fn_cj<4>(cj, rw);
+    case 8: return skinny_pairs_fn_cj<8>(cj, rw);
+    default: return nullptr;
+  }
+}
+
 template <int MT, int CJ, bool BF16>
 const void* skinny_fn_rw(int rw) {
   switch (rw) {
@@ -586,16 +611,16 @@ struct LaunchRows {
   int begin[fp::kMaxSeg + 1];
 };
 
-template <int KT>
+template <int KT, bool PAIRS>
 const void* smfma_fn_kt() {
-  return reinterpret_cast<const void*>(&fp::smfma_kernel<KT>);
+  return reinterpret_cast<const void*>(&fp::smfma_kernel<KT, PAIRS>);
 }
 
-const void* smfma_fn(const Tiling& t) {
+const void* smfma_fn(const Tiling& t, bool pairs) {
   switch (t.chunks) {
-    case 4: return smfma_fn_kt<4>();
-    case 8: return smfma_fn_kt<8>();
-    case 16: return smfma_fn_kt<16>();
+    case 4: return pairs ? smfma_fn_kt<4, true>() : smfma_fn_kt<4, false>();
+    case 8: return pairs ? smfma_fn_kt<8, true>() : smfma_fn_kt<8, false>();
+    case 16: return pairs ? smfma_fn_kt<16, true>() : smfma_fn_kt<16, false>();
     default: return nullptr;
   }
 }
@@ -608,7 +633,7 @@ const void* smfma_fn(const Tiling& t) {
 // segments, split-K workspace).
 fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
               const void* x, int64_t M, int64_t ldx, hipStream_t stream,
-              const fp::Epi* epi = nullptr) {
+              bool pairs = false) {
   const unsigned char* w_a = lr.w;
   const unsigned char* x_a = static_cast<const unsigned char*>(x);
   unsigned char* y0_a = lr.y[0];
@@ -631,23 +656,13 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   int32_t geo_a = 0;
   void* args[] = {&w_a, &x_a, &y0_a, &y1_a, &ldx_a, &n_rows_a, &kc_a, &M_a, &split_a,
                   &geo_a, &tail};
-  size_t epi_lds = 0;
-  if (epi != nullptr) {
-    // only the unsplit vector-ALU and small-M matrix-core launches finish an
-    // epilogue (checked by the caller)
-    tail.epi = *epi;
-    bool normed[fp::kMaxSeg];
-    for (int i = 0; i < fp::kMaxSeg; ++i) normed[i] = i < lr.n_seg && epi->gamma[i] != nullptr;
-    epi_lds = fp::epi_lds_bytes(epi->mode, (int)M, lr.n_seg, lr.begin, normed);
-  }
   if (t.path == FP_PATH_MFMA_SMALL) {
-    geo_a = t.rows | (t.kparts << 8) | (t.groups << 16) | (epi ? fp::kGeoEpi : 0);
+    geo_a = t.rows | (t.kparts << 8) | (t.groups << 16);
     const int64_t R = (int64_t)t.rows * t.groups;
-    const int64_t blocks = ceil_div(lr.n_rows, R);
-    tail.epi.n_blocks = (int32_t)blocks;
-    return launch(smfma_fn(t), blocks, t.groups * t.kparts * 64,
-                  std::max(smfma_lds(t), epi_lds), args, stream);
+    return launch(smfma_fn(t, pairs), ceil_div(lr.n_rows, R), t.groups * t.kparts * 64,
+                  smfma_lds(t), args, stream);
   }
+  if (pairs && t.path != FP_PATH_SKINNY) return FP_ERR_UNSUPPORTED;
   if (t.path == FP_PATH_MFMA) {
     geo_a = t.splits;
     const int64_t per = ceil_div(ceil_div(p->kc, 4), t.splits);
@@ -655,14 +670,13 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
     const size_t lds = std::max<size_t>(tile_lds(t.mt, per, t.kparts), 16);
     return launch(mfma_fn(t), blocks, t.kparts * 64, lds, args, stream);
   }
-  geo_a = t.kparts | (t.groups << 8) | (t.splits << 16) | (epi ? fp::kGeoEpi : 0);
+  geo_a = t.kparts | (t.groups << 8) | (t.splits << 16);
   const int64_t R = (int64_t)t.groups * t.rows;
   const int64_t blocks = ceil_div(lr.n_rows, R) * t.splits;
-  tail.epi.n_blocks = (int32_t)blocks;
-  const void* fn = p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
-                                       : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
-  return launch(fn, blocks, t.groups * t.kparts * 64, std::max(skinny_lds(t), epi_lds), args,
-                stream);
+  const void* fn = pairs ? skinny_pairs_fn(t.mt, t.chunks, t.rows)
+                   : p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
+                                         : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
+  return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
@@ -895,38 +909,52 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx, fp_plan_t p
   return FP_OK;
 }
 
+}  // extern "C"
+
 namespace {
-
-// The tiling of an epilogue call: the fused launch must be one unsplit
-// vector-ALU or small-M matrix-core launch (those kernels carry the finish).
-fp_status epi_tiling(const fp_plan_s* p, int64_t M, Tiling* t) {
-  if (!choose_tiling(p, M, p->n_total, t)) return FP_ERR_UNSUPPORTED;
-  if (t->splits != 1 || !(t->path == FP_PATH_SKINNY || t->path == FP_PATH_MFMA_SMALL))
-    return FP_ERR_UNSUPPORTED;
-  return FP_OK;
-}
-
-unsigned char* staging(const fp_plan_s* p, int i) {
-  return p->ws + counters_bytes(p->n_total) + (int64_t)fp::kEpiMaxM * p->off[i] * 2;
-}
 
 bool range_overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   return overlaps(a0, a0 + (uintptr_t)a_bytes, b0, b0 + (uintptr_t)b_bytes);
 }
 
-LaunchRows fused_rows(const fp_plan_s* p) {
+// The fused launch over every projection of a plan, output i to y[i].
+LaunchRows fused_rows(const fp_plan_s* p, void* const* y) {
   LaunchRows lr;
   std::memset(&lr, 0, sizeof lr);
   lr.w = p->w_cat;
   lr.n_seg = p->n_proj;
   lr.n_rows = (int)p->n_total;
-  for (int i = 0; i < p->n_proj; ++i) lr.begin[i] = (int)p->off[i];
+  for (int i = 0; i < p->n_proj; ++i) {
+    lr.begin[i] = (int)p->off[i];
+    lr.y[i] = static_cast<unsigned char*>(y[i]);
+  }
   lr.begin[p->n_proj] = (int)p->n_total;
   return lr;
 }
 
+// One RMSNorm launch over `n` tensors (host validated), M rows each.
+fp_status launch_rmsnorm(int n, const unsigned char* const* y, const unsigned char* const* gamma,
+                         unsigned char* const* out, const int64_t* N, int64_t M, float eps,
+                         hipStream_t stream) {
+  fp::NormTable t;
+  std::memset(&t, 0, sizeof t);
+  for (int i = 0; i < n; ++i) {
+    t.y[i] = y[i];
+    t.gamma[i] = gamma[i];
+    t.out[i] = out[i];
+    t.N[i] = (int32_t)N[i];
+  }
+  t.M = (int32_t)M;
+  t.eps = eps;
+  void* args[] = {&t};
+  return launch(reinterpret_cast<const void*>(&fp::rmsnorm_kernel), (int64_t)n * M, 64, 0, args,
+                stream);
+}
+
 }  // namespace
+
+extern "C" {
 
 fp_status fp_forward_rmsnorm(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
                              void* stream, const void* const* gamma, float eps,
@@ -937,9 +965,14 @@ fp_status fp_forward_rmsnorm(const void* x, int64_t M, int64_t ldx, fp_plan_t pl
   fp_status s = check_x(plan, M, x, ldx);
   if (s != FP_OK) return s;
   if (M == 0) return FP_OK;
-  if (plan->dtype != FP_BF16 || M > fp::kEpiMaxM) return FP_ERR_UNSUPPORTED;
+  if (plan->dtype != FP_BF16) return FP_ERR_UNSUPPORTED;
   s = check_outputs(plan, M, x, ldx, out);
   if (s != FP_OK) return s;
+  int n = 0;
+  const unsigned char* ny[FP_MAX_PROJ];
+  const unsigned char* ng[FP_MAX_PROJ];
+  unsigned char* no[FP_MAX_PROJ];
+  int64_t nn[FP_MAX_PROJ];
   for (int i = 0; i < plan->n_proj; ++i) {
     if (gamma[i] == nullptr) continue;
     const int64_t N = plan->N[i];
@@ -947,26 +980,19 @@ fp_status fp_forward_rmsnorm(const void* x, int64_t M, int64_t ldx, fp_plan_t pl
     if (!aligned(out[i], 16) || !aligned(gamma[i], 16)) return FP_ERR_UNSUPPORTED;
     for (int j = 0; j < plan->n_proj; ++j)
       if (range_overlaps(gamma[i], N * 2, out[j], M * plan->N[j] * 2)) return FP_ERR_INVALID_ARG;
+    ny[n] = static_cast<const unsigned char*>(out[i]);
+    ng[n] = static_cast<const unsigned char*>(gamma[i]);
+    no[n] = static_cast<unsigned char*>(out[i]);
+    nn[n] = N;
+    ++n;
   }
+  if ((int64_t)n * M > INT32_MAX) return FP_ERR_UNSUPPORTED;
   Tiling t;
-  s = epi_tiling(plan, M, &t);
-  if (s != FP_OK) return s;
-  LaunchRows lr = fused_rows(plan);
-  fp::Epi e;
-  std::memset(&e, 0, sizeof e);
-  bool normed[fp::kMaxSeg] = {};
-  for (int i = 0; i < plan->n_proj; ++i) {
-    normed[i] = gamma[i] != nullptr;
-    lr.y[i] = normed[i] ? staging(plan, i) : static_cast<unsigned char*>(out[i]);
-    e.out[i] = static_cast<unsigned char*>(out[i]);
-    e.gamma[i] = static_cast<const unsigned char*>(gamma[i]);
-  }
-  if (fp::epi_lds_bytes(fp::kEpiRmsNorm, (int)M, lr.n_seg, lr.begin, normed) > kMaxLds)
-    return FP_ERR_UNSUPPORTED;
-  e.counter = reinterpret_cast<uint32_t*>(plan->ws) + plan->n_total;
-  e.mode = fp::kEpiRmsNorm;
-  e.eps = eps;
-  return run(plan, t, lr, x, M, ldx, static_cast<hipStream_t>(stream), &e);
+  if (!choose_tiling(plan, M, plan->n_total, &t)) return FP_ERR_UNSUPPORTED;
+  // the projection writes every output; the normalisation then works in place
+  s = run(plan, t, fused_rows(plan, out), x, M, ldx, static_cast<hipStream_t>(stream));
+  if (s != FP_OK || n == 0) return s;
+  return launch_rmsnorm(n, ny, ng, no, nn, M, eps, static_cast<hipStream_t>(stream));
 }
 
 fp_status fp_forward_swiglu(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
@@ -978,27 +1004,19 @@ fp_status fp_forward_swiglu(const void* x, int64_t M, int64_t ldx, fp_plan_t pla
   if (M == 0) return FP_OK;
   if (h == nullptr) return FP_ERR_INVALID_ARG;
   const int64_t N = plan->N[0];
-  if (plan->dtype != FP_BF16 || M > fp::kEpiMaxM || N % 8 != 0) return FP_ERR_UNSUPPORTED;
+  if (plan->dtype != FP_BF16 || M > kSkinnyMaxM || N % 8 != 0) return FP_ERR_UNSUPPORTED;
   if (!aligned(h, 16)) return FP_ERR_UNSUPPORTED;
   const int64_t hb = M * N * 2;
   if (range_overlaps(h, hb, x, ((M - 1) * ldx + plan->K) * 2) ||
       range_overlaps(h, hb, plan->w_cat, plan->n_total * plan->K * 2) ||
       range_overlaps(h, hb, plan->ws, (int64_t)plan->ws_bytes))
     return FP_ERR_INVALID_ARG;
+  // one launch over the 2N rows taken in (gate j, up j) pairs
   Tiling t;
-  s = epi_tiling(plan, M, &t);
-  if (s != FP_OK) return s;
-  LaunchRows lr = fused_rows(plan);
-  lr.y[0] = staging(plan, 0);
-  lr.y[1] = staging(plan, 1);
-  if (fp::epi_lds_bytes(fp::kEpiSwiglu, (int)M, lr.n_seg, lr.begin, nullptr) > kMaxLds)
-    return FP_ERR_UNSUPPORTED;
-  fp::Epi e;
-  std::memset(&e, 0, sizeof e);
-  e.out[0] = static_cast<unsigned char*>(h);
-  e.counter = reinterpret_cast<uint32_t*>(plan->ws) + plan->n_total;
-  e.mode = fp::kEpiSwiglu;
-  return run(plan, t, lr, x, M, ldx, static_cast<hipStream_t>(stream), &e);
+  if (!choose_tiling(plan, M, plan->n_total, &t, true)) return FP_ERR_UNSUPPORTED;
+  if (!(t.path == FP_PATH_SKINNY || t.path == FP_PATH_MFMA_SMALL)) return FP_ERR_UNSUPPORTED;
+  void* hh[2] = {h, h};
+  return run(plan, t, fused_rows(plan, hh), x, M, ldx, static_cast<hipStream_t>(stream), true);
 }
 
 fp_status fp_rmsnorm(const void* y, int64_t M, int64_t N, const void* gamma, float eps,
@@ -1014,11 +1032,7 @@ fp_status fp_rmsnorm(const void* y, int64_t M, int64_t N, const void* gamma, flo
   const unsigned char* y_a = static_cast<const unsigned char*>(y);
   const unsigned char* g_a = static_cast<const unsigned char*>(gamma);
   unsigned char* o_a = static_cast<unsigned char*>(out);
-  int32_t n_a = (int32_t)N;
-  float eps_a = eps;
-  void* args[] = {&y_a, &g_a, &o_a, &n_a, &eps_a};
-  return launch(reinterpret_cast<const void*>(&fp::rmsnorm_kernel), M, 64, 0, args,
-                static_cast<hipStream_t>(stream));
+  return launch_rmsnorm(1, &y_a, &g_a, &o_a, &N, M, eps, static_cast<hipStream_t>(stream));
 }
 
 fp_status fp_swiglu(const void* g, const void* u, int64_t M, int64_t N, void* h,

@@ -35,38 +35,23 @@ struct OutTable {
   int32_t n_seg;
 };
 
-// Epilogue applied after the projection inside the same launch (set when
-// the geometry word carries kGeoEpi): the launch's outputs y[i] of the
-// output table are then staging buffers in the workspace, and the last
-// workgroup to finish reads them back and writes the final tensors.
-//   mode     kEpiRmsNorm: out[i] = RMSNorm(y_i) * gamma[i] for every segment
-//            with gamma[i] != nullptr; segments without a gain are written
-//            straight to their final tensor by the projection itself.
-//            kEpiSwiglu: out[0] = silu(y_0) * y_1 (two segments of equal
-//            width: gate rows, then up rows).
-//   counter  arrival counter (zero between calls; reset by the finisher)
-//   n_blocks workgroups of the launch
-constexpr int kEpiRmsNorm = 1;
-constexpr int kEpiSwiglu = 2;
-constexpr int kGeoEpi = 1 << 29;  // geometry-word flag: run the epilogue
-
-struct Epi {
-  unsigned char* out[kMaxSeg];
-  const unsigned char* gamma[kMaxSeg];
-  uint32_t* counter;
-  int32_t n_blocks;
-  int32_t mode;
-  float eps;
-};
-
 // Trailing kernel argument (not preloaded): the output table for launches
-// with more than two segments, the split-K workspace and the epilogue.
+// with more than two segments, and the split-K workspace.
 struct Tail {
   OutTable out;
   float* partial;      // [S][n_rows][M] when S > 1
   uint32_t* counters;  // one per row block when S > 1, zero between calls
-  Epi epi;
 };
+
+// Gate/up launches (the PAIRS variant of the kernels): the launch's n_rows =
+// 2N logical rows interleave the two halves of the weight buffer -- logical
+// row 2j is gate row j, 2j + 1 is up row j (buffer row N + j, N = split) --
+// so one row group holds both rows of a pair and writes
+// h[m, j] = silu(g) * u (g and u rounded to bf16 first) to y0, a dense
+// [M, N] tensor.  Buffer row of a logical row:
+__device__ __forceinline__ int pair_row(int row, int half) {
+  return (row >> 1) + (row & 1) * half;
+}
 
 constexpr int pow2ceil(int v) {
   int p = 1;

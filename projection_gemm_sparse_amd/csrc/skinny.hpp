@@ -55,7 +55,9 @@ namespace fp {
 // A K slice holds P * 64 * CJ chunks; a workgroup owns G * RW rows.  The
 // hardware preloads at most 14 argument dwords, exactly these; one more
 // would be read from memory before the first load could issue.
-template <int MT, int RW, int CJ, bool BF16>
+// PAIRS: a gate/up launch (rows taken in pairs, see pair_row; RW even,
+// S = 1, bf16) that writes silu(gate) * up instead of the projections.
+template <int MT, int RW, int CJ, bool BF16, bool PAIRS = false>
 __global__ void __launch_bounds__(skinny_max_threads(MT, RW, CJ))
 skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
               unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
@@ -73,9 +75,8 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   // the common single-group, unsplit case avoids the integer divisions
   const int P = geo & 0xff;
   const int Gv = (geo >> 8) & 0xff;
-  const int Sv = (geo >> 16) & 0x1fff;
-  const bool simple = ((geo >> 8) & 0x1fffff) == (1 | (1 << 8));
-  const bool epi = (geo & kGeoEpi) != 0;
+  const int Sv = geo >> 16;
+  const bool simple = (geo >> 8) == (1 | (1 << 8));
   const int p = simple ? wave : wave % P;
   const int gq = simple ? 0 : wave / P;
   const int rb = simple ? (int)blockIdx.x : (int)blockIdx.x / Sv;
@@ -113,7 +114,8 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   u32x4 wv[RW][CJ];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    const int row = wrow0 + r < n_rows ? wrow0 + r : n_rows - 1;
+    const int lrow = wrow0 + r < n_rows ? wrow0 + r : n_rows - 1;
+    const int row = PAIRS ? pair_row(lrow, split) : lrow;
     const u32x4* wrow = reinterpret_cast<const u32x4*>(w + (uint64_t)(uint32_t)row * row_bytes);
 #pragma unroll
     for (int j = 0; j < CJ; ++j) {
@@ -128,13 +130,6 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   float* partial = a.partial;
   uint32_t* counters = a.counters;
   if (Sv > 1) asm volatile("" : "+s"(partial), "+s"(counters));
-  uint32_t* ecounter = nullptr;
-  int eblocks = 0;
-  if (epi) {
-    ecounter = a.epi.counter;
-    eblocks = a.epi.n_blocks;
-    asm volatile("" : "+s"(ecounter), "+s"(eblocks));
-  }
   __builtin_amdgcn_sched_barrier(0);
   // activations past M or past K count as zero
 #pragma unroll
@@ -167,7 +162,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
 
   // 4. across the wave
   transpose_reduce<VP>(v, lane);
-  if (P == 1 && Sv == 1) {
+  if (P == 1 && Sv == 1 && !PAIRS) {
     // the wave holds whole rows: its lanes store the finished sums, no
     // workgroup barrier
     if (lane % LSTRIDE == 0) {
@@ -180,8 +175,6 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
         if (idx < V && m < M && row < n_rows) store_y<BF16>(om, a.out, row, m, v[q]);
       }
     }
-    if (epi) epi_finish(a.out, a.epi, ecounter, eblocks, M, Gv * P * 64,
-                        reinterpret_cast<unsigned char*>(smem));
     return;
   }
   // wave sums to LDS, transposed: output idx of row group gq owns 16
@@ -204,18 +197,20 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
     const int row = row_base + g2 * RW + r;
     if (m < M && row < n_rows) {
       const float sum = sum_wave_parts(smem + (g2 * VP + idx) * kMaxWaveParts, P);
-      if (Sv == 1) {
+      if constexpr (PAIRS) {
+        // even logical rows: gate row j, its up row in the next slot
+        if ((r & 1) == 0) {
+          const float u_sum = sum_wave_parts(smem + (g2 * VP + idx + MT) * kMaxWaveParts, P);
+          store_pair(y0, split, row, m, sum, u_sum);
+        }
+      } else if (Sv == 1) {
         store_y<BF16>(om, a.out, row, m, sum);
       } else {
         store_partial(partial + ((int64_t)s * n_rows + row) * M + m, sum);
       }
     }
   }
-  if (Sv == 1) {
-    if (epi) epi_finish(a.out, a.epi, ecounter, eblocks, M, Gv * P * 64,
-                        reinterpret_cast<unsigned char*>(smem));
-    return;
-  }
+  if (Sv == 1) return;
 
   // 6. split-K: the last workgroup of the row block adds the S partials
   splitk_finish<BF16>(n_rows, partial, counters, rb, Sv, row_base, (int64_t)Gv * RW, M,

@@ -58,7 +58,9 @@ constexpr int smfma_max_threads(int kt) {
 
 // Leading scalars preloaded into SGPRs (see skinny_kernel for w, x, y0,
 // y1, ldx, n_rows, kc, M, split); geo = RT | PK << 8 | G << 16.
-template <int KT>
+// PAIRS: a gate/up launch (rows taken in pairs, see pair_row; RT even)
+// that writes silu(gate) * up instead of the projections.
+template <int KT, bool PAIRS = false>
 __global__ void __launch_bounds__(smfma_max_threads(KT))
 smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
              unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
@@ -69,8 +71,7 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int RT = geo & 0xff;
   const int PK = (geo >> 8) & 0xff;
-  const int Gv = (geo >> 16) & 0xff;
-  const bool epi = (geo & kGeoEpi) != 0;
+  const int Gv = geo >> 16;
   const int p = Gv == 1 ? wave : wave % PK;
   const int g2 = Gv == 1 ? 0 : wave / PK;
   const int row_base = (int)blockIdx.x * (Gv * RT);
@@ -118,7 +119,8 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   u32x4 wv[KT];
   {
     const int rr = rl < RT ? row0 + rl : row0;
-    const int row = rr < n_rows ? rr : n_rows - 1;
+    const int lrow = rr < n_rows ? rr : n_rows - 1;
+    const int row = PAIRS ? pair_row(lrow, split) : lrow;
     const u32x4* wrow = reinterpret_cast<const u32x4*>(w + (uint64_t)(uint32_t)row * row_bytes);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
@@ -128,13 +130,6 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   }
   __builtin_amdgcn_sched_barrier(0);
   const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
-  uint32_t* ecounter = nullptr;
-  int eblocks = 0;
-  if (epi) {
-    ecounter = a.epi.counter;
-    eblocks = a.epi.n_blocks;
-    asm volatile("" : "+s"(ecounter), "+s"(eblocks));
-  }
   __builtin_amdgcn_sched_barrier(0);
   const bool tok_ok = r8 < M;
 
@@ -178,11 +173,18 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
       const float* q0 = smem + ((gg * 2 + 0) * 64 + r * 8 + m) * kMaxWaveParts;
       const float* q1 = smem + ((gg * 2 + 1) * 64 + r * 8 + m) * kMaxWaveParts;
       const float sum = sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK);
-      store_y<true>(om, a.out, row, m, sum);
+      if constexpr (PAIRS) {
+        // even logical rows: gate row j, its up row is tile row r + 1
+        if ((r & 1) == 0) {
+          const float u_sum = sum_wave_parts(q0 + 8 * kMaxWaveParts, PK) +
+                              sum_wave_parts(q1 + 8 * kMaxWaveParts, PK);
+          store_pair(y0, split, row, m, sum, u_sum);
+        }
+      } else {
+        store_y<true>(om, a.out, row, m, sum);
+      }
     }
   }
-  if (epi) epi_finish(a.out, a.epi, ecounter, eblocks, M, Gv * PK * 64,
-                      reinterpret_cast<unsigned char*>(smem));
 }
 
 }  // namespace fp

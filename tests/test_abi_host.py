@@ -201,12 +201,3 @@ def test_epilogue_argument_checks_before_any_hip_call():
     assert P.fp_forward_rmsnorm(FAKE, 1, 5120, None, 0, [None, None], 1e-6,
                                 [FAKE, FAKE]) == P.FP_ERR_INVALID_ARG
     assert P.fp_forward_swiglu(FAKE, 1, 5120, None, 0, FAKE) == P.FP_ERR_INVALID_ARG
-
-
-def test_workspace_holds_epilogue_staging():
-    # an epilogue call stages M <= 8 bf16 rows of every projection after the
-    # counters (one per row plus the epilogue's, 256-byte rounded)
-    n = 768 + 768
-    ws = P.fp_workspace_bytes(0, 6144, [768, 768], 8)
-    counters = ((n + 1) * 4 + 255) // 256 * 256
-    assert ws >= counters + 8 * n * 2

@@ -9,9 +9,11 @@ low-latency decode target for Rubin (TP16)", PR #20502).
 
 Every element is compared with the oracle's unrounded fp64 result under the
 derived bounds (``oracle.rmsnorm_bound`` / ``oracle.swiglu_bound``, pinned on
-the CPU); the fused call must be bitwise equal to the unfused chain (one
-projection launch per projection, then the standalone RMSNorm / SwiGLU
-kernel), to a repeat, and to graph replays.  Exact-sum data (every fp32
+the CPU); the fused call (RMSNorm: the fused projection and one
+normalisation launch; SwiGLU: one launch over gate/up row pairs) must be
+bitwise equal to the unfused chain (one projection launch per projection,
+then the standalone RMSNorm / SwiGLU kernel), to a repeat, and to graph
+replays.  Exact-sum data (every fp32
 partial sum exact) tightens the bounds to the rounding of the epilogue
 alone.
 """
@@ -160,6 +162,20 @@ def test_standalone_rmsnorm_in_place_and_bounds():
     assert ok, (worst, idx)
 
 
+@pytest.mark.parametrize("M", [9, 16])
+def test_rmsnorm_beyond_eight_tokens(M):
+    # the projection runs on the tile kernel, the normalisation launch is the same
+    x, ws = si.workload_case("crossover", M, 0)
+    g = torch.Generator().manual_seed(9)
+    gammas = [(1.0 + 0.1 * torch.randn(n, generator=g)).to(torch.bfloat16) for n in (1280, 512)]
+    fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=16)
+    xg = to_gpu(x)
+    gg = [to_gpu(t) for t in gammas]
+    outs = fp.forward_rmsnorm(xg, gg, EPS)
+    _check_norm(outs, x, ws, gammas, "M=%d" % M)
+    assert_bitwise_equal(outs, fp.forward_rmsnorm_separate(xg, gg, EPS), "chain M=%d" % M)
+
+
 def test_rmsnorm_refusals():
     x, ws, gammas = si.norm_case(8, 0)
     fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=16)
@@ -167,9 +183,9 @@ def test_rmsnorm_refusals():
     gp = [g.data_ptr() for g in g_dev]
     x16 = to_gpu(si.workload_case("crossover", 16, 0)[0])
     outs = [torch.empty(16, n, dtype=torch.bfloat16, device="cuda") for n in fp.N]
-    st = P.fp_forward_rmsnorm(x16.data_ptr(), 16, 5120, fp.plan, 0, gp, EPS,
+    st = P.fp_forward_rmsnorm(x16.data_ptr(), 17, 5120, fp.plan, 0, gp, EPS,
                               [o.data_ptr() for o in outs])
-    assert st == P.FP_ERR_UNSUPPORTED  # more than 8 tokens
+    assert st == P.FP_ERR_UNSUPPORTED  # above the plan's max_M
     st = P.fp_forward_rmsnorm(x16.data_ptr(), 4, 5120, fp.plan, 0, gp, -1.0,
                               [o.data_ptr() for o in outs])
     assert st == P.FP_ERR_INVALID_ARG  # negative eps
@@ -241,7 +257,9 @@ def test_swiglu_refusals():
     torch.cuda.synchronize()
 
 
-def test_epilogue_launch_count_is_one():
+def test_epilogue_launch_counts():
+    """RMSNorm: the projection launch plus one normalisation launch for all
+    normalised projections; SwiGLU: one launch."""
     from test_graph_gpu import _count_graph_nodes
     x, ws, gammas = si.norm_case(2, 0)
     fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=8)
@@ -249,9 +267,15 @@ def test_epilogue_launch_count_is_one():
     gg = [to_gpu(g) for g in gammas]
     outs = [torch.empty(2, n, dtype=torch.bfloat16, device="cuda") for n in fp.N]
     fp.forward_rmsnorm(xg, gg, EPS, out=outs)
+    xs, wsw = si.workload_case("gate_up_swiglu", 2, 0)
+    fs = P.FusedProjection([to_gpu(w) for w in wsw], max_M=8)
+    xsg = to_gpu(xs)
+    h = torch.empty(2, 768, dtype=torch.bfloat16, device="cuda")
+    fs.forward_swiglu(xsg, out=h)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        n = _count_graph_nodes(lambda: fp.forward_rmsnorm(xg, gg, EPS, out=outs, stream=s), s)
+        n_norm = _count_graph_nodes(lambda: fp.forward_rmsnorm(xg, gg, EPS, out=outs, stream=s), s)
+        n_swiglu = _count_graph_nodes(lambda: fs.forward_swiglu(xsg, out=h, stream=s), s)
     torch.cuda.synchronize()
-    assert n == 1
+    assert (n_norm, n_swiglu) == (2, 1)
