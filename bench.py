@@ -298,6 +298,37 @@ def epilogue_cells(P, torch, dev, plans, n_copies, steps, Ms=(1, 2, 4, 8)):
     return res
 
 
+def router_cells(P, torch, dev, steps, Ms=(1, 4, 8, 16)):
+    """The fp32-output router GEMV (256 expert logits at hidden 6144, bf16
+    operands) on a pool of weight copies rotated past the MALL."""
+    import synthetic_inputs as si
+    Kr, Nr = 6144, (256,)
+    wb = Nr[0] * Kr * 2
+    n = max(2, math.ceil((1 << 30) / wb))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    a = 1.0 / math.sqrt(Kr)
+    plans = [P.FusedProjection([((torch.rand(Nr[0], Kr, generator=g, device="cuda") * 2 - 1) * a)
+                                .to(torch.bfloat16)], max_M=16, out_dtype=torch.float32)
+             for _ in range(n)]
+    res = {}
+    for M in Ms:
+        x = si.make_case(Kr, Nr, "bf16", M, seed=500 + M)[0].to(dev)
+        out = [torch.empty(M, Nr[0], dtype=torch.float32, device=dev)]
+        gr = capture(torch, lambda: [p.forward(x, out=out) for p in plans])
+        t, _ = time_graphs(torch, [gr], steps, 2)
+        us = t * 1e3 / (steps * n)
+        b = wb + M * Kr * 2 + M * Nr[0] * 4
+        res[str(M)] = {"us": round(us, 4), "GBps": round(b / us / 1e3, 1), "bytes": b,
+                       "tiling": list(plans[0].get_tiling(M))}
+        del gr
+    for p in plans:
+        p.close()
+    res["note"] = ("fp32 logits of a [256, 6144] bf16 router weight, %d copies rotated "
+                   "(1 GiB), one call per copy, hipGraph replay" % n)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -486,6 +517,7 @@ def main():
     if not args.no_epilogues and not args.fused_only:
         line["epilogues"] = epilogue_cells(P, torch, dev, plans, n_copies,
                                            max(3, args.steps // 4))
+        line["router_f32"] = router_cells(P, torch, dev, max(3, args.steps // 4))
     if args.crossover:
         crossover(args.crossover, P, torch, dev, plans, n_copies)
     print(json.dumps(line), flush=True)

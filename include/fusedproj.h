@@ -214,6 +214,16 @@ fp_status fp_swiglu(const void* g, const void* u, int64_t M, int64_t N,
 fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path,
                         int32_t* launches_fused, int32_t* launches_separate);
 
+/* Output type of a plan's projections (default: the input type).  A bf16
+ * plan may store fp32 outputs (FP_F32): the fp32 sums are stored without
+ * rounding, as the router GEMV of PR #20502 (dense-MLP/router commits: bf16
+ * operands, fp32 logits, checked against an FP64 reference) needs.  Such a
+ * plan runs the vector-ALU kernel for 1 <= M <= 16 (M above 16 is
+ * FP_ERR_UNSUPPORTED), takes fp32 output buffers in every forward call, and
+ * has no epilogue forms.  An fp32 plan accepts only FP_F32.  Host-only; call
+ * it before the plan's forward calls. */
+fp_status fp_plan_set_out_dtype(fp_plan_t plan, int32_t out_dtype);
+
 /* Smallest M served by the MFMA tile path (bf16 plans; default: the
  * measured crossover).  Values below 2 or above FP_MAX_M+1 are rejected.
  * Changing it changes which kernel (hence which summation order) serves an

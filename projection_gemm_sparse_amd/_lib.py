@@ -83,6 +83,7 @@ _SIGS = {
     "fp_rmsnorm": (_i32, [_p, _i64, _i64, _p, ctypes.c_float, _p, _p]),
     "fp_swiglu": (_i32, [_p, _p, _i64, _i64, _p, _p]),
     "fp_plan_query": (_i32, [_p, _i64, _P_i32, _P_i32, _P_i32]),
+    "fp_plan_set_out_dtype": (_i32, [_p, _i32]),
     "fp_plan_set_mfma_min_m": (_i32, [_p, _i64]),
     "fp_plan_set_tiling": (_i32, [_p, _i64, ctypes.POINTER(FpTiling)]),
     "fp_plan_get_tiling": (_i32, [_p, _i64, _i64, ctypes.POINTER(FpTiling)]),
@@ -174,6 +175,10 @@ def fp_plan_query(plan: int, M: int):
     path, lf, ls = _i32(), _i32(), _i32()
     st = _lib.fp_plan_query(plan, M, ctypes.byref(path), ctypes.byref(lf), ctypes.byref(ls))
     return st, path.value, lf.value, ls.value
+
+
+def fp_plan_set_out_dtype(plan: int, out_dtype: int) -> int:
+    return _lib.fp_plan_set_out_dtype(plan, out_dtype)
 
 
 def fp_plan_set_mfma_min_m(plan: int, min_m: int) -> int:

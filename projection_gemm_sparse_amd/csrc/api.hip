@@ -69,6 +69,8 @@ struct fp_plan_s {
   unsigned char* ws;
   size_t ws_bytes;
   int64_t max_M;
+  bool out_f32;     // bf16 operands with fp32 outputs (vector-ALU kernel only)
+  int32_t osize;    // output element size
   int64_t mfma_min_m;
   int64_t small_mfma_min_m;
   bool has_override[FP_MAX_M + 1];
@@ -76,6 +78,8 @@ struct fp_plan_s {
 };
 
 namespace {
+
+int64_t skinny_max_m(const fp_plan_s* p) { return p->out_f32 ? 16 : kSkinnyMaxM; }
 
 std::mutex g_mu;
 std::unordered_set<const fp_plan_s*>& live_plans() {
@@ -92,7 +96,10 @@ bool plan_ok(const fp_plan_s* p) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int skinny_mt(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+int skinny_mt(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+
+// Largest M the vector-ALU kernel serves for a plan (fp32-output plans: 16).
+int64_t skinny_max_m(const fp_plan_s* p);
 int mfma_mt16(int64_t M) {
   const int64_t t = ceil_div(M, 16);
   return t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 16;
@@ -107,14 +114,15 @@ int64_t counters_bytes(int64_t n_total) {
 // the plan's total rows only.
 void default_skinny_order(int32_t dtype, int64_t kc, int64_t n_total, int mt,
                           Tiling* t) {
-  (void)mt;
   (void)n_total;
   // One workgroup covers a whole row whenever it can (16 waves * 64 lanes *
   // 2 chunks): finishing a K split across workgroups costs three dependent
   // memory round trips, more than the idle CUs of a short launch lose.
   const int64_t S = ceil_div(kc, 16 * 64 * 2);
   const int64_t per = ceil_div(kc, S);
-  const int64_t CJ = ceil_div(per, 16 * 64);
+  // the 16-token bucket holds twice the activations per chunk: two chunks
+  // per lane keep its workgroups within the register budget
+  const int64_t CJ = std::max<int64_t>(ceil_div(per, 16 * 64), mt >= 16 ? 2 : 1);
   const int64_t P = ceil_div(per, 64 * CJ);
   t->path = S > 1 ? FP_PATH_SKINNY_SPLITK : FP_PATH_SKINNY;
   t->kparts = (int)P;
@@ -338,7 +346,8 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     if ((int64_t)t.kparts * t.chunks * 8 < p->kc) return false;
     if (smfma_lds(t) > kMaxLds) return false;
   } else if (t.path == FP_PATH_SKINNY || t.path == FP_PATH_SKINNY_SPLITK) {
-    if (M > kSkinnyMaxM || t.kparts > fp::kMaxWaveParts) return false;
+    if (M > skinny_max_m(p) || t.kparts > fp::kMaxWaveParts) return false;
+    if (t.mt > 8 && !(p->out_f32 && t.chunks <= 2 && t.rows <= 4)) return false;
     if (t.rows > 8 || t.rows * t.mt > 64) return false;
     const bool cj_ok = t.chunks <= 2 || (t.mt <= 2 && t.rows <= 2 &&
         (t.chunks == 4 || t.chunks == 5 || t.chunks == 6 || t.chunks == 8 ||
@@ -373,18 +382,21 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
       t->path = t->splits > 1 ? FP_PATH_SKINNY_SPLITK : FP_PATH_SKINNY;
     }
   } else {
-    const bool mfma = p->dtype == FP_BF16 && (M >= p->mfma_min_m || M > kSkinnyMaxM);
-    const bool small = p->dtype == FP_BF16 && !mfma && M >= p->small_mfma_min_m &&
-                       default_smfma_order(p->kc, t);
+    // fp32-output plans run the vector-ALU kernel only
+    const bool mfma = p->dtype == FP_BF16 && !p->out_f32 &&
+                      (M >= p->mfma_min_m || M > kSkinnyMaxM);
+    const bool small = p->dtype == FP_BF16 && !p->out_f32 && !mfma &&
+                       M >= p->small_mfma_min_m && default_smfma_order(p->kc, t);
     if (mfma) {
       if (!default_mfma_order(p->kc, M, p->n_total, t)) return false;
     } else if (small) {
       // order fields already set
     } else {
-      if (M > kSkinnyMaxM) return false;
+      if (M > skinny_max_m(p)) return false;
       default_skinny_order(p->dtype, p->kc, p->n_total, skinny_mt(M), t);
     }
   }
+  if (p->out_f32 && t->path != FP_PATH_SKINNY && t->path != FP_PATH_SKINNY_SPLITK) return false;
   if (t->path == FP_PATH_MFMA) {
     t->mt = mfma_mt16(M);
     if (t->splits < 1) return false;
@@ -411,6 +423,7 @@ void scratch_plan(fp_plan_s* tmp, int32_t dtype, int64_t K, int64_t n_total,
   tmp->magic = kPlanMagic;
   tmp->dtype = dtype;
   tmp->esize = dtype == FP_BF16 ? 2 : 4;
+  tmp->osize = tmp->esize;
   tmp->K = K;
   tmp->kc = K * tmp->esize / 16;
   tmp->n_proj = 1;
@@ -451,10 +464,10 @@ size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) 
 template <int MT, int CJ>
 const void* skinny_pairs_fn_rw(int rw) {
   switch (rw) {
-    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, true>);
-    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, true>);
-    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, true, true>);
-    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, true>);
+    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, fp::kVarPairs>);
+    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, fp::kVarPairs>);
+    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, true, fp::kVarPairs>);
+    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, fp::kVarPairs>);
     default: return nullptr;
   }
 }
@@ -474,6 +487,42 @@ const void* skinny_pairs_fn(int mt, int cj, int rw) {
     case 2: return skinny_pairs_fn_cj<2>(cj, rw);
     case 4: return skinny_pairs_fn_cj<4>(cj, rw);
     case 8: return skinny_pairs_fn_cj<8>(cj, rw);
+    default: return nullptr;
+  }
+}
+
+// fp32 outputs from bf16 operands (router logits): up to 16 tokens, one or
+// two chunks per lane, at most 64 outputs per lane.
+template <int MT, int CJ>
+const void* skinny_f32out_fn_rw(int rw) {
+  switch (rw) {
+    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, true, fp::kVarF32Out>);
+    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, fp::kVarF32Out>);
+    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, fp::kVarF32Out>);
+    default: break;
+  }
+  if constexpr (MT <= 8) {
+    if (rw == 8) return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, fp::kVarF32Out>);
+  }
+  return nullptr;
+}
+
+template <int MT>
+const void* skinny_f32out_fn_cj(int cj, int rw) {
+  switch (cj) {
+    case 1: return skinny_f32out_fn_rw<MT, 1>(rw);
+    case 2: return skinny_f32out_fn_rw<MT, 2>(rw);
+    default: return nullptr;
+  }
+}
+
+const void* skinny_f32out_fn(int mt, int cj, int rw) {
+  switch (mt) {
+    case 1: return skinny_f32out_fn_cj<1>(cj, rw);
+    case 2: return skinny_f32out_fn_cj<2>(cj, rw);
+    case 4: return skinny_f32out_fn_cj<4>(cj, rw);
+    case 8: return skinny_f32out_fn_cj<8>(cj, rw);
+    case 16: return skinny_f32out_fn_cj<16>(cj, rw);
     default: return nullptr;
   }
 }
@@ -674,6 +723,7 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   const int64_t R = (int64_t)t.groups * t.rows;
   const int64_t blocks = ceil_div(lr.n_rows, R) * t.splits;
   const void* fn = pairs ? skinny_pairs_fn(t.mt, t.chunks, t.rows)
+                   : p->out_f32 ? skinny_f32out_fn(t.mt, t.chunks, t.rows)
                    : p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
                                          : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
   return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
@@ -701,6 +751,7 @@ fp_status check_x(const fp_plan_s* p, int64_t M, const void* x, int64_t ldx) {
   if (!aligned(x, 16) || (ldx * p->esize) % 16 != 0) return FP_ERR_UNSUPPORTED;
   if (ldx * p->esize > INT32_MAX) return FP_ERR_UNSUPPORTED;  // 32-bit row stride
   if (p->dtype == FP_F32 && M > kSkinnyMaxM) return FP_ERR_UNSUPPORTED;
+  if (p->out_f32 && M > skinny_max_m(p)) return FP_ERR_UNSUPPORTED;
   return FP_OK;
 }
 
@@ -714,14 +765,14 @@ fp_status check_outputs(const fp_plan_s* p, int64_t M, const void* x, int64_t ld
   const uintptr_t sb = reinterpret_cast<uintptr_t>(p->ws);
   const uintptr_t se = sb + p->ws_bytes;
   for (int i = 0; i < p->n_proj; ++i) {
-    if (y[i] == nullptr || !aligned(y[i], (uintptr_t)p->esize)) return FP_ERR_INVALID_ARG;
+    if (y[i] == nullptr || !aligned(y[i], (uintptr_t)p->osize)) return FP_ERR_INVALID_ARG;
     const uintptr_t b = reinterpret_cast<uintptr_t>(y[i]);
-    const uintptr_t e = b + (uintptr_t)(M * p->N[i] * p->esize);
+    const uintptr_t e = b + (uintptr_t)(M * p->N[i] * p->osize);
     if (overlaps(b, e, xb, xe) || overlaps(b, e, wb, we) || overlaps(b, e, sb, se))
       return FP_ERR_INVALID_ARG;
     for (int j = 0; j < i; ++j) {
       const uintptr_t b2 = reinterpret_cast<uintptr_t>(y[j]);
-      const uintptr_t e2 = b2 + (uintptr_t)(M * p->N[j] * p->esize);
+      const uintptr_t e2 = b2 + (uintptr_t)(M * p->N[j] * p->osize);
       if (overlaps(b, e, b2, e2)) return FP_ERR_INVALID_ARG;
     }
   }
@@ -774,6 +825,7 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
   p->magic = kPlanMagic;
   p->dtype = dtype;
   p->esize = esize;
+  p->osize = esize;
   p->K = K;
   p->kc = K * esize / 16;
   p->n_proj = n_proj;
@@ -965,7 +1017,7 @@ fp_status fp_forward_rmsnorm(const void* x, int64_t M, int64_t ldx, fp_plan_t pl
   fp_status s = check_x(plan, M, x, ldx);
   if (s != FP_OK) return s;
   if (M == 0) return FP_OK;
-  if (plan->dtype != FP_BF16) return FP_ERR_UNSUPPORTED;
+  if (plan->dtype != FP_BF16 || plan->out_f32) return FP_ERR_UNSUPPORTED;
   s = check_outputs(plan, M, x, ldx, out);
   if (s != FP_OK) return s;
   int n = 0;
@@ -1004,7 +1056,8 @@ fp_status fp_forward_swiglu(const void* x, int64_t M, int64_t ldx, fp_plan_t pla
   if (M == 0) return FP_OK;
   if (h == nullptr) return FP_ERR_INVALID_ARG;
   const int64_t N = plan->N[0];
-  if (plan->dtype != FP_BF16 || M > kSkinnyMaxM || N % 8 != 0) return FP_ERR_UNSUPPORTED;
+  if (plan->dtype != FP_BF16 || plan->out_f32 || M > kSkinnyMaxM || N % 8 != 0)
+    return FP_ERR_UNSUPPORTED;
   if (!aligned(h, 16)) return FP_ERR_UNSUPPORTED;
   const int64_t hb = M * N * 2;
   if (range_overlaps(h, hb, x, ((M - 1) * ldx + plan->K) * 2) ||
@@ -1067,12 +1120,23 @@ fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path, int32_t* launc
     if (launches_separate) *launches_separate = 0;
     return FP_OK;
   }
-  if (M > plan->max_M || (plan->dtype == FP_F32 && M > kSkinnyMaxM)) return FP_ERR_UNSUPPORTED;
+  if (M > plan->max_M || (plan->dtype == FP_F32 && M > kSkinnyMaxM) ||
+      (plan->out_f32 && M > skinny_max_m(plan)))
+    return FP_ERR_UNSUPPORTED;
   Tiling t;
   if (!choose_tiling(plan, M, plan->n_total, &t)) return FP_ERR_UNSUPPORTED;
   if (path) *path = t.path;
   if (launches_fused) *launches_fused = 1;
   if (launches_separate) *launches_separate = plan->n_proj;
+  return FP_OK;
+}
+
+fp_status fp_plan_set_out_dtype(fp_plan_t plan, int32_t out_dtype) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  if (out_dtype != FP_BF16 && out_dtype != FP_F32) return FP_ERR_INVALID_ARG;
+  if (plan->dtype == FP_F32) return out_dtype == FP_F32 ? FP_OK : FP_ERR_UNSUPPORTED;
+  plan->out_f32 = out_dtype == FP_F32;
+  plan->osize = plan->out_f32 ? 4 : 2;
   return FP_OK;
 }
 

@@ -43,6 +43,11 @@ struct Tail {
   uint32_t* counters;  // one per row block when S > 1, zero between calls
 };
 
+// Kernel variants (a compile-time parameter of the small-M kernels).
+constexpr int kVarPlain = 0;
+constexpr int kVarPairs = 1;
+constexpr int kVarF32Out = 2;
+
 // Gate/up launches (the PAIRS variant of the kernels): the launch's n_rows =
 // 2N logical rows interleave the two halves of the weight buffer -- logical
 // row 2j is gate row j, 2j + 1 is up row j (buffer row N + j, N = split) --

@@ -55,9 +55,13 @@ namespace fp {
 // A K slice holds P * 64 * CJ chunks; a workgroup owns G * RW rows.  The
 // hardware preloads at most 14 argument dwords, exactly these; one more
 // would be read from memory before the first load could issue.
-// PAIRS: a gate/up launch (rows taken in pairs, see pair_row; RW even,
-// S = 1, bf16) that writes silu(gate) * up instead of the projections.
-template <int MT, int RW, int CJ, bool BF16, bool PAIRS = false>
+// VAR selects a variant, each compiled only where it is used:
+//   kVarPlain   the projections, stored as the input type;
+//   kVarPairs   a gate/up launch (rows taken in pairs, see pair_row; RW
+//               even, S = 1, bf16) that writes silu(gate) * up;
+//   kVarF32Out  bf16 operands with fp32 outputs (router logits), up to 16
+//               tokens (MT = 16).
+template <int MT, int RW, int CJ, bool BF16, int VAR = kVarPlain>
 __global__ void __launch_bounds__(skinny_max_threads(MT, RW, CJ))
 skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
               unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
@@ -66,6 +70,8 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   constexpr int VP = pow2ceil(V);   // padded to a power of two
   constexpr int QV = VP >= 64 ? VP / 64 : 1;
   constexpr int LSTRIDE = VP >= 64 ? 1 : 64 / VP;
+  constexpr bool PAIRS = VAR == kVarPairs;
+  constexpr bool OUT_BF16 = BF16 && VAR != kVarF32Out;
 
   extern __shared__ float smem[];   // [G][VP][16] wave sums, then one flag
   const int tid = threadIdx.x;
@@ -172,7 +178,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
         const int r = idx / MT;
         const int m = idx - r * MT;
         const int row = wrow0 + r;
-        if (idx < V && m < M && row < n_rows) store_y<BF16>(om, a.out, row, m, v[q]);
+        if (idx < V && m < M && row < n_rows) store_y<OUT_BF16>(om, a.out, row, m, v[q]);
       }
     }
     return;
@@ -204,7 +210,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
           store_pair(y0, split, row, m, sum, u_sum);
         }
       } else if (Sv == 1) {
-        store_y<BF16>(om, a.out, row, m, sum);
+        store_y<OUT_BF16>(om, a.out, row, m, sum);
       } else {
         store_partial(partial + ((int64_t)s * n_rows + row) * M + m, sum);
       }
@@ -213,7 +219,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   if (Sv == 1) return;
 
   // 6. split-K: the last workgroup of the row block adds the S partials
-  splitk_finish<BF16>(n_rows, partial, counters, rb, Sv, row_base, (int64_t)Gv * RW, M,
+  splitk_finish<OUT_BF16>(n_rows, partial, counters, rb, Sv, row_base, (int64_t)Gv * RW, M,
                       Gv * P * 64, om, a.out,
                       reinterpret_cast<int*>(smem + Gv * VP * kMaxWaveParts));
 }

@@ -34,7 +34,7 @@ class FusedProjection:
     """
 
     def __init__(self, weights, max_M: int = 8, stream=None, copy_weights: bool = True,
-                 workspace_bytes: int | None = None):
+                 workspace_bytes: int | None = None, out_dtype=None):
         if not weights:
             raise ValueError("at least one projection")
         w0 = weights[0]
@@ -77,6 +77,12 @@ class FusedProjection:
                 (torch.cuda.current_stream() if stream is None else stream).synchronize()
                 del keep
         self.plan = plan
+        self.out_dtype = self.dtype if out_dtype is None else out_dtype
+        if self.out_dtype != self.dtype:
+            if self.out_dtype not in _DTYPES:
+                raise TypeError("out_dtype must be bfloat16 or float32")
+            L.check(L.fp_plan_set_out_dtype(plan, _DTYPES[self.out_dtype]),
+                    "fp_plan_set_out_dtype")
         self.offsets = []
         self.views = []
         for i in range(len(self.N)):
@@ -108,7 +114,7 @@ class FusedProjection:
     def _outputs(self, M: int, out):
         if out is not None:
             return out
-        return [torch.empty(M, n, dtype=self.dtype, device=self.device) for n in self.N]
+        return [torch.empty(M, n, dtype=self.out_dtype, device=self.device) for n in self.N]
 
     def _check_x(self, x):
         if x.dim() != 2 or int(x.shape[1]) != self.K or x.stride(1) != 1:

@@ -201,3 +201,7 @@ def test_epilogue_argument_checks_before_any_hip_call():
     assert P.fp_forward_rmsnorm(FAKE, 1, 5120, None, 0, [None, None], 1e-6,
                                 [FAKE, FAKE]) == P.FP_ERR_INVALID_ARG
     assert P.fp_forward_swiglu(FAKE, 1, 5120, None, 0, FAKE) == P.FP_ERR_INVALID_ARG
+
+
+def test_out_dtype_on_a_null_plan():
+    assert P.fp_plan_set_out_dtype(None, P.FP_F32) == P.FP_ERR_INVALID_ARG
