@@ -25,6 +25,12 @@ Sources (TensorRT-LLM pull-request pages):
 * "Staircase: GLM-5.2 NVFP4 low-latency decode target for Rubin (TP16)"
   (PR #20502), router GEMV commit: checked against an FP64 reference.
 
+MXFP8 weights (``oracle.c``, ``linear_mxfp8``): E4M3 codes with one E8M0
+scale per 32 elements along K, decoded from the open microscaling format's
+definition (the pages name MXFP8 projections without defining them); the
+sum is the same fp64 loop over the exact dequantised values, held to the
+bf16 rule.
+
 Epilogues (``oracle.c``), each applied with the pages' rounding points:
 
 * RMSNorm of a projection's bf16 output with a bf16 gain (q_norm over the
@@ -103,6 +109,14 @@ def _load():
             lib.oracle_round_bf16_array.restype = None
             lib.oracle_round_bf16_array.argtypes = [
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+            lib.oracle_e4m3_value.restype = ctypes.c_double
+            lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+            lib.oracle_e8m0_value.restype = ctypes.c_double
+            lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+            lib.oracle_linear_mxfp8.restype = ctypes.c_int
+            lib.oracle_linear_mxfp8.argtypes = [
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
             lib.oracle_rmsnorm_bf16.restype = ctypes.c_int
             lib.oracle_rmsnorm_bf16.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -214,6 +228,37 @@ def check_within_bound(y_out_f64: np.ndarray, y: np.ndarray, S: np.ndarray,
     worst = float(ratio[idx])
     ok = bool(np.all(np.isfinite(y_out_f64)) and worst <= 1.0)
     return ok, worst, idx
+
+
+# ------------------------------------------------------------------ MXFP8
+def e4m3_value(code: int) -> float:
+    """Exact value of one E4M3 code (``oracle.c``; NaN for the NaN codes)."""
+    return float(_load().oracle_e4m3_value(int(code) & 0xFF))
+
+
+def e8m0_value(code: int) -> float:
+    """Exact value of one E8M0 scale code, 2^(s - 127) (NaN for 255)."""
+    return float(_load().oracle_e8m0_value(int(code) & 0xFF))
+
+
+def linear_mxfp8(x_bits: np.ndarray, w_packed: np.ndarray, K: int):
+    """One projection with MXFP8 weights (``oracle.c``).  ``x_bits`` is bf16
+    [M, ldx] (first K columns read); ``w_packed`` is uint8 [N, K + K/32]:
+    per row the K E4M3 codes, then the K/32 E8M0 scales of its 32-element
+    blocks.  Returns ``(y, S)`` as float64 [M, N]."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w_packed, dtype=np.uint8)
+    if x.ndim != 2 or w.ndim != 2 or K % 32 != 0 or w.shape[1] != K + K // 32:
+        raise ValueError("x must be [M, ldx] bf16, w [N, K + K/32] uint8, K % 32 == 0")
+    M, ldx = x.shape
+    N = w.shape[0]
+    y = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    rc = _load().oracle_linear_mxfp8(M, N, K, ldx, x.ctypes.data, w.ctypes.data,
+                                     y.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_linear_mxfp8 rejected its arguments")
+    return y, S
 
 
 # --------------------------------------------------------------- epilogues

@@ -62,3 +62,45 @@ def linear_exact(x_rows, w_rows, frac_bits: int):
         y.append(yr)
         s.append(sr)
     return y, s
+
+
+def decode_e4m3(code: int) -> Fraction:
+    """E4M3 from its definition: sign, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN."""
+    code = int(code) & 0xFF
+    sign = -1 if code >> 7 else 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 15 and m == 7:
+        raise ValueError("NaN has no rational value")
+    if e == 0:
+        return sign * Fraction(m, 8) * Fraction(1, 2 ** 6)
+    return sign * (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+
+def decode_e8m0(code: int) -> Fraction:
+    code = int(code) & 0xFF
+    if code == 255:
+        raise ValueError("NaN has no rational value")
+    return Fraction(2) ** (code - 127)
+
+
+def linear_exact_mxfp8(x_rows, w_rows, K: int):
+    """``x_rows``: M lists of >= K bf16 patterns; ``w_rows``: N packed rows
+    (K E4M3 codes, then K/32 E8M0 scales).  Exact (y, S) as Fractions."""
+    xs = [[decode(b, 7) for b in row[:K]] for row in x_rows]
+    ws = []
+    for row in w_rows:
+        sc = [decode_e8m0(b) for b in row[K:K + K // 32]]
+        ws.append([decode_e4m3(row[k]) * sc[k // 32] for k in range(K)])
+    y, s = [], []
+    for xr in xs:
+        yr, sr = [], []
+        for wr in ws:
+            acc = sum((a * b for a, b in zip(xr, wr)), Fraction(0))
+            mag = sum((abs(a * b) for a, b in zip(xr, wr)), Fraction(0))
+            yr.append(acc)
+            sr.append(mag)
+        y.append(yr)
+        s.append(sr)
+    return y, s

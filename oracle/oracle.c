@@ -166,3 +166,68 @@ int oracle_swiglu_bf16(int64_t n, const uint16_t* g, const uint16_t* u, double* 
   }
   return 0;
 }
+
+/*
+ * MXFP8 weights (microscaling: 8-bit E4M3 elements sharing one 8-bit E8M0
+ * power-of-two scale per block of 32 consecutive elements along K).  The
+ * pages name MXFP8 projections for the DeepSeek-V4.1 wq_a / wkv weights
+ * ("tinygemm2 for the DeepSeek-V4.1 hidden-state projections", PR #20636,
+ * Description) without defining the encoding; the reading here is the open
+ * microscaling format, written from its definition:
+ *   E4M3: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0;
+ *         exponent 0: subnormal (m / 8) * 2^-6; otherwise (1 + m / 8) *
+ *         2^(e - 7); exponent 15 with mantissa 7 is NaN (no infinities;
+ *         largest finite 448).
+ *   E8M0: an unsigned biased exponent, value 2^(s - 127); 255 is NaN.
+ * Storage (this library's layout): each weight row is its K codes followed
+ * by its K / 32 scales, so a row takes K + K / 32 bytes.
+ */
+static double e4m3_value(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 0xF, m = c & 0x7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+static double e8m0_value(uint8_t s) {
+  if (s == 255) return NAN;
+  return ldexp(1.0, (int)s - 127);
+}
+
+double oracle_e4m3_value(uint8_t c) { return e4m3_value(c); }
+double oracle_e8m0_value(uint8_t s) { return e8m0_value(s); }
+
+/*
+ * One projection with MXFP8 weights and bf16 activations:
+ *   y[m][r] = sum_k X[m][k] * Q[r][k] * 2^(s[r][k / 32] - 127)
+ *   S[m][r] = sum_k |X[m][k] * Q[r][k] * 2^(s[r][k / 32] - 127)|
+ * X the exact bf16 values (row stride ldx >= K), Q the E4M3 values, w the
+ * packed rows (K codes, then K / 32 scales; row stride K + K / 32 bytes).
+ * Products are exact in double (at most 8 x 4 significant bits times a
+ * power of two), sums in double in increasing k.  K must be a multiple of
+ * 32.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_linear_mxfp8(int64_t M, int64_t N, int64_t K, int64_t ldx, const uint16_t* x,
+                        const uint8_t* w, double* y, double* s) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || ldx < K) return -1;
+  const int64_t row = K + K / 32;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t r = 0; r < N; ++r) {
+      const uint8_t* q = w + r * row;
+      const uint8_t* sc = q + K;
+      double acc = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double p = bf16_bits_value(x[m * ldx + k]) * (e4m3_value(q[k]) * e8m0_value(sc[k / 32]));
+        acc += p;
+        mag += fabs(p);
+      }
+      y[m * N + r] = acc;
+      s[m * N + r] = mag;
+    }
+  }
+  return 0;
+}

@@ -80,6 +80,42 @@ WORKLOADS = {
 }
 
 
+# MXFP8 weights: wq_a + wkv stored as E4M3 codes with one E8M0 scale per 32
+# elements along K, the DeepSeek-V4.1 projections' MXFP8 form named on the
+# pages.  Packed rows: K codes, then the K/32 scales.
+MXFP8_WORKLOADS = {
+    "wq_a+wkv_mxfp8": Workload("wq_a+wkv_mxfp8", 5120, (1280, 512), "mxfp8",
+                               "codes_uniform_scales_112_117", (1, 2, 3, 4, 5, 6, 7, 8),
+                               (0, 1), "MXFP8 weights, bf16 x and y"),
+}
+E4M3_NAN = (0x7F, 0xFF)
+
+
+def draw_mxfp8_weights(K: int, N, g: torch.Generator, scale_lo: int = 112,
+                       scale_hi: int = 117):
+    """One packed uint8 [N_i, K + K/32] tensor per projection: codes uniform
+    over the 254 non-NaN E4M3 codes, scales uniform in [scale_lo, scale_hi]
+    (2^-15 .. 2^-10, so the weights are of the order of 1/sqrt(K))."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    out = []
+    for n in N:
+        codes = torch.randint(0, 254, (int(n), K), generator=g, dtype=torch.int64)
+        codes = codes + (codes >= 0x7F).to(torch.int64)  # skip 0x7F; 0xFF is never drawn
+        scales = torch.randint(scale_lo, scale_hi + 1, (int(n), K // 32), generator=g,
+                               dtype=torch.int64)
+        out.append(torch.cat([codes, scales], dim=1).to(torch.uint8))
+    return out
+
+
+def mxfp8_case(M: int, seed: int, K: int = 5120, N=(1280, 512), ldx: int | None = None):
+    """Packed MXFP8 weights then bf16 x from one seeded generator."""
+    g = _gen(seed)
+    ws = draw_mxfp8_weights(K, N, g)
+    x = draw_x(M, K, "bf16", g, ldx=ldx)
+    return x, ws
+
+
 def draw_gamma(N: int, g: torch.Generator) -> torch.Tensor:
     """An RMSNorm gain of N entries near 1 (1 + 0.1 * N(0, 1), in bf16), drawn
     after the weights and x of the same seed."""
@@ -171,12 +207,15 @@ def workload_case(name: str, M: int, seed: int, ldx: int | None = None):
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """Raw bit patterns of a CPU tensor: uint16 for bf16, uint32 for fp32."""
+    """Raw bit patterns of a CPU tensor: uint16 for bf16, uint32 for fp32,
+    the bytes themselves for uint8 (packed MXFP8 rows)."""
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy().view(np.uint32)
+    if t.dtype == torch.uint8:
+        return t.numpy()
     raise TypeError(t.dtype)
 
 
