@@ -57,6 +57,8 @@ KERNEL_SOURCES = ("projection_gemm_sparse_amd/csrc/common.hpp",
                   "projection_gemm_sparse_amd/csrc/skinny.hpp",
                   "projection_gemm_sparse_amd/csrc/smfma.hpp",
                   "projection_gemm_sparse_amd/csrc/tile.hpp",
+                  "projection_gemm_sparse_amd/csrc/epilogue.hpp",
+                  "projection_gemm_sparse_amd/csrc/mxfp8.hpp",
                   "projection_gemm_sparse_amd/csrc/api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 

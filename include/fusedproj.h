@@ -57,8 +57,17 @@ typedef struct fp_plan_s* fp_plan_t;
 
 /* Storage and arithmetic type.  FP_BF16: bf16 inputs and outputs, fp32
  * accumulation, each output rounded once to bf16 (round to nearest even).
- * FP_F32: fp32 inputs and outputs with fp32 fused multiply-add. */
-typedef enum { FP_BF16 = 0, FP_F32 = 1 } fp_dtype;
+ * FP_F32: fp32 inputs and outputs with fp32 fused multiply-add.
+ * FP_MXFP8: MXFP8 weights (the MXFP8 projections named in PR #20636,
+ * Description; read as the open microscaling format: E4M3 codes, one E8M0
+ * scale 2^(s-127) per 32 consecutive elements along K), bf16 activations and
+ * outputs, fp32 accumulation, outputs rounded once to bf16.  Weight rows
+ * are packed: the K codes, then the K/32 scales (K + K/32 bytes per row; K
+ * a multiple of 512).  Every weight element is decoded exactly (an E4M3
+ * value times a power of two) for scaled values inside bf16's normal range;
+ * NaN codes and scales (0x7F/0xFF, 255) and scales above 2^119 are outside
+ * the served domain.  Served for 1 <= M <= 8 by the vector-ALU kernel. */
+typedef enum { FP_BF16 = 0, FP_F32 = 1, FP_MXFP8 = 2 } fp_dtype;
 
 typedef enum {
   FP_OK = 0,
@@ -95,15 +104,17 @@ size_t fp_workspace_bytes(int32_t dtype, int64_t K, int32_t n_proj,
 
 /* Load-time half ("post_load_weights" of PR #20636, Description).
  * Records the projection layout and, on `stream`, copies each w_src[i]
- * (device, [N[i], K] contiguous row-major) into rows off_i .. off_i+N[i]-1 of
- * w_cat (device, [sum N, K] row-major, 256-byte aligned), where off_0 = 0 and
- * off_{i+1} = off_i + N[i].  A NULL w_src (or a NULL entry, or an entry equal
- * to its destination) skips that copy: the caller fills the rows itself,
- * typically through the views fp_plan_view returns.  The workspace
- * (device, ws_bytes >= fp_workspace_bytes(...), 256-byte aligned) has its
- * counters cleared on `stream` by a fill kernel.
+ * (device, [N[i], K] contiguous row-major; FP_MXFP8: N[i] packed rows of
+ * K + K/32 bytes) into rows off_i .. off_i+N[i]-1 of w_cat (device,
+ * [sum N, K] row-major, or sum N packed rows for FP_MXFP8, 256-byte
+ * aligned), where off_0 = 0 and off_{i+1} = off_i + N[i].  A NULL w_src (or
+ * a NULL entry, or an entry equal to its destination) skips that copy: the
+ * caller fills the rows itself, typically through the views fp_plan_view
+ * returns.  The workspace (device, ws_bytes >= fp_workspace_bytes(...),
+ * 256-byte aligned) has its counters cleared on `stream` by a fill kernel.
  * Requirements: 1 <= n_proj <= FP_MAX_PROJ, every N[i] >= 1, K >= 1 with
- * K * sizeof(element) a multiple of 16, 1 <= max_M <= FP_MAX_M.
+ * K * sizeof(element) a multiple of 16 (FP_MXFP8: K a multiple of 512),
+ * 1 <= max_M <= FP_MAX_M.
  * On success *out receives the plan. */
 fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj,
                          const int64_t* N, const void* const* w_src,
@@ -127,6 +138,14 @@ fp_status fp_plan_destroy(fp_plan_t plan);
  * M < 0, NULL x with M > 0, stale plan).  The pattern of the dense-MLP
  * commit of PR #20502: a host query, refusal otherwise. */
 fp_status fp_supported(fp_plan_t plan, int64_t M, const void* x, int64_t ldx);
+
+/* Dequantise MXFP8 weight rows: w (device, `rows` packed rows of K codes and
+ * K/32 scales, 16-byte aligned) to out (device, dense [rows, K] bf16,
+ * 16-byte aligned, not overlapping w), with the decode the FP_MXFP8
+ * projection uses.  For a caller that needs the weights as bf16 (a fallback
+ * linear layer).  K a multiple of 512. */
+fp_status fp_mxfp8_to_bf16(const void* w, int64_t rows, int64_t K, void* out,
+                           void* stream);
 
 /* The fused call: one launch computes every projection.
  * x: device, M rows with row stride ldx >= K elements (x[m, k] at
@@ -153,8 +172,8 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx,
  * projection after its single rounding to bf16, as the unfused chain (one
  * projection launch per projection, then a second kernel) does, and both
  * give results bitwise equal to that chain (fp_forward_separate followed by
- * fp_rmsnorm / fp_swiglu on its outputs).  bf16 plans only; other cases
- * return FP_ERR_UNSUPPORTED with no launch.
+ * fp_rmsnorm / fp_swiglu on its outputs).  RMSNorm: bf16 and MXFP8 plans;
+ * SwiGLU: bf16 plans; other cases return FP_ERR_UNSUPPORTED with no launch.
  * --------------------------------------------------------------------- */
 
 /* Fused projection + RMSNorm per projection (q_norm over the q_a columns and

@@ -24,6 +24,7 @@
 #include "smfma.hpp"
 #include "tile.hpp"
 #include "epilogue.hpp"
+#include "mxfp8.hpp"
 
 namespace {
 
@@ -60,7 +61,8 @@ struct fp_plan_s {
   int32_t dtype;
   int32_t esize;
   int64_t K;
-  int64_t kc;  // 16-byte chunks per row
+  int64_t kc;  // 16-byte chunks per row (MXFP8: code chunks, K / 16)
+  int64_t wrow;  // bytes per weight row (MXFP8: K codes + K / 32 scales)
   int32_t n_proj;
   int64_t N[FP_MAX_PROJ];
   int64_t off[FP_MAX_PROJ];
@@ -80,6 +82,34 @@ struct fp_plan_s {
 namespace {
 
 int64_t skinny_max_m(const fp_plan_s* p) { return p->out_f32 ? 16 : kSkinnyMaxM; }
+
+// Per dtype: activation element size, bytes per weight row and the 16-byte
+// weight chunks per row the kernels count; false if K does not fit the
+// kernels' 16-byte chunking (MXFP8: K a multiple of 512, so that a packed row
+// of K codes and K/32 scales is a whole number of chunks).
+bool dtype_geometry(int32_t dtype, int64_t K, int* esize, int64_t* wrow, int64_t* kc) {
+  if (K < 1) return false;
+  if (dtype == FP_BF16 || dtype == FP_F32) {
+    const int es = dtype == FP_BF16 ? 2 : 4;
+    if ((K * es) % 16 != 0) return false;
+    *esize = es;
+    *wrow = K * es;
+    *kc = K * es / 16;
+    return true;
+  }
+  if (dtype == FP_MXFP8) {
+    if (K % 512 != 0) return false;
+    *esize = 2;
+    *wrow = K + K / 32;
+    *kc = K / 16;
+    return true;
+  }
+  return false;
+}
+
+int skinny_var(const fp_plan_s* p) {
+  return p->dtype == FP_MXFP8 ? fp::kVarMx8 : fp::kVarPlain;
+}
 
 std::mutex g_mu;
 std::unordered_set<const fp_plan_s*>& live_plans() {
@@ -234,7 +264,7 @@ bool default_smfma_order(int64_t kc, Tiling* t) {
 // ceil(ceil(n_rows / R) / CUs) * R (ties: the larger R, fewer workgroups);
 // RW <= min(8, 64 / MT) and G * P waves fit one workgroup.  Without a
 // one-round choice the largest R is taken.
-void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs) {
+void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs, int var) {
   const int rw_max = std::min(8, 64 / mt);
   const int64_t rows = n_rows * t->splits;  // work units: (row, K slice)
   if (t->rows > 0 && t->groups > 0) return;
@@ -242,7 +272,8 @@ void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs) {
   int64_t best_cost = INT64_MAX;
   for (int rw = pairs ? 2 : 1; rw <= rw_max; rw += pairs ? 2 : 1) {
     if (t->rows > 0 && rw != t->rows) continue;
-    const int g_cap = std::max(1, fp::skinny_max_threads(t->mt, rw, t->chunks) / (64 * t->kparts));
+    const int g_cap =
+        std::max(1, fp::skinny_max_threads(t->mt, rw, t->chunks, var) / (64 * t->kparts));
     for (int g = 1; g <= g_cap; ++g) {
       if (t->groups > 0 && g != t->groups) continue;
       const int64_t R = (int64_t)rw * g;
@@ -354,7 +385,9 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
          t.chunks == 10 || t.chunks == 12));
     if (!cj_ok) return false;
     if (t.groups < 1) return false;
-    if ((int64_t)t.groups * t.kparts * 64 > fp::skinny_max_threads(t.mt, t.rows, t.chunks))
+    if (p->dtype == FP_MXFP8 && t.chunks > 2) return false;
+    if ((int64_t)t.groups * t.kparts * 64 >
+        fp::skinny_max_threads(t.mt, t.rows, t.chunks, skinny_var(p)))
       return false;
     if ((int64_t)t.splits * t.kparts * 64 * t.chunks < p->kc) return false;
     if (skinny_lds(t) > kMaxLds) return false;
@@ -396,7 +429,9 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
       default_skinny_order(p->dtype, p->kc, p->n_total, skinny_mt(M), t);
     }
   }
-  if (p->out_f32 && t->path != FP_PATH_SKINNY && t->path != FP_PATH_SKINNY_SPLITK) return false;
+  if ((p->out_f32 || p->dtype == FP_MXFP8) && t->path != FP_PATH_SKINNY &&
+      t->path != FP_PATH_SKINNY_SPLITK)
+    return false;
   if (t->path == FP_PATH_MFMA) {
     t->mt = mfma_mt16(M);
     if (t->splits < 1) return false;
@@ -408,7 +443,7 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
   } else {
     t->mt = skinny_mt(M);
     if (t->kparts < 1) return false;
-    resolve_skinny_rows(n_rows, t->mt, t, pairs);
+    resolve_skinny_rows(n_rows, t->mt, t, pairs, skinny_var(p));
   }
   // a gate/up launch keeps both rows of a pair in one row group
   if (pairs && (t->rows % 2 != 0 || t->splits != 1)) return false;
@@ -422,10 +457,14 @@ void scratch_plan(fp_plan_s* tmp, int32_t dtype, int64_t K, int64_t n_total,
   std::memset(tmp, 0, sizeof *tmp);
   tmp->magic = kPlanMagic;
   tmp->dtype = dtype;
-  tmp->esize = dtype == FP_BF16 ? 2 : 4;
-  tmp->osize = tmp->esize;
+  int es = 2;
+  int64_t wrow = 0, kc = 0;
+  dtype_geometry(dtype, K, &es, &wrow, &kc);
+  tmp->esize = es;
+  tmp->osize = es;
+  tmp->wrow = wrow;
   tmp->K = K;
-  tmp->kc = K * tmp->esize / 16;
+  tmp->kc = kc;
   tmp->n_proj = 1;
   tmp->N[0] = n_total;
   tmp->n_total = n_total;
@@ -523,6 +562,41 @@ const void* skinny_f32out_fn(int mt, int cj, int rw) {
     case 4: return skinny_f32out_fn_cj<4>(cj, rw);
     case 8: return skinny_f32out_fn_cj<8>(cj, rw);
     case 16: return skinny_f32out_fn_cj<16>(cj, rw);
+    default: return nullptr;
+  }
+}
+
+// MXFP8 weights: up to 8 tokens, one or two chunks per lane.
+template <int MT, int CJ>
+const void* skinny_mx8_fn_rw(int rw) {
+  switch (rw) {
+    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, true, fp::kVarMx8>);
+    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, fp::kVarMx8>);
+    case 3: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 3, CJ, true, fp::kVarMx8>);
+    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, fp::kVarMx8>);
+    case 5: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 5, CJ, true, fp::kVarMx8>);
+    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, true, fp::kVarMx8>);
+    case 7: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 7, CJ, true, fp::kVarMx8>);
+    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, fp::kVarMx8>);
+    default: return nullptr;
+  }
+}
+
+template <int MT>
+const void* skinny_mx8_fn_cj(int cj, int rw) {
+  switch (cj) {
+    case 1: return skinny_mx8_fn_rw<MT, 1>(rw);
+    case 2: return skinny_mx8_fn_rw<MT, 2>(rw);
+    default: return nullptr;
+  }
+}
+
+const void* skinny_mx8_fn(int mt, int cj, int rw) {
+  switch (mt) {
+    case 1: return skinny_mx8_fn_cj<1>(cj, rw);
+    case 2: return skinny_mx8_fn_cj<2>(cj, rw);
+    case 4: return skinny_mx8_fn_cj<4>(cj, rw);
+    case 8: return skinny_mx8_fn_cj<8>(cj, rw);
     default: return nullptr;
   }
 }
@@ -724,6 +798,7 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   const int64_t blocks = ceil_div(lr.n_rows, R) * t.splits;
   const void* fn = pairs ? skinny_pairs_fn(t.mt, t.chunks, t.rows)
                    : p->out_f32 ? skinny_f32out_fn(t.mt, t.chunks, t.rows)
+                   : p->dtype == FP_MXFP8 ? skinny_mx8_fn(t.mt, t.chunks, t.rows)
                    : p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
                                          : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
   return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
@@ -761,7 +836,7 @@ fp_status check_outputs(const fp_plan_s* p, int64_t M, const void* x, int64_t ld
   const uintptr_t xb = reinterpret_cast<uintptr_t>(x);
   const uintptr_t xe = xb + (uintptr_t)(((M - 1) * ldx + p->K) * p->esize);
   const uintptr_t wb = reinterpret_cast<uintptr_t>(p->w_cat);
-  const uintptr_t we = wb + (uintptr_t)(p->n_total * p->K * p->esize);
+  const uintptr_t we = wb + (uintptr_t)(p->n_total * p->wrow);
   const uintptr_t sb = reinterpret_cast<uintptr_t>(p->ws);
   const uintptr_t se = sb + p->ws_bytes;
   for (int i = 0; i < p->n_proj; ++i) {
@@ -785,11 +860,12 @@ extern "C" {
 
 size_t fp_workspace_bytes(int32_t dtype, int64_t K, int32_t n_proj, const int64_t* N,
                           int64_t max_M) {
-  if ((dtype != FP_BF16 && dtype != FP_F32) || K < 1 || n_proj < 1 ||
+  if ((dtype != FP_BF16 && dtype != FP_F32 && dtype != FP_MXFP8) || K < 1 || n_proj < 1 ||
       n_proj > FP_MAX_PROJ || N == nullptr || max_M < 1 || max_M > FP_MAX_M)
     return 0;
-  const int esize = dtype == FP_BF16 ? 2 : 4;
-  if ((K * esize) % 16 != 0) return 0;
+  int esize = 0;
+  int64_t wrow = 0, kc = 0;
+  if (!dtype_geometry(dtype, K, &esize, &wrow, &kc)) return 0;
   int64_t n_total = 0;
   for (int i = 0; i < n_proj; ++i) {
     if (N[i] < 1) return 0;
@@ -803,12 +879,13 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
                          size_t ws_bytes, int64_t max_M, void* stream, fp_plan_t* out) {
   if (out == nullptr) return FP_ERR_INVALID_ARG;
   *out = nullptr;
-  if (dtype != FP_BF16 && dtype != FP_F32) return FP_ERR_INVALID_ARG;
+  if (dtype != FP_BF16 && dtype != FP_F32 && dtype != FP_MXFP8) return FP_ERR_INVALID_ARG;
   if (K < 1 || n_proj < 1 || n_proj > FP_MAX_PROJ || N == nullptr) return FP_ERR_INVALID_ARG;
   if (max_M < 1 || max_M > FP_MAX_M) return FP_ERR_INVALID_ARG;
   if (w_cat == nullptr || workspace == nullptr) return FP_ERR_INVALID_ARG;
-  const int esize = dtype == FP_BF16 ? 2 : 4;
-  if ((K * esize) % 16 != 0) return FP_ERR_UNSUPPORTED;
+  int esize = 0;
+  int64_t wrow = 0, kc = 0;
+  if (!dtype_geometry(dtype, K, &esize, &wrow, &kc)) return FP_ERR_UNSUPPORTED;
   if (!aligned(w_cat, 256) || !aligned(workspace, 256)) return FP_ERR_UNSUPPORTED;
   int64_t n_total = 0;
   for (int i = 0; i < n_proj; ++i) {
@@ -816,7 +893,7 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
     n_total += N[i];
   }
   // the kernels index rows and 16-byte chunks with 32-bit integers
-  if (n_total > kMaxRows || K * esize / 16 > kMaxRows) return FP_ERR_UNSUPPORTED;
+  if (n_total > kMaxRows || kc > kMaxRows || wrow > INT32_MAX) return FP_ERR_UNSUPPORTED;
   if (ws_bytes < workspace_need(dtype, K, n_total, max_M)) return FP_ERR_WORKSPACE;
 
   fp_plan_s* p = new (std::nothrow) fp_plan_s;
@@ -827,7 +904,8 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
   p->esize = esize;
   p->osize = esize;
   p->K = K;
-  p->kc = K * esize / 16;
+  p->kc = kc;
+  p->wrow = wrow;
   p->n_proj = n_proj;
   int64_t off = 0;
   for (int i = 0; i < n_proj; ++i) {
@@ -846,9 +924,9 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   // concatenate: W_cat[off_i + r, :] = W_i[r, :]
   for (int i = 0; i < n_proj && w_src != nullptr; ++i) {
-    unsigned char* dst = p->w_cat + p->off[i] * K * esize;
+    unsigned char* dst = p->w_cat + p->off[i] * wrow;
     if (w_src[i] == nullptr || w_src[i] == dst) continue;
-    hipError_t e = hipMemcpyAsync(dst, w_src[i], (size_t)(N[i] * K * esize),
+    hipError_t e = hipMemcpyAsync(dst, w_src[i], (size_t)(N[i] * wrow),
                                   hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) {
       delete p;
@@ -878,7 +956,7 @@ fp_status fp_plan_view(fp_plan_t plan, int32_t i, void** w_i, int64_t* row_offse
                        int64_t* rows) {
   if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
   if (i < 0 || i >= plan->n_proj) return FP_ERR_INVALID_ARG;
-  if (w_i) *w_i = plan->w_cat + plan->off[i] * plan->K * plan->esize;
+  if (w_i) *w_i = plan->w_cat + plan->off[i] * plan->wrow;
   if (row_offset) *row_offset = plan->off[i];
   if (rows) *rows = plan->N[i];
   return FP_OK;
@@ -948,7 +1026,7 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx, fp_plan_t p
     std::memset(&lr, 0, sizeof lr);
     lr.n_seg = 1;
     lr.n_rows = (int)plan->N[i];
-    const unsigned char* w = plan->w_cat + plan->off[i] * plan->K * plan->esize;
+    const unsigned char* w = plan->w_cat + plan->off[i] * plan->wrow;
     if (w_override != nullptr && w_override[i] != nullptr)
       w = static_cast<const unsigned char*>(w_override[i]);
     lr.w = w;
@@ -1017,7 +1095,9 @@ fp_status fp_forward_rmsnorm(const void* x, int64_t M, int64_t ldx, fp_plan_t pl
   fp_status s = check_x(plan, M, x, ldx);
   if (s != FP_OK) return s;
   if (M == 0) return FP_OK;
-  if (plan->dtype != FP_BF16 || plan->out_f32) return FP_ERR_UNSUPPORTED;
+  // bf16 outputs: bf16 and MXFP8 plans
+  if ((plan->dtype != FP_BF16 && plan->dtype != FP_MXFP8) || plan->out_f32)
+    return FP_ERR_UNSUPPORTED;
   s = check_outputs(plan, M, x, ldx, out);
   if (s != FP_OK) return s;
   int n = 0;
@@ -1061,7 +1141,7 @@ fp_status fp_forward_swiglu(const void* x, int64_t M, int64_t ldx, fp_plan_t pla
   if (!aligned(h, 16)) return FP_ERR_UNSUPPORTED;
   const int64_t hb = M * N * 2;
   if (range_overlaps(h, hb, x, ((M - 1) * ldx + plan->K) * 2) ||
-      range_overlaps(h, hb, plan->w_cat, plan->n_total * plan->K * 2) ||
+      range_overlaps(h, hb, plan->w_cat, plan->n_total * plan->wrow) ||
       range_overlaps(h, hb, plan->ws, (int64_t)plan->ws_bytes))
     return FP_ERR_INVALID_ARG;
   // one launch over the 2N rows taken in (gate j, up j) pairs
@@ -1110,6 +1190,24 @@ fp_status fp_swiglu(const void* g, const void* u, int64_t M, int64_t N, void* h,
                 0, args, static_cast<hipStream_t>(stream));
 }
 
+fp_status fp_mxfp8_to_bf16(const void* w, int64_t rows, int64_t K, void* out, void* stream) {
+  if (rows < 0 || K < 1) return FP_ERR_INVALID_ARG;
+  int esize = 0;
+  int64_t wrow = 0, kc = 0;
+  if (!dtype_geometry(FP_MXFP8, K, &esize, &wrow, &kc)) return FP_ERR_UNSUPPORTED;
+  if (rows == 0) return FP_OK;
+  if (w == nullptr || out == nullptr) return FP_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(out, 16)) return FP_ERR_UNSUPPORTED;
+  if (range_overlaps(w, rows * wrow, out, rows * K * 2)) return FP_ERR_INVALID_ARG;
+  const unsigned char* w_a = static_cast<const unsigned char*>(w);
+  unsigned char* o_a = static_cast<unsigned char*>(out);
+  int32_t kc_a = (int32_t)kc;
+  int64_t n_a = rows * kc;
+  void* args[] = {&w_a, &o_a, &kc_a, &n_a};
+  return launch(reinterpret_cast<const void*>(&fp::mxfp8_to_bf16_kernel), ceil_div(n_a, 256), 256,
+                0, args, static_cast<hipStream_t>(stream));
+}
+
 fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path, int32_t* launches_fused,
                         int32_t* launches_separate) {
   if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
@@ -1135,6 +1233,7 @@ fp_status fp_plan_set_out_dtype(fp_plan_t plan, int32_t out_dtype) {
   if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
   if (out_dtype != FP_BF16 && out_dtype != FP_F32) return FP_ERR_INVALID_ARG;
   if (plan->dtype == FP_F32) return out_dtype == FP_F32 ? FP_OK : FP_ERR_UNSUPPORTED;
+  if (plan->dtype == FP_MXFP8) return out_dtype == FP_BF16 ? FP_OK : FP_ERR_UNSUPPORTED;
   plan->out_f32 = out_dtype == FP_F32;
   plan->osize = plan->out_f32 ? 4 : 2;
   return FP_OK;
@@ -1194,10 +1293,12 @@ fp_status fp_plan_get_tiling(fp_plan_t plan, int64_t M, int64_t n_rows, fp_tilin
 
 fp_status fp_default_tiling(int32_t dtype, int64_t K, int64_t n_total, int64_t M,
                             int64_t n_rows, fp_tiling* out) {
-  if (out == nullptr || (dtype != FP_BF16 && dtype != FP_F32) || K < 1 || n_total < 1)
+  if (out == nullptr || (dtype != FP_BF16 && dtype != FP_F32 && dtype != FP_MXFP8) || K < 1 ||
+      n_total < 1)
     return FP_ERR_INVALID_ARG;
-  const int esize = dtype == FP_BF16 ? 2 : 4;
-  if ((K * esize) % 16 != 0) return FP_ERR_UNSUPPORTED;
+  int esize = 0;
+  int64_t wrow = 0, kc = 0;
+  if (!dtype_geometry(dtype, K, &esize, &wrow, &kc)) return FP_ERR_UNSUPPORTED;
   if (M < 1 || M > FP_MAX_M || n_rows < 1 || n_rows > n_total) return FP_ERR_INVALID_ARG;
   fp_plan_s tmp;
   scratch_plan(&tmp, dtype, K, n_total, FP_MAX_M);

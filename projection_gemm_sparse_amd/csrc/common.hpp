@@ -47,6 +47,7 @@ struct Tail {
 constexpr int kVarPlain = 0;
 constexpr int kVarPairs = 1;
 constexpr int kVarF32Out = 2;
+constexpr int kVarMx8 = 3;
 
 // Gate/up launches (the PAIRS variant of the kernels): the launch's n_rows =
 // 2N logical rows interleave the two halves of the weight buffer -- logical
@@ -80,8 +81,12 @@ constexpr int max_threads_for_regs(int regs) {
   return 256 * waves_per_simd;
 }
 
-constexpr int skinny_max_threads(int mt, int rw, int cj) {
-  return max_threads_for_regs(pow2ceil(rw * mt) + 4 * rw * cj + 4 * mt * cj + 32);
+// MXFP8 weights (kVarMx8) hold two activation chunks per weight chunk, a
+// scale per weight chunk and eight decoded pairs.
+constexpr int skinny_max_threads(int mt, int rw, int cj, int var = kVarPlain) {
+  return var == kVarMx8
+             ? max_threads_for_regs(pow2ceil(rw * mt) + 5 * rw * cj + 8 * mt * cj + 40)
+             : max_threads_for_regs(pow2ceil(rw * mt) + 4 * rw * cj + 4 * mt * cj + 32);
 }
 
 
@@ -214,6 +219,30 @@ __device__ __forceinline__ float dot_chunk(const u32x4& w, const u32x4& x,
     acc = __builtin_fmaf(u2f(w.z), u2f(x.z), acc);
     acc = __builtin_fmaf(u2f(w.w), u2f(x.w), acc);
   }
+  return acc;
+}
+
+// Two E4M3 codes (bytes 0-1 of `u`, or bytes 2-3 with `hi`) times an fp32
+// power-of-two scale, as a bf16 pair (element 0 from the lower byte):
+// v_cvt_scalef32_pk_bf16_fp8.  Exact whenever the scaled value lies in bf16's
+// normal range (an E4M3 value has at most 4 significant bits).
+__device__ __forceinline__ bf16x2 decode_e4m3_pair(unsigned u, float scale, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, scale, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, scale, false);
+}
+
+// Dot product of 16 decoded weights (eight bf16 pairs, element order) with
+// the 16 activations of two chunks, added into `acc` pair by pair in order.
+__device__ __forceinline__ float dot_decoded(const bf16x2* d, const u32x4& x0, const u32x4& x1,
+                                             float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[0], u2bf2(x0.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[1], u2bf2(x0.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[2], u2bf2(x0.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[3], u2bf2(x0.w), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[4], u2bf2(x1.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[5], u2bf2(x1.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[6], u2bf2(x1.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[7], u2bf2(x1.w), acc, false);
   return acc;
 }
 

@@ -1,0 +1,45 @@
+// mxfp8.hpp -- dequantisation of MXFP8 weight rows to bf16.
+//
+// The pages name MXFP8 projections for the DeepSeek-V4.1 wq_a / wkv weights
+// ("tinygemm2 for the DeepSeek-V4.1 hidden-state projections", TensorRT-LLM
+// PR #20636, Description) without defining the encoding; the reading is the
+// open microscaling format: E4M3 codes, one E8M0 scale per 32 consecutive
+// elements along K.  Storage (this library's layout): a row is its K codes
+// followed by its K/32 scales.  The projection kernels decode on the fly
+// (kVarMx8); this kernel writes the decoded weights out, for a caller that
+// needs them as bf16 (a fallback linear layer) and to check the decode.
+#pragma once
+
+#include "common.hpp"
+
+namespace fp {
+
+// Thread t decodes code chunk t (16 codes) of the rows: row t / kc, chunk
+// t % kc, to 32 bytes of bf16 at out[row, 16 * chunk ...].
+__global__ void __launch_bounds__(256)
+mxfp8_to_bf16_kernel(const unsigned char* __restrict__ w, unsigned char* __restrict__ out,
+                     int32_t kc, int64_t n_chunks) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_chunks) return;
+  const int64_t row = t / kc;
+  const int c = (int)(t - row * kc);
+  const uint64_t row_bytes = (uint64_t)kc * 16u + ((uint32_t)kc >> 1);
+  const unsigned char* wrow = w + (uint64_t)row * row_bytes;
+  const u32x4 q = *reinterpret_cast<const u32x4*>(wrow + (uint64_t)c * 16u);
+  const uint32_t sb = wrow[(uint64_t)kc * 16u + (uint32_t)(c >> 1)];
+  const float sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
+  u32x4 o0, o1;
+  o0.x = __builtin_bit_cast(unsigned, decode_e4m3_pair(q.x, sc, false));
+  o0.y = __builtin_bit_cast(unsigned, decode_e4m3_pair(q.x, sc, true));
+  o0.z = __builtin_bit_cast(unsigned, decode_e4m3_pair(q.y, sc, false));
+  o0.w = __builtin_bit_cast(unsigned, decode_e4m3_pair(q.y, sc, true));
+  o1.x = __builtin_bit_cast(unsigned, decode_e4m3_pair(q.z, sc, false));
+  o1.y = __builtin_bit_cast(unsigned, decode_e4m3_pair(q.z, sc, true));
+  o1.z = __builtin_bit_cast(unsigned, decode_e4m3_pair(q.w, sc, false));
+  o1.w = __builtin_bit_cast(unsigned, decode_e4m3_pair(q.w, sc, true));
+  u32x4* orow = reinterpret_cast<u32x4*>(out + ((uint64_t)row * kc * 16u + (uint64_t)c * 16u) * 2u);
+  orow[0] = o0;
+  orow[1] = o1;
+}
+
+}  // namespace fp

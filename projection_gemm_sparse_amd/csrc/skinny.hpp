@@ -60,9 +60,18 @@ namespace fp {
 //   kVarPairs   a gate/up launch (rows taken in pairs, see pair_row; RW
 //               even, S = 1, bf16) that writes silu(gate) * up;
 //   kVarF32Out  bf16 operands with fp32 outputs (router logits), up to 16
-//               tokens (MT = 16).
+//               tokens (MT = 16);
+//   kVarMx8     MXFP8 weights, bf16 activations and outputs.  A weight row
+//               is its K E4M3 codes followed by the K/32 E8M0 scales of its
+//               32-element blocks (row stride K + K/32 bytes); kc counts the
+//               16-byte code chunks (K/16), each 16 elements inside one
+//               block.  A chunk is decoded with its block's scale to eight
+//               bf16 pairs (v_cvt_scalef32_pk_bf16_fp8: exact, as an E4M3
+//               value times a power of two has at most 4 significant bits)
+//               and multiplied with the two activation chunks of its 16
+//               elements by v_dot2, in element order.
 template <int MT, int RW, int CJ, bool BF16, int VAR = kVarPlain>
-__global__ void __launch_bounds__(skinny_max_threads(MT, RW, CJ))
+__global__ void __launch_bounds__(skinny_max_threads(MT, RW, CJ, VAR))
 skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
               unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
               int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
@@ -72,6 +81,8 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   constexpr int LSTRIDE = VP >= 64 ? 1 : 64 / VP;
   constexpr bool PAIRS = VAR == kVarPairs;
   constexpr bool OUT_BF16 = BF16 && VAR != kVarF32Out;
+  constexpr bool MX8 = VAR == kVarMx8;
+  constexpr int XH = MX8 ? 2 : 1;  // activation chunks per weight chunk
 
   extern __shared__ float smem[];   // [G][VP][16] wave sums, then one flag
   const int tid = threadIdx.x;
@@ -90,7 +101,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   const int row_base = rb * (Gv * RW);
   const int wrow0 = row_base + gq * RW;
   const int cbase = s * (P * 64 * CJ) + p * (64 * CJ) + lane;
-  const uint32_t row_bytes = (uint32_t)kc * 16u;
+  const uint32_t row_bytes = MX8 ? (uint32_t)kc * 16u + ((uint32_t)kc >> 1) : (uint32_t)kc * 16u;
 
   // Loads are branch-free: an out-of-range chunk or row loads a clamped,
   // always-valid address, and out-of-range chunks are replaced by zero only
@@ -105,7 +116,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   // 1. the lane's activation chunks first: they come from L2/MALL and are
   //    needed by every row, so loading them ahead of the weights keeps them
   //    off the tail of the weight stream
-  u32x4 xv[MT][CJ];
+  u32x4 xv[MT][CJ * XH];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int mc = m < M ? m : M - 1;
@@ -113,11 +124,13 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
 #pragma unroll
     for (int j = 0; j < CJ; ++j) {
       const int c = cbase + j * 64;
-      xv[m][j] = xrow[c < kc ? c : kc - 1];
+#pragma unroll
+      for (int h = 0; h < XH; ++h) xv[m][j * XH + h] = xrow[(c < kc ? c : kc - 1) * XH + h];
     }
   }
   // 2. weight stream: every load of the lane issued up front, row by row
   u32x4 wv[RW][CJ];
+  uint32_t sv[MX8 ? RW : 1][CJ];  // E8M0 scale of each weight chunk (MXFP8)
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int lrow = wrow0 + r < n_rows ? wrow0 + r : n_rows - 1;
@@ -127,6 +140,14 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
     for (int j = 0; j < CJ; ++j) {
       const int c = cbase + j * 64;
       wv[r][j] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+    }
+    if constexpr (MX8) {
+      const unsigned char* srow = reinterpret_cast<const unsigned char*>(wrow) + (uint32_t)kc * 16u;
+#pragma unroll
+      for (int j = 0; j < CJ; ++j) {
+        const int c = cbase + j * 64;
+        sv[r][j] = srow[(c < kc ? c : kc - 1) >> 1];
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -141,7 +162,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
 #pragma unroll
-    for (int j = 0; j < CJ; ++j) xv[m][j] = (m < M && c_ok[j]) ? xv[m][j] : zero4;
+    for (int j = 0; j < CJ * XH; ++j) xv[m][j] = (m < M && c_ok[j / XH]) ? xv[m][j] : zero4;
   }
 
   // 3. per-lane partial sums in load order (row by row), so each row is
@@ -158,9 +179,24 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
 #pragma unroll
     for (int j = 0; j < CJ; ++j) {
       const u32x4 wj = c_ok[j] ? wv[r][j] : zero4;
+      if constexpr (MX8) {
+        // scale 2^(s - 127) as an fp32 (s = 0: the subnormal 2^-127)
+        const uint32_t sb = sv[r][j];
+        const float sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
+        const bf16x2 d[8] = {
+            decode_e4m3_pair(wj.x, sc, false), decode_e4m3_pair(wj.x, sc, true),
+            decode_e4m3_pair(wj.y, sc, false), decode_e4m3_pair(wj.y, sc, true),
+            decode_e4m3_pair(wj.z, sc, false), decode_e4m3_pair(wj.z, sc, true),
+            decode_e4m3_pair(wj.w, sc, false), decode_e4m3_pair(wj.w, sc, true)};
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        v[r * MT + m] = dot_chunk<BF16>(wj, xv[m][j], v[r * MT + m]);
+        for (int m = 0; m < MT; ++m) {
+          v[r * MT + m] = dot_decoded(d, xv[m][2 * j], xv[m][2 * j + 1], v[r * MT + m]);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          v[r * MT + m] = dot_chunk<BF16>(wj, xv[m][j], v[r * MT + m]);
+        }
       }
     }
   }

@@ -19,6 +19,8 @@ import torch
 from . import _lib as L
 
 _DTYPES = {torch.bfloat16: L.FP_BF16, torch.float32: L.FP_F32}
+# MXFP8 weights arrive as packed uint8 rows: K E4M3 codes, then K/32 E8M0
+# scales (K + K/32 bytes per row)
 
 
 def _stream_handle(stream) -> int:
@@ -31,6 +33,9 @@ class FusedProjection:
 
     ``copy_weights=True`` copies the given tensors into the concatenated
     buffer; the caller may then rebind its module weights to ``views``.
+    MXFP8 weights are uint8 tensors of packed rows [N_i, K + K/32] (the K
+    E4M3 codes, then the K/32 E8M0 scales); activations and outputs are
+    then bf16.
     """
 
     def __init__(self, weights, max_M: int = 8, stream=None, copy_weights: bool = True,
@@ -38,25 +43,37 @@ class FusedProjection:
         if not weights:
             raise ValueError("at least one projection")
         w0 = weights[0]
-        if w0.dtype not in _DTYPES:
-            raise TypeError("weights must be bfloat16 or float32, got %s" % w0.dtype)
+        if w0.dtype not in _DTYPES and w0.dtype != torch.uint8:
+            raise TypeError("weights must be bfloat16, float32 or packed MXFP8 (uint8), got %s"
+                            % w0.dtype)
         if not w0.is_cuda:
             raise ValueError("weights must be on a GPU")
-        self.dtype = w0.dtype
-        self.fp_dtype = _DTYPES[w0.dtype]
+        self.w_dtype = w0.dtype
+        if w0.dtype == torch.uint8:
+            cols = int(w0.shape[1])
+            if cols % 33 != 0:
+                raise ValueError("packed MXFP8 rows hold K + K/32 bytes")
+            self.dtype = torch.bfloat16  # activations and outputs
+            self.fp_dtype = L.FP_MXFP8
+            self.K = cols // 33 * 32
+        else:
+            self.dtype = w0.dtype
+            self.fp_dtype = _DTYPES[w0.dtype]
+            self.K = int(w0.shape[1])
         self.device = w0.device
-        self.K = int(w0.shape[1])
+        self.row_cols = int(w0.shape[1])
         self.N = [int(w.shape[0]) for w in weights]
         for w in weights:
-            if w.dtype != self.dtype or w.device != self.device or w.dim() != 2 \
-                    or int(w.shape[1]) != self.K:
+            if w.dtype != self.w_dtype or w.device != self.device or w.dim() != 2 \
+                    or int(w.shape[1]) != self.row_cols:
                 raise ValueError("all weights must be [N_i, K] of one dtype on one device")
         self.max_M = int(max_M)
         self.n_total = sum(self.N)
         # plan creation under no_grad: the concatenated buffer must not keep
         # an autograd graph alive (lesson of PR #20502's commit log)
         with torch.no_grad():
-            self.w_cat = torch.empty(self.n_total, self.K, dtype=self.dtype, device=self.device)
+            self.w_cat = torch.empty(self.n_total, self.row_cols, dtype=self.w_dtype,
+                                     device=self.device)
             self.ws_bytes = L.fp_workspace_bytes(self.fp_dtype, self.K, self.N, self.max_M)
             if self.ws_bytes == 0:
                 raise L.FusedProjError(L.FP_ERR_INVALID_ARG, "fp_workspace_bytes")
@@ -147,10 +164,10 @@ class FusedProjection:
                 if w is None:
                     ov.append(None)
                     continue
-                if tuple(w.shape) != (self.N[i], self.K) or not w.is_contiguous() \
-                        or w.dtype != self.dtype or w.device != self.device:
+                if tuple(w.shape) != (self.N[i], self.row_cols) or not w.is_contiguous() \
+                        or w.dtype != self.w_dtype or w.device != self.device:
                     raise ValueError("override %d must be a dense [%d, %d] tensor"
-                                     % (i, self.N[i], self.K))
+                                     % (i, self.N[i], self.row_cols))
                 ov.append(w.data_ptr())
         st = L.fp_forward_separate(x.data_ptr(), M, int(x.stride(0)), self.plan,
                                    _stream_handle(stream), [y.data_ptr() for y in ys], ov)

@@ -31,7 +31,7 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("args", [
-    (2, 5120, [1280, 512], 8),      # bad dtype
+    (3, 5120, [1280, 512], 8),      # bad dtype
     (0, 0, [1280, 512], 8),         # K < 1
     (0, 5121, [1280, 512], 8),      # K*2 not a multiple of 16
     (1, 7170, [128], 8),            # K*4 not a multiple of 16
@@ -205,3 +205,17 @@ def test_epilogue_argument_checks_before_any_hip_call():
 
 def test_out_dtype_on_a_null_plan():
     assert P.fp_plan_set_out_dtype(None, P.FP_F32) == P.FP_ERR_INVALID_ARG
+
+
+def test_mxfp8_geometry_checks():
+    # packed rows need K a multiple of 512; the dequantiser refuses before any launch
+    assert P.fp_workspace_bytes(P.FP_MXFP8, 5120, [1280, 512], 8) > 0
+    assert P.fp_workspace_bytes(P.FP_MXFP8, 5136, [1280, 512], 8) == 0
+    assert P.fp_mxfp8_to_bf16(FAKE, 2, 528, FAKE + (1 << 24), 0) == P.FP_ERR_UNSUPPORTED
+    assert P.fp_mxfp8_to_bf16(FAKE, -1, 512, FAKE + (1 << 24), 0) == P.FP_ERR_INVALID_ARG
+    assert P.fp_mxfp8_to_bf16(FAKE, 0, 512, FAKE + (1 << 24), 0) == P.FP_OK
+    assert P.fp_mxfp8_to_bf16(FAKE, 4, 512, FAKE + 64, 0) == P.FP_ERR_INVALID_ARG  # overlap
+    st, t = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 8, 1792)
+    assert st == P.FP_OK and t[0] == P.FP_PATH_SKINNY and t[1] * 64 * t[2] >= 320
+    st, _ = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 9, 1792)
+    assert st == P.FP_ERR_UNSUPPORTED
