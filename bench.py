@@ -331,6 +331,45 @@ def router_cells(P, torch, dev, steps, Ms=(1, 4, 8, 16)):
     return res
 
 
+def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8)):
+    """The wq_a + wkv projection with MXFP8 weights (E4M3 codes, one E8M0
+    scale per 32 elements; packed rows of K + K/32 bytes), bf16 x and y, on
+    a pool of weight copies rotated past the MALL."""
+    import synthetic_inputs as si
+    row = K + K // 32
+    wb = sum(N) * row
+    n = max(2, math.ceil((1 << 30) / wb))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    plans = []
+    for _ in range(n):
+        ws = []
+        for nr in N:
+            codes = torch.randint(0, 254, (nr, K), generator=g, device="cuda")
+            codes = codes + (codes >= 0x7F).to(codes.dtype)
+            sc = torch.randint(112, 118, (nr, K // 32), generator=g, device="cuda")
+            ws.append(torch.cat([codes, sc], 1).to(torch.uint8))
+        plans.append(P.FusedProjection(ws, max_M=8))
+        del ws
+    res = {}
+    for M in Ms:
+        x = si.make_case(K, N, "bf16", M, seed=600 + M)[0].to(dev)
+        out = [torch.empty(M, nr, dtype=torch.bfloat16, device=dev) for nr in N]
+        gr = capture(torch, lambda: [p.forward(x, out=out) for p in plans])
+        t, _ = time_graphs(torch, [gr], steps, 2)
+        us = t * 1e3 / (steps * n)
+        b = wb + 2 * M * K + 2 * M * sum(N)
+        res[str(M)] = {"us": round(us, 4), "GBps": round(b / us / 1e3, 1), "bytes": b,
+                       "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                       "tiling": list(plans[0].get_tiling(M))}
+        del gr
+    for p in plans:
+        p.close()
+    res["note"] = ("wq_a+wkv [1280,512]x5120 with MXFP8 weights (%d bytes per call), %d "
+                   "copies rotated (1 GiB), one call per copy, hipGraph replay" % (wb, n))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -520,6 +559,7 @@ def main():
         line["epilogues"] = epilogue_cells(P, torch, dev, plans, n_copies,
                                            max(3, args.steps // 4))
         line["router_f32"] = router_cells(P, torch, dev, max(3, args.steps // 4))
+        line["mxfp8"] = mxfp8_cells(P, torch, dev, max(3, args.steps // 4))
     if args.crossover:
         crossover(args.crossover, P, torch, dev, plans, n_copies)
     print(json.dumps(line), flush=True)

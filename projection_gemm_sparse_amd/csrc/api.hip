@@ -61,7 +61,7 @@ struct fp_plan_s {
   int32_t dtype;
   int32_t esize;
   int64_t K;
-  int64_t kc;  // 16-byte chunks per row (MXFP8: code chunks, K / 16)
+  int64_t kc;  // 16-byte chunks per row (MXFP8: 8-element units, K / 8)
   int64_t wrow;  // bytes per weight row (MXFP8: K codes + K / 32 scales)
   int32_t n_proj;
   int64_t N[FP_MAX_PROJ];
@@ -98,10 +98,11 @@ bool dtype_geometry(int32_t dtype, int64_t K, int* esize, int64_t* wrow, int64_t
     return true;
   }
   if (dtype == FP_MXFP8) {
+    // units of 8 elements (8 code bytes), as the bf16 kernel's chunks
     if (K % 512 != 0) return false;
     *esize = 2;
     *wrow = K + K / 32;
-    *kc = K / 16;
+    *kc = K / 8;
     return true;
   }
   return false;
@@ -1201,8 +1202,8 @@ fp_status fp_mxfp8_to_bf16(const void* w, int64_t rows, int64_t K, void* out, vo
   if (range_overlaps(w, rows * wrow, out, rows * K * 2)) return FP_ERR_INVALID_ARG;
   const unsigned char* w_a = static_cast<const unsigned char*>(w);
   unsigned char* o_a = static_cast<unsigned char*>(out);
-  int32_t kc_a = (int32_t)kc;
-  int64_t n_a = rows * kc;
+  int32_t kc_a = (int32_t)(K / 16);  // 16-code chunks
+  int64_t n_a = rows * kc_a;
   void* args[] = {&w_a, &o_a, &kc_a, &n_a};
   return launch(reinterpret_cast<const void*>(&fp::mxfp8_to_bf16_kernel), ceil_div(n_a, 256), 256,
                 0, args, static_cast<hipStream_t>(stream));

@@ -8,6 +8,7 @@
 namespace fp {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -81,11 +82,11 @@ constexpr int max_threads_for_regs(int regs) {
   return 256 * waves_per_simd;
 }
 
-// MXFP8 weights (kVarMx8) hold two activation chunks per weight chunk, a
-// scale per weight chunk and eight decoded pairs.
+// MXFP8 weights (kVarMx8) hold 8-byte code units, a scale per unit and four
+// decoded pairs.
 constexpr int skinny_max_threads(int mt, int rw, int cj, int var = kVarPlain) {
   return var == kVarMx8
-             ? max_threads_for_regs(pow2ceil(rw * mt) + 5 * rw * cj + 8 * mt * cj + 40)
+             ? max_threads_for_regs(pow2ceil(rw * mt) + 3 * rw * cj + 4 * mt * cj + 36)
              : max_threads_for_regs(pow2ceil(rw * mt) + 4 * rw * cj + 4 * mt * cj + 32);
 }
 
@@ -231,18 +232,14 @@ __device__ __forceinline__ bf16x2 decode_e4m3_pair(unsigned u, float scale, bool
             : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, scale, false);
 }
 
-// Dot product of 16 decoded weights (eight bf16 pairs, element order) with
-// the 16 activations of two chunks, added into `acc` pair by pair in order.
-__device__ __forceinline__ float dot_decoded(const bf16x2* d, const u32x4& x0, const u32x4& x1,
-                                             float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(d[0], u2bf2(x0.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(d[1], u2bf2(x0.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(d[2], u2bf2(x0.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(d[3], u2bf2(x0.w), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(d[4], u2bf2(x1.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(d[5], u2bf2(x1.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(d[6], u2bf2(x1.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(d[7], u2bf2(x1.w), acc, false);
+// Dot product of 8 decoded weights (four bf16 pairs, element order) with
+// the 8 activations of one chunk, added into `acc` pair by pair in order
+// (the order of dot_chunk).
+__device__ __forceinline__ float dot_decoded(const bf16x2* d, const u32x4& x, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[0], u2bf2(x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[1], u2bf2(x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[2], u2bf2(x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(d[3], u2bf2(x.w), acc, false);
   return acc;
 }
 

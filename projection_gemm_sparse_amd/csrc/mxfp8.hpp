@@ -15,7 +15,7 @@
 namespace fp {
 
 // Thread t decodes code chunk t (16 codes) of the rows: row t / kc, chunk
-// t % kc, to 32 bytes of bf16 at out[row, 16 * chunk ...].
+// t % kc (kc = K / 16), to 32 bytes of bf16 at out[row, 16 * chunk ...].
 __global__ void __launch_bounds__(256)
 mxfp8_to_bf16_kernel(const unsigned char* __restrict__ w, unsigned char* __restrict__ out,
                      int32_t kc, int64_t n_chunks) {

@@ -63,13 +63,15 @@ namespace fp {
 //               tokens (MT = 16);
 //   kVarMx8     MXFP8 weights, bf16 activations and outputs.  A weight row
 //               is its K E4M3 codes followed by the K/32 E8M0 scales of its
-//               32-element blocks (row stride K + K/32 bytes); kc counts the
-//               16-byte code chunks (K/16), each 16 elements inside one
-//               block.  A chunk is decoded with its block's scale to eight
-//               bf16 pairs (v_cvt_scalef32_pk_bf16_fp8: exact, as an E4M3
-//               value times a power of two has at most 4 significant bits)
-//               and multiplied with the two activation chunks of its 16
-//               elements by v_dot2, in element order.
+//               32-element blocks (row stride K + K/32 bytes).  The unit of
+//               work is 8 elements, as in the bf16 kernel: kc counts them
+//               (K/8); a lane loads the unit's 8 codes (8 bytes) and its
+//               block's scale, decodes them to four bf16 pairs
+//               (v_cvt_scalef32_pk_bf16_fp8: exact, an E4M3 value times a
+//               power of two has at most 4 significant bits) and multiplies
+//               them with the unit's activation chunk by v_dot2 in element
+//               order -- the bf16 kernel's arithmetic on half the weight
+//               bytes.
 template <int MT, int RW, int CJ, bool BF16, int VAR = kVarPlain>
 __global__ void __launch_bounds__(skinny_max_threads(MT, RW, CJ, VAR))
 skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
@@ -82,7 +84,6 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   constexpr bool PAIRS = VAR == kVarPairs;
   constexpr bool OUT_BF16 = BF16 && VAR != kVarF32Out;
   constexpr bool MX8 = VAR == kVarMx8;
-  constexpr int XH = MX8 ? 2 : 1;  // activation chunks per weight chunk
 
   extern __shared__ float smem[];   // [G][VP][16] wave sums, then one flag
   const int tid = threadIdx.x;
@@ -101,7 +102,8 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   const int row_base = rb * (Gv * RW);
   const int wrow0 = row_base + gq * RW;
   const int cbase = s * (P * 64 * CJ) + p * (64 * CJ) + lane;
-  const uint32_t row_bytes = MX8 ? (uint32_t)kc * 16u + ((uint32_t)kc >> 1) : (uint32_t)kc * 16u;
+  // MXFP8: 8 code bytes per unit, then one scale byte per 4 units
+  const uint32_t row_bytes = MX8 ? (uint32_t)kc * 8u + ((uint32_t)kc >> 2) : (uint32_t)kc * 16u;
 
   // Loads are branch-free: an out-of-range chunk or row loads a clamped,
   // always-valid address, and out-of-range chunks are replaced by zero only
@@ -116,7 +118,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   // 1. the lane's activation chunks first: they come from L2/MALL and are
   //    needed by every row, so loading them ahead of the weights keeps them
   //    off the tail of the weight stream
-  u32x4 xv[MT][CJ * XH];
+  u32x4 xv[MT][CJ];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int mc = m < M ? m : M - 1;
@@ -124,29 +126,37 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
 #pragma unroll
     for (int j = 0; j < CJ; ++j) {
       const int c = cbase + j * 64;
-#pragma unroll
-      for (int h = 0; h < XH; ++h) xv[m][j * XH + h] = xrow[(c < kc ? c : kc - 1) * XH + h];
+      xv[m][j] = xrow[c < kc ? c : kc - 1];
     }
   }
   // 2. weight stream: every load of the lane issued up front, row by row
-  u32x4 wv[RW][CJ];
-  uint32_t sv[MX8 ? RW : 1][CJ];  // E8M0 scale of each weight chunk (MXFP8)
+  u32x4 wv[MX8 ? 1 : RW][CJ];
+  u32x2 qv[MX8 ? RW : 1][CJ];     // MXFP8: the unit's 8 codes
+  uint32_t sv[MX8 ? RW : 1][CJ];  // MXFP8: its block's E8M0 scale
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int lrow = wrow0 + r < n_rows ? wrow0 + r : n_rows - 1;
     const int row = PAIRS ? pair_row(lrow, split) : lrow;
-    const u32x4* wrow = reinterpret_cast<const u32x4*>(w + (uint64_t)(uint32_t)row * row_bytes);
-#pragma unroll
-    for (int j = 0; j < CJ; ++j) {
-      const int c = cbase + j * 64;
-      wv[r][j] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
-    }
+    const unsigned char* wrow_b = w + (uint64_t)(uint32_t)row * row_bytes;
     if constexpr (MX8) {
-      const unsigned char* srow = reinterpret_cast<const unsigned char*>(wrow) + (uint32_t)kc * 16u;
+      const u32x2* wrow = reinterpret_cast<const u32x2*>(wrow_b);
 #pragma unroll
       for (int j = 0; j < CJ; ++j) {
         const int c = cbase + j * 64;
-        sv[r][j] = srow[(c < kc ? c : kc - 1) >> 1];
+        qv[r][j] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+      }
+      const unsigned char* srow = wrow_b + (uint32_t)kc * 8u;
+#pragma unroll
+      for (int j = 0; j < CJ; ++j) {
+        const int c = cbase + j * 64;
+        sv[r][j] = srow[(c < kc ? c : kc - 1) >> 2];
+      }
+    } else {
+      const u32x4* wrow = reinterpret_cast<const u32x4*>(wrow_b);
+#pragma unroll
+      for (int j = 0; j < CJ; ++j) {
+        const int c = cbase + j * 64;
+        wv[r][j] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
       }
     }
   }
@@ -162,7 +172,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
 #pragma unroll
-    for (int j = 0; j < CJ * XH; ++j) xv[m][j] = (m < M && c_ok[j / XH]) ? xv[m][j] : zero4;
+    for (int j = 0; j < CJ; ++j) xv[m][j] = (m < M && c_ok[j]) ? xv[m][j] : zero4;
   }
 
   // 3. per-lane partial sums in load order (row by row), so each row is
@@ -178,21 +188,21 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < CJ; ++j) {
-      const u32x4 wj = c_ok[j] ? wv[r][j] : zero4;
       if constexpr (MX8) {
-        // scale 2^(s - 127) as an fp32 (s = 0: the subnormal 2^-127)
+        // codes past K read as zero; scale 2^(s - 127) as an fp32 (s = 0:
+        // the subnormal 2^-127)
+        const u32x2 q = c_ok[j] ? qv[r][j] : u32x2{0u, 0u};
         const uint32_t sb = sv[r][j];
         const float sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
-        const bf16x2 d[8] = {
-            decode_e4m3_pair(wj.x, sc, false), decode_e4m3_pair(wj.x, sc, true),
-            decode_e4m3_pair(wj.y, sc, false), decode_e4m3_pair(wj.y, sc, true),
-            decode_e4m3_pair(wj.z, sc, false), decode_e4m3_pair(wj.z, sc, true),
-            decode_e4m3_pair(wj.w, sc, false), decode_e4m3_pair(wj.w, sc, true)};
+        const unsigned q0 = q.x, q1 = q.y;
+        const bf16x2 d[4] = {decode_e4m3_pair(q0, sc, false), decode_e4m3_pair(q0, sc, true),
+                             decode_e4m3_pair(q1, sc, false), decode_e4m3_pair(q1, sc, true)};
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          v[r * MT + m] = dot_decoded(d, xv[m][2 * j], xv[m][2 * j + 1], v[r * MT + m]);
+          v[r * MT + m] = dot_decoded(d, xv[m][j], v[r * MT + m]);
         }
       } else {
+        const u32x4 wj = c_ok[j] ? wv[r][j] : zero4;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           v[r * MT + m] = dot_chunk<BF16>(wj, xv[m][j], v[r * MT + m]);
