@@ -90,9 +90,9 @@ def kernel_name(P, M: int, tiling) -> str:
     path, kparts, chunks, splits, rows, groups = tiling
     if path in (P.FP_PATH_SKINNY, P.FP_PATH_SKINNY_SPLITK):
         mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
-        return "fp::skinny_kernel<%d, %d, %d, true>" % (mt, rows, chunks)
+        return "fp::skinny_kernel<%d, %d, %d, true, 0>" % (mt, rows, chunks)
     if path == P.FP_PATH_MFMA_SMALL:
-        return "fp::smfma_kernel<%d>" % chunks
+        return "fp::smfma_kernel<%d, false>" % chunks
     mt16 = next(b for b in (1, 2, 4, 8, 16) if 16 * b >= M)
     cs = 4 if chunks in (8, 16) else 5
     return "fp::tile_kernel<%d, %d, %d, %d>" % (mt16, kparts, cs, chunks // cs)
@@ -388,6 +388,9 @@ def main():
                     help="skip the fused RMSNorm / SwiGLU epilogue cells")
     ap.add_argument("--crossover", default="",
                     help="also time every kernel path per M in 1..128 and write the table here")
+    ap.add_argument("--mxfp8-only", action="store_true",
+                    help="time only the MXFP8-weight cell and print it (profiler runs of "
+                         "that kernel); not the benchmark line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -401,6 +404,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mxfp8_only:
+        res = mxfp8_cells(P, torch, dev, args.steps)
+        if args.calib_copy_mib:
+            src = torch.ones((args.calib_copy_mib << 20) // 2, dtype=torch.bfloat16, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                torch.neg(src, out=dst)
+            torch.cuda.synchronize()
+        print(json.dumps({"mxfp8": res}), flush=True)
+        return
     w_bytes = sum(N) * K * 2
     n_copies = max(2, math.ceil((args.pool_mib << 20) / w_bytes))
     print("bench: pool of %d weight copies (%.0f MiB), M=%s" %

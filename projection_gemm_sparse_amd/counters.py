@@ -1,7 +1,9 @@
 """Summaries of rocprofv3 runs of bench.py (kernel trace and HBM counters).
 
     python -m projection_gemm_sparse_amd.counters --trace DIR --pmc DIR [DIR ...] \\
-        --out-md FILE.md --out-json profiles/traffic.json --command "..."
+        --calib-bytes B --out-md FILE.md --out-json profiles/traffic.json --command "..."
+    python -m projection_gemm_sparse_amd.counters --trace DIR --trace-only \\
+        --out-md FILE.md --command "..."
 
 Reads the CSV files rocprofv3 writes (``*_kernel_stats.csv`` of a
 ``--kernel-trace --stats`` run; ``*_counter_collection.csv`` of ``--pmc``
@@ -78,19 +80,42 @@ def hbm_bytes(c):
     return rd, wr
 
 
+def trace_only(args):
+    """Markdown table of the library's kernels in one kernel-trace run."""
+    rows = [r for r in load_stats(args.trace)
+            if r["kernel"].startswith("void fp::") or r["kernel"].startswith("fp::")]
+    lines = ["# %s" % (args.title or "Kernel trace"), "",
+             "Command (run from /tmp with TMPDIR=/tmp, repository root $R):", "", "```"]
+    lines += args.command + ["```", ""]
+    lines += ["| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: r["kernel"]):
+        lines.append("| `%s` | %d | %.1f | %.0f | %.0f |" % (
+            r["kernel"].replace("void ", ""), r["calls"], r["avg_ns"], r["min_ns"], r["max_ns"]))
+    with open(args.out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("wrote", args.out_md)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
-    ap.add_argument("--pmc", nargs="+", required=True)
-    ap.add_argument("--calib-bytes", type=int, required=True,
+    ap.add_argument("--trace-only", action="store_true",
+                    help="only summarise the kernel trace (no counters)")
+    ap.add_argument("--pmc", nargs="+", default=[])
+    ap.add_argument("--calib-bytes", type=int, default=0,
                     help="bytes read (and written) by the calibration copy kernel")
     ap.add_argument("--calib-name", default="neg_kernel",
                     help="substring of the calibration kernel's name")
     ap.add_argument("--out-md", required=True)
-    ap.add_argument("--out-json", required=True)
+    ap.add_argument("--out-json", default="")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--title", default="")
     args = ap.parse_args()
+    if args.trace_only:
+        trace_only(args)
+        return
+    if not args.pmc or not args.calib_bytes or not args.out_json:
+        raise SystemExit("--pmc, --calib-bytes and --out-json are needed with counters")
 
     import sys
     sys.path.insert(0, ROOT)
