@@ -228,7 +228,8 @@ fp_status fp_swiglu(const void* g, const void* u, int64_t M, int64_t N,
                     void* h, void* stream);
 
 /* Which kernel fp_forward runs for M, and how many kernel launches
- * fp_forward and fp_forward_separate make (0 for M == 0).  Any output
+ * fp_forward and fp_forward_separate make (0 for M == 0; a split tile
+ * launch whose slices are added in a second launch counts two).  Any output
  * pointer may be NULL.  Host-only. */
 fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path,
                         int32_t* launches_fused, int32_t* launches_separate);
@@ -271,7 +272,11 @@ fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
  *   rows    skinny: rows per wave (RW, 1..8); mfma-small: rows per tile
  *           (1..8); 0 = chosen per launch from its row count; mfma: unused
  *   groups  skinny and mfma-small: row groups per workgroup (G); 0 =
- *           chosen per launch; mfma: unused */
+ *           chosen per launch; mfma: how the K slices are added -- 1 by
+ *           the last workgroup of each row block, in the launch; 2 by a
+ *           second launch spread over the GPU (same order, same bits); 0 =
+ *           chosen per launch (second launch when a row block's partials
+ *           exceed 64 KiB) */
 typedef struct {
   int32_t path;
   int32_t kparts;

@@ -337,13 +337,22 @@ size_t skinny_lds(const Tiling& t) {
   return (size_t)t.groups * VP * fp::kMaxWaveParts * 4 + 16;
 }
 
+// Partial-sum bytes one row block of a split tile launch leaves for its
+// finish, above which the slices are added in a second launch spread over
+// the GPU instead of by the row block's last workgroup.
+constexpr int64_t kSecondFinishBytes = 64 * 1024;
+
 void resolve_tile_launch(const fp_plan_s* p, int64_t n_rows, Tiling* t) {
   const int64_t n_steps = ceil_div(p->kc, 4);
   const int64_t per = ceil_div(n_steps, std::max(1, t->splits));
   if (t->kparts <= 0) t->kparts = tile_pick_nw(t->mt, n_steps, t->splits, n_rows);
   if (t->chunks <= 0) t->chunks = tile_per_bound(per);
-  t->rows = 1;    // unused by the tile kernel
-  t->groups = 1;
+  t->rows = 1;  // unused by the tile kernel
+  // groups: 1 = slices finished in the launch, 2 = in a second launch
+  if (t->groups <= 0) {
+    const int64_t block_bytes = (int64_t)t->splits * 16 * t->kparts * 16 * t->mt * 4;
+    t->groups = t->splits > 1 && block_bytes > kSecondFinishBytes ? 2 : 1;
+  }
 }
 
 // Partial-sum floats a tiling needs for a launch of n_rows rows and M tokens.
@@ -366,6 +375,7 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     for (int nw : kTileNws) nw_ok = nw_ok || nw == t.kparts;
     for (int b : kTilePers) per_ok = per_ok || b == t.chunks;
     if (!nw_ok || !per_ok || per > t.chunks) return false;
+    if (t.groups != 1 && t.groups != 2) return false;
     if (tile_lds(t.mt, per, t.kparts) > kMaxLds) return false;
     if (16 * (int64_t)t.mt < M) return false;
     // buffer offsets are 32-bit
@@ -788,11 +798,20 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   }
   if (pairs && t.path != FP_PATH_SKINNY) return FP_ERR_UNSUPPORTED;
   if (t.path == FP_PATH_MFMA) {
-    geo_a = t.splits;
+    const bool second = t.splits > 1 && t.groups == 2;
+    geo_a = t.splits | (second ? fp::kGeoSecondFinish : 0);
     const int64_t per = ceil_div(ceil_div(p->kc, 4), t.splits);
     const int64_t blocks = ceil_div(lr.n_rows, 16 * (int64_t)t.kparts) * t.splits;
     const size_t lds = std::max<size_t>(tile_lds(t.mt, per, t.kparts), 16);
-    return launch(mfma_fn(t), blocks, t.kparts * 64, lds, args, stream);
+    fp_status st = launch(mfma_fn(t), blocks, t.kparts * 64, lds, args, stream);
+    if (st != FP_OK || !second) return st;
+    // the slices, added in slice order over the whole GPU
+    const float* part_a = tail.partial;
+    int32_t mpad_a = 16 * t.mt;
+    int32_t s_a = t.splits;
+    void* rargs[] = {&part_a, &n_rows_a, &M_a, &mpad_a, &s_a, &tail.out};
+    return launch(reinterpret_cast<const void*>(&fp::splitk_reduce_kernel),
+                  ceil_div((int64_t)lr.n_rows * ceil_div(M, 4), 256), 256, 0, rargs, stream);
   }
   geo_a = t.kparts | (t.groups << 8) | (t.splits << 16);
   const int64_t R = (int64_t)t.groups * t.rows;
@@ -1224,9 +1243,19 @@ fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path, int32_t* launc
     return FP_ERR_UNSUPPORTED;
   Tiling t;
   if (!choose_tiling(plan, M, plan->n_total, &t)) return FP_ERR_UNSUPPORTED;
+  // a split tile launch finished in a second launch counts two
+  auto count = [](const Tiling& u) {
+    return u.path == FP_PATH_MFMA && u.splits > 1 && u.groups == 2 ? 2 : 1;
+  };
+  int32_t n_sep = 0;
+  for (int i = 0; i < plan->n_proj; ++i) {
+    Tiling ti;
+    if (!choose_tiling(plan, M, plan->N[i], &ti)) return FP_ERR_UNSUPPORTED;
+    n_sep += count(ti);
+  }
   if (path) *path = t.path;
-  if (launches_fused) *launches_fused = 1;
-  if (launches_separate) *launches_separate = plan->n_proj;
+  if (launches_fused) *launches_fused = count(t);
+  if (launches_separate) *launches_separate = n_sep;
   return FP_OK;
 }
 

@@ -140,7 +140,11 @@ __device__ __forceinline__ void splitk_finish_vec(const float* partial, uint32_t
 }
 
 // Leading scalars preloaded into SGPRs (see skinny_kernel for w, x, y0, y1,
-// ldx, n_rows, kc, M, split); geo = S (k-step slices across workgroups).
+// ldx, n_rows, kc, M, split); geo = S (k-step slices across workgroups),
+// plus kGeoSecondFinish: the slices are added by splitk_reduce_kernel in a
+// second launch instead of by the last workgroup of each row block.
+constexpr int kGeoSecondFinish = 1 << 30;
+
 template <int MT16, int NW, int CS, int C>
 __global__ void __launch_bounds__(NW * 64)
 tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
@@ -158,7 +162,7 @@ tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int S = geo;
+  const int S = geo & 0x1fff;
   const int rb = S == 1 ? (int)blockIdx.x : (int)blockIdx.x / S;
   const int s = S == 1 ? 0 : (int)blockIdx.x - rb * S;
   const int row_base = rb * (16 * NW);
@@ -272,9 +276,51 @@ tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict
       if (row < n_rows) store_partial(partial + ((int64_t)s * n_rows + row) * MP + m, val);
     }
   }
+  if (geo & kGeoSecondFinish) return;  // splitk_reduce_kernel adds the slices
   __syncthreads();  // every wave is done reading the activation slice
   splitk_finish_vec<true>(partial, counters, rb, S, row_base, 16 * NW, n_rows, M, MP, NT, om,
                           a.out, reinterpret_cast<int*>(lds_raw));
+}
+
+// The second-launch finish of a split tile launch: thread t adds, for launch
+// row t / ceil(M/4) and four consecutive tokens, the S slices of the
+// partials in slice order -- the order of splitk_finish_vec, so both
+// finishes give the same bits -- and stores the outputs rounded once.  A
+// launch of many tokens has large partials per row block (S * 16 * NW rows
+// * 16 * MT16 tokens); one workgroup per row block re-reading them (the
+// in-launch finish) is then slower than spreading the sum over the whole
+// GPU after a kernel boundary.
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ partial, int32_t n_rows, int32_t M, int32_t m_pad,
+                     int32_t S, const OutTable tab) {
+  const int vec_per_row = (M + 3) >> 2;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)n_rows * vec_per_row) return;
+  const int row = (int)(t / vec_per_row);
+  const int m0 = (int)(t - (int64_t)row * vec_per_row) * 4;
+  const int64_t sstride = (int64_t)n_rows * m_pad;
+  const f32x4* p = reinterpret_cast<const f32x4*>(partial + (int64_t)row * m_pad + m0);
+  f32x4 sum = p[0];
+  for (int ss = 1; ss < S; ++ss) {
+    const f32x4 v = p[ss * sstride / 4];
+    const float a0 = sum[0], a1 = sum[1], a2 = sum[2], a3 = sum[3];
+    const float b0 = v[0], b1 = v[1], b2 = v[2], b3 = v[3];
+    sum = f32x4{a0 + b0, a1 + b1, a2 + b2, a3 + b3};
+  }
+  // the row's segment: the last one whose first row is at or before it
+  int seg = 0;
+  for (int i = 1; i < tab.n_seg; ++i) seg = row >= tab.begin[i] ? i : seg;
+  OutMap om;
+  om.y0 = tab.y[seg];
+  om.y1 = tab.y[seg];
+  om.b0 = tab.begin[seg];
+  om.b1 = tab.begin[seg + 1];
+  om.e1 = tab.begin[seg + 1];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float vj = sum[j];
+    if (m0 + j < M) store_y<true>(om, tab, row, m0 + j, vj);
+  }
 }
 
 }  // namespace fp

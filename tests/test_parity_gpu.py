@@ -278,3 +278,24 @@ def test_small_mfma_path(case, M):
     assert fp.set_tiling(M, _small_mfma_tiling(fp.K)) == P.FP_OK
     assert fp.query(M)[0] == P.FP_PATH_MFMA_SMALL
     _check_case(fp, x, ws, "small-M MFMA %s M=%d" % (case, M))
+
+
+# ---- the split tile path finishes its K slices either in the launch (last
+#      workgroup of each row block) or in a second launch over the whole GPU;
+#      both add the slices in slice order: bitwise equal
+@pytest.mark.parametrize("M", [16, 64, 128])
+def test_tile_finish_in_launch_equals_second_launch(M):
+    x, ws = si.workload_case("crossover", M, 6)
+    fp = _plan(ws, max_M=128)
+    xg = to_gpu(x)
+    t = list(fp.get_tiling(M))
+    assert t[0] == P.FP_PATH_MFMA and t[3] > 1 and t[5] in (1, 2)
+    outs = {}
+    for g in (1, 2):
+        assert fp.set_tiling(M, tuple(t[:5] + [g])) == P.FP_OK
+        outs[g] = fp(xg)
+        assert_matches_oracle(outs[g], x, ws, label="finish %d M=%d" % (g, M))
+        assert_bitwise_equal(outs[g], fp.forward_separate(xg), "finish %d fused/sep" % g)
+        assert fp.query(M)[1] == g
+    assert_bitwise_equal(outs[1], outs[2], "in-launch vs second-launch finish")
+    fp.set_tiling(M, None)
