@@ -29,7 +29,8 @@ MXFP8 weights (``oracle.c``, ``linear_mxfp8``): E4M3 codes with one E8M0
 scale per 32 elements along K, decoded from the open microscaling format's
 definition (the pages name MXFP8 projections without defining them); the
 sum is the same fp64 loop over the exact dequantised values, held to the
-bf16 rule.
+bf16 rule.  MXFP4 (``linear_mxfp4``): E2M1 codes, two per byte, with the
+same block scales.
 
 Epilogues (``oracle.c``), each applied with the pages' rounding points:
 
@@ -115,6 +116,12 @@ def _load():
             lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
             lib.oracle_linear_mxfp8.restype = ctypes.c_int
             lib.oracle_linear_mxfp8.argtypes = [
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_e2m1_value.restype = ctypes.c_double
+            lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+            lib.oracle_linear_mxfp4.restype = ctypes.c_int
+            lib.oracle_linear_mxfp4.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
             lib.oracle_rmsnorm_bf16.restype = ctypes.c_int
@@ -258,6 +265,31 @@ def linear_mxfp8(x_bits: np.ndarray, w_packed: np.ndarray, K: int):
                                      y.ctypes.data, S.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_linear_mxfp8 rejected its arguments")
+    return y, S
+
+
+def e2m1_value(code: int) -> float:
+    """Exact value of one E2M1 (FP4) code, low 4 bits (``oracle.c``)."""
+    return float(_load().oracle_e2m1_value(int(code) & 0xF))
+
+
+def linear_mxfp4(x_bits: np.ndarray, w_packed: np.ndarray, K: int):
+    """One projection with MXFP4 weights (``oracle.c``).  ``w_packed`` is
+    uint8 [N, K/2 + K/32]: per row the K/2 code bytes (element 2i in the
+    low nibble of byte i, 2i+1 in the high nibble), then the K/32 E8M0
+    scales.  Returns ``(y, S)`` as float64 [M, N]."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w_packed, dtype=np.uint8)
+    if x.ndim != 2 or w.ndim != 2 or K % 32 != 0 or w.shape[1] != K // 2 + K // 32:
+        raise ValueError("x must be [M, ldx] bf16, w [N, K/2 + K/32] uint8, K % 32 == 0")
+    M, ldx = x.shape
+    N = w.shape[0]
+    y = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    rc = _load().oracle_linear_mxfp4(M, N, K, ldx, x.ctypes.data, w.ctypes.data,
+                                     y.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_linear_mxfp4 rejected its arguments")
     return y, S
 
 

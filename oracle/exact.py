@@ -104,3 +104,35 @@ def linear_exact_mxfp8(x_rows, w_rows, K: int):
         y.append(yr)
         s.append(sr)
     return y, s
+
+
+def decode_e2m1(code: int) -> Fraction:
+    """E2M1 (FP4) from its definition: sign, 2 exponent bits (bias 1), 1
+    mantissa bit; exponent 0 is subnormal (m * 1/2); no NaN or infinity."""
+    code = int(code) & 0xF
+    sign = -1 if code >> 3 else 1
+    e = (code >> 1) & 3
+    m = code & 1
+    if e == 0:
+        return sign * Fraction(m, 2)
+    return sign * (1 + Fraction(m, 2)) * Fraction(2) ** (e - 1)
+
+
+def linear_exact_mxfp4(x_rows, w_rows, K: int):
+    """Packed MXFP4 rows (K/2 code bytes, low nibble first, then K/32
+    scales); exact (y, S) as Fractions."""
+    xs = [[decode(b, 7) for b in row[:K]] for row in x_rows]
+    ws = []
+    for row in w_rows:
+        sc = [decode_e8m0(b) for b in row[K // 2:K // 2 + K // 32]]
+        vals = []
+        for k in range(K):
+            byte = int(row[k // 2])
+            code = (byte >> 4) if k % 2 else (byte & 0xF)
+            vals.append(decode_e2m1(code) * sc[k // 32])
+        ws.append(vals)
+    y, s = [], []
+    for xr in xs:
+        y.append([sum((a * b for a, b in zip(xr, wr)), Fraction(0)) for wr in ws])
+        s.append([sum((abs(a * b) for a, b in zip(xr, wr)), Fraction(0)) for wr in ws])
+    return y, s

@@ -231,3 +231,45 @@ int oracle_linear_mxfp8(int64_t M, int64_t N, int64_t K, int64_t ldx, const uint
   }
   return 0;
 }
+
+/*
+ * MXFP4 weights: 4-bit E2M1 elements sharing one E8M0 scale per block of 32
+ * consecutive elements along K (the microscaling FP4 format; the pages'
+ * quantized variants of the fused weight are FP4 checkpoints: "Fuse QK
+ * down_proj with indexer K + weight_proj for FP4 ckpt", PR #8771).
+ *   E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0;
+ *         exponent 0: subnormal m * 0.5; otherwise (1 + m / 2) * 2^(e - 1);
+ *         no infinities or NaN (values 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ * Storage (this library's layout): a row is its K / 2 code bytes, element
+ * 2i in the low nibble of byte i and element 2i + 1 in the high nibble,
+ * followed by its K / 32 scales (K / 2 + K / 32 bytes per row).
+ */
+static double e2m1_value(uint8_t c) {
+  const int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = e == 0 ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, e - 1);
+  return s ? -v : v;
+}
+
+double oracle_e2m1_value(uint8_t c) { return e2m1_value(c & 0xF); }
+
+int oracle_linear_mxfp4(int64_t M, int64_t N, int64_t K, int64_t ldx, const uint16_t* x,
+                        const uint8_t* w, double* y, double* s) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || ldx < K) return -1;
+  const int64_t row = K / 2 + K / 32;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t r = 0; r < N; ++r) {
+      const uint8_t* q = w + r * row;
+      const uint8_t* sc = q + K / 2;
+      double acc = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const uint8_t code = (k & 1) ? (uint8_t)(q[k / 2] >> 4) : (uint8_t)(q[k / 2] & 0xF);
+        double p = bf16_bits_value(x[m * ldx + k]) * (e2m1_value(code) * e8m0_value(sc[k / 32]));
+        acc += p;
+        mag += fabs(p);
+      }
+      y[m * N + r] = acc;
+      s[m * N + r] = mag;
+    }
+  }
+  return 0;
+}

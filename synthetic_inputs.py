@@ -108,6 +108,30 @@ def draw_mxfp8_weights(K: int, N, g: torch.Generator, scale_lo: int = 112,
     return out
 
 
+def draw_mxfp4_weights(K: int, N, g: torch.Generator, scale_lo: int = 116,
+                       scale_hi: int = 121):
+    """One packed uint8 [N_i, K/2 + K/32] tensor per projection: code bytes
+    uniform over 0..255 (two E2M1 codes each, every code valid), scales
+    uniform in [scale_lo, scale_hi] (weights of the order of 1/sqrt(K))."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    out = []
+    for n in N:
+        codes = torch.randint(0, 256, (int(n), K // 2), generator=g, dtype=torch.int64)
+        scales = torch.randint(scale_lo, scale_hi + 1, (int(n), K // 32), generator=g,
+                               dtype=torch.int64)
+        out.append(torch.cat([codes, scales], dim=1).to(torch.uint8))
+    return out
+
+
+def mxfp4_case(M: int, seed: int, K: int = 5120, N=(1280, 512), ldx: int | None = None):
+    """Packed MXFP4 weights then bf16 x from one seeded generator."""
+    g = _gen(seed)
+    ws = draw_mxfp4_weights(K, N, g)
+    x = draw_x(M, K, "bf16", g, ldx=ldx)
+    return x, ws
+
+
 def mxfp8_case(M: int, seed: int, K: int = 5120, N=(1280, 512), ldx: int | None = None):
     """Packed MXFP8 weights then bf16 x from one seeded generator."""
     g = _gen(seed)

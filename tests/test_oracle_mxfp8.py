@@ -1,5 +1,6 @@
 """Pins of the oracle's MXFP8 projection (E4M3 codes, one E8M0 scale per 32
-elements along K, packed rows of K codes then K/32 scales).
+elements along K, packed rows of K codes then K/32 scales) and MXFP4
+projection (E2M1 codes, two per byte, low nibble first, same scales).
 
 The pages name MXFP8 projections for the DeepSeek-V4.1 wq_a / wkv weights
 ("tinygemm2 for the DeepSeek-V4.1 hidden-state projections", Description)
@@ -27,7 +28,7 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "e4m
 
 
 def _golden():
-    e4, e8 = [], []
+    e4, e8, e2 = [], [], []
     for line in open(GOLDEN):
         line = line.split("#", 1)[0].strip()
         if not line:
@@ -35,12 +36,14 @@ def _golden():
         kind, code, val = line.split()
         if kind == "e4m3":
             e4.append((int(code, 16), val))
+        elif kind == "e2m1":
+            e2.append((int(code, 16), val))
         else:
             e8.append((int(code), val))
-    return e4, e8
+    return e4, e8, e2
 
 
-E4, E8 = _golden()
+E4, E8, E2 = _golden()
 
 
 def _parse(val):
@@ -209,3 +212,72 @@ def test_planted_block_mistakes_fail_the_bf16_equivalence(mutation):
                     int(w[r, K + blk]))
             diff |= abs(float(acc) - yb[m, r]) > 1e-12 * (1 + abs(yb[m, r]))
     assert diff
+
+
+# ------------------------------------------------------------------- MXFP4
+@pytest.mark.parametrize("code,val", E2)
+def test_e2m1_golden(code, val):
+    want = _parse(val)
+    got = oracle.e2m1_value(code)
+    assert Fraction(got) == want == exact.decode_e2m1(code)
+    if val == "-0":
+        assert np.signbit(got)
+    # a byte holds two codes: the oracle reads only the nibble it is given
+    assert oracle.e2m1_value(code | 0xF0) == got
+
+
+def _dequant4_bf16(w_packed, K):
+    N = w_packed.shape[0]
+    out = np.zeros((N, K), dtype=np.uint16)
+    for r in range(N):
+        for k in range(K):
+            byte = int(w_packed[r, k // 2])
+            code = (byte >> 4) if k % 2 else (byte & 0xF)
+            v = exact.decode_e2m1(code) * exact.decode_e8m0(int(w_packed[r, K // 2 + k // 32]))
+            f = np.float32(float(v))
+            assert Fraction(float(f)) == v
+            out[r, k] = np.array([f], dtype=np.float32).view(np.uint32)[0] >> 16
+    return out
+
+
+def _case4(M, K, N, seed):
+    g = torch.Generator().manual_seed(seed)
+    (w,) = si.draw_mxfp4_weights(K, (N,), g)
+    x = si.draw_x(M, K, "bf16", g)
+    return si.bits(x), si.bits(w)
+
+
+@pytest.mark.parametrize("M,K,N,seed", [(1, 32, 3, 10), (3, 64, 5, 11), (2, 160, 4, 12)])
+def test_mxfp4_equals_bf16_projection_of_dequantised_weights(M, K, N, seed):
+    x, w = _case4(M, K, N, seed)
+    y, s = oracle.linear_mxfp4(x, w, K)
+    yb, sb = oracle.linear(x, _dequant4_bf16(w, K))
+    assert np.array_equal(y, yb) and np.array_equal(s, sb)
+
+
+def test_mxfp4_brute_force_rationals():
+    x, w = _case4(2, 64, 3, 13)
+    y, _ = oracle.linear_mxfp4(x, w, 64)
+    ye, se = exact.linear_exact_mxfp4(x.tolist(), w.tolist(), 64)
+    for m in range(2):
+        for r in range(3):
+            assert abs(Fraction(y[m, r]) - ye[m][r]) <= 64 * 2.0 ** -53 * float(se[m][r])
+
+
+def test_mxfp4_planted_nibble_swap_fails():
+    # reading the high nibble first must change the result
+    x, w = _case4(2, 64, 3, 14)
+    y, _ = oracle.linear_mxfp4(x, w, 64)
+    w2 = w.copy()
+    w2[:, :32] = ((w[:, :32] >> 4) | (w[:, :32] << 4)) & 0xFF
+    y2, _ = oracle.linear_mxfp4(x, w2, 64)
+    assert not np.array_equal(y, y2)
+    # and the bf16 equivalence pins the order: the swapped reading disagrees
+    yb, _ = oracle.linear(x, _dequant4_bf16(w, 64))
+    assert np.array_equal(y, yb) and not np.array_equal(y2, yb)
+
+
+def test_mxfp4_argument_checks():
+    x, w = _case4(1, 32, 2, 15)
+    with pytest.raises(ValueError):
+        oracle.linear_mxfp4(x, w[:, :16], 32)
