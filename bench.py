@@ -331,12 +331,13 @@ def router_cells(P, torch, dev, steps, Ms=(1, 4, 8, 16)):
     return res
 
 
-def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8)):
-    """The wq_a + wkv projection with MXFP8 weights (E4M3 codes, one E8M0
-    scale per 32 elements; packed rows of K + K/32 bytes), bf16 x and y, on
-    a pool of weight copies rotated past the MALL."""
+def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8), fmt="mxfp8"):
+    """The wq_a + wkv projection with MX weights, bf16 x and y, on a pool of
+    weight copies rotated past the MALL.  mxfp8: E4M3 codes, one E8M0 scale
+    per 32 elements, packed rows of K + K/32 bytes; mxfp4: E2M1 codes two per
+    byte, rows of K/2 + K/32 bytes."""
     import synthetic_inputs as si
-    row = K + K // 32
+    row = (K if fmt == "mxfp8" else K // 2) + K // 32
     wb = sum(N) * row
     n = max(2, math.ceil((1 << 30) / wb))
     g = torch.Generator(device="cuda")
@@ -345,11 +346,15 @@ def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8)):
     for _ in range(n):
         ws = []
         for nr in N:
-            codes = torch.randint(0, 254, (nr, K), generator=g, device="cuda")
-            codes = codes + (codes >= 0x7F).to(codes.dtype)
-            sc = torch.randint(112, 118, (nr, K // 32), generator=g, device="cuda")
+            if fmt == "mxfp8":
+                codes = torch.randint(0, 254, (nr, K), generator=g, device="cuda")
+                codes = codes + (codes >= 0x7F).to(codes.dtype)
+                sc = torch.randint(112, 118, (nr, K // 32), generator=g, device="cuda")
+            else:
+                codes = torch.randint(0, 256, (nr, K // 2), generator=g, device="cuda")
+                sc = torch.randint(116, 122, (nr, K // 32), generator=g, device="cuda")
             ws.append(torch.cat([codes, sc], 1).to(torch.uint8))
-        plans.append(P.FusedProjection(ws, max_M=8))
+        plans.append(P.FusedProjection(ws, max_M=8, weight_format=fmt))
         del ws
     res = {}
     for M in Ms:
@@ -365,8 +370,9 @@ def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8)):
         del gr
     for p in plans:
         p.close()
-    res["note"] = ("wq_a+wkv [1280,512]x5120 with MXFP8 weights (%d bytes per call), %d "
-                   "copies rotated (1 GiB), one call per copy, hipGraph replay" % (wb, n))
+    res["note"] = ("wq_a+wkv [1280,512]x5120 with %s weights (%d bytes per call), %d "
+                   "copies rotated (1 GiB), one call per copy, hipGraph replay"
+                   % (fmt.upper(), wb, n))
     return res
 
 
@@ -389,8 +395,8 @@ def main():
     ap.add_argument("--crossover", default="",
                     help="also time every kernel path per M in 1..128 and write the table here")
     ap.add_argument("--mxfp8-only", action="store_true",
-                    help="time only the MXFP8-weight cell and print it (profiler runs of "
-                         "that kernel); not the benchmark line")
+                    help="time only the MXFP8- and MXFP4-weight cells and print them "
+                         "(profiler runs of those kernels); not the benchmark line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -405,14 +411,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.mxfp8_only:
-        res = mxfp8_cells(P, torch, dev, args.steps)
+        res = {"mxfp8": mxfp8_cells(P, torch, dev, args.steps),
+               "mxfp4": mxfp8_cells(P, torch, dev, args.steps, fmt="mxfp4")}
         if args.calib_copy_mib:
             src = torch.ones((args.calib_copy_mib << 20) // 2, dtype=torch.bfloat16, device=dev)
             dst = torch.empty_like(src)
             for _ in range(3):
                 torch.neg(src, out=dst)
             torch.cuda.synchronize()
-        print(json.dumps({"mxfp8": res}), flush=True)
+        print(json.dumps(res), flush=True)
         return
     w_bytes = sum(N) * K * 2
     n_copies = max(2, math.ceil((args.pool_mib << 20) / w_bytes))
@@ -573,6 +580,7 @@ def main():
                                            max(3, args.steps // 4))
         line["router_f32"] = router_cells(P, torch, dev, max(3, args.steps // 4))
         line["mxfp8"] = mxfp8_cells(P, torch, dev, max(3, args.steps // 4))
+        line["mxfp4"] = mxfp8_cells(P, torch, dev, max(3, args.steps // 4), fmt="mxfp4")
     if args.crossover:
         crossover(args.crossover, P, torch, dev, plans, n_copies)
     print(json.dumps(line), flush=True)

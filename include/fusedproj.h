@@ -66,8 +66,13 @@ typedef struct fp_plan_s* fp_plan_t;
  * a multiple of 512).  Every weight element is decoded exactly (an E4M3
  * value times a power of two) for scaled values inside bf16's normal range;
  * NaN codes and scales (0x7F/0xFF, 255) and scales above 2^119 are outside
- * the served domain.  Served for 1 <= M <= 8 by the vector-ALU kernel. */
-typedef enum { FP_BF16 = 0, FP_F32 = 1, FP_MXFP8 = 2 } fp_dtype;
+ * the served domain.  Served for 1 <= M <= 8 by the vector-ALU kernel.
+ * FP_MXFP4: the same with E2M1 elements (sign, 2 exponent bits of bias 1,
+ * 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), the FP4 form of the fused
+ * weight named in PR #8771; two codes per byte, element 2i in the low
+ * nibble; a row is its K/2 code bytes, then its K/32 scales (K/2 + K/32
+ * bytes, K a multiple of 512). */
+typedef enum { FP_BF16 = 0, FP_F32 = 1, FP_MXFP8 = 2, FP_MXFP4 = 3 } fp_dtype;
 
 typedef enum {
   FP_OK = 0,
@@ -104,16 +109,17 @@ size_t fp_workspace_bytes(int32_t dtype, int64_t K, int32_t n_proj,
 
 /* Load-time half ("post_load_weights" of PR #20636, Description).
  * Records the projection layout and, on `stream`, copies each w_src[i]
- * (device, [N[i], K] contiguous row-major; FP_MXFP8: N[i] packed rows of
- * K + K/32 bytes) into rows off_i .. off_i+N[i]-1 of w_cat (device,
- * [sum N, K] row-major, or sum N packed rows for FP_MXFP8, 256-byte
+ * (device, [N[i], K] contiguous row-major; FP_MXFP8 / FP_MXFP4: N[i]
+ * packed rows of K + K/32 / K/2 + K/32 bytes) into rows off_i ..
+ * off_i+N[i]-1 of w_cat (device, [sum N, K] row-major, or sum N packed rows
+ * for the MX formats, 256-byte
  * aligned), where off_0 = 0 and off_{i+1} = off_i + N[i].  A NULL w_src (or
  * a NULL entry, or an entry equal to its destination) skips that copy: the
  * caller fills the rows itself, typically through the views fp_plan_view
  * returns.  The workspace (device, ws_bytes >= fp_workspace_bytes(...),
  * 256-byte aligned) has its counters cleared on `stream` by a fill kernel.
  * Requirements: 1 <= n_proj <= FP_MAX_PROJ, every N[i] >= 1, K >= 1 with
- * K * sizeof(element) a multiple of 16 (FP_MXFP8: K a multiple of 512),
+ * K * sizeof(element) a multiple of 16 (MX formats: K a multiple of 512),
  * 1 <= max_M <= FP_MAX_M.
  * On success *out receives the plan. */
 fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj,
@@ -147,6 +153,13 @@ fp_status fp_supported(fp_plan_t plan, int64_t M, const void* x, int64_t ldx);
 fp_status fp_mxfp8_to_bf16(const void* w, int64_t rows, int64_t K, void* out,
                            void* stream);
 
+/* Dequantise MXFP4 weight rows (K/2 code bytes, low nibble first, then K/32
+ * scales; 16-byte aligned) to dense [rows, K] bf16 (16-byte aligned, not
+ * overlapping w), with the decode the FP_MXFP4 projection uses.  K a
+ * multiple of 512. */
+fp_status fp_mxfp4_to_bf16(const void* w, int64_t rows, int64_t K, void* out,
+                           void* stream);
+
 /* The fused call: one launch computes every projection.
  * x: device, M rows with row stride ldx >= K elements (x[m, k] at
  *    x + m*ldx + k), 16-byte aligned rows.
@@ -172,7 +185,7 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx,
  * projection after its single rounding to bf16, as the unfused chain (one
  * projection launch per projection, then a second kernel) does, and both
  * give results bitwise equal to that chain (fp_forward_separate followed by
- * fp_rmsnorm / fp_swiglu on its outputs).  RMSNorm: bf16 and MXFP8 plans;
+ * fp_rmsnorm / fp_swiglu on its outputs).  RMSNorm: bf16 and MX plans;
  * SwiGLU: bf16 plans; other cases return FP_ERR_UNSUPPORTED with no launch.
  * --------------------------------------------------------------------- */
 

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfusedproj.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fusedproj.h")
 
-FP_BF16, FP_F32, FP_MXFP8 = 0, 1, 2
+FP_BF16, FP_F32, FP_MXFP8, FP_MXFP4 = 0, 1, 2, 3
 FP_OK, FP_ERR_INVALID_ARG, FP_ERR_UNSUPPORTED, FP_ERR_HIP, FP_ERR_WORKSPACE = range(5)
 FP_PATH_NONE, FP_PATH_SKINNY, FP_PATH_SKINNY_SPLITK, FP_PATH_MFMA, FP_PATH_MFMA_SMALL = range(5)
 FP_MAX_PROJ = 16
@@ -79,6 +79,7 @@ _SIGS = {
     "fp_forward": (_i32, [_p, _i64, _i64, _p, _p, _P_p]),
     "fp_forward_separate": (_i32, [_p, _i64, _i64, _p, _p, _P_p, _P_p]),
     "fp_mxfp8_to_bf16": (_i32, [_p, _i64, _i64, _p, _p]),
+    "fp_mxfp4_to_bf16": (_i32, [_p, _i64, _i64, _p, _p]),
     "fp_forward_rmsnorm": (_i32, [_p, _i64, _i64, _p, _p, _P_p, ctypes.c_float, _P_p]),
     "fp_forward_swiglu": (_i32, [_p, _i64, _i64, _p, _p, _p]),
     "fp_rmsnorm": (_i32, [_p, _i64, _i64, _p, ctypes.c_float, _p, _p]),
@@ -155,6 +156,10 @@ def fp_forward_separate(x: int, M: int, ldx: int, plan: int, stream: int, y,
 
 def fp_mxfp8_to_bf16(w: int, rows: int, K: int, out: int, stream: int) -> int:
     return _lib.fp_mxfp8_to_bf16(w, rows, K, out, stream)
+
+
+def fp_mxfp4_to_bf16(w: int, rows: int, K: int, out: int, stream: int) -> int:
+    return _lib.fp_mxfp4_to_bf16(w, rows, K, out, stream)
 
 
 def fp_forward_rmsnorm(x: int, M: int, ldx: int, plan: int, stream: int, gamma, eps: float,

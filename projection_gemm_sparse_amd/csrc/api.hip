@@ -97,11 +97,11 @@ bool dtype_geometry(int32_t dtype, int64_t K, int* esize, int64_t* wrow, int64_t
     *kc = K * es / 16;
     return true;
   }
-  if (dtype == FP_MXFP8) {
-    // units of 8 elements (8 code bytes), as the bf16 kernel's chunks
+  if (dtype == FP_MXFP8 || dtype == FP_MXFP4) {
+    // units of 8 elements (8 or 4 code bytes), as the bf16 kernel's chunks
     if (K % 512 != 0) return false;
     *esize = 2;
-    *wrow = K + K / 32;
+    *wrow = (dtype == FP_MXFP8 ? K : K / 2) + K / 32;
     *kc = K / 8;
     return true;
   }
@@ -109,7 +109,13 @@ bool dtype_geometry(int32_t dtype, int64_t K, int* esize, int64_t* wrow, int64_t
 }
 
 int skinny_var(const fp_plan_s* p) {
-  return p->dtype == FP_MXFP8 ? fp::kVarMx8 : fp::kVarPlain;
+  return p->dtype == FP_MXFP8 ? fp::kVarMx8 : p->dtype == FP_MXFP4 ? fp::kVarMx4 : fp::kVarPlain;
+}
+
+bool is_mx(int32_t dtype) { return dtype == FP_MXFP8 || dtype == FP_MXFP4; }
+
+bool dtype_known(int32_t dtype) {
+  return dtype == FP_BF16 || dtype == FP_F32 || dtype == FP_MXFP8 || dtype == FP_MXFP4;
 }
 
 std::mutex g_mu;
@@ -396,7 +402,7 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
          t.chunks == 10 || t.chunks == 12));
     if (!cj_ok) return false;
     if (t.groups < 1) return false;
-    if (p->dtype == FP_MXFP8 && t.chunks > 2) return false;
+    if (is_mx(p->dtype) && t.chunks > 2) return false;
     if ((int64_t)t.groups * t.kparts * 64 >
         fp::skinny_max_threads(t.mt, t.rows, t.chunks, skinny_var(p)))
       return false;
@@ -440,7 +446,7 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
       default_skinny_order(p->dtype, p->kc, p->n_total, skinny_mt(M), t);
     }
   }
-  if ((p->out_f32 || p->dtype == FP_MXFP8) && t->path != FP_PATH_SKINNY &&
+  if ((p->out_f32 || is_mx(p->dtype)) && t->path != FP_PATH_SKINNY &&
       t->path != FP_PATH_SKINNY_SPLITK)
     return false;
   if (t->path == FP_PATH_MFMA) {
@@ -577,37 +583,39 @@ const void* skinny_f32out_fn(int mt, int cj, int rw) {
   }
 }
 
-// MXFP8 weights: up to 8 tokens, one or two chunks per lane.
-template <int MT, int CJ>
-const void* skinny_mx8_fn_rw(int rw) {
+// MXFP8 / MXFP4 weights (VAR kVarMx8 / kVarMx4): up to 8 tokens, one or two
+// units per lane.
+template <int VAR, int MT, int CJ>
+const void* skinny_mx_fn_rw(int rw) {
   switch (rw) {
-    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, true, fp::kVarMx8>);
-    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, fp::kVarMx8>);
-    case 3: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 3, CJ, true, fp::kVarMx8>);
-    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, fp::kVarMx8>);
-    case 5: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 5, CJ, true, fp::kVarMx8>);
-    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, true, fp::kVarMx8>);
-    case 7: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 7, CJ, true, fp::kVarMx8>);
-    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, fp::kVarMx8>);
+    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, true, VAR>);
+    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, VAR>);
+    case 3: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 3, CJ, true, VAR>);
+    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, VAR>);
+    case 5: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 5, CJ, true, VAR>);
+    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, true, VAR>);
+    case 7: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 7, CJ, true, VAR>);
+    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, VAR>);
     default: return nullptr;
   }
 }
 
-template <int MT>
-const void* skinny_mx8_fn_cj(int cj, int rw) {
+template <int VAR, int MT>
+const void* skinny_mx_fn_cj(int cj, int rw) {
   switch (cj) {
-    case 1: return skinny_mx8_fn_rw<MT, 1>(rw);
-    case 2: return skinny_mx8_fn_rw<MT, 2>(rw);
+    case 1: return skinny_mx_fn_rw<VAR, MT, 1>(rw);
+    case 2: return skinny_mx_fn_rw<VAR, MT, 2>(rw);
     default: return nullptr;
   }
 }
 
-const void* skinny_mx8_fn(int mt, int cj, int rw) {
+template <int VAR>
+const void* skinny_mx_fn(int mt, int cj, int rw) {
   switch (mt) {
-    case 1: return skinny_mx8_fn_cj<1>(cj, rw);
-    case 2: return skinny_mx8_fn_cj<2>(cj, rw);
-    case 4: return skinny_mx8_fn_cj<4>(cj, rw);
-    case 8: return skinny_mx8_fn_cj<8>(cj, rw);
+    case 1: return skinny_mx_fn_cj<VAR, 1>(cj, rw);
+    case 2: return skinny_mx_fn_cj<VAR, 2>(cj, rw);
+    case 4: return skinny_mx_fn_cj<VAR, 4>(cj, rw);
+    case 8: return skinny_mx_fn_cj<VAR, 8>(cj, rw);
     default: return nullptr;
   }
 }
@@ -818,7 +826,8 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   const int64_t blocks = ceil_div(lr.n_rows, R) * t.splits;
   const void* fn = pairs ? skinny_pairs_fn(t.mt, t.chunks, t.rows)
                    : p->out_f32 ? skinny_f32out_fn(t.mt, t.chunks, t.rows)
-                   : p->dtype == FP_MXFP8 ? skinny_mx8_fn(t.mt, t.chunks, t.rows)
+                   : p->dtype == FP_MXFP8 ? skinny_mx_fn<fp::kVarMx8>(t.mt, t.chunks, t.rows)
+                   : p->dtype == FP_MXFP4 ? skinny_mx_fn<fp::kVarMx4>(t.mt, t.chunks, t.rows)
                    : p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
                                          : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
   return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
@@ -880,7 +889,7 @@ extern "C" {
 
 size_t fp_workspace_bytes(int32_t dtype, int64_t K, int32_t n_proj, const int64_t* N,
                           int64_t max_M) {
-  if ((dtype != FP_BF16 && dtype != FP_F32 && dtype != FP_MXFP8) || K < 1 || n_proj < 1 ||
+  if (!dtype_known(dtype) || K < 1 || n_proj < 1 ||
       n_proj > FP_MAX_PROJ || N == nullptr || max_M < 1 || max_M > FP_MAX_M)
     return 0;
   int esize = 0;
@@ -899,7 +908,7 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
                          size_t ws_bytes, int64_t max_M, void* stream, fp_plan_t* out) {
   if (out == nullptr) return FP_ERR_INVALID_ARG;
   *out = nullptr;
-  if (dtype != FP_BF16 && dtype != FP_F32 && dtype != FP_MXFP8) return FP_ERR_INVALID_ARG;
+  if (!dtype_known(dtype)) return FP_ERR_INVALID_ARG;
   if (K < 1 || n_proj < 1 || n_proj > FP_MAX_PROJ || N == nullptr) return FP_ERR_INVALID_ARG;
   if (max_M < 1 || max_M > FP_MAX_M) return FP_ERR_INVALID_ARG;
   if (w_cat == nullptr || workspace == nullptr) return FP_ERR_INVALID_ARG;
@@ -1116,7 +1125,7 @@ fp_status fp_forward_rmsnorm(const void* x, int64_t M, int64_t ldx, fp_plan_t pl
   if (s != FP_OK) return s;
   if (M == 0) return FP_OK;
   // bf16 outputs: bf16 and MXFP8 plans
-  if ((plan->dtype != FP_BF16 && plan->dtype != FP_MXFP8) || plan->out_f32)
+  if ((plan->dtype != FP_BF16 && !is_mx(plan->dtype)) || plan->out_f32)
     return FP_ERR_UNSUPPORTED;
   s = check_outputs(plan, M, x, ldx, out);
   if (s != FP_OK) return s;
@@ -1228,6 +1237,24 @@ fp_status fp_mxfp8_to_bf16(const void* w, int64_t rows, int64_t K, void* out, vo
                 0, args, static_cast<hipStream_t>(stream));
 }
 
+fp_status fp_mxfp4_to_bf16(const void* w, int64_t rows, int64_t K, void* out, void* stream) {
+  if (rows < 0 || K < 1) return FP_ERR_INVALID_ARG;
+  int esize = 0;
+  int64_t wrow = 0, kc = 0;
+  if (!dtype_geometry(FP_MXFP4, K, &esize, &wrow, &kc)) return FP_ERR_UNSUPPORTED;
+  if (rows == 0) return FP_OK;
+  if (w == nullptr || out == nullptr) return FP_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(out, 16)) return FP_ERR_UNSUPPORTED;
+  if (range_overlaps(w, rows * wrow, out, rows * K * 2)) return FP_ERR_INVALID_ARG;
+  const unsigned char* w_a = static_cast<const unsigned char*>(w);
+  unsigned char* o_a = static_cast<unsigned char*>(out);
+  int32_t kc_a = (int32_t)(K / 32);  // 16-byte chunks of 32 codes: one per block
+  int64_t n_a = rows * kc_a;
+  void* args[] = {&w_a, &o_a, &kc_a, &n_a};
+  return launch(reinterpret_cast<const void*>(&fp::mxfp4_to_bf16_kernel), ceil_div(n_a, 256), 256,
+                0, args, static_cast<hipStream_t>(stream));
+}
+
 fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path, int32_t* launches_fused,
                         int32_t* launches_separate) {
   if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
@@ -1263,7 +1290,7 @@ fp_status fp_plan_set_out_dtype(fp_plan_t plan, int32_t out_dtype) {
   if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
   if (out_dtype != FP_BF16 && out_dtype != FP_F32) return FP_ERR_INVALID_ARG;
   if (plan->dtype == FP_F32) return out_dtype == FP_F32 ? FP_OK : FP_ERR_UNSUPPORTED;
-  if (plan->dtype == FP_MXFP8) return out_dtype == FP_BF16 ? FP_OK : FP_ERR_UNSUPPORTED;
+  if (is_mx(plan->dtype)) return out_dtype == FP_BF16 ? FP_OK : FP_ERR_UNSUPPORTED;
   plan->out_f32 = out_dtype == FP_F32;
   plan->osize = plan->out_f32 ? 4 : 2;
   return FP_OK;
@@ -1323,7 +1350,7 @@ fp_status fp_plan_get_tiling(fp_plan_t plan, int64_t M, int64_t n_rows, fp_tilin
 
 fp_status fp_default_tiling(int32_t dtype, int64_t K, int64_t n_total, int64_t M,
                             int64_t n_rows, fp_tiling* out) {
-  if (out == nullptr || (dtype != FP_BF16 && dtype != FP_F32 && dtype != FP_MXFP8) || K < 1 ||
+  if (out == nullptr || !dtype_known(dtype) || K < 1 ||
       n_total < 1)
     return FP_ERR_INVALID_ARG;
   int esize = 0;

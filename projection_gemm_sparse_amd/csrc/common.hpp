@@ -49,6 +49,7 @@ constexpr int kVarPlain = 0;
 constexpr int kVarPairs = 1;
 constexpr int kVarF32Out = 2;
 constexpr int kVarMx8 = 3;
+constexpr int kVarMx4 = 4;
 
 // Gate/up launches (the PAIRS variant of the kernels): the launch's n_rows =
 // 2N logical rows interleave the two halves of the weight buffer -- logical
@@ -82,10 +83,10 @@ constexpr int max_threads_for_regs(int regs) {
   return 256 * waves_per_simd;
 }
 
-// MXFP8 weights (kVarMx8) hold 8-byte code units, a scale per unit and four
-// decoded pairs.
+// MXFP8 / MXFP4 weights (kVarMx8, kVarMx4) hold 8- or 4-byte code units, a
+// scale per unit and four decoded pairs.
 constexpr int skinny_max_threads(int mt, int rw, int cj, int var = kVarPlain) {
-  return var == kVarMx8
+  return var == kVarMx8 || var == kVarMx4
              ? max_threads_for_regs(pow2ceil(rw * mt) + 3 * rw * cj + 4 * mt * cj + 36)
              : max_threads_for_regs(pow2ceil(rw * mt) + 4 * rw * cj + 4 * mt * cj + 32);
 }
@@ -230,6 +231,15 @@ __device__ __forceinline__ float dot_chunk(const u32x4& w, const u32x4& x,
 __device__ __forceinline__ bf16x2 decode_e4m3_pair(unsigned u, float scale, bool hi) {
   return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, scale, true)
             : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, scale, false);
+}
+
+// Two E2M1 codes (the low and high nibble of byte `b` of `u`; the low nibble
+// is element 0) times an fp32 power-of-two scale, as a bf16 pair:
+// v_cvt_scalef32_pk_bf16_fp4.  Exact whenever the scaled value lies in
+// bf16's normal range (an E2M1 value has at most 2 significant bits).
+template <int B>
+__device__ __forceinline__ bf16x2 decode_e2m1_pair(unsigned u, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, scale, B);
 }
 
 // Dot product of 8 decoded weights (four bf16 pairs, element order) with

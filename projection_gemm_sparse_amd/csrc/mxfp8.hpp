@@ -1,4 +1,4 @@
-// mxfp8.hpp -- dequantisation of MXFP8 weight rows to bf16.
+// mxfp8.hpp -- dequantisation of MXFP8 and MXFP4 weight rows to bf16.
 //
 // The pages name MXFP8 projections for the DeepSeek-V4.1 wq_a / wkv weights
 // ("tinygemm2 for the DeepSeek-V4.1 hidden-state projections", TensorRT-LLM
@@ -40,6 +40,34 @@ mxfp8_to_bf16_kernel(const unsigned char* __restrict__ w, unsigned char* __restr
   u32x4* orow = reinterpret_cast<u32x4*>(out + ((uint64_t)row * kc * 16u + (uint64_t)c * 16u) * 2u);
   orow[0] = o0;
   orow[1] = o1;
+}
+
+// MXFP4 rows (K/2 code bytes, low nibble first, then K/32 scales): thread t
+// decodes code chunk t (16 bytes = 32 codes, one block) of row t / kc, kc =
+// K / 32, to 64 bytes of bf16.
+__global__ void __launch_bounds__(256)
+mxfp4_to_bf16_kernel(const unsigned char* __restrict__ w, unsigned char* __restrict__ out,
+                     int32_t kc, int64_t n_chunks) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_chunks) return;
+  const int64_t row = t / kc;
+  const int c = (int)(t - row * kc);
+  const uint64_t row_bytes = (uint64_t)kc * 16u + (uint32_t)kc;
+  const unsigned char* wrow = w + (uint64_t)row * row_bytes;
+  const u32x4 q = *reinterpret_cast<const u32x4*>(wrow + (uint64_t)c * 16u);
+  const uint32_t sb = wrow[(uint64_t)kc * 16u + (uint32_t)c];
+  const float sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
+  u32x4* orow = reinterpret_cast<u32x4*>(out + ((uint64_t)row * kc * 32u + (uint64_t)c * 32u) * 2u);
+  const unsigned qs[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 o;
+    o.x = __builtin_bit_cast(unsigned, decode_e2m1_pair<0>(qs[i], sc));
+    o.y = __builtin_bit_cast(unsigned, decode_e2m1_pair<1>(qs[i], sc));
+    o.z = __builtin_bit_cast(unsigned, decode_e2m1_pair<2>(qs[i], sc));
+    o.w = __builtin_bit_cast(unsigned, decode_e2m1_pair<3>(qs[i], sc));
+    orow[i] = o;
+  }
 }
 
 }  // namespace fp

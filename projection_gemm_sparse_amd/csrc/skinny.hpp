@@ -71,7 +71,11 @@ namespace fp {
 //               power of two has at most 4 significant bits) and multiplies
 //               them with the unit's activation chunk by v_dot2 in element
 //               order -- the bf16 kernel's arithmetic on half the weight
-//               bytes.
+//               bytes;
+//   kVarMx4     MXFP4 weights: the same with E2M1 codes, two per byte (the
+//               low nibble first): a unit is 4 code bytes, a row K/2 code
+//               bytes followed by its K/32 scales, and each code byte
+//               decodes to one bf16 pair (v_cvt_scalef32_pk_bf16_fp4).
 template <int MT, int RW, int CJ, bool BF16, int VAR = kVarPlain>
 __global__ void __launch_bounds__(skinny_max_threads(MT, RW, CJ, VAR))
 skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
@@ -84,6 +88,9 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   constexpr bool PAIRS = VAR == kVarPairs;
   constexpr bool OUT_BF16 = BF16 && VAR != kVarF32Out;
   constexpr bool MX8 = VAR == kVarMx8;
+  constexpr bool MX4 = VAR == kVarMx4;
+  constexpr bool MX = MX8 || MX4;
+  constexpr uint32_t UB = MX8 ? 8u : 4u;  // code bytes per 8-element unit
 
   extern __shared__ float smem[];   // [G][VP][16] wave sums, then one flag
   const int tid = threadIdx.x;
@@ -102,8 +109,8 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   const int row_base = rb * (Gv * RW);
   const int wrow0 = row_base + gq * RW;
   const int cbase = s * (P * 64 * CJ) + p * (64 * CJ) + lane;
-  // MXFP8: 8 code bytes per unit, then one scale byte per 4 units
-  const uint32_t row_bytes = MX8 ? (uint32_t)kc * 8u + ((uint32_t)kc >> 2) : (uint32_t)kc * 16u;
+  // MXFP8 / MXFP4: UB code bytes per unit, then one scale byte per 4 units
+  const uint32_t row_bytes = MX ? (uint32_t)kc * UB + ((uint32_t)kc >> 2) : (uint32_t)kc * 16u;
 
   // Loads are branch-free: an out-of-range chunk or row loads a clamped,
   // always-valid address, and out-of-range chunks are replaced by zero only
@@ -130,9 +137,10 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
     }
   }
   // 2. weight stream: every load of the lane issued up front, row by row
-  u32x4 wv[MX8 ? 1 : RW][CJ];
+  u32x4 wv[MX ? 1 : RW][CJ];
   u32x2 qv[MX8 ? RW : 1][CJ];     // MXFP8: the unit's 8 codes
-  uint32_t sv[MX8 ? RW : 1][CJ];  // MXFP8: its block's E8M0 scale
+  uint32_t q4[MX4 ? RW : 1][CJ];  // MXFP4: the unit's 8 codes (4 bytes)
+  uint32_t sv[MX ? RW : 1][CJ];   // MXFP8 / MXFP4: the block's E8M0 scale
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int lrow = wrow0 + r < n_rows ? wrow0 + r : n_rows - 1;
@@ -146,6 +154,19 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
         qv[r][j] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
       }
       const unsigned char* srow = wrow_b + (uint32_t)kc * 8u;
+#pragma unroll
+      for (int j = 0; j < CJ; ++j) {
+        const int c = cbase + j * 64;
+        sv[r][j] = srow[(c < kc ? c : kc - 1) >> 2];
+      }
+    } else if constexpr (MX4) {
+      const uint32_t* wrow = reinterpret_cast<const uint32_t*>(wrow_b);
+#pragma unroll
+      for (int j = 0; j < CJ; ++j) {
+        const int c = cbase + j * 64;
+        q4[r][j] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+      }
+      const unsigned char* srow = wrow_b + (uint32_t)kc * 4u;
 #pragma unroll
       for (int j = 0; j < CJ; ++j) {
         const int c = cbase + j * 64;
@@ -197,6 +218,16 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
         const unsigned q0 = q.x, q1 = q.y;
         const bf16x2 d[4] = {decode_e4m3_pair(q0, sc, false), decode_e4m3_pair(q0, sc, true),
                              decode_e4m3_pair(q1, sc, false), decode_e4m3_pair(q1, sc, true)};
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          v[r * MT + m] = dot_decoded(d, xv[m][j], v[r * MT + m]);
+        }
+      } else if constexpr (MX4) {
+        const unsigned q = c_ok[j] ? q4[r][j] : 0u;
+        const uint32_t sb = sv[r][j];
+        const float sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
+        const bf16x2 d[4] = {decode_e2m1_pair<0>(q, sc), decode_e2m1_pair<1>(q, sc),
+                             decode_e2m1_pair<2>(q, sc), decode_e2m1_pair<3>(q, sc)};
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           v[r * MT + m] = dot_decoded(d, xv[m][j], v[r * MT + m]);

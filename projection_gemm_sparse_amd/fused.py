@@ -34,12 +34,16 @@ class FusedProjection:
     ``copy_weights=True`` copies the given tensors into the concatenated
     buffer; the caller may then rebind its module weights to ``views``.
     MXFP8 weights are uint8 tensors of packed rows [N_i, K + K/32] (the K
-    E4M3 codes, then the K/32 E8M0 scales); activations and outputs are
-    then bf16.
+    E4M3 codes, then the K/32 E8M0 scales), MXFP4 weights packed rows
+    [N_i, K/2 + K/32] (two E2M1 codes per byte, low nibble first, then the
+    scales); ``weight_format`` ("mxfp8" or "mxfp4") names the format of
+    uint8 weights when their width does not tell it.  Activations and
+    outputs are then bf16.
     """
 
     def __init__(self, weights, max_M: int = 8, stream=None, copy_weights: bool = True,
-                 workspace_bytes: int | None = None, out_dtype=None):
+                 workspace_bytes: int | None = None, out_dtype=None,
+                 weight_format: str | None = None):
         if not weights:
             raise ValueError("at least one projection")
         w0 = weights[0]
@@ -51,11 +55,18 @@ class FusedProjection:
         self.w_dtype = w0.dtype
         if w0.dtype == torch.uint8:
             cols = int(w0.shape[1])
-            if cols % 33 != 0:
-                raise ValueError("packed MXFP8 rows hold K + K/32 bytes")
+            fits = {"mxfp8": cols % 33 == 0, "mxfp4": cols % 17 == 0}
+            fmt = weight_format
+            if fmt is None:
+                cand = [f for f, ok in fits.items() if ok]
+                if len(cand) != 1:
+                    raise ValueError("packed rows of %d bytes: pass weight_format" % cols)
+                fmt = cand[0]
+            if fmt not in fits or not fits[fmt]:
+                raise ValueError("packed %s rows cannot be %d bytes wide" % (fmt, cols))
             self.dtype = torch.bfloat16  # activations and outputs
-            self.fp_dtype = L.FP_MXFP8
-            self.K = cols // 33 * 32
+            self.fp_dtype = L.FP_MXFP8 if fmt == "mxfp8" else L.FP_MXFP4
+            self.K = cols // 33 * 32 if fmt == "mxfp8" else cols // 17 * 32
         else:
             self.dtype = w0.dtype
             self.fp_dtype = _DTYPES[w0.dtype]

@@ -31,7 +31,7 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("args", [
-    (3, 5120, [1280, 512], 8),      # bad dtype
+    (4, 5120, [1280, 512], 8),      # bad dtype
     (0, 0, [1280, 512], 8),         # K < 1
     (0, 5121, [1280, 512], 8),      # K*2 not a multiple of 16
     (1, 7170, [128], 8),            # K*4 not a multiple of 16
@@ -69,7 +69,7 @@ def _create(dtype=0, K=5120, N=(1280, 512), w_cat=FAKE, ws=FAKE, ws_bytes=None, 
 
 
 def test_plan_create_validation_before_any_hip_call():
-    assert _create(dtype=3)[0] == P.FP_ERR_INVALID_ARG
+    assert _create(dtype=4)[0] == P.FP_ERR_INVALID_ARG
     assert _create(K=-1)[0] == P.FP_ERR_INVALID_ARG
     assert _create(N=(0,))[0] == P.FP_ERR_INVALID_ARG
     assert _create(max_M=0)[0] == P.FP_ERR_INVALID_ARG
@@ -219,3 +219,13 @@ def test_mxfp8_geometry_checks():
     assert st == P.FP_OK and t[0] == P.FP_PATH_SKINNY and t[1] * 64 * t[2] >= 320
     st, _ = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 9, 1792)
     assert st == P.FP_ERR_UNSUPPORTED
+
+
+def test_mxfp4_geometry_checks():
+    assert P.fp_workspace_bytes(P.FP_MXFP4, 5120, [1280, 512], 8) > 0
+    assert P.fp_workspace_bytes(P.FP_MXFP4, 5136, [1280, 512], 8) == 0
+    assert P.fp_mxfp4_to_bf16(FAKE, 2, 528, FAKE + (1 << 24), 0) == P.FP_ERR_UNSUPPORTED
+    assert P.fp_mxfp4_to_bf16(FAKE, 0, 512, FAKE + (1 << 24), 0) == P.FP_OK
+    assert P.fp_mxfp4_to_bf16(FAKE, 4, 512, FAKE + 64, 0) == P.FP_ERR_INVALID_ARG  # overlap
+    st, t = P.fp_default_tiling(P.FP_MXFP4, 5120, 1792, 4, 1792)
+    assert st == P.FP_OK and t[0] == P.FP_PATH_SKINNY
