@@ -39,12 +39,21 @@ def _short(name: str) -> str:
     return re.sub(r"\(.*$", "", name).strip()
 
 
+def _open_csv(path):
+    if path.endswith(".gz"):
+        import gzip
+        return gzip.open(path, "rt")
+    return open(path)
+
+
 def load_pmc(dirs):
-    """{(kernel, grid): {counter: [values per dispatch]}}"""
+    """{(kernel, grid): {counter: [values per dispatch]}} from the
+    ``*counter_collection.csv`` (or ``.csv.gz``) files of the runs."""
     out = {}
     for d in dirs:
-        for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
-            with open(path) as fh:
+        for path in (glob.glob(os.path.join(d, "*counter_collection.csv")) +
+                     glob.glob(os.path.join(d, "*counter_collection.csv.gz"))):
+            with _open_csv(path) as fh:
                 for r in csv.DictReader(fh):
                     key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
                     out.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
