@@ -394,6 +394,10 @@ def main():
                     help="skip the fused RMSNorm / SwiGLU epilogue cells")
     ap.add_argument("--crossover", default="",
                     help="also time every kernel path per M in 1..128 and write the table here")
+    ap.add_argument("--mfma-only", action="store_true",
+                    help="time only the matrix-core cells (M = 8 on the small-M kernel, "
+                         "9..128 on the tile kernel) and print them (profiler runs of the "
+                         "MFMA counters); not the benchmark line")
     ap.add_argument("--mxfp8-only", action="store_true",
                     help="time only the MXFP8- and MXFP4-weight cells and print them "
                          "(profiler runs of those kernels); not the benchmark line")
@@ -410,6 +414,23 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mfma_only:
+        import synthetic_inputs as si2
+        w_bytes = sum(N) * K * 2
+        n_copies = max(2, math.ceil((args.pool_mib << 20) / w_bytes))
+        plans = build_pool(P, torch, n_copies, 128)
+        res = {}
+        for M in (8, 9, 16, 32, 64, 128):
+            x = si2.make_case(K, N, "bf16", M, seed=800 + M)[0].to(dev)
+            out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
+            gr = capture(torch, lambda: [p.forward(x, out=out) for p in plans])
+            t, _ = time_graphs(torch, [gr], args.steps, 1)
+            res[str(M)] = {"us": round(t * 1e3 / (args.steps * n_copies), 4),
+                           "tiling": list(plans[0].get_tiling(M)),
+                           "flops": 2 * M * sum(N) * K}
+            del gr
+        print(json.dumps({"mfma": res}), flush=True)
+        return
     if args.mxfp8_only:
         res = {"mxfp8": mxfp8_cells(P, torch, dev, args.steps),
                "mxfp4": mxfp8_cells(P, torch, dev, args.steps, fmt="mxfp4")}

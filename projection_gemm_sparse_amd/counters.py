@@ -4,6 +4,8 @@
         --calib-bytes B --out-md FILE.md --out-json profiles/traffic.json --command "..."
     python -m projection_gemm_sparse_amd.counters --trace DIR --trace-only \\
         --out-md FILE.md --command "..."
+    python -m projection_gemm_sparse_amd.counters --mfma --pmc DIR [--trace DIR] \\
+        --out-md FILE.md --command "..."
 
 Reads the CSV files rocprofv3 writes (``*_kernel_stats.csv`` of a
 ``--kernel-trace --stats`` run; ``*_counter_collection.csv`` of ``--pmc``
@@ -105,11 +107,67 @@ def trace_only(args):
     print("wrote", args.out_md)
 
 
+def mfma_summary(args):
+    """Matrix-core use per kernel from one --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 and
+    GRBM_GUI_ACTIVE (medians per dispatch) and the kernel trace's average
+    duration: busy fraction = busy SIMD-cycles / (SIMDs x duration x clock),
+    bf16 rate = MOPS x 512 flops / duration against the dense bf16 peak.
+    The profiler's own MfmaUtil divides by GRBM_GUI_ACTIVE instead, which
+    under counter collection covers the whole serialized dispatch and is
+    summed over the XCDs; it is listed as read."""
+    simds, ghz, peak = args.simds, args.clock_ghz, args.peak_tflops
+    pmc = load_pmc(args.pmc)
+    stats = {r["kernel"]: r for r in load_stats(args.trace)} if args.trace else {}
+    lines = ["# %s" % (args.title or "Matrix-core utilisation"), "",
+             "Commands (run from /tmp with TMPDIR=/tmp, repository root $R):", "", "```"]
+    lines += args.command + ["```", ""]
+    lines += ["Busy = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x trace duration x %.1f GHz); "
+              "rate = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops / trace duration, against "
+              "%.0f TFLOP/s dense bf16; cycles/MFMA = busy cycles / (MOPS / 32) "
+              "(one 16x16x32 bf16 MFMA = 32 MOPS); medians per dispatch; the profiler's "
+              "MfmaUtil (busy / (GRBM_GUI_ACTIVE x SIMDs)) as read."
+              % (simds, ghz, peak), ""]
+    lines += ["| kernel | grid | dispatches | avg ns (trace) | MFMA flops / dispatch | "
+              "bf16 TFLOP/s | % of peak | busy % | cycles / MFMA | MfmaUtil as read % |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    for (k, grid), c in sorted(pmc.items()):
+        if not (k.startswith("void fp::") or k.startswith("fp::")):
+            continue
+        busy = med(c.get("SQ_VALU_MFMA_BUSY_CYCLES", []))
+        mops = med(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", []))
+        act = med(c.get("GRBM_GUI_ACTIVE", []))
+        if busy is None or act is None or not mops:
+            continue
+        st = stats.get(k) or {}
+        ns = st.get("avg_ns")
+        flops = mops * 512
+        if ns:
+            rate = flops / ns / 1e3
+            cells = "%.0f | %.4g | %.1f | %.2f | %.2f | %.2f" % (
+                ns, flops, rate, 100.0 * rate / peak, 100.0 * busy / (simds * ns * ghz),
+                busy / (mops / 32))
+        else:
+            cells = " | %.4g | | | | %.2f" % (flops, busy / (mops / 32))
+        lines.append("| `%s` | %d | %d | %s | %.2f |" % (
+            k.replace("void ", ""), grid, len(c.get("GRBM_GUI_ACTIVE", [])), cells,
+            100.0 * busy / (act * simds)))
+    with open(args.out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("wrote", args.out_md)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--trace", required=True)
+    ap.add_argument("--trace", default="")
     ap.add_argument("--trace-only", action="store_true",
                     help="only summarise the kernel trace (no counters)")
+    ap.add_argument("--mfma", action="store_true",
+                    help="summarise one run of the MFMA counters (see mfma_summary)")
+    ap.add_argument("--simds", type=int, default=1024, help="SIMDs of the GPU (MI355X: 1024)")
+    ap.add_argument("--clock-ghz", type=float, default=2.4, help="engine clock (MI355X: 2.4)")
+    ap.add_argument("--peak-tflops", type=float, default=2500.0,
+                    help="dense bf16 matrix peak (MI355X: 2500)")
     ap.add_argument("--pmc", nargs="+", default=[])
     ap.add_argument("--calib-bytes", type=int, default=0,
                     help="bytes read (and written) by the calibration copy kernel")
@@ -122,6 +180,9 @@ def main():
     args = ap.parse_args()
     if args.trace_only:
         trace_only(args)
+        return
+    if args.mfma:
+        mfma_summary(args)
         return
     if not args.pmc or not args.calib_bytes or not args.out_json:
         raise SystemExit("--pmc, --calib-bytes and --out-json are needed with counters")
