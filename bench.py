@@ -92,7 +92,8 @@ def kernel_name(P, M: int, tiling) -> str:
         mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
         return "fp::skinny_kernel<%d, %d, %d, true, 0>" % (mt, rows, chunks)
     if path == P.FP_PATH_MFMA_SMALL:
-        return "fp::smfma_kernel<%d, false>" % chunks
+        return ("fp::smfma_kernel<%d, false>" % chunks if M <= 8
+                else "fp::smfma_kernel<%d, false, 2>" % chunks)
     mt16 = next(b for b in (1, 2, 4, 8, 16) if 16 * b >= M)
     cs = 4 if chunks in (8, 16) else 5
     return "fp::tile_kernel<%d, %d, %d, %d>" % (mt16, kparts, cs, chunks // cs)
@@ -182,20 +183,29 @@ def crossover(path, P, torch, dev, plans, n_copies):
     del plans
     torch.cuda.empty_cache()
     big = build_pool(P, torch, n_copies, 128)
+    n_total = sum(N)
+    tile_min = next(m for m in range(2, 257)
+                    if P.fp_default_tiling(0, K, n_total, m, n_total)[1][0] == P.FP_PATH_MFMA)
     rows = []
     for M in (1, 2, 4, 8, 9, 16, 32, 64, 128):
         xc, _ = si.make_case(K, N, "bf16", M, seed=200 + M)
         x = xc.to(dev)
         out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
         cands = [("default", None)]
+        kc = K * 2 // 16
+        steps = -(-kc // 8)
+        kt = 4 if steps <= 64 else 8 if steps <= 128 else 16
         if M <= 8:
-            kc = K * 2 // 16
-            steps = -(-kc // 8)
-            kt = 4 if steps <= 64 else 8 if steps <= 128 else 16
-            cands += [("skinny", (P.FP_PATH_SKINNY, 10, 1, 1, 0, 0)),
-                      ("mfma_small", (P.FP_PATH_MFMA_SMALL, -(-steps // kt), kt, 1, 0, 0))]
+            cands.append(("skinny", (P.FP_PATH_SKINNY, 10, 1, 1, 0, 0)))
+        if M <= 16:
+            cands.append(("mfma_small", (P.FP_PATH_MFMA_SMALL, -(-steps // kt), kt, 1, 0, 0)))
+        if 8 < M < tile_min:
+            cands.append(("tile", "tile"))
         for name, t in cands:
-            if t is not None and any(p.set_tiling(M, t) for p in big):
+            if t == "tile":
+                for p in big:
+                    p.set_mfma_min_m(M)
+            elif t is not None and any(p.set_tiling(M, t) for p in big):
                 for p in big:
                     p.set_tiling(M, None)
                 continue
@@ -210,6 +220,7 @@ def crossover(path, P, torch, dev, plans, n_copies):
             print("bench: crossover %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
             for p in big:
                 p.set_tiling(M, None)
+                p.set_mfma_min_m(tile_min)
             del g
     with open(path, "w") as fh:
         json.dump({"workload": "wq_a+wkv [1280,512]x5120 bf16, %d rotated copies" % n_copies,

@@ -92,7 +92,7 @@ typedef enum {
                               across workgroups and a fixed-order finish
                               inside the same launch */
   FP_PATH_MFMA = 3,        /* MFMA tile kernel (bf16, M above the crossover) */
-  FP_PATH_MFMA_SMALL = 4   /* matrix-core kernel for few tokens (bf16, M <= 8):
+  FP_PATH_MFMA_SMALL = 4   /* matrix-core kernel for few tokens (bf16, M <= 16):
                               8-row x 2-sub-slice tiles, one launch */
 } fp_path;
 
@@ -271,7 +271,7 @@ fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
  * chunks -- so fused and separate calls of one plan stay bitwise equal
  * under any tiling.
  *   path    FP_PATH_SKINNY / FP_PATH_SKINNY_SPLITK (same kernel; the
- *           splits field decides), FP_PATH_MFMA_SMALL (bf16, M <= 8) or
+ *           splits field decides), FP_PATH_MFMA_SMALL (bf16, M <= 16) or
  *           FP_PATH_MFMA (the tile kernel, bf16)
  *   kparts  skinny: waves splitting one K slice (P, <= 16); mfma-small:
  *           waves splitting K (PK, <= 16); mfma: 16-row tiles per

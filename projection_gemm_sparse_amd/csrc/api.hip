@@ -31,7 +31,11 @@ namespace {
 constexpr uint64_t kPlanMagic = 0x66757365'6470726full;  // "fusedpro"
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kSkinnyMaxM = 8;      // largest M the skinny kernel serves
-constexpr int kDefaultMfmaMinM = 9; // crossover (smallest M on the MFMA path)
+constexpr int kSmallMfmaMaxM = 16;  // largest M the small-M matrix-core kernel serves
+// Crossover to the tile kernel (smallest M on the MFMA tile path), measured
+// on MI355X at K = 5120, 1792 rows: the small-M matrix-core kernel with two
+// token halves serves M = 9..16 faster than the tile kernel.
+constexpr int kDefaultMfmaMinM = 17;
 // Smallest M the small-M matrix-core kernel serves by default (bf16); the
 // vector-ALU kernel runs below it.  Measured on MI355X at K = 5120, 1792
 // rows: the vector-ALU kernel is faster up to M = 4 (5.52 vs 5.87 us at
@@ -312,7 +316,8 @@ void resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs) {
   int64_t best_cost = INT64_MAX;
   for (int rt = pairs ? 2 : 1; rt <= 8; rt += pairs ? 2 : 1) {
     if (t->rows > 0 && rt != t->rows) continue;
-    const int g_cap = std::max(1, fp::smfma_max_threads(t->chunks) / (64 * t->kparts));
+    const int g_cap =
+        std::max(1, fp::smfma_max_threads(t->chunks, t->mt / 8) / (64 * t->kparts));
     for (int g = 1; g <= g_cap; ++g) {
       if (t->groups > 0 && g != t->groups) continue;
       const int64_t R = (int64_t)rt * g;
@@ -333,7 +338,7 @@ void resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs) {
 }
 
 size_t smfma_lds(const Tiling& t) {
-  return (size_t)t.groups * 2 * 64 * fp::kMaxWaveParts * 4;
+  return (size_t)t.groups * (t.mt / 8) * 2 * 64 * fp::kMaxWaveParts * 4;
 }
 
 size_t skinny_lds(const Tiling& t) {
@@ -387,10 +392,11 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     // buffer offsets are 32-bit
     if ((int64_t)t.splits * n_rows * 16 * t.mt * 4 >= ((int64_t)1 << 31)) return false;
   } else if (t.path == FP_PATH_MFMA_SMALL) {
-    if (p->dtype != FP_BF16 || M > kSkinnyMaxM) return false;
+    if (p->dtype != FP_BF16 || M > kSmallMfmaMaxM || t.mt < M) return false;
     if (!(t.chunks == 4 || t.chunks == 8 || t.chunks == 16)) return false;
     if (t.splits != 1 || t.kparts > fp::kMaxWaveParts || t.rows > 8 || t.groups < 1) return false;
-    if ((int64_t)t.groups * t.kparts * 64 > fp::smfma_max_threads(t.chunks)) return false;
+    if ((int64_t)t.groups * t.kparts * 64 > fp::smfma_max_threads(t.chunks, t.mt / 8))
+      return false;
     if ((int64_t)t.kparts * t.chunks * 8 < p->kc) return false;
     if (smfma_lds(t) > kMaxLds) return false;
   } else if (t.path == FP_PATH_SKINNY || t.path == FP_PATH_SKINNY_SPLITK) {
@@ -434,9 +440,10 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
   } else {
     // fp32-output plans run the vector-ALU kernel only
     const bool mfma = p->dtype == FP_BF16 && !p->out_f32 &&
-                      (M >= p->mfma_min_m || M > kSkinnyMaxM);
+                      (M >= p->mfma_min_m || M > kSmallMfmaMaxM);
     const bool small = p->dtype == FP_BF16 && !p->out_f32 && !mfma &&
-                       M >= p->small_mfma_min_m && default_smfma_order(p->kc, t);
+                       (M >= p->small_mfma_min_m || M > kSkinnyMaxM) &&
+                       default_smfma_order(p->kc, t);
     if (mfma) {
       if (!default_mfma_order(p->kc, M, p->n_total, t)) return false;
     } else if (small) {
@@ -454,7 +461,7 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
     if (t->splits < 1) return false;
     resolve_tile_launch(p, n_rows, t);
   } else if (t->path == FP_PATH_MFMA_SMALL) {
-    t->mt = 8;
+    t->mt = M > 8 ? 16 : 8;  // one or two token halves
     if (t->kparts < 1 || t->chunks < 1) return false;
     resolve_smfma_rows(n_rows, t, pairs);
   } else {
@@ -753,16 +760,18 @@ struct LaunchRows {
   int begin[fp::kMaxSeg + 1];
 };
 
-template <int KT, bool PAIRS>
-const void* smfma_fn_kt() {
-  return reinterpret_cast<const void*>(&fp::smfma_kernel<KT, PAIRS>);
+template <int KT>
+const void* smfma_fn_kt(bool pairs, int mt) {
+  if (mt == 16) return pairs ? nullptr : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 2>);
+  return pairs ? reinterpret_cast<const void*>(&fp::smfma_kernel<KT, true>)
+               : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false>);
 }
 
 const void* smfma_fn(const Tiling& t, bool pairs) {
   switch (t.chunks) {
-    case 4: return pairs ? smfma_fn_kt<4, true>() : smfma_fn_kt<4, false>();
-    case 8: return pairs ? smfma_fn_kt<8, true>() : smfma_fn_kt<8, false>();
-    case 16: return pairs ? smfma_fn_kt<16, true>() : smfma_fn_kt<16, false>();
+    case 4: return smfma_fn_kt<4>(pairs, t.mt);
+    case 8: return smfma_fn_kt<8>(pairs, t.mt);
+    case 16: return smfma_fn_kt<16>(pairs, t.mt);
     default: return nullptr;
   }
 }

@@ -1,4 +1,4 @@
-// smfma.hpp -- matrix-core kernel for y = x . W^T with few tokens (M <= 8),
+// smfma.hpp -- matrix-core kernel for y = x . W^T with few tokens (M <= 16),
 // bf16 in, fp32 accumulate, bf16 out.
 //
 // Why matrix cores at M <= 8.  The weight stream is the cost, but once the
@@ -31,6 +31,11 @@
 // quarter-wave on two rows (2 x 128 contiguous bytes) and a four-dword
 // lane shuffle (ds_bpermute) moves each chunk to its MFMA lane.
 //
+// Nine to sixteen tokens (MH = 2 token halves): every step multiplies the
+// same A operand with the B operands of tokens 0..7 and 8..15 (two MFMAs,
+// two accumulators); the weights are still loaded once.  Per token the
+// arithmetic, hence the result, is the same as with one half.
+//
 // Work split.  A workgroup owns G row groups of RT <= 8 rows (a tile with
 // RT < 8 leaves its last A rows unused; the 1792-row fused launch uses 7
 // rows per workgroup so that its 256 workgroups cover the 256 CUs once).
@@ -52,20 +57,22 @@
 
 namespace fp {
 
-constexpr int smfma_max_threads(int kt) {
-  return max_threads_for_regs(8 * kt + 24);
+constexpr int smfma_max_threads(int kt, int mh = 1) {
+  return max_threads_for_regs(4 * kt * (mh + 1) + 24 + 16 * (mh - 1));
 }
 
 // Leading scalars preloaded into SGPRs (see skinny_kernel for w, x, y0,
 // y1, ldx, n_rows, kc, M, split); geo = RT | PK << 8 | G << 16.
 // PAIRS: a gate/up launch (rows taken in pairs, see pair_row; RT even)
-// that writes silu(gate) * up instead of the projections.
-template <int KT, bool PAIRS = false>
-__global__ void __launch_bounds__(smfma_max_threads(KT))
+// that writes silu(gate) * up instead of the projections.  MH: token halves
+// (1: M <= 8, 2: M <= 16).
+template <int KT, bool PAIRS = false, int MH = 1>
+__global__ void __launch_bounds__(smfma_max_threads(KT, MH))
 smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
              unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
              int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
-  extern __shared__ float smem[];  // [G][2][8][8][16]
+  static_assert(MH == 1 || (MH == 2 && !PAIRS), "token halves");
+  extern __shared__ float smem[];  // [G][MH][2][8][8][16]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,14 +113,15 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   // 1. activations (token rl, clamped to a valid row; tokens past M are
   //    zeroed after the shuffle), then the weights (row rl of the tile,
   //    clamped to the launch): all loads issued before the first MFMA
-  u32x4 xv[KT];
-  {
-    const int mc = rl < M ? rl : M - 1;
+  u32x4 xv[MH][KT];
+#pragma unroll
+  for (int h = 0; h < MH; ++h) {
+    const int mc = rl + 8 * h < M ? rl + 8 * h : M - 1;
     const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       const int c = cw + 8 * t + cl;
-      xv[t] = xrow[c < kc ? c : kc - 1];
+      xv[h][t] = xrow[c < kc ? c : kc - 1];
     }
   }
   u32x4 wv[KT];
@@ -131,38 +139,60 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   __builtin_amdgcn_sched_barrier(0);
   const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
   __builtin_amdgcn_sched_barrier(0);
-  const bool tok_ok = r8 < M;
-
   // 2. MFMA steps in order; chunks past K contribute zero
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[MH];
+#pragma unroll
+  for (int h = 0; h < MH; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     __builtin_amdgcn_sched_barrier(0);
     const bool c_ok = c0 + 8 * t < kc;
     const u32x4 wa = shuffle(wv[t]);
-    const u32x4 xb = shuffle(xv[t]);
     const bf16x8 A = u4bf8(c_ok ? wa : zero4);
-    const bf16x8 B = u4bf8(c_ok && tok_ok ? xb : zero4);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+      const bool tok_ok = r8 + 8 * h < M;
+      const u32x4 xb = shuffle(xv[h][t]);
+      const bf16x8 B = u4bf8(c_ok && tok_ok ? xb : zero4);
+      acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[h], 0, 0, 0);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. the diagonal blocks to LDS: lane (i16, g) holds D[4g + v][i16]; the
   //    D row's sub-slice is (4g + v) / 8 = g / 2, the column's is i16 / 8.
-  //    Layout [G][sub-slice][row][token][16 wave slots]: the PK wave sums of
-  //    one (sub-slice, row, token) are contiguous.
+  //    Layout [G][half][sub-slice][row][token][16 wave slots]: the PK wave
+  //    sums of one (half, sub-slice, row, token) are contiguous.
   if ((g >> 1) == sub) {
-    float* red = smem + ((g2 * 2 + sub) * 64 + r8) * kMaxWaveParts + p;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = (4 * g + v) & 7;
-      red[r * 8 * kMaxWaveParts] = acc[v];
+    for (int h = 0; h < MH; ++h) {
+      float* red = smem + (((g2 * MH + h) * 2 + sub) * 64 + r8) * kMaxWaveParts + p;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = (4 * g + v) & 7;
+        red[r * 8 * kMaxWaveParts] = acc[h][v];
+      }
     }
   }
   __syncthreads();
 
   // 4. one thread per output: each sub-slice over the PK waves in wave
   //    order, then sub-slice 0 + sub-slice 1
+  if constexpr (MH == 2) {
+    const int n_out = Gv * 128;
+    for (int o = tid; o < n_out; o += Gv * PK * 64) {
+      const int gh = o >> 6;  // g2 * 2 + half
+      const int r = (o >> 3) & 7;
+      const int m = (gh & 1) * 8 + (o & 7);
+      const int row = row_base + (gh >> 1) * RT + r;
+      if (r < RT && m < M && row < n_rows) {
+        const float* q0 = smem + ((gh * 2 + 0) * 64 + (o & 63)) * kMaxWaveParts;
+        const float* q1 = smem + ((gh * 2 + 1) * 64 + (o & 63)) * kMaxWaveParts;
+        store_y<true>(om, a.out, row, m, sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK));
+      }
+    }
+    return;
+  }
   const int n_out = Gv * 64;
   if (tid < n_out) {
     const int gg = tid >> 6;

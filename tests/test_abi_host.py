@@ -147,11 +147,11 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
         if path == P.FP_PATH_MFMA:
             # kparts = row tiles per workgroup, chunks = compiled register
             # bound of k steps (4 pieces of 16 bytes) per slice
-            assert M >= 9 and kp in (2, 4, 8) and ch in (8, 10, 16, 20, 40)
+            assert M >= 17 and kp in (2, 4, 8) and ch in (8, 10, 16, 20, 40)
             n_steps = -(-kc // 4)
             assert -(-n_steps // S) <= ch
         elif path == P.FP_PATH_MFMA_SMALL:
-            assert dtype == 0 and 5 <= M <= 8
+            assert dtype == 0 and 5 <= M <= 16
             assert S == 1 and kp <= 16 and kp * ch * 8 >= kc
             assert 1 <= rows <= 8 and groups >= 1
         else:
@@ -167,14 +167,15 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
 
 def test_default_crossover():
     # bf16: vector-ALU kernel up to M = 4, small-M matrix-core kernel for
-    # M = 5..8, tile kernel above; fp32: vector-ALU kernel (M <= 8)
+    # M = 5..16 (one token half up to 8, two above), tile kernel above;
+    # fp32: vector-ALU kernel (M <= 8)
     for M in range(1, 5):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_SKINNY
-    for M in range(5, 9):
+    for M in range(5, 17):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA_SMALL
     for M in range(1, 9):
         assert P.fp_default_tiling(1, 7168, 192, M, 192)[1][0] in (1, 2)
-    for M in (9, 16, 32, 64, 128):
+    for M in (17, 32, 64, 128):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA
 
 

@@ -184,11 +184,15 @@ def test_tilings_all_pass(M):
     for t in tilings:
         st = fp.set_tiling(M, t)
         if st != P.FP_OK:
-            # skinny tilings above M = 8 and packed MFMA tiles above 16/Q
-            # tokens are refused
+            # skinny tilings above M = 8, tile tilings at M <= 8 and
+            # small-M MFMA workgroups above the register bound of two token
+            # halves are refused
             assert st == P.FP_ERR_UNSUPPORTED, (t, st)
-            assert ((t[0] != P.FP_PATH_MFMA and (M > 8 or (t[2] > 2 and M > 2)))
-                    or (t[0] == P.FP_PATH_MFMA and M <= 8)), (t, st)
+            assert ((t[0] in (P.FP_PATH_SKINNY, P.FP_PATH_SKINNY_SPLITK)
+                     and (M > 8 or (t[2] > 2 and M > 2)))
+                    or (t[0] == P.FP_PATH_MFMA and M <= 8)
+                    or (t[0] == P.FP_PATH_MFMA_SMALL and M > 8
+                        and max(1, t[5]) * t[1] * 64 > _smfma_thread_cap(t[2], 2))), (t, st)
             continue
         ran += 1
         ys = fp(xg)
@@ -254,6 +258,13 @@ def test_single_row_projections_and_one_projection():
 
 
 # ---- the small-M matrix-core kernel (opt-in tiling) on every workload shape
+def _smfma_thread_cap(kt, mh):
+    """Largest workgroup of the small-M matrix-core kernel: its register
+    estimate per lane, 4 waves per SIMD at most."""
+    regs = 4 * kt * (mh + 1) + 24 + 16 * (mh - 1)
+    return 256 * max(1, min(4, 512 // regs))
+
+
 def _small_mfma_tiling(K, esize=2):
     kc = K * esize // 16
     steps = -(-kc // 8)
@@ -262,7 +273,7 @@ def _small_mfma_tiling(K, esize=2):
 
 
 @pytest.mark.parametrize("case", ["wq_a+wkv", "fused_a_3way", "ragged", "single_rows", "k8"])
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 12, 16])
 def test_small_mfma_path(case, M):
     if case == "wq_a+wkv":
         x, ws = si.workload_case("wq_a+wkv_m2_8", M, 1)
@@ -274,7 +285,7 @@ def test_small_mfma_path(case, M):
         x, ws = si.make_case(1024, (1,) * 16, "bf16", M, seed=61 + M)
     else:
         x, ws = si.make_case(8, (300, 29), "bf16", M, seed=62 + M)
-    fp = _plan(ws)
+    fp = _plan(ws, max_M=16)
     assert fp.set_tiling(M, _small_mfma_tiling(fp.K)) == P.FP_OK
     assert fp.query(M)[0] == P.FP_PATH_MFMA_SMALL
     _check_case(fp, x, ws, "small-M MFMA %s M=%d" % (case, M))
@@ -287,6 +298,7 @@ def test_small_mfma_path(case, M):
 def test_tile_finish_in_launch_equals_second_launch(M):
     x, ws = si.workload_case("crossover", M, 6)
     fp = _plan(ws, max_M=128)
+    fp.set_mfma_min_m(9)  # the tile kernel also at M = 16
     xg = to_gpu(x)
     t = list(fp.get_tiling(M))
     assert t[0] == P.FP_PATH_MFMA and t[3] > 1 and t[5] in (1, 2)
