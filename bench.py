@@ -57,6 +57,7 @@ KERNEL_SOURCES = ("projection_gemm_sparse_amd/csrc/common.hpp",
                   "projection_gemm_sparse_amd/csrc/skinny.hpp",
                   "projection_gemm_sparse_amd/csrc/smfma.hpp",
                   "projection_gemm_sparse_amd/csrc/tile.hpp",
+                  "projection_gemm_sparse_amd/csrc/tile_ring.hpp",
                   "projection_gemm_sparse_amd/csrc/epilogue.hpp",
                   "projection_gemm_sparse_amd/csrc/mxfp8.hpp",
                   "projection_gemm_sparse_amd/csrc/api.hip")

@@ -91,7 +91,10 @@ typedef enum {
   FP_PATH_SKINNY_SPLITK = 2, /* same kernel with the K contraction split
                               across workgroups and a fixed-order finish
                               inside the same launch */
-  FP_PATH_MFMA = 3,        /* MFMA tile kernel (bf16, M above the crossover) */
+  FP_PATH_MFMA = 3,        /* MFMA tile kernels (bf16, M above the crossover):
+                              the tile kernel (whole K slice in LDS) up to
+                              32 tokens, the ring tile kernel (K slice
+                              streamed through a ring of LDS stages) from 33 */
   FP_PATH_MFMA_SMALL = 4   /* matrix-core kernel for few tokens (bf16, M <= 16):
                               8-row x 2-sub-slice tiles, one launch */
 } fp_path;
@@ -267,19 +270,24 @@ fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
  * the kernels accept gives results within the same error bound; the
  * summation order, hence the exact bits, depends on path and the order
  * fields (skinny: kparts, chunks, splits; mfma-small: kparts, chunks;
- * mfma: splits) -- never on rows, groups or the tile kernel's kparts and
- * chunks -- so fused and separate calls of one plan stay bitwise equal
- * under any tiling.
+ * mfma: splits) -- never on rows, groups or the tile kernels' kparts and
+ * chunks (the two tile kernels give the same bits for the same splits) --
+ * so fused and separate calls of one plan stay bitwise equal under any
+ * tiling.
  *   path    FP_PATH_SKINNY / FP_PATH_SKINNY_SPLITK (same kernel; the
  *           splits field decides), FP_PATH_MFMA_SMALL (bf16, M <= 16) or
- *           FP_PATH_MFMA (the tile kernel, bf16)
+ *           FP_PATH_MFMA (the tile kernels, bf16)
  *   kparts  skinny: waves splitting one K slice (P, <= 16); mfma-small:
  *           waves splitting K (PK, <= 16); mfma: 16-row tiles per
- *           workgroup (2, 4 or 8; 0 = chosen per launch)
+ *           workgroup (tile kernel: 2, 4 or 8, 0 = chosen per launch;
+ *           ring kernel: 4)
  *   chunks  skinny: 16-byte chunks per lane and row (CJ, 1..2);
  *           mfma-small: MFMA steps of 64 k per wave (KT: 4, 8, 16);
- *           mfma: compiled bound of 32-wide k steps per slice (8, 10, 16,
- *           20 or 40, at least ceil(ceil(K/32) / splits); 0 = smallest)
+ *           mfma: 3, 4 or 6 select the ring kernel with that many stage
+ *           buffers of 64 k (3 only for more than 128 tokens, 6 only up to
+ *           64); otherwise the tile kernel's compiled bound of 32-wide k
+ *           steps per slice (8, 10, 16, 20 or 40, at least
+ *           ceil(ceil(K/32) / splits); 0 = smallest)
  *   splits  K slices across workgroups (S >= 1), finished in-launch
  *           (mfma-small: 1)
  *   rows    skinny: rows per wave (RW, 1..8); mfma-small: rows per tile

@@ -23,6 +23,7 @@
 #include "skinny.hpp"
 #include "smfma.hpp"
 #include "tile.hpp"
+#include "tile_ring.hpp"
 #include "epilogue.hpp"
 #include "mxfp8.hpp"
 
@@ -179,6 +180,22 @@ void default_skinny_order(int32_t dtype, int64_t kc, int64_t n_total, int mt,
 constexpr int kTilePers[] = {8, 10, 16, 20, 40};  // compiled slice bounds (k steps)
 constexpr int kTileNws[] = {2, 4, 8};
 
+// Ring tile kernel: a tiling of the MFMA path whose chunks field is a ring
+// depth (stage buffers) selects it; kparts is then 4 (64-row blocks).
+constexpr int kRingStages[] = {3, 4, 6};
+bool is_ring(const Tiling& t) {
+  for (int st : kRingStages)
+    if (t.chunks == st) return true;
+  return false;
+}
+size_t ring_lds(int mt16, int stages) {
+  return (size_t)fp::ring_lds_bytes(16 * mt16, stages);
+}
+bool ring_fits(int mt16, int stages) {
+  const int J = fp::ring_stage_slots(16 * mt16) / 256;
+  return ring_lds(mt16, stages) <= kMaxLds && (stages - 2) * J <= 63;
+}
+
 int tile_per_bound(int64_t per) {
   for (int b : kTilePers)
     if (per <= b) return b;
@@ -220,9 +237,25 @@ int tile_pick_nw(int mt16, int64_t n_steps, int64_t S, int64_t n_rows) {
 }
 
 bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
-  (void)n_total;
   const int mt16 = mfma_mt16(M);
   const int64_t n_steps = ceil_div(kc, 4);
+  if (mt16 >= 4) {
+    // 33 tokens and more: the ring tile kernel, four stage buffers (three
+    // for 256-token blocks, the most LDS holds), one workgroup per CU over
+    // the plan's 64-row blocks, at least two stages per slice.  Measured on
+    // MI355X (K = 5120, 1792 rows, 9 slices, second-launch finish): 12.9 us
+    // at M = 64 and 16.8 at M = 128, against 19.7 / 22.0 for the tile
+    // kernel.  The choice depends on (K, M bucket, plan rows) only.
+    const int64_t blocks = ceil_div(n_total, fp::kRingRows);
+    int64_t S = std::max<int64_t>(1, kCus / blocks);
+    S = std::min<int64_t>(S, std::max<int64_t>(1, n_steps / 4));
+    S = std::min<int64_t>(S, 0x1fff);
+    t->path = FP_PATH_MFMA;
+    t->splits = (int)S;
+    t->kparts = 4;
+    t->chunks = mt16 >= 16 ? 3 : 4;
+    return true;
+  }
   // Measured on MI355X (K = 5120, 1792 rows): four row tiles per workgroup
   // (eight from 128 tokens), and the fewest slices whose slice fills a
   // compiled slice bound nearly (no wasted LDS rows) and fits in LDS.  The
@@ -354,6 +387,15 @@ size_t skinny_lds(const Tiling& t) {
 constexpr int64_t kSecondFinishBytes = 64 * 1024;
 
 void resolve_tile_launch(const fp_plan_s* p, int64_t n_rows, Tiling* t) {
+  if (is_ring(*t)) {
+    if (t->kparts <= 0) t->kparts = 4;
+    t->rows = 1;
+    if (t->groups <= 0) {
+      const int64_t block_bytes = (int64_t)t->splits * fp::kRingRows * 16 * t->mt * 4;
+      t->groups = t->splits > 1 && block_bytes > kSecondFinishBytes ? 2 : 1;
+    }
+    return;
+  }
   const int64_t n_steps = ceil_div(p->kc, 4);
   const int64_t per = ceil_div(n_steps, std::max(1, t->splits));
   if (t->kparts <= 0) t->kparts = tile_pick_nw(t->mt, n_steps, t->splits, n_rows);
@@ -378,7 +420,14 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
   if (t.splits < 1 || t.kparts < 1 || t.chunks < 1 || t.rows < 1) return false;
   // packed into 8- and 16-bit fields of the kernels' scalar arguments
   if (t.splits > 0x1fff || t.kparts > 0xff || t.rows > 0xff || t.groups > 0xff) return false;
-  if (t.path == FP_PATH_MFMA) {
+  if (t.path == FP_PATH_MFMA && is_ring(t)) {
+    if (p->dtype != FP_BF16 || t.kparts != 4 || !ring_fits(t.mt, t.chunks)) return false;
+    if (t.groups != 1 && t.groups != 2) return false;
+    if (16 * (int64_t)t.mt < M) return false;
+    // buffer offsets are 32-bit, with 0x80000000 reserved as out of range
+    if ((int64_t)t.splits * n_rows * 16 * t.mt * 4 >= ((int64_t)1 << 31)) return false;
+    if (n_rows * p->kc * 16 >= ((int64_t)1 << 31)) return false;
+  } else if (t.path == FP_PATH_MFMA) {
     if (p->dtype != FP_BF16) return false;
     const int64_t n_steps = ceil_div(p->kc, 4);
     const int64_t per = ceil_div(n_steps, t.splits);
@@ -707,7 +756,36 @@ const void* tile_fn_nw(int nw, int per) {
   }
 }
 
+template <int WR, int A, int WM, int B>
+const void* ring_fn_st(int stages) {
+  switch (stages) {
+    case 3: return reinterpret_cast<const void*>(&fp::ring_tile_kernel<WR, A, WM, B, 3>);
+    case 4:
+      if constexpr (B <= 4)
+        return reinterpret_cast<const void*>(&fp::ring_tile_kernel<WR, A, WM, B, 4>);
+      return nullptr;
+    case 6:
+      if constexpr (B <= 4)
+        return reinterpret_cast<const void*>(&fp::ring_tile_kernel<WR, A, WM, B, 6>);
+      return nullptr;
+    default: return nullptr;
+  }
+}
+
+// Wave grids of the ring kernel per token block (16 * mt16 slots).
+const void* ring_fn(const Tiling& t) {
+  switch (t.mt) {
+    case 1: return ring_fn_st<4, 1, 1, 1>(t.chunks);
+    case 2: return ring_fn_st<4, 1, 1, 2>(t.chunks);
+    case 4: return ring_fn_st<2, 2, 2, 2>(t.chunks);
+    case 8: return ring_fn_st<2, 2, 2, 4>(t.chunks);
+    case 16: return ring_fn_st<2, 2, 2, 8>(t.chunks);
+    default: return nullptr;
+  }
+}
+
 const void* mfma_fn(const Tiling& t) {
+  if (is_ring(t)) return ring_fn(t);
   switch (t.mt) {
     case 1: return tile_fn_nw<1>(t.kparts, t.chunks);
     case 2: return tile_fn_nw<2>(t.kparts, t.chunks);
@@ -815,11 +893,14 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   }
   if (pairs && t.path != FP_PATH_SKINNY) return FP_ERR_UNSUPPORTED;
   if (t.path == FP_PATH_MFMA) {
+    // the tile kernels address x with 32-bit buffer offsets
+    if ((M - 1) * (int64_t)ldx_a + p->kc * 16 >= ((int64_t)1 << 31)) return FP_ERR_UNSUPPORTED;
     const bool second = t.splits > 1 && t.groups == 2;
     geo_a = t.splits | (second ? fp::kGeoSecondFinish : 0);
     const int64_t per = ceil_div(ceil_div(p->kc, 4), t.splits);
     const int64_t blocks = ceil_div(lr.n_rows, 16 * (int64_t)t.kparts) * t.splits;
-    const size_t lds = std::max<size_t>(tile_lds(t.mt, per, t.kparts), 16);
+    const size_t lds = is_ring(t) ? ring_lds(t.mt, t.chunks)
+                                  : std::max<size_t>(tile_lds(t.mt, per, t.kparts), 16);
     fp_status st = launch(mfma_fn(t), blocks, t.kparts * 64, lds, args, stream);
     if (st != FP_OK || !second) return st;
     // the slices, added in slice order over the whole GPU

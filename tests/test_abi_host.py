@@ -144,10 +144,14 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
     for M in range(1, maxm + 1):
         st, (path, kp, ch, S, rows, groups) = P.fp_default_tiling(dtype, K, n_total, M, n_total)
         assert st == 0
-        if path == P.FP_PATH_MFMA:
+        if path == P.FP_PATH_MFMA and ch in (3, 4, 6):
+            # the ring tile kernel (33 tokens and more): 64-row blocks,
+            # chunks = stage buffers
+            assert M >= 33 and kp == 4 and (ch == 3) == (M > 128)
+        elif path == P.FP_PATH_MFMA:
             # kparts = row tiles per workgroup, chunks = compiled register
             # bound of k steps (4 pieces of 16 bytes) per slice
-            assert M >= 17 and kp in (2, 4, 8) and ch in (8, 10, 16, 20, 40)
+            assert 17 <= M <= 32 and kp in (2, 4, 8) and ch in (8, 10, 16, 20, 40)
             n_steps = -(-kc // 4)
             assert -(-n_steps // S) <= ch
         elif path == P.FP_PATH_MFMA_SMALL:

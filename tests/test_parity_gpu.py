@@ -311,3 +311,65 @@ def test_tile_finish_in_launch_equals_second_launch(M):
         assert fp.query(M)[1] == g
     assert_bitwise_equal(outs[1], outs[2], "in-launch vs second-launch finish")
     fp.set_tiling(M, None)
+
+
+# ---- the ring tile kernel (an MFMA tiling whose chunks field is a ring
+#      depth of 3, 4 or 6 stage buffers; 64-row blocks)
+def _ring(stages, S, finish=0):
+    return (P.FP_PATH_MFMA, 4, stages, S, 0, finish)
+
+
+@pytest.mark.parametrize("M", [17, 64, 128])
+@pytest.mark.parametrize("stages", [3, 4, 6])
+def test_ring_tile_full_shape(M, stages):
+    x, ws = si.workload_case("crossover", M, 11)
+    fp = _plan(ws, max_M=128, workspace_bytes=64 << 20)
+    xg = to_gpu(x)
+    rows = sorted({0, 1, M // 2, M - 1} | set(range(3, M, 29)))
+    ran = compared = 0
+    for S in (1, 9, 13):
+        for finish in (1, 2):
+            if S == 1 and finish == 2:
+                continue
+            st = fp.set_tiling(M, _ring(stages, S, finish))
+            if st != P.FP_OK:
+                # a ring of 6 stages of 256-token blocks does not fit in LDS
+                assert st == P.FP_ERR_UNSUPPORTED and stages == 6 and M > 64, (M, stages, S)
+                continue
+            ran += 1
+            label = "ring M=%d stages=%d S=%d finish=%d" % (M, stages, S, finish)
+            ys = _check_case(fp, x, ws, label, rows=rows)
+            # the tile kernel with the same slices adds in the same order
+            # (where a slice of its activations fits in LDS)
+            if fp.set_tiling(M, (P.FP_PATH_MFMA, 2, 0, S, 0, finish)) == P.FP_OK:
+                assert_bitwise_equal(ys, fp(xg), label + " vs tile kernel")
+                compared += 1
+    fp.set_tiling(M, None)
+    assert ran >= 1 or stages == 6
+    assert compared >= 1 or ran == 0
+
+
+@pytest.mark.parametrize("M", [2, 9, 16, 33, 100])
+def test_ring_tile_ragged(M):
+    K, N = 136, (37, 5, 70, 1)
+    x, ws = si.make_case(K, N, "bf16", M, seed=70 + M)
+    fp = _plan(ws, max_M=128, workspace_bytes=16 << 20)
+    for stages in (3, 4):
+        for S in (1, 2, 5):  # 5 slices of 17 steps' worth: some slices empty
+            assert fp.set_tiling(M, _ring(stages, S)) == P.FP_OK
+            _check_case(fp, x, ws, "ring ragged M=%d stages=%d S=%d" % (M, stages, S))
+    fp.set_tiling(M, None)
+
+
+def test_ring_tile_max_m_and_strided_x():
+    M, K = 256, 1024
+    x, ws = si.make_case(K, (300, 77), "bf16", M, seed=71, ldx=K + 64)
+    fp = _plan(ws, max_M=256, workspace_bytes=64 << 20)
+    rows = [0, 1, 100, 127, 128, 200, 254, 255]
+    for S in (1, 3):
+        for finish in (1, 2):
+            if S == 1 and finish == 2:
+                continue
+            assert fp.set_tiling(M, _ring(3, S, finish)) == P.FP_OK
+            _check_case(fp, x, ws, "ring M=256 S=%d finish=%d" % (S, finish), rows=rows)
+    fp.set_tiling(M, None)
