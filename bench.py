@@ -343,11 +343,12 @@ def router_cells(P, torch, dev, steps, Ms=(1, 4, 8, 16)):
     return res
 
 
-def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8), fmt="mxfp8"):
+def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8), fmt="mxfp8", variants=False):
     """The wq_a + wkv projection with MX weights, bf16 x and y, on a pool of
     weight copies rotated past the MALL.  mxfp8: E4M3 codes, one E8M0 scale
     per 32 elements, packed rows of K + K/32 bytes; mxfp4: E2M1 codes two per
-    byte, rows of K/2 + K/32 bytes."""
+    byte, rows of K/2 + K/32 bytes.  variants: also time the vector-ALU and
+    the small-M matrix-core kernels at every M (crossover runs)."""
     import synthetic_inputs as si
     row = (K if fmt == "mxfp8" else K // 2) + K // 32
     wb = sum(N) * row
@@ -380,6 +381,21 @@ def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8), fmt="mxfp8"):
                        "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
                        "tiling": list(plans[0].get_tiling(M))}
         del gr
+        if variants:
+            steps64 = K // 64
+            kt = 4 if steps64 <= 64 else 8 if steps64 <= 128 else 16
+            for name, t in (("skinny", (P.FP_PATH_SKINNY, 10, 1, 1, 0, 0)),
+                            ("mfma_small", (P.FP_PATH_MFMA_SMALL, -(-steps64 // kt), kt, 1, 0, 0))):
+                if any(p.set_tiling(M, t) for p in plans):
+                    for p in plans:
+                        p.set_tiling(M, None)
+                    continue
+                gr = capture(torch, lambda: [p.forward(x, out=out) for p in plans])
+                t2, _ = time_graphs(torch, [gr], steps, 2)
+                res[str(M)][name + "_us"] = round(t2 * 1e3 / (steps * n), 4)
+                del gr
+                for p in plans:
+                    p.set_tiling(M, None)
     for p in plans:
         p.close()
     res["note"] = ("wq_a+wkv [1280,512]x5120 with %s weights (%d bytes per call), %d "
@@ -410,6 +426,8 @@ def main():
                     help="time only the matrix-core cells (M = 8 on the small-M kernel, "
                          "9..128 on the tile kernel) and print them (profiler runs of the "
                          "MFMA counters); not the benchmark line")
+    ap.add_argument("--mx-variants", action="store_true",
+                    help="with --mxfp8-only: M = 1..8 and both MX kernels at every M")
     ap.add_argument("--mxfp8-only", action="store_true",
                     help="time only the MXFP8- and MXFP4-weight cells and print them "
                          "(profiler runs of those kernels); not the benchmark line")
@@ -444,8 +462,10 @@ def main():
         print(json.dumps({"mfma": res}), flush=True)
         return
     if args.mxfp8_only:
-        res = {"mxfp8": mxfp8_cells(P, torch, dev, args.steps),
-               "mxfp4": mxfp8_cells(P, torch, dev, args.steps, fmt="mxfp4")}
+        Ms = tuple(range(1, 9)) if args.mx_variants else (1, 2, 4, 8)
+        res = {"mxfp8": mxfp8_cells(P, torch, dev, args.steps, Ms=Ms, variants=args.mx_variants),
+               "mxfp4": mxfp8_cells(P, torch, dev, args.steps, Ms=Ms, fmt="mxfp4",
+                                    variants=args.mx_variants)}
         if args.calib_copy_mib:
             src = torch.ones((args.calib_copy_mib << 20) // 2, dtype=torch.bfloat16, device=dev)
             dst = torch.empty_like(src)

@@ -441,7 +441,8 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     // buffer offsets are 32-bit
     if ((int64_t)t.splits * n_rows * 16 * t.mt * 4 >= ((int64_t)1 << 31)) return false;
   } else if (t.path == FP_PATH_MFMA_SMALL) {
-    if (p->dtype != FP_BF16 || M > kSmallMfmaMaxM || t.mt < M) return false;
+    if (!(p->dtype == FP_BF16 || (is_mx(p->dtype) && M <= kSkinnyMaxM))) return false;
+    if (M > kSmallMfmaMaxM || t.mt < M) return false;
     if (!(t.chunks == 4 || t.chunks == 8 || t.chunks == 16)) return false;
     if (t.splits != 1 || t.kparts > fp::kMaxWaveParts || t.rows > 8 || t.groups < 1) return false;
     if ((int64_t)t.groups * t.kparts * 64 > fp::smfma_max_threads(t.chunks, t.mt / 8))
@@ -490,7 +491,9 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
     // fp32-output plans run the vector-ALU kernel only
     const bool mfma = p->dtype == FP_BF16 && !p->out_f32 &&
                       (M >= p->mfma_min_m || M > kSmallMfmaMaxM);
-    const bool small = p->dtype == FP_BF16 && !p->out_f32 && !mfma &&
+    // MX plans: the small-M kernel up to 8 tokens (bf16 up to 16)
+    const bool small = (p->dtype == FP_BF16 || (is_mx(p->dtype) && M <= kSkinnyMaxM)) &&
+                       !p->out_f32 && !mfma &&
                        (M >= p->small_mfma_min_m || M > kSkinnyMaxM) &&
                        default_smfma_order(p->kc, t);
     if (mfma) {
@@ -502,8 +505,9 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
       default_skinny_order(p->dtype, p->kc, p->n_total, skinny_mt(M), t);
     }
   }
-  if ((p->out_f32 || is_mx(p->dtype)) && t->path != FP_PATH_SKINNY &&
-      t->path != FP_PATH_SKINNY_SPLITK)
+  if (p->out_f32 && t->path != FP_PATH_SKINNY && t->path != FP_PATH_SKINNY_SPLITK) return false;
+  if (is_mx(p->dtype) && t->path != FP_PATH_SKINNY && t->path != FP_PATH_SKINNY_SPLITK &&
+      t->path != FP_PATH_MFMA_SMALL)
     return false;
   if (t->path == FP_PATH_MFMA) {
     t->mt = mfma_mt16(M);
@@ -845,7 +849,21 @@ const void* smfma_fn_kt(bool pairs, int mt) {
                : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false>);
 }
 
-const void* smfma_fn(const Tiling& t, bool pairs) {
+template <int FMT>
+const void* smfma_mx_fn(int kt) {
+  switch (kt) {
+    case 4: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<4, FMT>);
+    case 8: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<8, FMT>);
+    case 16: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<16, FMT>);
+    default: return nullptr;
+  }
+}
+
+const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype) {
+  if (dtype == FP_MXFP8 || dtype == FP_MXFP4) {
+    if (pairs || t.mt != 8) return nullptr;
+    return dtype == FP_MXFP8 ? smfma_mx_fn<8>(t.chunks) : smfma_mx_fn<4>(t.chunks);
+  }
   switch (t.chunks) {
     case 4: return smfma_fn_kt<4>(pairs, t.mt);
     case 8: return smfma_fn_kt<8>(pairs, t.mt);
@@ -888,7 +906,7 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   if (t.path == FP_PATH_MFMA_SMALL) {
     geo_a = t.rows | (t.kparts << 8) | (t.groups << 16);
     const int64_t R = (int64_t)t.rows * t.groups;
-    return launch(smfma_fn(t, pairs), ceil_div(lr.n_rows, R), t.groups * t.kparts * 64,
+    return launch(smfma_fn(t, pairs, p->dtype), ceil_div(lr.n_rows, R), t.groups * t.kparts * 64,
                   smfma_lds(t), args, stream);
   }
   if (pairs && t.path != FP_PATH_SKINNY) return FP_ERR_UNSUPPORTED;

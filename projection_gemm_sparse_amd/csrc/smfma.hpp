@@ -217,4 +217,172 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// MX weights (FMT 8: MXFP8, FMT 4: MXFP4; rows of K codes, then K/32 E8M0
+// scales), at most 8 tokens.  Tile, sub-slices, work split, reduction and
+// stores are those of smfma_kernel; the weights are decoded to bf16 in the
+// registers that feed the matrix unit, so the products and their sums are
+// those of bf16 weights equal to the decoded values.
+//
+// A 16-byte load of codes holds G units of 8 elements (G = 2 for MXFP8,
+// 4 for MXFP4).  So that one load serves one MFMA lane for G steps, the
+// k-slot mapping runs over groups of G steps: at step G u + e of a wave,
+// MFMA lane (i16 = r8 + 8 sub, g) carries unit
+//     c = cw + 8 G u + G (2 g + sub) + e
+// of weight row r8 (A) and token r8 (B).  Load lane L holds row L / 8,
+// units cw + 8 G u + G (L % 8) + 0 .. G - 1 -- a quarter-wave covers 2 rows
+// x 128 contiguous bytes of codes -- and MFMA lane (r8, sub, g) takes them
+// from load lane 8 r8 + 2 g + sub (four ds_bpermute per load).  The
+// activations use the same mapping (load lane L: token L / 8, the same G
+// units; G 16-byte loads).  A group's G units lie in one 32-element block
+// (K is a multiple of 512), whose scale the MFMA lane reads itself.
+template <int KT, int FMT>
+__global__ void __launch_bounds__(smfma_max_threads(KT))
+smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
+                unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
+                int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
+  static_assert(FMT == 8 || FMT == 4, "MXFP8 or MXFP4");
+  constexpr int G = FMT == 8 ? 2 : 4;      // steps per 16-byte load of codes
+  constexpr int NU = KT / G;               // code loads per lane
+  constexpr uint32_t UB = FMT == 8 ? 8u : 4u;  // code bytes per unit
+  static_assert(KT % G == 0, "whole step groups");
+  extern __shared__ float smem[];  // [G][2][8][8][16]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int RT = geo & 0xff;
+  const int PK = (geo >> 8) & 0xff;
+  const int Gv = geo >> 16;
+  const int p = Gv == 1 ? wave : wave % PK;
+  const int g2 = Gv == 1 ? 0 : wave / PK;
+  const int row_base = (int)blockIdx.x * (Gv * RT);
+  const int row0 = row_base + g2 * RT;
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const int sub = i16 >> 3;
+  const int r8 = i16 & 7;
+  const int cw = p * (8 * KT);                        // first unit of the wave
+  const int cg = cw + G * (2 * g + sub);              // this MFMA lane's unit at u = 0
+  const uint32_t row_bytes = (uint32_t)kc * UB + ((uint32_t)kc >> 2);
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  const int rl = lane >> 3;    // load lane: row / token
+  const int pl = lane & 7;     // load lane: unit group in the step group
+  const int src4 = (8 * r8 + 2 * g + sub) * 4;
+  auto shuffle = [&](const u32x4& v) {
+    u32x4 o;
+    o.x = (unsigned)__builtin_amdgcn_ds_bpermute(src4, (int)(unsigned)v.x);
+    o.y = (unsigned)__builtin_amdgcn_ds_bpermute(src4, (int)(unsigned)v.y);
+    o.z = (unsigned)__builtin_amdgcn_ds_bpermute(src4, (int)(unsigned)v.z);
+    o.w = (unsigned)__builtin_amdgcn_ds_bpermute(src4, (int)(unsigned)v.w);
+    return o;
+  };
+
+  // 1. activations (token rl clamped; tokens past M zeroed after the
+  //    shuffle), then the codes (row rl of the tile clamped to the launch),
+  //    then this MFMA lane's block scales: all loads before the first MFMA
+  u32x4 xv[NU][G];
+  {
+    const int mc = rl < M ? rl : M - 1;
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        const int c = cw + 8 * G * u + G * pl + e;
+        xv[u][e] = xrow[c < kc ? c : kc - 1];
+      }
+  }
+  u32x4 qv[NU];
+  {
+    const int rr = rl < RT ? row0 + rl : row0;
+    const int row = rr < n_rows ? rr : n_rows - 1;
+    const unsigned char* wrow = w + (uint64_t)(uint32_t)row * row_bytes;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c0 = cw + 8 * G * u + G * pl;   // first unit of the load
+      const int c = c0 < kc ? c0 : kc - G;
+      qv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (uint32_t)c * UB));
+    }
+  }
+  uint32_t sv[NU];
+  {
+    const int rr = r8 < RT ? row0 + r8 : row0;
+    const int row = rr < n_rows ? rr : n_rows - 1;
+    const unsigned char* srow = w + (uint64_t)(uint32_t)row * row_bytes + (uint32_t)kc * UB;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = cg + 8 * G * u;
+      sv[u] = srow[(c < kc ? c : kc - 1) >> 2];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
+  __builtin_amdgcn_sched_barrier(0);
+  const bool tok_ok = r8 < M;
+
+  // 2. step groups in order, steps in order inside a group; units past K
+  //    contribute zero
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    __builtin_amdgcn_sched_barrier(0);
+    const bool c_ok = cg + 8 * G * u < kc;
+    const u32x4 q = shuffle(qv[u]);
+    // scale 2^(s - 127) as an fp32 (s = 0: the subnormal 2^-127)
+    const uint32_t sb = sv[u];
+    const float sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      bf16x2 d[4];
+      if constexpr (FMT == 8) {
+        const unsigned q0 = e == 0 ? q.x : q.z;
+        const unsigned q1 = e == 0 ? q.y : q.w;
+        d[0] = decode_e4m3_pair(q0, sc, false);
+        d[1] = decode_e4m3_pair(q0, sc, true);
+        d[2] = decode_e4m3_pair(q1, sc, false);
+        d[3] = decode_e4m3_pair(q1, sc, true);
+      } else {
+        const unsigned qe = e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
+        d[0] = decode_e2m1_pair<0>(qe, sc);
+        d[1] = decode_e2m1_pair<1>(qe, sc);
+        d[2] = decode_e2m1_pair<2>(qe, sc);
+        d[3] = decode_e2m1_pair<3>(qe, sc);
+      }
+      const u32x4 wa = u32x4{__builtin_bit_cast(unsigned, d[0]), __builtin_bit_cast(unsigned, d[1]),
+                             __builtin_bit_cast(unsigned, d[2]), __builtin_bit_cast(unsigned, d[3])};
+      const u32x4 xb = shuffle(xv[u][e]);
+      const bf16x8 A = u4bf8(c_ok ? wa : zero4);
+      const bf16x8 B = u4bf8(c_ok && tok_ok ? xb : zero4);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. the diagonal blocks to LDS (as smfma_kernel)
+  if ((g >> 1) == sub) {
+    float* red = smem + ((g2 * 2 + sub) * 64 + r8) * kMaxWaveParts + p;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = (4 * g + v) & 7;
+      red[r * 8 * kMaxWaveParts] = acc[v];
+    }
+  }
+  __syncthreads();
+
+  // 4. one thread per output: each sub-slice over the PK waves in wave
+  //    order, then sub-slice 0 + sub-slice 1
+  const int n_out = Gv * 64;
+  if (tid < n_out) {
+    const int gg = tid >> 6;
+    const int r = (tid >> 3) & 7;
+    const int m = tid & 7;
+    const int row = row_base + gg * RT + r;
+    if (r < RT && m < M && row < n_rows) {
+      const float* q0 = smem + ((gg * 2 + 0) * 64 + r * 8 + m) * kMaxWaveParts;
+      const float* q1 = smem + ((gg * 2 + 1) * 64 + r * 8 + m) * kMaxWaveParts;
+      store_y<true>(om, a.out, row, m, sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK));
+    }
+  }
+}
+
 }  // namespace fp

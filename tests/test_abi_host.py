@@ -220,8 +220,12 @@ def test_mxfp8_geometry_checks():
     assert P.fp_mxfp8_to_bf16(FAKE, -1, 512, FAKE + (1 << 24), 0) == P.FP_ERR_INVALID_ARG
     assert P.fp_mxfp8_to_bf16(FAKE, 0, 512, FAKE + (1 << 24), 0) == P.FP_OK
     assert P.fp_mxfp8_to_bf16(FAKE, 4, 512, FAKE + 64, 0) == P.FP_ERR_INVALID_ARG  # overlap
-    st, t = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 8, 1792)
+    # vector-ALU kernel up to 4 tokens, the small-M matrix-core kernel for
+    # 5..8 (K = 5120: 80 MFMA steps of 64 k over 10 waves), nothing above 8
+    st, t = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 4, 1792)
     assert st == P.FP_OK and t[0] == P.FP_PATH_SKINNY and t[1] * 64 * t[2] >= 320
+    st, t = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 8, 1792)
+    assert st == P.FP_OK and t[0] == P.FP_PATH_MFMA_SMALL and t[1] * t[2] * 8 >= 640
     st, _ = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 9, 1792)
     assert st == P.FP_ERR_UNSUPPORTED
 

@@ -74,7 +74,7 @@ def test_decode_all_codes_bit_exact():
 def test_mxfp8_wq_a_wkv(M, seed):
     x, ws = si.mxfp8_case(M, seed)
     fp = _plan(ws)
-    assert fp.K == 5120 and fp.query(M)[0] == P.FP_PATH_SKINNY
+    assert fp.K == 5120 and fp.query(M)[0] in (P.FP_PATH_SKINNY, P.FP_PATH_MFMA_SMALL)
     xg = to_gpu(x)
     ys = fp(xg)
     _check(ys, x, ws, 5120, "mxfp8 M=%d seed=%d" % (M, seed))
