@@ -187,7 +187,7 @@ def crossover(path, P, torch, dev, plans, n_copies):
     tile_min = next(m for m in range(2, 257)
                     if P.fp_default_tiling(0, K, n_total, m, n_total)[1][0] == P.FP_PATH_MFMA)
     rows = []
-    for M in (1, 2, 4, 8, 9, 16, 32, 64, 128):
+    for M in (1, 2, 3, 4, 5, 8, 9, 16, 32, 64, 128):
         xc, _ = si.make_case(K, N, "bf16", M, seed=200 + M)
         x = xc.to(dev)
         out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]

@@ -37,13 +37,21 @@ constexpr int kSmallMfmaMaxM = 16;  // largest M the small-M matrix-core kernel 
 // on MI355X at K = 5120, 1792 rows: the small-M matrix-core kernel with two
 // token halves serves M = 9..16 faster than the tile kernel.
 constexpr int kDefaultMfmaMinM = 17;
-// Smallest M the small-M matrix-core kernel serves by default (bf16); the
+// Smallest M the small-M matrix-core kernel serves by default; the
 // vector-ALU kernel runs below it.  Measured on MI355X at K = 5120, 1792
-// rows: the vector-ALU kernel is faster up to M = 4 (5.52 vs 5.87 us at
-// M = 4), the matrix-core kernel from M = 5 (5.94 vs 6.53 us at M = 5, 6.12
-// vs 6.56 at M = 8), where the vector-ALU kernel's multiply-adds and
-// 64-value lane reduction start to show after the last weights land.
-constexpr int kDefaultSmallMfmaMinM = 5;
+// rows (bf16): the vector-ALU kernel is faster up to M = 2 (5.22 vs 5.41
+// us), the matrix-core kernel from M = 3 (5.41 vs 5.60 us at M = 3, 5.51 vs
+// 5.68 at M = 4, 5.89 vs 6.64 at M = 8), where the vector-ALU kernel's
+// multiply-adds and 64-value lane reduction start to show after the last
+// weights land.
+constexpr int kDefaultSmallMfmaMinM = 3;
+// MX weights: measured at the same shape, the vector-ALU kernel stays
+// faster through M = 4 (MXFP8 4.95 vs 5.36 us, MXFP4 4.37 vs 4.60).
+constexpr int kDefaultSmallMfmaMinMMx = 5;
+int default_small_mfma_min_m(int32_t dtype) {
+  return dtype == FP_MXFP8 || dtype == FP_MXFP4 ? kDefaultSmallMfmaMinMMx
+                                                : kDefaultSmallMfmaMinM;
+}
 constexpr int kCus = 256;           // MI355X compute units
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // rows and chunks per row, 32-bit indexing
 
@@ -547,7 +555,7 @@ void scratch_plan(fp_plan_s* tmp, int32_t dtype, int64_t K, int64_t n_total,
   tmp->n_total = n_total;
   tmp->max_M = max_M;
   tmp->mfma_min_m = kDefaultMfmaMinM;
-  tmp->small_mfma_min_m = kDefaultSmallMfmaMinM;
+  tmp->small_mfma_min_m = default_small_mfma_min_m(dtype);
   tmp->ws_bytes = SIZE_MAX;
 }
 
@@ -1056,7 +1064,7 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
   p->ws_bytes = ws_bytes;
   p->max_M = max_M;
   p->mfma_min_m = kDefaultMfmaMinM;
-  p->small_mfma_min_m = kDefaultSmallMfmaMinM;
+  p->small_mfma_min_m = default_small_mfma_min_m(dtype);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // concatenate: W_cat[off_i + r, :] = W_i[r, :]

@@ -111,29 +111,51 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   };
 
   // 1. activations (token rl, clamped to a valid row; tokens past M are
-  //    zeroed after the shuffle), then the weights (row rl of the tile,
-  //    clamped to the launch): all loads issued before the first MFMA
+  //    zeroed after the shuffle) and the weights (row rl of the tile,
+  //    clamped to the launch): all loads issued before the first MFMA.
+  //    Measured on MI355X at [1792, 5120]: with one token half, issuing each
+  //    step's activation and weight chunks in turn beats all activations
+  //    first (M = 8: 5.9 vs 6.15 us; M = 4: 5.5 vs 5.95); with two halves
+  //    the activations first stay faster (M = 16: 7.45 vs 7.7).
   u32x4 xv[MH][KT];
-#pragma unroll
-  for (int h = 0; h < MH; ++h) {
-    const int mc = rl + 8 * h < M ? rl + 8 * h : M - 1;
-    const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const int c = cw + 8 * t + cl;
-      xv[h][t] = xrow[c < kc ? c : kc - 1];
-    }
-  }
   u32x4 wv[KT];
   {
+    const u32x4* xrow[MH];
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+      const int mc = rl + 8 * h < M ? rl + 8 * h : M - 1;
+      xrow[h] = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
+    }
     const int rr = rl < RT ? row0 + rl : row0;
     const int lrow = rr < n_rows ? rr : n_rows - 1;
     const int row = PAIRS ? pair_row(lrow, split) : lrow;
     const u32x4* wrow = reinterpret_cast<const u32x4*>(w + (uint64_t)(uint32_t)row * row_bytes);
+    if constexpr (MH == 1) {
+      // one token half: the activation and weight chunks of each step in
+      // turn, so the weight stream starts with the first load
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const int c = cw + 8 * t + cl;
-      wv[t] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+      for (int t = 0; t < KT; ++t) {
+        const int c = cw + 8 * t + cl;
+        const int cc = c < kc ? c : kc - 1;
+        xv[0][t] = xrow[0][cc];
+        wv[t] = __builtin_nontemporal_load(wrow + cc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // two halves: every activation chunk first (twice the weight bytes,
+      // from L2), then the weights
+#pragma unroll
+      for (int h = 0; h < MH; ++h)
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          const int c = cw + 8 * t + cl;
+          xv[h][t] = xrow[h][c < kc ? c : kc - 1];
+        }
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const int c = cw + 8 * t + cl;
+        wv[t] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -280,39 +302,33 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
   // 1. activations (token rl clamped; tokens past M zeroed after the
   //    shuffle), then the codes (row rl of the tile clamped to the launch),
   //    then this MFMA lane's block scales: all loads before the first MFMA
+  //    Group by group: the codes (starting the weight stream with the
+  //    first load), the scale, then the group's activation chunks.
   u32x4 xv[NU][G];
+  u32x4 qv[NU];
+  uint32_t sv[NU];
   {
     const int mc = rl < M ? rl : M - 1;
     const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
-#pragma unroll
-    for (int u = 0; u < NU; ++u)
-#pragma unroll
-      for (int e = 0; e < G; ++e) {
-        const int c = cw + 8 * G * u + G * pl + e;
-        xv[u][e] = xrow[c < kc ? c : kc - 1];
-      }
-  }
-  u32x4 qv[NU];
-  {
     const int rr = rl < RT ? row0 + rl : row0;
     const int row = rr < n_rows ? rr : n_rows - 1;
     const unsigned char* wrow = w + (uint64_t)(uint32_t)row * row_bytes;
+    const int sr = r8 < RT ? row0 + r8 : row0;
+    const int srw = sr < n_rows ? sr : n_rows - 1;
+    const unsigned char* srow = w + (uint64_t)(uint32_t)srw * row_bytes + (uint32_t)kc * UB;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int c0 = cw + 8 * G * u + G * pl;   // first unit of the load
       const int c = c0 < kc ? c0 : kc - G;
       qv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (uint32_t)c * UB));
-    }
-  }
-  uint32_t sv[NU];
-  {
-    const int rr = r8 < RT ? row0 + r8 : row0;
-    const int row = rr < n_rows ? rr : n_rows - 1;
-    const unsigned char* srow = w + (uint64_t)(uint32_t)row * row_bytes + (uint32_t)kc * UB;
+      const int cs = cg + 8 * G * u;
+      sv[u] = srow[(cs < kc ? cs : kc - 1) >> 2];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int c = cg + 8 * G * u;
-      sv[u] = srow[(c < kc ? c : kc - 1) >> 2];
+      for (int e = 0; e < G; ++e) {
+        const int cx = c0 + e;
+        xv[u][e] = xrow[cx < kc ? cx : kc - 1];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);

@@ -155,7 +155,7 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
             n_steps = -(-kc // 4)
             assert -(-n_steps // S) <= ch
         elif path == P.FP_PATH_MFMA_SMALL:
-            assert dtype == 0 and 5 <= M <= 16
+            assert dtype == 0 and 3 <= M <= 16
             assert S == 1 and kp <= 16 and kp * ch * 8 >= kc
             assert 1 <= rows <= 8 and groups >= 1
         else:
@@ -170,12 +170,12 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
 
 
 def test_default_crossover():
-    # bf16: vector-ALU kernel up to M = 4, small-M matrix-core kernel for
-    # M = 5..16 (one token half up to 8, two above), tile kernel above;
+    # bf16: vector-ALU kernel up to M = 2, small-M matrix-core kernel for
+    # M = 3..16 (one token half up to 8, two above), tile kernels above;
     # fp32: vector-ALU kernel (M <= 8)
-    for M in range(1, 5):
+    for M in range(1, 3):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_SKINNY
-    for M in range(5, 17):
+    for M in range(3, 17):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA_SMALL
     for M in range(1, 9):
         assert P.fp_default_tiling(1, 7168, 192, M, 192)[1][0] in (1, 2)
