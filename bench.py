@@ -60,6 +60,7 @@ KERNEL_SOURCES = ("projection_gemm_sparse_amd/csrc/common.hpp",
                   "projection_gemm_sparse_amd/csrc/tile_ring.hpp",
                   "projection_gemm_sparse_amd/csrc/epilogue.hpp",
                   "projection_gemm_sparse_amd/csrc/mxfp8.hpp",
+                  "projection_gemm_sparse_amd/csrc/stream.hpp",
                   "projection_gemm_sparse_amd/csrc/api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -171,9 +172,154 @@ def cpu_baseline(plan0_weights_cpu, xs_cpu, budget_s=12.0):
             break
     byts = passes * sum(algorithmic_bytes(M, K, N) for M in MS)
     return {"value": byts / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host": host_info(),
             "sample": "%d pass(es) of the M=1..8 sweep over one [1792, 5120] bf16 "
                       "weight copy, %.1f s, single-threaded C fp64 loop" % (passes, el),
             "us_per_call": el / (passes * len(MS)) * 1e6}
+
+
+def stream_ceiling(P, torch, dev, plans, n_copies, steps):
+    """The read-only streaming ceiling on the same pool: fp_stream_read
+    over every copy's W_cat (the weight bytes, the fused call's launch
+    shape, nothing else), one call per copy, hipGraph replay."""
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    wb = plans[0].n_total * K * 2
+    ptrs = [p.views[0].data_ptr() for p in plans]
+
+    def calls():
+        h = torch.cuda.current_stream().cuda_stream
+        for ptr in ptrs:
+            st = P.fp_stream_read(ptr, wb, sink.data_ptr(), h)
+            if st != P.FP_OK:
+                raise RuntimeError("fp_stream_read: %d" % st)
+    g = capture(torch, calls)
+    t, _ = time_graphs(torch, [g], steps, 2)
+    us = t * 1e3 / (steps * n_copies)
+    return {"us_per_call": round(us, 4), "GBps": round(wb / us / 1e3, 1),
+            "frac_of_peak": round(wb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": wb,
+            "note": "fp_stream_read of each copy's W_cat (18,350,080 B) with the fused "
+                    "call's launch shape and no other work; same pool and protocol"}
+
+
+def trial_stats(torch, graphs, n_calls, trials=15, min_calls=2000):
+    """Per graph: median, p10 and p90 of the per-call time over `trials`
+    trials of R replays each (R * n_calls >= min_calls)."""
+    reps = max(1, -(-min_calls // n_calls))
+    out = []
+    for g in graphs:
+        vals = []
+        for _ in range(trials):
+            _, per = time_graphs(torch, [g], reps, 0)
+            vals.append(per[0] * 1e3 / (reps * n_calls))
+        vals.sort()
+        q = lambda f: vals[min(len(vals) - 1, max(0, round(f * (len(vals) - 1))))]
+        out.append({"median": round(q(0.5), 4), "p10": round(q(0.1), 4),
+                    "p90": round(q(0.9), 4)})
+    return out, reps
+
+
+def eager_us(torch, fn, n_calls, reps=3):
+    """Per-call time of eager (not captured) calls from Python: `fn` makes
+    n_calls calls; best of `reps` runs, bracketed by synchronisations."""
+    best = float("inf")
+    fn()
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        best = min(best, time.perf_counter() - t0)
+    return round(best * 1e6 / n_calls, 4)
+
+
+def workload_cells(P, torch, dev, steps, name):
+    """The other workloads of the projection on their own pools past the
+    MALL, fused and one launch per projection: the fp32 indexer fusion
+    (K = 7168, [128, 64], fp32 in and out, M = 1, 4, 8) and the three-way
+    fused-A shape (K = 6144, [2048, 576, 128], bf16, M = 1..8)."""
+    import synthetic_inputs as si
+    wl = si.WORKLOADS[name]
+    esize = 4 if wl.dtype == "f32" else 2
+    dt = torch.float32 if esize == 4 else torch.bfloat16
+    wb = sum(wl.N) * wl.K * esize
+    n = max(2, math.ceil((1 << 30) / wb))
+    Ms = (1, 4, 8) if esize == 4 else tuple(range(1, 9))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    plans = []
+    for _ in range(n):
+        if esize == 4:
+            ws = [(torch.randn(nr, wl.K, generator=g, device="cuda") * 0.02) for nr in wl.N]
+        else:
+            a = 1.0 / math.sqrt(wl.K)
+            ws = [((torch.rand(nr, wl.K, generator=g, device="cuda") * 2 - 1) * a).to(dt)
+                  for nr in wl.N]
+        plans.append(P.FusedProjection(ws, max_M=max(Ms)))
+        del ws
+    res = {}
+    for M in Ms:
+        x = si.make_case(wl.K, wl.N, wl.dtype, M, seed=700 + M)[0].to(dev)
+        out = [torch.empty(M, nr, dtype=dt, device=dev) for nr in wl.N]
+        gf = capture(torch, lambda: [p.forward(x, out=out) for p in plans])
+        gs = capture(torch, lambda: [p.forward_separate(x, out=out) for p in plans])
+        _, per = time_graphs(torch, [gf, gs], steps, 2)
+        uf = per[0] * 1e3 / (steps * n)
+        us_ = per[1] * 1e3 / (steps * n)
+        b = esize * (sum(wl.N) * wl.K + M * wl.K + M * sum(wl.N))
+        res[str(M)] = {"fused_us": round(uf, 4), "separate_us": round(us_, 4),
+                       "GBps": round(b / uf / 1e3, 1),
+                       "frac_of_peak": round(b / uf / 1e3 / HBM_PEAK_GBS, 4), "bytes": b,
+                       "path": P._lib.PATH_NAMES[plans[0].query(M)[0]],
+                       "tiling": list(plans[0].get_tiling(M))}
+        del gf, gs
+    for p in plans:
+        p.close()
+    res["note"] = ("%s: K=%d N=%s %s, %d copies rotated (>= 1 GiB), one call per copy, "
+                   "hipGraph replay" % (name, wl.K, list(wl.N), wl.dtype, n))
+    return res
+
+
+def pool_sweep(P, torch, dev, steps, Ms=(1, 8)):
+    """Per-call time of the fused call against the size of the rotated pool
+    (one copy, then 64 MiB .. 2 GiB): the time must level off once the pool
+    is well past the 256 MiB MALL."""
+    import synthetic_inputs as si
+    w_bytes = sum(N) * K * 2
+    rows = []
+    for mib in (0, 64, 128, 256, 512, 1024, 2048):
+        n = max(1, math.ceil((mib << 20) / w_bytes)) if mib else 1
+        plans = build_pool(P, torch, n, max(Ms))
+        for M in Ms:
+            x = si.make_case(K, N, "bf16", M, seed=100 + M)[0].to(dev)
+            out = [torch.empty(M, nn, dtype=torch.bfloat16, device=dev) for nn in N]
+            reps = max(1, 400 // n)
+            gr = capture(torch, lambda: [p.forward(x, out=out) for p in plans * reps])
+            t, _ = time_graphs(torch, [gr], steps, 2)
+            us = t * 1e3 / (steps * n * reps)
+            rows.append({"pool_MiB": round(n * w_bytes / 2**20, 1), "copies": n, "M": M,
+                         "us": round(us, 4),
+                         "GBps": round(algorithmic_bytes(M, K, N) / us / 1e3, 1)})
+            print("bench: pool sweep %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            del gr
+        for p in plans:
+            p.close()
+        del plans
+        torch.cuda.empty_cache()
+    return rows
+
+
+def host_info():
+    """CPU model name and logical CPU count of the host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
 
 
 def crossover(path, P, torch, dev, plans, n_copies):
@@ -425,6 +571,9 @@ def main():
                     help="time only the matrix-core cells (M = 8 on the small-M kernel, "
                          "9..128 on the tile kernel) and print them (profiler runs of the "
                          "MFMA counters); not the benchmark line")
+    ap.add_argument("--pool-sweep", default="",
+                    help="write a pool-size sweep (per-call time vs rotated pool size) to this "
+                         "JSON file and exit")
     ap.add_argument("--mx-variants", action="store_true",
                     help="with --mxfp8-only: M = 1..8 and both MX kernels at every M")
     ap.add_argument("--mxfp8-only", action="store_true",
@@ -459,6 +608,13 @@ def main():
                            "flops": 2 * M * sum(N) * K}
             del gr
         print(json.dumps({"mfma": res}), flush=True)
+        return
+    if args.pool_sweep:
+        rows = pool_sweep(P, torch, dev, max(3, args.steps // 4))
+        with open(args.pool_sweep, "w") as fh:
+            json.dump({"workload": "wq_a+wkv [1280,512]x5120 bf16 fused calls", "rows": rows},
+                      fh, indent=1)
+        print(json.dumps({"pool_sweep": rows}), flush=True)
         return
     if args.mxfp8_only:
         Ms = tuple(range(1, 9)) if args.mx_variants else (1, 2, 4, 8)
@@ -514,6 +670,10 @@ def main():
         sep_graphs = [capture(torch, separate_calls(M)) for M in MS]
         _, sep_ms = time_graphs(torch, sep_graphs, sep_steps, 1)
 
+    trials, trial_reps = trial_stats(torch, fused_graphs, n_copies)
+    eager = {str(M): eager_us(torch, fused_calls(M), n_copies) for M in (1, 8)}
+    ceiling = stream_ceiling(P, torch, dev, plans, n_copies, max(3, args.steps // 2))
+
     calls = args.steps * n_copies
     per_m = {}
     step_bytes = 0
@@ -532,6 +692,7 @@ def main():
             "path": P._lib.PATH_NAMES[plans[0].query(M)[0]],
             "tiling": list(tl),
             "kernel": kernel_name(P, M, tl),
+            "trials_us": trials[i],
         }
     ms_per_step = total_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -622,6 +783,15 @@ def main():
                                              floor_us * 1e-6 * n_copies * len(MS)) / 1e9, 1),
         },
         "roofline": roofline,
+        "stream_ceiling": dict(ceiling, fused_M1_over_ceiling=round(
+            per_m["1"]["fused_us"] / ceiling["us_per_call"], 4)),
+        "timing_protocol": {
+            "trials": "per M: 15 trials of %d graph replays (%d calls each); median, p10, "
+                      "p90 per call in per_m[M].trials_us; fused_us is the timed step "
+                      "region" % (trial_reps, trial_reps * n_copies),
+            "eager_us_per_call": eager,
+            "eager_note": "the same fused calls launched one by one from Python (ctypes), "
+                          "not captured; includes the Python call overhead"},
         "cpu_baseline": cpu,
         "per_m": per_m,
         "context": {"pages_sm107_fused_m1_us": 4.13,
@@ -633,6 +803,10 @@ def main():
         line["router_f32"] = router_cells(P, torch, dev, max(3, args.steps // 4))
         line["mxfp8"] = mxfp8_cells(P, torch, dev, max(3, args.steps // 4))
         line["mxfp4"] = mxfp8_cells(P, torch, dev, max(3, args.steps // 4), fmt="mxfp4")
+        line["indexer_f32"] = workload_cells(P, torch, dev, max(3, args.steps // 4),
+                                             "indexer_f32")
+        line["fused_a_3way"] = workload_cells(P, torch, dev, max(3, args.steps // 4),
+                                              "fused_a_3way")
     if args.crossover:
         crossover(args.crossover, P, torch, dev, plans, n_copies)
     print(json.dumps(line), flush=True)

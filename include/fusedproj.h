@@ -167,6 +167,20 @@ fp_status fp_mxfp8_to_bf16(const void* w, int64_t rows, int64_t K, void* out,
 fp_status fp_mxfp4_to_bf16(const void* w, int64_t rows, int64_t K, void* out,
                            void* stream);
 
+/* Measurement aid (no projection): read `bytes` of device memory at `buf`
+ * the way the fused call reads W_cat -- 256 workgroups of 640 threads,
+ * workgroup b reading the b-th contiguous 1/256 of the buffer with 16-byte
+ * non-temporal loads, all of a lane's loads issued before any is used --
+ * and do nothing else.  Its time per call is the read-only streaming
+ * ceiling of the projection kernels on the machine it runs on (the
+ * "weights rotated past L2" protocol of "tinygemm2 for the DeepSeek-V4.1
+ * hidden-state projections", Description).  buf 16-byte aligned, bytes a
+ * multiple of 16 below 2^31 (else FP_ERR_UNSUPPORTED); sink: device, 256
+ * words, not overlapping buf, written only in a case that never occurs
+ * for real data (it keeps the loads from being removed).  Asynchronous on
+ * `stream`. */
+fp_status fp_stream_read(const void* buf, int64_t bytes, void* sink, void* stream);
+
 /* The fused call: one launch computes every projection.
  * x: device, M rows with row stride ldx >= K elements (x[m, k] at
  *    x + m*ldx + k), 16-byte aligned rows.

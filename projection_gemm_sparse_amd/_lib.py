@@ -80,6 +80,7 @@ _SIGS = {
     "fp_forward_separate": (_i32, [_p, _i64, _i64, _p, _p, _P_p, _P_p]),
     "fp_mxfp8_to_bf16": (_i32, [_p, _i64, _i64, _p, _p]),
     "fp_mxfp4_to_bf16": (_i32, [_p, _i64, _i64, _p, _p]),
+    "fp_stream_read": (_i32, [_p, _i64, _p, _p]),
     "fp_forward_rmsnorm": (_i32, [_p, _i64, _i64, _p, _p, _P_p, ctypes.c_float, _P_p]),
     "fp_forward_swiglu": (_i32, [_p, _i64, _i64, _p, _p, _p]),
     "fp_rmsnorm": (_i32, [_p, _i64, _i64, _p, ctypes.c_float, _p, _p]),
@@ -160,6 +161,10 @@ def fp_mxfp8_to_bf16(w: int, rows: int, K: int, out: int, stream: int) -> int:
 
 def fp_mxfp4_to_bf16(w: int, rows: int, K: int, out: int, stream: int) -> int:
     return _lib.fp_mxfp4_to_bf16(w, rows, K, out, stream)
+
+
+def fp_stream_read(buf: int, nbytes: int, sink: int, stream: int) -> int:
+    return _lib.fp_stream_read(buf, nbytes, sink, stream)
 
 
 def fp_forward_rmsnorm(x: int, M: int, ldx: int, plan: int, stream: int, gamma, eps: float,

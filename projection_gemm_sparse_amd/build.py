@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfusedproj.so")
 SOURCES = [os.path.join(CSRC, "api.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("common.hpp", "skinny.hpp", "smfma.hpp", "tile.hpp",
-                                           "tile_ring.hpp", "epilogue.hpp", "mxfp8.hpp")] + [
+                                           "tile_ring.hpp", "epilogue.hpp", "mxfp8.hpp",
+                                           "stream.hpp")] + [
     os.path.join(ROOT, "include", "fusedproj.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -26,6 +26,7 @@
 #include "tile_ring.hpp"
 #include "epilogue.hpp"
 #include "mxfp8.hpp"
+#include "stream.hpp"
 
 namespace {
 
@@ -1351,6 +1352,22 @@ fp_status fp_mxfp8_to_bf16(const void* w, int64_t rows, int64_t K, void* out, vo
   void* args[] = {&w_a, &o_a, &kc_a, &n_a};
   return launch(reinterpret_cast<const void*>(&fp::mxfp8_to_bf16_kernel), ceil_div(n_a, 256), 256,
                 0, args, static_cast<hipStream_t>(stream));
+}
+
+fp_status fp_stream_read(const void* buf, int64_t bytes, void* sink, void* stream) {
+  if (bytes < 0) return FP_ERR_INVALID_ARG;
+  if (bytes == 0) return FP_OK;
+  if (buf == nullptr || sink == nullptr) return FP_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(sink, 4) || bytes % 16 != 0) return FP_ERR_UNSUPPORTED;
+  if (bytes >= ((int64_t)1 << 31)) return FP_ERR_UNSUPPORTED;
+  if (range_overlaps(buf, bytes, sink, 4 * fp::kStreamGroups)) return FP_ERR_INVALID_ARG;
+  const unsigned char* b_a = static_cast<const unsigned char*>(buf);
+  uint32_t bytes_a = (uint32_t)bytes;
+  uint32_t per_a = (uint32_t)ceil_div(bytes / 16, fp::kStreamGroups);
+  uint32_t* s_a = static_cast<uint32_t*>(sink);
+  void* args[] = {&b_a, &bytes_a, &per_a, &s_a};
+  return launch(reinterpret_cast<const void*>(&fp::stream_read_kernel), fp::kStreamGroups,
+                fp::kStreamThreads, 0, args, static_cast<hipStream_t>(stream));
 }
 
 fp_status fp_mxfp4_to_bf16(const void* w, int64_t rows, int64_t K, void* out, void* stream) {

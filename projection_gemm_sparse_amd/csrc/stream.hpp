@@ -1,0 +1,48 @@
+// stream.hpp -- a read-only streaming kernel: the ceiling the projection
+// kernels are measured against on the same machine.  It reads a buffer the
+// way the fused call reads W_cat -- 256 workgroups (one per CU) of 640
+// threads, workgroup b reading the b-th contiguous 1/256 of the buffer,
+// consecutive lanes on consecutive 16-byte vectors, non-temporal loads,
+// every load of a lane issued before any is used -- and does nothing else
+// (one word per workgroup is written only if the xor of the data hits a
+// fixed value, so the loads are not removed).
+#pragma once
+
+#include "tile.hpp"
+
+namespace fp {
+
+constexpr int kStreamThreads = 640;
+constexpr int kStreamGroups = 256;
+constexpr int kStreamBatch = 8;    // loads in flight per lane and batch
+
+__global__ void __launch_bounds__(kStreamThreads)
+stream_read_kernel(const unsigned char* __restrict__ buf, uint32_t bytes, uint32_t per_wg,
+                   uint32_t* __restrict__ sink) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(buf, bytes);
+  const uint32_t v0 = blockIdx.x * per_wg;          // first vector of the workgroup
+  const uint32_t v1 = v0 + per_wg;
+  const uint32_t n_vec = bytes >> 4;
+  const uint32_t end = v1 < n_vec ? v1 : n_vec;
+  // vector rounds of the workgroup (640 vectors each), the same for every
+  // lane: only the rounds that exist are issued
+  const uint32_t rounds = end > v0 ? (end - v0 + kStreamThreads - 1) / kStreamThreads : 0u;
+  unsigned acc = 0u;
+  for (uint32_t j0 = 0; j0 < rounds; j0 += kStreamBatch) {
+    u32x4 v[kStreamBatch];
+#pragma unroll
+    for (int j = 0; j < kStreamBatch; ++j) {
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (j0 + j < rounds) {
+        const uint32_t i = v0 + (j0 + j) * kStreamThreads + threadIdx.x;
+        const uint32_t off = i < end ? i * 16u : kOob;
+        v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNt));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kStreamBatch; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
+}  // namespace fp

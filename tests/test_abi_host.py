@@ -238,3 +238,14 @@ def test_mxfp4_geometry_checks():
     assert P.fp_mxfp4_to_bf16(FAKE, 4, 512, FAKE + 64, 0) == P.FP_ERR_INVALID_ARG  # overlap
     st, t = P.fp_default_tiling(P.FP_MXFP4, 5120, 1792, 4, 1792)
     assert st == P.FP_OK and t[0] == P.FP_PATH_SKINNY
+
+
+def test_stream_read_refusals_before_any_hip_call():
+    assert P.fp_stream_read(FAKE, 0, FAKE + (1 << 24), 0) == P.FP_OK  # nothing to read
+    assert P.fp_stream_read(FAKE, -16, FAKE + (1 << 24), 0) == P.FP_ERR_INVALID_ARG
+    assert P.fp_stream_read(0, 1024, FAKE + (1 << 24), 0) == P.FP_ERR_INVALID_ARG
+    assert P.fp_stream_read(FAKE, 1024, 0, 0) == P.FP_ERR_INVALID_ARG
+    assert P.fp_stream_read(FAKE + 8, 1024, FAKE + (1 << 24), 0) == P.FP_ERR_UNSUPPORTED
+    assert P.fp_stream_read(FAKE, 1000, FAKE + (1 << 24), 0) == P.FP_ERR_UNSUPPORTED
+    assert P.fp_stream_read(FAKE, 1 << 31, FAKE + (1 << 32), 0) == P.FP_ERR_UNSUPPORTED
+    assert P.fp_stream_read(FAKE, 4096, FAKE + 2048, 0) == P.FP_ERR_INVALID_ARG  # overlap
