@@ -35,7 +35,7 @@ def _capture(fp, x_static, outs):
 
 CASES = [("wq_a+wkv_m1", 1), ("wq_a+wkv_m2_8", 8), ("indexer_f32", 4),
          ("fused_a_3way", 1), ("fused_a_3way", 5), ("fused_a_3way", 8),
-         ("crossover", 32)]
+         ("crossover", 12), ("crossover", 32), ("crossover", 64), ("crossover", 128)]
 
 
 @pytest.mark.parametrize("name,M", CASES)
@@ -45,6 +45,9 @@ def test_replay_bitwise_equal_to_eager(name, M):
     x_static = to_gpu(x0)
     outs = [torch.empty(M, n, dtype=x_static.dtype, device="cuda") for n in fp.N]
     g = _capture(fp, x_static, outs)
+    # above 16 tokens the oracle checks sampled token rows (every element is
+    # still compared with the eager call)
+    rows = None if M <= 16 else sorted({0, 1, M // 2, M - 1} | set(range(5, M, 31)))
     for seed in (11, 12, 13):
         xn, _ = si.workload_case(name, M, seed)
         x_static.copy_(to_gpu(xn))
@@ -52,7 +55,7 @@ def test_replay_bitwise_equal_to_eager(name, M):
         torch.cuda.synchronize()
         eager = fp(x_static)  # eager call between replays
         assert_bitwise_equal(outs, eager, "%s M=%d replay seed %d" % (name, M, seed))
-        assert_matches_oracle(outs, xn, ws, label="%s replay" % name)
+        assert_matches_oracle(outs, xn, ws, rows=rows, label="%s replay" % name)
 
 
 @pytest.mark.parametrize("name,M", [("wq_a+wkv_m1", 1), ("indexer_f32", 8), ("crossover", 16)])

@@ -144,8 +144,9 @@ def test_mxfp8_graph_replay_equals_eager():
         _check(outs, xn, ws, 5120, "replay seed %d" % seed)
 
 
-def test_mxfp8_rmsnorm_epilogue():
-    M = 4
+@pytest.mark.parametrize("M", [4, 8])
+def test_mxfp8_rmsnorm_epilogue(M):
+    # M = 4: the vector-ALU kernel; M = 8: the small-M matrix-core kernel
     x, ws = si.mxfp8_case(M, 4)
     g = torch.Generator().manual_seed(4)
     gammas = [(1.0 + 0.1 * torch.randn(n, generator=g)).to(torch.bfloat16) for n in (1280, 512)]
