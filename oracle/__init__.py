@@ -124,6 +124,11 @@ def _load():
             lib.oracle_linear_mxfp4.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_linear_nvfp4.restype = ctypes.c_int
+            lib.oracle_linear_nvfp4.argtypes = [
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                ctypes.c_void_p]
             lib.oracle_rmsnorm_bf16.restype = ctypes.c_int
             lib.oracle_rmsnorm_bf16.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -290,6 +295,27 @@ def linear_mxfp4(x_bits: np.ndarray, w_packed: np.ndarray, K: int):
                                      y.ctypes.data, S.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_linear_mxfp4 rejected its arguments")
+    return y, S
+
+
+def linear_nvfp4(x_bits: np.ndarray, w_packed: np.ndarray, K: int, g: float):
+    """One projection with NVFP4 weights (``oracle.c``).  ``w_packed`` is
+    uint8 [N, K/2 + K/16]: per row the K/2 code bytes (element 2i in the
+    low nibble of byte i), then the K/16 E4M3 scales of its 16-element
+    blocks; ``g`` is the tensor's fp32 scale (taken as float32).  Returns
+    ``(y, S)`` as float64 [M, N]."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w_packed, dtype=np.uint8)
+    if x.ndim != 2 or w.ndim != 2 or K % 16 != 0 or w.shape[1] != K // 2 + K // 16:
+        raise ValueError("x must be [M, ldx] bf16, w [N, K/2 + K/16] uint8, K % 16 == 0")
+    M, ldx = x.shape
+    N = w.shape[0]
+    y = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    rc = _load().oracle_linear_nvfp4(M, N, K, ldx, x.ctypes.data, w.ctypes.data,
+                                     float(np.float32(g)), y.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_linear_nvfp4 rejected its arguments")
     return y, S
 
 

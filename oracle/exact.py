@@ -136,3 +136,25 @@ def linear_exact_mxfp4(x_rows, w_rows, K: int):
         y.append([sum((a * b for a, b in zip(xr, wr)), Fraction(0)) for wr in ws])
         s.append([sum((abs(a * b) for a, b in zip(xr, wr)), Fraction(0)) for wr in ws])
     return y, s
+
+
+def linear_exact_nvfp4(x_rows, w_rows, K: int, g):
+    """Packed NVFP4 rows (K/2 code bytes, low nibble first, then K/16 E4M3
+    block scales), tensor scale ``g`` (a Fraction or an exactly
+    representable float); exact (y, S) as Fractions."""
+    g = Fraction(g)
+    xs = [[decode(b, 7) for b in row[:K]] for row in x_rows]
+    ws = []
+    for row in w_rows:
+        sc = [decode_e4m3(b) for b in row[K // 2:K // 2 + K // 16]]
+        vals = []
+        for k in range(K):
+            byte = int(row[k // 2])
+            code = (byte >> 4) if k % 2 else (byte & 0xF)
+            vals.append(decode_e2m1(code) * sc[k // 16] * g)
+        ws.append(vals)
+    y, s = [], []
+    for xr in xs:
+        y.append([sum((a * b for a, b in zip(xr, wr)), Fraction(0)) for wr in ws])
+        s.append([sum((abs(a * b) for a, b in zip(xr, wr)), Fraction(0)) for wr in ws])
+    return y, s

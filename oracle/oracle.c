@@ -273,3 +273,42 @@ int oracle_linear_mxfp4(int64_t M, int64_t N, int64_t K, int64_t ldx, const uint
   }
   return 0;
 }
+
+/*
+ * NVFP4 weights: E2M1 elements (as above) with one E4M3 scale per block of
+ * 16 consecutive elements along K and one fp32 scale g per tensor:
+ *   w[r][k] = e2m1(q[r][k]) * e4m3(sc[r][k / 16]) * g
+ * The pages' FP4 fused weight is the NVFP4 checkpoint of "Fuse QK down_proj
+ * with indexer K + weight_proj for FP4 ckpt" (PR #8771, first titled as
+ * NVFP4 only) and of the GLM-5.2 NVFP4 target (PR #20502); they do not
+ * define the encoding, read as the public two-level NVFP4 format above.
+ * Storage (this library's layout): a row is its K / 2 code bytes (element
+ * 2i in the low nibble of byte i), then its K / 16 scale bytes (K / 2 +
+ * K / 16 bytes per row).
+ *   y[m][r] = sum_k X[m][k] * w[r][k],  S[m][r] = sum_k |X[m][k] * w[r][k]|
+ * Each product is exact in double (bf16 x E2M1 x E4M3 x fp32: at most
+ * 8 + 2 + 4 + 24 significant bits), sums in double in increasing k.  K a
+ * multiple of 16; g finite.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_linear_nvfp4(int64_t M, int64_t N, int64_t K, int64_t ldx, const uint16_t* x,
+                        const uint8_t* w, float g, double* y, double* s) {
+  if (M < 0 || N < 0 || K < 0 || K % 16 != 0 || ldx < K || !isfinite(g)) return -1;
+  const int64_t row = K / 2 + K / 16;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t r = 0; r < N; ++r) {
+      const uint8_t* q = w + r * row;
+      const uint8_t* sc = q + K / 2;
+      double acc = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const uint8_t code = (k & 1) ? (uint8_t)(q[k / 2] >> 4) : (uint8_t)(q[k / 2] & 0xF);
+        const double wv = e2m1_value(code) * e4m3_value(sc[k / 16]) * (double)g;
+        const double p = bf16_bits_value(x[m * ldx + k]) * wv;
+        acc += p;
+        mag += fabs(p);
+      }
+      y[m * N + r] = acc;
+      s[m * N + r] = mag;
+    }
+  }
+  return 0;
+}

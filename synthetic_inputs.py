@@ -124,6 +124,35 @@ def draw_mxfp4_weights(K: int, N, g: torch.Generator, scale_lo: int = 116,
     return out
 
 
+def draw_nvfp4_weights(K: int, N, g: torch.Generator, scale_lo: int = 0x28,
+                       scale_hi: int = 0x40):
+    """One packed uint8 [N_i, K/2 + K/16] tensor per projection (code bytes
+    uniform over 0..255, every E2M1 code valid; E4M3 block scales uniform
+    over the codes scale_lo..scale_hi, i.e. 0.25 .. 2), and one fp32 tensor
+    scale per projection, 2^-7 * (1 + u) with u uniform in [0, 1) rounded to
+    fp32 (not a power of two): weights of the order of 1/sqrt(K)."""
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    out, gs = [], []
+    for n in N:
+        codes = torch.randint(0, 256, (int(n), K // 2), generator=g, dtype=torch.int64)
+        scales = torch.randint(scale_lo, scale_hi + 1, (int(n), K // 16), generator=g,
+                               dtype=torch.int64)
+        out.append(torch.cat([codes, scales], dim=1).to(torch.uint8))
+        u = float(torch.rand((), generator=g, dtype=torch.float64))
+        gs.append(float(np.float32(2.0 ** -7 * (1.0 + u))))
+    return out, gs
+
+
+def nvfp4_case(M: int, seed: int, K: int = 5120, N=(1280, 512), ldx: int | None = None):
+    """Packed NVFP4 weights, their fp32 tensor scales, then bf16 x from one
+    seeded generator."""
+    g = _gen(seed)
+    ws, gs = draw_nvfp4_weights(K, N, g)
+    x = draw_x(M, K, "bf16", g, ldx=ldx)
+    return x, ws, gs
+
+
 def mxfp4_case(M: int, seed: int, K: int = 5120, N=(1280, 512), ldx: int | None = None):
     """Packed MXFP4 weights then bf16 x from one seeded generator."""
     g = _gen(seed)
