@@ -492,10 +492,12 @@ def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8), fmt="mxfp8", variants=Fal
     """The wq_a + wkv projection with MX weights, bf16 x and y, on a pool of
     weight copies rotated past the MALL.  mxfp8: E4M3 codes, one E8M0 scale
     per 32 elements, packed rows of K + K/32 bytes; mxfp4: E2M1 codes two per
-    byte, rows of K/2 + K/32 bytes.  variants: also time the vector-ALU and
-    the small-M matrix-core kernels at every M (crossover runs)."""
+    byte, rows of K/2 + K/32 bytes; nvfp4: E2M1 codes two per byte, one E4M3
+    scale per 16 elements and an fp32 tensor scale per projection, rows of
+    K/2 + K/16 bytes.  variants: also time the vector-ALU and the small-M
+    matrix-core kernels at every M (crossover runs)."""
     import synthetic_inputs as si
-    row = (K if fmt == "mxfp8" else K // 2) + K // 32
+    row = {"mxfp8": K + K // 32, "mxfp4": K // 2 + K // 32, "nvfp4": K // 2 + K // 16}[fmt]
     wb = sum(N) * row
     n = max(2, math.ceil((1 << 30) / wb))
     g = torch.Generator(device="cuda")
@@ -508,11 +510,15 @@ def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8), fmt="mxfp8", variants=Fal
                 codes = torch.randint(0, 254, (nr, K), generator=g, device="cuda")
                 codes = codes + (codes >= 0x7F).to(codes.dtype)
                 sc = torch.randint(112, 118, (nr, K // 32), generator=g, device="cuda")
-            else:
+            elif fmt == "mxfp4":
                 codes = torch.randint(0, 256, (nr, K // 2), generator=g, device="cuda")
                 sc = torch.randint(116, 122, (nr, K // 32), generator=g, device="cuda")
+            else:
+                codes = torch.randint(0, 256, (nr, K // 2), generator=g, device="cuda")
+                sc = torch.randint(0x28, 0x41, (nr, K // 16), generator=g, device="cuda")
             ws.append(torch.cat([codes, sc], 1).to(torch.uint8))
-        plans.append(P.FusedProjection(ws, max_M=8, weight_format=fmt))
+        ts = [0.0087890625, 0.0107421875] if fmt == "nvfp4" else None
+        plans.append(P.FusedProjection(ws, max_M=8, weight_format=fmt, tensor_scales=ts))
         del ws
     res = {}
     for M in Ms:
@@ -546,6 +552,8 @@ def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8), fmt="mxfp8", variants=Fal
     res["note"] = ("wq_a+wkv [1280,512]x5120 with %s weights (%d bytes per call), %d "
                    "copies rotated (1 GiB), one call per copy, hipGraph replay"
                    % (fmt.upper(), wb, n))
+    if fmt == "nvfp4":
+        res["note"] += "; fp32 tensor scales %s" % ts
     return res
 
 
@@ -620,6 +628,8 @@ def main():
         Ms = tuple(range(1, 9)) if args.mx_variants else (1, 2, 4, 8)
         res = {"mxfp8": mxfp8_cells(P, torch, dev, args.steps, Ms=Ms, variants=args.mx_variants),
                "mxfp4": mxfp8_cells(P, torch, dev, args.steps, Ms=Ms, fmt="mxfp4",
+                                    variants=args.mx_variants),
+               "nvfp4": mxfp8_cells(P, torch, dev, args.steps, Ms=Ms, fmt="nvfp4",
                                     variants=args.mx_variants)}
         if args.calib_copy_mib:
             src = torch.ones((args.calib_copy_mib << 20) // 2, dtype=torch.bfloat16, device=dev)
@@ -803,6 +813,7 @@ def main():
         line["router_f32"] = router_cells(P, torch, dev, max(3, args.steps // 4))
         line["mxfp8"] = mxfp8_cells(P, torch, dev, max(3, args.steps // 4))
         line["mxfp4"] = mxfp8_cells(P, torch, dev, max(3, args.steps // 4), fmt="mxfp4")
+        line["nvfp4"] = mxfp8_cells(P, torch, dev, max(3, args.steps // 4), fmt="nvfp4")
         line["indexer_f32"] = workload_cells(P, torch, dev, max(3, args.steps // 4),
                                              "indexer_f32")
         line["fused_a_3way"] = workload_cells(P, torch, dev, max(3, args.steps // 4),

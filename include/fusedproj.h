@@ -74,8 +74,18 @@ typedef struct fp_plan_s* fp_plan_t;
  * 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), the FP4 form of the fused
  * weight named in PR #8771; two codes per byte, element 2i in the low
  * nibble; a row is its K/2 code bytes, then its K/32 scales (K/2 + K/32
- * bytes, K a multiple of 512). */
-typedef enum { FP_BF16 = 0, FP_F32 = 1, FP_MXFP8 = 2, FP_MXFP4 = 3 } fp_dtype;
+ * bytes, K a multiple of 512).
+ * FP_NVFP4: the FP4 checkpoint form of the pages' fused weight (PR #8771,
+ * first titled as NVFP4 only; the GLM-5.2 NVFP4 target of PR #20502), read
+ * as the public two-level NVFP4 format: E2M1 codes as FP_MXFP4, one E4M3
+ * scale per 16 consecutive elements along K, and one fp32 scale per
+ * projection (fp_plan_set_tensor_scales, default 1).  A row is its K/2
+ * code bytes, then its K/16 scale bytes (K/2 + K/16 bytes, K a multiple of
+ * 512).  Each weight is decoded exactly as E2M1 x E4M3 (at most 6
+ * significant bits); each output's fp32 sum is multiplied by its
+ * projection's tensor scale in fp32, then rounded once to bf16.  Served as
+ * FP_MXFP4 (1 <= M <= 8). */
+typedef enum { FP_BF16 = 0, FP_F32 = 1, FP_MXFP8 = 2, FP_MXFP4 = 3, FP_NVFP4 = 4 } fp_dtype;
 
 typedef enum {
   FP_OK = 0,
@@ -166,6 +176,22 @@ fp_status fp_mxfp8_to_bf16(const void* w, int64_t rows, int64_t K, void* out,
  * multiple of 512. */
 fp_status fp_mxfp4_to_bf16(const void* w, int64_t rows, int64_t K, void* out,
                            void* stream);
+
+/* Dequantise NVFP4 weight rows (K/2 code bytes, low nibble first, then
+ * K/16 E4M3 scales) with tensor scale g: out[r, k] = bf16(e2m1 * e4m3 * g),
+ * the E2M1 x E4M3 product exact, times g in fp32, rounded once (nearest
+ * even).  w, out as fp_mxfp8_to_bf16 (device, 16-byte aligned, not
+ * overlapping); K a multiple of 512 (else FP_ERR_UNSUPPORTED); g finite
+ * (else FP_ERR_INVALID_ARG).  Asynchronous on `stream`. */
+fp_status fp_nvfp4_to_bf16(const void* w, int64_t rows, int64_t K, float g, void* out,
+                           void* stream);
+
+/* NVFP4 plans: the fp32 tensor scale of each projection (host array of the
+ * plan's n_proj values, finite; copied).  FP_ERR_UNSUPPORTED for other
+ * dtypes, FP_ERR_INVALID_ARG for a null plan, null array or a non-finite
+ * value (nothing changed then).  Host-only; call it before the plan's
+ * forward calls (captured graphs keep the scales of their capture). */
+fp_status fp_plan_set_tensor_scales(fp_plan_t plan, const float* scales);
 
 /* Measurement aid (no projection): read `bytes` of device memory at `buf`
  * the way the fused call reads W_cat -- 256 workgroups of 640 threads,

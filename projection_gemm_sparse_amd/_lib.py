@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfusedproj.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fusedproj.h")
 
-FP_BF16, FP_F32, FP_MXFP8, FP_MXFP4 = 0, 1, 2, 3
+FP_BF16, FP_F32, FP_MXFP8, FP_MXFP4, FP_NVFP4 = 0, 1, 2, 3, 4
 FP_OK, FP_ERR_INVALID_ARG, FP_ERR_UNSUPPORTED, FP_ERR_HIP, FP_ERR_WORKSPACE = range(5)
 FP_PATH_NONE, FP_PATH_SKINNY, FP_PATH_SKINNY_SPLITK, FP_PATH_MFMA, FP_PATH_MFMA_SMALL = range(5)
 FP_MAX_PROJ = 16
@@ -80,6 +80,8 @@ _SIGS = {
     "fp_forward_separate": (_i32, [_p, _i64, _i64, _p, _p, _P_p, _P_p]),
     "fp_mxfp8_to_bf16": (_i32, [_p, _i64, _i64, _p, _p]),
     "fp_mxfp4_to_bf16": (_i32, [_p, _i64, _i64, _p, _p]),
+    "fp_nvfp4_to_bf16": (_i32, [_p, _i64, _i64, ctypes.c_float, _p, _p]),
+    "fp_plan_set_tensor_scales": (_i32, [_p, ctypes.POINTER(ctypes.c_float)]),
     "fp_stream_read": (_i32, [_p, _i64, _p, _p]),
     "fp_forward_rmsnorm": (_i32, [_p, _i64, _i64, _p, _p, _P_p, ctypes.c_float, _P_p]),
     "fp_forward_swiglu": (_i32, [_p, _i64, _i64, _p, _p, _p]),
@@ -161,6 +163,19 @@ def fp_mxfp8_to_bf16(w: int, rows: int, K: int, out: int, stream: int) -> int:
 
 def fp_mxfp4_to_bf16(w: int, rows: int, K: int, out: int, stream: int) -> int:
     return _lib.fp_mxfp4_to_bf16(w, rows, K, out, stream)
+
+
+def fp_nvfp4_to_bf16(w: int, rows: int, K: int, g: float, out: int, stream: int) -> int:
+    return _lib.fp_nvfp4_to_bf16(w, rows, K, float(g), out, stream)
+
+
+def fp_plan_set_tensor_scales(plan: int, scales) -> int:
+    """``scales``: one fp32 tensor scale per projection (host values), or
+    None (passed as a null pointer)."""
+    if scales is None:
+        return _lib.fp_plan_set_tensor_scales(plan, None)
+    arr = (ctypes.c_float * len(scales))(*[float(v) for v in scales])
+    return _lib.fp_plan_set_tensor_scales(plan, arr)
 
 
 def fp_stream_read(buf: int, nbytes: int, sink: int, stream: int) -> int:

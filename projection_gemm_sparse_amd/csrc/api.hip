@@ -50,8 +50,8 @@ constexpr int kDefaultSmallMfmaMinM = 3;
 // faster through M = 4 (MXFP8 4.95 vs 5.36 us, MXFP4 4.37 vs 4.60).
 constexpr int kDefaultSmallMfmaMinMMx = 5;
 int default_small_mfma_min_m(int32_t dtype) {
-  return dtype == FP_MXFP8 || dtype == FP_MXFP4 ? kDefaultSmallMfmaMinMMx
-                                                : kDefaultSmallMfmaMinM;
+  return dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4 ? kDefaultSmallMfmaMinMMx
+                                                                      : kDefaultSmallMfmaMinM;
 }
 constexpr int kCus = 256;           // MI355X compute units
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // rows and chunks per row, 32-bit indexing
@@ -89,6 +89,7 @@ struct fp_plan_s {
   int32_t osize;    // output element size
   int64_t mfma_min_m;
   int64_t small_mfma_min_m;
+  float tscale[FP_MAX_PROJ];  // NVFP4: each projection's fp32 tensor scale (1 otherwise)
   bool has_override[FP_MAX_M + 1];
   fp_tiling override_t[FP_MAX_M + 1];
 };
@@ -111,11 +112,11 @@ bool dtype_geometry(int32_t dtype, int64_t K, int* esize, int64_t* wrow, int64_t
     *kc = K * es / 16;
     return true;
   }
-  if (dtype == FP_MXFP8 || dtype == FP_MXFP4) {
+  if (dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4) {
     // units of 8 elements (8 or 4 code bytes), as the bf16 kernel's chunks
     if (K % 512 != 0) return false;
     *esize = 2;
-    *wrow = (dtype == FP_MXFP8 ? K : K / 2) + K / 32;
+    *wrow = dtype == FP_MXFP8 ? K + K / 32 : dtype == FP_MXFP4 ? K / 2 + K / 32 : K / 2 + K / 16;
     *kc = K / 8;
     return true;
   }
@@ -123,13 +124,19 @@ bool dtype_geometry(int32_t dtype, int64_t K, int* esize, int64_t* wrow, int64_t
 }
 
 int skinny_var(const fp_plan_s* p) {
-  return p->dtype == FP_MXFP8 ? fp::kVarMx8 : p->dtype == FP_MXFP4 ? fp::kVarMx4 : fp::kVarPlain;
+  return p->dtype == FP_MXFP8   ? fp::kVarMx8
+         : p->dtype == FP_MXFP4 ? fp::kVarMx4
+         : p->dtype == FP_NVFP4 ? fp::kVarNv4
+                                : fp::kVarPlain;
 }
 
-bool is_mx(int32_t dtype) { return dtype == FP_MXFP8 || dtype == FP_MXFP4; }
+// Block-scaled weight formats (MXFP8, MXFP4, NVFP4): decoded in the kernels,
+// served up to 8 tokens by the vector-ALU and small-M matrix-core kernels.
+bool is_mx(int32_t dtype) { return dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4; }
 
 bool dtype_known(int32_t dtype) {
-  return dtype == FP_BF16 || dtype == FP_F32 || dtype == FP_MXFP8 || dtype == FP_MXFP4;
+  return dtype == FP_BF16 || dtype == FP_F32 || dtype == FP_MXFP8 || dtype == FP_MXFP4 ||
+         dtype == FP_NVFP4;
 }
 
 std::mutex g_mu;
@@ -849,6 +856,7 @@ struct LaunchRows {
   int n_seg;
   unsigned char* y[fp::kMaxSeg];
   int begin[fp::kMaxSeg + 1];
+  float scale[fp::kMaxSeg];  // segment tensor scales (NVFP4)
 };
 
 template <int KT>
@@ -869,9 +877,11 @@ const void* smfma_mx_fn(int kt) {
 }
 
 const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype) {
-  if (dtype == FP_MXFP8 || dtype == FP_MXFP4) {
+  if (dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4) {
     if (pairs || t.mt != 8) return nullptr;
-    return dtype == FP_MXFP8 ? smfma_mx_fn<8>(t.chunks) : smfma_mx_fn<4>(t.chunks);
+    return dtype == FP_MXFP8   ? smfma_mx_fn<8>(t.chunks)
+           : dtype == FP_MXFP4 ? smfma_mx_fn<4>(t.chunks)
+                               : smfma_mx_fn<fp::kFmtNv4>(t.chunks);
   }
   switch (t.chunks) {
     case 4: return smfma_fn_kt<4>(pairs, t.mt);
@@ -905,6 +915,7 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   for (int i = 0; i < fp::kMaxSeg; ++i) {
     tail.out.y[i] = i < lr.n_seg ? lr.y[i] : nullptr;
     tail.out.begin[i] = i < lr.n_seg ? lr.begin[i] : lr.n_rows;
+    tail.out.tscale[i] = i < lr.n_seg ? lr.scale[i] : 1.0f;
   }
   tail.out.begin[fp::kMaxSeg] = lr.n_rows;
   tail.partial = reinterpret_cast<float*>(p->ws + counters_bytes(p->n_total));
@@ -945,6 +956,7 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
                    : p->out_f32 ? skinny_f32out_fn(t.mt, t.chunks, t.rows)
                    : p->dtype == FP_MXFP8 ? skinny_mx_fn<fp::kVarMx8>(t.mt, t.chunks, t.rows)
                    : p->dtype == FP_MXFP4 ? skinny_mx_fn<fp::kVarMx4>(t.mt, t.chunks, t.rows)
+                   : p->dtype == FP_NVFP4 ? skinny_mx_fn<fp::kVarNv4>(t.mt, t.chunks, t.rows)
                    : p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
                                          : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
   return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
@@ -1065,6 +1077,7 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
   p->ws_bytes = ws_bytes;
   p->max_M = max_M;
   p->mfma_min_m = kDefaultMfmaMinM;
+  for (int i = 0; i < FP_MAX_PROJ; ++i) p->tscale[i] = 1.0f;
   p->small_mfma_min_m = default_small_mfma_min_m(dtype);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1146,6 +1159,7 @@ fp_status fp_forward(const void* x, int64_t M, int64_t ldx, fp_plan_t plan, void
   for (int i = 0; i < plan->n_proj; ++i) {
     lr.y[i] = static_cast<unsigned char*>(y[i]);
     lr.begin[i] = (int)plan->off[i];
+    lr.scale[i] = plan->tscale[i];
   }
   lr.begin[plan->n_proj] = (int)plan->n_total;
   return run(plan, t, lr, x, M, ldx, static_cast<hipStream_t>(stream));
@@ -1179,6 +1193,7 @@ fp_status fp_forward_separate(const void* x, int64_t M, int64_t ldx, fp_plan_t p
     lr.y[0] = static_cast<unsigned char*>(y[i]);
     lr.begin[0] = 0;
     lr.begin[1] = (int)plan->N[i];
+    lr.scale[0] = plan->tscale[i];
     s = run(plan, ts[i], lr, x, M, ldx, static_cast<hipStream_t>(stream));
     if (s != FP_OK) return s;
   }
@@ -1204,6 +1219,7 @@ LaunchRows fused_rows(const fp_plan_s* p, void* const* y) {
   for (int i = 0; i < p->n_proj; ++i) {
     lr.begin[i] = (int)p->off[i];
     lr.y[i] = static_cast<unsigned char*>(y[i]);
+    lr.scale[i] = p->tscale[i];
   }
   lr.begin[p->n_proj] = (int)p->n_total;
   return lr;
@@ -1386,6 +1402,35 @@ fp_status fp_mxfp4_to_bf16(const void* w, int64_t rows, int64_t K, void* out, vo
   void* args[] = {&w_a, &o_a, &kc_a, &n_a};
   return launch(reinterpret_cast<const void*>(&fp::mxfp4_to_bf16_kernel), ceil_div(n_a, 256), 256,
                 0, args, static_cast<hipStream_t>(stream));
+}
+
+fp_status fp_nvfp4_to_bf16(const void* w, int64_t rows, int64_t K, float g, void* out,
+                           void* stream) {
+  if (rows < 0 || K < 1 || !std::isfinite(g)) return FP_ERR_INVALID_ARG;
+  int esize = 0;
+  int64_t wrow = 0, kc = 0;
+  if (!dtype_geometry(FP_NVFP4, K, &esize, &wrow, &kc)) return FP_ERR_UNSUPPORTED;
+  if (rows == 0) return FP_OK;
+  if (w == nullptr || out == nullptr) return FP_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(out, 16)) return FP_ERR_UNSUPPORTED;
+  if (range_overlaps(w, rows * wrow, out, rows * K * 2)) return FP_ERR_INVALID_ARG;
+  const unsigned char* w_a = static_cast<const unsigned char*>(w);
+  unsigned char* o_a = static_cast<unsigned char*>(out);
+  int32_t kc_a = (int32_t)(K / 32);  // 16-byte chunks of 32 codes: two blocks each
+  int64_t n_a = rows * kc_a;
+  float g_a = g;
+  void* args[] = {&w_a, &o_a, &kc_a, &n_a, &g_a};
+  return launch(reinterpret_cast<const void*>(&fp::nvfp4_to_bf16_kernel), ceil_div(n_a, 256), 256,
+                0, args, static_cast<hipStream_t>(stream));
+}
+
+fp_status fp_plan_set_tensor_scales(fp_plan_t plan, const float* scales) {
+  if (!plan_ok(plan) || scales == nullptr) return FP_ERR_INVALID_ARG;
+  if (plan->dtype != FP_NVFP4) return FP_ERR_UNSUPPORTED;
+  for (int i = 0; i < plan->n_proj; ++i)
+    if (!std::isfinite(scales[i])) return FP_ERR_INVALID_ARG;
+  for (int i = 0; i < plan->n_proj; ++i) plan->tscale[i] = scales[i];
+  return FP_OK;
 }
 
 fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path, int32_t* launches_fused,

@@ -34,6 +34,7 @@ struct OutTable {
   unsigned char* y[kMaxSeg];
   int32_t begin[kMaxSeg + 1];
   int32_t n_seg;
+  float tscale[kMaxSeg];  // NVFP4: each segment's fp32 tensor scale
 };
 
 // Trailing kernel argument (not preloaded): the output table for launches
@@ -50,6 +51,7 @@ constexpr int kVarPairs = 1;
 constexpr int kVarF32Out = 2;
 constexpr int kVarMx8 = 3;
 constexpr int kVarMx4 = 4;
+constexpr int kVarNv4 = 5;
 
 // Gate/up launches (the PAIRS variant of the kernels): the launch's n_rows =
 // 2N logical rows interleave the two halves of the weight buffer -- logical
@@ -86,7 +88,7 @@ constexpr int max_threads_for_regs(int regs) {
 // MXFP8 / MXFP4 weights (kVarMx8, kVarMx4) hold 8- or 4-byte code units, a
 // scale per unit and four decoded pairs.
 constexpr int skinny_max_threads(int mt, int rw, int cj, int var = kVarPlain) {
-  return var == kVarMx8 || var == kVarMx4
+  return var == kVarMx8 || var == kVarMx4 || var == kVarNv4
              ? max_threads_for_regs(pow2ceil(rw * mt) + 3 * rw * cj + 4 * mt * cj + 36)
              : max_threads_for_regs(pow2ceil(rw * mt) + 4 * rw * cj + 4 * mt * cj + 32);
 }
@@ -116,6 +118,7 @@ struct OutMap {
   unsigned char* y0;
   unsigned char* y1;
   int b0, b1, e1;
+  int i0;  // segment index of y0 (y1 is segment i0 + 1)
 };
 
 __device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char* y1, int split,
@@ -127,6 +130,7 @@ __device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char*
     o.b0 = 0;
     o.b1 = split;
     o.e1 = n_rows;
+    o.i0 = 0;
     return o;
   }
   const int n_seg = tab.n_seg;
@@ -140,6 +144,7 @@ __device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char*
   o.b0 = tab.begin[i0];
   o.b1 = tab.begin[i0 + 1];
   o.e1 = tab.begin[i2];
+  o.i0 = i0;
   asm volatile("" : "+s"(o.y0), "+s"(o.y1), "+s"(o.b0), "+s"(o.b1), "+s"(o.e1));
   return o;
 }
@@ -147,17 +152,22 @@ __device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char*
 // Stores output element (launch row `row`, token m) rounded once to the
 // output type (bf16: round to nearest even).  Agent-coherent (sc1) stores:
 // the line is written through instead of left dirty in this XCD's L2.
-template <bool BF16>
+// SCALED (NVFP4): the fp32 sum is first multiplied by its segment's tensor
+// scale (one fp32 multiply, then the single rounding).
+template <bool BF16, bool SCALED = false>
 __device__ __forceinline__ void store_y(const OutMap& o, const OutTable& tab, int row, int m,
                                         float v) {
   unsigned char* y;
   int idx;
+  int seg = 0;
   if (row < o.b1) {
     y = o.y0;
     idx = m * (o.b1 - o.b0) + (row - o.b0);
+    seg = o.i0;
   } else if (row < o.e1) {
     y = o.y1;
     idx = m * (o.e1 - o.b1) + (row - o.b1);
+    seg = o.i0 + 1;
   } else {
     // a third segment inside the workgroup (more than two projections only)
     y = nullptr;
@@ -166,9 +176,14 @@ __device__ __forceinline__ void store_y(const OutMap& o, const OutTable& tab, in
       if (row >= tab.begin[i] && row < tab.begin[i + 1]) {
         y = tab.y[i];
         idx = m * (tab.begin[i + 1] - tab.begin[i]) + (row - tab.begin[i]);
+        seg = i;
       }
     }
     if (y == nullptr) return;
+  }
+  if constexpr (SCALED) {
+#pragma clang fp contract(off)
+    v = v * tab.tscale[seg < kMaxSeg ? seg : kMaxSeg - 1];
   }
   // global (not generic) address space: a global_store, no aperture check
   typedef __attribute__((address_space(1))) uint16_t g_u16;
@@ -240,6 +255,33 @@ __device__ __forceinline__ bf16x2 decode_e4m3_pair(unsigned u, float scale, bool
 template <int B>
 __device__ __forceinline__ bf16x2 decode_e2m1_pair(unsigned u, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, scale, B);
+}
+
+// Two E2M1 codes (byte B of u) times an NVFP4 block scale `s` (an E4M3
+// value as fp32: at most 4 significant bits), as a bf16 pair.
+// v_cvt_scalef32_pk_bf16_fp4 applies only the exponent of its fp32 scale
+// operand (measured on MI355X: code 0.5 at scale 1.5 gives 0.5), which is
+// all an E8M0 scale has; here the codes are decoded at scale 1, multiplied
+// by s in fp32 (exact: at most 2 + 4 significant bits) and cut back to
+// bf16 (exact for the same reason).
+template <int B>
+__device__ __forceinline__ bf16x2 decode_e2m1_pair_nv(unsigned u, float s) {
+#pragma clang fp contract(off)
+  const unsigned d = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, B));
+  const float lo = u2f(d << 16) * s;
+  const float hi = u2f(d & 0xffff0000u) * s;
+  return __builtin_bit_cast(bf16x2, (__builtin_bit_cast(unsigned, lo) >> 16) |
+                                        (__builtin_bit_cast(unsigned, hi) & 0xffff0000u));
+}
+
+// An E4M3 code as an fp32 value (exact: 4 significant bits; sign, 4
+// exponent bits of bias 7, 3 mantissa bits, subnormals m * 2^-9).  The NaN
+// codes (0x7F, 0xFF) are outside the served domain and decode to a large
+// finite value.
+__device__ __forceinline__ float e4m3_to_f32(unsigned b) {
+  const unsigned e = (b >> 3) & 0xFu, m = b & 7u, s = (b & 0x80u) << 24;
+  const float sub = (float)m * 0.001953125f;  // m * 2^-9
+  return e != 0u ? u2f(s | ((e + 120u) << 23) | (m << 20)) : (s ? -sub : sub);
 }
 
 // Dot product of 8 decoded weights (four bf16 pairs, element order) with
@@ -380,7 +422,7 @@ __device__ __forceinline__ float load_partial(const float* p) {
 }
 
 // Must be called by every thread of the workgroup (it has barriers).
-template <bool BF16>
+template <bool BF16, bool SCALED = false>
 __device__ __forceinline__ void splitk_finish(int n_rows_i,
                                               const float* partial,
                                               uint32_t* counters, int rb,
@@ -410,7 +452,7 @@ __device__ __forceinline__ void splitk_finish(int n_rows_i,
     const float* pp = partial + row * M + m;
     float sum = load_partial(pp);
     for (int ss = 1; ss < S; ++ss) sum += load_partial(pp + ss * sstride);
-    store_y<BF16>(os, tab, (int)row, m, sum);
+    store_y<BF16, SCALED>(os, tab, (int)row, m, sum);
   }
   if (threadIdx.x == 0) {
     __hip_atomic_store((gu32*)(counters + rb), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -1,4 +1,4 @@
-// mxfp8.hpp -- dequantisation of MXFP8 and MXFP4 weight rows to bf16.
+// mxfp8.hpp -- dequantisation of MXFP8, MXFP4 and NVFP4 weight rows to bf16.
 //
 // The pages name MXFP8 projections for the DeepSeek-V4.1 wq_a / wkv weights
 // ("tinygemm2 for the DeepSeek-V4.1 hidden-state projections", TensorRT-LLM
@@ -66,6 +66,42 @@ mxfp4_to_bf16_kernel(const unsigned char* __restrict__ w, unsigned char* __restr
     o.y = __builtin_bit_cast(unsigned, decode_e2m1_pair<1>(qs[i], sc));
     o.z = __builtin_bit_cast(unsigned, decode_e2m1_pair<2>(qs[i], sc));
     o.w = __builtin_bit_cast(unsigned, decode_e2m1_pair<3>(qs[i], sc));
+    orow[i] = o;
+  }
+}
+
+// NVFP4 rows (K/2 code bytes, low nibble first, then K/16 E4M3 scales):
+// thread t decodes code chunk t (16 bytes, 32 codes, two 16-element
+// blocks) of the rows to 64 bytes of bf16: each element e2m1 * e4m3 (exact
+// in fp32) times the tensor scale g in fp32, rounded once to bf16.
+__global__ void __launch_bounds__(256)
+nvfp4_to_bf16_kernel(const unsigned char* __restrict__ w, unsigned char* __restrict__ out,
+                     int32_t kc, int64_t n_chunks, float g) {
+#pragma clang fp contract(off)
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_chunks) return;
+  const int64_t row = t / kc;
+  const int c = (int)(t - row * kc);
+  const uint64_t row_bytes = (uint64_t)kc * 16u + (uint32_t)kc * 2u;
+  const unsigned char* wrow = w + (uint64_t)row * row_bytes;
+  const u32x4 q = *reinterpret_cast<const u32x4*>(wrow + (uint64_t)c * 16u);
+  const unsigned sb = *reinterpret_cast<const uint16_t*>(wrow + (uint64_t)kc * 16u + 2u * c);
+  const float sc[2] = {e4m3_to_f32(sb & 0xffu), e4m3_to_f32(sb >> 8)};
+  u32x4* orow = reinterpret_cast<u32x4*>(out + ((uint64_t)row * kc * 32u + (uint64_t)c * 32u) * 2u);
+  const unsigned qs[4] = {q.x, q.y, q.z, q.w};
+  auto scaled = [&](bf16x2 d) {
+    const unsigned u = __builtin_bit_cast(unsigned, d);
+    const float lo = u2f(u << 16) * g, hi = u2f(u & 0xffff0000u) * g;
+    return (unsigned)f32_to_bf16_rne(lo) | ((unsigned)f32_to_bf16_rne(hi) << 16);
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float s = sc[i >> 1];  // 8 codes per word: words 0, 1 in block 0
+    u32x4 o;
+    o.x = scaled(decode_e2m1_pair_nv<0>(qs[i], s));
+    o.y = scaled(decode_e2m1_pair_nv<1>(qs[i], s));
+    o.z = scaled(decode_e2m1_pair_nv<2>(qs[i], s));
+    o.w = scaled(decode_e2m1_pair_nv<3>(qs[i], s));
     orow[i] = o;
   }
 }

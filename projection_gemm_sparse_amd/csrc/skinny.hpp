@@ -76,6 +76,14 @@ namespace fp {
 //               low nibble first): a unit is 4 code bytes, a row K/2 code
 //               bytes followed by its K/32 scales, and each code byte
 //               decodes to one bf16 pair (v_cvt_scalef32_pk_bf16_fp4).
+//   kVarNv4     NVFP4 weights: E2M1 codes as kVarMx4, one E4M3 scale per
+//               16 elements (a row: K/2 code bytes, then K/16 scales), so
+//               two units share a scale; writing the scale as 2^E * f,
+//               the unit decodes exactly at 2^E and its 8-term sum (from
+//               0, in element order) is added into the output's sum with
+//               one fused multiply-add by f; each finished sum is
+//               multiplied by its projection's fp32 tensor scale before the
+//               single rounding.
 template <int MT, int RW, int CJ, bool BF16, int VAR = kVarPlain>
 __global__ void __launch_bounds__(skinny_max_threads(MT, RW, CJ, VAR))
 skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
@@ -88,7 +96,8 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   constexpr bool PAIRS = VAR == kVarPairs;
   constexpr bool OUT_BF16 = BF16 && VAR != kVarF32Out;
   constexpr bool MX8 = VAR == kVarMx8;
-  constexpr bool MX4 = VAR == kVarMx4;
+  constexpr bool NV4 = VAR == kVarNv4;
+  constexpr bool MX4 = VAR == kVarMx4 || NV4;  // 4-bit codes, 4 bytes per unit
   constexpr bool MX = MX8 || MX4;
   constexpr uint32_t UB = MX8 ? 8u : 4u;  // code bytes per 8-element unit
 
@@ -110,7 +119,10 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   const int wrow0 = row_base + gq * RW;
   const int cbase = s * (P * 64 * CJ) + p * (64 * CJ) + lane;
   // MXFP8 / MXFP4: UB code bytes per unit, then one scale byte per 4 units
-  const uint32_t row_bytes = MX ? (uint32_t)kc * UB + ((uint32_t)kc >> 2) : (uint32_t)kc * 16u;
+  // (NVFP4: one scale per 2 units)
+  const uint32_t row_bytes = NV4  ? (uint32_t)kc * UB + ((uint32_t)kc >> 1)
+                             : MX ? (uint32_t)kc * UB + ((uint32_t)kc >> 2)
+                                  : (uint32_t)kc * 16u;
 
   // Loads are branch-free: an out-of-range chunk or row loads a clamped,
   // always-valid address, and out-of-range chunks are replaced by zero only
@@ -170,7 +182,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
 #pragma unroll
       for (int j = 0; j < CJ; ++j) {
         const int c = cbase + j * 64;
-        sv[r][j] = srow[(c < kc ? c : kc - 1) >> 2];
+        sv[r][j] = srow[(c < kc ? c : kc - 1) >> (NV4 ? 1 : 2)];
       }
     } else {
       const u32x4* wrow = reinterpret_cast<const u32x4*>(wrow_b);
@@ -225,12 +237,33 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
       } else if constexpr (MX4) {
         const unsigned q = c_ok[j] ? q4[r][j] : 0u;
         const uint32_t sb = sv[r][j];
-        const float sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
-        const bf16x2 d[4] = {decode_e2m1_pair<0>(q, sc), decode_e2m1_pair<1>(q, sc),
-                             decode_e2m1_pair<2>(q, sc), decode_e2m1_pair<3>(q, sc)};
+        // MXFP4: E8M0 scale 2^(s - 127); NVFP4: the E4M3 block scale (the
+        // tensor scale is applied to the finished sum)
+        if constexpr (NV4) {
+          // the E4M3 scale as 2^E * f: the codes decode at the power of
+          // two (the decode instruction applies only a scale's exponent;
+          // exact), the unit's 8-term sum is formed from 0 and added in
+          // with one fused multiply-add by f (f = 1 + m/8, or m for the
+          // subnormal scales m * 2^-9)
+          const unsigned e = (sb >> 3) & 0xFu, mb = sb & 7u;
+          const float p2 = u2f(e != 0u ? (e + 120u) << 23 : 0x3B000000u);  // 2^(e-7) or 2^-9
+          const float fm = (sb & 0x80u) ? -1.0f : 1.0f;
+          const float f = e != 0u ? fm * (1.0f + 0.125f * (float)mb) : fm * (float)mb;
+          const bf16x2 d[4] = {decode_e2m1_pair<0>(q, p2), decode_e2m1_pair<1>(q, p2),
+                               decode_e2m1_pair<2>(q, p2), decode_e2m1_pair<3>(q, p2)};
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          v[r * MT + m] = dot_decoded(d, xv[m][j], v[r * MT + m]);
+          for (int m = 0; m < MT; ++m) {
+            const float t = dot_decoded(d, xv[m][j], 0.0f);
+            v[r * MT + m] = __builtin_fmaf(t, f, v[r * MT + m]);
+          }
+        } else {
+          const float sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
+          const bf16x2 d[4] = {decode_e2m1_pair<0>(q, sc), decode_e2m1_pair<1>(q, sc),
+                               decode_e2m1_pair<2>(q, sc), decode_e2m1_pair<3>(q, sc)};
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            v[r * MT + m] = dot_decoded(d, xv[m][j], v[r * MT + m]);
+          }
         }
       } else {
         const u32x4 wj = c_ok[j] ? wv[r][j] : zero4;
@@ -255,7 +288,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
         const int r = idx / MT;
         const int m = idx - r * MT;
         const int row = wrow0 + r;
-        if (idx < V && m < M && row < n_rows) store_y<OUT_BF16>(om, a.out, row, m, v[q]);
+        if (idx < V && m < M && row < n_rows) store_y<OUT_BF16, NV4>(om, a.out, row, m, v[q]);
       }
     }
     return;
@@ -287,7 +320,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
           store_pair(y0, split, row, m, sum, u_sum);
         }
       } else if (Sv == 1) {
-        store_y<OUT_BF16>(om, a.out, row, m, sum);
+        store_y<OUT_BF16, NV4>(om, a.out, row, m, sum);
       } else {
         store_partial(partial + ((int64_t)s * n_rows + row) * M + m, sum);
       }
@@ -296,7 +329,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   if (Sv == 1) return;
 
   // 6. split-K: the last workgroup of the row block adds the S partials
-  splitk_finish<OUT_BF16>(n_rows, partial, counters, rb, Sv, row_base, (int64_t)Gv * RW, M,
+  splitk_finish<OUT_BF16, NV4>(n_rows, partial, counters, rb, Sv, row_base, (int64_t)Gv * RW, M,
                       Gv * P * 64, om, a.out,
                       reinterpret_cast<int*>(smem + Gv * VP * kMaxWaveParts));
 }

@@ -57,6 +57,8 @@
 
 namespace fp {
 
+constexpr int kFmtNv4 = 5;  // the NVFP4 form of smfma_mx_kernel
+
 constexpr int smfma_max_threads(int kt, int mh = 1) {
   return max_threads_for_regs(4 * kt * (mh + 1) + 24 + 16 * (mh - 1));
 }
@@ -258,12 +260,17 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
 // activations use the same mapping (load lane L: token L / 8, the same G
 // units; G 16-byte loads).  A group's G units lie in one 32-element block
 // (K is a multiple of 512), whose scale the MFMA lane reads itself.
+// NVFP4 (FMT kFmtNv4): E2M1 codes as MXFP4 (G = 4) with one E4M3 scale per
+// 16 elements, so a group spans two blocks and the lane reads both scale
+// bytes; the finished sums are multiplied by their projection's fp32
+// tensor scale before the single rounding (store_y SCALED).
 template <int KT, int FMT>
 __global__ void __launch_bounds__(smfma_max_threads(KT))
 smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
                 unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
                 int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
-  static_assert(FMT == 8 || FMT == 4, "MXFP8 or MXFP4");
+  static_assert(FMT == 8 || FMT == 4 || FMT == kFmtNv4, "MXFP8, MXFP4 or NVFP4");
+  constexpr bool NV = FMT == kFmtNv4;
   constexpr int G = FMT == 8 ? 2 : 4;      // steps per 16-byte load of codes
   constexpr int NU = KT / G;               // code loads per lane
   constexpr uint32_t UB = FMT == 8 ? 8u : 4u;  // code bytes per unit
@@ -285,7 +292,8 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
   const int r8 = i16 & 7;
   const int cw = p * (8 * KT);                        // first unit of the wave
   const int cg = cw + G * (2 * g + sub);              // this MFMA lane's unit at u = 0
-  const uint32_t row_bytes = (uint32_t)kc * UB + ((uint32_t)kc >> 2);
+  // scales after the codes: one per 4 units (MX), per 2 units (NVFP4)
+  const uint32_t row_bytes = (uint32_t)kc * UB + ((uint32_t)kc >> (NV ? 1 : 2));
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
   const int rl = lane >> 3;    // load lane: row / token
   const int pl = lane & 7;     // load lane: unit group in the step group
@@ -322,7 +330,13 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
       const int c = c0 < kc ? c0 : kc - G;
       qv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (uint32_t)c * UB));
       const int cs = cg + 8 * G * u;
-      sv[u] = srow[(cs < kc ? cs : kc - 1) >> 2];
+      if constexpr (NV) {
+        // the group's 4 units span two 16-element blocks: both scale bytes
+        const int cc = cs < kc ? cs : kc - 4;
+        sv[u] = *reinterpret_cast<const uint16_t*>(srow + (cc >> 1));
+      } else {
+        sv[u] = srow[(cs < kc ? cs : kc - 1) >> 2];
+      }
 #pragma unroll
       for (int e = 0; e < G; ++e) {
         const int cx = c0 + e;
@@ -344,11 +358,14 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
     __builtin_amdgcn_sched_barrier(0);
     const bool c_ok = cg + 8 * G * u < kc;
     const u32x4 q = shuffle(qv[u]);
-    // scale 2^(s - 127) as an fp32 (s = 0: the subnormal 2^-127)
+    // MX: scale 2^(s - 127) as an fp32 (s = 0: the subnormal 2^-127);
+    // NVFP4: the E4M3 scales of the group's two blocks (units 0, 1 and 2, 3)
     const uint32_t sb = sv[u];
-    const float sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
+    const float sc = NV ? e4m3_to_f32(sb & 0xffu) : u2f(sb != 0u ? sb << 23 : 0x00400000u);
+    const float sc_hi = NV ? e4m3_to_f32(sb >> 8) : sc;
 #pragma unroll
     for (int e = 0; e < G; ++e) {
+      const float sce = e < 2 ? sc : sc_hi;
       bf16x2 d[4];
       if constexpr (FMT == 8) {
         const unsigned q0 = e == 0 ? q.x : q.z;
@@ -359,10 +376,17 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
         d[3] = decode_e4m3_pair(q1, sc, true);
       } else {
         const unsigned qe = e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
-        d[0] = decode_e2m1_pair<0>(qe, sc);
-        d[1] = decode_e2m1_pair<1>(qe, sc);
-        d[2] = decode_e2m1_pair<2>(qe, sc);
-        d[3] = decode_e2m1_pair<3>(qe, sc);
+        if constexpr (NV) {
+          d[0] = decode_e2m1_pair_nv<0>(qe, sce);
+          d[1] = decode_e2m1_pair_nv<1>(qe, sce);
+          d[2] = decode_e2m1_pair_nv<2>(qe, sce);
+          d[3] = decode_e2m1_pair_nv<3>(qe, sce);
+        } else {
+          d[0] = decode_e2m1_pair<0>(qe, sce);
+          d[1] = decode_e2m1_pair<1>(qe, sce);
+          d[2] = decode_e2m1_pair<2>(qe, sce);
+          d[3] = decode_e2m1_pair<3>(qe, sce);
+        }
       }
       const u32x4 wa = u32x4{__builtin_bit_cast(unsigned, d[0]), __builtin_bit_cast(unsigned, d[1]),
                              __builtin_bit_cast(unsigned, d[2]), __builtin_bit_cast(unsigned, d[3])};
@@ -396,7 +420,7 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
     if (r < RT && m < M && row < n_rows) {
       const float* q0 = smem + ((gg * 2 + 0) * 64 + r * 8 + m) * kMaxWaveParts;
       const float* q1 = smem + ((gg * 2 + 1) * 64 + r * 8 + m) * kMaxWaveParts;
-      store_y<true>(om, a.out, row, m, sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK));
+      store_y<true, NV>(om, a.out, row, m, sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK));
     }
   }
 }

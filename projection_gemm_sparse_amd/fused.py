@@ -36,14 +36,17 @@ class FusedProjection:
     MXFP8 weights are uint8 tensors of packed rows [N_i, K + K/32] (the K
     E4M3 codes, then the K/32 E8M0 scales), MXFP4 weights packed rows
     [N_i, K/2 + K/32] (two E2M1 codes per byte, low nibble first, then the
-    scales); ``weight_format`` ("mxfp8" or "mxfp4") names the format of
+    scales), NVFP4 weights packed rows [N_i, K/2 + K/16] (two E2M1 codes
+    per byte, low nibble first, then one E4M3 scale per 16 elements) with
+    one fp32 ``tensor_scales[i]`` per projection (default 1);
+    ``weight_format`` ("mxfp8", "mxfp4" or "nvfp4") names the format of
     uint8 weights when their width does not tell it.  Activations and
     outputs are then bf16.
     """
 
     def __init__(self, weights, max_M: int = 8, stream=None, copy_weights: bool = True,
                  workspace_bytes: int | None = None, out_dtype=None,
-                 weight_format: str | None = None):
+                 weight_format: str | None = None, tensor_scales=None):
         if not weights:
             raise ValueError("at least one projection")
         w0 = weights[0]
@@ -55,7 +58,7 @@ class FusedProjection:
         self.w_dtype = w0.dtype
         if w0.dtype == torch.uint8:
             cols = int(w0.shape[1])
-            fits = {"mxfp8": cols % 33 == 0, "mxfp4": cols % 17 == 0}
+            fits = {"mxfp8": cols % 33 == 0, "mxfp4": cols % 17 == 0, "nvfp4": cols % 9 == 0}
             fmt = weight_format
             if fmt is None:
                 cand = [f for f, ok in fits.items() if ok]
@@ -65,8 +68,10 @@ class FusedProjection:
             if fmt not in fits or not fits[fmt]:
                 raise ValueError("packed %s rows cannot be %d bytes wide" % (fmt, cols))
             self.dtype = torch.bfloat16  # activations and outputs
-            self.fp_dtype = L.FP_MXFP8 if fmt == "mxfp8" else L.FP_MXFP4
-            self.K = cols // 33 * 32 if fmt == "mxfp8" else cols // 17 * 32
+            self.fp_dtype = {"mxfp8": L.FP_MXFP8, "mxfp4": L.FP_MXFP4,
+                             "nvfp4": L.FP_NVFP4}[fmt]
+            self.K = {"mxfp8": cols // 33 * 32, "mxfp4": cols // 17 * 32,
+                      "nvfp4": cols // 9 * 16}[fmt]
         else:
             self.dtype = w0.dtype
             self.fp_dtype = _DTYPES[w0.dtype]
@@ -105,6 +110,13 @@ class FusedProjection:
                 (torch.cuda.current_stream() if stream is None else stream).synchronize()
                 del keep
         self.plan = plan
+        self.tensor_scales = None
+        if tensor_scales is not None:
+            if len(tensor_scales) != len(self.N):
+                raise ValueError("one tensor scale per projection")
+            L.check(L.fp_plan_set_tensor_scales(plan, list(tensor_scales)),
+                    "fp_plan_set_tensor_scales")
+            self.tensor_scales = [float(v) for v in tensor_scales]
         self.out_dtype = self.dtype if out_dtype is None else out_dtype
         if self.out_dtype != self.dtype:
             if self.out_dtype not in _DTYPES:

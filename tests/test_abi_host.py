@@ -31,7 +31,7 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("args", [
-    (4, 5120, [1280, 512], 8),      # bad dtype
+    (5, 5120, [1280, 512], 8),      # bad dtype
     (0, 0, [1280, 512], 8),         # K < 1
     (0, 5121, [1280, 512], 8),      # K*2 not a multiple of 16
     (1, 7170, [128], 8),            # K*4 not a multiple of 16
@@ -69,7 +69,7 @@ def _create(dtype=0, K=5120, N=(1280, 512), w_cat=FAKE, ws=FAKE, ws_bytes=None, 
 
 
 def test_plan_create_validation_before_any_hip_call():
-    assert _create(dtype=4)[0] == P.FP_ERR_INVALID_ARG
+    assert _create(dtype=5)[0] == P.FP_ERR_INVALID_ARG
     assert _create(K=-1)[0] == P.FP_ERR_INVALID_ARG
     assert _create(N=(0,))[0] == P.FP_ERR_INVALID_ARG
     assert _create(max_M=0)[0] == P.FP_ERR_INVALID_ARG
@@ -249,3 +249,23 @@ def test_stream_read_refusals_before_any_hip_call():
     assert P.fp_stream_read(FAKE, 1000, FAKE + (1 << 24), 0) == P.FP_ERR_UNSUPPORTED
     assert P.fp_stream_read(FAKE, 1 << 31, FAKE + (1 << 32), 0) == P.FP_ERR_UNSUPPORTED
     assert P.fp_stream_read(FAKE, 4096, FAKE + 2048, 0) == P.FP_ERR_INVALID_ARG  # overlap
+
+
+def test_nvfp4_geometry_and_refusals():
+    # rows of K/2 code bytes and K/16 E4M3 scales, K a multiple of 512
+    assert P.fp_workspace_bytes(P.FP_NVFP4, 5120, [1280, 512], 8) > 0
+    assert P.fp_workspace_bytes(P.FP_NVFP4, 5136, [1280, 512], 8) == 0
+    st, t = P.fp_default_tiling(P.FP_NVFP4, 5120, 1792, 4, 1792)
+    assert st == P.FP_OK and t[0] == P.FP_PATH_SKINNY
+    st, t = P.fp_default_tiling(P.FP_NVFP4, 5120, 1792, 8, 1792)
+    assert st == P.FP_OK and t[0] == P.FP_PATH_MFMA_SMALL
+    assert P.fp_default_tiling(P.FP_NVFP4, 5120, 1792, 9, 1792)[0] == P.FP_ERR_UNSUPPORTED
+    # dequantiser: argument checks before any launch
+    assert P.fp_nvfp4_to_bf16(FAKE, 2, 528, 1.0, FAKE + (1 << 24), 0) == P.FP_ERR_UNSUPPORTED
+    assert P.fp_nvfp4_to_bf16(FAKE, 2, 512, float("nan"), FAKE + (1 << 24), 0) == \
+        P.FP_ERR_INVALID_ARG
+    assert P.fp_nvfp4_to_bf16(FAKE, 0, 512, 1.0, FAKE + (1 << 24), 0) == P.FP_OK
+    assert P.fp_nvfp4_to_bf16(FAKE, 4, 512, 1.0, FAKE + 64, 0) == P.FP_ERR_INVALID_ARG
+    # tensor scales on a null plan
+    assert P.fp_plan_set_tensor_scales(None, [1.0]) == P.FP_ERR_INVALID_ARG
+    assert P.fp_plan_set_tensor_scales(FAKE, [1.0]) == P.FP_ERR_INVALID_ARG

@@ -26,7 +26,7 @@ SCALES = (1, 100, 112, 127, 140, 200)
 
 
 def _plan(ws, max_M=8):
-    return P.FusedProjection([to_gpu(w) for w in ws], max_M=max_M)
+    return P.FusedProjection([to_gpu(w) for w in ws], max_M=max_M, weight_format="mxfp8")
 
 
 def _check(ys, x_cpu, ws, K, label):
