@@ -518,7 +518,7 @@ def mxfp8_cells(P, torch, dev, steps, Ms=(1, 2, 4, 8), fmt="mxfp8", variants=Fal
                 sc = torch.randint(0x28, 0x41, (nr, K // 16), generator=g, device="cuda")
             ws.append(torch.cat([codes, sc], 1).to(torch.uint8))
         ts = [0.0087890625, 0.0107421875] if fmt == "nvfp4" else None
-        plans.append(P.FusedProjection(ws, max_M=8, weight_format=fmt, tensor_scales=ts))
+        plans.append(P.FusedProjection(ws, max_M=16, weight_format=fmt, tensor_scales=ts))
         del ws
     res = {}
     for M in Ms:
@@ -625,7 +625,7 @@ def main():
         print(json.dumps({"pool_sweep": rows}), flush=True)
         return
     if args.mxfp8_only:
-        Ms = tuple(range(1, 9)) if args.mx_variants else (1, 2, 4, 8)
+        Ms = tuple(range(1, 9)) + (12, 16) if args.mx_variants else (1, 2, 4, 8)
         res = {"mxfp8": mxfp8_cells(P, torch, dev, args.steps, Ms=Ms, variants=args.mx_variants),
                "mxfp4": mxfp8_cells(P, torch, dev, args.steps, Ms=Ms, fmt="mxfp4",
                                     variants=args.mx_variants),

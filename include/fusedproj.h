@@ -66,10 +66,10 @@ typedef struct fp_plan_s* fp_plan_t;
  * a multiple of 512).  Every weight element is decoded exactly (an E4M3
  * value times a power of two) for scaled values inside bf16's normal range;
  * NaN codes and scales (0x7F/0xFF, 255) and scales above 2^119 are outside
- * the served domain.  Served for 1 <= M <= 8: the vector-ALU kernel up to
- * 4 tokens, the small-M matrix-core kernel (weights decoded to bf16 in the
- * registers feeding the matrix unit) from 5 (both by default; tilings may
- * pick either).
+ * the served domain.  Served for 1 <= M <= 16: the vector-ALU kernel up
+ * to 4 tokens, the small-M matrix-core kernel (weights decoded to bf16 in
+ * the registers feeding the matrix unit; two token halves above 8) from 5
+ * (by default; tilings may pick either kernel up to 8 tokens).
  * FP_MXFP4: the same with E2M1 elements (sign, 2 exponent bits of bias 1,
  * 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), the FP4 form of the fused
  * weight named in PR #8771; two codes per byte, element 2i in the low
@@ -84,7 +84,7 @@ typedef struct fp_plan_s* fp_plan_t;
  * 512).  Each weight is decoded exactly as E2M1 x E4M3 (at most 6
  * significant bits); each output's fp32 sum is multiplied by its
  * projection's tensor scale in fp32, then rounded once to bf16.  Served as
- * FP_MXFP4 (1 <= M <= 8). */
+ * FP_MXFP4 (1 <= M <= 16). */
 typedef enum { FP_BF16 = 0, FP_F32 = 1, FP_MXFP8 = 2, FP_MXFP4 = 3, FP_NVFP4 = 4 } fp_dtype;
 
 typedef enum {
@@ -108,8 +108,7 @@ typedef enum {
                               the tile kernel (whole K slice in LDS) up to
                               32 tokens, the ring tile kernel (K slice
                               streamed through a ring of LDS stages) from 33 */
-  FP_PATH_MFMA_SMALL = 4   /* matrix-core kernel for few tokens (bf16 M <= 16,
-                              MX weights M <= 8):
+  FP_PATH_MFMA_SMALL = 4   /* matrix-core kernel for few tokens (M <= 16):
                               8-row x 2-sub-slice tiles, one launch */
 } fp_path;
 
@@ -319,8 +318,7 @@ fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
  * so fused and separate calls of one plan stay bitwise equal under any
  * tiling.
  *   path    FP_PATH_SKINNY / FP_PATH_SKINNY_SPLITK (same kernel; the
- *           splits field decides), FP_PATH_MFMA_SMALL (bf16 M <= 16, MX
- *           M <= 8) or
+ *           splits field decides), FP_PATH_MFMA_SMALL (M <= 16) or
  *           FP_PATH_MFMA (the tile kernels, bf16)
  *   kparts  skinny: waves splitting one K slice (P, <= 16); mfma-small:
  *           waves splitting K (PK, <= 16); mfma: 16-row tiles per

@@ -457,7 +457,7 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     // buffer offsets are 32-bit
     if ((int64_t)t.splits * n_rows * 16 * t.mt * 4 >= ((int64_t)1 << 31)) return false;
   } else if (t.path == FP_PATH_MFMA_SMALL) {
-    if (!(p->dtype == FP_BF16 || (is_mx(p->dtype) && M <= kSkinnyMaxM))) return false;
+    if (!(p->dtype == FP_BF16 || is_mx(p->dtype))) return false;
     if (M > kSmallMfmaMaxM || t.mt < M) return false;
     if (!(t.chunks == 4 || t.chunks == 8 || t.chunks == 16)) return false;
     if (t.splits != 1 || t.kparts > fp::kMaxWaveParts || t.rows > 8 || t.groups < 1) return false;
@@ -507,8 +507,8 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
     // fp32-output plans run the vector-ALU kernel only
     const bool mfma = p->dtype == FP_BF16 && !p->out_f32 &&
                       (M >= p->mfma_min_m || M > kSmallMfmaMaxM);
-    // MX plans: the small-M kernel up to 8 tokens (bf16 up to 16)
-    const bool small = (p->dtype == FP_BF16 || (is_mx(p->dtype) && M <= kSkinnyMaxM)) &&
+    // bf16 and block-scaled weights: the small-M kernel up to 16 tokens
+    const bool small = (p->dtype == FP_BF16 || is_mx(p->dtype)) &&
                        !p->out_f32 && !mfma &&
                        (M >= p->small_mfma_min_m || M > kSkinnyMaxM) &&
                        default_smfma_order(p->kc, t);
@@ -866,22 +866,28 @@ const void* smfma_fn_kt(bool pairs, int mt) {
                : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false>);
 }
 
-template <int FMT>
+template <int FMT, int MH>
 const void* smfma_mx_fn(int kt) {
   switch (kt) {
-    case 4: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<4, FMT>);
-    case 8: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<8, FMT>);
-    case 16: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<16, FMT>);
+    case 4: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<4, FMT, MH>);
+    case 8: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<8, FMT, MH>);
+    case 16: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<16, FMT, MH>);
     default: return nullptr;
   }
 }
 
+template <int MH>
+const void* smfma_mx_fn_fmt(int32_t dtype, int kt) {
+  return dtype == FP_MXFP8   ? smfma_mx_fn<8, MH>(kt)
+         : dtype == FP_MXFP4 ? smfma_mx_fn<4, MH>(kt)
+                             : smfma_mx_fn<fp::kFmtNv4, MH>(kt);
+}
+
 const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype) {
   if (dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4) {
-    if (pairs || t.mt != 8) return nullptr;
-    return dtype == FP_MXFP8   ? smfma_mx_fn<8>(t.chunks)
-           : dtype == FP_MXFP4 ? smfma_mx_fn<4>(t.chunks)
-                               : smfma_mx_fn<fp::kFmtNv4>(t.chunks);
+    if (pairs) return nullptr;
+    return t.mt == 8 ? smfma_mx_fn_fmt<1>(dtype, t.chunks)
+                     : smfma_mx_fn_fmt<2>(dtype, t.chunks);
   }
   switch (t.chunks) {
     case 4: return smfma_fn_kt<4>(pairs, t.mt);

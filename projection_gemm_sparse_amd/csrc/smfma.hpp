@@ -264,8 +264,8 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
 // 16 elements, so a group spans two blocks and the lane reads both scale
 // bytes; the finished sums are multiplied by their projection's fp32
 // tensor scale before the single rounding (store_y SCALED).
-template <int KT, int FMT>
-__global__ void __launch_bounds__(smfma_max_threads(KT))
+template <int KT, int FMT, int MH = 1>
+__global__ void __launch_bounds__(smfma_max_threads(KT, MH))
 smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
                 unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
                 int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
@@ -275,7 +275,8 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
   constexpr int NU = KT / G;               // code loads per lane
   constexpr uint32_t UB = FMT == 8 ? 8u : 4u;  // code bytes per unit
   static_assert(KT % G == 0, "whole step groups");
-  extern __shared__ float smem[];  // [G][2][8][8][16]
+  static_assert(MH == 1 || MH == 2, "token halves");
+  extern __shared__ float smem[];  // [G][MH][2][8][8][16]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -307,17 +308,21 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
     return o;
   };
 
-  // 1. activations (token rl clamped; tokens past M zeroed after the
-  //    shuffle), then the codes (row rl of the tile clamped to the launch),
-  //    then this MFMA lane's block scales: all loads before the first MFMA
-  //    Group by group: the codes (starting the weight stream with the
-  //    first load), the scale, then the group's activation chunks.
-  u32x4 xv[NU][G];
+  // 1. all loads before the first MFMA, group by group: the codes (row rl
+  //    of the tile clamped to the launch; the weight stream starts with
+  //    the first load), this MFMA lane's block scale(s), then the group's
+  //    activation chunks of each token half (token rl + 8h clamped; tokens
+  //    past M are zeroed after the shuffle)
+  u32x4 xv[MH][NU][G];
   u32x4 qv[NU];
   uint32_t sv[NU];
   {
-    const int mc = rl < M ? rl : M - 1;
-    const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
+    const u32x4* xrow[MH];
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+      const int mc = rl + 8 * h < M ? rl + 8 * h : M - 1;
+      xrow[h] = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
+    }
     const int rr = rl < RT ? row0 + rl : row0;
     const int row = rr < n_rows ? rr : n_rows - 1;
     const unsigned char* wrow = w + (uint64_t)(uint32_t)row * row_bytes;
@@ -338,21 +343,24 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
         sv[u] = srow[(cs < kc ? cs : kc - 1) >> 2];
       }
 #pragma unroll
-      for (int e = 0; e < G; ++e) {
-        const int cx = c0 + e;
-        xv[u][e] = xrow[cx < kc ? cx : kc - 1];
-      }
+      for (int h = 0; h < MH; ++h)
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+          const int cx = c0 + e;
+          xv[h][u][e] = xrow[h][cx < kc ? cx : kc - 1];
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
   const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
   __builtin_amdgcn_sched_barrier(0);
-  const bool tok_ok = r8 < M;
 
   // 2. step groups in order, steps in order inside a group; units past K
   //    contribute zero
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[MH];
+#pragma unroll
+  for (int h = 0; h < MH; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     __builtin_amdgcn_sched_barrier(0);
@@ -390,27 +398,49 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
       }
       const u32x4 wa = u32x4{__builtin_bit_cast(unsigned, d[0]), __builtin_bit_cast(unsigned, d[1]),
                              __builtin_bit_cast(unsigned, d[2]), __builtin_bit_cast(unsigned, d[3])};
-      const u32x4 xb = shuffle(xv[u][e]);
       const bf16x8 A = u4bf8(c_ok ? wa : zero4);
-      const bf16x8 B = u4bf8(c_ok && tok_ok ? xb : zero4);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < MH; ++h) {
+        const bool tok_ok = r8 + 8 * h < M;
+        const u32x4 xb = shuffle(xv[h][u][e]);
+        const bf16x8 B = u4bf8(c_ok && tok_ok ? xb : zero4);
+        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[h], 0, 0, 0);
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. the diagonal blocks to LDS (as smfma_kernel)
   if ((g >> 1) == sub) {
-    float* red = smem + ((g2 * 2 + sub) * 64 + r8) * kMaxWaveParts + p;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = (4 * g + v) & 7;
-      red[r * 8 * kMaxWaveParts] = acc[v];
+    for (int h = 0; h < MH; ++h) {
+      float* red = smem + (((g2 * MH + h) * 2 + sub) * 64 + r8) * kMaxWaveParts + p;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = (4 * g + v) & 7;
+        red[r * 8 * kMaxWaveParts] = acc[h][v];
+      }
     }
   }
   __syncthreads();
 
   // 4. one thread per output: each sub-slice over the PK waves in wave
   //    order, then sub-slice 0 + sub-slice 1
+  if constexpr (MH == 2) {
+    const int n_out = Gv * 128;
+    for (int o = tid; o < n_out; o += Gv * PK * 64) {
+      const int gh = o >> 6;  // g2 * 2 + half
+      const int r = (o >> 3) & 7;
+      const int m = (gh & 1) * 8 + (o & 7);
+      const int row = row_base + (gh >> 1) * RT + r;
+      if (r < RT && m < M && row < n_rows) {
+        const float* q0 = smem + ((gh * 2 + 0) * 64 + (o & 63)) * kMaxWaveParts;
+        const float* q1 = smem + ((gh * 2 + 1) * 64 + (o & 63)) * kMaxWaveParts;
+        store_y<true, NV>(om, a.out, row, m, sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK));
+      }
+    }
+    return;
+  }
   const int n_out = Gv * 64;
   if (tid < n_out) {
     const int gg = tid >> 6;

@@ -221,12 +221,13 @@ def test_mxfp8_geometry_checks():
     assert P.fp_mxfp8_to_bf16(FAKE, 0, 512, FAKE + (1 << 24), 0) == P.FP_OK
     assert P.fp_mxfp8_to_bf16(FAKE, 4, 512, FAKE + 64, 0) == P.FP_ERR_INVALID_ARG  # overlap
     # vector-ALU kernel up to 4 tokens, the small-M matrix-core kernel for
-    # 5..8 (K = 5120: 80 MFMA steps of 64 k over 10 waves), nothing above 8
+    # 5..16 (K = 5120: 80 MFMA steps of 64 k over 10 waves), nothing above 16
     st, t = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 4, 1792)
     assert st == P.FP_OK and t[0] == P.FP_PATH_SKINNY and t[1] * 64 * t[2] >= 320
-    st, t = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 8, 1792)
-    assert st == P.FP_OK and t[0] == P.FP_PATH_MFMA_SMALL and t[1] * t[2] * 8 >= 640
-    st, _ = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 9, 1792)
+    for M in (8, 9, 16):
+        st, t = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, M, 1792)
+        assert st == P.FP_OK and t[0] == P.FP_PATH_MFMA_SMALL and t[1] * t[2] * 8 >= 640
+    st, _ = P.fp_default_tiling(P.FP_MXFP8, 5120, 1792, 17, 1792)
     assert st == P.FP_ERR_UNSUPPORTED
 
 
@@ -259,7 +260,8 @@ def test_nvfp4_geometry_and_refusals():
     assert st == P.FP_OK and t[0] == P.FP_PATH_SKINNY
     st, t = P.fp_default_tiling(P.FP_NVFP4, 5120, 1792, 8, 1792)
     assert st == P.FP_OK and t[0] == P.FP_PATH_MFMA_SMALL
-    assert P.fp_default_tiling(P.FP_NVFP4, 5120, 1792, 9, 1792)[0] == P.FP_ERR_UNSUPPORTED
+    assert P.fp_default_tiling(P.FP_NVFP4, 5120, 1792, 16, 1792)[1][0] == P.FP_PATH_MFMA_SMALL
+    assert P.fp_default_tiling(P.FP_NVFP4, 5120, 1792, 17, 1792)[0] == P.FP_ERR_UNSUPPORTED
     # dequantiser: argument checks before any launch
     assert P.fp_nvfp4_to_bf16(FAKE, 2, 528, 1.0, FAKE + (1 << 24), 0) == P.FP_ERR_UNSUPPORTED
     assert P.fp_nvfp4_to_bf16(FAKE, 2, 512, float("nan"), FAKE + (1 << 24), 0) == \

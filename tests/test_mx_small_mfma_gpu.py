@@ -10,8 +10,9 @@ codes to bf16 in the registers that feed v_mfma_f32_16x16x32_bf16.
 Checked, for both formats: every projection element against the oracle's
 fp64 sum under the bf16 rule at M = 1..8 (opt-in tiling and the default),
 on the DeepSeek shape, a three-way shape with strided x, ragged projections
-and the shortest K; exact data bit exact; repeats, fused vs one launch per
-projection and graph replays bitwise equal; refusals above 8 tokens.
+and the shortest K; two token halves at M = 9..16; exact data bit exact;
+repeats, fused vs one launch per projection and graph replays bitwise
+equal; refusals above 16 tokens.
 """
 import numpy as np
 import pytest
@@ -151,11 +152,26 @@ def test_mx_small_mfma_graph_replay(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("M", [9, 12, 16])
+def test_mx_small_mfma_two_token_halves(fmt, M):
+    # 9..16 tokens: the same kernel with two token halves (the default path)
+    x, ws = CASES[fmt][0](M, 90 + M)
+    fp = _plan(ws, fmt, max_M=16)
+    assert fp.query(M)[0] == P.FP_PATH_MFMA_SMALL
+    xg = to_gpu(x)
+    ys = fp(xg)
+    _check(ys, x, ws, 5120, fmt, "%s two halves M=%d" % (fmt, M))
+    assert_bitwise_equal(ys, fp(xg), "repeat")
+    assert_bitwise_equal(ys, fp.forward_separate(xg), "fused vs separate")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
 def test_mx_small_mfma_refusals(fmt):
     x, ws = CASES[fmt][0](1, 0)
-    fp = _plan(ws, fmt, max_M=16)
-    # no matrix-core path above 8 tokens for MX weights, no tile kernel
-    assert fp.set_tiling(9, _small_tiling(5120)) == P.FP_ERR_UNSUPPORTED
+    fp = _plan(ws, fmt, max_M=32)
+    # no path above 16 tokens for block-scaled weights, no tile kernel
+    assert fp.set_tiling(17, _small_tiling(5120)) == P.FP_ERR_UNSUPPORTED
+    assert fp.supported(to_gpu(CASES[fmt][0](17, 0)[0])) is False
     assert fp.set_tiling(8, (P.FP_PATH_MFMA, 4, 4, 9, 0, 2)) == P.FP_ERR_UNSUPPORTED
     assert fp.set_tiling(8, (P.FP_PATH_MFMA, 2, 0, 8, 0, 0)) == P.FP_ERR_UNSUPPORTED
     torch.cuda.synchronize()

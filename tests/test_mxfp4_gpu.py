@@ -128,9 +128,9 @@ def test_mxfp4_three_way_strided_x_graph_replay():
 
 def test_mxfp4_refusals_and_format_inference():
     x, ws = si.mxfp4_case(1, 0)
-    fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=16)  # 2720 = 17 * 160: mxfp4
+    fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=32)  # 2720 = 17 * 160: mxfp4
     assert fp.fp_dtype == P.FP_MXFP4 and fp.K == 5120
-    x9 = to_gpu(si.mxfp4_case(9, 0)[0])
-    assert fp.supported(x9) is False
+    x17 = to_gpu(si.mxfp4_case(17, 0)[0])
+    assert fp.supported(x17) is False  # above 16 tokens
     assert P.fp_plan_set_out_dtype(fp.plan, P.FP_F32) == P.FP_ERR_UNSUPPORTED
     torch.cuda.synchronize()

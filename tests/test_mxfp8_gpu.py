@@ -170,9 +170,9 @@ def test_mxfp8_rmsnorm_epilogue(M):
 
 def test_mxfp8_refusals():
     x, ws = si.mxfp8_case(1, 0)
-    fp = _plan(ws, max_M=16)
-    x9 = to_gpu(si.mxfp8_case(9, 0)[0])
-    assert fp.supported(x9) is False  # above 8 tokens
+    fp = _plan(ws, max_M=32)
+    x17 = to_gpu(si.mxfp8_case(17, 0)[0])
+    assert fp.supported(x17) is False  # above 16 tokens
     assert P.fp_plan_set_out_dtype(fp.plan, P.FP_F32) == P.FP_ERR_UNSUPPORTED
     buf = torch.empty(2, 544, dtype=torch.uint8, device="cuda")
     out = torch.empty(2, 528, dtype=torch.bfloat16, device="cuda")

@@ -82,10 +82,10 @@ def test_dequantiser_all_code_bytes(g):
                 byte, k, s, g, got[r, k], want)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16])
 def test_nvfp4_wq_a_wkv(M):
     x, ws, gs = si.nvfp4_case(M, 30 + M)
-    fp = _plan(ws, gs)
+    fp = _plan(ws, gs, max_M=16)
     xg = to_gpu(x)
     ys = fp(xg)
     _check(ys, x, ws, gs, 5120, "nvfp4 default M=%d" % M)
@@ -197,8 +197,8 @@ def test_nvfp4_rmsnorm_epilogue(M):
 
 def test_nvfp4_refusals():
     x, ws, gs = si.nvfp4_case(1, 0)
-    fp = _plan(ws, gs, max_M=16)
-    assert fp.supported(to_gpu(si.nvfp4_case(9, 0)[0])) is False  # above 8 tokens
+    fp = _plan(ws, gs, max_M=32)
+    assert fp.supported(to_gpu(si.nvfp4_case(17, 0)[0])) is False  # above 16 tokens
     assert P.fp_plan_set_tensor_scales(fp.plan, [1.0, float("inf")]) == P.FP_ERR_INVALID_ARG
     assert P.fp_plan_set_tensor_scales(fp.plan, None) == P.FP_ERR_INVALID_ARG
     assert P.fp_plan_set_out_dtype(fp.plan, P.FP_F32) == P.FP_ERR_UNSUPPORTED
