@@ -119,6 +119,10 @@ struct OutMap {
   unsigned char* y1;
   int b0, b1, e1;
   int i0;  // segment index of y0 (y1 is segment i0 + 1)
+  // segments to search for a row past e1 (0 with two segments: there is
+  // none; read here, while the loads are in flight, so that no
+  // kernel-argument load is left for the stores)
+  int n_seg;
 };
 
 __device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char* y1, int split,
@@ -131,9 +135,11 @@ __device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char*
     o.b1 = split;
     o.e1 = n_rows;
     o.i0 = 0;
+    o.n_seg = 0;
     return o;
   }
   const int n_seg = tab.n_seg;
+  o.n_seg = n_seg;
   int i0 = 0;
 #pragma unroll
   for (int i = 1; i < kMaxSeg; ++i) i0 = (i < n_seg && first_row >= tab.begin[i]) ? i : i0;
@@ -145,7 +151,7 @@ __device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char*
   o.b1 = tab.begin[i0 + 1];
   o.e1 = tab.begin[i2];
   o.i0 = i0;
-  asm volatile("" : "+s"(o.y0), "+s"(o.y1), "+s"(o.b0), "+s"(o.b1), "+s"(o.e1));
+  asm volatile("" : "+s"(o.y0), "+s"(o.y1), "+s"(o.b0), "+s"(o.b1), "+s"(o.e1), "+s"(o.n_seg));
   return o;
 }
 
@@ -160,19 +166,19 @@ __device__ __forceinline__ void store_y(const OutMap& o, const OutTable& tab, in
   unsigned char* y;
   int idx;
   int seg = 0;
-  if (row < o.b1) {
-    y = o.y0;
-    idx = m * (o.b1 - o.b0) + (row - o.b0);
-    seg = o.i0;
-  } else if (row < o.e1) {
-    y = o.y1;
-    idx = m * (o.e1 - o.b1) + (row - o.b1);
-    seg = o.i0 + 1;
+  if (row < o.e1) {
+    // the workgroup's first two segments: selects, no branch
+    const bool first = row < o.b1;
+    y = first ? o.y0 : o.y1;
+    const int b = first ? o.b0 : o.b1;
+    const int n = first ? o.b1 - o.b0 : o.e1 - o.b1;
+    idx = m * n + (row - b);
+    seg = first ? o.i0 : o.i0 + 1;
   } else {
     // a third segment inside the workgroup (more than two projections only)
     y = nullptr;
     idx = 0;
-    for (int i = 0; i < tab.n_seg; ++i) {
+    for (int i = 0; i < o.n_seg; ++i) {
       if (row >= tab.begin[i] && row < tab.begin[i + 1]) {
         y = tab.y[i];
         idx = m * (tab.begin[i + 1] - tab.begin[i]) + (row - tab.begin[i]);
@@ -197,24 +203,35 @@ __device__ __forceinline__ void store_y(const OutMap& o, const OutTable& tab, in
   }
 }
 
-// Sum of the P <= kMaxWaveParts per-wave partial sums of one output, stored
-// contiguously (slot p at q[p]; q 16-byte aligned), added in wave order.
-// The four 16-byte LDS reads are at fixed offsets; slots at and past P are
-// read (never written for this output) and left out by the selects.
-__device__ __forceinline__ float sum_wave_parts(const float* q, int P) {
-  const f32x4* q4 = reinterpret_cast<const f32x4*>(q);
-  const f32x4 a0 = q4[0], a1 = q4[1], a2 = q4[2], a3 = q4[3];
+// Cross-wave sums in LDS.  A kernel whose waves split K writes the partial
+// sums of wave part p (p < P <= kMaxWaveParts) of a block of `per` outputs
+// to smem[(block * kMaxWaveParts + p) * per + output]: the outputs of one
+// part side by side, so that the threads of consecutive outputs read
+// consecutive words.  The slots of parts P .. kMaxWaveParts - 1 hold -0.0f,
+// which leaves every fp32 sum bitwise unchanged: the reader adds all
+// kMaxWaveParts slots in part order, one chain of adds with no selects.
+
+// -0.0f into the slots of parts P .. kMaxWaveParts - 1 of `blocks` blocks
+// (every thread of the workgroup takes part; before the barrier that
+// precedes the reads).
+__device__ __forceinline__ void fill_unused_parts(float* smem, int blocks, int P, int per,
+                                                  int tid, int n_threads) {
+  const int per_block = (kMaxWaveParts - P) * per;
+  for (int i = tid; i < blocks * per_block; i += n_threads) {
+    const int b = i / per_block;
+    smem[(b * kMaxWaveParts + P) * per + (i - b * per_block)] = -0.0f;
+  }
+}
+
+// The sum over the wave parts of one output, slot p at q[p * stride], in
+// part order.
+__device__ __forceinline__ float sum_wave_parts(const float* q, int stride) {
   float v[kMaxWaveParts];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = a0[i];
-    v[4 + i] = a1[i];
-    v[8 + i] = a2[i];
-    v[12 + i] = a3[i];
-  }
+  for (int i = 0; i < kMaxWaveParts; ++i) v[i] = q[i * stride];
   float sum = v[0];
 #pragma unroll
-  for (int pp = 1; pp < kMaxWaveParts; ++pp) sum = pp < P ? sum + v[pp] : sum;
+  for (int i = 1; i < kMaxWaveParts; ++i) sum += v[i];
   return sum;
 }
 

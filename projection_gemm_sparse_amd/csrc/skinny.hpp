@@ -23,9 +23,9 @@
 //      in element order;
 //   2. across the 64 lanes of the wave by the transpose reduce of
 //      common.hpp (one fixed tree of lane pairings);
-//   3. across the P waves of the row group in LDS, in wave order (each
-//      output's P wave sums sit in 16 consecutive slots, read as four
-//      16-byte vectors);
+//   3. across the P waves of the row group in LDS, in wave order (the
+//      sums of one wave part side by side, so that the threads of
+//      consecutive outputs read consecutive words);
 //   4. with S > 1, across the S workgroups of the row block: each writes its
 //      partial sums to the workspace, and the last workgroup to arrive
 //      (arrival counter) adds the S partials in slice order, stores the
@@ -200,6 +200,8 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   float* partial = a.partial;
   uint32_t* counters = a.counters;
   if (Sv > 1) asm volatile("" : "+s"(partial), "+s"(counters));
+  // the cross-wave slots of absent wave parts read as -0.0f
+  if (P > 1 || Sv > 1 || PAIRS) fill_unused_parts(smem, Gv, P, VP, tid, Gv * P * 64);
   __builtin_amdgcn_sched_barrier(0);
   // activations past M or past K count as zero
 #pragma unroll
@@ -293,12 +295,12 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
     }
     return;
   }
-  // wave sums to LDS, transposed: output idx of row group gq owns 16
-  // consecutive slots, slot p for wave p
-  float* red = smem + gq * VP * kMaxWaveParts + p;
+  // wave sums to LDS, [row group][wave part][output]: the VP outputs of one
+  // wave part side by side
+  float* red = smem + (gq * kMaxWaveParts + p) * VP;
   if (lane % LSTRIDE == 0) {
 #pragma unroll
-    for (int q = 0; q < QV; ++q) red[(q + QV * (lane / LSTRIDE)) * kMaxWaveParts] = v[q];
+    for (int q = 0; q < QV; ++q) red[q + QV * (lane / LSTRIDE)] = v[q];
   }
   __syncthreads();
 
@@ -312,11 +314,12 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
     const int m = idx - r * MT;
     const int row = row_base + g2 * RW + r;
     if (m < M && row < n_rows) {
-      const float sum = sum_wave_parts(smem + (g2 * VP + idx) * kMaxWaveParts, P);
+      const float* q0 = smem + g2 * kMaxWaveParts * VP + idx;
+      const float sum = sum_wave_parts(q0, VP);
       if constexpr (PAIRS) {
         // even logical rows: gate row j, its up row in the next slot
         if ((r & 1) == 0) {
-          const float u_sum = sum_wave_parts(smem + (g2 * VP + idx + MT) * kMaxWaveParts, P);
+          const float u_sum = sum_wave_parts(q0 + MT, VP);
           store_pair(y0, split, row, m, sum, u_sum);
         }
       } else if (Sv == 1) {

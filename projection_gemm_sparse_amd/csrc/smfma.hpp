@@ -63,6 +63,36 @@ constexpr int smfma_max_threads(int kt, int mh = 1) {
   return max_threads_for_regs(4 * kt * (mh + 1) + 24 + 16 * (mh - 1));
 }
 
+// Output stage of both small-M kernels (not gate/up).  The cross-wave
+// slots hold, per block gh = g2 * MH + h (row group g2, token half h) and
+// wave part, the 2 x 64 sums [sub-slice][row][token]; the outputs of a block
+// go in chunks of 32 (chunk c & 1 of block c / 2: outputs o = 32 (c & 1)
+// .. + 31, row o / 8, token 8 h + o % 8), one chunk per wave at a time.
+// Lanes 0..31 add sub-slice 0 of their output over the wave parts, lanes
+// 32..63 sub-slice 1, and one lane swap (v_permlane32_swap) brings the two
+// together: sub-slice 0 + sub-slice 1.
+template <int MH, bool SCALED>
+__device__ __forceinline__ void smfma_store_outputs(const float* smem, int Gv, int n_waves,
+                                                    int wave, int lane, int RT, int row_base,
+                                                    int M, int n_rows, const OutMap& om,
+                                                    const OutTable& tab) {
+  const int n_chunks = Gv * MH * 2;
+  for (int c = wave; c < n_chunks; c += n_waves) {
+    const int gh = c >> 1;
+    const int o = 32 * (c & 1) + (lane & 31);
+    const float* q = smem + gh * kMaxWaveParts * 128 + (lane >> 5) * 64 + o;
+    const float part = sum_wave_parts(q, 128);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                     __float_as_uint(part), false, false);
+    const int g2 = gh / MH;
+    const int m = 8 * (gh - g2 * MH) + (o & 7);
+    const int r = o >> 3;
+    const int row = row_base + g2 * RT + r;
+    if (lane < 32 && r < RT && m < M && row < n_rows)
+      store_y<true, SCALED>(om, tab, row, m, __uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+  }
+}
+
 // Leading scalars preloaded into SGPRs (see skinny_kernel for w, x, y0,
 // y1, ldx, n_rows, kc, M, split); geo = RT | PK << 8 | G << 16.
 // PAIRS: a gate/up launch (rows taken in pairs, see pair_row; RT even)
@@ -74,7 +104,7 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
              unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
              int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
   static_assert(MH == 1 || (MH == 2 && !PAIRS), "token halves");
-  extern __shared__ float smem[];  // [G][MH][2][8][8][16]
+  extern __shared__ float smem[];  // [G][MH][16 wave parts][2][8][8]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,6 +192,7 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   }
   __builtin_amdgcn_sched_barrier(0);
   const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
+  fill_unused_parts(smem, Gv * MH, PK, 128, tid, Gv * PK * 64);
   __builtin_amdgcn_sched_barrier(0);
   // 2. MFMA steps in order; chunks past K contribute zero
   f32x4 acc[MH];
@@ -185,57 +216,41 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
 
   // 3. the diagonal blocks to LDS: lane (i16, g) holds D[4g + v][i16]; the
   //    D row's sub-slice is (4g + v) / 8 = g / 2, the column's is i16 / 8.
-  //    Layout [G][half][sub-slice][row][token][16 wave slots]: the PK wave
-  //    sums of one (half, sub-slice, row, token) are contiguous.
+  //    Layout [G][half][wave part][sub-slice][row][token]: the 128 sums of
+  //    one wave part side by side, so that the threads of consecutive
+  //    outputs read consecutive words.
   if ((g >> 1) == sub) {
 #pragma unroll
     for (int h = 0; h < MH; ++h) {
-      float* red = smem + (((g2 * MH + h) * 2 + sub) * 64 + r8) * kMaxWaveParts + p;
+      float* red = smem + ((g2 * MH + h) * kMaxWaveParts + p) * 128 + sub * 64 + r8;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = (4 * g + v) & 7;
-        red[r * 8 * kMaxWaveParts] = acc[h][v];
+        red[r * 8] = acc[h][v];
       }
     }
   }
   __syncthreads();
 
-  // 4. one thread per output: each sub-slice over the PK waves in wave
-  //    order, then sub-slice 0 + sub-slice 1
-  if constexpr (MH == 2) {
-    const int n_out = Gv * 128;
-    for (int o = tid; o < n_out; o += Gv * PK * 64) {
-      const int gh = o >> 6;  // g2 * 2 + half
-      const int r = (o >> 3) & 7;
-      const int m = (gh & 1) * 8 + (o & 7);
-      const int row = row_base + (gh >> 1) * RT + r;
-      if (r < RT && m < M && row < n_rows) {
-        const float* q0 = smem + ((gh * 2 + 0) * 64 + (o & 63)) * kMaxWaveParts;
-        const float* q1 = smem + ((gh * 2 + 1) * 64 + (o & 63)) * kMaxWaveParts;
-        store_y<true>(om, a.out, row, m, sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK));
-      }
-    }
-    return;
-  }
-  const int n_out = Gv * 64;
-  if (tid < n_out) {
-    const int gg = tid >> 6;
-    const int r = (tid >> 3) & 7;
-    const int m = tid & 7;
-    const int row = row_base + gg * RT + r;
-    if (r < RT && m < M && row < n_rows) {
-      const float* q0 = smem + ((gg * 2 + 0) * 64 + r * 8 + m) * kMaxWaveParts;
-      const float* q1 = smem + ((gg * 2 + 1) * 64 + r * 8 + m) * kMaxWaveParts;
-      const float sum = sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK);
-      if constexpr (PAIRS) {
-        // even logical rows: gate row j, its up row is tile row r + 1
-        if ((r & 1) == 0) {
-          const float u_sum = sum_wave_parts(q0 + 8 * kMaxWaveParts, PK) +
-                              sum_wave_parts(q1 + 8 * kMaxWaveParts, PK);
-          store_pair(y0, split, row, m, sum, u_sum);
-        }
-      } else {
-        store_y<true>(om, a.out, row, m, sum);
+  // 4. per output: each sub-slice over the PK wave parts in part order,
+  //    then sub-slice 0 + sub-slice 1
+  if constexpr (!PAIRS) {
+    smfma_store_outputs<MH, false>(smem, Gv, Gv * PK, wave, lane, RT, row_base, M, n_rows, om,
+                                   a.out);
+  } else {
+    // gate/up: one thread per output; even logical rows are gate rows j,
+    // the up row is tile row r + 1
+    const int n_out = Gv * 64;
+    if (tid < n_out) {
+      const int gg = tid >> 6;
+      const int r = (tid >> 3) & 7;
+      const int m = tid & 7;
+      const int row = row_base + gg * RT + r;
+      if (r < RT && m < M && row < n_rows && (r & 1) == 0) {
+        const float* q0 = smem + gg * kMaxWaveParts * 128 + r * 8 + m;
+        const float sum = sum_wave_parts(q0, 128) + sum_wave_parts(q0 + 64, 128);
+        const float u_sum = sum_wave_parts(q0 + 8, 128) + sum_wave_parts(q0 + 64 + 8, 128);
+        store_pair(y0, split, row, m, sum, u_sum);
       }
     }
   }
@@ -276,7 +291,7 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
   constexpr uint32_t UB = FMT == 8 ? 8u : 4u;  // code bytes per unit
   static_assert(KT % G == 0, "whole step groups");
   static_assert(MH == 1 || MH == 2, "token halves");
-  extern __shared__ float smem[];  // [G][MH][2][8][8][16]
+  extern __shared__ float smem[];  // [G][MH][16 wave parts][2][8][8]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -354,6 +369,7 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
   }
   __builtin_amdgcn_sched_barrier(0);
   const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
+  fill_unused_parts(smem, Gv * MH, PK, 128, tid, Gv * PK * 64);
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. step groups in order, steps in order inside a group; units past K
@@ -414,45 +430,19 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
   if ((g >> 1) == sub) {
 #pragma unroll
     for (int h = 0; h < MH; ++h) {
-      float* red = smem + (((g2 * MH + h) * 2 + sub) * 64 + r8) * kMaxWaveParts + p;
+      float* red = smem + ((g2 * MH + h) * kMaxWaveParts + p) * 128 + sub * 64 + r8;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = (4 * g + v) & 7;
-        red[r * 8 * kMaxWaveParts] = acc[h][v];
+        red[r * 8] = acc[h][v];
       }
     }
   }
   __syncthreads();
 
-  // 4. one thread per output: each sub-slice over the PK waves in wave
-  //    order, then sub-slice 0 + sub-slice 1
-  if constexpr (MH == 2) {
-    const int n_out = Gv * 128;
-    for (int o = tid; o < n_out; o += Gv * PK * 64) {
-      const int gh = o >> 6;  // g2 * 2 + half
-      const int r = (o >> 3) & 7;
-      const int m = (gh & 1) * 8 + (o & 7);
-      const int row = row_base + (gh >> 1) * RT + r;
-      if (r < RT && m < M && row < n_rows) {
-        const float* q0 = smem + ((gh * 2 + 0) * 64 + (o & 63)) * kMaxWaveParts;
-        const float* q1 = smem + ((gh * 2 + 1) * 64 + (o & 63)) * kMaxWaveParts;
-        store_y<true, NV>(om, a.out, row, m, sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK));
-      }
-    }
-    return;
-  }
-  const int n_out = Gv * 64;
-  if (tid < n_out) {
-    const int gg = tid >> 6;
-    const int r = (tid >> 3) & 7;
-    const int m = tid & 7;
-    const int row = row_base + gg * RT + r;
-    if (r < RT && m < M && row < n_rows) {
-      const float* q0 = smem + ((gg * 2 + 0) * 64 + r * 8 + m) * kMaxWaveParts;
-      const float* q1 = smem + ((gg * 2 + 1) * 64 + r * 8 + m) * kMaxWaveParts;
-      store_y<true, NV>(om, a.out, row, m, sum_wave_parts(q0, PK) + sum_wave_parts(q1, PK));
-    }
-  }
+  // 4. per output: each sub-slice over the PK wave parts in part order,
+  //    then sub-slice 0 + sub-slice 1
+  smfma_store_outputs<MH, NV>(smem, Gv, Gv * PK, wave, lane, RT, row_base, M, n_rows, om, a.out);
 }
 
 }  // namespace fp

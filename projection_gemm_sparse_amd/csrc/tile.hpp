@@ -336,6 +336,8 @@ splitk_reduce_kernel(const float* __restrict__ partial, int32_t n_rows, int32_t 
   om.b0 = tab.begin[seg];
   om.b1 = tab.begin[seg + 1];
   om.e1 = tab.begin[seg + 1];
+  om.i0 = seg;
+  om.n_seg = 0;  // the row lies in segment seg
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float vj = sum[j];
