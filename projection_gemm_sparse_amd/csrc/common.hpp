@@ -118,24 +118,33 @@ struct OutMap {
   unsigned char* y0;
   unsigned char* y1;
   int b0, b1, e1;
-  int i0;  // segment index of y0 (y1 is segment i0 + 1)
   // segments to search for a row past e1 (0 with two segments: there is
   // none; read here, while the loads are in flight, so that no
   // kernel-argument load is left for the stores)
   int n_seg;
+  // tensor scales of y0's and y1's segments (SCALED: NVFP4 weights; 1
+  // otherwise), read and pinned at the start for the same reason
+  float ts0, ts1;
 };
 
+template <bool SCALED = false>
 __device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char* y1, int split,
                                                int n_rows, const OutTable& tab, int first_row) {
   OutMap o;
+  o.ts0 = 1.0f;
+  o.ts1 = 1.0f;
   if (split >= 0) {
     o.y0 = y0;
     o.y1 = y1;
     o.b0 = 0;
     o.b1 = split;
     o.e1 = n_rows;
-    o.i0 = 0;
     o.n_seg = 0;
+    if constexpr (SCALED) {
+      o.ts0 = tab.tscale[0];
+      o.ts1 = tab.tscale[1];
+      asm volatile("" : "+s"(o.ts0), "+s"(o.ts1));
+    }
     return o;
   }
   const int n_seg = tab.n_seg;
@@ -150,7 +159,11 @@ __device__ __forceinline__ OutMap make_out_map(unsigned char* y0, unsigned char*
   o.b0 = tab.begin[i0];
   o.b1 = tab.begin[i0 + 1];
   o.e1 = tab.begin[i2];
-  o.i0 = i0;
+  if constexpr (SCALED) {
+    o.ts0 = tab.tscale[i0];
+    o.ts1 = tab.tscale[i1];
+    asm volatile("" : "+s"(o.ts0), "+s"(o.ts1));
+  }
   asm volatile("" : "+s"(o.y0), "+s"(o.y1), "+s"(o.b0), "+s"(o.b1), "+s"(o.e1), "+s"(o.n_seg));
   return o;
 }
@@ -165,7 +178,7 @@ __device__ __forceinline__ void store_y(const OutMap& o, const OutTable& tab, in
                                         float v) {
   unsigned char* y;
   int idx;
-  int seg = 0;
+  float ts = 1.0f;
   if (row < o.e1) {
     // the workgroup's first two segments: selects, no branch
     const bool first = row < o.b1;
@@ -173,7 +186,7 @@ __device__ __forceinline__ void store_y(const OutMap& o, const OutTable& tab, in
     const int b = first ? o.b0 : o.b1;
     const int n = first ? o.b1 - o.b0 : o.e1 - o.b1;
     idx = m * n + (row - b);
-    seg = first ? o.i0 : o.i0 + 1;
+    ts = first ? o.ts0 : o.ts1;
   } else {
     // a third segment inside the workgroup (more than two projections only)
     y = nullptr;
@@ -182,14 +195,14 @@ __device__ __forceinline__ void store_y(const OutMap& o, const OutTable& tab, in
       if (row >= tab.begin[i] && row < tab.begin[i + 1]) {
         y = tab.y[i];
         idx = m * (tab.begin[i + 1] - tab.begin[i]) + (row - tab.begin[i]);
-        seg = i;
+        ts = tab.tscale[i];
       }
     }
     if (y == nullptr) return;
   }
   if constexpr (SCALED) {
 #pragma clang fp contract(off)
-    v = v * tab.tscale[seg < kMaxSeg ? seg : kMaxSeg - 1];
+    v = v * ts;
   }
   // global (not generic) address space: a global_store, no aperture check
   typedef __attribute__((address_space(1))) uint16_t g_u16;

@@ -196,7 +196,7 @@ skinny_kernel(const unsigned char* __restrict__ w, const unsigned char* __restri
   __builtin_amdgcn_sched_barrier(0);
   // where this workgroup's outputs go, and the split-K workspace, resolved
   // while the loads are in flight
-  const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
+  const OutMap om = make_out_map<NV4>(y0, y1, split, n_rows, a.out, row_base);
   float* partial = a.partial;
   uint32_t* counters = a.counters;
   if (Sv > 1) asm volatile("" : "+s"(partial), "+s"(counters));

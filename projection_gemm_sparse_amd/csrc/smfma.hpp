@@ -66,10 +66,11 @@ constexpr int smfma_max_threads(int kt, int mh = 1) {
 // Output stage of both small-M kernels (not gate/up).  The cross-wave
 // slots hold, per block gh = g2 * MH + h (row group g2, token half h) and
 // wave part, the 2 x 64 sums [sub-slice][row][token]; the outputs of a block
-// go in chunks of 32 (chunk c & 1 of block c / 2: outputs o = 32 (c & 1)
-// .. + 31, row o / 8, token 8 h + o % 8), one chunk per wave at a time.
-// Lanes 0..31 add sub-slice 0 of their output over the wave parts, lanes
-// 32..63 sub-slice 1, and one lane swap (v_permlane32_swap) brings the two
+// go in chunks of 32, four tokens x the eight rows (chunk c & 1 of block
+// c / 2: tokens 8 h + 4 (c & 1) .. + 3), one chunk per wave at a time, so
+// that one store instruction writes each token's rows of the tile.  Lanes
+// 0..31 add sub-slice 0 of their output over the wave parts, lanes 32..63
+// sub-slice 1, and one lane swap (v_permlane32_swap) brings the two
 // together: sub-slice 0 + sub-slice 1.
 template <int MH, bool SCALED>
 __device__ __forceinline__ void smfma_store_outputs(const float* smem, int Gv, int n_waves,
@@ -79,14 +80,14 @@ __device__ __forceinline__ void smfma_store_outputs(const float* smem, int Gv, i
   const int n_chunks = Gv * MH * 2;
   for (int c = wave; c < n_chunks; c += n_waves) {
     const int gh = c >> 1;
-    const int o = 32 * (c & 1) + (lane & 31);
-    const float* q = smem + gh * kMaxWaveParts * 128 + (lane >> 5) * 64 + o;
+    const int r = lane & 7;
+    const int mt = 4 * (c & 1) + ((lane >> 3) & 3);  // token in the half
+    const float* q = smem + gh * kMaxWaveParts * 128 + (lane >> 5) * 64 + r * 8 + mt;
     const float part = sum_wave_parts(q, 128);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
                                                      __float_as_uint(part), false, false);
     const int g2 = gh / MH;
-    const int m = 8 * (gh - g2 * MH) + (o & 7);
-    const int r = o >> 3;
+    const int m = 8 * (gh - g2 * MH) + mt;
     const int row = row_base + g2 * RT + r;
     if (lane < 32 && r < RT && m < M && row < n_rows)
       store_y<true, SCALED>(om, tab, row, m, __uint_as_float(sw[0]) + __uint_as_float(sw[1]));
@@ -368,7 +369,7 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
+  const OutMap om = make_out_map<NV>(y0, y1, split, n_rows, a.out, row_base);
   fill_unused_parts(smem, Gv * MH, PK, 128, tid, Gv * PK * 64);
   __builtin_amdgcn_sched_barrier(0);
 

@@ -336,8 +336,9 @@ splitk_reduce_kernel(const float* __restrict__ partial, int32_t n_rows, int32_t 
   om.b0 = tab.begin[seg];
   om.b1 = tab.begin[seg + 1];
   om.e1 = tab.begin[seg + 1];
-  om.i0 = seg;
   om.n_seg = 0;  // the row lies in segment seg
+  om.ts0 = 1.0f;
+  om.ts1 = 1.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float vj = sum[j];
