@@ -859,9 +859,18 @@ struct LaunchRows {
   float scale[fp::kMaxSeg];  // segment tensor scales (NVFP4)
 };
 
+// Two token halves: up to 12 tokens the loads of each step go in turn
+// (first half, weights, second half), above that every activation first.
+constexpr int kSmfmaInterleaveMaxM = 12;
+
 template <int KT>
-const void* smfma_fn_kt(bool pairs, int mt) {
-  if (mt == 16) return pairs ? nullptr : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 2>);
+const void* smfma_fn_kt(bool pairs, int mt, int64_t M) {
+  if (mt == 16) {
+    if (pairs) return nullptr;
+    return M <= kSmfmaInterleaveMaxM
+               ? reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 2, false>)
+               : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 2>);
+  }
   return pairs ? reinterpret_cast<const void*>(&fp::smfma_kernel<KT, true>)
                : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false>);
 }
@@ -883,16 +892,16 @@ const void* smfma_mx_fn_fmt(int32_t dtype, int kt) {
                              : smfma_mx_fn<fp::kFmtNv4, MH>(kt);
 }
 
-const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype) {
+const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype, int64_t M) {
   if (dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4) {
     if (pairs) return nullptr;
     return t.mt == 8 ? smfma_mx_fn_fmt<1>(dtype, t.chunks)
                      : smfma_mx_fn_fmt<2>(dtype, t.chunks);
   }
   switch (t.chunks) {
-    case 4: return smfma_fn_kt<4>(pairs, t.mt);
-    case 8: return smfma_fn_kt<8>(pairs, t.mt);
-    case 16: return smfma_fn_kt<16>(pairs, t.mt);
+    case 4: return smfma_fn_kt<4>(pairs, t.mt, M);
+    case 8: return smfma_fn_kt<8>(pairs, t.mt, M);
+    case 16: return smfma_fn_kt<16>(pairs, t.mt, M);
     default: return nullptr;
   }
 }
@@ -932,8 +941,8 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   if (t.path == FP_PATH_MFMA_SMALL) {
     geo_a = t.rows | (t.kparts << 8) | (t.groups << 16);
     const int64_t R = (int64_t)t.rows * t.groups;
-    return launch(smfma_fn(t, pairs, p->dtype), ceil_div(lr.n_rows, R), t.groups * t.kparts * 64,
-                  smfma_lds(t), args, stream);
+    return launch(smfma_fn(t, pairs, p->dtype, M_a), ceil_div(lr.n_rows, R),
+                  t.groups * t.kparts * 64, smfma_lds(t), args, stream);
   }
   if (pairs && t.path != FP_PATH_SKINNY) return FP_ERR_UNSUPPORTED;
   if (t.path == FP_PATH_MFMA) {

@@ -98,8 +98,10 @@ __device__ __forceinline__ void smfma_store_outputs(const float* smem, int Gv, i
 // y1, ldx, n_rows, kc, M, split); geo = RT | PK << 8 | G << 16.
 // PAIRS: a gate/up launch (rows taken in pairs, see pair_row; RT even)
 // that writes silu(gate) * up instead of the projections.  MH: token halves
-// (1: M <= 8, 2: M <= 16).
-template <int KT, bool PAIRS = false, int MH = 1>
+// (1: M <= 8, 2: M <= 16).  XFIRST (two halves): every activation load
+// before the weights (the fuller second halves) instead of each step's
+// first-half, weight and second-half chunks in turn.
+template <int KT, bool PAIRS = false, int MH = 1, bool XFIRST = true>
 __global__ void __launch_bounds__(smfma_max_threads(KT, MH))
 smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
              unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
@@ -149,7 +151,8 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   //    Measured on MI355X at [1792, 5120]: with one token half, issuing each
   //    step's activation and weight chunks in turn beats all activations
   //    first (M = 8: 5.9 vs 6.15 us; M = 4: 5.5 vs 5.95); with two halves
-  //    the activations first stay faster (M = 16: 7.45 vs 7.7).
+  //    that order pays only while the second half is at most half full
+  //    (XFIRST picks; a branch on M inside one kernel slowed both orders).
   u32x4 xv[MH][KT];
   u32x4 wv[KT];
   {
@@ -174,9 +177,22 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
         wv[t] = __builtin_nontemporal_load(wrow + cc);
         __builtin_amdgcn_sched_barrier(0);
       }
+    } else if constexpr (!XFIRST) {
+      // two halves, the second at most half full: per step the first
+      // half's chunk, the weight chunk, the second half's chunk (M = 9:
+      // 6.69 vs 6.96 us with the activations first)
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const int c = cw + 8 * t + cl;
+        const int cc = c < kc ? c : kc - 1;
+        xv[0][t] = xrow[0][cc];
+        wv[t] = __builtin_nontemporal_load(wrow + cc);
+        xv[MH - 1][t] = xrow[MH - 1][cc];
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else {
-      // two halves: every activation chunk first (twice the weight bytes,
-      // from L2), then the weights
+      // two fuller halves: every activation chunk first (twice the weight
+      // bytes, from L2), then the weights (M = 16: 7.2 vs 7.6 us)
 #pragma unroll
       for (int h = 0; h < MH; ++h)
 #pragma unroll
