@@ -94,7 +94,9 @@ def kernel_name(P, M: int, tiling) -> str:
         mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
         return "fp::skinny_kernel<%d, %d, %d, true, 0>" % (mt, rows, chunks)
     if path == P.FP_PATH_MFMA_SMALL:
-        return "fp::smfma_kernel<%d, false, %d>" % (chunks, 1 if M <= 8 else 2)
+        # token halves; with two, up to 12 tokens the interleaved load order
+        return "fp::smfma_kernel<%d, false, %d, %s>" % (
+            chunks, 1 if M <= 8 else 2, "false" if 8 < M <= 12 else "true")
     mt16 = next(b for b in (1, 2, 4, 8, 16) if 16 * b >= M)
     cs = 4 if chunks in (8, 16) else 5
     return "fp::tile_kernel<%d, %d, %d, %d>" % (mt16, kparts, cs, chunks // cs)
