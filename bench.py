@@ -326,7 +326,7 @@ def host_info():
 
 def crossover(path, P, torch, dev, plans, n_copies):
     """Per token count, every kernel path that serves it, on the rotated
-    pool (plans are made for max_M = 8, so this builds a second pool)."""
+    pool (plans are made for max_M = 8, so a second pool is built)."""
     import synthetic_inputs as si
     del plans
     torch.cuda.empty_cache()

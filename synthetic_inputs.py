@@ -17,7 +17,7 @@ Shapes follow the pages' projections: DeepSeek-V4.1 wq_a (5120 -> 1280) with
 wkv (5120 -> 512) from "tinygemm2 for the DeepSeek-V4.1 hidden-state
 projections" (TensorRT-LLM PR #20636), Description; the DS-V3.2 indexer
 wk + weights_proj in FP32 from PR #12055 (dimensions not on the page:
-K=7168 with [128, 64] rows is this build's reading); GLM's fused-A
+K=7168 with [128, 64] rows is a reading, not a figure of the page); GLM's fused-A
 (q_a 2048 + compressed KV + rope, hidden 6144) from the fused-A commit of
 PR #20502, with the split [2048, 576, 128].
 """
