@@ -49,11 +49,15 @@ constexpr int kDefaultSmallMfmaMinM = 3;
 // MX weights: measured at the same shape, the vector-ALU kernel stays
 // faster through M = 4 (MXFP8 4.95 vs 5.36 us, MXFP4 4.37 vs 4.60).
 constexpr int kDefaultSmallMfmaMinMMx = 5;
-int default_small_mfma_min_m(int32_t dtype) {
-  return dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4 ? kDefaultSmallMfmaMinMMx
-                                                                      : kDefaultSmallMfmaMinM;
-}
 constexpr int kCus = 256;           // MI355X compute units
+// bf16 launches of more rows than one 8-row tile per CU (the small-M kernel
+// then runs more than one workgroup per CU) keep the vector-ALU kernel
+// through M = 4 as well: measured at the three-way shape (K = 6144, 2752
+// rows) 7.84 vs 8.04-8.20 us at M = 3 and 7.99 vs 8.20 at M = 4.
+int default_small_mfma_min_m(int32_t dtype, int64_t n_total) {
+  if (dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4) return kDefaultSmallMfmaMinMMx;
+  return n_total > 8 * (int64_t)kCus ? kDefaultSmallMfmaMinMMx : kDefaultSmallMfmaMinM;
+}
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // rows and chunks per row, 32-bit indexing
 
 thread_local int32_t g_last_hip = 0;
@@ -563,7 +567,7 @@ void scratch_plan(fp_plan_s* tmp, int32_t dtype, int64_t K, int64_t n_total,
   tmp->n_total = n_total;
   tmp->max_M = max_M;
   tmp->mfma_min_m = kDefaultMfmaMinM;
-  tmp->small_mfma_min_m = default_small_mfma_min_m(dtype);
+  tmp->small_mfma_min_m = default_small_mfma_min_m(dtype, n_total);
   tmp->ws_bytes = SIZE_MAX;
 }
 
@@ -1093,7 +1097,7 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
   p->max_M = max_M;
   p->mfma_min_m = kDefaultMfmaMinM;
   for (int i = 0; i < FP_MAX_PROJ; ++i) p->tscale[i] = 1.0f;
-  p->small_mfma_min_m = default_small_mfma_min_m(dtype);
+  p->small_mfma_min_m = default_small_mfma_min_m(dtype, n_total);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // concatenate: W_cat[off_i + r, :] = W_i[r, :]

@@ -181,6 +181,14 @@ def test_default_crossover():
         assert P.fp_default_tiling(1, 7168, 192, M, 192)[1][0] in (1, 2)
     for M in (17, 32, 64, 128):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA
+    # more rows than one 8-row tile per CU (the three-way fused-A shape):
+    # the vector-ALU kernel through M = 4
+    for M in range(1, 5):
+        assert P.fp_default_tiling(0, 6144, 2752, M, 2752)[1][0] == P.FP_PATH_SKINNY
+    for M in range(5, 17):
+        assert P.fp_default_tiling(0, 6144, 2752, M, 2752)[1][0] == P.FP_PATH_MFMA_SMALL
+    assert P.fp_default_tiling(0, 5120, 2048, 3, 2048)[1][0] == P.FP_PATH_MFMA_SMALL
+    assert P.fp_default_tiling(0, 5120, 2049, 3, 2049)[1][0] == P.FP_PATH_SKINNY
 
 
 def test_epilogue_argument_checks_before_any_hip_call():
