@@ -53,15 +53,17 @@ N = (1280, 512)
 MS = (1, 2, 3, 4, 5, 6, 7, 8)
 
 
-KERNEL_SOURCES = ("projection_gemm_sparse_amd/csrc/common.hpp",
-                  "projection_gemm_sparse_amd/csrc/skinny.hpp",
-                  "projection_gemm_sparse_amd/csrc/smfma.hpp",
-                  "projection_gemm_sparse_amd/csrc/tile.hpp",
-                  "projection_gemm_sparse_amd/csrc/tile_ring.hpp",
-                  "projection_gemm_sparse_amd/csrc/epilogue.hpp",
-                  "projection_gemm_sparse_amd/csrc/mxfp8.hpp",
-                  "projection_gemm_sparse_amd/csrc/stream.hpp",
-                  "projection_gemm_sparse_amd/csrc/api.hip")
+def _kernel_sources():
+    """The library's HIP sources and headers, in a fixed order (the digest
+    that gates recorded counter values)."""
+    import glob
+    d = os.path.join(ROOT, "projection_gemm_sparse_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(d, "*.hip")) + glob.glob(os.path.join(d, "*.hpp")) +
+                   glob.glob(os.path.join(d, "*.h")))
+    return tuple(os.path.relpath(f, ROOT) for f in files)
+
+
+KERNEL_SOURCES = _kernel_sources()
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

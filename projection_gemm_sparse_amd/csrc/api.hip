@@ -27,6 +27,7 @@
 #include "epilogue.hpp"
 #include "mxfp8.hpp"
 #include "stream.hpp"
+#include "kernels.h"
 
 namespace {
 
@@ -595,229 +596,14 @@ size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) 
 }
 
 // ------------------------------------------------------------------ kernels
-// Gate/up launches (PAIRS): bf16, an even number of rows per wave, one or
-// two chunks per lane.
-template <int MT, int CJ>
-const void* skinny_pairs_fn_rw(int rw) {
-  switch (rw) {
-    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, fp::kVarPairs>);
-    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, fp::kVarPairs>);
-    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, true, fp::kVarPairs>);
-    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, fp::kVarPairs>);
-    default: return nullptr;
-  }
-}
-
-template <int MT>
-const void* skinny_pairs_fn_cj(int cj, int rw) {
-  switch (cj) {
-    case 1: return skinny_pairs_fn_rw<MT, 1>(rw);
-    case 2: return skinny_pairs_fn_rw<MT, 2>(rw);
-    default: return nullptr;
-  }
-}
-
-const void* skinny_pairs_fn(int mt, int cj, int rw) {
-  switch (mt) {
-    case 1: return skinny_pairs_fn_cj<1>(cj, rw);
-    case 2: return skinny_pairs_fn_cj<2>(cj, rw);
-    case 4: return skinny_pairs_fn_cj<4>(cj, rw);
-    case 8: return skinny_pairs_fn_cj<8>(cj, rw);
-    default: return nullptr;
-  }
-}
-
-// fp32 outputs from bf16 operands (router logits): up to 16 tokens, one or
-// two chunks per lane, at most 64 outputs per lane.
-template <int MT, int CJ>
-const void* skinny_f32out_fn_rw(int rw) {
-  switch (rw) {
-    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, true, fp::kVarF32Out>);
-    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, fp::kVarF32Out>);
-    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, fp::kVarF32Out>);
-    default: break;
-  }
-  if constexpr (MT <= 8) {
-    if (rw == 8) return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, fp::kVarF32Out>);
-  }
-  return nullptr;
-}
-
-template <int MT>
-const void* skinny_f32out_fn_cj(int cj, int rw) {
-  switch (cj) {
-    case 1: return skinny_f32out_fn_rw<MT, 1>(rw);
-    case 2: return skinny_f32out_fn_rw<MT, 2>(rw);
-    default: return nullptr;
-  }
-}
-
-const void* skinny_f32out_fn(int mt, int cj, int rw) {
-  switch (mt) {
-    case 1: return skinny_f32out_fn_cj<1>(cj, rw);
-    case 2: return skinny_f32out_fn_cj<2>(cj, rw);
-    case 4: return skinny_f32out_fn_cj<4>(cj, rw);
-    case 8: return skinny_f32out_fn_cj<8>(cj, rw);
-    case 16: return skinny_f32out_fn_cj<16>(cj, rw);
-    default: return nullptr;
-  }
-}
-
-// MXFP8 / MXFP4 weights (VAR kVarMx8 / kVarMx4): up to 8 tokens, one or two
-// units per lane.
-template <int VAR, int MT, int CJ>
-const void* skinny_mx_fn_rw(int rw) {
-  switch (rw) {
-    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, true, VAR>);
-    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, true, VAR>);
-    case 3: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 3, CJ, true, VAR>);
-    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, true, VAR>);
-    case 5: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 5, CJ, true, VAR>);
-    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, true, VAR>);
-    case 7: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 7, CJ, true, VAR>);
-    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, true, VAR>);
-    default: return nullptr;
-  }
-}
-
-template <int VAR, int MT>
-const void* skinny_mx_fn_cj(int cj, int rw) {
-  switch (cj) {
-    case 1: return skinny_mx_fn_rw<VAR, MT, 1>(rw);
-    case 2: return skinny_mx_fn_rw<VAR, MT, 2>(rw);
-    default: return nullptr;
-  }
-}
-
-template <int VAR>
-const void* skinny_mx_fn(int mt, int cj, int rw) {
-  switch (mt) {
-    case 1: return skinny_mx_fn_cj<VAR, 1>(cj, rw);
-    case 2: return skinny_mx_fn_cj<VAR, 2>(cj, rw);
-    case 4: return skinny_mx_fn_cj<VAR, 4>(cj, rw);
-    case 8: return skinny_mx_fn_cj<VAR, 8>(cj, rw);
-    default: return nullptr;
-  }
-}
-
-template <int MT, int CJ, bool BF16>
-const void* skinny_fn_rw(int rw) {
-  switch (rw) {
-    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, BF16>);
-    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, BF16>);
-    case 3: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 3, CJ, BF16>);
-    case 4: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 4, CJ, BF16>);
-    case 5: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 5, CJ, BF16>);
-    case 6: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 6, CJ, BF16>);
-    case 7: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 7, CJ, BF16>);
-    case 8: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 8, CJ, BF16>);
-    default: return nullptr;
-  }
-}
-
-// Long per-lane chunk runs (a wave covering a whole row) only for one or
-// two rows per wave and at most two tokens.
-template <int MT, int CJ, bool BF16>
-const void* skinny_fn_rw_long(int rw) {
-  switch (rw) {
-    case 1: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 1, CJ, BF16>);
-    case 2: return reinterpret_cast<const void*>(&fp::skinny_kernel<MT, 2, CJ, BF16>);
-    default: return nullptr;
-  }
-}
-
-template <int MT, bool BF16>
-const void* skinny_fn_cj(int cj, int rw) {
-  switch (cj) {
-    case 1: return skinny_fn_rw<MT, 1, BF16>(rw);
-    case 2: return skinny_fn_rw<MT, 2, BF16>(rw);
-    default: break;
-  }
-  if constexpr (MT <= 2) {
-    switch (cj) {
-      case 4: return skinny_fn_rw_long<MT, 4, BF16>(rw);
-      case 5: return skinny_fn_rw_long<MT, 5, BF16>(rw);
-      case 6: return skinny_fn_rw_long<MT, 6, BF16>(rw);
-      case 8: return skinny_fn_rw_long<MT, 8, BF16>(rw);
-      case 10: return skinny_fn_rw_long<MT, 10, BF16>(rw);
-      case 12: return skinny_fn_rw_long<MT, 12, BF16>(rw);
-      default: break;
-    }
-  }
-  return nullptr;
-}
-
-template <bool BF16>
-const void* skinny_fn_mt(int mt, int cj, int rw) {
-  switch (mt) {
-    case 1: return skinny_fn_cj<1, BF16>(cj, rw);
-    case 2: return skinny_fn_cj<2, BF16>(cj, rw);
-    case 4: return skinny_fn_cj<4, BF16>(cj, rw);
-    case 8: return skinny_fn_cj<8, BF16>(cj, rw);
-    default: return nullptr;
-  }
-}
-
-template <int MT16, int NW>
-const void* tile_fn_per(int per) {
-  switch (per) {
-    case 8: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 4, 2>);
-    case 10: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 5, 2>);
-    case 16: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 4, 4>);
-    case 20: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 5, 4>);
-    case 40: return reinterpret_cast<const void*>(&fp::tile_kernel<MT16, NW, 5, 8>);
-    default: return nullptr;
-  }
-}
-
-template <int MT16>
-const void* tile_fn_nw(int nw, int per) {
-  switch (nw) {
-    case 2: return tile_fn_per<MT16, 2>(per);
-    case 4: return tile_fn_per<MT16, 4>(per);
-    case 8: return tile_fn_per<MT16, 8>(per);
-    default: return nullptr;
-  }
-}
-
-template <int WR, int A, int WM, int B>
-const void* ring_fn_st(int stages) {
-  switch (stages) {
-    case 3: return reinterpret_cast<const void*>(&fp::ring_tile_kernel<WR, A, WM, B, 3>);
-    case 4:
-      if constexpr (B <= 4)
-        return reinterpret_cast<const void*>(&fp::ring_tile_kernel<WR, A, WM, B, 4>);
-      return nullptr;
-    case 6:
-      if constexpr (B <= 4)
-        return reinterpret_cast<const void*>(&fp::ring_tile_kernel<WR, A, WM, B, 6>);
-      return nullptr;
-    default: return nullptr;
-  }
-}
-
-// Wave grids of the ring kernel per token block (16 * mt16 slots).
-const void* ring_fn(const Tiling& t) {
-  switch (t.mt) {
-    case 1: return ring_fn_st<4, 1, 1, 1>(t.chunks);
-    case 2: return ring_fn_st<4, 1, 1, 2>(t.chunks);
-    case 4: return ring_fn_st<2, 2, 2, 2>(t.chunks);
-    case 8: return ring_fn_st<2, 2, 2, 4>(t.chunks);
-    case 16: return ring_fn_st<2, 2, 2, 8>(t.chunks);
-    default: return nullptr;
-  }
-}
-
+// Kernel addresses come from the per-family units (kernels.h).
 const void* mfma_fn(const Tiling& t) {
-  if (is_ring(t)) return ring_fn(t);
-  switch (t.mt) {
-    case 1: return tile_fn_nw<1>(t.kparts, t.chunks);
-    case 2: return tile_fn_nw<2>(t.kparts, t.chunks);
-    case 4: return tile_fn_nw<4>(t.kparts, t.chunks);
-    case 8: return tile_fn_nw<8>(t.kparts, t.chunks);
-    case 16: return tile_fn_nw<16>(t.kparts, t.chunks);
-    default: return nullptr;
-  }
+  return is_ring(t) ? fpk::ring(t.mt, t.chunks) : fpk::tile(t.mt, t.kparts, t.chunks);
+}
+
+const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype, int64_t M) {
+  if (is_mx(dtype)) return pairs ? nullptr : fpk::smfma_mx(dtype, t.mt / 8, t.chunks);
+  return fpk::smfma(t.chunks, pairs, t.mt, M);
 }
 
 std::mutex g_attr_mu;
@@ -862,53 +648,6 @@ struct LaunchRows {
   int begin[fp::kMaxSeg + 1];
   float scale[fp::kMaxSeg];  // segment tensor scales (NVFP4)
 };
-
-// Two token halves: up to 12 tokens the loads of each step go in turn
-// (first half, weights, second half), above that every activation first.
-constexpr int kSmfmaInterleaveMaxM = 12;
-
-template <int KT>
-const void* smfma_fn_kt(bool pairs, int mt, int64_t M) {
-  if (mt == 16) {
-    if (pairs) return nullptr;
-    return M <= kSmfmaInterleaveMaxM
-               ? reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 2, false>)
-               : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 2>);
-  }
-  return pairs ? reinterpret_cast<const void*>(&fp::smfma_kernel<KT, true>)
-               : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false>);
-}
-
-template <int FMT, int MH>
-const void* smfma_mx_fn(int kt) {
-  switch (kt) {
-    case 4: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<4, FMT, MH>);
-    case 8: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<8, FMT, MH>);
-    case 16: return reinterpret_cast<const void*>(&fp::smfma_mx_kernel<16, FMT, MH>);
-    default: return nullptr;
-  }
-}
-
-template <int MH>
-const void* smfma_mx_fn_fmt(int32_t dtype, int kt) {
-  return dtype == FP_MXFP8   ? smfma_mx_fn<8, MH>(kt)
-         : dtype == FP_MXFP4 ? smfma_mx_fn<4, MH>(kt)
-                             : smfma_mx_fn<fp::kFmtNv4, MH>(kt);
-}
-
-const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype, int64_t M) {
-  if (dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4) {
-    if (pairs) return nullptr;
-    return t.mt == 8 ? smfma_mx_fn_fmt<1>(dtype, t.chunks)
-                     : smfma_mx_fn_fmt<2>(dtype, t.chunks);
-  }
-  switch (t.chunks) {
-    case 4: return smfma_fn_kt<4>(pairs, t.mt, M);
-    case 8: return smfma_fn_kt<8>(pairs, t.mt, M);
-    case 16: return smfma_fn_kt<16>(pairs, t.mt, M);
-    default: return nullptr;
-  }
-}
 
 // One launch over `lr` with tiling t.  Every kernel takes the same 14
 // leading argument dwords, all preloaded into SGPRs at wave launch (the
@@ -965,25 +704,17 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
     int32_t mpad_a = 16 * t.mt;
     int32_t s_a = t.splits;
     void* rargs[] = {&part_a, &n_rows_a, &M_a, &mpad_a, &s_a, &tail.out};
-    return launch(reinterpret_cast<const void*>(&fp::splitk_reduce_kernel),
+    return launch(fpk::splitk_reduce(),
                   ceil_div((int64_t)lr.n_rows * ceil_div(M, 4), 256), 256, 0, rargs, stream);
   }
   geo_a = t.kparts | (t.groups << 8) | (t.splits << 16);
   const int64_t R = (int64_t)t.groups * t.rows;
   const int64_t blocks = ceil_div(lr.n_rows, R) * t.splits;
-  const void* fn = pairs ? skinny_pairs_fn(t.mt, t.chunks, t.rows)
-                   : p->out_f32 ? skinny_f32out_fn(t.mt, t.chunks, t.rows)
-                   : p->dtype == FP_MXFP8 ? skinny_mx_fn<fp::kVarMx8>(t.mt, t.chunks, t.rows)
-                   : p->dtype == FP_MXFP4 ? skinny_mx_fn<fp::kVarMx4>(t.mt, t.chunks, t.rows)
-                   : p->dtype == FP_NVFP4 ? skinny_mx_fn<fp::kVarNv4>(t.mt, t.chunks, t.rows)
-                   : p->dtype == FP_BF16 ? skinny_fn_mt<true>(t.mt, t.chunks, t.rows)
-                                         : skinny_fn_mt<false>(t.mt, t.chunks, t.rows);
+  const void* fn = pairs ? fpk::skinny_pairs(t.mt, t.chunks, t.rows)
+                   : p->out_f32 ? fpk::skinny_f32out(t.mt, t.chunks, t.rows)
+                   : is_mx(p->dtype) ? fpk::skinny_mx(skinny_var(p), t.mt, t.chunks, t.rows)
+                                     : fpk::skinny(p->dtype == FP_BF16, t.mt, t.chunks, t.rows);
   return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
-}
-
-__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
 }
 
 bool aligned(const void* p, uintptr_t a) {
@@ -1116,7 +847,7 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
   uint32_t* cptr = reinterpret_cast<uint32_t*>(p->ws);
   uint32_t zero = 0u;
   void* fargs[] = {&cptr, &nc, &zero};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fill_u32_kernel),
+  hipError_t e = hipLaunchKernel(fpk::fill_u32(),
                                  dim3((unsigned)ceil_div(nc, 256)), dim3(256), fargs, 0, st);
   if (e != hipSuccess) {
     delete p;
@@ -1259,7 +990,7 @@ fp_status launch_rmsnorm(int n, const unsigned char* const* y, const unsigned ch
   t.M = (int32_t)M;
   t.eps = eps;
   void* args[] = {&t};
-  return launch(reinterpret_cast<const void*>(&fp::rmsnorm_kernel), (int64_t)n * M, 64, 0, args,
+  return launch(fpk::rmsnorm(), (int64_t)n * M, 64, 0, args,
                 stream);
 }
 
@@ -1367,7 +1098,7 @@ fp_status fp_swiglu(const void* g, const void* u, int64_t M, int64_t N, void* h,
   unsigned char* h_a = static_cast<unsigned char*>(h);
   int32_t n_a = (int32_t)chunks;
   void* args[] = {&g_a, &u_a, &h_a, &n_a};
-  return launch(reinterpret_cast<const void*>(&fp::swiglu_kernel), ceil_div(chunks, 256), 256,
+  return launch(fpk::swiglu(), ceil_div(chunks, 256), 256,
                 0, args, static_cast<hipStream_t>(stream));
 }
 
@@ -1385,7 +1116,7 @@ fp_status fp_mxfp8_to_bf16(const void* w, int64_t rows, int64_t K, void* out, vo
   int32_t kc_a = (int32_t)(K / 16);  // 16-code chunks
   int64_t n_a = rows * kc_a;
   void* args[] = {&w_a, &o_a, &kc_a, &n_a};
-  return launch(reinterpret_cast<const void*>(&fp::mxfp8_to_bf16_kernel), ceil_div(n_a, 256), 256,
+  return launch(fpk::mxfp8_to_bf16(), ceil_div(n_a, 256), 256,
                 0, args, static_cast<hipStream_t>(stream));
 }
 
@@ -1401,7 +1132,7 @@ fp_status fp_stream_read(const void* buf, int64_t bytes, void* sink, void* strea
   uint32_t per_a = (uint32_t)ceil_div(bytes / 16, fp::kStreamGroups);
   uint32_t* s_a = static_cast<uint32_t*>(sink);
   void* args[] = {&b_a, &bytes_a, &per_a, &s_a};
-  return launch(reinterpret_cast<const void*>(&fp::stream_read_kernel), fp::kStreamGroups,
+  return launch(fpk::stream_read(), fp::kStreamGroups,
                 fp::kStreamThreads, 0, args, static_cast<hipStream_t>(stream));
 }
 
@@ -1419,7 +1150,7 @@ fp_status fp_mxfp4_to_bf16(const void* w, int64_t rows, int64_t K, void* out, vo
   int32_t kc_a = (int32_t)(K / 32);  // 16-byte chunks of 32 codes: one per block
   int64_t n_a = rows * kc_a;
   void* args[] = {&w_a, &o_a, &kc_a, &n_a};
-  return launch(reinterpret_cast<const void*>(&fp::mxfp4_to_bf16_kernel), ceil_div(n_a, 256), 256,
+  return launch(fpk::mxfp4_to_bf16(), ceil_div(n_a, 256), 256,
                 0, args, static_cast<hipStream_t>(stream));
 }
 
@@ -1439,7 +1170,7 @@ fp_status fp_nvfp4_to_bf16(const void* w, int64_t rows, int64_t K, float g, void
   int64_t n_a = rows * kc_a;
   float g_a = g;
   void* args[] = {&w_a, &o_a, &kc_a, &n_a, &g_a};
-  return launch(reinterpret_cast<const void*>(&fp::nvfp4_to_bf16_kernel), ceil_div(n_a, 256), 256,
+  return launch(fpk::nvfp4_to_bf16(), ceil_div(n_a, 256), 256,
                 0, args, static_cast<hipStream_t>(stream));
 }
 

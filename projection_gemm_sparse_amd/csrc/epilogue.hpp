@@ -131,6 +131,9 @@ struct NormTable {
   float eps;
 };
 
+// The epilogue kernels: defined only in the unit that compiles the non-template
+// kernels (k_misc.hip), so each is emitted once.
+#ifdef FP_DEFINE_MISC_KERNELS
 __global__ void __launch_bounds__(64) rmsnorm_kernel(const NormTable t) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x;
@@ -174,5 +177,7 @@ swiglu_kernel(const unsigned char* __restrict__ g, const unsigned char* __restri
   reinterpret_cast<u32x4*>(h)[f] = swiglu_chunk(reinterpret_cast<const u32x4*>(g)[f],
                                                 reinterpret_cast<const u32x4*>(u)[f]);
 }
+
+#endif  // FP_DEFINE_MISC_KERNELS
 
 }  // namespace fp

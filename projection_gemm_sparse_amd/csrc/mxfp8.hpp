@@ -14,6 +14,9 @@
 
 namespace fp {
 
+// The decode kernels: defined only in the unit that compiles the non-template
+// kernels (k_misc.hip), so each is emitted once.
+#ifdef FP_DEFINE_MISC_KERNELS
 // Thread t decodes code chunk t (16 codes) of the rows: row t / kc, chunk
 // t % kc (kc = K / 16), to 32 bytes of bf16 at out[row, 16 * chunk ...].
 __global__ void __launch_bounds__(256)
@@ -105,5 +108,7 @@ nvfp4_to_bf16_kernel(const unsigned char* __restrict__ w, unsigned char* __restr
     orow[i] = o;
   }
 }
+
+#endif  // FP_DEFINE_MISC_KERNELS
 
 }  // namespace fp

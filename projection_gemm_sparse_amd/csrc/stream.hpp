@@ -16,6 +16,9 @@ constexpr int kStreamThreads = 640;
 constexpr int kStreamGroups = 256;
 constexpr int kStreamBatch = 8;    // loads in flight per lane and batch
 
+// The streaming kernel: defined only in the unit that compiles the non-template
+// kernels (k_misc.hip), so each is emitted once.
+#ifdef FP_DEFINE_MISC_KERNELS
 __global__ void __launch_bounds__(kStreamThreads)
 stream_read_kernel(const unsigned char* __restrict__ buf, uint32_t bytes, uint32_t per_wg,
                    uint32_t* __restrict__ sink) {
@@ -44,5 +47,7 @@ stream_read_kernel(const unsigned char* __restrict__ buf, uint32_t bytes, uint32
   }
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }
+
+#endif  // FP_DEFINE_MISC_KERNELS
 
 }  // namespace fp

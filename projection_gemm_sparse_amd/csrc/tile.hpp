@@ -292,6 +292,9 @@ tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict
                           a.out, reinterpret_cast<int*>(lds_raw));
 }
 
+// The second-launch finish: defined only in the unit that compiles the non-template
+// kernels (k_misc.hip), so each is emitted once.
+#ifdef FP_DEFINE_MISC_KERNELS
 // The second-launch finish of a split tile launch: thread t adds, for launch
 // row t / ceil(M/4) and four consecutive tokens, the S slices of the
 // partials in slice order -- the order of splitk_finish_vec, so both
@@ -345,5 +348,7 @@ splitk_reduce_kernel(const float* __restrict__ partial, int32_t n_rows, int32_t 
     if (m0 + j < M) store_y<true>(om, tab, row, m0 + j, vj);
   }
 }
+
+#endif  // FP_DEFINE_MISC_KERNELS
 
 }  // namespace fp

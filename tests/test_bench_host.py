@@ -26,7 +26,7 @@ def test_kernel_names_of_the_default_tilings():
 def test_two_halves_order_threshold_matches_the_library():
     # the library picks the interleaved two-halves instantiation up to this
     # many tokens; the bench names it the same way
-    src = open(os.path.join(bench.ROOT, "projection_gemm_sparse_amd", "csrc", "api.hip")).read()
+    src = open(os.path.join(bench.ROOT, "projection_gemm_sparse_amd", "csrc", "k_smfma.hip")).read()
     m = re.search(r"constexpr int kSmfmaInterleaveMaxM = (\d+);", src)
     assert m is not None
     lim = int(m.group(1))
