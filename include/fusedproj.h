@@ -370,6 +370,26 @@ fp_status fp_plan_get_tiling(fp_plan_t plan, int64_t M, int64_t n_rows,
 fp_status fp_default_tiling(int32_t dtype, int64_t K, int64_t n_total, int64_t M,
                             int64_t n_rows, fp_tiling* out);
 
+/* The fused call without a caller-provided workspace, for callers that
+ * cannot allocate device memory at call time or hold a workspace per plan
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Arguments, checks, kernels and results are fp_forward's
+ * (bitwise equal outputs), but the split-K arrival counters and partial
+ * sums live in a static device array of the library -- 24 MiB per GPU,
+ * held until the process ends: the first 256 KiB hold the counters (plans
+ * of at most 65536 rows), the rest the partials -- instead of the plan's
+ * workspace, which this call does not touch.  It calls no allocating
+ * routine.  The first call on a device looks the array up and clears its
+ * counter words with a fill kernel on `stream`; every call leaves the
+ * counters at zero.  `stream` must belong to the current device
+ * (FP_ERR_INVALID_ARG otherwise).  FP_ERR_WORKSPACE when the call's
+ * counters or partials exceed the array (the plan's rows, or a tiling with
+ * more split-K partials than fit), with no launch.  All calls on one GPU
+ * share the array: calls that overlap on one GPU (two streams, two
+ * threads) race and must be ordered by the caller. */
+fp_status fp_forward_noalloc(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
+                             void* stream, void* const* y);
+
 /* Static text for a status code. */
 const char* fp_status_str(int32_t status);
 

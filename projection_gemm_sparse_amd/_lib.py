@@ -78,6 +78,7 @@ _SIGS = {
     "fp_supported": (_i32, [_p, _i64, _p, _i64]),
     "fp_forward": (_i32, [_p, _i64, _i64, _p, _p, _P_p]),
     "fp_forward_separate": (_i32, [_p, _i64, _i64, _p, _p, _P_p, _P_p]),
+    "fp_forward_noalloc": (_i32, [_p, _i64, _i64, _p, _p, _P_p]),
     "fp_mxfp8_to_bf16": (_i32, [_p, _i64, _i64, _p, _p]),
     "fp_mxfp4_to_bf16": (_i32, [_p, _i64, _i64, _p, _p]),
     "fp_nvfp4_to_bf16": (_i32, [_p, _i64, _i64, ctypes.c_float, _p, _p]),
@@ -155,6 +156,10 @@ def fp_forward_separate(x: int, M: int, ldx: int, plan: int, stream: int, y,
                         w_override=None) -> int:
     ov = None if w_override is None else _ptr_array(w_override)
     return _lib.fp_forward_separate(x, M, ldx, plan, stream, _ptr_array(y), ov)
+
+
+def fp_forward_noalloc(x: int, M: int, ldx: int, plan: int, stream: int, y) -> int:
+    return _lib.fp_forward_noalloc(x, M, ldx, plan, stream, _ptr_array(y))
 
 
 def fp_mxfp8_to_bf16(w: int, rows: int, K: int, out: int, stream: int) -> int:

@@ -437,7 +437,31 @@ int64_t partial_floats(const Tiling& t, int64_t n_rows, int64_t M) {
   return (int64_t)t.splits * n_rows * mcols;
 }
 
-bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t) {
+// Where a launch keeps its split-K state: the arrival counters (one uint32
+// per row, zero between calls) and the fp32 partial sums, with the bytes
+// available for each.  Normally the plan's workspace; fp_forward_noalloc
+// uses the library's static scratch instead.
+struct WsView {
+  unsigned char* counters;
+  unsigned char* partial;
+  int64_t counter_bytes;
+  int64_t partial_bytes;  // negative: no room at all
+};
+
+WsView plan_ws(const fp_plan_s* p) {
+  const int64_t cb = counters_bytes(p->n_total);
+  WsView w;
+  w.counters = p->ws;
+  w.partial = p->ws + cb;
+  w.counter_bytes = cb;
+  w.partial_bytes = p->ws_bytes < (size_t)cb ? -1
+                    : p->ws_bytes - (size_t)cb > (size_t)INT64_MAX ? INT64_MAX
+                                                                     : (int64_t)(p->ws_bytes - (size_t)cb);
+  return w;
+}
+
+bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t,
+                  const WsView& ws) {
   if (t.splits < 1 || t.kparts < 1 || t.chunks < 1 || t.rows < 1) return false;
   // packed into 8- and 16-bit fields of the kernels' scalar arguments
   if (t.splits > 0x1fff || t.kparts > 0xff || t.rows > 0xff || t.groups > 0xff) return false;
@@ -488,14 +512,14 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
   } else {
     return false;
   }
-  const int64_t need = counters_bytes(p->n_total) + partial_floats(t, n_rows, M) * 4;
-  return (size_t)need <= p->ws_bytes;
+  return counters_bytes(p->n_total) <= ws.counter_bytes &&
+         partial_floats(t, n_rows, M) * 4 <= ws.partial_bytes;
 }
 
 // The tiling for (M, launch rows); the summation-order fields come from the
 // plan's default or the user's override for M and never from n_rows.
 bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
-                   bool pairs = false) {
+                   bool pairs = false, const WsView* ws = nullptr) {
   *t = Tiling();
   if (M >= 1 && M <= FP_MAX_M && p->has_override[M]) {
     const fp_tiling& o = p->override_t[M];
@@ -545,12 +569,12 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
   }
   // a gate/up launch keeps both rows of a pair in one row group
   if (pairs && (t->rows % 2 != 0 || t->splits != 1)) return false;
-  return tiling_valid(p, M, n_rows, *t);
+  return tiling_valid(p, M, n_rows, *t, ws != nullptr ? *ws : plan_ws(p));
 }
 
 // A host-only stand-in plan with default settings and unlimited workspace,
 // for questions about default tilings.
-void scratch_plan(fp_plan_s* tmp, int32_t dtype, int64_t K, int64_t n_total,
+void standin_plan(fp_plan_s* tmp, int32_t dtype, int64_t K, int64_t n_total,
                   int64_t max_M) {
   std::memset(tmp, 0, sizeof *tmp);
   tmp->magic = kPlanMagic;
@@ -576,7 +600,7 @@ size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) 
   // counters for every possible row block, plus the largest partial buffer
   // over the default tilings of every M up to max_M (fused launch: all rows)
   fp_plan_s tmp;
-  scratch_plan(&tmp, dtype, K, n_total, max_M);
+  standin_plan(&tmp, dtype, K, n_total, max_M);
   int64_t most = 0;
   for (int64_t M = 1; M <= max_M; ++M) {
     Tiling t;
@@ -657,7 +681,7 @@ struct LaunchRows {
 // segments, split-K workspace).
 fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
               const void* x, int64_t M, int64_t ldx, hipStream_t stream,
-              bool pairs = false) {
+              bool pairs = false, const WsView* ws = nullptr) {
   const unsigned char* w_a = lr.w;
   const unsigned char* x_a = static_cast<const unsigned char*>(x);
   unsigned char* y0_a = lr.y[0];
@@ -676,8 +700,9 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
     tail.out.tscale[i] = i < lr.n_seg ? lr.scale[i] : 1.0f;
   }
   tail.out.begin[fp::kMaxSeg] = lr.n_rows;
-  tail.partial = reinterpret_cast<float*>(p->ws + counters_bytes(p->n_total));
-  tail.counters = reinterpret_cast<uint32_t*>(p->ws);
+  const WsView wsv = ws != nullptr ? *ws : plan_ws(p);
+  tail.partial = reinterpret_cast<float*>(wsv.partial);
+  tail.counters = reinterpret_cast<uint32_t*>(wsv.counters);
   int32_t geo_a = 0;
   void* args[] = {&w_a, &x_a, &y0_a, &y1_a, &ldx_a, &n_rows_a, &kc_a, &M_a, &split_a,
                   &geo_a, &tail};
@@ -1286,7 +1311,7 @@ fp_status fp_default_tiling(int32_t dtype, int64_t K, int64_t n_total, int64_t M
   if (!dtype_geometry(dtype, K, &esize, &wrow, &kc)) return FP_ERR_UNSUPPORTED;
   if (M < 1 || M > FP_MAX_M || n_rows < 1 || n_rows > n_total) return FP_ERR_INVALID_ARG;
   fp_plan_s tmp;
-  scratch_plan(&tmp, dtype, K, n_total, FP_MAX_M);
+  standin_plan(&tmp, dtype, K, n_total, FP_MAX_M);
   Tiling t;
   if (!choose_tiling(&tmp, M, n_rows, &t)) return FP_ERR_UNSUPPORTED;
   out->path = t.path;
@@ -1310,5 +1335,107 @@ const char* fp_status_str(int32_t status) {
 }
 
 int32_t fp_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"
+
+// ---------------------------------------------------------- no-allocation form
+// fp_forward_noalloc keeps the split-K state of its launches in `scratch`, a
+// device array of this library (each GPU the library runs on holds its own
+// copy until the process ends), instead of the plan's workspace.  Layout:
+// the arrival counters (one uint32 per row of the plan, zero between calls)
+// in the first kScratchCounterBytes, the fp32 partial sums after them, so
+// plans of any row count leave each other's counters untouched.  Every call
+// on one GPU shares the array; calls that overlap on one GPU race.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)24 << 20;
+constexpr size_t kScratchCounterBytes = (size_t)256 << 10;  // 65536 rows
+constexpr int kScratchMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Per device: the address of its copy of `scratch` (host code never uses
+// the array's own name as a device address).
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kScratchMaxDevices];
+
+// The current device's scratch address.  On the first call on a device
+// (with that device current) it looks the address up and clears the
+// counter words with the fill kernel on `stream` (a kernel, not a memset:
+// graph-capture friendly).  Allocates nothing.
+fp_status scratch_for_stream(hipStream_t stream, unsigned char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kScratchMaxDevices) return FP_ERR_UNSUPPORTED;
+  if (stream != nullptr) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (sdev != dev) return FP_ERR_INVALID_ARG;  // the stream's device must be current
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return hip_fail(e != hipSuccess ? e : hipErrorUnknown);
+    uint32_t* cptr = static_cast<uint32_t*>(ptr);
+    int64_t nc = (int64_t)(kScratchCounterBytes / 4);
+    uint32_t zero = 0u;
+    void* fargs[] = {&cptr, &nc, &zero};
+    e = hipLaunchKernel(fpk::fill_u32(), dim3((unsigned)ceil_div(nc, 256)), dim3(256), fargs, 0,
+                        stream);
+    if (e != hipSuccess) return hip_fail(e);
+    g_scratch_ptr[dev] = static_cast<unsigned char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return FP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp_status fp_forward_noalloc(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
+                             void* stream, void* const* y) {
+  if (!plan_ok(plan)) return FP_ERR_INVALID_ARG;
+  fp_status s = check_x(plan, M, x, ldx);
+  if (s != FP_OK) return s;
+  if (M == 0) return FP_OK;
+  s = check_outputs(plan, M, x, ldx, y);
+  if (s != FP_OK) return s;
+  // the scratch's capacity takes the place of the plan's workspace; the
+  // tiling is the plan's (same kernels, same bits as fp_forward)
+  if (counters_bytes(plan->n_total) > (int64_t)kScratchCounterBytes) return FP_ERR_WORKSPACE;
+  WsView cap;
+  cap.counters = nullptr;
+  cap.partial = nullptr;
+  cap.counter_bytes = (int64_t)kScratchCounterBytes;
+  cap.partial_bytes = (int64_t)(kScratchBytes - kScratchCounterBytes);
+  Tiling t;
+  if (!choose_tiling(plan, M, plan->n_total, &t, false, &cap)) {
+    // runnable with the plan's own workspace: the partials exceed the scratch
+    Tiling t2;
+    return choose_tiling(plan, M, plan->n_total, &t2) ? FP_ERR_WORKSPACE : FP_ERR_UNSUPPORTED;
+  }
+  unsigned char* base = nullptr;
+  s = scratch_for_stream(static_cast<hipStream_t>(stream), &base);
+  if (s != FP_OK) return s;
+  WsView ws = cap;
+  ws.counters = base;
+  ws.partial = base + kScratchCounterBytes;
+  LaunchRows lr;
+  std::memset(&lr, 0, sizeof lr);
+  lr.w = plan->w_cat;
+  lr.n_seg = plan->n_proj;
+  lr.n_rows = (int)plan->n_total;
+  for (int i = 0; i < plan->n_proj; ++i) {
+    lr.y[i] = static_cast<unsigned char*>(y[i]);
+    lr.begin[i] = (int)plan->off[i];
+    lr.scale[i] = plan->tscale[i];
+  }
+  lr.begin[plan->n_proj] = (int)plan->n_total;
+  return run(plan, t, lr, x, M, ldx, static_cast<hipStream_t>(stream), false, &ws);
+}
 
 }  // extern "C"

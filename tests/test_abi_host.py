@@ -91,6 +91,7 @@ def test_calls_on_a_stale_or_null_plan():
         assert P.fp_supported(plan, 1, FAKE, 5120) == P.FP_ERR_INVALID_ARG
         assert P.fp_forward(FAKE, 1, 5120, plan, 0, [FAKE, FAKE]) == P.FP_ERR_INVALID_ARG
         assert P.fp_forward_separate(FAKE, 1, 5120, plan, 0, [FAKE, FAKE]) == P.FP_ERR_INVALID_ARG
+        assert L.fp_forward_noalloc(FAKE, 1, 5120, plan, 0, [FAKE, FAKE]) == P.FP_ERR_INVALID_ARG
         assert P.fp_plan_view(plan, 0)[0] == P.FP_ERR_INVALID_ARG
         assert P.fp_plan_query(plan, 1)[0] == P.FP_ERR_INVALID_ARG
         assert P.fp_plan_set_mfma_min_m(plan, 9) == P.FP_ERR_INVALID_ARG
