@@ -75,9 +75,10 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter record,
-    or None when there is none or the kernel sources changed since."""
+def recorded_kernel(kernel: str):
+    """The committed rocprofv3 record of `kernel` (its kernel-trace average
+    duration and HBM bytes per launch), or None when there is none or the
+    kernel sources changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
@@ -85,7 +86,13 @@ def recorded_traffic(kernel: str):
         return None
     if rec.get("kernel_sources_sha256_16") != kernel_sources_digest():
         return None
-    ent = rec.get("kernels", {}).get(kernel)
+    return rec.get("kernels", {}).get(kernel)
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter record,
+    or None when there is none or the kernel sources changed since."""
+    ent = recorded_kernel(kernel)
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
@@ -157,29 +164,47 @@ def time_graphs(torch, graphs, steps, warmup):
     return total, per
 
 
-def cpu_baseline(plan0_weights_cpu, xs_cpu, budget_s=12.0):
-    """The oracle (single-threaded C loop, fp64) on the M = 1..8 sweep over
-    one weight copy, repeated until ``budget_s`` of CPU time is spent."""
+def cpu_baseline(plan0_weights_cpu, xs_cpu, run_s=2.0, runs=5):
+    """The oracle (plain C loop, fp64) on the M = 1..8 sweep over one weight
+    copy, in two forms: single-threaded, and with the output elements spread
+    over all host threads (OpenMP, the same per-element loop).  Each form:
+    `runs` runs of repeated sweeps of at least `run_s` seconds each; the
+    median run gives the seconds per sweep."""
     import oracle
     import synthetic_inputs as si
     oracle.build(force=False)
     wb = [si.bits(w) for w in plan0_weights_cpu]
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        for M in MS:
-            xb = si.bits(xs_cpu[M])
-            for w in wb:
-                oracle.linear(xb, w)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or passes >= 50:
-            break
-    byts = passes * sum(algorithmic_bytes(M, K, N) for M in MS)
-    return {"value": byts / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    xb = {M: si.bits(xs_cpu[M]) for M in MS}
+    sweep_bytes = sum(algorithmic_bytes(M, K, N) for M in MS)
+    variants = {}
+    for name, lin, cores in (("single_thread", oracle.linear, 1),
+                             ("openmp", oracle.linear_omp, oracle.omp_threads())):
+        per = []
+        for _ in range(runs):
+            n, t0 = 0, time.perf_counter()
+            while True:
+                for M in MS:
+                    for w in wb:
+                        lin(xb[M], w)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= run_s:
+                    break
+            per.append(el / n)
+        per.sort()
+        med = per[len(per) // 2]
+        variants[name] = {"value": round(sweep_bytes / med / 1e9, 4), "unit": "GB/s",
+                          "cores": cores, "sweep_s_median": round(med, 5),
+                          "sweep_s_runs": [round(v, 5) for v in per],
+                          "us_per_call": round(med / len(MS) * 1e6, 1)}
+    omp = variants["openmp"]
+    return {"value": omp["value"], "unit": "GB/s", "cores": omp["cores"], "kind": "oracle",
             "host": host_info(),
-            "sample": "%d pass(es) of the M=1..8 sweep over one [1792, 5120] bf16 "
-                      "weight copy, %.1f s, single-threaded C fp64 loop" % (passes, el),
-            "us_per_call": el / (passes * len(MS)) * 1e6}
+            "sample": "the M=1..8 sweep (16 projection calls) over one [1792, 5120] bf16 weight "
+                      "copy; median of %d runs of >= %.0f s each; C fp64 loop (gcc -O2, no "
+                      "fast-math), output elements over %d OpenMP threads; the single-threaded "
+                      "form in single_thread" % (runs, run_s, omp["cores"]),
+            "us_per_call": omp["us_per_call"], "single_thread": variants["single_thread"]}
 
 
 def stream_ceiling(P, torch, dev, plans, n_copies, steps):
@@ -203,6 +228,173 @@ def stream_ceiling(P, torch, dev, plans, n_copies, steps):
             "frac_of_peak": round(wb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": wb,
             "note": "fp_stream_read of each copy's W_cat (18,350,080 B) with the fused "
                     "call's launch shape and no other work; same pool and protocol"}
+
+
+def command_line() -> str:
+    """The command that produced a table, for its summary."""
+    return "python -u bench.py " + " ".join(sys.argv[1:])
+
+
+def write_table_md(path, title, header, rows, notes=()):
+    """A markdown summary: title, the producing command, notes, one table."""
+    lines = ["# " + title, "", "Command (run from the repository root):", "", "```",
+             command_line(), "```", ""]
+    for n in notes:
+        lines += [n, ""]
+    lines.append("| " + " | ".join(header) + " |")
+    lines.append("|" + "---|" * len(header))
+    for r in rows:
+        lines.append("| " + " | ".join("" if c is None else str(c) for c in r) + " |")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def write_outputs(prefix, title, payload, header, rows, notes=()):
+    with open(prefix + ".json", "w") as fh:
+        json.dump(payload, fh, indent=1)
+    write_table_md(prefix + ".md", title, header, rows, notes)
+    print("bench: wrote %s.json and %s.md" % (prefix, prefix), file=sys.stderr, flush=True)
+
+
+# Launch shapes of the streaming-ceiling sweep: (workgroups, threads,
+# loads in flight per lane); the first is the fused call's shape.
+STREAM_SHAPES = ((256, 640, 8), (256, 256, 32), (256, 512, 16), (256, 1024, 8), (512, 512, 8),
+                 (1024, 256, 8), (2048, 128, 8), (4096, 64, 8), (224, 640, 8), (128, 640, 16),
+                 (256, 256, 8))
+
+
+def ceiling_sweep(P, torch, dev, plans, n_copies, steps, prefix):
+    """The read-only streaming ceiling against the launch shape, and where a
+    fused call's time goes: the per-launch floor (a graph of tiny kernels,
+    and a launch of the fused call's shape that reads one vector), the
+    stream of the weights, and the fused calls (M = 1, 8) on the same pool
+    and protocol."""
+    import synthetic_inputs as si
+    sink = torch.zeros(65536, dtype=torch.int32, device=dev)
+    wb = plans[0].n_total * K * 2
+    ptrs = [p.views[0].data_ptr() for p in plans]
+
+    def per_call(fn):
+        g = capture(torch, fn)
+        t, _ = time_graphs(torch, [g], steps, 2)
+        del g
+        return t * 1e3 / (steps * n_copies)
+
+    def shaped(groups, threads, batch, nbytes):
+        def calls():
+            h = torch.cuda.current_stream().cuda_stream
+            for ptr in ptrs:
+                st = P.fp_stream_read_shaped(ptr, nbytes, groups, threads, batch,
+                                             sink.data_ptr(), h)
+                if st != P.FP_OK:
+                    raise RuntimeError("fp_stream_read_shaped: %d" % st)
+        return per_call(calls)
+
+    tiny = torch.zeros(64, device=dev)
+    floor_tiny = per_call(lambda: [tiny.add_(1.0) for _ in range(n_copies)])
+    floor_shape = shaped(256, 640, 8, 16)
+    rows, shapes = [], []
+    for groups, threads, batch in STREAM_SHAPES:
+        us = shaped(groups, threads, batch, wb)
+        shapes.append({"groups": groups, "threads": threads, "batch": batch,
+                       "us": round(us, 4), "GBps": round(wb / us / 1e3, 1)})
+        rows.append(("%d x %d" % (groups, threads), batch,
+                     -(-wb // 16 // groups // threads), "%.3f" % us, "%.0f" % (wb / us / 1e3),
+                     "%.1f" % (100 * wb / us / 1e3 / HBM_PEAK_GBS)))
+        print("bench: stream shape %s" % json.dumps(shapes[-1]), file=sys.stderr, flush=True)
+    fused = {}
+    for M in (1, 8):
+        x = si.make_case(K, N, "bf16", M, seed=100 + M)[0].to(dev)
+        out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
+        fused[M] = per_call(lambda: [p.forward(x, out=out) for p in plans])
+    ceil_us = shapes[0]["us"]
+    decomp = [("graph of tiny kernels (per launch)", "%.3f" % floor_tiny, "", ""),
+              ("fused-call launch shape reading one vector", "%.3f" % floor_shape, "", ""),
+              ("stream of the weights, fused-call shape", "%.3f" % ceil_us,
+               "%.3f" % (ceil_us - floor_shape), ""),
+              ("fused call, M = 1", "%.3f" % fused[1], "%.3f" % (fused[1] - floor_shape),
+               "%.3f" % (fused[1] - ceil_us)),
+              ("fused call, M = 8", "%.3f" % fused[8], "%.3f" % (fused[8] - floor_shape),
+               "%.3f" % (fused[8] - ceil_us))]
+    payload = {"workload": "wq_a+wkv [1280,512]x5120 bf16, %d copies rotated" % n_copies,
+               "weight_bytes": wb, "floor_tiny_us": round(floor_tiny, 4),
+               "floor_fused_shape_us": round(floor_shape, 4), "shapes": shapes,
+               "fused_us": {str(k): round(v, 4) for k, v in fused.items()}}
+    notes = ["Every row: one call per weight copy (%d copies of %d bytes, %.0f MiB, past the "
+             "256 MiB MALL), captured in a hipGraph, %d timed replays; microseconds per call."
+             % (n_copies, wb, n_copies * wb / 2 ** 20, steps),
+             "Where a call's time goes (us per call; 'above launch' subtracts the fused-call "
+             "launch shape reading one vector, 'above ceiling' the stream of the same bytes):",
+             "\n".join(["| part | us | above launch | above ceiling |", "|---|---|---|---|"] +
+                       ["| %s |" % " | ".join(r) for r in decomp]),
+             "Streaming ceiling against the launch shape (fp_stream_read_shaped: workgroup b "
+             "reads the b-th contiguous 1/groups of the copy, 16-byte non-temporal loads):"]
+    write_outputs(prefix, "Streaming ceiling and per-launch floor, wq_a+wkv [1792, 5120] bf16 "
+                  "weights rotated past the MALL", payload,
+                  ["workgroups x threads", "loads in flight / lane", "loads / lane", "us / call",
+                   "GB/s", "% of 8 TB/s"], rows, notes)
+    return payload
+
+
+# Forced K splits of the fp32 indexer fusion: (name, tiling) with tiling
+# (path, waves per slice P, chunks per lane CJ, slices S, rows, groups).
+INDEXER_SPLITS = (("S=1 (P=14, CJ=2)", None), ("S=2 (P=14, CJ=1)", (2, 14, 1, 2, 0, 0)),
+                  ("S=2 (P=7, CJ=2)", (2, 7, 2, 2, 0, 0)), ("S=4 (P=7, CJ=1)", (2, 7, 1, 4, 0, 0)),
+                  ("S=7 (P=2, CJ=2)", (2, 2, 2, 7, 0, 0)), ("S=7 (P=4, CJ=1)", (2, 4, 1, 7, 0, 0)),
+                  ("S=14 (P=2, CJ=1)", (2, 2, 1, 14, 0, 0)))
+
+
+def indexer_split_sweep(P, torch, dev, steps, prefix, Ms=(1, 4, 8)):
+    """The fp32 indexer fusion (K = 7168, [128, 64], fp32) with its K split
+    across 1..14 workgroups per row block, on a pool past the MALL: the
+    measurement its default split is chosen from."""
+    import synthetic_inputs as si
+    wl = si.WORKLOADS["indexer_f32"]
+    wb = sum(wl.N) * wl.K * 4
+    n = max(2, math.ceil((1 << 30) / wb))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    plans = []
+    for _ in range(n):
+        ws = [(torch.randn(nr, wl.K, generator=g, device="cuda") * 0.02) for nr in wl.N]
+        plans.append(P.FusedProjection(ws, max_M=max(Ms), workspace_bytes=1 << 20))
+        del ws
+    res, rows = [], []
+    for M in Ms:
+        x = si.make_case(wl.K, wl.N, wl.dtype, M, seed=700 + M)[0].to(dev)
+        out = [torch.empty(M, nr, dtype=torch.float32, device=dev) for nr in wl.N]
+        for name, t in INDEXER_SPLITS:
+            for p in plans:
+                p.set_tiling(M, None)
+            if t is not None:
+                st = plans[0].set_tiling(M, t)
+                if st != P.FP_OK:
+                    res.append({"M": M, "split": name, "status": st})
+                    continue
+                for p in plans[1:]:
+                    p.set_tiling(M, t)
+            gr = capture(torch, lambda: [p.forward(x, out=out) for p in plans])
+            tt, _ = time_graphs(torch, [gr], steps, 2)
+            del gr
+            us = tt * 1e3 / (steps * n)
+            tl = list(plans[0].get_tiling(M))
+            wgs = -(-sum(wl.N) // (tl[4] * tl[5])) * tl[3]
+            b = 4 * (sum(wl.N) * wl.K + M * wl.K + M * sum(wl.N))
+            res.append({"M": M, "split": name, "tiling": tl, "workgroups": wgs,
+                        "us": round(us, 4), "GBps": round(b / us / 1e3, 1)})
+            rows.append((M, name, tl, wgs, "%.3f" % us, "%.0f" % (b / us / 1e3)))
+            print("bench: indexer split %s" % json.dumps(res[-1]), file=sys.stderr, flush=True)
+    for p in plans:
+        p.close()
+    write_outputs(prefix, "fp32 indexer fusion [192, 7168] (wk 128 + weights_proj 64): K split "
+                  "across workgroups", {"workload": "indexer_f32 K=7168 N=[128, 64] fp32, %d "
+                                        "copies rotated" % n, "rows": res},
+                  ["M", "split", "tiling (path, P, CJ, S, RW, G)", "workgroups", "us / call",
+                   "GB/s"], rows,
+                  ["One fused call per weight copy (%d copies of %d bytes, past the MALL), "
+                   "hipGraph replay, %d timed replays; the split is forced with "
+                   "fp_plan_set_tiling (S=1 is the default)." % (n, wb, steps)])
+    return res
 
 
 def trial_stats(torch, graphs, n_calls, trials=15, min_calls=2000):
@@ -326,55 +518,65 @@ def host_info():
     return {"cpu_model": model, "nproc": os.cpu_count()}
 
 
-def crossover(path, P, torch, dev, plans, n_copies):
+def crossover(prefix, P, torch, dev, plans, n_copies, Ms=(1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 24,
+                                                           32, 48, 64, 96, 128)):
     """Per token count, every kernel path that serves it, on the rotated
-    pool (plans are made for max_M = 8, so a second pool is built)."""
+    pool (plans are made for max_M = 8, so a second pool is built): the
+    measured crossovers that place each kernel."""
     import synthetic_inputs as si
     del plans
     torch.cuda.empty_cache()
-    big = build_pool(P, torch, n_copies, 128)
-    n_total = sum(N)
-    tile_min = next(m for m in range(2, 257)
-                    if P.fp_default_tiling(0, K, n_total, m, n_total)[1][0] == P.FP_PATH_MFMA)
-    rows = []
-    for M in (1, 2, 3, 4, 5, 8, 9, 16, 32, 64, 128):
+    big = build_pool(P, torch, n_copies, max(Ms))
+    kc = K * 2 // 16
+    steps = -(-kc // 8)
+    kt = 4 if steps <= 64 else 8 if steps <= 128 else 16
+    res, rows = [], []
+    for M in Ms:
         xc, _ = si.make_case(K, N, "bf16", M, seed=200 + M)
         x = xc.to(dev)
         out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
         cands = [("default", None)]
-        kc = K * 2 // 16
-        steps = -(-kc // 8)
-        kt = 4 if steps <= 64 else 8 if steps <= 128 else 16
         if M <= 8:
-            cands.append(("skinny", (P.FP_PATH_SKINNY, 10, 1, 1, 0, 0)))
+            cands.append(("vector ALU", (P.FP_PATH_SKINNY, 10, 1, 1, 0, 0)))
         if M <= 16:
-            cands.append(("mfma_small", (P.FP_PATH_MFMA_SMALL, -(-steps // kt), kt, 1, 0, 0)))
-        if 8 < M < tile_min:
-            cands.append(("tile", "tile"))
+            cands.append(("small-M MFMA", (P.FP_PATH_MFMA_SMALL, -(-steps // kt), kt, 1, 0, 0)))
+        if M > 8:
+            cands.append(("tile (S=8)", (P.FP_PATH_MFMA, 0, 0, 8, 0, 0)))
+            cands.append(("ring tile (S=9)", (P.FP_PATH_MFMA, 4, 3 if M > 128 else 4, 9, 0, 0)))
+            cands.append(("weight-resident (S=8)", (P.FP_PATH_MFMA, 4, 2, 8, 0, 0)))
+            cands.append(("weight-resident (S=9)", (P.FP_PATH_MFMA, 4, 2, 9, 0, 0)))
+        default_t = list(big[0].get_tiling(M))
         for name, t in cands:
-            if t == "tile":
-                for p in big:
-                    p.set_mfma_min_m(M)
-            elif t is not None and any(p.set_tiling(M, t) for p in big):
-                for p in big:
-                    p.set_tiling(M, None)
-                continue
+            if t is not None:
+                if any(p.set_tiling(M, t) for p in big):
+                    for p in big:
+                        p.set_tiling(M, None)
+                    continue
+                if name != "default" and list(big[0].get_tiling(M)) == default_t:
+                    name += " = default"
             g = capture(torch, lambda: [p.forward(x, out=out) for p in big])
             ms, _ = time_graphs(torch, [g], 10, 2)
             us = ms * 1e3 / (10 * n_copies)
             b = algorithmic_bytes(M, K, N)
-            rows.append({"M": M, "variant": name,
-                         "path": P._lib.PATH_NAMES[big[0].query(M)[0]],
-                         "tiling": list(big[0].get_tiling(M)), "us": round(us, 3),
-                         "GBps": round(b / us / 1e3, 1)})
-            print("bench: crossover %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            tl = list(big[0].get_tiling(M))
+            res.append({"M": M, "variant": name, "path": P._lib.PATH_NAMES[big[0].query(M)[0]],
+                        "tiling": tl, "us": round(us, 3), "GBps": round(b / us / 1e3, 1)})
+            rows.append((M, name, tl, "%.3f" % us, "%.0f" % (b / us / 1e3),
+                         "%.1f" % (100 * b / us / 1e3 / HBM_PEAK_GBS)))
+            print("bench: crossover %s" % json.dumps(res[-1]), file=sys.stderr, flush=True)
             for p in big:
                 p.set_tiling(M, None)
-                p.set_mfma_min_m(tile_min)
             del g
-    with open(path, "w") as fh:
-        json.dump({"workload": "wq_a+wkv [1280,512]x5120 bf16, %d rotated copies" % n_copies,
-                   "rows": rows}, fh, indent=1)
+    for p in big:
+        p.close()
+    write_outputs(prefix, "Kernel crossover, wq_a+wkv [1792, 5120] bf16, weights rotated past "
+                  "the MALL", {"workload": "wq_a+wkv [1280,512]x5120 bf16, %d rotated copies"
+                               % n_copies, "rows": res},
+                  ["M", "kernel", "tiling (path, kparts, chunks, S, rows, groups)", "us / call",
+                   "GB/s", "% of 8 TB/s"], rows,
+                  ["Every kernel that serves M, forced with fp_plan_set_tiling, on one pool "
+                   "of %d copies (one fused call per copy, hipGraph replay, 10 timed replays); "
+                   "'default' is the library's choice." % n_copies])
 
 
 def epilogue_cells(P, torch, dev, plans, n_copies, steps, Ms=(1, 2, 4, 8)):
@@ -578,14 +780,24 @@ def main():
     ap.add_argument("--no-epilogues", action="store_true",
                     help="skip the fused RMSNorm / SwiGLU epilogue cells")
     ap.add_argument("--crossover", default="",
-                    help="also time every kernel path per M in 1..128 and write the table here")
+                    help="time every kernel path per M in 1..128, write PREFIX.json and "
+                         "PREFIX.md and exit")
+    ap.add_argument("--ceiling", default="",
+                    help="time the streaming ceiling against the launch shape and the "
+                         "per-launch floor, write PREFIX.json and PREFIX.md and exit")
+    ap.add_argument("--indexer-splits", default="",
+                    help="time the fp32 indexer fusion with its K split across 1..14 "
+                         "workgroups, write PREFIX.json and PREFIX.md and exit")
+    ap.add_argument("--timed-only", action="store_true",
+                    help="only the warm-up and timed steps of the fused graphs (profiler runs: "
+                         "every dispatch is a graph replay of the timed step)")
     ap.add_argument("--mfma-only", action="store_true",
                     help="time only the matrix-core cells (M = 8 on the small-M kernel, "
                          "9..128 on the tile kernel) and print them (profiler runs of the "
                          "MFMA counters); not the benchmark line")
     ap.add_argument("--pool-sweep", default="",
-                    help="write a pool-size sweep (per-call time vs rotated pool size) to this "
-                         "JSON file and exit")
+                    help="write a pool-size sweep (per-call time vs rotated pool size) to "
+                         "PREFIX.json and PREFIX.md and exit")
     ap.add_argument("--mx-variants", action="store_true",
                     help="with --mxfp8-only: M = 1..8 and both MX kernels at every M")
     ap.add_argument("--mxfp8-only", action="store_true",
@@ -621,11 +833,18 @@ def main():
             del gr
         print(json.dumps({"mfma": res}), flush=True)
         return
+    if args.indexer_splits:
+        indexer_split_sweep(P, torch, dev, args.steps, args.indexer_splits)
+        return
     if args.pool_sweep:
         rows = pool_sweep(P, torch, dev, max(3, args.steps // 4))
-        with open(args.pool_sweep, "w") as fh:
-            json.dump({"workload": "wq_a+wkv [1280,512]x5120 bf16 fused calls", "rows": rows},
-                      fh, indent=1)
+        write_outputs(args.pool_sweep, "Pool-size sweep, wq_a+wkv [1792, 5120] bf16 fused calls",
+                      {"workload": "wq_a+wkv [1280,512]x5120 bf16 fused calls", "rows": rows},
+                      ["pool MiB", "copies", "M", "us / call", "GB/s"],
+                      [(r["pool_MiB"], r["copies"], r["M"], r["us"], r["GBps"]) for r in rows],
+                      ["Per-call time of the fused call against the size of the rotated pool "
+                       "(one copy, then 64 MiB .. 2 GiB); the time levels off once the pool is "
+                       "past the 256 MiB MALL."])
         print(json.dumps({"pool_sweep": rows}), flush=True)
         return
     if args.mxfp8_only:
@@ -648,6 +867,12 @@ def main():
     print("bench: pool of %d weight copies (%.0f MiB), M=%s" %
           (n_copies, n_copies * w_bytes / 2**20, list(MS)), file=sys.stderr, flush=True)
     plans = build_pool(P, torch, n_copies, max(MS))
+    if args.crossover:
+        crossover(args.crossover, P, torch, dev, plans, n_copies)
+        return
+    if args.ceiling:
+        ceiling_sweep(P, torch, dev, plans, n_copies, args.steps, args.ceiling)
+        return
 
     xs_cpu, xs, outs = {}, {}, {}
     for M in MS:
@@ -678,15 +903,19 @@ def main():
     print("bench: graphs captured", file=sys.stderr, flush=True)
     total_ms, per_ms = time_graphs(torch, fused_graphs, args.steps, args.warmup)
     sep_steps = max(3, args.steps // 4)
-    if args.fused_only:
+    if args.fused_only or args.timed_only:
         sep_ms = [float("nan")] * len(MS)
     else:
         sep_graphs = [capture(torch, separate_calls(M)) for M in MS]
         _, sep_ms = time_graphs(torch, sep_graphs, sep_steps, 1)
 
-    trials, trial_reps = trial_stats(torch, fused_graphs, n_copies)
-    eager = {str(M): eager_us(torch, fused_calls(M), n_copies) for M in (1, 8)}
-    ceiling = stream_ceiling(P, torch, dev, plans, n_copies, max(3, args.steps // 2))
+    if args.timed_only:
+        trials, trial_reps = [None] * len(MS), 0
+        eager, ceiling = None, None
+    else:
+        trials, trial_reps = trial_stats(torch, fused_graphs, n_copies)
+        eager = {str(M): eager_us(torch, fused_calls(M), n_copies) for M in (1, 8)}
+        ceiling = stream_ceiling(P, torch, dev, plans, n_copies, max(3, args.steps // 2))
 
     calls = args.steps * n_copies
     per_m = {}
@@ -698,7 +927,7 @@ def main():
         tl = plans[0].get_tiling(M)
         per_m[str(M)] = {
             "fused_us": round(us, 4),
-            "separate_us": (None if args.fused_only else
+            "separate_us": (None if args.fused_only or args.timed_only else
                             round(sep_ms[i] * 1e3 / (sep_steps * n_copies), 4)),
             "bytes": b,
             "fused_GBps": round(b / us / 1e3, 1),
@@ -736,7 +965,7 @@ def main():
         sys.exit(3)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.timed_only:
         w0 = [v.cpu() for v in plans[0].views]
         cpu = cpu_baseline(w0, xs_cpu)
 
@@ -749,8 +978,13 @@ def main():
         by_kernel[k] = (t_us + e["fused_us"], b_sum + e["bytes"], n + 1)
     dom = max(by_kernel, key=lambda k: by_kernel[k][0])
     t_us, b_sum, n_m = by_kernel[dom]
-    achieved = b_sum / t_us / 1e3  # GB/s: bytes per launch / average launch duration
-    traffic = recorded_traffic(dom)
+    bytes_launch = b_sum / n_m
+    ev_us = t_us / n_m  # HIP events: timed region / launches, gaps included
+    rec = recorded_kernel(dom)
+    trace_us = (rec or {}).get("trace_avg_ns")
+    trace_us = None if not trace_us else trace_us / 1e3
+    launch_us = trace_us if trace_us else ev_us
+    achieved = bytes_launch / launch_us / 1e3  # GB/s
     roofline = {
         "kernel": dom,
         "bound": "hbm",
@@ -758,13 +992,21 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": traffic,
-        "launch_us": round(t_us / n_m, 4),
-        "bytes_per_launch": round(b_sum / n_m),
-        "note": "per launch, over the token counts this kernel serves in the step; launch "
-                "duration = timed region / launches (HIP events on the launch stream); "
-                "traffic = HBM bytes per launch from rocprofv3 counters (null if the "
-                "kernel changed since they were taken)",
+        "traffic": (rec or {}).get("hbm_bytes_per_launch"),
+        "launch_us": round(launch_us, 4),
+        "launch_us_source": ("rocprofv3 kernel-trace average of the kernel's graph-replayed "
+                             "dispatches, profiles/traffic.json" if trace_us else
+                             "HIP events (no current profile record)"),
+        "bytes_per_launch": round(bytes_launch),
+        "launch_us_events": round(ev_us, 4),
+        "achieved_events": round(bytes_launch / ev_us / 1e3, 1),
+        "frac_events": round(bytes_launch / ev_us / 1e3 / HBM_PEAK_GBS, 4),
+        "note": "per launch, over the token counts this kernel serves in the step: "
+                "achieved = algorithmic bytes per launch / average launch duration; "
+                "launch_us_events = timed region / launches (HIP events on the launch "
+                "stream, inter-kernel gaps included); traffic = HBM bytes per launch from "
+                "rocprofv3 counters; both recorded values are used only while the kernel "
+                "sources match the record",
     }
     us_all = [per_m[str(M)]["fused_us"] for M in MS]
     line = {
@@ -797,8 +1039,10 @@ def main():
                                              floor_us * 1e-6 * n_copies * len(MS)) / 1e9, 1),
         },
         "roofline": roofline,
-        "stream_ceiling": dict(ceiling, fused_M1_over_ceiling=round(
-            per_m["1"]["fused_us"] / ceiling["us_per_call"], 4)),
+        "stream_ceiling": None if ceiling is None else dict(
+            ceiling, fused_M1_over_ceiling=round(per_m["1"]["fused_us"] / ceiling["us_per_call"], 4),
+            fused_minus_ceiling_us={str(M): round(per_m[str(M)]["fused_us"] -
+                                                  ceiling["us_per_call"], 4) for M in MS}),
         "timing_protocol": {
             "trials": "per M: 15 trials of %d graph replays (%d calls each); median, p10, "
                       "p90 per call in per_m[M].trials_us; fused_us is the timed step "
@@ -811,7 +1055,7 @@ def main():
         "context": {"pages_sm107_fused_m1_us": 4.13,
                     "note": "Vera Rubin figure from the pages, other hardware"},
     }
-    if not args.no_epilogues and not args.fused_only:
+    if not args.no_epilogues and not args.fused_only and not args.timed_only:
         line["epilogues"] = epilogue_cells(P, torch, dev, plans, n_copies,
                                            max(3, args.steps // 4))
         line["router_f32"] = router_cells(P, torch, dev, max(3, args.steps // 4))
@@ -822,8 +1066,6 @@ def main():
                                              "indexer_f32")
         line["fused_a_3way"] = workload_cells(P, torch, dev, max(3, args.steps // 4),
                                               "fused_a_3way")
-    if args.crossover:
-        crossover(args.crossover, P, torch, dev, plans, n_copies)
     print(json.dumps(line), flush=True)
     if args.details:
         with open(args.details, "w") as fh:

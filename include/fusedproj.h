@@ -206,6 +206,21 @@ fp_status fp_plan_set_tensor_scales(fp_plan_t plan, const float* scales);
  * `stream`. */
 fp_status fp_stream_read(const void* buf, int64_t bytes, void* sink, void* stream);
 
+/* Measurement aid: fp_stream_read with the launch shape as a parameter --
+ * `groups` workgroups (1..65536) of `threads` threads (a multiple of 64, at
+ * most 1024 for batch 8 and 16, 512 for batch 32), workgroup b reading the
+ * b-th contiguous 1/groups of the buffer, `batch` (8, 16 or 32) 16-byte
+ * non-temporal loads in flight per lane.  Times of the shapes on one pool
+ * show whether the streaming ceiling depends on the launch shape (the
+ * "weights rotated past L2" protocol of "tinygemm2 for the DeepSeek-V4.1
+ * hidden-state projections", Description, applied to a read-only stream).
+ * buf and bytes as fp_stream_read; sink: device, `groups` words, not
+ * overlapping buf.  FP_ERR_UNSUPPORTED for shapes outside these limits,
+ * FP_ERR_INVALID_ARG for negative or null arguments.  Asynchronous on
+ * `stream`. */
+fp_status fp_stream_read_shaped(const void* buf, int64_t bytes, int32_t groups,
+                                int32_t threads, int32_t batch, void* sink, void* stream);
+
 /* The fused call: one launch computes every projection.
  * x: device, M rows with row stride ldx >= K elements (x[m, k] at
  *    x + m*ldx + k), 16-byte aligned rows.

@@ -87,7 +87,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+            ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
              _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -105,6 +105,10 @@ def _load():
                 ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                 ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                 ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_linear_omp.restype = ctypes.c_int
+            lib.oracle_linear_omp.argtypes = lib.oracle_linear.argtypes
+            lib.oracle_omp_threads.restype = ctypes.c_int
+            lib.oracle_omp_threads.argtypes = []
             lib.oracle_round_bf16.restype = ctypes.c_uint16
             lib.oracle_round_bf16.argtypes = [ctypes.c_double]
             lib.oracle_round_bf16_array.restype = None
@@ -176,6 +180,29 @@ def linear(x_bits: np.ndarray, w_bits: np.ndarray, M: int | None = None,
     if rc != 0:
         raise ValueError("oracle_linear rejected its arguments")
     return y, s
+
+
+def linear_omp(x_bits: np.ndarray, w_bits: np.ndarray):
+    """``linear`` with the output elements spread over the host's threads
+    (same per-element loop, bitwise equal results): the multi-core CPU
+    baseline."""
+    dt = _dtype_of(x_bits)
+    x = np.ascontiguousarray(x_bits)
+    w = np.ascontiguousarray(w_bits)
+    N, K = w.shape
+    M, ldx = x.shape
+    y = np.zeros((M, N), dtype=np.float64)
+    s = np.zeros((M, N), dtype=np.float64)
+    rc = _load().oracle_linear_omp(dt, M, N, K, ldx, x.ctypes.data, w.ctypes.data,
+                                   y.ctypes.data, s.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_linear_omp rejected its arguments")
+    return y, s
+
+
+def omp_threads() -> int:
+    """Threads ``linear_omp`` uses."""
+    return int(_load().oracle_omp_threads())
 
 
 def fused_projection(x_bits: np.ndarray, weights: list):

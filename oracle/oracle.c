@@ -29,11 +29,15 @@
  * reference is the pattern of the router GEMV commit of "Staircase: GLM-5.2
  * NVFP4 low-latency decode target for Rubin (TP16)" (TensorRT-LLM PR #20502).
  *
- * Build: gcc -O2 -fPIC -shared (no -ffast-math: IEEE semantics are needed).
+ * Build: gcc -O2 -fopenmp -fPIC -shared (no -ffast-math: IEEE semantics are
+ * needed; OpenMP only spreads oracle_linear_omp's output elements).
  */
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* Exact value of a bf16 bit pattern: bf16 is the upper half of an IEEE
  * binary32, so widening is a 16-bit left shift of the pattern. */
@@ -80,6 +84,41 @@ int oracle_linear(int dtype, int64_t M, int64_t N, int64_t K, int64_t ldx,
     }
   }
   return 0;
+}
+
+/*
+ * oracle_linear with the (m, r) output elements spread over the host's
+ * threads (OpenMP): each element is still the same sequential loop over k,
+ * so the results are bitwise those of oracle_linear.  The multi-core form of
+ * the CPU baseline; the acceptance tests use oracle_linear.
+ */
+int oracle_linear_omp(int dtype, int64_t M, int64_t N, int64_t K, int64_t ldx,
+                      const void* x, const void* w, double* y, double* s) {
+  if ((dtype != 0 && dtype != 1) || M < 0 || N < 0 || K < 0 || ldx < K)
+    return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t r = 0; r < N; ++r) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double p = element(dtype, x, m * ldx + k) * element(dtype, w, r * K + k);
+        acc += p;
+        mag += fabs(p);
+      }
+      y[m * N + r] = acc;
+      s[m * N + r] = mag;
+    }
+  }
+  return 0;
+}
+
+/* Threads oracle_linear_omp runs on (1 when built without OpenMP). */
+int oracle_omp_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 /*

@@ -16,7 +16,7 @@ from ._lib import (FP_BF16, FP_F32, FP_MXFP8, FP_MXFP4, FP_NVFP4, FP_OK, FP_ERR_
                    fp_plan_view, fp_plan_destroy, fp_supported, fp_forward,
                    fp_forward_separate, fp_forward_rmsnorm, fp_mxfp8_to_bf16,
                    fp_mxfp4_to_bf16, fp_nvfp4_to_bf16, fp_plan_set_tensor_scales,
-                   fp_stream_read,
+                   fp_stream_read, fp_stream_read_shaped, fp_forward_noalloc,
                    fp_forward_swiglu, fp_rmsnorm, fp_swiglu, fp_plan_query, fp_plan_set_out_dtype,
                    fp_plan_set_mfma_min_m,
                    fp_plan_set_tiling, fp_plan_get_tiling, fp_default_tiling,

@@ -84,6 +84,7 @@ _SIGS = {
     "fp_nvfp4_to_bf16": (_i32, [_p, _i64, _i64, ctypes.c_float, _p, _p]),
     "fp_plan_set_tensor_scales": (_i32, [_p, ctypes.POINTER(ctypes.c_float)]),
     "fp_stream_read": (_i32, [_p, _i64, _p, _p]),
+    "fp_stream_read_shaped": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p]),
     "fp_forward_rmsnorm": (_i32, [_p, _i64, _i64, _p, _p, _P_p, ctypes.c_float, _P_p]),
     "fp_forward_swiglu": (_i32, [_p, _i64, _i64, _p, _p, _p]),
     "fp_rmsnorm": (_i32, [_p, _i64, _i64, _p, ctypes.c_float, _p, _p]),
@@ -185,6 +186,11 @@ def fp_plan_set_tensor_scales(plan: int, scales) -> int:
 
 def fp_stream_read(buf: int, nbytes: int, sink: int, stream: int) -> int:
     return _lib.fp_stream_read(buf, nbytes, sink, stream)
+
+
+def fp_stream_read_shaped(buf: int, nbytes: int, groups: int, threads: int, batch: int,
+                          sink: int, stream: int) -> int:
+    return _lib.fp_stream_read_shaped(buf, nbytes, groups, threads, batch, sink, stream)
 
 
 def fp_forward_rmsnorm(x: int, M: int, ldx: int, plan: int, stream: int, gamma, eps: float,

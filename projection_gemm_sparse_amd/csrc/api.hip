@@ -24,6 +24,7 @@
 #include "smfma.hpp"
 #include "tile.hpp"
 #include "tile_ring.hpp"
+#include "tile_wres.hpp"
 #include "epilogue.hpp"
 #include "mxfp8.hpp"
 #include "stream.hpp"
@@ -204,6 +205,19 @@ constexpr int kTileNws[] = {2, 4, 8};
 // Ring tile kernel: a tiling of the MFMA path whose chunks field is a ring
 // depth (stage buffers) selects it; kparts is then 4 (64-row blocks).
 constexpr int kRingStages[] = {3, 4, 6};
+// Weight-resident tile kernel: a tiling of the MFMA path whose chunks
+// field is kWresCode selects it; kparts is then 4 (64-row blocks).
+constexpr int kWresCode = 2;
+bool is_wres(const Tiling& t) { return t.chunks == kWresCode; }
+// Stages of two k steps one slice spans with S slices.
+int64_t wres_stages(int64_t kc, int64_t S) {
+  const int64_t per = ceil_div(ceil_div(kc, 4), S);
+  return ceil_div(per, 2);
+}
+bool wres_fits(int64_t kc, int mt16, int64_t S) {
+  return mt16 >= 2 && mt16 <= 16 && wres_stages(kc, S) <= fp::wres_max_stages(16 * mt16);
+}
+
 bool is_ring(const Tiling& t) {
   for (int st : kRingStages)
     if (t.chunks == st) return true;
@@ -275,6 +289,11 @@ bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
     t->splits = (int)S;
     t->kparts = 4;
     t->chunks = mt16 >= 16 ? 3 : 4;
+    // 65..128 tokens: the weight-resident kernel (same slices, same bits)
+    // when its slice fits in LDS; measured on MI355X at K = 5120, 1792 rows,
+    // 9 slices: 16.2 vs 17.0 us at M = 128, 15.3 vs 15.8 at M = 96 (the
+    // ring kernel stays ahead at 64 tokens: 13.0 vs 13.9)
+    if (mt16 == 8 && wres_fits(kc, mt16, S)) t->chunks = kWresCode;
     return true;
   }
   // Measured on MI355X (K = 5120, 1792 rows): four row tiles per workgroup
@@ -306,6 +325,15 @@ bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
   t->splits = (int)pick;
   t->kparts = 0;  // NW, per launch
   t->chunks = 0;  // register bound, per launch
+  // 17..32 tokens: the weight-resident kernel with the same slices (same
+  // bits) when its slice fits in LDS and the launch stays within one round
+  // of workgroups; measured on MI355X at K = 5120, 1792 rows, 8 slices:
+  // 10.0 vs 10.9 us at M = 17, 10.8 vs 11.2 at M = 32
+  if (mt16 == 2 && wres_fits(kc, mt16, pick) &&
+      ceil_div(n_total, fp::kWresRows) * pick <= kCus) {
+    t->kparts = 4;
+    t->chunks = kWresCode;
+  }
   return true;
 }
 
@@ -408,7 +436,7 @@ size_t skinny_lds(const Tiling& t) {
 constexpr int64_t kSecondFinishBytes = 64 * 1024;
 
 void resolve_tile_launch(const fp_plan_s* p, int64_t n_rows, Tiling* t) {
-  if (is_ring(*t)) {
+  if (is_ring(*t) || is_wres(*t)) {
     if (t->kparts <= 0) t->kparts = 4;
     t->rows = 1;
     if (t->groups <= 0) {
@@ -465,7 +493,13 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
   if (t.splits < 1 || t.kparts < 1 || t.chunks < 1 || t.rows < 1) return false;
   // packed into 8- and 16-bit fields of the kernels' scalar arguments
   if (t.splits > 0x1fff || t.kparts > 0xff || t.rows > 0xff || t.groups > 0xff) return false;
-  if (t.path == FP_PATH_MFMA && is_ring(t)) {
+  if (t.path == FP_PATH_MFMA && is_wres(t)) {
+    if (p->dtype != FP_BF16 || t.kparts != 4 || !wres_fits(p->kc, t.mt, t.splits)) return false;
+    if (t.groups != 1 && t.groups != 2) return false;
+    if (16 * (int64_t)t.mt < M) return false;
+    if ((int64_t)t.splits * n_rows * 16 * t.mt * 4 >= ((int64_t)1 << 31)) return false;
+    if (n_rows * p->kc * 16 >= ((int64_t)1 << 31)) return false;
+  } else if (t.path == FP_PATH_MFMA && is_ring(t)) {
     if (p->dtype != FP_BF16 || t.kparts != 4 || !ring_fits(t.mt, t.chunks)) return false;
     if (t.groups != 1 && t.groups != 2) return false;
     if (16 * (int64_t)t.mt < M) return false;
@@ -521,6 +555,8 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
 bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
                    bool pairs = false, const WsView* ws = nullptr) {
   *t = Tiling();
+  // outputs are indexed m * N_i + r with 32-bit integers
+  if (M * n_rows > INT32_MAX) return false;
   if (M >= 1 && M <= FP_MAX_M && p->has_override[M]) {
     const fp_tiling& o = p->override_t[M];
     t->path = o.path;
@@ -622,7 +658,9 @@ size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) 
 // ------------------------------------------------------------------ kernels
 // Kernel addresses come from the per-family units (kernels.h).
 const void* mfma_fn(const Tiling& t) {
-  return is_ring(t) ? fpk::ring(t.mt, t.chunks) : fpk::tile(t.mt, t.kparts, t.chunks);
+  return is_wres(t)   ? fpk::wres(t.mt)
+         : is_ring(t) ? fpk::ring(t.mt, t.chunks)
+                      : fpk::tile(t.mt, t.kparts, t.chunks);
 }
 
 const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype, int64_t M) {
@@ -720,9 +758,11 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
     geo_a = t.splits | (second ? fp::kGeoSecondFinish : 0);
     const int64_t per = ceil_div(ceil_div(p->kc, 4), t.splits);
     const int64_t blocks = ceil_div(lr.n_rows, 16 * (int64_t)t.kparts) * t.splits;
-    const size_t lds = is_ring(t) ? ring_lds(t.mt, t.chunks)
+    const size_t lds = is_wres(t)   ? (size_t)fp::wres_lds_bytes(16 * t.mt)
+                       : is_ring(t) ? ring_lds(t.mt, t.chunks)
                                   : std::max<size_t>(tile_lds(t.mt, per, t.kparts), 16);
-    fp_status st = launch(mfma_fn(t), blocks, t.kparts * 64, lds, args, stream);
+    const int threads = is_wres(t) ? fp::wres_threads(16 * t.mt) : t.kparts * 64;
+    fp_status st = launch(mfma_fn(t), blocks, threads, lds, args, stream);
     if (st != FP_OK || !second) return st;
     // the slices, added in slice order over the whole GPU
     const float* part_a = tail.partial;
@@ -760,6 +800,9 @@ fp_status check_x(const fp_plan_s* p, int64_t M, const void* x, int64_t ldx) {
   if (ldx * p->esize > INT32_MAX) return FP_ERR_UNSUPPORTED;  // 32-bit row stride
   if (p->dtype == FP_F32 && M > kSkinnyMaxM) return FP_ERR_UNSUPPORTED;
   if (p->out_f32 && M > skinny_max_m(p)) return FP_ERR_UNSUPPORTED;
+  // the kernels index an output element m * N_i + r with 32-bit integers
+  for (int i = 0; i < p->n_proj; ++i)
+    if (M * p->N[i] > INT32_MAX) return FP_ERR_UNSUPPORTED;
   return FP_OK;
 }
 
@@ -1159,6 +1202,25 @@ fp_status fp_stream_read(const void* buf, int64_t bytes, void* sink, void* strea
   void* args[] = {&b_a, &bytes_a, &per_a, &s_a};
   return launch(fpk::stream_read(), fp::kStreamGroups,
                 fp::kStreamThreads, 0, args, static_cast<hipStream_t>(stream));
+}
+
+fp_status fp_stream_read_shaped(const void* buf, int64_t bytes, int32_t groups, int32_t threads,
+                                int32_t batch, void* sink, void* stream) {
+  if (bytes < 0 || groups < 1 || threads < 64) return FP_ERR_INVALID_ARG;
+  if (bytes == 0) return FP_OK;
+  if (buf == nullptr || sink == nullptr) return FP_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(sink, 4) || bytes % 16 != 0) return FP_ERR_UNSUPPORTED;
+  if (bytes >= ((int64_t)1 << 31) || groups > 65536 || threads % 64 != 0) return FP_ERR_UNSUPPORTED;
+  if (!(batch == 8 || batch == 16 || batch == 32)) return FP_ERR_UNSUPPORTED;
+  if (threads > fp::stream_shaped_max_threads(batch)) return FP_ERR_UNSUPPORTED;
+  if (range_overlaps(buf, bytes, sink, 4 * (int64_t)groups)) return FP_ERR_INVALID_ARG;
+  const unsigned char* b_a = static_cast<const unsigned char*>(buf);
+  uint32_t bytes_a = (uint32_t)bytes;
+  uint32_t per_a = (uint32_t)ceil_div(bytes / 16, groups);
+  uint32_t* s_a = static_cast<uint32_t*>(sink);
+  void* args[] = {&b_a, &bytes_a, &per_a, &s_a};
+  return launch(fpk::stream_read_shaped(batch), groups, threads, 0, args,
+                static_cast<hipStream_t>(stream));
 }
 
 fp_status fp_mxfp4_to_bf16(const void* w, int64_t rows, int64_t K, void* out, void* stream) {

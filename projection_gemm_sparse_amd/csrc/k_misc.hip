@@ -27,5 +27,13 @@ const void* mxfp4_to_bf16() { return reinterpret_cast<const void*>(&fp::mxfp4_to
 const void* nvfp4_to_bf16() { return reinterpret_cast<const void*>(&fp::nvfp4_to_bf16_kernel); }
 const void* stream_read() { return reinterpret_cast<const void*>(&fp::stream_read_kernel); }
 const void* fill_u32() { return reinterpret_cast<const void*>(&fp::fill_u32_kernel); }
+const void* stream_read_shaped(int batch) {
+  switch (batch) {
+    case 8: return reinterpret_cast<const void*>(&fp::stream_read_shaped_kernel<8>);
+    case 16: return reinterpret_cast<const void*>(&fp::stream_read_shaped_kernel<16>);
+    case 32: return reinterpret_cast<const void*>(&fp::stream_read_shaped_kernel<32>);
+    default: return nullptr;
+  }
+}
 
 }  // namespace fpk

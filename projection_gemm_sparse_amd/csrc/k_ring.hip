@@ -1,6 +1,8 @@
-// k_ring.hip -- ring tile kernel instantiations (tile_ring.hpp).
+// k_ring.hip -- ring tile and weight-resident tile kernel instantiations
+// (tile_ring.hpp, tile_wres.hpp).
 #include "kernels.h"
 #include "tile_ring.hpp"
+#include "tile_wres.hpp"
 
 namespace {
 
@@ -32,6 +34,16 @@ const void* ring(int mt16, int stages) {
     case 4: return ring_st<2, 2, 2, 2>(stages);
     case 8: return ring_st<2, 2, 2, 4>(stages);
     case 16: return ring_st<2, 2, 2, 8>(stages);
+    default: return nullptr;
+  }
+}
+
+const void* wres(int mt16) {
+  switch (mt16) {
+    case 2: return reinterpret_cast<const void*>(&fp::wres_tile_kernel<1>);
+    case 4: return reinterpret_cast<const void*>(&fp::wres_tile_kernel<2>);
+    case 8: return reinterpret_cast<const void*>(&fp::wres_tile_kernel<4>);
+    case 16: return reinterpret_cast<const void*>(&fp::wres_tile_kernel<8>);
     default: return nullptr;
   }
 }

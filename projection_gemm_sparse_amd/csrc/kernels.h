@@ -33,6 +33,9 @@ const void* smfma_mx(int32_t dtype, int mh, int kt);
 const void* tile(int mt16, int nw, int per);
 // Ring tile kernel (tile_ring.hpp): 16 * mt16 token slots, `stages` buffers.
 const void* ring(int mt16, int stages);
+// Weight-resident tile kernel (tile_wres.hpp): 16 * mt16 token slots
+// (mt16 2, 4, 8 or 16).
+const void* wres(int mt16);
 // Second-launch finish of a split tile launch.
 const void* splitk_reduce();
 
@@ -44,5 +47,8 @@ const void* mxfp4_to_bf16();
 const void* nvfp4_to_bf16();
 const void* stream_read();
 const void* fill_u32();
+// The streaming kernel with its launch shape as a parameter: BATCH loads in
+// flight per lane (8, 16 or 32).
+const void* stream_read_shaped(int batch);
 
 }  // namespace fpk

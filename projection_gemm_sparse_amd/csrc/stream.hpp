@@ -50,4 +50,41 @@ stream_read_kernel(const unsigned char* __restrict__ buf, uint32_t bytes, uint32
 
 #endif  // FP_DEFINE_MISC_KERNELS
 
+// The same read-only stream with the launch shape as a parameter (the
+// launch-shape sweep of the streaming ceiling): `gridDim.x` workgroups of
+// `blockDim.x` threads (<= the bound below), workgroup b reading the b-th
+// contiguous per_wg vectors, BATCH loads in flight per lane.
+__host__ __device__ constexpr int stream_shaped_max_threads(int batch) {
+  return batch <= 16 ? 1024 : 512;
+}
+
+template <int BATCH>
+__global__ void __launch_bounds__(stream_shaped_max_threads(BATCH))
+stream_read_shaped_kernel(const unsigned char* __restrict__ buf, uint32_t bytes, uint32_t per_wg,
+                          uint32_t* __restrict__ sink) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(buf, bytes);
+  const uint32_t nt = blockDim.x;
+  const uint32_t v0 = blockIdx.x * per_wg;
+  const uint32_t v1 = v0 + per_wg;
+  const uint32_t n_vec = bytes >> 4;
+  const uint32_t end = v1 < n_vec ? v1 : n_vec;
+  const uint32_t rounds = end > v0 ? (end - v0 + nt - 1) / nt : 0u;
+  unsigned acc = 0u;
+  for (uint32_t j0 = 0; j0 < rounds; j0 += BATCH) {
+    u32x4 v[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (j0 + j < rounds) {
+        const uint32_t i = v0 + (j0 + j) * nt + threadIdx.x;
+        const uint32_t off = i < end ? i * 16u : kOob;
+        v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNt));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
 }  // namespace fp

@@ -28,6 +28,18 @@ def _stream_handle(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _hold_for_stream(tensors, stream) -> None:
+    """Tensors allocated here (on the current stream's pool) and used by work
+    enqueued on another ``stream``: mark them in use by that stream, so the
+    caching allocator does not hand their memory out again before that work
+    has run (torch's record_stream)."""
+    if stream is None or not hasattr(stream, "cuda_stream"):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 class FusedProjection:
     """Fuses projections ``weights[i]`` ([N_i, K], one dtype, on one GPU).
 
@@ -151,10 +163,12 @@ class FusedProjection:
         return L.fp_supported(self.plan, int(x.shape[0]), x.data_ptr(), int(x.stride(0))) == L.FP_OK
 
     # ---------------------------------------------------------------- calls
-    def _outputs(self, M: int, out):
+    def _outputs(self, M: int, out, stream=None):
         if out is not None:
             return out
-        return [torch.empty(M, n, dtype=self.out_dtype, device=self.device) for n in self.N]
+        ys = [torch.empty(M, n, dtype=self.out_dtype, device=self.device) for n in self.N]
+        _hold_for_stream(ys, stream)
+        return ys
 
     def _check_x(self, x):
         if x.dim() != 2 or int(x.shape[1]) != self.K or x.stride(1) != 1:
@@ -166,7 +180,7 @@ class FusedProjection:
         """Fused call: returns one dense [M, N_i] tensor per projection."""
         self._check_x(x)
         M = int(x.shape[0])
-        ys = self._outputs(M, out)
+        ys = self._outputs(M, out, stream)
         st = L.fp_forward(x.data_ptr(), M, int(x.stride(0)), self.plan,
                           _stream_handle(stream), [y.data_ptr() for y in ys])
         L.check(st, "fp_forward")
@@ -179,7 +193,7 @@ class FusedProjection:
         replaces projection i's view."""
         self._check_x(x)
         M = int(x.shape[0])
-        ys = self._outputs(M, out)
+        ys = self._outputs(M, out, stream)
         ov = None
         if w_override is not None:
             ov = []
@@ -204,6 +218,10 @@ class FusedProjection:
         if all(intact):
             return self.forward(x, out=out, stream=stream)
         ov = [None if ok else w.detach().contiguous() for ok, w in zip(intact, weights)]
+        # a non-contiguous replaced weight gets a contiguous temporary that
+        # the separate launches on `stream` read after this call returns
+        _hold_for_stream([t for t, w in zip(ov, weights) if t is not None and t is not w],
+                         stream)
         return self.forward_separate(x, out=out, w_override=ov, stream=stream)
 
     # ------------------------------------------------------------ epilogues
@@ -226,7 +244,7 @@ class FusedProjection:
         ``gammas[i]`` (bf16 [N_i]) or returned as is when that entry is None."""
         self._check_x(x)
         M = int(x.shape[0])
-        ys = self._outputs(M, out)
+        ys = self._outputs(M, out, stream)
         st = L.fp_forward_rmsnorm(x.data_ptr(), M, int(x.stride(0)), self.plan,
                                   _stream_handle(stream), self._gains(gammas), eps,
                                   [y.data_ptr() for y in ys])
@@ -252,8 +270,10 @@ class FusedProjection:
         gate first): returns h, dense [M, N]."""
         self._check_x(x)
         M = int(x.shape[0])
-        h = out if out is not None else torch.empty(M, self.N[0], dtype=self.dtype,
-                                                    device=self.device)
+        h = out
+        if h is None:
+            h = torch.empty(M, self.N[0], dtype=self.dtype, device=self.device)
+            _hold_for_stream([h], stream)
         st = L.fp_forward_swiglu(x.data_ptr(), M, int(x.stride(0)), self.plan,
                                  _stream_handle(stream), h.data_ptr())
         L.check(st, "fp_forward_swiglu")

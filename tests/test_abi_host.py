@@ -149,6 +149,11 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
             # the ring tile kernel (33 tokens and more): 64-row blocks,
             # chunks = stage buffers
             assert M >= 33 and kp == 4 and (ch == 3) == (M > 128)
+        elif path == P.FP_PATH_MFMA and ch == 2:
+            # the weight-resident tile kernel (17..32 and 65..128 tokens):
+            # 64-row blocks, a slice of at most 16 (12) stages of 64 k
+            assert (17 <= M <= 32 or 65 <= M <= 128) and kp == 4
+            assert -(-(-(-kc // 4) // S) // 2) <= (16 if M <= 32 else 12)
         elif path == P.FP_PATH_MFMA:
             # kparts = row tiles per workgroup, chunks = compiled register
             # bound of k steps (4 pieces of 16 bytes) per slice
@@ -280,3 +285,10 @@ def test_nvfp4_geometry_and_refusals():
     # tensor scales on a null plan
     assert P.fp_plan_set_tensor_scales(None, [1.0]) == P.FP_ERR_INVALID_ARG
     assert P.fp_plan_set_tensor_scales(FAKE, [1.0]) == P.FP_ERR_INVALID_ARG
+
+
+def test_outputs_beyond_32_bit_indexing_are_refused():
+    # 8 tokens x 310M rows: an output index m * N + r past 2^31 - 1
+    n = 310 * 1000 * 1000
+    assert P.fp_default_tiling(P.FP_BF16, 8, n, 8, n)[0] == P.FP_ERR_UNSUPPORTED
+    assert P.fp_default_tiling(P.FP_BF16, 8, n, 6, n)[0] == P.FP_OK  # 1.86e9 < 2^31

@@ -7,8 +7,10 @@ with no positive control.  Here every replay gets new inputs written into
 the captured input buffer, the program's own eager calls and
 synchronizations run between replays, every replay is compared with an
 eager run, and a positive control (a perturbed input) must be detected.
-The split-K path is included: its arrival counters reset themselves, so
-replays need no host action.
+Split-K launches are included -- the tile and ring tile kernels of the
+crossover cases (32, 64 and 128 tokens) and a forced K split of the
+vector-ALU kernel (the fp32 indexer fusion, its in-launch finish) -- and
+their arrival counters reset themselves, so replays need no host action.
 """
 import ctypes
 
@@ -136,3 +138,39 @@ def test_launch_count_fused_one_separate_n(name, M):
     torch.cuda.synchronize()
     path, lf, ls = fp.query(M)
     assert (n_fused, n_sep) == (lf, ls) == (1, len(fp.N))
+
+
+def test_replay_of_a_split_vector_alu_launch():
+    """The vector-ALU kernel's in-launch split-K finish under replay: the
+    fp32 indexer fusion with its K split across 4 workgroups (partials in
+    the workspace, the last workgroup adds them), three new inputs and a
+    300-replay stress, each replay against an eager call."""
+    M = 8
+    split = (P.FP_PATH_SKINNY_SPLITK, 7, 1, 4, 0, 0)
+    x0, ws = si.workload_case("indexer_f32", M, 0)
+    fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=M, workspace_bytes=1 << 20)
+    assert fp.set_tiling(M, split) == P.FP_OK
+    assert fp.query(M)[0] == P.FP_PATH_SKINNY_SPLITK
+    x_static = to_gpu(x0)
+    outs = [torch.empty(M, n, dtype=x_static.dtype, device="cuda") for n in fp.N]
+    g = _capture(fp, x_static, outs)
+    for seed in (21, 22, 23):
+        xn, _ = si.workload_case("indexer_f32", M, seed)
+        x_static.copy_(to_gpu(xn))
+        g.replay()
+        torch.cuda.synchronize()
+        eager = fp(x_static)
+        assert_bitwise_equal(outs, eager, "split replay seed %d" % seed)
+        assert_matches_oracle(outs, xn, ws, label="split replay")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+    mismatches = 0
+    for _ in range(300):
+        x_static.copy_(torch.randn(x_static.shape, generator=gen, device="cuda"))
+        g.replay()
+        eager = fp(x_static)
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            mismatches += int(not torch.equal(a.view(torch.int32), b.view(torch.int32)))
+    assert mismatches == 0
+    fp.set_tiling(M, None)

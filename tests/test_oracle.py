@@ -391,3 +391,17 @@ def test_pins_catch_planted_mistakes(mutation):
             if not np.array_equal(bad, expect):
                 caught = True
     assert caught, mutation
+
+
+def test_multicore_oracle_is_the_same_loop():
+    # the OpenMP form spreads the output elements over threads; every
+    # element is still the sequential k loop, so the results are bitwise
+    # those of the single-threaded oracle (bf16 and fp32 patterns)
+    rng = np.random.default_rng(21)
+    for dt, mask in ((np.uint16, 0x3fff), (np.uint32, 0x3fffffff)):
+        x = (rng.integers(0, 2 ** 31, (5, 300)) & mask).astype(dt)
+        w = (rng.integers(0, 2 ** 31, (37, 288)) & mask).astype(dt)
+        ya, sa = oracle.linear(x, w, K=288)
+        yb, sb = oracle.linear_omp(np.ascontiguousarray(x[:, :288]), w)
+        assert np.array_equal(ya, yb) and np.array_equal(sa, sb)
+    assert oracle.omp_threads() >= 1

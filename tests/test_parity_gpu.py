@@ -373,3 +373,53 @@ def test_ring_tile_max_m_and_strided_x():
             assert fp.set_tiling(M, _ring(3, S, finish)) == P.FP_OK
             _check_case(fp, x, ws, "ring M=256 S=%d finish=%d" % (S, finish), rows=rows)
     fp.set_tiling(M, None)
+
+
+# ---- the weight-resident tile kernel (an MFMA tiling whose chunks field is
+#      2; 64-row blocks, the slice's weights resident in LDS, activations
+#      through a ring filled by producer waves): same bits as the ring tile
+#      kernel for the same slices, either finish
+def _wres(S, finish):
+    return (P.FP_PATH_MFMA, 4, 2, S, 0, finish)
+
+
+@pytest.mark.parametrize("M", [17, 32, 40, 64, 100, 128, 200])
+def test_weight_resident_tile_kernel(M):
+    x, ws = si.workload_case("crossover", M, 12)
+    fp = _plan(ws, max_M=256, workspace_bytes=64 << 20)
+    xg = to_gpu(x)
+    rows = sorted({0, 1, M // 2, M - 1} | set(range(3, M, 29)))
+    ran = 0
+    for S in (5, 7, 9, 12):
+        for finish in (1, 2):
+            st = fp.set_tiling(M, _wres(S, finish))
+            if st != P.FP_OK:
+                # a slice longer than the LDS holds (few slices, many tokens)
+                assert st == P.FP_ERR_UNSUPPORTED, (M, S, st)
+                continue
+            ran += 1
+            label = "wres M=%d S=%d finish=%d" % (M, S, finish)
+            ys = fp(xg)
+            assert_matches_oracle(ys, x, ws, rows=rows, label=label)
+            assert_bitwise_equal(ys, fp.forward_separate(xg), label + " fused/sep")
+            assert_bitwise_equal(ys, fp(xg), label + " repeat")
+            assert fp.set_tiling(M, _ring(3 if M > 128 else 4, S, finish)) == P.FP_OK
+            assert_bitwise_equal(ys, fp(xg), label + " vs ring tile kernel")
+    assert ran >= 2, M
+    fp.set_tiling(M, None)
+
+
+def test_weight_resident_tile_kernel_ragged_rows():
+    # row counts that leave a partial 64-row block and 16-row tile, K with a
+    # partial last stage (K = 5120 + 32)
+    K, N, M = 5152, (100, 37, 200), 48
+    x, ws = si.make_case(K, N, "bf16", M, seed=5)
+    fp = _plan(ws, max_M=64, workspace_bytes=32 << 20)
+    xg = to_gpu(x)
+    for S in (6, 9):
+        for finish in (1, 2):
+            assert fp.set_tiling(M, _wres(S, finish)) == P.FP_OK
+            ys = fp(xg)
+            assert_matches_oracle(ys, x, ws, label="wres ragged S=%d f=%d" % (S, finish))
+            assert_bitwise_equal(ys, fp.forward_separate(xg), "wres ragged fused/sep")
+    fp.set_tiling(M, None)
