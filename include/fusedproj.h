@@ -117,7 +117,11 @@ typedef enum {
 
 /* Bytes of device workspace a plan needs (split-K partial sums and the
  * self-resetting arrival counters), for dtype `dtype`, contraction length K,
- * the n_proj row counts N[] and token counts up to max_M.  Returns 0 on an
+ * the n_proj row counts N[] and token counts up to max_M.  The fp32 sums
+ * of a row's K slices are kept apart and added in a fixed order ("FP32 in a
+ * fixed order", dense-MLP commit of PR #20502; the fused-A commit splits
+ * its 6144 contraction over two CTAs the same way), which is what needs
+ * this memory.  Returns 0 on an
  * invalid argument (and for shapes that need no workspace it still returns a
  * small positive size for the counters). */
 size_t fp_workspace_bytes(int32_t dtype, int64_t K, int32_t n_proj,
@@ -150,7 +154,10 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj,
 fp_status fp_plan_view(fp_plan_t plan, int32_t i, void** w_i,
                        int64_t* row_offset, int64_t* rows);
 
-/* Frees the plan's host state.  The borrowed buffers are untouched. */
+/* Frees the plan's host state.  The borrowed buffers are untouched: the
+ * concatenated weight and its views outlive the plan, as the fused buffer
+ * of PR #20636 (Description) outlives the modules that view it.  A stale or
+ * already destroyed plan returns FP_ERR_INVALID_ARG. */
 fp_status fp_plan_destroy(fp_plan_t plan);
 
 /* Host-only predicate (no HIP call): FP_OK if fp_forward serves token count
@@ -221,7 +228,10 @@ fp_status fp_stream_read(const void* buf, int64_t bytes, void* sink, void* strea
 fp_status fp_stream_read_shaped(const void* buf, int64_t bytes, int32_t groups,
                                 int32_t threads, int32_t batch, void* sink, void* stream);
 
-/* The fused call: one launch computes every projection.
+/* The fused call: one launch computes every projection ("one call for the
+ * fused weight", the halves "returned with dense strides": PR #20636,
+ * Description; outputs rounded to bf16 once from fp32 sums added in a fixed
+ * order: fused-A commit of PR #20502).
  * x: device, M rows with row stride ldx >= K elements (x[m, k] at
  *    x + m*ldx + k), 16-byte aligned rows.
  * y: host array of n_proj device pointers; y[i] receives the dense
@@ -405,10 +415,15 @@ fp_status fp_default_tiling(int32_t dtype, int64_t K, int64_t n_total, int64_t M
 fp_status fp_forward_noalloc(const void* x, int64_t M, int64_t ldx, fp_plan_t plan,
                              void* stream, void* const* y);
 
-/* Static text for a status code. */
+/* Static text for a status code: the reason a call was refused, for the
+ * caller's fallback to its plain linear layers (the fallback list of PR
+ * #20636, Description; "raise otherwise" in the dense-MLP commit of PR
+ * #20502). */
 const char* fp_status_str(int32_t status);
 
-/* The hipError_t of the last failing HIP call made by this thread. */
+/* The hipError_t of the last failing HIP call made by this thread (the
+ * detail behind FP_ERR_HIP; the C ABI carries no exceptions, the
+ * boundary the dense-MLP commit of PR #20502 draws with its host query). */
 int32_t fp_last_hip_error(void);
 
 #ifdef __cplusplus

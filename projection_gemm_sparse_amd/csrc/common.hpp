@@ -291,17 +291,25 @@ __device__ __forceinline__ bf16x2 decode_e2m1_pair(unsigned u, float scale) {
 // value as fp32: at most 4 significant bits), as a bf16 pair.
 // v_cvt_scalef32_pk_bf16_fp4 applies only the exponent of its fp32 scale
 // operand (measured on MI355X: code 0.5 at scale 1.5 gives 0.5), which is
-// all an E8M0 scale has; here the codes are decoded at scale 1, multiplied
-// by s in fp32 (exact: at most 2 + 4 significant bits) and cut back to
-// bf16 (exact for the same reason).
+// all an E8M0 scale has; here the codes are decoded to fp32 at scale 1
+// (v_cvt_scalef32_pk_f32_fp4), multiplied by s in fp32 (exact: at most
+// 2 + 4 significant bits) and converted to bf16 (v_cvt_pk_bf16_f32, exact
+// for the same reason).
 template <int B>
 __device__ __forceinline__ bf16x2 decode_e2m1_pair_nv(unsigned u, float s) {
 #pragma clang fp contract(off)
-  const unsigned d = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, B));
-  const float lo = u2f(d << 16) * s;
-  const float hi = u2f(d & 0xffff0000u) * s;
-  return __builtin_bit_cast(bf16x2, (__builtin_bit_cast(unsigned, lo) >> 16) |
-                                        (__builtin_bit_cast(unsigned, hi) & 0xffff0000u));
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, B);
+  const float lo = d[0] * s;
+  const float hi = d[1] * s;
+  return bf16x2{(__bf16)lo, (__bf16)hi};
+}
+
+// Two E4M3 codes (bytes 0 and 1 of u) as fp32 values (exact; OCP E4M3:
+// bias 7, subnormals m * 2^-9): v_cvt_scalef32_pk_f32_fp8 at scale 1.
+__device__ __forceinline__ void e4m3x2_to_f32(unsigned u, float* lo, float* hi) {
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, 1.0f, false);
+  *lo = d[0];
+  *hi = d[1];
 }
 
 // An E4M3 code as an fp32 value (exact: 4 significant bits; sign, 4

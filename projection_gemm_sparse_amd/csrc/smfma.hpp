@@ -402,8 +402,13 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
     // MX: scale 2^(s - 127) as an fp32 (s = 0: the subnormal 2^-127);
     // NVFP4: the E4M3 scales of the group's two blocks (units 0, 1 and 2, 3)
     const uint32_t sb = sv[u];
-    const float sc = NV ? e4m3_to_f32(sb & 0xffu) : u2f(sb != 0u ? sb << 23 : 0x00400000u);
-    const float sc_hi = NV ? e4m3_to_f32(sb >> 8) : sc;
+    float sc, sc_hi;
+    if constexpr (NV) {
+      e4m3x2_to_f32(sb, &sc, &sc_hi);
+    } else {
+      sc = u2f(sb != 0u ? sb << 23 : 0x00400000u);
+      sc_hi = sc;
+    }
 #pragma unroll
     for (int e = 0; e < G; ++e) {
       const float sce = e < 2 ? sc : sc_hi;
