@@ -88,6 +88,54 @@ __host__ __device__ constexpr int tile_slots(int mt16, int per, int nw, int cs, 
 // counter words (one per row).
 constexpr int kTileCounterStride = 32;
 
+// The S partial slices of four consecutive token slots, added in slice
+// order s = 0, 1, ..., S-1 (the first slice as is, then one fp32 add per
+// slice and slot).  Loads are issued in groups of GRP before the adds of
+// the group: one memory latency per group.  From a buffer resource (byte
+// offset `off` of slice 0, `sstride` bytes between slices; agent-coherent
+// loads) or from a plain pointer (slice stride `vstride` 16-byte vectors).
+template <int GRP>
+__device__ __forceinline__ f32x4 sum_slices_rsrc(__amdgpu_buffer_rsrc_t pr, uint32_t off,
+                                                 uint32_t sstride, int S) {
+  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += GRP) {
+    f32x4 v[GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const uint32_t o = s0 + j < S ? off + (uint32_t)(s0 + j) * sstride : kOob;
+      v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, 16));
+    }
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      if (s0 + j < S) {
+        const float a0 = sum[0], a1 = sum[1], a2 = sum[2], a3 = sum[3];
+        const float b0 = v[j][0], b1 = v[j][1], b2 = v[j][2], b3 = v[j][3];
+        sum = s0 + j == 0 ? v[j] : f32x4{a0 + b0, a1 + b1, a2 + b2, a3 + b3};
+      }
+    }
+  }
+  return sum;
+}
+
+template <int GRP>
+__device__ __forceinline__ f32x4 sum_slices_ptr(const f32x4* p, int64_t vstride, int S) {
+  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += GRP) {
+    f32x4 v[GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) v[j] = s0 + j < S ? p[(s0 + j) * vstride] : sum;
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      if (s0 + j < S) {
+        const float a0 = sum[0], a1 = sum[1], a2 = sum[2], a3 = sum[3];
+        const float b0 = v[j][0], b1 = v[j][1], b2 = v[j][2], b3 = v[j][3];
+        sum = s0 + j == 0 ? v[j] : f32x4{a0 + b0, a1 + b1, a2 + b2, a3 + b3};
+      }
+    }
+  }
+  return sum;
+}
+
 // Sum of the S partial slices of a row block, in slice order, by the
 // workgroup that arrives last; four consecutive token slots per thread and
 // step (partials are [S][n_rows][m_pad] fp32, m_pad a multiple of 16, stored
@@ -118,25 +166,10 @@ __device__ __forceinline__ void splitk_finish_vec(const float* partial, uint32_t
     const int m0 = (t - rr * vec_per_row) * 4;
     const int row = row_base + rr;
     const uint32_t off = ((uint32_t)row * (uint32_t)m_pad + (uint32_t)m0) * 4u;
-    // the S slices in groups of 8: all loads of a group are issued before
-    // the first add, then added in slice order
-    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      f32x4 v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t o = s0 + j < S ? off + (uint32_t)(s0 + j) * sstride : kOob;
-        v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, 16));
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (s0 + j < S) {
-          const float a0 = sum[0], a1 = sum[1], a2 = sum[2], a3 = sum[3];
-          const float b0 = v[j][0], b1 = v[j][1], b2 = v[j][2], b3 = v[j][3];
-          sum = s0 + j == 0 ? v[j] : f32x4{a0 + b0, a1 + b1, a2 + b2, a3 + b3};
-        }
-      }
-    }
+    // the S slices in groups (8, or 16 above 8 slices): all loads of a
+    // group are issued before the first add, then added in slice order
+    const f32x4 sum = S <= 8 ? sum_slices_rsrc<8>(pr, off, sstride, S)
+                             : sum_slices_rsrc<16>(pr, off, sstride, S);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float vj = sum[j];
@@ -313,23 +346,10 @@ splitk_reduce_kernel(const float* __restrict__ partial, int32_t n_rows, int32_t 
   const int m0 = (int)(t - (int64_t)row * vec_per_row) * 4;
   const int64_t sstride = (int64_t)n_rows * m_pad;
   const f32x4* p = reinterpret_cast<const f32x4*>(partial + (int64_t)row * m_pad + m0);
-  // the slices in groups of 8: all loads of a group are issued before the
-  // first add (one load latency per group, not per slice), then added in
-  // slice order
-  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    f32x4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = s0 + j < S ? p[(s0 + j) * sstride / 4] : sum;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (s0 + j < S) {
-        const float a0 = sum[0], a1 = sum[1], a2 = sum[2], a3 = sum[3];
-        const float b0 = v[j][0], b1 = v[j][1], b2 = v[j][2], b3 = v[j][3];
-        sum = s0 + j == 0 ? v[j] : f32x4{a0 + b0, a1 + b1, a2 + b2, a3 + b3};
-      }
-    }
-  }
+  // the slices in groups (8, or 16 above 8 slices): all loads of a group
+  // are issued before the first add (one load latency per group, not per
+  // slice), then added in slice order
+  const f32x4 sum = S <= 8 ? sum_slices_ptr<8>(p, sstride / 4, S) : sum_slices_ptr<16>(p, sstride / 4, S);
   // the row's segment: the last one whose first row is at or before it
   int seg = 0;
   for (int i = 1; i < tab.n_seg; ++i) seg = row >= tab.begin[i] ? i : seg;
