@@ -792,9 +792,9 @@ def main():
                     help="only the warm-up and timed steps of the fused graphs (profiler runs: "
                          "every dispatch is a graph replay of the timed step)")
     ap.add_argument("--mfma-only", action="store_true",
-                    help="time only the matrix-core cells (M = 8 on the small-M kernel, "
-                         "9..128 on the tile kernel) and print them (profiler runs of the "
-                         "MFMA counters); not the benchmark line")
+                    help="time only the matrix-core cells (M = 8..16 on the small-M kernel, "
+                         "17..128 on the tile kernels) and print them (profiler runs of the "
+                         "MFMA and HBM counters); not the benchmark line")
     ap.add_argument("--pool-sweep", default="",
                     help="write a pool-size sweep (per-call time vs rotated pool size) to "
                          "PREFIX.json and PREFIX.md and exit")
@@ -822,7 +822,7 @@ def main():
         n_copies = max(2, math.ceil((args.pool_mib << 20) / w_bytes))
         plans = build_pool(P, torch, n_copies, 128)
         res = {}
-        for M in (8, 9, 16, 32, 64, 128):
+        for M in (8, 9, 16, 17, 32, 48, 64, 96, 128):
             x = si2.make_case(K, N, "bf16", M, seed=800 + M)[0].to(dev)
             out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
             gr = capture(torch, lambda: [p.forward(x, out=out) for p in plans])
@@ -831,6 +831,12 @@ def main():
                            "tiling": list(plans[0].get_tiling(M)),
                            "flops": 2 * M * sum(N) * K}
             del gr
+        if args.calib_copy_mib:
+            src = torch.ones((args.calib_copy_mib << 20) // 2, dtype=torch.bfloat16, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                torch.neg(src, out=dst)
+            torch.cuda.synchronize()
         print(json.dumps({"mfma": res}), flush=True)
         return
     if args.indexer_splits:
