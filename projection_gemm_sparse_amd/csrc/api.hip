@@ -530,6 +530,10 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     if (smfma_lds(t) > kMaxLds) return false;
   } else if (t.path == FP_PATH_SKINNY || t.path == FP_PATH_SKINNY_SPLITK) {
     if (M > skinny_max_m(p) || t.kparts > fp::kMaxWaveParts) return false;
+    // fp32 outputs are held to 1e-5 * S: every output passes through at
+    // most 8 + 6 + 15 adds before the slices and S - 1 after them, which
+    // 128 slices keep below the 166 that bound allows
+    if ((p->dtype == FP_F32 || p->out_f32) && t.splits > 128) return false;
     if (t.mt > 8 && !(p->out_f32 && t.chunks <= 2 && t.rows <= 4)) return false;
     if (t.rows > 8 || t.rows * t.mt > 64) return false;
     const bool cj_ok = t.chunks <= 2 || (t.mt <= 2 && t.rows <= 2 &&
