@@ -6,6 +6,8 @@ fp64 result under the acceptance bound (bf16: 2^-7 * S + 1e-6, fp32:
 outputs must be bitwise equal, and so must repeats.  Integer-valued data
 must be bit exact (every partial sum is an exact integer below 2^24).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -423,3 +425,49 @@ def test_weight_resident_tile_kernel_ragged_rows():
             assert_matches_oracle(ys, x, ws, label="wres ragged S=%d f=%d" % (S, finish))
             assert_bitwise_equal(ys, fp.forward_separate(xg), "wres ragged fused/sep")
     fp.set_tiling(M, None)
+
+
+# ---- the pages' own fused-A shapes at hidden 6144 (pinned as concatenation
+#      shapes in tests/golden/page_shapes.txt): 2624 rows = 2048 + 512 + 64,
+#      and 2784 rows with the 160 indexer rows appended as a fourth
+#      projection; every token count the fused call serves by default up to
+#      16, each kernel on these row counts, and graph replay of the 2784-row
+#      plan
+def _page_shape(name):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "page_shapes.txt")
+    for ln in open(path):
+        f = ln.split()
+        if f and f[0] == name:
+            eq = f.index("=")
+            return int(f[1]), tuple(int(v) for v in f[2:eq])
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["glm_fused_a", "glm_fused_a_indexer"])
+@pytest.mark.parametrize("M", [1, 3, 5, 8, 13, 16])
+def test_page_fused_a_shapes_through_the_kernels(name, M):
+    K, N = _page_shape(name)
+    x, ws = si.make_case(K, N, "bf16", M, seed=31 + M)
+    fp = _plan(ws, max_M=16)
+    _check_case(fp, x, ws, "%s M=%d" % (name, M))
+
+
+def test_page_fused_a_indexer_shape_graph_replay():
+    K, N = _page_shape("glm_fused_a_indexer")
+    M = 4
+    x0, ws = si.make_case(K, N, "bf16", M, seed=40)
+    fp = _plan(ws, max_M=8)
+    xs = to_gpu(x0)
+    outs = [torch.empty(M, n, dtype=BF16, device="cuda") for n in N]
+    fp(xs, out=outs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp(xs, out=outs)
+    for seed in (41, 42, 43):
+        xn, _ = si.make_case(K, N, "bf16", M, seed=seed)
+        xs.copy_(to_gpu(xn))
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise_equal(outs, fp(xs), "2784 rows replay seed %d" % seed)
+        assert_matches_oracle(outs, xn, ws, label="2784 rows replay")
