@@ -17,18 +17,23 @@ HIP events on the launch stream, bracketed by device synchronizations.
 Reported: ``value`` = algorithmic bytes (W_cat + x + y per call, summed over
 the step) / step time, in GB/s; ``roofline`` for the dominant kernel (the
 kernel instantiation with the most time in the step): its algorithmic bytes
-per launch over its average launch duration (HIP events over the timed
-region, on the launch stream), against the 8 TB/s HBM peak, with the HBM
-traffic per launch measured by rocprofv3 counters when the recorded
-measurement (profiles/traffic.json) matches the current kernel sources;
+per launch over its average launch duration -- the back-to-back average of
+the committed rocprofv3 kernel trace when that record matches the current
+kernel sources, with the HIP-event average over the timed region (on the
+launch stream) beside it -- against the 8 TB/s HBM peak, with the HBM
+traffic per launch from the rocprofv3 counters of the same record;
 per-M microseconds per call for the fused and the one-launch-per-projection
-path; ``cpu_baseline`` = the CPU oracle (single thread) on a bounded sample
-of the same M sweep over one copy.
+path; ``cpu_baseline`` = the CPU oracle (one thread and OpenMP over the host
+cores, median of 5 runs) on a bounded sample of the same M sweep over one
+copy.
 
-``--crossover FILE`` additionally times, per token count M in
-{1, 2, 4, 8, 9, 16, 32, 64, 128}, every kernel path that serves M (vector
-ALU, small-M matrix core, tile) on the same rotated pool and writes the
-table to FILE: the measured crossover that places the MFMA path.
+Table modes (each writes PREFIX.json and PREFIX.md and exits):
+``--crossover`` times every kernel path that serves each M on a rotated
+pool (``--crossover-workload``: the headline weights, the three-way fused-A
+shape or the pages' 2624-row fused-A shape); ``--ceiling`` the streaming
+ceiling against the launch shape and the per-launch floor;
+``--indexer-splits`` the fp32 indexer fusion with its K split across
+workgroups; ``--pool-sweep`` the per-call time against the pool size.
 """
 from __future__ import annotations
 
@@ -103,9 +108,11 @@ def kernel_name(P, M: int, tiling) -> str:
         mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
         return "fp::skinny_kernel<%d, %d, %d, true, 0>" % (mt, rows, chunks)
     if path == P.FP_PATH_MFMA_SMALL:
-        # token halves; with two, up to 12 tokens the interleaved load order
-        return "fp::smfma_kernel<%d, false, %d, %s>" % (
-            chunks, 1 if M <= 8 else 2, "false" if 8 < M <= 12 else "true")
+        # token halves; with two, up to 12 tokens the interleaved load order;
+        # row tiles per wave (rows above 8: two tiles of rows / 2)
+        return "fp::smfma_kernel<%d, false, %d, %s, %d>" % (
+            chunks, 1 if M <= 8 else 2, "false" if 8 < M <= 12 else "true",
+            2 if rows > 8 else 1)
     mt16 = next(b for b in (1, 2, 4, 8, 16) if 16 * b >= M)
     cs = 4 if chunks in (8, 16) else 5
     return "fp::tile_kernel<%d, %d, %d, %d>" % (mt16, kparts, cs, chunks // cs)
@@ -116,16 +123,18 @@ def algorithmic_bytes(M: int, K: int, N, esize: int = 2) -> int:
     return esize * (n_total * K + M * K + M * n_total)
 
 
-def build_pool(P, torch, n_copies, max_M, seed=0):
+def build_pool(P, torch, n_copies, max_M, seed=0, shape=None):
     """n_copies independent weight sets U(-1/sqrt(K), 1/sqrt(K)) -> bf16,
-    drawn on the GPU, each concatenated by its own plan."""
+    drawn on the GPU, each concatenated by its own plan (shape: (K, N),
+    default the headline's)."""
+    k, ns = shape if shape is not None else (K, N)
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
-    a = 1.0 / math.sqrt(K)
+    a = 1.0 / math.sqrt(k)
     plans = []
     for _ in range(n_copies):
-        ws = [((torch.rand(n, K, generator=g, device="cuda") * 2 - 1) * a)
-              .to(torch.bfloat16) for n in N]
+        ws = [((torch.rand(n, k, generator=g, device="cuda") * 2 - 1) * a)
+              .to(torch.bfloat16) for n in ns]
         plans.append(P.FusedProjection(ws, max_M=max_M))
         del ws
     return plans
@@ -518,28 +527,48 @@ def host_info():
     return {"cpu_model": model, "nproc": os.cpu_count()}
 
 
-def crossover(prefix, P, torch, dev, plans, n_copies, Ms=(1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 24,
-                                                           32, 48, 64, 96, 128)):
-    """Per token count, every kernel path that serves it, on the rotated
-    pool (plans are made for max_M = 8, so a second pool is built): the
-    measured crossovers that place each kernel."""
+# Workloads of the crossover tables: (title, K, N, token counts, small-M
+# row layouts forced besides the library's: (label, rows, groups); rows
+# above 8 are two row tiles of rows / 2 per wave, one token half only).
+CROSSOVER_SHAPES = {
+    "wq_a+wkv": ("wq_a+wkv [1792, 5120] bf16", 5120, (1280, 512),
+                 (1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 24, 32, 48, 64, 96, 128), ()),
+    "fused_a_3way": ("three-way fused-A [2752, 6144] bf16", 6144, (2048, 576, 128),
+                     tuple(range(1, 17)) + (17, 32),
+                     (("one tile of 6 rows", 6, 1), ("one tile of 8 rows", 8, 1),
+                      ("two tiles of 6 rows", 12, 1), ("two tiles of 8 rows", 16, 1))),
+    "glm_fused_a": ("fused-A of the pages [2624, 6144] bf16 (2048 + 512 + 64)", 6144,
+                    (2048, 512, 64), tuple(range(1, 17)),
+                    (("one tile of 6 rows", 6, 1), ("one tile of 8 rows", 8, 1),
+                     ("two tiles of 6 rows", 12, 1), ("two tiles of 8 rows", 16, 1))),
+}
+
+
+def crossover(prefix, P, torch, dev, workload="wq_a+wkv", pool_mib=1024):
+    """Per token count, every kernel path that serves it, on a rotated pool
+    of the workload's weights past the MALL: the measured crossovers that
+    place each kernel."""
     import synthetic_inputs as si
-    del plans
-    torch.cuda.empty_cache()
-    big = build_pool(P, torch, n_copies, max(Ms))
-    kc = K * 2 // 16
+    title, k, ns, Ms, small_rows = CROSSOVER_SHAPES[workload]
+    n_copies = max(2, math.ceil((pool_mib << 20) / (sum(ns) * k * 2)))
+    big = build_pool(P, torch, n_copies, max(Ms), shape=(k, ns))
+    kc = k * 2 // 16
     steps = -(-kc // 8)
     kt = 4 if steps <= 64 else 8 if steps <= 128 else 16
+    pk = -(-steps // kt)
     res, rows = [], []
     for M in Ms:
-        xc, _ = si.make_case(K, N, "bf16", M, seed=200 + M)
+        xc, _ = si.make_case(k, ns, "bf16", M, seed=200 + M)
         x = xc.to(dev)
-        out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
+        out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in ns]
         cands = [("default", None)]
         if M <= 8:
-            cands.append(("vector ALU", (P.FP_PATH_SKINNY, 10, 1, 1, 0, 0)))
+            cands.append(("vector ALU", (P.FP_PATH_SKINNY, min(16, -(-kc // 64)), 1, 1, 0, 0)))
         if M <= 16:
-            cands.append(("small-M MFMA", (P.FP_PATH_MFMA_SMALL, -(-steps // kt), kt, 1, 0, 0)))
+            cands.append(("small-M MFMA", (P.FP_PATH_MFMA_SMALL, pk, kt, 1, 0, 0)))
+            for label, r, g in small_rows:
+                if r <= 8 or M <= 8:
+                    cands.append(("small-M MFMA, " + label, (P.FP_PATH_MFMA_SMALL, pk, kt, 1, r, g)))
         if M > 8:
             cands.append(("tile (S=8)", (P.FP_PATH_MFMA, 0, 0, 8, 0, 0)))
             cands.append(("ring tile (S=9)", (P.FP_PATH_MFMA, 4, 3 if M > 128 else 4, 9, 0, 0)))
@@ -557,7 +586,7 @@ def crossover(prefix, P, torch, dev, plans, n_copies, Ms=(1, 2, 3, 4, 5, 8, 9, 1
             g = capture(torch, lambda: [p.forward(x, out=out) for p in big])
             ms, _ = time_graphs(torch, [g], 10, 2)
             us = ms * 1e3 / (10 * n_copies)
-            b = algorithmic_bytes(M, K, N)
+            b = algorithmic_bytes(M, k, ns)
             tl = list(big[0].get_tiling(M))
             res.append({"M": M, "variant": name, "path": P._lib.PATH_NAMES[big[0].query(M)[0]],
                         "tiling": tl, "us": round(us, 3), "GBps": round(b / us / 1e3, 1)})
@@ -569,14 +598,15 @@ def crossover(prefix, P, torch, dev, plans, n_copies, Ms=(1, 2, 3, 4, 5, 8, 9, 1
             del g
     for p in big:
         p.close()
-    write_outputs(prefix, "Kernel crossover, wq_a+wkv [1792, 5120] bf16, weights rotated past "
-                  "the MALL", {"workload": "wq_a+wkv [1280,512]x5120 bf16, %d rotated copies"
-                               % n_copies, "rows": res},
+    write_outputs(prefix, "Kernel crossover, %s, weights rotated past the MALL" % title,
+                  {"workload": "%s, %d rotated copies" % (title, n_copies), "rows": res},
                   ["M", "kernel", "tiling (path, kparts, chunks, S, rows, groups)", "us / call",
                    "GB/s", "% of 8 TB/s"], rows,
                   ["Every kernel that serves M, forced with fp_plan_set_tiling, on one pool "
                    "of %d copies (one fused call per copy, hipGraph replay, 10 timed replays); "
-                   "'default' is the library's choice." % n_copies])
+                   "'default' is the library's choice.  Small-M rows: rows per row group "
+                   "(above 8: two row tiles of rows / 2 per wave sharing the activation "
+                   "operand); 0 = chosen per launch." % n_copies])
 
 
 def epilogue_cells(P, torch, dev, plans, n_copies, steps, Ms=(1, 2, 4, 8)):
@@ -782,6 +812,9 @@ def main():
     ap.add_argument("--crossover", default="",
                     help="time every kernel path per M in 1..128, write PREFIX.json and "
                          "PREFIX.md and exit")
+    ap.add_argument("--crossover-workload", default="wq_a+wkv",
+                    choices=sorted(CROSSOVER_SHAPES),
+                    help="the weights of the --crossover table")
     ap.add_argument("--ceiling", default="",
                     help="time the streaming ceiling against the launch shape and the "
                          "per-launch floor, write PREFIX.json and PREFIX.md and exit")
@@ -874,7 +907,9 @@ def main():
           (n_copies, n_copies * w_bytes / 2**20, list(MS)), file=sys.stderr, flush=True)
     plans = build_pool(P, torch, n_copies, max(MS))
     if args.crossover:
-        crossover(args.crossover, P, torch, dev, plans, n_copies)
+        del plans
+        torch.cuda.empty_cache()
+        crossover(args.crossover, P, torch, dev, args.crossover_workload, args.pool_mib)
         return
     if args.ceiling:
         ceiling_sweep(P, torch, dev, plans, n_copies, args.steps, args.ceiling)

@@ -392,35 +392,65 @@ void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs, int var)
 // Rows per tile (<= 8) and row groups per workgroup of the small-M
 // matrix-core kernel, by the same one-round, least-loaded-CU rule as the
 // skinny kernel.
-void resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs) {
+// Small-M kernel rows: `rows` 1..8 is one tile of that many rows per wave;
+// an even 10..16 is two tiles of rows / 2 (one token half, bf16, not
+// gate/up) that share each wave's activation operand.
+int smfma_tiles(const Tiling& t) { return t.rows > 8 ? 2 : 1; }
+int smfma_rt(const Tiling& t) { return t.rows / smfma_tiles(t); }
+
+// Rows per workgroup R = G * TT * RT.  Every workgroup loads the whole
+// activation block once per row group, so the bytes a CU takes in are
+// (workgroups on the CU) x (R weight rows + G x mt activation rows); the
+// choice keeps every workgroup resident at once (one round) and, among
+// those, minimises that figure for the busiest CU (ties: the larger R,
+// fewer workgroups).  Two tiles per wave (more registers, at most 16 waves
+// per CU) are offered to bf16 plans with one token half.  Without a
+// one-round choice the largest R is taken.  Measured on MI355X (weights
+// rotated past the MALL, us per call): K = 6144, 2752 rows, M = 8: two
+// tiles of 6 rows per wave (230 workgroups) 8.86 against one tile of 6
+// (459) 10.61; M = 5: 8.54 vs 8.88.  Short K, where the former rule (rows
+// on the busiest CU alone) took one-row groups that each reload the
+// activations, M = 8: K = 512, 1792 rows 3.27 vs 7.03 (seven groups of
+// one row); K = 1024, 2048 rows 3.00 vs 5.01; K = 2048 3.86 vs 4.69.
+void resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs, bool two_tiles) {
   if (t->rows > 0 && t->groups > 0) return;
-  int best_rt = pairs ? 2 : 1, best_g = 1;
+  int best_rows = pairs ? 2 : 1, best_g = 1;
   int64_t best_cost = INT64_MAX;
-  for (int rt = pairs ? 2 : 1; rt <= 8; rt += pairs ? 2 : 1) {
-    if (t->rows > 0 && rt != t->rows) continue;
-    const int g_cap =
-        std::max(1, fp::smfma_max_threads(t->chunks, t->mt / 8) / (64 * t->kparts));
-    for (int g = 1; g <= g_cap; ++g) {
-      if (t->groups > 0 && g != t->groups) continue;
-      const int64_t R = (int64_t)rt * g;
-      const int64_t nb = ceil_div(n_rows, R);
-      const int waves = g * t->kparts;
-      const int64_t resident = std::max(1, std::min(2, 32 / waves));
-      const bool one_round = nb <= resident * kCus;
-      const int64_t cost = one_round ? ceil_div(nb, kCus) * R : INT64_MAX / 2 - R;
-      if (cost < best_cost || (cost == best_cost && R > (int64_t)best_rt * best_g)) {
-        best_cost = cost;
-        best_rt = rt;
-        best_g = g;
+  const int mh = t->mt / 8;
+  for (int tt = 1; tt <= 2; ++tt) {
+    if (tt == 2 && (!two_tiles || pairs || mh != 1)) continue;
+    for (int rt = pairs ? 2 : 1; rt <= 8; rt += pairs ? 2 : 1) {
+      if (tt == 2 && rt < 5) continue;  // rows <= 8 denote one tile
+      const int rows = tt * rt;
+      if (t->rows > 0 && rows != t->rows) continue;
+      const int g_cap =
+          std::max(1, fp::smfma_max_threads(t->chunks, mh, tt) / (64 * t->kparts));
+      for (int g = 1; g <= g_cap; ++g) {
+        if (t->groups > 0 && g != t->groups) continue;
+        // the cross-wave sums of every (row group, tile, token half) in LDS
+        if ((int64_t)g * tt * mh * 2 * 64 * fp::kMaxWaveParts * 4 > kMaxLds) continue;
+        const int64_t R = (int64_t)rows * g;
+        const int64_t nb = ceil_div(n_rows, R);
+        const int waves = g * t->kparts;
+        const int cu_waves = tt == 1 ? 32 : 16;
+        const int64_t resident = std::max(1, std::min(2, cu_waves / waves));
+        const bool one_round = nb <= resident * kCus;
+        const int64_t cost =
+            one_round ? ceil_div(nb, kCus) * (R + (int64_t)g * t->mt) : INT64_MAX / 2 - R;
+        if (cost < best_cost || (cost == best_cost && R > (int64_t)best_rows * best_g)) {
+          best_cost = cost;
+          best_rows = rows;
+          best_g = g;
+        }
       }
     }
   }
-  t->rows = best_rt;
+  t->rows = best_rows;
   t->groups = best_g;
 }
 
 size_t smfma_lds(const Tiling& t) {
-  return (size_t)t.groups * (t.mt / 8) * 2 * 64 * fp::kMaxWaveParts * 4;
+  return (size_t)t.groups * smfma_tiles(t) * (t.mt / 8) * 2 * 64 * fp::kMaxWaveParts * 4;
 }
 
 size_t skinny_lds(const Tiling& t) {
@@ -523,8 +553,10 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     if (!(p->dtype == FP_BF16 || is_mx(p->dtype))) return false;
     if (M > kSmallMfmaMaxM || t.mt < M) return false;
     if (!(t.chunks == 4 || t.chunks == 8 || t.chunks == 16)) return false;
-    if (t.splits != 1 || t.kparts > fp::kMaxWaveParts || t.rows > 8 || t.groups < 1) return false;
-    if ((int64_t)t.groups * t.kparts * 64 > fp::smfma_max_threads(t.chunks, t.mt / 8))
+    if (t.splits != 1 || t.kparts > fp::kMaxWaveParts || t.rows > 16 || t.groups < 1) return false;
+    if (t.rows > 8 && (t.rows % 2 != 0 || t.mt != 8 || p->dtype != FP_BF16)) return false;
+    if ((int64_t)t.groups * t.kparts * 64 >
+        fp::smfma_max_threads(t.chunks, t.mt / 8, smfma_tiles(t)))
       return false;
     if ((int64_t)t.kparts * t.chunks * 8 < p->kc) return false;
     if (smfma_lds(t) > kMaxLds) return false;
@@ -601,14 +633,16 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
   } else if (t->path == FP_PATH_MFMA_SMALL) {
     t->mt = M > 8 ? 16 : 8;  // one or two token halves
     if (t->kparts < 1 || t->chunks < 1) return false;
-    resolve_smfma_rows(n_rows, t, pairs);
+    resolve_smfma_rows(n_rows, t, pairs, p->dtype == FP_BF16);
   } else {
     t->mt = skinny_mt(M);
     if (t->kparts < 1) return false;
     resolve_skinny_rows(n_rows, t->mt, t, pairs, skinny_var(p));
   }
-  // a gate/up launch keeps both rows of a pair in one row group
+  // a gate/up launch keeps both rows of a pair in one row group (and one
+  // tile per wave)
   if (pairs && (t->rows % 2 != 0 || t->splits != 1)) return false;
+  if (pairs && t->path == FP_PATH_MFMA_SMALL && smfma_tiles(*t) != 1) return false;
   return tiling_valid(p, M, n_rows, *t, ws != nullptr ? *ws : plan_ws(p));
 }
 
@@ -669,7 +703,7 @@ const void* mfma_fn(const Tiling& t) {
 
 const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype, int64_t M) {
   if (is_mx(dtype)) return pairs ? nullptr : fpk::smfma_mx(dtype, t.mt / 8, t.chunks);
-  return fpk::smfma(t.chunks, pairs, t.mt, M);
+  return fpk::smfma(t.chunks, pairs, t.mt, M, smfma_tiles(t));
 }
 
 std::mutex g_attr_mu;
@@ -749,7 +783,7 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   void* args[] = {&w_a, &x_a, &y0_a, &y1_a, &ldx_a, &n_rows_a, &kc_a, &M_a, &split_a,
                   &geo_a, &tail};
   if (t.path == FP_PATH_MFMA_SMALL) {
-    geo_a = t.rows | (t.kparts << 8) | (t.groups << 16);
+    geo_a = smfma_rt(t) | (t.kparts << 8) | (t.groups << 16);
     const int64_t R = (int64_t)t.rows * t.groups;
     return launch(smfma_fn(t, pairs, p->dtype, M_a), ceil_div(lr.n_rows, R),
                   t.groups * t.kparts * 64, smfma_lds(t), args, stream);

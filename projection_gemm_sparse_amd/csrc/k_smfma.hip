@@ -11,7 +11,12 @@ namespace {
 constexpr int kSmfmaInterleaveMaxM = 12;
 
 template <int KT>
-const void* smfma_kt(bool pairs, int mt, int64_t M) {
+const void* smfma_kt(bool pairs, int mt, int64_t M, int tt) {
+  if (tt == 2) {
+    if (pairs || mt != 8) return nullptr;
+    return reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 1, true, 2>);
+  }
+  if (tt != 1) return nullptr;
   if (mt == 16) {
     if (pairs) return nullptr;
     return M <= kSmfmaInterleaveMaxM
@@ -44,11 +49,11 @@ const void* smfma_mx_fmt(int32_t dtype, int kt) {
 
 namespace fpk {
 
-const void* smfma(int kt, bool pairs, int mt, int64_t M) {
+const void* smfma(int kt, bool pairs, int mt, int64_t M, int tt) {
   switch (kt) {
-    case 4: return smfma_kt<4>(pairs, mt, M);
-    case 8: return smfma_kt<8>(pairs, mt, M);
-    case 16: return smfma_kt<16>(pairs, mt, M);
+    case 4: return smfma_kt<4>(pairs, mt, M, tt);
+    case 8: return smfma_kt<8>(pairs, mt, M, tt);
+    case 16: return smfma_kt<16>(pairs, mt, M, tt);
     default: return nullptr;
   }
 }

@@ -36,9 +36,15 @@
 // two accumulators); the weights are still loaded once.  Per token the
 // arithmetic, hence the result, is the same as with one half.
 //
-// Work split.  A workgroup owns G row groups of RT <= 8 rows (a tile with
-// RT < 8 leaves its last A rows unused; the 1792-row fused launch uses 7
-// rows per workgroup so that its 256 workgroups cover the 256 CUs once).
+// Work split.  A workgroup owns G row groups of TT tiles of RT <= 8 rows (a
+// tile with RT < 8 leaves its last A rows unused; the 1792-row fused launch
+// uses one tile of 7 rows per workgroup so that its 256 workgroups cover
+// the 256 CUs once).  With TT = 2 tiles (one token half) every wave
+// multiplies the same activation operand with the weights of two tiles:
+// a launch of more rows than 8 per CU then keeps one workgroup per CU,
+// and each CU loads the activations once instead of once per workgroup
+// (at M = 8 and K = 6144 the activations are 98 KB per workgroup, more
+// than the 74 KB of six weight rows).
 // The PK waves of a row group split K into PK parts of KT steps (8 chunks
 // each).  All of a wave's weight and activation loads are issued before its
 // first MFMA, and the steps consume them in issue order.
@@ -59,8 +65,8 @@ namespace fp {
 
 constexpr int kFmtNv4 = 5;  // the NVFP4 form of smfma_mx_kernel
 
-constexpr int smfma_max_threads(int kt, int mh = 1) {
-  return max_threads_for_regs(4 * kt * (mh + 1) + 24 + 16 * (mh - 1));
+constexpr int smfma_max_threads(int kt, int mh = 1, int tt = 1) {
+  return max_threads_for_regs(4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1));
 }
 
 // Output stage of both small-M kernels (not gate/up).  The cross-wave
@@ -100,14 +106,17 @@ __device__ __forceinline__ void smfma_store_outputs(const float* smem, int Gv, i
 // that writes silu(gate) * up instead of the projections.  MH: token halves
 // (1: M <= 8, 2: M <= 16).  XFIRST (two halves): every activation load
 // before the weights (the fuller second halves) instead of each step's
-// first-half, weight and second-half chunks in turn.
-template <int KT, bool PAIRS = false, int MH = 1, bool XFIRST = true>
-__global__ void __launch_bounds__(smfma_max_threads(KT, MH))
+// first-half, weight and second-half chunks in turn.  TT: row tiles per
+// wave (2 only with one token half, not gate/up); tile j of row group g2
+// holds rows row_base + (g2 TT + j) RT ...
+template <int KT, bool PAIRS = false, int MH = 1, bool XFIRST = true, int TT = 1>
+__global__ void __launch_bounds__(smfma_max_threads(KT, MH, TT))
 smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
              unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
              int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
   static_assert(MH == 1 || (MH == 2 && !PAIRS), "token halves");
-  extern __shared__ float smem[];  // [G][MH][16 wave parts][2][8][8]
+  static_assert(TT == 1 || (TT == 2 && MH == 1 && !PAIRS), "two tiles: one half, no pairs");
+  extern __shared__ float smem[];  // [G][TT][MH][16 wave parts][2][8][8]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -116,8 +125,8 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   const int Gv = geo >> 16;
   const int p = Gv == 1 ? wave : wave % PK;
   const int g2 = Gv == 1 ? 0 : wave / PK;
-  const int row_base = (int)blockIdx.x * (Gv * RT);
-  const int row0 = row_base + g2 * RT;
+  const int row_base = (int)blockIdx.x * (Gv * TT * RT);
+  const int row0 = row_base + g2 * TT * RT;
   const int i16 = lane & 15;
   const int g = lane >> 4;
   const int sub = i16 >> 3;   // sub-slice of this lane's A row and B column
@@ -154,7 +163,7 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   //    that order pays only while the second half is at most half full
   //    (XFIRST picks; a branch on M inside one kernel slowed both orders).
   u32x4 xv[MH][KT];
-  u32x4 wv[KT];
+  u32x4 wv[TT][KT];
   {
     const u32x4* xrow[MH];
 #pragma unroll
@@ -162,19 +171,25 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
       const int mc = rl + 8 * h < M ? rl + 8 * h : M - 1;
       xrow[h] = reinterpret_cast<const u32x4*>(x + (uint64_t)(uint32_t)mc * ldx);
     }
-    const int rr = rl < RT ? row0 + rl : row0;
-    const int lrow = rr < n_rows ? rr : n_rows - 1;
-    const int row = PAIRS ? pair_row(lrow, split) : lrow;
-    const u32x4* wrow = reinterpret_cast<const u32x4*>(w + (uint64_t)(uint32_t)row * row_bytes);
+    const u32x4* wrows[TT];
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+      const int rr = row0 + j * RT + (rl < RT ? rl : 0);
+      const int lrow = rr < n_rows ? rr : n_rows - 1;
+      const int row = PAIRS ? pair_row(lrow, split) : lrow;
+      wrows[j] = reinterpret_cast<const u32x4*>(w + (uint64_t)(uint32_t)row * row_bytes);
+    }
+    const u32x4* wrow = wrows[0];
     if constexpr (MH == 1) {
       // one token half: the activation and weight chunks of each step in
-      // turn, so the weight stream starts with the first load
+      // turn (every tile's), so the weight stream starts with the first load
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         const int c = cw + 8 * t + cl;
         const int cc = c < kc ? c : kc - 1;
         xv[0][t] = xrow[0][cc];
-        wv[t] = __builtin_nontemporal_load(wrow + cc);
+#pragma unroll
+        for (int j = 0; j < TT; ++j) wv[j][t] = __builtin_nontemporal_load(wrows[j] + cc);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else if constexpr (!XFIRST) {
@@ -186,7 +201,7 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
         const int c = cw + 8 * t + cl;
         const int cc = c < kc ? c : kc - 1;
         xv[0][t] = xrow[0][cc];
-        wv[t] = __builtin_nontemporal_load(wrow + cc);
+        wv[0][t] = __builtin_nontemporal_load(wrow + cc);
         xv[MH - 1][t] = xrow[MH - 1][cc];
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -203,30 +218,37 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         const int c = cw + 8 * t + cl;
-        wv[t] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+        wv[0][t] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
       }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
   const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
-  fill_unused_parts(smem, Gv * MH, PK, 128, tid, Gv * PK * 64);
+  fill_unused_parts(smem, Gv * TT * MH, PK, 128, tid, Gv * PK * 64);
   __builtin_amdgcn_sched_barrier(0);
-  // 2. MFMA steps in order; chunks past K contribute zero
-  f32x4 acc[MH];
+  // 2. MFMA steps in order; chunks past K contribute zero.  acc[j * MH + h]:
+  //    tile j, token half h
+  f32x4 acc[TT * MH];
 #pragma unroll
-  for (int h = 0; h < MH; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < TT * MH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     __builtin_amdgcn_sched_barrier(0);
     const bool c_ok = c0 + 8 * t < kc;
-    const u32x4 wa = shuffle(wv[t]);
-    const bf16x8 A = u4bf8(c_ok ? wa : zero4);
+    bf16x8 B[MH];
 #pragma unroll
     for (int h = 0; h < MH; ++h) {
       const bool tok_ok = r8 + 8 * h < M;
       const u32x4 xb = shuffle(xv[h][t]);
-      const bf16x8 B = u4bf8(c_ok && tok_ok ? xb : zero4);
-      acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[h], 0, 0, 0);
+      B[h] = u4bf8(c_ok && tok_ok ? xb : zero4);
+    }
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+      const u32x4 wa = shuffle(wv[j][t]);
+      const bf16x8 A = u4bf8(c_ok ? wa : zero4);
+#pragma unroll
+      for (int h = 0; h < MH; ++h)
+        acc[j * MH + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[h], acc[j * MH + h], 0, 0, 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -238,22 +260,26 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
   //    outputs read consecutive words.
   if ((g >> 1) == sub) {
 #pragma unroll
-    for (int h = 0; h < MH; ++h) {
-      float* red = smem + ((g2 * MH + h) * kMaxWaveParts + p) * 128 + sub * 64 + r8;
+    for (int j = 0; j < TT; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = (4 * g + v) & 7;
-        red[r * 8] = acc[h][v];
+      for (int h = 0; h < MH; ++h) {
+        float* red =
+            smem + (((g2 * TT + j) * MH + h) * kMaxWaveParts + p) * 128 + sub * 64 + r8;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = (4 * g + v) & 7;
+          red[r * 8] = acc[j * MH + h][v];
+        }
       }
-    }
   }
   __syncthreads();
 
   // 4. per output: each sub-slice over the PK wave parts in part order,
-  //    then sub-slice 0 + sub-slice 1
+  //    then sub-slice 0 + sub-slice 1 (the tiles of the workgroup in row
+  //    order: tile g2 TT + j starts at row_base + (g2 TT + j) RT)
   if constexpr (!PAIRS) {
-    smfma_store_outputs<MH, false>(smem, Gv, Gv * PK, wave, lane, RT, row_base, M, n_rows, om,
-                                   a.out);
+    smfma_store_outputs<MH, false>(smem, Gv * TT, Gv * PK, wave, lane, RT, row_base, M, n_rows,
+                                   om, a.out);
   } else {
     // gate/up: one thread per output; even logical rows are gate rows j,
     // the up row is tile row r + 1

@@ -16,11 +16,14 @@ def test_kernel_names_of_the_default_tilings():
             == "fp::skinny_kernel<2, 7, 1, true, 0>")
     small = (P.FP_PATH_MFMA_SMALL, 10, 8, 1, 7, 1)
     for M in range(3, 9):
-        assert bench.kernel_name(P, M, small) == "fp::smfma_kernel<8, false, 1, true>"
+        assert bench.kernel_name(P, M, small) == "fp::smfma_kernel<8, false, 1, true, 1>"
     for M in range(9, 13):
-        assert bench.kernel_name(P, M, small) == "fp::smfma_kernel<8, false, 2, false>"
+        assert bench.kernel_name(P, M, small) == "fp::smfma_kernel<8, false, 2, false, 1>"
     for M in range(13, 17):
-        assert bench.kernel_name(P, M, small) == "fp::smfma_kernel<8, false, 2, true>"
+        assert bench.kernel_name(P, M, small) == "fp::smfma_kernel<8, false, 2, true, 1>"
+    # two row tiles of 6 per wave (plans of more rows than 8 per CU)
+    two = (P.FP_PATH_MFMA_SMALL, 12, 8, 1, 12, 1)
+    assert bench.kernel_name(P, 8, two) == "fp::smfma_kernel<8, false, 1, true, 2>"
 
 
 def test_two_halves_order_threshold_matches_the_library():
@@ -31,12 +34,12 @@ def test_two_halves_order_threshold_matches_the_library():
     assert m is not None
     lim = int(m.group(1))
     small = (P.FP_PATH_MFMA_SMALL, 10, 8, 1, 7, 1)
-    assert bench.kernel_name(P, lim, small).endswith(", false>")
-    assert bench.kernel_name(P, lim + 1, small).endswith(", true>")
+    assert bench.kernel_name(P, lim, small).endswith(", false, 1>")
+    assert bench.kernel_name(P, lim + 1, small).endswith(", true, 1>")
 
 
 def test_recorded_traffic_needs_the_current_kernel_sources(tmp_path, monkeypatch):
-    name = "fp::smfma_kernel<8, false, 1, true>"
+    name = "fp::smfma_kernel<8, false, 1, true, 1>"
     rec = {"kernel_sources_sha256_16": bench.kernel_sources_digest(),
            "kernels": {name: {"hbm_bytes_per_launch": 12345}}}
     f = tmp_path / "traffic.json"

@@ -181,6 +181,8 @@ def test_tilings_all_pass(M):
         (P.FP_PATH_MFMA_SMALL, 5, 16, 1, 8, 1),
         (P.FP_PATH_MFMA_SMALL, 5, 16, 1, 3, 2),  # two row groups of 3 rows
         (P.FP_PATH_MFMA_SMALL, 16, 8, 1, 1, 0),  # more K parts than needed
+        (P.FP_PATH_MFMA_SMALL, 10, 8, 1, 12, 1),  # two tiles of 6 rows per wave
+        (P.FP_PATH_MFMA_SMALL, 5, 16, 1, 16, 1),  # two tiles of 8 rows per wave
     ]
     ran = 0
     for t in tilings:
@@ -194,7 +196,8 @@ def test_tilings_all_pass(M):
                      and (M > 8 or (t[2] > 2 and M > 2)))
                     or (t[0] == P.FP_PATH_MFMA and M <= 8)
                     or (t[0] == P.FP_PATH_MFMA_SMALL and M > 8
-                        and max(1, t[5]) * t[1] * 64 > _smfma_thread_cap(t[2], 2))), (t, st)
+                        and (t[4] > 8
+                             or max(1, t[5]) * t[1] * 64 > _smfma_thread_cap(t[2], 2)))), (t, st)
             continue
         ran += 1
         ys = fp(xg)
@@ -260,10 +263,10 @@ def test_single_row_projections_and_one_projection():
 
 
 # ---- the small-M matrix-core kernel (opt-in tiling) on every workload shape
-def _smfma_thread_cap(kt, mh):
+def _smfma_thread_cap(kt, mh, tt=1):
     """Largest workgroup of the small-M matrix-core kernel: its register
-    estimate per lane, 4 waves per SIMD at most."""
-    regs = 4 * kt * (mh + 1) + 24 + 16 * (mh - 1)
+    estimate per lane (tt row tiles per wave), 4 waves per SIMD at most."""
+    regs = 4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1)
     return 256 * max(1, min(4, 512 // regs))
 
 
@@ -291,6 +294,55 @@ def test_small_mfma_path(case, M):
     assert fp.set_tiling(M, _small_mfma_tiling(fp.K)) == P.FP_OK
     assert fp.query(M)[0] == P.FP_PATH_MFMA_SMALL
     _check_case(fp, x, ws, "small-M MFMA %s M=%d" % (case, M))
+
+
+# ---- two row tiles per wave (rows 10..16: two tiles of rows / 2 sharing the
+#      activation operand): same per-row order as one tile, so the outputs
+#      are bitwise those of one tile of rows / 2, and within the bound
+@pytest.mark.parametrize("case", ["fused_a_3way", "ragged", "single_rows", "k8", "page_2784"])
+@pytest.mark.parametrize("M", [1, 3, 5, 8])
+def test_small_mfma_two_tiles_per_wave(case, M):
+    if case == "fused_a_3way":
+        x, ws = si.workload_case("fused_a_3way", M, 2)
+    elif case == "ragged":
+        x, ws = si.make_case(136, (37, 5, 70, 1), "bf16", M, seed=70 + M)
+    elif case == "single_rows":
+        x, ws = si.make_case(1024, (1,) * 16, "bf16", M, seed=71 + M)
+    elif case == "k8":
+        x, ws = si.make_case(8, (300, 29), "bf16", M, seed=72 + M)
+    else:
+        K, N = _page_shape("glm_fused_a_indexer")
+        x, ws = si.make_case(K, N, "bf16", M, seed=73 + M)
+    fp = _plan(ws, max_M=8)
+    base = _small_mfma_tiling(fp.K)
+    xg = to_gpu(x)
+    ref = None
+    for rows, groups in ((10, 1), (12, 1), (14, 2), (16, 1), (6, 1)):
+        st = fp.set_tiling(M, base[:4] + (rows, groups))
+        if groups * base[1] * 64 > _smfma_thread_cap(base[2], 1, 2 if rows > 8 else 1):
+            assert st == P.FP_ERR_UNSUPPORTED, (rows, groups)
+            continue
+        assert st == P.FP_OK, (rows, groups)
+        assert fp.query(M)[0] == P.FP_PATH_MFMA_SMALL
+        label = "two tiles %s M=%d rows=%d G=%d" % (case, M, rows, groups)
+        ys = _check_case(fp, x, ws, label)
+        if ref is None:
+            ref = ys
+        else:
+            assert_bitwise_equal(ys, ref, label + " vs rows=10")
+    fp.set_tiling(M, None)
+
+
+def test_small_mfma_two_tiles_refused_where_unsupported():
+    x, ws = si.workload_case("fused_a_3way", 9, 0)
+    fp = _plan(ws, max_M=16)
+    base = _small_mfma_tiling(fp.K)
+    # two token halves, odd row counts above 8, more than 16 rows
+    assert fp.set_tiling(9, base[:4] + (12, 1)) == P.FP_ERR_UNSUPPORTED
+    assert fp.set_tiling(8, base[:4] + (11, 1)) == P.FP_ERR_UNSUPPORTED
+    assert fp.set_tiling(8, base[:4] + (18, 1)) == P.FP_ERR_UNSUPPORTED
+    assert fp.set_tiling(8, base[:4] + (12, 1)) == P.FP_OK
+    fp.set_tiling(8, None)
 
 
 # ---- the split tile path finishes its K slices either in the launch (last
