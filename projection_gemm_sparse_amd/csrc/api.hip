@@ -52,10 +52,11 @@ constexpr int kDefaultSmallMfmaMinM = 3;
 // faster through M = 4 (MXFP8 4.95 vs 5.36 us, MXFP4 4.37 vs 4.60).
 constexpr int kDefaultSmallMfmaMinMMx = 5;
 constexpr int kCus = 256;           // MI355X compute units
-// bf16 launches of more rows than one 8-row tile per CU (the small-M kernel
-// then runs more than one workgroup per CU) keep the vector-ALU kernel
-// through M = 4 as well: measured at the three-way shape (K = 6144, 2752
-// rows) 7.84 vs 8.04-8.20 us at M = 3 and 7.99 vs 8.20 at M = 4.
+// bf16 launches of more rows than one 8-row tile per CU keep the vector-ALU
+// kernel through M = 4 as well: measured at the three-way shape (K = 6144,
+// 2752 rows), against the small-M kernel with two row tiles of 6 per wave,
+// 8.02 vs 8.27 us at M = 3 and 8.19 vs 8.30 at M = 4 (one tile of 6: 9.05,
+// 8.48).
 int default_small_mfma_min_m(int32_t dtype, int64_t n_total) {
   if (dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4) return kDefaultSmallMfmaMinMMx;
   return n_total > 8 * (int64_t)kCus ? kDefaultSmallMfmaMinMMx : kDefaultSmallMfmaMinM;
