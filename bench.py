@@ -123,10 +123,11 @@ def algorithmic_bytes(M: int, K: int, N, esize: int = 2) -> int:
     return esize * (n_total * K + M * K + M * n_total)
 
 
-def build_pool(P, torch, n_copies, max_M, seed=0, shape=None):
+def build_pool(P, torch, n_copies, max_M, seed=0, shape=None, workspace_bytes=None):
     """n_copies independent weight sets U(-1/sqrt(K), 1/sqrt(K)) -> bf16,
     drawn on the GPU, each concatenated by its own plan (shape: (K, N),
-    default the headline's)."""
+    default the headline's; workspace_bytes: each plan's split-K workspace,
+    default what its default tilings need)."""
     k, ns = shape if shape is not None else (K, N)
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
@@ -135,7 +136,7 @@ def build_pool(P, torch, n_copies, max_M, seed=0, shape=None):
     for _ in range(n_copies):
         ws = [((torch.rand(n, k, generator=g, device="cuda") * 2 - 1) * a)
               .to(torch.bfloat16) for n in ns]
-        plans.append(P.FusedProjection(ws, max_M=max_M))
+        plans.append(P.FusedProjection(ws, max_M=max_M, workspace_bytes=workspace_bytes))
         del ws
     return plans
 
@@ -528,19 +529,19 @@ def host_info():
 
 
 # Workloads of the crossover tables: (title, K, N, token counts, small-M
-# row layouts forced besides the library's: (label, rows, groups); rows
-# above 8 are two row tiles of rows / 2 per wave, one token half only).
+# row layouts forced besides the library's: (label, rows, groups) -- rows
+# above 8 are two row tiles of rows / 2 per wave, one token half only --,
+# K slice counts of the ring tile kernel).
+_SMALL_ROWS = (("one tile of 6 rows", 6, 1), ("one tile of 8 rows", 8, 1),
+               ("two tiles of 6 rows", 12, 1), ("two tiles of 8 rows", 16, 1))
 CROSSOVER_SHAPES = {
     "wq_a+wkv": ("wq_a+wkv [1792, 5120] bf16", 5120, (1280, 512),
-                 (1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 24, 32, 48, 64, 96, 128), ()),
+                 (1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 24, 32, 48, 64, 96, 128), (), (9,)),
     "fused_a_3way": ("three-way fused-A [2752, 6144] bf16", 6144, (2048, 576, 128),
-                     tuple(range(1, 17)) + (17, 32),
-                     (("one tile of 6 rows", 6, 1), ("one tile of 8 rows", 8, 1),
-                      ("two tiles of 6 rows", 12, 1), ("two tiles of 8 rows", 16, 1))),
+                     tuple(range(1, 17)) + (17, 32, 48, 64, 96, 128), _SMALL_ROWS,
+                     (5, 7, 9)),
     "glm_fused_a": ("fused-A of the pages [2624, 6144] bf16 (2048 + 512 + 64)", 6144,
-                    (2048, 512, 64), tuple(range(1, 17)),
-                    (("one tile of 6 rows", 6, 1), ("one tile of 8 rows", 8, 1),
-                     ("two tiles of 6 rows", 12, 1), ("two tiles of 8 rows", 16, 1))),
+                    (2048, 512, 64), tuple(range(1, 17)), _SMALL_ROWS, (9,)),
 }
 
 
@@ -549,9 +550,11 @@ def crossover(prefix, P, torch, dev, workload="wq_a+wkv", pool_mib=1024):
     of the workload's weights past the MALL: the measured crossovers that
     place each kernel."""
     import synthetic_inputs as si
-    title, k, ns, Ms, small_rows = CROSSOVER_SHAPES[workload]
+    title, k, ns, Ms, small_rows, ring_slices = CROSSOVER_SHAPES[workload]
     n_copies = max(2, math.ceil((pool_mib << 20) / (sum(ns) * k * 2)))
-    big = build_pool(P, torch, n_copies, max(Ms), shape=(k, ns))
+    # room for the partials of every forced slice count
+    ws_bytes = (64 << 10) + max(ring_slices + (9,)) * sum(ns) * 16 * (-(-max(Ms) // 16)) * 4
+    big = build_pool(P, torch, n_copies, max(Ms), shape=(k, ns), workspace_bytes=ws_bytes)
     kc = k * 2 // 16
     steps = -(-kc // 8)
     kt = 4 if steps <= 64 else 8 if steps <= 128 else 16
@@ -571,7 +574,9 @@ def crossover(prefix, P, torch, dev, workload="wq_a+wkv", pool_mib=1024):
                     cands.append(("small-M MFMA, " + label, (P.FP_PATH_MFMA_SMALL, pk, kt, 1, r, g)))
         if M > 8:
             cands.append(("tile (S=8)", (P.FP_PATH_MFMA, 0, 0, 8, 0, 0)))
-            cands.append(("ring tile (S=9)", (P.FP_PATH_MFMA, 4, 3 if M > 128 else 4, 9, 0, 0)))
+            for rs in ring_slices:
+                cands.append(("ring tile (S=%d)" % rs,
+                              (P.FP_PATH_MFMA, 4, 3 if M > 128 else 4, rs, 0, 0)))
             cands.append(("weight-resident (S=8)", (P.FP_PATH_MFMA, 4, 2, 8, 0, 0)))
             cands.append(("weight-resident (S=9)", (P.FP_PATH_MFMA, 4, 2, 9, 0, 0)))
         default_t = list(big[0].get_tiling(M))

@@ -272,18 +272,52 @@ int tile_pick_nw(int mt16, int64_t n_steps, int64_t S, int64_t n_rows) {
   return 0;
 }
 
+// The ring tile kernel addresses the weights with 32-bit buffer offsets.
+bool ring_addressable(int64_t n_rows, int64_t kc) {
+  return n_rows * kc * 16 < ((int64_t)1 << 31);
+}
+
+// Slices of the tile kernel for few tokens: the fewest whose slice fills a
+// compiled slice bound nearly (no wasted LDS rows) and fits in LDS; 0 if
+// none.
+int64_t tile_pick_slices(int64_t n_steps, int mt16, int nw) {
+  for (int64_t S = 1; S <= n_steps && S <= 0x1fff; ++S) {
+    const int64_t per = ceil_div(n_steps, S);
+    const int b = tile_per_bound(per);
+    if (b == 0 || per + 2 < b) continue;
+    if (tile_lds(mt16, per, nw) > kMaxLds) continue;
+    return S;
+  }
+  return 0;
+}
+
 bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
   const int mt16 = mfma_mt16(M);
   const int64_t n_steps = ceil_div(kc, 4);
-  if (mt16 >= 4) {
-    // 33 tokens and more: the ring tile kernel, four stage buffers (three
-    // for 256-token blocks, the most LDS holds), one workgroup per CU over
-    // the plan's 64-row blocks, at least two stages per slice.  Measured on
-    // MI355X (K = 5120, 1792 rows, 9 slices, second-launch finish): 12.9 us
-    // at M = 64 and 16.8 at M = 128, against 19.7 / 22.0 for the tile
-    // kernel.  The choice depends on (K, M bucket, plan rows) only.
-    const int64_t blocks = ceil_div(n_total, fp::kRingRows);
+  const int64_t blocks = ceil_div(n_total, fp::kRingRows);
+  // Up to 32 tokens the tile and weight-resident kernels run one workgroup
+  // per (64-row block, slice) and need them all resident at once; a plan
+  // with more blocks than that allows takes the ring tile kernel (measured
+  // on MI355X at K = 6144, 2752 rows, 9 slices: 14.88 / 15.19 us at M = 17 /
+  // 32 against 19.18 / 19.17 for the tile kernel).
+  const int64_t few_pick = mt16 <= 2 ? tile_pick_slices(n_steps, mt16, 4) : 0;
+  const bool ring = mt16 >= 4 || (few_pick > 0 && blocks * few_pick > kCus &&
+                                  ring_addressable(n_total, kc));
+  if (ring) {
+    // The ring tile kernel, four stage buffers (three for 256-token blocks,
+    // the most LDS holds), over the plan's 64-row blocks: one workgroup per
+    // CU, and up to 64 tokens up to 9 slices while that keeps at most three
+    // per CU; at least two stages per slice.  Measured on MI355X
+    // (second-launch finish from 17 tokens): K = 5120, 1792 rows, 9 slices:
+    // 12.9 us at M = 64 and 16.8 at M = 128, against 19.7 / 22.0 for the
+    // tile kernel; K = 6144, 2752 rows: 9 slices ahead of 5, 6, 7 and 12 up
+    // to 64 tokens (M = 9: 12.28 against 13.76 .. 13.23; M = 17: 14.88
+    // against 17.51 .. 16.13; M = 64: 18.38 against 21.05 with 5), but not
+    // above (M = 96: 5 slices 25.32, 9 slices 28.62, the weight-resident
+    // kernel at 9 slices 26.06).  The choice depends on (K, M bucket, plan
+    // rows) only.
     int64_t S = std::max<int64_t>(1, kCus / blocks);
+    if (mt16 <= 4) S = std::max<int64_t>(S, std::min<int64_t>(9, 3 * kCus / blocks));
     S = std::min<int64_t>(S, std::max<int64_t>(1, n_steps / 4));
     S = std::min<int64_t>(S, 0x1fff);
     t->path = FP_PATH_MFMA;
@@ -297,21 +331,13 @@ bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
     if (mt16 == 8 && wres_fits(kc, mt16, S)) t->chunks = kWresCode;
     return true;
   }
-  // Measured on MI355X (K = 5120, 1792 rows): four row tiles per workgroup
-  // (eight from 128 tokens), and the fewest slices whose slice fills a
-  // compiled slice bound nearly (no wasted LDS rows) and fits in LDS.  The
-  // choice depends on (K, M bucket) only, so every launch of a plan adds
-  // the same slices in the same order.
-  const int nw = mt16 >= 8 ? 8 : 4;
-  int64_t pick = 0;
-  for (int64_t S = 1; S <= n_steps && S <= 0x1fff; ++S) {
-    const int64_t per = ceil_div(n_steps, S);
-    const int b = tile_per_bound(per);
-    if (b == 0 || per + 2 < b) continue;
-    if (tile_lds(mt16, per, nw) > kMaxLds) continue;
-    pick = S;
-    break;
-  }
+  // Measured on MI355X (K = 5120, 1792 rows): four row tiles per workgroup,
+  // and the fewest slices whose slice fills a compiled slice bound nearly
+  // (no wasted LDS rows) and fits in LDS.  The choice depends on (K, M
+  // bucket, plan rows) only, so every launch of a plan adds the same slices
+  // in the same order.
+  const int nw = 4;
+  int64_t pick = few_pick;
   if (pick == 0) {
     // short K or odd shapes: any slice count that fits
     for (int64_t S = 1; S <= n_steps && S <= 0x1fff && pick == 0; ++S) {
@@ -399,27 +425,39 @@ void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs, int var)
 int smfma_tiles(const Tiling& t) { return t.rows > 8 ? 2 : 1; }
 int smfma_rt(const Tiling& t) { return t.rows / smfma_tiles(t); }
 
+// Waves of the small-M kernel one CU holds, from the register estimate of
+// its instantiation (KT steps, MH token halves, TT row tiles).  It never
+// exceeds what the compiled kernels reach on gfx950 (KT 8: 24 waves with
+// one half and one tile, 16 with two halves or two tiles; the estimate
+// gives 20, 12 and 16).
+int smfma_cu_waves(int kt, int mh, int tt) {
+  const int regs = 4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1);
+  return 4 * std::max(1, std::min(8, 512 / ((regs + 7) / 8 * 8)));
+}
+
 // Rows per workgroup R = G * TT * RT.  Every workgroup loads the whole
 // activation block once per row group, so the bytes a CU takes in are
 // (workgroups on the CU) x (R weight rows + G x mt activation rows); the
 // choice keeps every workgroup resident at once (one round) and, among
 // those, minimises that figure for the busiest CU (ties: the larger R,
-// fewer workgroups).  Two tiles per wave (more registers, at most 16 waves
-// per CU) are offered to bf16 plans with one token half.  Without a
-// one-round choice the largest R is taken.  Measured on MI355X (weights
+// fewer workgroups), with at most two workgroups per CU counted resident
+// and the waves a CU holds taken from the kernel's register estimate
+// (bf16; block-scaled kernels: 32).  Two tiles per wave are offered to
+// bf16 plans with one token half.  Without a one-round choice the largest
+// R is taken; the result says whether a one-round layout exists.  Measured on MI355X (weights
 // rotated past the MALL, us per call): K = 6144, 2752 rows, M = 8: two
 // tiles of 6 rows per wave (230 workgroups) 8.86 against one tile of 6
 // (459) 10.61; M = 5: 8.54 vs 8.88.  Short K, where the former rule (rows
 // on the busiest CU alone) took one-row groups that each reload the
 // activations, M = 8: K = 512, 1792 rows 3.27 vs 7.03 (seven groups of
 // one row); K = 1024, 2048 rows 3.00 vs 5.01; K = 2048 3.86 vs 4.69.
-void resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs, bool two_tiles) {
-  if (t->rows > 0 && t->groups > 0) return;
+bool resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs, bool bf16) {
+  if (t->rows > 0 && t->groups > 0) return true;
   int best_rows = pairs ? 2 : 1, best_g = 1;
   int64_t best_cost = INT64_MAX;
   const int mh = t->mt / 8;
   for (int tt = 1; tt <= 2; ++tt) {
-    if (tt == 2 && (!two_tiles || pairs || mh != 1)) continue;
+    if (tt == 2 && (!bf16 || pairs || mh != 1)) continue;
     for (int rt = pairs ? 2 : 1; rt <= 8; rt += pairs ? 2 : 1) {
       if (tt == 2 && rt < 5) continue;  // rows <= 8 denote one tile
       const int rows = tt * rt;
@@ -433,7 +471,9 @@ void resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs, bool two_tiles) {
         const int64_t R = (int64_t)rows * g;
         const int64_t nb = ceil_div(n_rows, R);
         const int waves = g * t->kparts;
-        const int cu_waves = tt == 1 ? 32 : 16;
+        // block-scaled kernels: 32 waves per CU assumed, as measured for
+        // their rows choice
+        const int cu_waves = bf16 ? smfma_cu_waves(t->chunks, mh, tt) : 32;
         const int64_t resident = std::max(1, std::min(2, cu_waves / waves));
         const bool one_round = nb <= resident * kCus;
         const int64_t cost =
@@ -448,6 +488,7 @@ void resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs, bool two_tiles) {
   }
   t->rows = best_rows;
   t->groups = best_g;
+  return best_cost < INT64_MAX / 4;  // a one-round layout was found
 }
 
 size_t smfma_lds(const Tiling& t) {
@@ -536,7 +577,7 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     if (16 * (int64_t)t.mt < M) return false;
     // buffer offsets are 32-bit, with 0x80000000 reserved as out of range
     if ((int64_t)t.splits * n_rows * 16 * t.mt * 4 >= ((int64_t)1 << 31)) return false;
-    if (n_rows * p->kc * 16 >= ((int64_t)1 << 31)) return false;
+    if (!ring_addressable(n_rows, p->kc)) return false;
   } else if (t.path == FP_PATH_MFMA) {
     if (p->dtype != FP_BF16) return false;
     const int64_t n_steps = ceil_div(p->kc, 4);
@@ -609,12 +650,35 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
     // fp32-output plans run the vector-ALU kernel only
     const bool mfma = p->dtype == FP_BF16 && !p->out_f32 &&
                       (M >= p->mfma_min_m || M > kSmallMfmaMaxM);
-    // bf16 and block-scaled weights: the small-M kernel up to 16 tokens
-    const bool small = (p->dtype == FP_BF16 || is_mx(p->dtype)) &&
-                       !p->out_f32 && !mfma &&
-                       (M >= p->small_mfma_min_m || M > kSkinnyMaxM) &&
-                       default_smfma_order(p->kc, t);
-    if (mfma) {
+    // bf16 and block-scaled weights: the small-M kernel up to 16 tokens,
+    // when its workgroup of K parts fits the kernel's thread bound (long K
+    // with two token halves does not: up to 8 tokens the vector-ALU kernel
+    // serves, above that bf16 takes the matrix-core path).  A bf16 plan
+    // whose two-half launches cannot keep every workgroup resident at once
+    // (more rows than one workgroup per CU holds) takes the matrix-core
+    // path too: measured on MI355X at K = 6144, 2752 rows, M = 9 / 16: ring
+    // tile kernel 12.28 / 12.64 us against the small-M kernel's two rounds,
+    // 13.87 / 14.01.
+    bool small = (p->dtype == FP_BF16 || is_mx(p->dtype)) &&
+                 !p->out_f32 && !mfma &&
+                 (M >= p->small_mfma_min_m || M > kSkinnyMaxM) &&
+                 default_smfma_order(p->kc, t);
+    if (small) {
+      Tiling probe = *t;
+      probe.mt = M > 8 ? 16 : 8;
+      const bool one_round = resolve_smfma_rows(p->n_total, &probe, pairs,
+                                                p->dtype == FP_BF16);
+      const bool fits = (int64_t)probe.groups * probe.kparts * 64 <=
+                        fp::smfma_max_threads(probe.chunks, probe.mt / 8, smfma_tiles(probe));
+      if (!fits)
+        small = false;
+      else if (!one_round && !pairs && p->dtype == FP_BF16 && M > 8 &&
+               ring_addressable(p->n_total, p->kc))
+        small = false;
+    }
+    const bool to_mfma = mfma || (!small && p->dtype == FP_BF16 && !p->out_f32 &&
+                                  M > kSkinnyMaxM);
+    if (to_mfma) {
       if (!default_mfma_order(p->kc, M, p->n_total, t)) return false;
     } else if (small) {
       // order fields already set

@@ -146,9 +146,11 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
         st, (path, kp, ch, S, rows, groups) = P.fp_default_tiling(dtype, K, n_total, M, n_total)
         assert st == 0
         if path == P.FP_PATH_MFMA and ch in (3, 4, 6):
-            # the ring tile kernel (33 tokens and more): 64-row blocks,
-            # chunks = stage buffers
-            assert M >= 33 and kp == 4 and (ch == 3) == (M > 128)
+            # the ring tile kernel (33 tokens and more, or from 9 tokens on
+            # plans of more 64-row blocks than the tile kernels run in one
+            # round): 64-row blocks, chunks = stage buffers
+            assert (M >= 33 or (M >= 9 and n_total > 1792)) and kp == 4
+            assert (ch == 3) == (M > 128)
         elif path == P.FP_PATH_MFMA and ch == 2:
             # the weight-resident tile kernel (17..32 and 65..128 tokens):
             # 64-row blocks, a slice of at most 16 (12) stages of 64 k
@@ -190,11 +192,26 @@ def test_default_crossover():
     for M in (17, 32, 64, 128):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA
     # more rows than one 8-row tile per CU (the three-way fused-A shape):
-    # the vector-ALU kernel through M = 4
+    # the vector-ALU kernel through M = 4, the small-M kernel with two row
+    # tiles per wave for 5..8, the ring tile kernel with 9 slices from 9 on
+    # (two-half small-M launches would need two rounds of workgroups)
     for M in range(1, 5):
         assert P.fp_default_tiling(0, 6144, 2752, M, 2752)[1][0] == P.FP_PATH_SKINNY
-    for M in range(5, 17):
-        assert P.fp_default_tiling(0, 6144, 2752, M, 2752)[1][0] == P.FP_PATH_MFMA_SMALL
+    for M in range(5, 9):
+        st, t = P.fp_default_tiling(0, 6144, 2752, M, 2752)
+        assert t[0] == P.FP_PATH_MFMA_SMALL and t[4] == 12
+    for M in (9, 16, 17, 32, 48, 64):
+        st, t = P.fp_default_tiling(0, 6144, 2752, M, 2752)
+        assert t[0] == P.FP_PATH_MFMA and t[1] == 4 and t[2] == 4 and t[3] == 9
+    # above 64 tokens one slice per CU's share of the 43 row blocks
+    for M in (96, 128):
+        st, t = P.fp_default_tiling(0, 6144, 2752, M, 2752)
+        assert t[0] == P.FP_PATH_MFMA and t[2] == 4 and t[3] == 5
+    # long K with two token halves (the small-M workgroup would exceed its
+    # thread bound): the tile kernels, not a refusal
+    for M in (9, 16):
+        assert P.fp_default_tiling(0, 7168, 1536, M, 1536)[1][0] == P.FP_PATH_MFMA
+        assert P.fp_default_tiling(0, 7168, 2112, M, 2112)[1][0] == P.FP_PATH_MFMA
     assert P.fp_default_tiling(0, 5120, 2048, 3, 2048)[1][0] == P.FP_PATH_MFMA_SMALL
     assert P.fp_default_tiling(0, 5120, 2049, 3, 2049)[1][0] == P.FP_PATH_SKINNY
 

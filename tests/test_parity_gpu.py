@@ -523,3 +523,24 @@ def test_page_fused_a_indexer_shape_graph_replay():
         torch.cuda.synchronize()
         assert_bitwise_equal(outs, fp(xs), "2784 rows replay seed %d" % seed)
         assert_matches_oracle(outs, xn, ws, label="2784 rows replay")
+
+
+# ---- plans past one round of small-M or tile workgroups: the ring tile
+#      kernel from 9 tokens on the three-way fused-A shape, and the tile
+#      kernels where a two-half small-M workgroup would exceed its thread
+#      bound (K = 7168); defaults, against the oracle
+@pytest.mark.parametrize("M", [9, 16, 17, 32, 48, 64])
+def test_three_way_defaults_above_eight_tokens(M):
+    x, ws = si.make_case(6144, (2048, 576, 128), "bf16", M, seed=90 + M)
+    fp = _plan(ws, max_M=M)
+    assert fp.query(M)[0] == P.FP_PATH_MFMA
+    _check_case(fp, x, ws, "three-way default M=%d" % M)
+
+
+@pytest.mark.parametrize("N", [(1536,), (1536, 576)])
+@pytest.mark.parametrize("M", [9, 12, 16])
+def test_long_k_two_halves_defaults(N, M):
+    x, ws = si.make_case(7168, N, "bf16", M, seed=80 + M)
+    fp = _plan(ws, max_M=16)
+    assert fp.query(M)[0] == P.FP_PATH_MFMA
+    _check_case(fp, x, ws, "K=7168 %s M=%d" % (N, M))
