@@ -504,11 +504,14 @@ def test_page_fused_a_shapes_through_the_kernels(name, M):
     _check_case(fp, x, ws, "%s M=%d" % (name, M))
 
 
-def test_page_fused_a_indexer_shape_graph_replay():
+# M = 4: vector-ALU kernel; 8: small-M kernel with two row tiles per wave;
+# 16: ring tile kernel with its in-launch finish; 32: ring tile kernel and
+# the second-launch finish
+@pytest.mark.parametrize("M", [4, 8, 16, 32])
+def test_page_fused_a_indexer_shape_graph_replay(M):
     K, N = _page_shape("glm_fused_a_indexer")
-    M = 4
     x0, ws = si.make_case(K, N, "bf16", M, seed=40)
-    fp = _plan(ws, max_M=8)
+    fp = _plan(ws, max_M=max(8, M))
     xs = to_gpu(x0)
     outs = [torch.empty(M, n, dtype=BF16, device="cuda") for n in N]
     fp(xs, out=outs)
@@ -521,8 +524,8 @@ def test_page_fused_a_indexer_shape_graph_replay():
         xs.copy_(to_gpu(xn))
         g.replay()
         torch.cuda.synchronize()
-        assert_bitwise_equal(outs, fp(xs), "2784 rows replay seed %d" % seed)
-        assert_matches_oracle(outs, xn, ws, label="2784 rows replay")
+        assert_bitwise_equal(outs, fp(xs), "2784 rows replay M=%d seed %d" % (M, seed))
+        assert_matches_oracle(outs, xn, ws, label="2784 rows replay M=%d" % M)
 
 
 # ---- plans past one round of small-M or tile workgroups: the ring tile

@@ -43,6 +43,10 @@ def _rows(M):
     ("crossover", (64, 20, 4), None),
     # fp32 indexer with a forced skinny K split (partials + counters)
     ("indexer_f32", (8, 3), (P.FP_PATH_SKINNY_SPLITK, 7, 1, 4, 0, 0)),
+    # three-way fused-A (2752 rows): ring tile kernel with 9 slices and the
+    # second-launch finish, then its in-launch finish, then the small-M
+    # kernel with two row tiles per wave
+    ("fused_a_3way", (64, 16, 8), None),
 ])
 def test_noalloc_equals_fp_forward_on_shrinking_calls(name, Ms, tiling):
     x0, ws = si.workload_case(name, max(Ms), 0)
