@@ -3,7 +3,9 @@
 "tinygemm2 for the DeepSeek-V4.1 hidden-state projections" (TensorRT-LLM
 PR #20636), Test Coverage: CUDA graph capture/replay of the fused call is
 bitwise equal to eager over three new inputs, and a 20,000-replay stress
-with no positive control.  Here every replay gets new inputs written into
+with no positive control.  Here the 20,000 replays run too (fixed input,
+every replay compared with the first), and in the shorter stresses every
+replay gets new inputs written into
 the captured input buffer, the program's own eager calls and
 synchronizations run between replays, every replay is compared with an
 eager run, and a positive control (a perturbed input) must be detected.
@@ -91,6 +93,32 @@ def test_replay_stress_with_positive_control(name, M):
     torch.cuda.synchronize()
     differs = any(not np.array_equal(p, q) for p, q in zip(out_bits(outs), out_bits(eager)))
     assert differs, "comparison cannot see a perturbed input"
+
+
+@pytest.mark.parametrize("name,M", [("wq_a+wkv_m1", 1), ("wq_a+wkv_m2_8", 8), ("crossover", 32)])
+def test_twenty_thousand_replays_stay_bitwise_stable(name, M):
+    """The pages' stress length: 20,000 replays of one captured call on a
+    fixed input, every replay's outputs compared on the device with the
+    first replay's (and those with an eager call); at 32 tokens the split
+    finish's arrival counters must reset themselves every time."""
+    x0, ws = si.workload_case(name, M, 5)
+    fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=max(8, M))
+    x_static = to_gpu(x0)
+    outs = [torch.empty(M, n, dtype=x_static.dtype, device="cuda") for n in fp.N]
+    g = _capture(fp, x_static, outs)
+    g.replay()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    assert_bitwise_equal(ref, fp(x_static), "%s M=%d first replay vs eager" % (name, M))
+    diff = torch.zeros((), dtype=torch.int64, device="cuda")
+    for _ in range(20000):
+        g.replay()
+        for o, r in zip(outs, ref):
+            diff += (o.view(torch.int16) != r.view(torch.int16)).sum()
+    torch.cuda.synchronize()
+    assert int(diff) == 0, "%d output elements changed over 20,000 replays" % int(diff)
+    assert_matches_oracle(outs, x0, ws, rows=None if M <= 16 else [0, M - 1],
+                          label="%s M=%d after 20,000 replays" % (name, M))
 
 
 def _hip():
