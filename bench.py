@@ -530,8 +530,8 @@ def host_info():
 
 # Workloads of the crossover tables: (title, K, N, token counts, small-M
 # row layouts forced besides the library's: (label, rows, groups) -- rows
-# above 8 are two row tiles of rows / 2 per wave, one token half only --,
-# K slice counts of the ring tile kernel).
+# above 8 are two row tiles of rows / 2 per wave --, K slice counts of the
+# ring tile kernel).
 _SMALL_ROWS = (("one tile of 6 rows", 6, 1), ("one tile of 8 rows", 8, 1),
                ("two tiles of 6 rows", 12, 1), ("two tiles of 8 rows", 16, 1))
 CROSSOVER_SHAPES = {
@@ -570,8 +570,7 @@ def crossover(prefix, P, torch, dev, workload="wq_a+wkv", pool_mib=1024):
         if M <= 16:
             cands.append(("small-M MFMA", (P.FP_PATH_MFMA_SMALL, pk, kt, 1, 0, 0)))
             for label, r, g in small_rows:
-                if r <= 8 or M <= 8:
-                    cands.append(("small-M MFMA, " + label, (P.FP_PATH_MFMA_SMALL, pk, kt, 1, r, g)))
+                cands.append(("small-M MFMA, " + label, (P.FP_PATH_MFMA_SMALL, pk, kt, 1, r, g)))
         if M > 8:
             cands.append(("tile (S=8)", (P.FP_PATH_MFMA, 0, 0, 8, 0, 0)))
             for rs in ring_slices:

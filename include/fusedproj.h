@@ -360,8 +360,8 @@ fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
  *           (mfma-small: 1)
  *   rows    skinny: rows per wave (RW, 1..8); mfma-small: rows per row
  *           group, 1..8 as one tile, or an even 10..16 as two tiles of
- *           rows / 2 per wave sharing the activations (bf16, M <= 8, not
- *           gate/up); 0 = chosen per launch from its row count; mfma: unused
+ *           rows / 2 per wave sharing the activations (bf16, not gate/up);
+ *           0 = chosen per launch from its row count; mfma: unused
  *   groups  skinny and mfma-small: row groups per workgroup (G); 0 =
  *           chosen per launch; mfma: how the K slices are added -- 1 by
  *           the last workgroup of each row block, in the launch; 2 by a

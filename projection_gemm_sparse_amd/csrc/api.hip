@@ -416,22 +416,19 @@ void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs, int var)
   t->groups = best_g;
 }
 
-// Rows per tile (<= 8) and row groups per workgroup of the small-M
-// matrix-core kernel, by the same one-round, least-loaded-CU rule as the
-// skinny kernel.
 // Small-M kernel rows: `rows` 1..8 is one tile of that many rows per wave;
-// an even 10..16 is two tiles of rows / 2 (one token half, bf16, not
-// gate/up) that share each wave's activation operand.
+// an even 10..16 is two tiles of rows / 2 (bf16, not gate/up) that share
+// each wave's activation operand.
 int smfma_tiles(const Tiling& t) { return t.rows > 8 ? 2 : 1; }
 int smfma_rt(const Tiling& t) { return t.rows / smfma_tiles(t); }
 
 // Waves of the small-M kernel one CU holds, from the register estimate of
 // its instantiation (KT steps, MH token halves, TT row tiles).  It never
 // exceeds what the compiled kernels reach on gfx950 (KT 8: 24 waves with
-// one half and one tile, 16 with two halves or two tiles; the estimate
-// gives 20, 12 and 16).
+// one half and one tile, 16 with two halves or two tiles, 12 with both;
+// the estimate gives 20, 12, 16 and 12).
 int smfma_cu_waves(int kt, int mh, int tt) {
-  const int regs = 4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1);
+  const int regs = fp::smfma_regs(kt, mh, tt);
   return 4 * std::max(1, std::min(8, 512 / ((regs + 7) / 8 * 8)));
 }
 
@@ -443,21 +440,23 @@ int smfma_cu_waves(int kt, int mh, int tt) {
 // fewer workgroups), with at most two workgroups per CU counted resident
 // and the waves a CU holds taken from the kernel's register estimate
 // (bf16; block-scaled kernels: 32).  Two tiles per wave are offered to
-// bf16 plans with one token half.  Without a one-round choice the largest
-// R is taken; the result says whether a one-round layout exists.  Measured on MI355X (weights
-// rotated past the MALL, us per call): K = 6144, 2752 rows, M = 8: two
-// tiles of 6 rows per wave (230 workgroups) 8.86 against one tile of 6
-// (459) 10.61; M = 5: 8.54 vs 8.88.  Short K, where the former rule (rows
-// on the busiest CU alone) took one-row groups that each reload the
-// activations, M = 8: K = 512, 1792 rows 3.27 vs 7.03 (seven groups of
-// one row); K = 1024, 2048 rows 3.00 vs 5.01; K = 2048 3.86 vs 4.69.
+// bf16 plans (not gate/up).  Without a one-round choice the largest R is
+// taken; the result says whether a one-round layout exists.
+//
+// Measured on MI355X (weights rotated past the MALL, us per call): K =
+// 6144, 2752 rows, M = 8: two tiles of 6 rows per wave (230 workgroups)
+// 8.86 against one tile of 6 (459) 10.61; M = 5: 8.54 vs 8.88.  Short K,
+// where the former rule (rows on the busiest CU alone) took one-row groups
+// that each reload the activations, M = 8: K = 512, 1792 rows 3.27 vs 7.03
+// (seven groups of one row); K = 1024, 2048 rows 3.00 vs 5.01; K = 2048
+// 3.86 vs 4.69.
 bool resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs, bool bf16) {
   if (t->rows > 0 && t->groups > 0) return true;
   int best_rows = pairs ? 2 : 1, best_g = 1;
   int64_t best_cost = INT64_MAX;
   const int mh = t->mt / 8;
   for (int tt = 1; tt <= 2; ++tt) {
-    if (tt == 2 && (!bf16 || pairs || mh != 1)) continue;
+    if (tt == 2 && (!bf16 || pairs)) continue;
     for (int rt = pairs ? 2 : 1; rt <= 8; rt += pairs ? 2 : 1) {
       if (tt == 2 && rt < 5) continue;  // rows <= 8 denote one tile
       const int rows = tt * rt;
@@ -554,9 +553,10 @@ WsView plan_ws(const fp_plan_s* p) {
   w.counters = p->ws;
   w.partial = p->ws + cb;
   w.counter_bytes = cb;
-  w.partial_bytes = p->ws_bytes < (size_t)cb ? -1
-                    : p->ws_bytes - (size_t)cb > (size_t)INT64_MAX ? INT64_MAX
-                                                                     : (int64_t)(p->ws_bytes - (size_t)cb);
+  const size_t rest = p->ws_bytes < (size_t)cb ? 0 : p->ws_bytes - (size_t)cb;
+  w.partial_bytes = p->ws_bytes < (size_t)cb           ? -1
+                    : rest > (size_t)INT64_MAX ? INT64_MAX
+                                               : (int64_t)rest;
   return w;
 }
 
@@ -596,7 +596,7 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
     if (M > kSmallMfmaMaxM || t.mt < M) return false;
     if (!(t.chunks == 4 || t.chunks == 8 || t.chunks == 16)) return false;
     if (t.splits != 1 || t.kparts > fp::kMaxWaveParts || t.rows > 16 || t.groups < 1) return false;
-    if (t.rows > 8 && (t.rows % 2 != 0 || t.mt != 8 || p->dtype != FP_BF16)) return false;
+    if (t.rows > 8 && (t.rows % 2 != 0 || p->dtype != FP_BF16)) return false;
     if ((int64_t)t.groups * t.kparts * 64 >
         fp::smfma_max_threads(t.chunks, t.mt / 8, smfma_tiles(t)))
       return false;

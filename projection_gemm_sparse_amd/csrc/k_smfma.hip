@@ -13,7 +13,11 @@ constexpr int kSmfmaInterleaveMaxM = 12;
 template <int KT>
 const void* smfma_kt(bool pairs, int mt, int64_t M, int tt) {
   if (tt == 2) {
-    if (pairs || mt != 8) return nullptr;
+    if (pairs) return nullptr;
+    if (mt == 16)
+      return M <= kSmfmaInterleaveMaxM
+                 ? reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 2, false, 2>)
+                 : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 2, true, 2>);
     return reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 1, true, 2>);
   }
   if (tt != 1) return nullptr;

@@ -39,8 +39,8 @@
 // Work split.  A workgroup owns G row groups of TT tiles of RT <= 8 rows (a
 // tile with RT < 8 leaves its last A rows unused; the 1792-row fused launch
 // uses one tile of 7 rows per workgroup so that its 256 workgroups cover
-// the 256 CUs once).  With TT = 2 tiles (one token half) every wave
-// multiplies the same activation operand with the weights of two tiles:
+// the 256 CUs once).  With TT = 2 tiles every wave multiplies the same
+// activation operand (each token half's) with the weights of two tiles:
 // a launch of more rows than 8 per CU then keeps one workgroup per CU,
 // and each CU loads the activations once instead of once per workgroup
 // (at M = 8 and K = 6144 the activations are 98 KB per workgroup, more
@@ -65,8 +65,18 @@ namespace fp {
 
 constexpr int kFmtNv4 = 5;  // the NVFP4 form of smfma_mx_kernel
 
+// Per-lane register estimate: the KT steps' 16-byte chunks of every tile's
+// weights and every half's activations, plus addresses and accumulators.
+// The two-tile two-half form is counted as compiled (144-152 VGPRs on
+// gfx950 at KT = 8, so that 12 waves fit a CU); the other forms keep the
+// estimate they were tuned with.
+constexpr int smfma_regs(int kt, int mh, int tt) {
+  return tt == 2 && mh == 2 ? 4 * kt * 4 + 40
+                            : 4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1);
+}
+
 constexpr int smfma_max_threads(int kt, int mh = 1, int tt = 1) {
-  return max_threads_for_regs(4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1));
+  return max_threads_for_regs(smfma_regs(kt, mh, tt));
 }
 
 // Output stage of both small-M kernels (not gate/up).  The cross-wave
@@ -107,15 +117,15 @@ __device__ __forceinline__ void smfma_store_outputs(const float* smem, int Gv, i
 // (1: M <= 8, 2: M <= 16).  XFIRST (two halves): every activation load
 // before the weights (the fuller second halves) instead of each step's
 // first-half, weight and second-half chunks in turn.  TT: row tiles per
-// wave (2 only with one token half, not gate/up); tile j of row group g2
-// holds rows row_base + (g2 TT + j) RT ...
+// wave (2: not gate/up); tile j of row group g2 holds rows
+// row_base + (g2 TT + j) RT ...
 template <int KT, bool PAIRS = false, int MH = 1, bool XFIRST = true, int TT = 1>
 __global__ void __launch_bounds__(smfma_max_threads(KT, MH, TT))
 smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
              unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
              int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
   static_assert(MH == 1 || (MH == 2 && !PAIRS), "token halves");
-  static_assert(TT == 1 || (TT == 2 && MH == 1 && !PAIRS), "two tiles: one half, no pairs");
+  static_assert(TT == 1 || (TT == 2 && !PAIRS), "two tiles: not gate/up");
   extern __shared__ float smem[];  // [G][TT][MH][16 wave parts][2][8][8]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -194,14 +204,15 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
       }
     } else if constexpr (!XFIRST) {
       // two halves, the second at most half full: per step the first
-      // half's chunk, the weight chunk, the second half's chunk (M = 9:
+      // half's chunk, the weight chunks, the second half's chunk (M = 9:
       // 6.69 vs 6.96 us with the activations first)
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         const int c = cw + 8 * t + cl;
         const int cc = c < kc ? c : kc - 1;
         xv[0][t] = xrow[0][cc];
-        wv[0][t] = __builtin_nontemporal_load(wrow + cc);
+#pragma unroll
+        for (int j = 0; j < TT; ++j) wv[j][t] = __builtin_nontemporal_load(wrows[j] + cc);
         xv[MH - 1][t] = xrow[MH - 1][cc];
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -218,7 +229,9 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         const int c = cw + 8 * t + cl;
-        wv[0][t] = __builtin_nontemporal_load(wrow + (c < kc ? c : kc - 1));
+#pragma unroll
+        for (int j = 0; j < TT; ++j)
+          wv[j][t] = __builtin_nontemporal_load(wrows[j] + (c < kc ? c : kc - 1));
       }
     }
   }
@@ -249,15 +262,23 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
         acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[h], 0, 0, 0);
       }
     } else {
-      // the activations once, then each tile's weights and product
-      const bool tok_ok = r8 < M;
-      const u32x4 xb = shuffle(xv[0][t]);
-      const bf16x8 B = u4bf8(c_ok && tok_ok ? xb : zero4);
+      // the activations of each half once, then each tile's weights and
+      // its products with every half
+      bf16x8 B[MH];
+#pragma unroll
+      for (int h = 0; h < MH; ++h) {
+        const bool tok_ok = r8 + 8 * h < M;
+        const u32x4 xb = shuffle(xv[h][t]);
+        B[h] = u4bf8(c_ok && tok_ok ? xb : zero4);
+      }
 #pragma unroll
       for (int j = 0; j < TT; ++j) {
         const u32x4 wa = shuffle(wv[j][t]);
         const bf16x8 A = u4bf8(c_ok ? wa : zero4);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[j], 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < MH; ++h)
+          acc[j * MH + h] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[h], acc[j * MH + h], 0, 0, 0);
       }
     }
   }
@@ -470,8 +491,9 @@ smfma_mx_kernel(const unsigned char* __restrict__ w, const unsigned char* __rest
           d[3] = decode_e2m1_pair<3>(qe, sce);
         }
       }
-      const u32x4 wa = u32x4{__builtin_bit_cast(unsigned, d[0]), __builtin_bit_cast(unsigned, d[1]),
-                             __builtin_bit_cast(unsigned, d[2]), __builtin_bit_cast(unsigned, d[3])};
+      const u32x4 wa =
+          u32x4{__builtin_bit_cast(unsigned, d[0]), __builtin_bit_cast(unsigned, d[1]),
+                __builtin_bit_cast(unsigned, d[2]), __builtin_bit_cast(unsigned, d[3])};
       const bf16x8 A = u4bf8(c_ok ? wa : zero4);
 #pragma unroll
       for (int h = 0; h < MH; ++h) {

@@ -349,7 +349,8 @@ splitk_reduce_kernel(const float* __restrict__ partial, int32_t n_rows, int32_t 
   // the slices in groups (8, or 16 above 8 slices): all loads of a group
   // are issued before the first add (one load latency per group, not per
   // slice), then added in slice order
-  const f32x4 sum = S <= 8 ? sum_slices_ptr<8>(p, sstride / 4, S) : sum_slices_ptr<16>(p, sstride / 4, S);
+  const f32x4 sum =
+      S <= 8 ? sum_slices_ptr<8>(p, sstride / 4, S) : sum_slices_ptr<16>(p, sstride / 4, S);
   // the row's segment: the last one whose first row is at or before it
   int seg = 0;
   for (int i = 1; i < tab.n_seg; ++i) seg = row >= tab.begin[i] ? i : seg;

@@ -165,9 +165,9 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
         elif path == P.FP_PATH_MFMA_SMALL:
             assert dtype == 0 and 3 <= M <= 16
             assert S == 1 and kp <= 16 and kp * ch * 8 >= kc
-            # rows per row group: one tile of 1..8 rows, or (one token
-            # half) two tiles of rows / 2 sharing the activations
-            assert (1 <= rows <= 8 or (rows in (10, 12, 14, 16) and M <= 8)) and groups >= 1
+            # rows per row group: one tile of 1..8 rows, or two tiles of
+            # rows / 2 sharing the activations
+            assert (1 <= rows <= 8 or rows in (10, 12, 14, 16)) and groups >= 1
         else:
             assert M <= 8
             assert S * kp * 64 * ch >= kc
@@ -193,14 +193,14 @@ def test_default_crossover():
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA
     # more rows than one 8-row tile per CU (the three-way fused-A shape):
     # the vector-ALU kernel through M = 4, the small-M kernel with two row
-    # tiles per wave for 5..8, the ring tile kernel with 9 slices from 9 on
-    # (two-half small-M launches would need two rounds of workgroups)
+    # tiles of 6 per wave for 5..16 (one or two token halves), the ring
+    # tile kernel with 9 slices from 17 on
     for M in range(1, 5):
         assert P.fp_default_tiling(0, 6144, 2752, M, 2752)[1][0] == P.FP_PATH_SKINNY
-    for M in range(5, 9):
+    for M in range(5, 17):
         st, t = P.fp_default_tiling(0, 6144, 2752, M, 2752)
-        assert t[0] == P.FP_PATH_MFMA_SMALL and t[4] == 12
-    for M in (9, 16, 17, 32, 48, 64):
+        assert t[0] == P.FP_PATH_MFMA_SMALL and t[4] == 12 and t[5] == 1
+    for M in (17, 32, 48, 64):
         st, t = P.fp_default_tiling(0, 6144, 2752, M, 2752)
         assert t[0] == P.FP_PATH_MFMA and t[1] == 4 and t[2] == 4 and t[3] == 9
     # above 64 tokens one slice per CU's share of the 43 row blocks

@@ -196,8 +196,8 @@ def test_tilings_all_pass(M):
                      and (M > 8 or (t[2] > 2 and M > 2)))
                     or (t[0] == P.FP_PATH_MFMA and M <= 8)
                     or (t[0] == P.FP_PATH_MFMA_SMALL and M > 8
-                        and (t[4] > 8
-                             or max(1, t[5]) * t[1] * 64 > _smfma_thread_cap(t[2], 2)))), (t, st)
+                        and max(1, t[5]) * t[1] * 64 >
+                        _smfma_thread_cap(t[2], 2, 2 if t[4] > 8 else 1))), (t, st)
             continue
         ran += 1
         ys = fp(xg)
@@ -266,7 +266,10 @@ def test_single_row_projections_and_one_projection():
 def _smfma_thread_cap(kt, mh, tt=1):
     """Largest workgroup of the small-M matrix-core kernel: its register
     estimate per lane (tt row tiles per wave), 4 waves per SIMD at most."""
-    regs = 4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1)
+    if tt == 2 and mh == 2:
+        regs = 4 * kt * 4 + 40
+    else:
+        regs = 4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1)
     return 256 * max(1, min(4, 512 // regs))
 
 
@@ -300,7 +303,7 @@ def test_small_mfma_path(case, M):
 #      activation operand): same per-row order as one tile, so the outputs
 #      are bitwise those of one tile of rows / 2, and within the bound
 @pytest.mark.parametrize("case", ["fused_a_3way", "ragged", "single_rows", "k8", "page_2784"])
-@pytest.mark.parametrize("M", [1, 3, 5, 8])
+@pytest.mark.parametrize("M", [1, 3, 5, 8, 9, 12, 13, 16])
 def test_small_mfma_two_tiles_per_wave(case, M):
     if case == "fused_a_3way":
         x, ws = si.workload_case("fused_a_3way", M, 2)
@@ -313,13 +316,14 @@ def test_small_mfma_two_tiles_per_wave(case, M):
     else:
         K, N = _page_shape("glm_fused_a_indexer")
         x, ws = si.make_case(K, N, "bf16", M, seed=73 + M)
-    fp = _plan(ws, max_M=8)
+    fp = _plan(ws, max_M=16)
     base = _small_mfma_tiling(fp.K)
+    mh = 2 if M > 8 else 1
     xg = to_gpu(x)
     ref = None
     for rows, groups in ((10, 1), (12, 1), (14, 2), (16, 1), (6, 1)):
         st = fp.set_tiling(M, base[:4] + (rows, groups))
-        if groups * base[1] * 64 > _smfma_thread_cap(base[2], 1, 2 if rows > 8 else 1):
+        if groups * base[1] * 64 > _smfma_thread_cap(base[2], mh, 2 if rows > 8 else 1):
             assert st == P.FP_ERR_UNSUPPORTED, (rows, groups)
             continue
         assert st == P.FP_OK, (rows, groups)
@@ -337,12 +341,15 @@ def test_small_mfma_two_tiles_refused_where_unsupported():
     x, ws = si.workload_case("fused_a_3way", 9, 0)
     fp = _plan(ws, max_M=16)
     base = _small_mfma_tiling(fp.K)
-    # two token halves, odd row counts above 8, more than 16 rows
-    assert fp.set_tiling(9, base[:4] + (12, 1)) == P.FP_ERR_UNSUPPORTED
+    # odd row counts above 8, more than 16 rows, a workgroup past the
+    # two-tile two-half thread bound (16 K parts of 64 lanes > 768)
     assert fp.set_tiling(8, base[:4] + (11, 1)) == P.FP_ERR_UNSUPPORTED
     assert fp.set_tiling(8, base[:4] + (18, 1)) == P.FP_ERR_UNSUPPORTED
+    assert fp.set_tiling(9, (P.FP_PATH_MFMA_SMALL, 16, 8, 1, 12, 1)) == P.FP_ERR_UNSUPPORTED
     assert fp.set_tiling(8, base[:4] + (12, 1)) == P.FP_OK
+    assert fp.set_tiling(9, base[:4] + (12, 1)) == P.FP_OK
     fp.set_tiling(8, None)
+    fp.set_tiling(9, None)
 
 
 # ---- the split tile path finishes its K slices either in the launch (last
@@ -504,12 +511,17 @@ def test_page_fused_a_shapes_through_the_kernels(name, M):
     _check_case(fp, x, ws, "%s M=%d" % (name, M))
 
 
-# M = 4: vector-ALU kernel; 8: small-M kernel with two row tiles per wave;
-# 16: ring tile kernel with its in-launch finish; 32: ring tile kernel and
-# the second-launch finish
-@pytest.mark.parametrize("M", [4, 8, 16, 32])
-def test_page_fused_a_indexer_shape_graph_replay(M):
-    K, N = _page_shape("glm_fused_a_indexer")
+# M = 4: vector-ALU kernel; 8 and 16: small-M kernel with two row tiles per
+# wave (one and two token halves); 32: ring tile kernel and the
+# second-launch finish.  K = 7168 over 2112 rows at 12 tokens: the ring
+# tile kernel with its in-launch finish.
+@pytest.mark.parametrize("case,M", [("page", 4), ("page", 8), ("page", 16), ("page", 32),
+                                    ("k7168", 12)])
+def test_page_fused_a_indexer_shape_graph_replay(case, M):
+    if case == "page":
+        K, N = _page_shape("glm_fused_a_indexer")
+    else:
+        K, N = 7168, (1536, 576)
     x0, ws = si.make_case(K, N, "bf16", M, seed=40)
     fp = _plan(ws, max_M=max(8, M))
     xs = to_gpu(x0)
@@ -524,8 +536,8 @@ def test_page_fused_a_indexer_shape_graph_replay(M):
         xs.copy_(to_gpu(xn))
         g.replay()
         torch.cuda.synchronize()
-        assert_bitwise_equal(outs, fp(xs), "2784 rows replay M=%d seed %d" % (M, seed))
-        assert_matches_oracle(outs, xn, ws, label="2784 rows replay M=%d" % M)
+        assert_bitwise_equal(outs, fp(xs), "%s replay M=%d seed %d" % (case, M, seed))
+        assert_matches_oracle(outs, xn, ws, label="%s replay M=%d" % (case, M))
 
 
 # ---- plans past one round of small-M or tile workgroups: the ring tile
@@ -536,7 +548,7 @@ def test_page_fused_a_indexer_shape_graph_replay(M):
 def test_three_way_defaults_above_eight_tokens(M):
     x, ws = si.make_case(6144, (2048, 576, 128), "bf16", M, seed=90 + M)
     fp = _plan(ws, max_M=M)
-    assert fp.query(M)[0] == P.FP_PATH_MFMA
+    assert fp.query(M)[0] == (P.FP_PATH_MFMA_SMALL if M <= 16 else P.FP_PATH_MFMA)
     _check_case(fp, x, ws, "three-way default M=%d" % M)
 
 
