@@ -111,7 +111,7 @@ def kernel_name(P, M: int, tiling) -> str:
         # token halves; with two, up to 12 tokens the interleaved load order;
         # row tiles per wave (rows above 8: two tiles of rows / 2)
         return "fp::smfma_kernel<%d, false, %d, %s, %d>" % (
-            chunks, 1 if M <= 8 else 2, "false" if 8 < M <= 12 else "true",
+            chunks, 1 if M <= 8 else 2 if M <= 16 else 3, "false" if 8 < M <= 12 else "true",
             2 if rows > 8 else 1)
     mt16 = next(b for b in (1, 2, 4, 8, 16) if 16 * b >= M)
     cs = 4 if chunks in (8, 16) else 5
@@ -567,7 +567,7 @@ def crossover(prefix, P, torch, dev, workload="wq_a+wkv", pool_mib=1024):
         cands = [("default", None)]
         if M <= 8:
             cands.append(("vector ALU", (P.FP_PATH_SKINNY, min(16, -(-kc // 64)), 1, 1, 0, 0)))
-        if M <= 16:
+        if M <= 24:
             cands.append(("small-M MFMA", (P.FP_PATH_MFMA_SMALL, pk, kt, 1, 0, 0)))
             for label, r, g in small_rows:
                 cands.append(("small-M MFMA, " + label, (P.FP_PATH_MFMA_SMALL, pk, kt, 1, r, g)))
@@ -829,8 +829,8 @@ def main():
                     help="only the warm-up and timed steps of the fused graphs (profiler runs: "
                          "every dispatch is a graph replay of the timed step)")
     ap.add_argument("--mfma-only", action="store_true",
-                    help="time only the matrix-core cells (M = 8..16 on the small-M kernel, "
-                         "17..128 on the tile kernels) and print them (profiler runs of the "
+                    help="time only the matrix-core cells (M = 8..24 on the small-M kernel, "
+                         "32..128 on the tile kernels) and print them (profiler runs of the "
                          "MFMA and HBM counters); not the benchmark line")
     ap.add_argument("--pool-sweep", default="",
                     help="write a pool-size sweep (per-call time vs rotated pool size) to "
@@ -859,7 +859,7 @@ def main():
         n_copies = max(2, math.ceil((args.pool_mib << 20) / w_bytes))
         plans = build_pool(P, torch, n_copies, 128)
         res = {}
-        for M in (8, 9, 16, 17, 32, 48, 64, 96, 128):
+        for M in (8, 9, 16, 17, 24, 32, 48, 64, 96, 128):
             x = si2.make_case(K, N, "bf16", M, seed=800 + M)[0].to(dev)
             out = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in N]
             gr = capture(torch, lambda: [p.forward(x, out=out) for p in plans])

@@ -35,11 +35,15 @@ namespace {
 constexpr uint64_t kPlanMagic = 0x66757365'6470726full;  // "fusedpro"
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kSkinnyMaxM = 8;      // largest M the skinny kernel serves
-constexpr int kSmallMfmaMaxM = 16;  // largest M the small-M matrix-core kernel serves
-// Crossover to the tile kernel (smallest M on the MFMA tile path), measured
-// on MI355X at K = 5120, 1792 rows: the small-M matrix-core kernel with two
-// token halves serves M = 9..16 faster than the tile kernel.
-constexpr int kDefaultMfmaMinM = 17;
+// Largest M the small-M matrix-core kernel serves: three token halves for
+// bf16, two for block-scaled weights.
+constexpr int kSmallMfmaMaxM = 24;
+constexpr int kSmallMfmaMaxMMx = 16;
+// Crossover to the tile kernels (smallest M on the MFMA tile path),
+// measured on MI355X at K = 5120, 1792 rows: the small-M matrix-core
+// kernel with two token halves serves M = 9..16 and with three halves M =
+// 17..24 faster than the tile kernels.
+constexpr int kDefaultMfmaMinM = 25;
 // Smallest M the small-M matrix-core kernel serves by default; the
 // vector-ALU kernel runs below it.  Measured on MI355X at K = 5120, 1792
 // rows (bf16): the vector-ALU kernel is faster up to M = 2 (5.22 vs 5.41
@@ -416,6 +420,9 @@ void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs, int var)
   t->groups = best_g;
 }
 
+// Token slots of the small-M kernel: one, two or three halves of 8.
+int smfma_mt(int64_t M) { return M > 16 ? 24 : M > 8 ? 16 : 8; }
+
 // Small-M kernel rows: `rows` 1..8 is one tile of that many rows per wave;
 // an even 10..16 is two tiles of rows / 2 (bf16, not gate/up) that share
 // each wave's activation operand.
@@ -456,7 +463,7 @@ bool resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs, bool bf16) {
   int64_t best_cost = INT64_MAX;
   const int mh = t->mt / 8;
   for (int tt = 1; tt <= 2; ++tt) {
-    if (tt == 2 && (!bf16 || pairs)) continue;
+    if (tt == 2 && (!bf16 || pairs || mh > 2)) continue;
     for (int rt = pairs ? 2 : 1; rt <= 8; rt += pairs ? 2 : 1) {
       if (tt == 2 && rt < 5) continue;  // rows <= 8 denote one tile
       const int rows = tt * rt;
@@ -470,6 +477,7 @@ bool resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs, bool bf16) {
         const int64_t R = (int64_t)rows * g;
         const int64_t nb = ceil_div(n_rows, R);
         const int waves = g * t->kparts;
+        if (waves * 64 > fp::smfma_max_threads(t->chunks, mh, tt)) continue;
         // block-scaled kernels: 32 waves per CU assumed, as measured for
         // their rows choice
         const int cu_waves = bf16 ? smfma_cu_waves(t->chunks, mh, tt) : 32;
@@ -594,6 +602,8 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
   } else if (t.path == FP_PATH_MFMA_SMALL) {
     if (!(p->dtype == FP_BF16 || is_mx(p->dtype))) return false;
     if (M > kSmallMfmaMaxM || t.mt < M) return false;
+    if (is_mx(p->dtype) && (M > kSmallMfmaMaxMMx || t.mt > 16)) return false;
+    if (t.rows > 8 && t.mt > 16) return false;  // two tiles: at most two halves
     if (!(t.chunks == 4 || t.chunks == 8 || t.chunks == 16)) return false;
     if (t.splits != 1 || t.kparts > fp::kMaxWaveParts || t.rows > 16 || t.groups < 1) return false;
     if (t.rows > 8 && (t.rows % 2 != 0 || p->dtype != FP_BF16)) return false;
@@ -665,7 +675,7 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
                  default_smfma_order(p->kc, t);
     if (small) {
       Tiling probe = *t;
-      probe.mt = M > 8 ? 16 : 8;
+      probe.mt = smfma_mt(M);
       const bool one_round = resolve_smfma_rows(p->n_total, &probe, pairs,
                                                 p->dtype == FP_BF16);
       const bool fits = (int64_t)probe.groups * probe.kparts * 64 <=
@@ -696,7 +706,7 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
     if (t->splits < 1) return false;
     resolve_tile_launch(p, n_rows, t);
   } else if (t->path == FP_PATH_MFMA_SMALL) {
-    t->mt = M > 8 ? 16 : 8;  // one or two token halves
+    t->mt = smfma_mt(M);
     if (t->kparts < 1 || t->chunks < 1) return false;
     resolve_smfma_rows(n_rows, t, pairs, p->dtype == FP_BF16);
   } else {

@@ -13,7 +13,7 @@ constexpr int kSmfmaInterleaveMaxM = 12;
 template <int KT>
 const void* smfma_kt(bool pairs, int mt, int64_t M, int tt) {
   if (tt == 2) {
-    if (pairs) return nullptr;
+    if (pairs || mt > 16) return nullptr;
     if (mt == 16)
       return M <= kSmfmaInterleaveMaxM
                  ? reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 2, false, 2>)
@@ -21,6 +21,8 @@ const void* smfma_kt(bool pairs, int mt, int64_t M, int tt) {
     return reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 1, true, 2>);
   }
   if (tt != 1) return nullptr;
+  if (mt == 24)
+    return pairs ? nullptr : reinterpret_cast<const void*>(&fp::smfma_kernel<KT, false, 3>);
   if (mt == 16) {
     if (pairs) return nullptr;
     return M <= kSmfmaInterleaveMaxM

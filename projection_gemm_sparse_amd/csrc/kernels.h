@@ -20,9 +20,10 @@ const void* skinny_f32out(int mt, int cj, int rw);
 // Block-scaled weights: var = fp::kVarMx8, kVarMx4 or kVarNv4.
 const void* skinny_mx(int var, int mt, int cj, int rw);
 
-// Small-M matrix-core kernel (smfma.hpp): KT steps per wave; mt 8 (one
-// token half) or 16 (two); pairs = gate/up SwiGLU form; M picks the load
-// order of the two-half forms; tt row tiles per wave (2: not gate/up).
+// Small-M matrix-core kernel (smfma.hpp): KT steps per wave; mt 8, 16 or
+// 24 (one to three token halves); pairs = gate/up SwiGLU form; M picks the
+// load order of the two-half forms; tt row tiles per wave (2: not gate/up,
+// at most two halves).
 const void* smfma(int kt, bool pairs, int mt, int64_t M, int tt = 1);
 // Block-scaled weights on the small-M matrix-core kernel: dtype FP_MXFP8,
 // FP_MXFP4 or FP_NVFP4; mh token halves (1 or 2).

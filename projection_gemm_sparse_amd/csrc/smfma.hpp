@@ -31,10 +31,11 @@
 // quarter-wave on two rows (2 x 128 contiguous bytes) and a four-dword
 // lane shuffle (ds_bpermute) moves each chunk to its MFMA lane.
 //
-// Nine to sixteen tokens (MH = 2 token halves): every step multiplies the
-// same A operand with the B operands of tokens 0..7 and 8..15 (two MFMAs,
-// two accumulators); the weights are still loaded once.  Per token the
-// arithmetic, hence the result, is the same as with one half.
+// Nine to sixteen tokens (MH = 2 token halves; 17..24: MH = 3): every step
+// multiplies the same A operand with the B operands of tokens 0..7, 8..15
+// (and 16..23) -- one MFMA and one accumulator per half; the weights are
+// still loaded once.  Per token the arithmetic, hence the result, is the
+// same as with one half.
 //
 // Work split.  A workgroup owns G row groups of TT tiles of RT <= 8 rows (a
 // tile with RT < 8 leaves its last A rows unused; the 1792-row fused launch
@@ -67,12 +68,13 @@ constexpr int kFmtNv4 = 5;  // the NVFP4 form of smfma_mx_kernel
 
 // Per-lane register estimate: the KT steps' 16-byte chunks of every tile's
 // weights and every half's activations, plus addresses and accumulators.
-// The two-tile two-half form is counted as compiled (144-152 VGPRs on
-// gfx950 at KT = 8, so that 12 waves fit a CU); the other forms keep the
-// estimate they were tuned with.
+// Forms of four or more operand sets (two tiles with two halves, three
+// halves) are counted as compiled (144-152 VGPRs on gfx950 at KT = 8, so
+// that 12 waves fit a CU); the others keep the estimate they were tuned
+// with.
 constexpr int smfma_regs(int kt, int mh, int tt) {
-  return tt == 2 && mh == 2 ? 4 * kt * 4 + 40
-                            : 4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1);
+  return mh + tt >= 4 ? 4 * kt * (mh + tt) + 24
+                      : 4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1);
 }
 
 constexpr int smfma_max_threads(int kt, int mh = 1, int tt = 1) {
@@ -114,9 +116,9 @@ __device__ __forceinline__ void smfma_store_outputs(const float* smem, int Gv, i
 // y1, ldx, n_rows, kc, M, split); geo = RT | PK << 8 | G << 16.
 // PAIRS: a gate/up launch (rows taken in pairs, see pair_row; RT even)
 // that writes silu(gate) * up instead of the projections.  MH: token halves
-// (1: M <= 8, 2: M <= 16).  XFIRST (two halves): every activation load
-// before the weights (the fuller second halves) instead of each step's
-// first-half, weight and second-half chunks in turn.  TT: row tiles per
+// (1: M <= 8, 2: M <= 16, 3: M <= 24).  XFIRST (two or more halves): every
+// activation load before the weights (the fuller later halves) instead of
+// each step's first-half, weight and later-half chunks in turn.  TT: row tiles per
 // wave (2: not gate/up); tile j of row group g2 holds rows
 // row_base + (g2 TT + j) RT ...
 template <int KT, bool PAIRS = false, int MH = 1, bool XFIRST = true, int TT = 1>
@@ -124,7 +126,7 @@ __global__ void __launch_bounds__(smfma_max_threads(KT, MH, TT))
 smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
              unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows,
              int32_t kc, int32_t M, int32_t split, int32_t geo, const Tail a) {
-  static_assert(MH == 1 || (MH == 2 && !PAIRS), "token halves");
+  static_assert(MH == 1 || ((MH == 2 || MH == 3) && !PAIRS), "token halves");
   static_assert(TT == 1 || (TT == 2 && !PAIRS), "two tiles: not gate/up");
   extern __shared__ float smem[];  // [G][TT][MH][16 wave parts][2][8][8]
   const int tid = threadIdx.x;
@@ -213,7 +215,8 @@ smfma_kernel(const unsigned char* __restrict__ w, const unsigned char* __restric
         xv[0][t] = xrow[0][cc];
 #pragma unroll
         for (int j = 0; j < TT; ++j) wv[j][t] = __builtin_nontemporal_load(wrows[j] + cc);
-        xv[MH - 1][t] = xrow[MH - 1][cc];
+#pragma unroll
+        for (int h = 1; h < MH; ++h) xv[h][t] = xrow[h][cc];
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {

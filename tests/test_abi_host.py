@@ -163,7 +163,7 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
             n_steps = -(-kc // 4)
             assert -(-n_steps // S) <= ch
         elif path == P.FP_PATH_MFMA_SMALL:
-            assert dtype == 0 and 3 <= M <= 16
+            assert dtype == 0 and 3 <= M <= 24
             assert S == 1 and kp <= 16 and kp * ch * 8 >= kc
             # rows per row group: one tile of 1..8 rows, or two tiles of
             # rows / 2 sharing the activations
@@ -181,7 +181,8 @@ def test_default_tiling_covers_k_and_fits_workspace(dtype, K, N):
 
 def test_default_crossover():
     # bf16: vector-ALU kernel up to M = 2, small-M matrix-core kernel for
-    # M = 3..16 (one token half up to 8, two above), tile kernels above;
+    # M = 3..24 (one token half up to 8, two to 16, three above), tile
+    # kernels above;
     # fp32: vector-ALU kernel (M <= 8)
     for M in range(1, 3):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_SKINNY
@@ -189,7 +190,11 @@ def test_default_crossover():
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA_SMALL
     for M in range(1, 9):
         assert P.fp_default_tiling(1, 7168, 192, M, 192)[1][0] in (1, 2)
-    for M in (17, 32, 64, 128):
+    # three token halves through M = 24, the tile kernels above
+    for M in (17, 20, 24):
+        st, t = P.fp_default_tiling(0, 5120, 1792, M, 1792)
+        assert t[0] == P.FP_PATH_MFMA_SMALL and t[4] == 7
+    for M in (25, 32, 64, 128):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][0] == P.FP_PATH_MFMA
     # more rows than one 8-row tile per CU (the three-way fused-A shape):
     # the vector-ALU kernel through M = 4, the small-M kernel with two row

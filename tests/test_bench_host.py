@@ -21,6 +21,8 @@ def test_kernel_names_of_the_default_tilings():
         assert bench.kernel_name(P, M, small) == "fp::smfma_kernel<8, false, 2, false, 1>"
     for M in range(13, 17):
         assert bench.kernel_name(P, M, small) == "fp::smfma_kernel<8, false, 2, true, 1>"
+    for M in range(17, 25):
+        assert bench.kernel_name(P, M, small) == "fp::smfma_kernel<8, false, 3, true, 1>"
     # two row tiles of 6 per wave (plans of more rows than 8 per CU)
     two = (P.FP_PATH_MFMA_SMALL, 12, 8, 1, 12, 1)
     assert bench.kernel_name(P, 8, two) == "fp::smfma_kernel<8, false, 1, true, 2>"

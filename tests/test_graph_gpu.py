@@ -62,7 +62,8 @@ def test_replay_bitwise_equal_to_eager(name, M):
         assert_matches_oracle(outs, xn, ws, rows=rows, label="%s replay" % name)
 
 
-@pytest.mark.parametrize("name,M", [("wq_a+wkv_m1", 1), ("indexer_f32", 8), ("crossover", 16)])
+@pytest.mark.parametrize("name,M", [("wq_a+wkv_m1", 1), ("indexer_f32", 8), ("crossover", 16),
+                                    ("crossover", 20)])
 def test_replay_stress_with_positive_control(name, M):
     x0, ws = si.workload_case(name, M, 0)
     fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=max(8, M))

@@ -91,7 +91,7 @@ def test_fused_a_three_way(M):
 
 # ---- crossover sweep, strided x (row stride K + 64); sampled token rows
 #      for large M (the oracle's cost grows with M; rows are independent)
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 9, 16, 32, 64, 128])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 9, 16, 17, 24, 32, 64, 128])
 def test_crossover_sweep_strided_x(M):
     K = 5120
     x_full, ws = si.workload_case("crossover", M, 0, ldx=K + 64)
@@ -155,10 +155,10 @@ def test_integer_data_bit_exact(dt, K, N, M):
 
 
 # ---- every tiling the kernels accept passes; fused == separate under each
-@pytest.mark.parametrize("M", [1, 4, 8, 16])
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 24])
 def test_tilings_all_pass(M):
     x, ws = si.workload_case("crossover", M, 3)
-    fp = _plan(ws, max_M=16, workspace_bytes=64 << 20)
+    fp = _plan(ws, max_M=24, workspace_bytes=64 << 20)
     xg = to_gpu(x)
     tilings = [
         (P.FP_PATH_SKINNY, 10, 1, 1, 0, 0),
@@ -188,16 +188,18 @@ def test_tilings_all_pass(M):
     for t in tilings:
         st = fp.set_tiling(M, t)
         if st != P.FP_OK:
-            # skinny tilings above M = 8, tile tilings at M <= 8 and
-            # small-M MFMA workgroups above the register bound of two token
-            # halves are refused
+            # skinny tilings above M = 8, tile tilings at M <= 8 (and above
+            # 16 tokens where their slice of 32 token rows exceeds LDS) and
+            # small-M MFMA workgroups above the register bound of their
+            # token halves are refused
             assert st == P.FP_ERR_UNSUPPORTED, (t, st)
             assert ((t[0] in (P.FP_PATH_SKINNY, P.FP_PATH_SKINNY_SPLITK)
                      and (M > 8 or (t[2] > 2 and M > 2)))
-                    or (t[0] == P.FP_PATH_MFMA and M <= 8)
+                    or (t[0] == P.FP_PATH_MFMA and (M <= 8 or (M > 16 and t[2] >= 20)))
                     or (t[0] == P.FP_PATH_MFMA_SMALL and M > 8
-                        and max(1, t[5]) * t[1] * 64 >
-                        _smfma_thread_cap(t[2], 2, 2 if t[4] > 8 else 1))), (t, st)
+                        and (max(1, t[5]) * t[1] * 64 >
+                             _smfma_thread_cap(t[2], 3 if M > 16 else 2, 2 if t[4] > 8 else 1)
+                             or (M > 16 and t[4] > 8)))), (t, st)
             continue
         ran += 1
         ys = fp(xg)
@@ -266,8 +268,8 @@ def test_single_row_projections_and_one_projection():
 def _smfma_thread_cap(kt, mh, tt=1):
     """Largest workgroup of the small-M matrix-core kernel: its register
     estimate per lane (tt row tiles per wave), 4 waves per SIMD at most."""
-    if tt == 2 and mh == 2:
-        regs = 4 * kt * 4 + 40
+    if mh + tt >= 4:
+        regs = 4 * kt * (mh + tt) + 24
     else:
         regs = 4 * kt * (mh + tt) + 24 + 16 * (mh - 1) + 4 * (tt - 1)
     return 256 * max(1, min(4, 512 // regs))
@@ -281,7 +283,7 @@ def _small_mfma_tiling(K, esize=2):
 
 
 @pytest.mark.parametrize("case", ["wq_a+wkv", "fused_a_3way", "ragged", "single_rows", "k8"])
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 12, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 12, 16, 17, 20, 24])
 def test_small_mfma_path(case, M):
     if case == "wq_a+wkv":
         x, ws = si.workload_case("wq_a+wkv_m2_8", M, 1)
@@ -293,7 +295,7 @@ def test_small_mfma_path(case, M):
         x, ws = si.make_case(1024, (1,) * 16, "bf16", M, seed=61 + M)
     else:
         x, ws = si.make_case(8, (300, 29), "bf16", M, seed=62 + M)
-    fp = _plan(ws, max_M=16)
+    fp = _plan(ws, max_M=24)
     assert fp.set_tiling(M, _small_mfma_tiling(fp.K)) == P.FP_OK
     assert fp.query(M)[0] == P.FP_PATH_MFMA_SMALL
     _check_case(fp, x, ws, "small-M MFMA %s M=%d" % (case, M))
