@@ -72,8 +72,8 @@ def test_plans_of_different_rows_share_the_scratch():
     xb0, wsb = si.workload_case("crossover", 32, 0)
     fa = P.FusedProjection([to_gpu(w) for w in wsa], max_M=32)
     fb = P.FusedProjection([to_gpu(w) for w in wsb], max_M=32)
-    assert fa.get_tiling(32)[3] > 1 and fb.get_tiling(24)[3] > 1
-    for fp, ws, name, M in ((fa, wsa, "fused_a_3way", 32), (fb, wsb, "crossover", 24),
+    assert fa.get_tiling(32)[3] > 1 and fb.get_tiling(32)[3] > 1 and fa.get_tiling(17)[3] > 1
+    for fp, ws, name, M in ((fa, wsa, "fused_a_3way", 32), (fb, wsb, "crossover", 32),
                             (fa, wsa, "fused_a_3way", 17)):
         xc, _ = si.workload_case(name, M, 90 + M)
         ya, yb = _calls(fp, to_gpu(xc), M)
