@@ -104,12 +104,16 @@ typedef enum {
   FP_PATH_SKINNY_SPLITK = 2, /* same kernel with the K contraction split
                               across workgroups and a fixed-order finish
                               inside the same launch */
-  FP_PATH_MFMA = 3,        /* MFMA tile kernels (bf16, M above the crossover):
-                              the tile kernel (whole K slice in LDS) up to
-                              32 tokens, the ring tile kernel (K slice
-                              streamed through a ring of LDS stages) from 33 */
-  FP_PATH_MFMA_SMALL = 4   /* matrix-core kernel for few tokens (M <= 16):
-                              8-row x 2-sub-slice tiles, one launch */
+  FP_PATH_MFMA = 3,        /* MFMA tile kernels (bf16, M above the crossover,
+                              or plans the small-M kernel cannot cover in
+                              one round): the tile and weight-resident
+                              kernels (K slice in LDS) to 32 tokens and for
+                              65..128, the ring tile kernel (K slice streamed
+                              through a ring of LDS stages) for 33..64,
+                              above 128 and on large plans */
+  FP_PATH_MFMA_SMALL = 4   /* matrix-core kernel for few tokens (bf16 M <= 24,
+                              block-scaled M <= 16): 8-row x 2-sub-slice
+                              tiles, one or two per wave, one launch */
 } fp_path;
 
 #define FP_MAX_PROJ 16     /* projections per plan */
@@ -343,7 +347,8 @@ fp_status fp_plan_set_mfma_min_m(fp_plan_t plan, int64_t min_m);
  * so fused and separate calls of one plan stay bitwise equal under any
  * tiling.
  *   path    FP_PATH_SKINNY / FP_PATH_SKINNY_SPLITK (same kernel; the
- *           splits field decides), FP_PATH_MFMA_SMALL (M <= 16) or
+ *           splits field decides), FP_PATH_MFMA_SMALL (M <= 24; block-
+ *           scaled weights M <= 16) or
  *           FP_PATH_MFMA (the tile kernels, bf16)
  *   kparts  skinny: waves splitting one K slice (P, <= 16); mfma-small:
  *           waves splitting K (PK, <= 16); mfma: 16-row tiles per
