@@ -80,8 +80,9 @@ def load_back_to_back(d, gap_ns=1000):
     (graph replays of back-to-back calls, not eager launches from the host):
     {kernel: (count, average duration ns)}."""
     acc = {}
-    for path in glob.glob(os.path.join(d, "*kernel_trace.csv")):
-        with open(path) as fh:
+    for path in (glob.glob(os.path.join(d, "*kernel_trace.csv")) +
+                 glob.glob(os.path.join(d, "*kernel_trace.csv.gz"))):
+        with _open_csv(path) as fh:
             rows = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Queue_Id"],
                      _short(r["Kernel_Name"])) for r in csv.DictReader(fh)]
         rows.sort()
@@ -93,6 +94,19 @@ def load_back_to_back(d, gap_ns=1000):
                 acc[k] = (n + 1, tot + (en - st))
             last_end[q] = en
     return {k: (n, tot / n) for k, (n, tot) in acc.items()}
+
+
+def back_to_back_runs(dirs, gap_ns=1000):
+    """load_back_to_back over repeated runs of one command (one directory
+    each): {kernel: (median over the runs of the run's average, [each run's
+    average])}.  The profiler spaces graph-replayed dispatches unevenly and
+    differently from box to box, so one run's average is a noisy figure;
+    the median of several independent runs is the one recorded."""
+    per = {}
+    for d in dirs:
+        for k, (n, avg) in load_back_to_back(d, gap_ns).items():
+            per.setdefault(k, []).append(avg)
+    return {k: (statistics.median(v), v) for k, v in per.items()}
 
 
 def med(vals):
@@ -114,12 +128,12 @@ def hbm_bytes(c):
 
 def trace_only(args):
     """Markdown table of the library's kernels in one kernel-trace run."""
-    rows = [r for r in load_stats(args.trace)
+    rows = [r for r in load_stats(args.trace[0])
             if r["kernel"].startswith("void fp::") or r["kernel"].startswith("fp::")]
     lines = ["# %s" % (args.title or "Kernel trace"), "",
              "Command (run from /tmp with TMPDIR=/tmp, repository root $R):", "", "```"]
     lines += args.command + ["```", ""]
-    b2b = load_back_to_back(args.trace)
+    b2b = load_back_to_back(args.trace[0])
     lines += ["Back-to-back: the dispatches that started within 1 us of the previous one's "
               "end on the same queue (graph replays of consecutive calls; the trace's "
               "durations then tile the timeline, launch gaps included).", ""]
@@ -146,7 +160,7 @@ def mfma_summary(args):
     summed over the XCDs; it is listed as read."""
     simds, ghz, peak = args.simds, args.clock_ghz, args.peak_tflops
     pmc = load_pmc(args.pmc)
-    stats = {r["kernel"]: r for r in load_stats(args.trace)} if args.trace else {}
+    stats = {r["kernel"]: r for r in load_stats(args.trace[0])} if args.trace else {}
     lines = ["# %s" % (args.title or "Matrix-core utilisation"), "",
              "Commands (run from /tmp with TMPDIR=/tmp, repository root $R):", "", "```"]
     lines += args.command + ["```", ""]
@@ -187,7 +201,9 @@ def mfma_summary(args):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--trace", default="")
+    ap.add_argument("--trace", nargs="+", default=[],
+                    help="kernel-trace run directories (repeated runs of one command: the "
+                         "median of their back-to-back averages is recorded)")
     ap.add_argument("--trace-only", action="store_true",
                     help="only summarise the kernel trace (no counters)")
     ap.add_argument("--mfma", action="store_true",
@@ -233,8 +249,8 @@ def main():
     f_fetch = (med(calib.get("FETCH_SIZE", [])) or 0) * 1024 / args.calib_bytes or None
     f_write = (med(calib.get("WRITE_SIZE", [])) or 0) * 1024 / args.calib_bytes or None
 
-    stats = {r["kernel"]: r for r in load_stats(args.trace)}
-    b2b = load_back_to_back(args.trace)
+    stats = {r["kernel"]: r for r in load_stats(args.trace[0])}
+    b2b = back_to_back_runs(args.trace)
     lines = ["# %s" % (args.title or "Fused projection kernels: duration and HBM traffic"), "",
              "Commands (run from /tmp with TMPDIR=/tmp, repository root $R):", "", "```"]
     lines += args.command + ["```", ""]
@@ -246,13 +262,17 @@ def main():
                   None if f_wr is None else round(f_wr, 4),
                   None if f_fetch is None else round(f_fetch, 4),
                   None if f_write is None else round(f_write, 4)), ""]
+    if len(args.trace) > 1:
+        lines += ["The kernel-trace command ran %d times, each in a separate GPU session; "
+                  "avg ns (back-to-back) is the median over those runs of each run's "
+                  "average, every run's average listed beside it." % len(args.trace), ""]
     lines += ["avg ns (back-to-back): the kernel-trace average over the dispatches that "
               "started within 1 us of the previous one's end (graph replays of consecutive "
-              "calls); avg ns (all) includes eager launches.", ""]
-    lines += ["| kernel | grid | calls | avg ns (all) | avg ns (back-to-back) | min ns | "
-              "HBM read B/launch | HBM write B/launch | FETCH_SIZE B (scaled) | "
+              "calls); avg ns (all) includes eager launches (first run).", ""]
+    lines += ["| kernel | grid | calls | avg ns (all) | avg ns (back-to-back) | per run | "
+              "min ns | HBM read B/launch | HBM write B/launch | FETCH_SIZE B (scaled) | "
               "WRITE_SIZE B (scaled) |",
-              "|---|---|---|---|---|---|---|---|---|---|"]
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
     rec = {"kernel_sources_sha256_16": bench.kernel_sources_digest(), "kernels": {},
            "calibration": {"bytes": args.calib_bytes, "read_factor": f_rd, "write_factor": f_wr}}
     for (k, grid), c in sorted(pmc.items()):
@@ -267,10 +287,11 @@ def main():
         fs = fs * 1024 / f_fetch if (fs is not None and f_fetch) else None
         ws = ws * 1024 / f_write if (ws is not None and f_write) else None
         st = stats.get(k) or stats.get(name) or {}
-        bb = (b2b.get(k) or b2b.get(name) or (0, None))[1]
-        lines.append("| `%s` | %d | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+        bb, runs = b2b.get(k) or b2b.get(name) or (None, [])
+        lines.append("| `%s` | %d | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
             name, grid, st.get("calls", ""), st.get("avg_ns", ""),
-            "" if bb is None else round(bb, 1), st.get("min_ns", ""),
+            "" if bb is None else round(bb, 1), ", ".join("%.1f" % v for v in runs),
+            st.get("min_ns", ""),
             None if rd is None else round(rd), None if wr is None else round(wr),
             None if fs is None else round(fs), None if ws is None else round(ws)))
         if rd is not None and wr is not None:
@@ -278,6 +299,7 @@ def main():
                                     "hbm_write_bytes_per_launch": round(wr),
                                     "hbm_bytes_per_launch": round(rd + wr),
                                     "trace_avg_ns": None if bb is None else round(bb, 1),
+                                    "trace_avg_ns_runs": [round(v, 1) for v in runs],
                                     "trace_avg_ns_all": st.get("avg_ns")}
     with open(args.out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")

@@ -61,3 +61,26 @@ def test_algorithmic_bytes_of_the_headline_call():
     assert bench.algorithmic_bytes(1, 5120, (1280, 512)) == 2 * (1792 * 5120 + 5120 + 1792)
     assert bench.algorithmic_bytes(8, 5120, (1280, 512)) == 18350080 + 2 * 8 * (5120 + 1792)
     assert bench.algorithmic_bytes(1, 7168, (128, 64), esize=4) == 4 * (192 * 7168 + 7168 + 192)
+
+
+def test_trace_runs_record_the_median_of_each_runs_back_to_back_average(tmp_path):
+    from projection_gemm_sparse_amd import counters
+    head = "Kind,Queue_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n"
+
+    def run(name, durations, gap=100):
+        d = tmp_path / name
+        d.mkdir()
+        t, lines = 0, []
+        for du in durations:
+            lines.append("KERNEL_DISPATCH,1,fp::k(int),%d,%d" % (t, t + du))
+            t += du + gap
+        # an eager launch far from the previous end: not back-to-back
+        lines.append("KERNEL_DISPATCH,1,fp::k(int),%d,%d" % (t + 50000, t + 59000))
+        (d / "bench_kernel_trace.csv").write_text(head + "\n".join(lines) + "\n")
+        return str(d)
+
+    dirs = [run("a", [100, 100, 100]), run("b", [300, 300, 300]), run("c", [200, 220, 180])]
+    one = counters.load_back_to_back(dirs[0])
+    assert one["fp::k"] == (2, 100.0)  # the first dispatch has no predecessor
+    med, per = counters.back_to_back_runs(dirs)["fp::k"]
+    assert per == [100.0, 300.0, 200.0] and med == 200.0
