@@ -53,10 +53,13 @@ constexpr int kWresStageSlots = 512;   // 64 rows x 8 pieces
 // for 32 tokens).
 __host__ __device__ constexpr int wres_producers(int bm) { return bm <= 64 ? 1 : bm / 64; }
 __host__ __device__ constexpr int wres_threads(int bm) { return 64 * (4 + wres_producers(bm)); }
-// Ring depth and the most stages a slice may span (its weight slice fills
-// LDS beside the ring): 160 KiB for every token block.
+// Ring depth and the most stages a slice may span (its weight slice sits in
+// LDS beside the ring; the two stay within 160 KiB).  Four stages of
+// activations ahead are enough: the ring refills from L2, and a deeper ring
+// measured slower (more producer loads queued in front of the weights'
+// first stages).
 __host__ __device__ constexpr int wres_ring(int bm) {
-  return bm <= 32 ? 8 : bm <= 64 ? 6 : bm <= 128 ? 4 : 3;
+  return bm <= 64 ? 4 : 3;
 }
 __host__ __device__ constexpr int wres_max_stages(int bm) {
   return bm <= 32 ? 16 : bm <= 64 ? 14 : bm <= 128 ? 12 : 8;
