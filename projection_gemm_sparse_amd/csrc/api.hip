@@ -539,9 +539,9 @@ void resolve_tile_launch(const fp_plan_s* p, int64_t n_rows, Tiling* t) {
 // Partial-sum floats a tiling needs for a launch of n_rows rows and M tokens.
 int64_t partial_floats(const Tiling& t, int64_t n_rows, int64_t M) {
   if (t.splits <= 1) return 0;
-  // the tile kernel keeps 16-token-aligned partial rows
-  const int64_t mcols = t.path == FP_PATH_MFMA ? 16 * (int64_t)mfma_mt16(M) : M;
-  return (int64_t)t.splits * n_rows * mcols;
+  // the tile kernels keep token-major slices with a 4-row pitch
+  if (t.path == FP_PATH_MFMA) return (int64_t)t.splits * M * fp::tile_partial_pitch((int)n_rows);
+  return (int64_t)t.splits * n_rows * M;
 }
 
 // Where a launch keeps its split-K state: the arrival counters (one uint32
@@ -634,8 +634,11 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
   } else {
     return false;
   }
-  return counters_bytes(p->n_total) <= ws.counter_bytes &&
-         partial_floats(t, n_rows, M) * 4 <= ws.partial_bytes;
+  // the tile kernels' in-launch finish addresses the partials with 32-bit
+  // byte offsets
+  const int64_t pbytes = partial_floats(t, n_rows, M) * 4;
+  if (t.path == FP_PATH_MFMA && pbytes >= ((int64_t)1 << 32)) return false;
+  return counters_bytes(p->n_total) <= ws.counter_bytes && pbytes <= ws.partial_bytes;
 }
 
 // The tiling for (M, launch rows); the summation-order fields come from the
@@ -879,11 +882,10 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
     if (st != FP_OK || !second) return st;
     // the slices, added in slice order over the whole GPU
     const float* part_a = tail.partial;
-    int32_t mpad_a = 16 * t.mt;
     int32_t s_a = t.splits;
-    void* rargs[] = {&part_a, &n_rows_a, &M_a, &mpad_a, &s_a, &tail.out};
+    void* rargs[] = {&part_a, &n_rows_a, &M_a, &s_a, &tail.out};
     return launch(fpk::splitk_reduce(),
-                  ceil_div((int64_t)lr.n_rows * ceil_div(M, 4), 256), 256, 0, rargs, stream);
+                  ceil_div(M * ceil_div(lr.n_rows, 4), 256), 256, 0, rargs, stream);
   }
   geo_a = t.kparts | (t.groups << 8) | (t.splits << 16);
   const int64_t R = (int64_t)t.groups * t.rows;

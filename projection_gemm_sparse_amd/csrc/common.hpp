@@ -41,7 +41,7 @@ struct OutTable {
 // with more than two segments, and the split-K workspace.
 struct Tail {
   OutTable out;
-  float* partial;      // [S][n_rows][M] when S > 1
+  float* partial;      // S > 1: [S][n_rows][M] (vector-ALU), [S][M][n_rows rounded to 4] (tile kernels)
   uint32_t* counters;  // one per row block when S > 1, zero between calls
 };
 
@@ -214,6 +214,34 @@ __device__ __forceinline__ void store_y(const OutMap& o, const OutTable& tab, in
     __hip_atomic_store((g_f32*)(reinterpret_cast<float*>(y) + idx), v, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// bf16 outputs of four consecutive rows row .. row + 3 of token m (each
+// rounded once, as store_y): one 8-byte store where the four rows lie below
+// n_rows in one of the map's first two segments at an 8-byte aligned
+// address -- the outputs of one token are contiguous in its projection's
+// [M, N_i] tensor, so a wave's quads of consecutive rows write whole lines --
+// else one store_y per row below n_rows.
+__device__ __forceinline__ void store_y4(const OutMap& o, const OutTable& tab, int row, int m,
+                                         f32x4 v, int n_rows) {
+  typedef __attribute__((address_space(1))) uint64_t g_u64;
+  if (row + 3 < n_rows && row + 3 < o.e1 && (row + 3 < o.b1 || row >= o.b1)) {
+    const bool first = row < o.b1;
+    const int b = first ? o.b0 : o.b1;
+    const int n = first ? o.b1 - o.b0 : o.e1 - o.b1;
+    uint16_t* y = reinterpret_cast<uint16_t*>(first ? o.y0 : o.y1) + (m * n + (row - b));
+    if ((reinterpret_cast<uintptr_t>(y) & 7) == 0) {
+      const uint64_t q = (uint64_t)f32_to_bf16_rne(v[0]) |
+                         ((uint64_t)f32_to_bf16_rne(v[1]) << 16) |
+                         ((uint64_t)f32_to_bf16_rne(v[2]) << 32) |
+                         ((uint64_t)f32_to_bf16_rne(v[3]) << 48);
+      __hip_atomic_store((g_u64*)y, q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (row + j < n_rows) store_y<true>(o, tab, row + j, m, v[j]);
 }
 
 // Cross-wave sums in LDS.  A kernel whose waves split K writes the partial
@@ -437,7 +465,8 @@ __device__ __forceinline__ void transpose_reduce(float* v, int lane) {
 // Split-K partial sums and their finish inside the same launch.
 //
 // Each of the S workgroups of row block rb writes its fp32 partial sums to
-// partial[s][row][m] with agent-coherent stores (sc1: written through to the
+// partial[s][row][m] (the tile kernels: partial[s][m][row], see
+// splitk_finish_vec) with agent-coherent stores (sc1: written through to the
 // point of coherence shared by all XCDs instead of staying dirty in this
 // XCD's L2), waits until they are acknowledged, and then arrives on
 // counters[rb].  The workgroup that arrives last reads the S partials with

@@ -61,9 +61,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer resource, dword 3 (gfx9)
 constexpr uint32_t kOob = 0x80000000u;       // an offset past every buffer's end
 constexpr int kAuxNt = 2;                    // buffer cache policy: non-temporal
+constexpr int kAuxSc1 = 16;                  // buffer cache policy: sc1 (agent-coherent)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufFlags);
+}
+
+// Four consecutive partials of one token, element e of the token-major
+// partial buffer pr: one 16-byte store, agent-coherent (sc1) as
+// store_partial.
+__device__ __forceinline__ void store_partial4(__amdgpu_buffer_rsrc_t pr, uint32_t e, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), pr, e * 4u, 0, kAuxSc1);
 }
 
 // LDS layout of a tile launch, in 16-byte slots (host and device):
@@ -103,7 +111,7 @@ __device__ __forceinline__ f32x4 sum_slices_rsrc(__amdgpu_buffer_rsrc_t pr, uint
 #pragma unroll
     for (int j = 0; j < GRP; ++j) {
       const uint32_t o = s0 + j < S ? off + (uint32_t)(s0 + j) * sstride : kOob;
-      v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, 16));
+      v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, kAuxSc1));
     }
 #pragma unroll
     for (int j = 0; j < GRP; ++j) {
@@ -136,14 +144,19 @@ __device__ __forceinline__ f32x4 sum_slices_ptr(const f32x4* p, int64_t vstride,
   return sum;
 }
 
+// Split-K partials of the tile kernels are token-major: slice s, token m,
+// row r at partial[(s * M + m) * RP + r] with the row pitch RP = n_rows
+// rounded up to a multiple of 4 (16 bytes), so that a lane's four
+// accumulator rows of one token are one 16-byte run and a finish that takes
+// four consecutive rows per thread reads and writes whole lines.
+__host__ __device__ constexpr int tile_partial_pitch(int n_rows) { return (n_rows + 3) & ~3; }
+
 // Sum of the S partial slices of a row block, in slice order, by the
-// workgroup that arrives last; four consecutive token slots per thread and
-// step (partials are [S][n_rows][m_pad] fp32, m_pad a multiple of 16, stored
-// and read agent-coherent).
-template <bool BF16>
+// workgroup that arrives last; four consecutive rows of one token per
+// thread and step (stored and read agent-coherent).
 __device__ __forceinline__ void splitk_finish_vec(const float* partial, uint32_t* counters,
                                                   int rb, int S, int row_base, int R,
-                                                  int n_rows, int M, int m_pad, int nthreads,
+                                                  int n_rows, int M, int nthreads,
                                                   const OutMap& os, const OutTable& tab,
                                                   int* flag) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // this thread's partial stores are done
@@ -157,24 +170,20 @@ __device__ __forceinline__ void splitk_finish_vec(const float* partial, uint32_t
   __syncthreads();
   if (*flag == 0) return;
   const int rows_here = n_rows - row_base < R ? n_rows - row_base : R;
-  const int vec_per_row = (M + 3) >> 2;
-  const int n_vec = rows_here * vec_per_row;
-  const uint32_t sstride = (uint32_t)n_rows * (uint32_t)m_pad * 4u;
+  const int quads = (rows_here + 3) >> 2;
+  const int n_vec = M * quads;
+  const uint32_t rp = (uint32_t)tile_partial_pitch(n_rows);
+  const uint32_t sstride = (uint32_t)M * rp * 4u;
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(partial, (uint32_t)S * sstride);
   for (int t = threadIdx.x; t < n_vec; t += nthreads) {
-    const int rr = t / vec_per_row;
-    const int m0 = (t - rr * vec_per_row) * 4;
-    const int row = row_base + rr;
-    const uint32_t off = ((uint32_t)row * (uint32_t)m_pad + (uint32_t)m0) * 4u;
+    const int m = t / quads;
+    const int row = row_base + 4 * (t - m * quads);
+    const uint32_t off = ((uint32_t)m * rp + (uint32_t)row) * 4u;
     // the S slices in groups (8, or 16 above 8 slices): all loads of a
     // group are issued before the first add, then added in slice order
     const f32x4 sum = S <= 8 ? sum_slices_rsrc<8>(pr, off, sstride, S)
                              : sum_slices_rsrc<16>(pr, off, sstride, S);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float vj = sum[j];
-      if (m0 + j < M) store_y<BF16>(os, tab, row, m0 + j, vj);
-    }
+    store_y4(os, tab, row, m, sum, n_rows);
   }
   if (threadIdx.x == 0) {
     __hip_atomic_store((gu32*)(counters + rb * kTileCounterStride), 0u, __ATOMIC_RELAXED,
@@ -193,7 +202,6 @@ __global__ void __launch_bounds__(NW * 64)
 tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict__ x,
             unsigned char* y0, unsigned char* y1, uint32_t ldx, int32_t n_rows, int32_t kc,
             int32_t M, int32_t split, int32_t geo, const Tail a) {
-  constexpr int MP = 16 * MT16;  // token slots
   constexpr int NT = NW * 64;
   constexpr int WP = 4 * CS + 1;                     // weight row pitch (slots)
   constexpr int WCS = tile_w_chunk_slots(CS);        // slots of one wave chunk
@@ -309,65 +317,64 @@ tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict
     }
     return;
   }
+  const uint32_t rp = (uint32_t)tile_partial_pitch(n_rows);
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(partial, (uint32_t)S * (uint32_t)M * rp * 4u);
 #pragma unroll
   for (int mt = 0; mt < MT16; ++mt) {
     const int m = mt * 16 + i16;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = row_t + v;
-      const float val = acc[mt][v];
-      if (row < n_rows) store_partial(partial + ((int64_t)s * n_rows + row) * MP + m, val);
-    }
+    if (m < M && row_t < n_rows)
+      store_partial4(prs, ((uint32_t)s * (uint32_t)M + (uint32_t)m) * rp + (uint32_t)row_t,
+                     acc[mt]);
   }
   if (geo & kGeoSecondFinish) return;  // splitk_reduce_kernel adds the slices
   __syncthreads();  // every wave is done reading the activation slice
-  splitk_finish_vec<true>(partial, counters, rb, S, row_base, 16 * NW, n_rows, M, MP, NT, om,
-                          a.out, reinterpret_cast<int*>(lds_raw));
+  splitk_finish_vec(partial, counters, rb, S, row_base, 16 * NW, n_rows, M, NT, om, a.out,
+                    reinterpret_cast<int*>(lds_raw));
 }
 
 // The second-launch finish: defined only in the unit that compiles the non-template
 // kernels (k_misc.hip), so each is emitted once.
 #ifdef FP_DEFINE_MISC_KERNELS
-// The second-launch finish of a split tile launch: thread t adds, for launch
-// row t / ceil(M/4) and four consecutive tokens, the S slices of the
+// The second-launch finish of a split tile launch: thread t adds, for token
+// t / ceil(n_rows / 4) and four consecutive rows, the S slices of the
 // partials in slice order -- the order of splitk_finish_vec, so both
-// finishes give the same bits -- and stores the outputs rounded once.  A
+// finishes give the same bits -- and stores the outputs rounded once (a
+// wave's 64 threads read and write 256 consecutive rows of one token).  A
 // launch of many tokens has large partials per row block (S * 16 * NW rows
 // * 16 * MT16 tokens); one workgroup per row block re-reading them (the
 // in-launch finish) is then slower than spreading the sum over the whole
 // GPU after a kernel boundary.
 __global__ void __launch_bounds__(256)
-splitk_reduce_kernel(const float* __restrict__ partial, int32_t n_rows, int32_t M, int32_t m_pad,
-                     int32_t S, const OutTable tab) {
-  const int vec_per_row = (M + 3) >> 2;
+splitk_reduce_kernel(const float* __restrict__ partial, int32_t n_rows, int32_t M, int32_t S,
+                     const OutTable tab) {
+  const int quads = (n_rows + 3) >> 2;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)n_rows * vec_per_row) return;
-  const int row = (int)(t / vec_per_row);
-  const int m0 = (int)(t - (int64_t)row * vec_per_row) * 4;
-  const int64_t sstride = (int64_t)n_rows * m_pad;
-  const f32x4* p = reinterpret_cast<const f32x4*>(partial + (int64_t)row * m_pad + m0);
+  if (t >= (int64_t)M * quads) return;
+  const int m = (int)(t / quads);
+  const int row = 4 * (int)(t - (int64_t)m * quads);
+  const int64_t rp = tile_partial_pitch(n_rows);
+  const f32x4* p = reinterpret_cast<const f32x4*>(partial + (int64_t)m * rp + row);
+  const int64_t vstride = (int64_t)M * rp / 4;  // 16-byte vectors between slices
   // the slices in groups (8, or 16 above 8 slices): all loads of a group
   // are issued before the first add (one load latency per group, not per
   // slice), then added in slice order
-  const f32x4 sum =
-      S <= 8 ? sum_slices_ptr<8>(p, sstride / 4, S) : sum_slices_ptr<16>(p, sstride / 4, S);
-  // the row's segment: the last one whose first row is at or before it
+  const f32x4 sum = S <= 8 ? sum_slices_ptr<8>(p, vstride, S) : sum_slices_ptr<16>(p, vstride, S);
+  // the segment of the quad's first row (the last one that starts at or
+  // before it) and the next one; store_y4 searches every segment for rows
+  // past those
   int seg = 0;
   for (int i = 1; i < tab.n_seg; ++i) seg = row >= tab.begin[i] ? i : seg;
+  const int seg1 = seg + 1 < tab.n_seg ? seg + 1 : seg;
   OutMap om;
   om.y0 = tab.y[seg];
-  om.y1 = tab.y[seg];
+  om.y1 = tab.y[seg1];
   om.b0 = tab.begin[seg];
   om.b1 = tab.begin[seg + 1];
-  om.e1 = tab.begin[seg + 1];
-  om.n_seg = 0;  // the row lies in segment seg
+  om.e1 = tab.begin[seg1 + 1];
+  om.n_seg = tab.n_seg;
   om.ts0 = 1.0f;
   om.ts1 = 1.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float vj = sum[j];
-    if (m0 + j < M) store_y<true>(om, tab, row, m0 + j, vj);
-  }
+  store_y4(om, tab, row, m, sum, n_rows);
 }
 
 #endif  // FP_DEFINE_MISC_KERNELS

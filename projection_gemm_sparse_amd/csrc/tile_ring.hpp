@@ -25,7 +25,7 @@
 //
 // Compared with loading a whole slice at once, the ring lets a slice span
 // many stages, so few slices (S ~ CUs / row blocks) cover K and the fp32
-// partial sums, S x rows x BM, stay small next to the weights.
+// partial sums, S x M x rows, stay small next to the weights.
 //
 // Reduction order, fixed by (K, S): each output's k steps in order (the
 // matrix unit's order inside a step), then the S slice sums in slice order
@@ -195,21 +195,22 @@ ring_tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __res
     return;
   }
   float* partial = a.partial;
+  const uint32_t rp = (uint32_t)tile_partial_pitch(n_rows);
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(partial, (uint32_t)S * (uint32_t)M * rp * 4u);
 #pragma unroll
   for (int i = 0; i < A; ++i)
 #pragma unroll
-    for (int k = 0; k < B; ++k)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = row_w + 16 * i + v;
-        const int m = m_w + 16 * k;
-        if (row < n_rows)
-          store_partial(partial + ((int64_t)s * n_rows + row) * BM + m, acc[i][k][v]);
-      }
+    for (int k = 0; k < B; ++k) {
+      const int row = row_w + 16 * i;
+      const int m = m_w + 16 * k;
+      if (m < M && row < n_rows)
+        store_partial4(prs, ((uint32_t)s * (uint32_t)M + (uint32_t)m) * rp + (uint32_t)row,
+                       acc[i][k]);
+    }
   if (geo & kGeoSecondFinish) return;  // splitk_reduce_kernel adds the slices
   __syncthreads();  // every wave is done with the stage buffers
-  splitk_finish_vec<true>(partial, a.counters, rb, S, row_base, BR, n_rows, M, BM, 256, om,
-                          a.out, reinterpret_cast<int*>(lds_raw));
+  splitk_finish_vec(partial, a.counters, rb, S, row_base, BR, n_rows, M, 256, om, a.out,
+                    reinterpret_cast<int*>(lds_raw));
 }
 
 }  // namespace fp

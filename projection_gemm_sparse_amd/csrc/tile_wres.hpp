@@ -187,17 +187,18 @@ wres_tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __res
           }
     } else {
       float* partial = a.partial;
+      const uint32_t rp = (uint32_t)tile_partial_pitch(n_rows);
+      const __amdgpu_buffer_rsrc_t prs = make_rsrc(partial, (uint32_t)S * (uint32_t)M * rp * 4u);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int k = 0; k < B; ++k)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int row = row_w + 16 * i + v;
-            const int m = m_w + 16 * k;
-            if (row < n_rows)
-              store_partial(partial + ((int64_t)s * n_rows + row) * BM + m, acc[i][k][v]);
-          }
+        for (int k = 0; k < B; ++k) {
+          const int row = row_w + 16 * i;
+          const int m = m_w + 16 * k;
+          if (m < M && row < n_rows)
+            store_partial4(prs, ((uint32_t)s * (uint32_t)M + (uint32_t)m) * rp + (uint32_t)row,
+                           acc[i][k]);
+        }
     }
   } else {
     // ------------------------------------------------ producer waves
@@ -245,8 +246,8 @@ wres_tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __res
   // in-launch finish: every wave (producers included) takes part
   __syncthreads();
   const OutMap om = make_out_map(y0, y1, split, n_rows, a.out, row_base);
-  splitk_finish_vec<true>(a.partial, a.counters, rb, S, row_base, kWresRows, n_rows, M, BM, NT,
-                          om, a.out, reinterpret_cast<int*>(lds_raw));
+  splitk_finish_vec(a.partial, a.counters, rb, S, row_base, kWresRows, n_rows, M, NT, om, a.out,
+                    reinterpret_cast<int*>(lds_raw));
 }
 
 }  // namespace fp
