@@ -308,12 +308,7 @@ tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict
 #pragma unroll
     for (int mt = 0; mt < MT16; ++mt) {
       const int m = mt * 16 + i16;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = row_t + v;
-        const float val = acc[mt][v];
-        if (m < M && row < n_rows) store_y<true>(om, a.out, row, m, val);
-      }
+      if (m < M && row_t < n_rows) store_y4(om, a.out, row_t, m, acc[mt], n_rows);
     }
     return;
   }

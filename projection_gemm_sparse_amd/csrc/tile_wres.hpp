@@ -178,13 +178,11 @@ wres_tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __res
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int k = 0; k < B; ++k)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int row = row_w + 16 * i + v;
-            const int m = m_w + 16 * k;
-            if (m < M && row < n_rows) store_y<true>(om, a.out, row, m, acc[i][k][v]);
-          }
+        for (int k = 0; k < B; ++k) {
+          const int row = row_w + 16 * i;
+          const int m = m_w + 16 * k;
+          if (m < M && row < n_rows) store_y4(om, a.out, row, m, acc[i][k], n_rows);
+        }
     } else {
       float* partial = a.partial;
       const uint32_t rp = (uint32_t)tile_partial_pitch(n_rows);
