@@ -321,7 +321,26 @@ bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
     // kernel at 9 slices 26.06).  The choice depends on (K, M bucket, plan
     // rows) only.
     int64_t S = std::max<int64_t>(1, kCus / blocks);
-    if (mt16 <= 4) S = std::max<int64_t>(S, std::min<int64_t>(9, 3 * kCus / blocks));
+    if (mt16 <= 4) {
+      S = std::max<int64_t>(S, std::min<int64_t>(9, 3 * kCus / blocks));
+      // Where that leaves some CUs two workgroups and others one, more
+      // slices while the busiest CU's share of a row block, ceil(blocks S /
+      // CUs) / S, does not grow, with at most two workgroups per CU (two
+      // rings of up to 64 tokens fit in LDS) and slices of at least 16 k
+      // steps.  Measured on MI355X (second-launch finish, us per call):
+      // K = 6144, 2752 rows (43 blocks): 11 slices against 9 12.9 / 13.8 at
+      // M = 17, 13.6 / 14.4 at M = 32, 15.8 / 16.0 at M = 48; 2624 rows (41
+      // blocks): 12 slices against 9 12.5 / 13.6 at M = 17, 13.4 / 14.3 at
+      // M = 32, 16.8 / 17.3 at M = 64; K = 7168, 2048 rows (32 blocks): 14
+      // slices against 9 9.8 / 14.5 at M = 9, 11.4 / 16.5 at M = 17, 15.5 /
+      // 22.2 at M = 64.  At 1792 rows (28 blocks, one per CU at 9 slices) 9
+      // stays: 14, 16 and 18 slices measured 12.2..15.4 against 11.4 at
+      // M = 48.
+      if (blocks * S > kCus) {
+        for (int64_t S2 = S + 1; blocks * S2 <= 2 * kCus && S2 * 16 <= n_steps; ++S2)
+          if (ceil_div(blocks * S2, kCus) * S <= ceil_div(blocks * S, kCus) * S2) S = S2;
+      }
+    }
     S = std::min<int64_t>(S, std::max<int64_t>(1, n_steps / 4));
     S = std::min<int64_t>(S, 0x1fff);
     t->path = FP_PATH_MFMA;

@@ -199,7 +199,8 @@ def test_default_crossover():
     # more rows than one 8-row tile per CU (the three-way fused-A shape):
     # the vector-ALU kernel through M = 4, the small-M kernel with two row
     # tiles of 6 per wave for 5..16 (one or two token halves), the ring
-    # tile kernel with 9 slices from 17 on
+    # tile kernel from 17 on, its 43 row blocks in 11 slices (473
+    # workgroups: the busiest CU's share 2/11 against 2/9 with 9 slices)
     for M in range(1, 5):
         assert P.fp_default_tiling(0, 6144, 2752, M, 2752)[1][0] == P.FP_PATH_SKINNY
     for M in range(5, 17):
@@ -207,7 +208,15 @@ def test_default_crossover():
         assert t[0] == P.FP_PATH_MFMA_SMALL and t[4] == 12 and t[5] == 1
     for M in (17, 32, 48, 64):
         st, t = P.fp_default_tiling(0, 6144, 2752, M, 2752)
-        assert t[0] == P.FP_PATH_MFMA and t[1] == 4 and t[2] == 4 and t[3] == 9
+        assert t[0] == P.FP_PATH_MFMA and t[1] == 4 and t[2] == 4 and t[3] == 11
+    # the ring's slice count from the busiest CU's share: 41 blocks take 12
+    # slices (492 workgroups), 28 blocks keep 9 (one per CU), K = 7168 at
+    # 2048 rows 14 (slices of 16 k steps)
+    for M in (17, 64):
+        assert P.fp_default_tiling(0, 6144, 2624, M, 2624)[1][3] == 12
+        assert P.fp_default_tiling(0, 7168, 2048, M, 2048)[1][3] == 14
+    for M in (48, 64):
+        assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][3] == 9
     # above 64 tokens one slice per CU's share of the 43 row blocks
     for M in (96, 128):
         st, t = P.fp_default_tiling(0, 6144, 2752, M, 2752)
