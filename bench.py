@@ -539,9 +539,10 @@ CROSSOVER_SHAPES = {
                  (1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 24, 32, 48, 64, 96, 128), (), (9,)),
     "fused_a_3way": ("three-way fused-A [2752, 6144] bf16", 6144, (2048, 576, 128),
                      tuple(range(1, 17)) + (17, 32, 48, 64, 96, 128), _SMALL_ROWS,
-                     (5, 7, 9)),
+                     (5, 7, 9, 11)),
     "glm_fused_a": ("fused-A of the pages [2624, 6144] bf16 (2048 + 512 + 64)", 6144,
-                    (2048, 512, 64), tuple(range(1, 17)), _SMALL_ROWS, (9,)),
+                    (2048, 512, 64), tuple(range(1, 17)) + (17, 32, 48, 64), _SMALL_ROWS,
+                    (9, 12)),
 }
 
 
