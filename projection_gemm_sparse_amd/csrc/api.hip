@@ -311,15 +311,15 @@ bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
     // The ring tile kernel, four stage buffers (three for 256-token blocks,
     // the most LDS holds), over the plan's 64-row blocks: one workgroup per
     // CU, and up to 64 tokens up to 9 slices while that keeps at most three
-    // per CU; at least two stages per slice.  Measured on MI355X
-    // (second-launch finish from 17 tokens): K = 5120, 1792 rows, 9 slices:
-    // 12.9 us at M = 64 and 16.8 at M = 128, against 19.7 / 22.0 for the
-    // tile kernel; K = 6144, 2752 rows: 9 slices ahead of 5, 6, 7 and 12 up
-    // to 64 tokens (M = 9: 12.28 against 13.76 .. 13.23; M = 17: 14.88
-    // against 17.51 .. 16.13; M = 64: 18.38 against 21.05 with 5), but not
-    // above (M = 96: 5 slices 25.32, 9 slices 28.62, the weight-resident
-    // kernel at 9 slices 26.06).  The choice depends on (K, M bucket, plan
-    // rows) only.
+    // per CU (then balanced below); at least two stages per slice.  Measured
+    // on MI355X (second-launch finish from 17 tokens): K = 5120, 1792 rows,
+    // 9 slices: 12.9 us at M = 64 and 16.8 at M = 128, against 19.7 / 22.0
+    // for the tile kernel; K = 6144, 2752 rows: 9 slices ahead of 5, 6 and 7
+    // up to 64 tokens (M = 17: 14.88 against 17.51 .. 16.13; M = 64: 18.38
+    // against 21.05 with 5) and of 12 (three workgroups on some CUs), but
+    // one workgroup per CU above 64 tokens (M = 96: 5 slices 25.32, 9 slices
+    // 28.62, the weight-resident kernel at 9 slices 26.06).  The choice
+    // depends on (K, M bucket, plan rows) only.
     int64_t S = std::max<int64_t>(1, kCus / blocks);
     if (mt16 <= 4) {
       S = std::max<int64_t>(S, std::min<int64_t>(9, 3 * kCus / blocks));
