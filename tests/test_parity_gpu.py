@@ -488,6 +488,34 @@ def test_weight_resident_tile_kernel_ragged_rows():
     fp.set_tiling(M, None)
 
 
+# ---- outputs that start 2 bytes past an 8-byte boundary: the tile kernels
+#      store four rows of one token as one 8-byte run only where the address
+#      allows it and fall back to one store per row elsewhere, with the same
+#      values (both finishes and the unsplit ring launch)
+@pytest.mark.parametrize("M", [17, 32, 64, 128])
+def test_tile_outputs_at_two_byte_offsets(M):
+    x, ws = si.workload_case("crossover", M, 13)
+    fp = _plan(ws, max_M=128, workspace_bytes=64 << 20)
+    xg = to_gpu(x)
+    rows = sorted({0, 1, M // 2, M - 1})
+    cases = [None, _ring(4, 1, 1), _ring(4, 9, 1), _ring(4, 9, 2), _wres(9, 1), _wres(9, 2)]
+    for t in cases:
+        if fp.set_tiling(M, t) != P.FP_OK:
+            assert t is not None and t[2] == 2, (M, t)  # weight-resident slices too long
+            continue
+        label = "outputs at +2 bytes M=%d tiling %s" % (M, t)
+        ref = fp(xg)
+        assert_matches_oracle(ref, x, ws, rows=rows, label=label)
+        bufs = [torch.full((M * n + 1,), float("nan"), dtype=torch.bfloat16, device=xg.device)
+                for n in fp.N]
+        out = [b[1:].view(M, n) for b, n in zip(bufs, fp.N)]
+        assert all(o.data_ptr() % 8 == 2 for o in out)
+        fp.forward(xg, out=out)
+        assert_bitwise_equal(out, ref, label)
+        assert all(torch.isnan(b[0]) for b in bufs), label + ": wrote before the output"
+    fp.set_tiling(M, None)
+
+
 # ---- the pages' own fused-A shapes at hidden 6144 (pinned as concatenation
 #      shapes in tests/golden/page_shapes.txt): 2624 rows = 2048 + 512 + 64,
 #      and 2784 rows with the 160 indexer rows appended as a fourth
