@@ -38,6 +38,14 @@ constexpr int kSkinnyMaxM = 8;      // largest M the skinny kernel serves
 // Largest M the small-M matrix-core kernel serves: three token halves for
 // bf16, two for block-scaled weights.
 constexpr int kSmallMfmaMaxM = 24;
+// Two row tiles per wave only for workgroups of at least this many K parts
+// (K >= 1536 in bf16): with fewer waves per workgroup the two-tile form
+// leaves a CU too few waves (measured on MI355X at 4096 and 6144 rows, M = 8
+// / 16, us per call: K = 512 4.44 / 7.03 against 3.87 / 5.95 for one 8-row
+// tile, K = 768 4.03 / 5.84 against 3.56 / 5.28, K = 1024 3.98 / 5.71
+// against 3.91 / 5.02 at 4096 rows; at 6144 rows K = 768 5.53 / 7.90
+// against 4.55 / 6.57 for three groups of one 8-row tile).
+constexpr int kSmfmaTwoTileMinParts = 6;
 constexpr int kSmallMfmaMaxMMx = 16;
 // Crossover to the tile kernels (smallest M on the MFMA tile path),
 // measured on MI355X at K = 5120, 1792 rows: the small-M matrix-core
@@ -476,13 +484,29 @@ int smfma_cu_waves(int kt, int mh, int tt) {
 // that each reload the activations, M = 8: K = 512, 1792 rows 3.27 vs 7.03
 // (seven groups of one row); K = 1024, 2048 rows 3.00 vs 5.01; K = 2048
 // 3.86 vs 4.69.
+bool resolve_smfma_rows_pass(int64_t n_rows, Tiling* t, bool pairs, bool bf16, bool few_parts_tt2);
+
 bool resolve_smfma_rows(int64_t n_rows, Tiling* t, bool pairs, bool bf16) {
   if (t->rows > 0 && t->groups > 0) return true;
+  // two tiles per wave for workgroups of few K parts only where no one-round
+  // layout exists without them (then the largest rows win: 65536 rows, K =
+  // 1024, M = 5: two tiles of 8 rows 24.5 us against one tile 27.2)
+  Tiling one = *t;
+  if (resolve_smfma_rows_pass(n_rows, &one, pairs, bf16, false)) {
+    *t = one;
+    return true;
+  }
+  return resolve_smfma_rows_pass(n_rows, t, pairs, bf16, true);
+}
+
+bool resolve_smfma_rows_pass(int64_t n_rows, Tiling* t, bool pairs, bool bf16,
+                             bool few_parts_tt2) {
   int best_rows = pairs ? 2 : 1, best_g = 1;
   int64_t best_cost = INT64_MAX;
   const int mh = t->mt / 8;
   for (int tt = 1; tt <= 2; ++tt) {
     if (tt == 2 && (!bf16 || pairs || mh > 2)) continue;
+    if (tt == 2 && !few_parts_tt2 && t->kparts < kSmfmaTwoTileMinParts) continue;
     for (int rt = pairs ? 2 : 1; rt <= 8; rt += pairs ? 2 : 1) {
       if (tt == 2 && rt < 5) continue;  // rows <= 8 denote one tile
       const int rows = tt * rt;
