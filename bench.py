@@ -30,7 +30,8 @@ copy.
 Table modes (each writes PREFIX.json and PREFIX.md and exits):
 ``--crossover`` times every kernel path that serves each M on a rotated
 pool (``--crossover-workload``: the headline weights, the three-way fused-A
-shape or the pages' 2624-row fused-A shape); ``--ceiling`` the streaming
+shape, the pages' 2624-row fused-A shape or the dense-MLP down projection
+[6144, 768]); ``--ceiling`` the streaming
 ceiling against the launch shape and the per-launch floor;
 ``--indexer-splits`` the fp32 indexer fusion with its K split across
 workgroups; ``--pool-sweep`` the per-call time against the pool size.
@@ -543,6 +544,12 @@ CROSSOVER_SHAPES = {
     "glm_fused_a": ("fused-A of the pages [2624, 6144] bf16 (2048 + 512 + 64)", 6144,
                     (2048, 512, 64), tuple(range(1, 17)) + (17, 32, 48, 64), _SMALL_ROWS,
                     (9, 12)),
+    # the dense-MLP down projection of the pages' small-M MLP (one projection,
+    # K = 768): row layouts of three K parts
+    "mlp_down": ("dense-MLP down projection [6144, 768] bf16", 768, (6144,),
+                 (1, 2, 3, 4, 5, 8, 9, 12, 16), _SMALL_ROWS + (
+                     ("three groups of one 8-row tile", 8, 3),
+                     ("two groups of two tiles of 6 rows", 12, 2)), (9,)),
 }
 
 

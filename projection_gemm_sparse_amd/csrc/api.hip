@@ -39,13 +39,17 @@ constexpr int kSkinnyMaxM = 8;      // largest M the skinny kernel serves
 // bf16, two for block-scaled weights.
 constexpr int kSmallMfmaMaxM = 24;
 // Two row tiles per wave only for workgroups of at least this many K parts
-// (K >= 1536 in bf16): with fewer waves per workgroup the two-tile form
-// leaves a CU too few waves (measured on MI355X at 4096 and 6144 rows, M = 8
-// / 16, us per call: K = 512 4.44 / 7.03 against 3.87 / 5.95 for one 8-row
-// tile, K = 768 4.03 / 5.84 against 3.56 / 5.28, K = 1024 3.98 / 5.71
-// against 3.91 / 5.02 at 4096 rows; at 6144 rows K = 768 5.53 / 7.90
-// against 4.55 / 6.57 for three groups of one 8-row tile).
-constexpr int kSmfmaTwoTileMinParts = 6;
+// (K >= 2048 in bf16): with fewer waves per workgroup the two-tile form
+// leaves a CU too few waves.  Small-M workgroups are counted resident up to
+// kSmfmaMaxResident per CU (fewer where the CU's waves do not allow them).
+// Measured on MI355X against the former limits (two tiles from any K, two
+// workgroups per CU, ties to more rows), us per call: K = 768, 6144 rows
+// M = 8 5.47 -> 4.24, M = 16 7.88 -> 6.48; K = 512, 6144 rows M = 12 10.53
+// -> 6.27; K = 1024, 4096 rows M = 12 6.58 -> 4.88; K = 1536, 6144 rows
+// M = 24 14.00 -> 9.26; K = 2048, 6144 rows M = 8 6.92 -> 6.57; the
+// largest loss K = 512, 4096 rows M = 24 7.24 -> 7.74.
+constexpr int kSmfmaTwoTileMinParts = 8;
+constexpr int kSmfmaMaxResident = 4;
 constexpr int kSmallMfmaMaxMMx = 16;
 // Crossover to the tile kernels (smallest M on the MFMA tile path),
 // measured on MI355X at K = 5120, 1792 rows: the small-M matrix-core
@@ -470,12 +474,15 @@ int smfma_cu_waves(int kt, int mh, int tt) {
 // activation block once per row group, so the bytes a CU takes in are
 // (workgroups on the CU) x (R weight rows + G x mt activation rows); the
 // choice keeps every workgroup resident at once (one round) and, among
-// those, minimises that figure for the busiest CU (ties: the larger R,
-// fewer workgroups), with at most two workgroups per CU counted resident
+// those, minimises that figure for the busiest CU (ties: fewer row groups,
+// then the larger R; block-scaled kernels: the larger R), with at most
+// kSmfmaMaxResident workgroups per CU counted resident (block-scaled: two)
 // and the waves a CU holds taken from the kernel's register estimate
-// (bf16; block-scaled kernels: 32).  Two tiles per wave are offered to
-// bf16 plans (not gate/up).  Without a one-round choice the largest R is
-// taken; the result says whether a one-round layout exists.
+// (bf16; block-scaled kernels: 32).  Two tiles per wave
+// are offered to bf16 plans (not gate/up) of kSmfmaTwoTileMinParts K parts
+// or more, or of any K where no one-round layout exists without them.
+// Without a one-round choice the largest R is taken; the result says
+// whether a one-round layout exists.
 //
 // Measured on MI355X (weights rotated past the MALL, us per call): K =
 // 6144, 2752 rows, M = 8: two tiles of 6 rows per wave (230 workgroups)
@@ -524,11 +531,17 @@ bool resolve_smfma_rows_pass(int64_t n_rows, Tiling* t, bool pairs, bool bf16,
         // block-scaled kernels: 32 waves per CU assumed, as measured for
         // their rows choice
         const int cu_waves = bf16 ? smfma_cu_waves(t->chunks, mh, tt) : 32;
-        const int64_t resident = std::max(1, std::min(2, cu_waves / waves));
+        // block-scaled kernels: two per CU and ties to more rows, as
+        // measured for their rows choice
+        const int64_t resident =
+            std::max(1, std::min(bf16 ? kSmfmaMaxResident : 2, cu_waves / waves));
         const bool one_round = nb <= resident * kCus;
         const int64_t cost =
             one_round ? ceil_div(nb, kCus) * (R + (int64_t)g * t->mt) : INT64_MAX / 2 - R;
-        if (cost < best_cost || (cost == best_cost && R > (int64_t)best_rows * best_g)) {
+        const bool fewer_groups = bf16 && g < best_g;
+        const bool same_groups = !bf16 || g == best_g;
+        if (cost < best_cost || (cost == best_cost && (fewer_groups ||
+                                                     (same_groups && R > (int64_t)best_rows * best_g)))) {
           best_cost = cost;
           best_rows = rows;
           best_g = g;

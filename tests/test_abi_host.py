@@ -226,14 +226,15 @@ def test_default_crossover():
     for M in (9, 16):
         assert P.fp_default_tiling(0, 7168, 1536, M, 1536)[1][0] == P.FP_PATH_MFMA
         assert P.fp_default_tiling(0, 7168, 2112, M, 2112)[1][0] == P.FP_PATH_MFMA
-    # two row tiles per wave only for workgroups of six K parts or more
-    # (K >= 1536) while a one-round layout exists: the dense-MLP down
-    # projection [6144, 768] takes three groups of one 8-row tile, the
-    # three-way fused-A shape (12 K parts) keeps two tiles of 6, and a
-    # 65536-row plan (no one-round layout) keeps the largest rows
+    # two row tiles per wave only for workgroups of eight K parts or more
+    # (K >= 2048) while a one-round layout exists, up to four small
+    # workgroups per CU, ties to fewer row groups: the dense-MLP down
+    # projection [6144, 768] takes workgroups of one 8-row tile (three per
+    # CU), the three-way fused-A shape (12 K parts) keeps two tiles of 6,
+    # and a 65536-row plan (no one-round layout) keeps the largest rows
     for M in (5, 8, 16):
         t = P.fp_default_tiling(0, 768, 6144, M, 6144)[1]
-        assert t[0] == P.FP_PATH_MFMA_SMALL and (t[4], t[5]) == (8, 3)
+        assert t[0] == P.FP_PATH_MFMA_SMALL and (t[4], t[5]) == (8, 1)
         assert P.fp_default_tiling(0, 6144, 2752, M, 2752)[1][4:6] == (12, 1)
     assert P.fp_default_tiling(0, 1024, 65536, 8, 65536)[1][4:6] == (16, 4)
     assert P.fp_default_tiling(0, 5120, 2048, 3, 2048)[1][0] == P.FP_PATH_MFMA_SMALL
