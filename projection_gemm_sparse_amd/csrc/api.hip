@@ -50,6 +50,9 @@ constexpr int kSmallMfmaMaxM = 24;
 // largest loss K = 512, 4096 rows M = 24 7.24 -> 7.74.
 constexpr int kSmfmaTwoTileMinParts = 8;
 constexpr int kSmfmaMaxResident = 4;
+// Most slices the ring tile kernel's default takes where a CU gets two
+// workgroups (the measured range).
+constexpr int64_t kRingMaxSlices = 16;
 constexpr int kSmallMfmaMaxMMx = 16;
 // Crossover to the tile kernels (smallest M on the MFMA tile path),
 // measured on MI355X at K = 5120, 1792 rows: the small-M matrix-core
@@ -334,24 +337,31 @@ bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
     // depends on (K, M bucket, plan rows) only.
     int64_t S = std::max<int64_t>(1, kCus / blocks);
     if (mt16 <= 4) {
-      S = std::max<int64_t>(S, std::min<int64_t>(9, 3 * kCus / blocks));
-      // Where that leaves some CUs two workgroups and others one, more
-      // slices while the busiest CU's share of a row block, ceil(blocks S /
-      // CUs) / S, does not grow, with at most two workgroups per CU (two
-      // rings of up to 64 tokens fit in LDS) and slices of at least 16 k
-      // steps.  Measured on MI355X (second-launch finish, us per call):
-      // K = 6144, 2752 rows (43 blocks): 11 slices against 9 12.9 / 13.8 at
-      // M = 17, 13.6 / 14.4 at M = 32, 15.8 / 16.0 at M = 48; 2624 rows (41
-      // blocks): 12 slices against 9 12.5 / 13.6 at M = 17, 13.4 / 14.3 at
-      // M = 32, 16.8 / 17.3 at M = 64; K = 7168, 2048 rows (32 blocks): 14
-      // slices against 9 9.8 / 14.5 at M = 9, 11.4 / 16.5 at M = 17, 15.5 /
-      // 22.2 at M = 64.  At 1792 rows (28 blocks, one per CU at 9 slices) 9
-      // stays: 14, 16 and 18 slices measured 12.2..15.4 against 11.4 at
-      // M = 48.
-      if (blocks * S > kCus) {
-        for (int64_t S2 = S + 1; blocks * S2 <= 2 * kCus && S2 * 16 <= n_steps; ++S2)
-          if (ceil_div(blocks * S2, kCus) * S <= ceil_div(blocks * S, kCus) * S2) S = S2;
+      // Up to 64 tokens (two rings fit in a CU's LDS): the slice count that
+      // minimises the busiest CU's share of a row block, ceil(blocks S /
+      // CUs) / S, among slices of an even number of k steps (128-byte
+      // aligned: a slice that starts mid-line costs 30-40 %) and at least 4,
+      // at most two workgroups per CU, and beyond kRingMaxSlices slices only
+      // one workgroup per CU (small plans); ties to more slices.  Fitted to a sweep of S = 4..16 on MI355X (K =
+      // 2048..7168, 1024..4096 rows, M = 16 / 32 / 64): within 0.6 % of the
+      // best slice count on average, 7 % at worst, where the former rule
+      // (toward 9, at most three per CU) lost up to 30 %.  Examples (us per
+      // call): K = 7168, 4096 rows M = 32 8 slices 17.9 against 25.3 with 9;
+      // K = 4096, 2048 rows M = 64 16 slices 10.7 against 16.1 with 9; 1792
+      // rows at K = 5120 keep 9 (one per CU), 2752 rows at K = 6144 keep 11.
+      int64_t best = 0, best_w = 1;
+      for (int64_t S2 = 1; blocks * S2 <= 2 * kCus && S2 <= 0x1fff; ++S2) {
+        const int64_t per = ceil_div(n_steps, S2);
+        if (per < 4 || per % 2 != 0) continue;
+        if (S2 > kRingMaxSlices && blocks * S2 > kCus) continue;
+        const int64_t w = ceil_div(blocks * S2, kCus);
+        if (best == 0 || w * best <= best_w * S2) {
+          best = S2;
+          best_w = w;
+        }
       }
+      if (best > 0) S = best;
+      else S = std::max<int64_t>(S, std::min<int64_t>(9, 3 * kCus / blocks));
     }
     S = std::min<int64_t>(S, std::max<int64_t>(1, n_steps / 4));
     S = std::min<int64_t>(S, 0x1fff);

@@ -209,14 +209,26 @@ def test_default_crossover():
     for M in (17, 32, 48, 64):
         st, t = P.fp_default_tiling(0, 6144, 2752, M, 2752)
         assert t[0] == P.FP_PATH_MFMA and t[1] == 4 and t[2] == 4 and t[3] == 11
-    # the ring's slice count from the busiest CU's share: 41 blocks take 12
-    # slices (492 workgroups), 28 blocks keep 9 (one per CU), K = 7168 at
-    # 2048 rows 14 (slices of 16 k steps)
+    # the ring's slice count from the busiest CU's share among slices of an
+    # even number of k steps, at most two workgroups per CU: 41 blocks take
+    # 12 slices (492 workgroups), 28 blocks keep 9 (one per CU), K = 7168
+    # at 2048 rows 16 (14 steps each), at 4096 rows 8 (not 9: 25 steps,
+    # three workgroups on some CUs), K = 4096 at 8192 rows 4; a 192-row
+    # plan, one workgroup per CU, is not held to the 16-slice bound
     for M in (17, 64):
         assert P.fp_default_tiling(0, 6144, 2624, M, 2624)[1][3] == 12
-        assert P.fp_default_tiling(0, 7168, 2048, M, 2048)[1][3] == 14
+        assert P.fp_default_tiling(0, 7168, 2048, M, 2048)[1][3] == 16
+        assert P.fp_default_tiling(0, 7168, 4096, M, 4096)[1][3] == 8
+        assert P.fp_default_tiling(0, 4096, 8192, M, 8192)[1][3] == 4
     for M in (48, 64):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][3] == 9
+        assert P.fp_default_tiling(0, 7168, 192, M, 192)[1][3] == 56
+    for n_rows, K in ((1792, 5120), (2624, 6144), (2752, 6144), (2048, 7168), (4096, 4096)):
+        for M in (17, 32, 64):
+            t = P.fp_default_tiling(0, K, n_rows, M, n_rows)[1]
+            if t[0] == P.FP_PATH_MFMA and t[2] == 4:
+                steps = -(-K * 2 // 16 // 4)
+                assert (-(-steps // t[3])) % 2 == 0, (n_rows, K, M, t)
     # above 64 tokens one slice per CU's share of the 43 row blocks
     for M in (96, 128):
         st, t = P.fp_default_tiling(0, 6144, 2752, M, 2752)
