@@ -310,6 +310,35 @@ int64_t tile_pick_slices(int64_t n_steps, int mt16, int nw) {
   return 0;
 }
 
+// Slice count of a split tile launch over `blocks` 64-row blocks that
+// minimises the busiest CU's share of a row block, ceil(blocks S / CUs) /
+// S, among slices of an even number of k steps (128-byte aligned: a slice
+// that starts mid-line costs 30-40 %) and at least 4, with at most
+// `per_cu` workgroups per CU and beyond kRingMaxSlices only one (small
+// plans; `capped`: never); for the weight-resident kernel (`wres`, mt16
+// token tiles) only slices that fit its LDS.  Ties go to more slices.
+// S = 0: none.
+struct Slices {
+  int64_t S = 0;
+  int64_t w = 1;  // workgroups on the busiest CU
+};
+Slices balanced_slices(int64_t n_steps, int64_t blocks, int64_t per_cu, int64_t kc, bool wres,
+                       int mt16, bool capped = false) {
+  Slices best;
+  for (int64_t S = 1; blocks * S <= per_cu * kCus && S <= 0x1fff; ++S) {
+    const int64_t per = ceil_div(n_steps, S);
+    if (per < 4 || per % 2 != 0) continue;
+    if (S > kRingMaxSlices && (capped || blocks * S > kCus)) continue;
+    if (wres && !wres_fits(kc, mt16, S)) continue;
+    const int64_t w = ceil_div(blocks * S, kCus);
+    if (best.S == 0 || w * best.S <= best.w * S) {
+      best.S = S;
+      best.w = w;
+    }
+  }
+  return best;
+}
+
 bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
   const int mt16 = mfma_mt16(M);
   const int64_t n_steps = ceil_div(kc, 4);
@@ -319,6 +348,41 @@ bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
   // with more blocks than that allows takes the ring tile kernel (measured
   // on MI355X at K = 6144, 2752 rows, 9 slices: 14.88 / 15.19 us at M = 17 /
   // 32 against 19.18 / 19.17 for the tile kernel).
+  // 17..32 tokens (where the small-M kernel does not serve): the
+  // weight-resident kernel with balanced slices of one workgroup per CU
+  // (its LDS holds one), or the ring kernel with balanced slices of up to
+  // two per CU where that gives the busiest CU a smaller share.  Measured
+  // on MI355X at M = 32 (us per call) against the former choice (the tile
+  // kernel's fewest slices, weight-resident where one round): K = 5120,
+  // 1024 rows weight-resident 16 slices 8.2 against 8 slices 9.5; K =
+  // 7168, 1024 rows 16 slices 9.2 against 12 (19 steps) 10.9; K = 4096,
+  // 1024 rows 7.8 against 7 slices 10.1; K = 2048, 1024 rows 6.7 against 4
+  // slices 8.2; at most 8 % above the best slice count of either kernel
+  // (K = 2048, 2048 rows).
+  if (mt16 == 2 && ring_addressable(n_total, kc)) {
+    // at most kRingMaxSlices here (a 192-row plan at K = 7168: 12 slices
+    // 9.8 us at M = 17, 74 slices of 4 steps 10.3)
+    const Slices w = balanced_slices(n_steps, blocks, 1, kc, true, mt16, true);
+    const Slices r = balanced_slices(n_steps, blocks, 2, kc, false, mt16, true);
+    // equal shares: the weight-resident kernel where both take the same
+    // slices, the ring where it gets there with more (two per CU)
+    const bool wres_first = w.S > 0 && (r.S == 0 || w.w * r.S < r.w * w.S ||
+                                        (w.w * r.S == r.w * w.S && w.S >= r.S));
+    if (wres_first) {
+      t->path = FP_PATH_MFMA;
+      t->splits = (int)w.S;
+      t->kparts = 4;
+      t->chunks = kWresCode;
+      return true;
+    }
+    if (r.S > 0) {
+      t->path = FP_PATH_MFMA;
+      t->splits = (int)r.S;
+      t->kparts = 4;
+      t->chunks = 4;
+      return true;
+    }
+  }
   const int64_t few_pick = mt16 <= 2 ? tile_pick_slices(n_steps, mt16, 4) : 0;
   const bool ring = mt16 >= 4 || (few_pick > 0 && blocks * few_pick > kCus &&
                                   ring_addressable(n_total, kc));
@@ -349,18 +413,8 @@ bool default_mfma_order(int64_t kc, int64_t M, int64_t n_total, Tiling* t) {
       // call): K = 7168, 4096 rows M = 32 8 slices 17.9 against 25.3 with 9;
       // K = 4096, 2048 rows M = 64 16 slices 10.7 against 16.1 with 9; 1792
       // rows at K = 5120 keep 9 (one per CU), 2752 rows at K = 6144 keep 11.
-      int64_t best = 0, best_w = 1;
-      for (int64_t S2 = 1; blocks * S2 <= 2 * kCus && S2 <= 0x1fff; ++S2) {
-        const int64_t per = ceil_div(n_steps, S2);
-        if (per < 4 || per % 2 != 0) continue;
-        if (S2 > kRingMaxSlices && blocks * S2 > kCus) continue;
-        const int64_t w = ceil_div(blocks * S2, kCus);
-        if (best == 0 || w * best <= best_w * S2) {
-          best = S2;
-          best_w = w;
-        }
-      }
-      if (best > 0) S = best;
+      const Slices bs = balanced_slices(n_steps, blocks, 2, kc, false, mt16);
+      if (bs.S > 0) S = bs.S;
       else S = std::max<int64_t>(S, std::min<int64_t>(9, 3 * kCus / blocks));
     }
     S = std::min<int64_t>(S, std::max<int64_t>(1, n_steps / 4));

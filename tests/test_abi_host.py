@@ -223,6 +223,15 @@ def test_default_crossover():
     for M in (48, 64):
         assert P.fp_default_tiling(0, 5120, 1792, M, 1792)[1][3] == 9
         assert P.fp_default_tiling(0, 7168, 192, M, 192)[1][3] == 56
+    # 25..32 tokens: the weight-resident kernel with balanced slices of one
+    # workgroup per CU, or the ring where it reaches an equal or smaller
+    # share with more slices
+    t = P.fp_default_tiling(0, 5120, 1024, 32, 1024)[1]
+    assert t[0] == P.FP_PATH_MFMA and t[2] == 2 and t[3] == 16
+    t = P.fp_default_tiling(0, 7168, 2048, 32, 2048)[1]
+    assert t[0] == P.FP_PATH_MFMA and t[2] == 4 and t[3] == 16
+    t = P.fp_default_tiling(0, 5120, 1792, 32, 1792)[1]
+    assert t[0] == P.FP_PATH_MFMA and t[2] == 2 and t[3] == 9
     for n_rows, K in ((1792, 5120), (2624, 6144), (2752, 6144), (2048, 7168), (4096, 4096)):
         for M in (17, 32, 64):
             t = P.fp_default_tiling(0, K, n_rows, M, n_rows)[1]

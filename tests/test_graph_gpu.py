@@ -149,10 +149,12 @@ def _count_graph_nodes(fn, stream: torch.cuda.Stream) -> int:
 @pytest.mark.parametrize("name,M", [("wq_a+wkv_m1", 1), ("wq_a+wkv_m2_8", 2),
                                      ("wq_a+wkv_m2_8", 8), ("fused_a_3way", 4),
                                      ("indexer_f32", 8), ("crossover", 9),
-                                     ("crossover", 32)])
+                                     ("crossover", 32), ("crossover", 64)])
 def test_launch_count_fused_one_separate_n(name, M):
     """The pages count tinygemm2 calls per token count; here the fused call
-    is always one kernel node and the separate path one per projection."""
+    is one kernel node (two where its split-K slices are added by a second
+    launch, as its tiling says) and the separate path as many per
+    projection; the graph holds exactly what fp_plan_query reports."""
     x0, ws = si.workload_case(name, M, 0)
     fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=max(8, M))
     x = to_gpu(x0)
@@ -166,7 +168,9 @@ def test_launch_count_fused_one_separate_n(name, M):
         n_sep = _count_graph_nodes(lambda: fp.forward_separate(x, out=outs, stream=s), s)
     torch.cuda.synchronize()
     path, lf, ls = fp.query(M)
-    assert (n_fused, n_sep) == (lf, ls) == (1, len(fp.N))
+    t = fp.get_tiling(M)
+    per_call = 2 if (t[0] == P.FP_PATH_MFMA and t[3] > 1 and t[5] == 2) else 1
+    assert (n_fused, n_sep) == (lf, ls) == (per_call, per_call * len(fp.N))
 
 
 def test_replay_of_a_split_vector_alu_launch():
