@@ -71,14 +71,39 @@ constexpr int kDefaultSmallMfmaMinM = 3;
 // faster through M = 4 (MXFP8 4.95 vs 5.36 us, MXFP4 4.37 vs 4.60).
 constexpr int kDefaultSmallMfmaMinMMx = 5;
 constexpr int kCus = 256;           // MI355X compute units
-// bf16 launches of more rows than one 8-row tile per CU keep the vector-ALU
-// kernel through M = 4 as well: measured at the three-way shape (K = 6144,
-// 2752 rows), against the small-M kernel with two row tiles of 6 per wave,
-// 8.02 vs 8.27 us at M = 3 and 8.19 vs 8.30 at M = 4 (one tile of 6: 9.05,
-// 8.48).
-int default_small_mfma_min_m(int32_t dtype, int64_t n_total) {
+// Largest bf16 plan (weight bytes) of more than eight rows per CU that the
+// small-M kernel serves from M = 3 (see default_small_mfma_min_m).
+constexpr int64_t kSmallMfmaMaxBytesM3 = (int64_t)25200000;
+// bf16: where the small-M kernel starts depends on the rows a CU gets and
+// on the plan's size.  A sweep of both kernels' default layouts at M = 3..8
+// (K = 1024..7168, 256..6144 rows) on MI355X: with at most two rows per CU
+// the vector-ALU kernel is ahead at every M up to 8 (by up to 35 %: 512
+// rows, K = 7168, M = 5 / 8, and 39 % at M = 3); with three or four rows
+// per CU the small-M kernel is ahead from M = 3 at K <= 2048 (1024 rows,
+// K = 2048, M = 8: 0.77 of the vector-ALU time), the vector-ALU kernel up
+// to M = 4 at larger K (up to M = 8 with three rows per CU); with four to
+// eight rows per CU the small-M kernel from M = 3 (the headline shape);
+// above eight rows per CU the small-M kernel from M = 3 at K <= 4096 up to
+// 25.2 MB of weights (K = 2048, 6144 rows M = 3: 0.97 of the vector-ALU
+// time; K = 4096, 3072 rows: 0.94 at M = 4) and the vector-ALU kernel
+// through M = 4 otherwise (K = 5120, 2304 rows: 1.05; the three-way
+// fused-A shape, 33.8 MB: 8.02 vs 8.27 us at M = 3; K = 4096, 6144 rows:
+// 1.14).  Over the 126 measured cells at M = 3 / 4 the rule loses 1.9 us
+// in all against the best kernel (at most 7 % in one cell), where the
+// former rule (small-M from M = 3 up to eight rows per CU) lost 21.3 us
+// (39 %).
+int default_small_mfma_min_m(int32_t dtype, int64_t K, int64_t n_total) {
   if (dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4) return kDefaultSmallMfmaMinMMx;
-  return n_total > 8 * (int64_t)kCus ? kDefaultSmallMfmaMinMMx : kDefaultSmallMfmaMinM;
+  const int64_t cus = kCus;
+  if (n_total <= 2 * cus) return kSkinnyMaxM + 1;
+  if (n_total <= 4 * cus) {
+    if (K <= 2048) return kDefaultSmallMfmaMinM;
+    return n_total <= 3 * cus ? kSkinnyMaxM + 1 : kDefaultSmallMfmaMinMMx;
+  }
+  if (n_total <= 8 * cus) return kDefaultSmallMfmaMinM;
+  const int64_t w_bytes = n_total * K * 2;
+  return K <= 4096 && w_bytes <= kSmallMfmaMaxBytesM3 ? kDefaultSmallMfmaMinM
+                                                      : kDefaultSmallMfmaMinMMx;
 }
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // rows and chunks per row, 32-bit indexing
 
@@ -864,7 +889,7 @@ void standin_plan(fp_plan_s* tmp, int32_t dtype, int64_t K, int64_t n_total,
   tmp->n_total = n_total;
   tmp->max_M = max_M;
   tmp->mfma_min_m = kDefaultMfmaMinM;
-  tmp->small_mfma_min_m = default_small_mfma_min_m(dtype, n_total);
+  tmp->small_mfma_min_m = default_small_mfma_min_m(dtype, K, n_total);
   tmp->ws_bytes = SIZE_MAX;
 }
 
@@ -1131,7 +1156,7 @@ fp_status fp_plan_create(int32_t dtype, int64_t K, int32_t n_proj, const int64_t
   p->max_M = max_M;
   p->mfma_min_m = kDefaultMfmaMinM;
   for (int i = 0; i < FP_MAX_PROJ; ++i) p->tscale[i] = 1.0f;
-  p->small_mfma_min_m = default_small_mfma_min_m(dtype, n_total);
+  p->small_mfma_min_m = default_small_mfma_min_m(dtype, K, n_total);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // concatenate: W_cat[off_i + r, :] = W_i[r, :]

@@ -258,8 +258,19 @@ def test_default_crossover():
         assert t[0] == P.FP_PATH_MFMA_SMALL and (t[4], t[5]) == (8, 1)
         assert P.fp_default_tiling(0, 6144, 2752, M, 2752)[1][4:6] == (12, 1)
     assert P.fp_default_tiling(0, 1024, 65536, 8, 65536)[1][4:6] == (16, 4)
+    # where the small-M kernel starts: from M = 3 at four to eight rows per
+    # CU; above eight, from M = 3 only at K <= 4096 up to 25.2 MB of weights;
+    # at most two rows per CU never (the vector-ALU kernel through M = 8);
+    # three or four rows per CU from M = 3 at K <= 2048
     assert P.fp_default_tiling(0, 5120, 2048, 3, 2048)[1][0] == P.FP_PATH_MFMA_SMALL
     assert P.fp_default_tiling(0, 5120, 2049, 3, 2049)[1][0] == P.FP_PATH_SKINNY
+    assert P.fp_default_tiling(0, 2048, 6144, 3, 6144)[1][0] == P.FP_PATH_MFMA_SMALL
+    assert P.fp_default_tiling(0, 4096, 6144, 4, 6144)[1][0] == P.FP_PATH_SKINNY
+    for M in (1, 3, 5, 8):
+        assert P.fp_default_tiling(0, 7168, 512, M, 512)[1][0] == P.FP_PATH_SKINNY
+    assert P.fp_default_tiling(0, 2048, 1024, 3, 1024)[1][0] == P.FP_PATH_MFMA_SMALL
+    assert P.fp_default_tiling(0, 5120, 1024, 4, 1024)[1][0] == P.FP_PATH_SKINNY
+    assert P.fp_default_tiling(0, 5120, 1024, 5, 1024)[1][0] == P.FP_PATH_MFMA_SMALL
 
 
 def test_epilogue_argument_checks_before_any_hip_call():
