@@ -69,7 +69,9 @@ typedef struct fp_plan_s* fp_plan_t;
  * the served domain.  Served for 1 <= M <= 16: the vector-ALU kernel up
  * to 4 tokens, the small-M matrix-core kernel (weights decoded to bf16 in
  * the registers feeding the matrix unit; two token halves above 8) from 5
- * (by default; tilings may pick either kernel up to 8 tokens).
+ * (by default; tilings may pick either kernel up to 8 tokens).  Two token
+ * halves need K <= 8192 (one workgroup spans K); 9..16 tokens on longer
+ * rows return FP_ERR_UNSUPPORTED.
  * FP_MXFP4: the same with E2M1 elements (sign, 2 exponent bits of bias 1,
  * 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), the FP4 form of the fused
  * weight named in PR #8771; two codes per byte, element 2i in the low

@@ -516,8 +516,10 @@ void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs, int var)
   int64_t best_cost = INT64_MAX;
   for (int rw = pairs ? 2 : 1; rw <= rw_max; rw += pairs ? 2 : 1) {
     if (t->rows > 0 && rw != t->rows) continue;
-    const int g_cap =
-        std::max(1, fp::skinny_max_threads(t->mt, rw, t->chunks, var) / (64 * t->kparts));
+    // only layouts whose workgroup fits the instantiation's thread bound
+    // (long fp32 rows at 5..8 tokens: seven rows per workgroup would need
+    // more registers than ten K parts leave)
+    const int g_cap = fp::skinny_max_threads(t->mt, rw, t->chunks, var) / (64 * t->kparts);
     for (int g = 1; g <= g_cap; ++g) {
       if (t->groups > 0 && g != t->groups) continue;
       const int64_t R = (int64_t)rw * g;
@@ -822,12 +824,27 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
                  (M >= p->small_mfma_min_m || M > kSkinnyMaxM) &&
                  default_smfma_order(p->kc, t);
     if (small) {
-      Tiling probe = *t;
-      probe.mt = smfma_mt(M);
-      const bool one_round = resolve_smfma_rows(p->n_total, &probe, pairs,
-                                                p->dtype == FP_BF16);
-      const bool fits = (int64_t)probe.groups * probe.kparts * 64 <=
-                        fp::smfma_max_threads(probe.chunks, probe.mt / 8, smfma_tiles(probe));
+      bool one_round = false;
+      auto probe_fits = [&]() {
+        Tiling probe = *t;
+        probe.mt = smfma_mt(M);
+        one_round = resolve_smfma_rows(p->n_total, &probe, pairs, p->dtype == FP_BF16);
+        return (int64_t)probe.groups * probe.kparts * 64 <=
+               fp::smfma_max_threads(probe.chunks, probe.mt / 8, smfma_tiles(probe));
+      };
+      bool fits = probe_fits();
+      // Block-scaled weights have no tile kernel to fall back on: where two
+      // token halves at eight K steps per wave need more waves than the
+      // thread bound allows (K = 6656..8192: 13..16 parts against 12), the
+      // sixteen-step form (no scratch, 163..192 VGPRs) halves the waves.
+      if (!fits && is_mx(p->dtype) && t->chunks < 16) {
+        const int64_t pk16 = ceil_div(ceil_div(p->kc, 8), 16);
+        if (pk16 <= fp::kMaxWaveParts) {
+          t->chunks = 16;
+          t->kparts = (int)pk16;
+          fits = probe_fits();
+        }
+      }
       if (!fits)
         small = false;
       else if (!one_round && !pairs && p->dtype == FP_BF16 && M > 8 &&

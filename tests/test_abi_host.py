@@ -368,3 +368,47 @@ def test_outputs_beyond_32_bit_indexing_are_refused():
     n = 310 * 1000 * 1000
     assert P.fp_default_tiling(P.FP_BF16, 8, n, 8, n)[0] == P.FP_ERR_UNSUPPORTED
     assert P.fp_default_tiling(P.FP_BF16, 8, n, 6, n)[0] == P.FP_OK  # 1.86e9 < 2^31
+
+
+def _random_shapes(n, seed):
+    """Seeded (K, projection sizes) pairs: K a multiple of 8 from 8 to 16384
+    and one to four projections of 1..4096 rows, both log-uniform."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        K = 8 * int(round(np.exp(rng.uniform(0.0, np.log(2048.0)))))
+        N = tuple(int(round(np.exp(rng.uniform(0.0, np.log(4096.0)))))
+                  for _ in range(int(rng.integers(1, 5))))
+        out.append((K, N))
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_default_tiling_on_random_shapes(seed):
+    """Every M a plan may be called with gets a default tiling (bf16 up to
+    256 tokens, fp32 up to 8, block-scaled weights up to 16), and a launch
+    of one projection keeps the summation order of the fused launch, on
+    shapes no other test names.  (fp32 at 5..8 tokens with long rows was
+    refused before the row layout search kept to layouts that fit the
+    kernel's thread bound: [1792, 5120] at M = 5; block-scaled weights at
+    9..16 tokens with K = 6656..8192 were refused before two token halves
+    took sixteen K steps per wave there.)"""
+    for K, N in _random_shapes(40, 1000 + seed):
+        n_total = sum(N)
+        kmx = max(512, K // 512 * 512)  # block-scaled K: a multiple of 512
+        for dtype, maxm, k in ((0, 256, K), (1, 8, K), (P.FP_MXFP8, 16, kmx),
+                               (P.FP_MXFP4, 16, kmx), (P.FP_NVFP4, 16, kmx)):
+            for M in range(1, maxm + 1):
+                st, fused = P.fp_default_tiling(dtype, k, n_total, M, n_total)
+                if dtype >= P.FP_MXFP8 and M > 8 and k > 8192:
+                    # two token halves of block-scaled weights span K in one
+                    # workgroup: longer rows are refused at 9..16 tokens
+                    assert st == P.FP_ERR_UNSUPPORTED, (dtype, k, N, M, st)
+                    continue
+                assert st == 0, (dtype, k, N, M, st)
+                order = (lambda t: (t[0], t[3])) if fused[0] == P.FP_PATH_MFMA else (lambda t: t[:4])
+                for n in set(N):
+                    st, sep = P.fp_default_tiling(dtype, k, n_total, M, n)
+                    assert st == 0, (dtype, k, N, M, n, st)
+                    assert order(sep) == order(fused), (dtype, k, N, M, n, fused, sep)

@@ -175,3 +175,35 @@ def test_mx_small_mfma_refusals(fmt):
     assert fp.set_tiling(8, (P.FP_PATH_MFMA, 4, 4, 9, 0, 2)) == P.FP_ERR_UNSUPPORTED
     assert fp.set_tiling(8, (P.FP_PATH_MFMA, 2, 0, 8, 0, 0)) == P.FP_ERR_UNSUPPORTED
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("M", [9, 13, 16])
+def test_mx_two_token_halves_at_k7168(fmt, M):
+    # K = 7168 (the DeepSeek hidden size): two token halves at eight K steps
+    # per wave would need 14 K parts, more waves than the two-half form's
+    # thread bound; the default takes sixteen steps per wave (7 parts)
+    K = 7168
+    x, ws = CASES[fmt][0](M, 110 + M, K=K, N=(1536, 576))
+    fp = _plan(ws, fmt, max_M=16)
+    assert fp.query(M)[0] == P.FP_PATH_MFMA_SMALL
+    assert tuple(fp.get_tiling(M)[1:3]) == (7, 16)
+    xg = to_gpu(x)
+    ys = fp(xg)
+    _check(ys, x, ws, K, fmt, "%s K=7168 M=%d" % (fmt, M))
+    assert_bitwise_equal(ys, fp(xg), "repeat")
+    assert_bitwise_equal(ys, fp.forward_separate(xg), "fused vs separate")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_mx_two_token_halves_refused_past_k8192(fmt):
+    # one workgroup spans K: past 8192 two token halves do not fit, and the
+    # call is refused without a launch; 8 tokens are still served
+    K = 8704
+    x, ws = CASES[fmt][0](9, 5, K=K, N=(64, 7))
+    fp = _plan(ws, fmt, max_M=16)
+    xg = to_gpu(x)
+    assert fp.supported(xg) is False
+    assert fp.supported(xg[:8]) is True
+    ys = fp(xg[:8])
+    _check(ys, x[:8], ws, K, fmt, "%s K=8704 M=8" % fmt)

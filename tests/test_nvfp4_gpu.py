@@ -209,3 +209,18 @@ def test_nvfp4_refusals():
     # the refused calls changed nothing: results still match the scales given
     ys = fp(to_gpu(x))
     _check(ys, x, ws, gs, 5120, "after refusals")
+
+
+@pytest.mark.parametrize("M", [9, 16])
+def test_nvfp4_two_token_halves_at_k7168(M):
+    # K = 7168: two token halves take sixteen K steps per wave (7 parts), as
+    # eight steps would need more waves than their thread bound allows
+    K = 7168
+    x, ws, gs = si.nvfp4_case(M, 120 + M, K=K, N=(1536, 576))
+    fp = _plan(ws, gs, max_M=16)
+    assert fp.query(M)[0] == P.FP_PATH_MFMA_SMALL
+    assert tuple(fp.get_tiling(M)[1:3]) == (7, 16)
+    xg = to_gpu(x)
+    ys = fp(xg)
+    _check(ys, x, ws, gs, K, "nvfp4 K=7168 M=%d" % M)
+    assert_bitwise_equal(ys, fp.forward_separate(xg), "fused vs separate")

@@ -589,3 +589,44 @@ def test_long_k_two_halves_defaults(N, M):
     fp = _plan(ws, max_M=16)
     assert fp.query(M)[0] == P.FP_PATH_MFMA
     _check_case(fp, x, ws, "K=7168 %s M=%d" % (N, M))
+
+
+@pytest.mark.parametrize("K,N", [(5120, (1280, 512)), (3712, (5, 3585, 263))])
+@pytest.mark.parametrize("M", [5, 8])
+def test_fp32_long_rows_at_five_to_eight_tokens(K, N, M):
+    """fp32 with long rows at 5..8 tokens: the row layout keeps to
+    workgroups that fit the kernel's thread bound (these calls were refused
+    while a seven-row layout that does not fit won on cost)."""
+    x, ws = si.make_case(K, N, "f32", M, seed=300 + M, w_dist="normal_0.02")
+    fp = _plan(ws, max_M=8)
+    assert fp.query(M)[0] == P.FP_PATH_SKINNY
+    _check_case(fp, x, ws, "f32 K=%d %s M=%d" % (K, N, M))
+
+
+def _random_routing_cases(n, seed):
+    """Seeded bf16 shapes (K a multiple of 8 from 64 to 8192, one to three
+    projections of 4..4096 rows, at most 12M weight elements) and two token
+    counts each, drawn around the kernels' boundaries."""
+    rng = np.random.default_rng(seed)
+    ms = [1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 24, 25, 31, 32, 33, 48, 64, 65, 96, 128]
+    out = []
+    while len(out) < n:
+        K = 8 * int(round(np.exp(rng.uniform(np.log(8.0), np.log(1024.0)))))
+        N = tuple(int(round(np.exp(rng.uniform(np.log(4.0), np.log(4096.0)))))
+                  for _ in range(int(rng.integers(1, 4))))
+        if sum(N) * K > 12_000_000:
+            continue
+        for M in rng.choice(ms, size=2, replace=False):
+            out.append((K, N, int(M)))
+    return out
+
+
+@pytest.mark.parametrize("K,N,M", _random_routing_cases(40, 7) + _random_routing_cases(40, 11))
+def test_default_routing_on_random_shapes(K, N, M):
+    """Whatever kernel and layout the default routing picks for a shape no
+    other test names: oracle parity (sampled token rows above 16), repeats
+    and fused vs one launch per projection bitwise equal."""
+    x, ws = si.make_case(K, N, "bf16", M, seed=K + M)
+    fp = _plan(ws, max_M=max(8, M))
+    rows = None if M <= 16 else sorted({0, 1, M // 2, M - 1} | set(range(3, M, 17)))
+    _check_case(fp, x, ws, "K=%d N=%s M=%d %s" % (K, N, M, fp.get_tiling(M)), rows=rows)
