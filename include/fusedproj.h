@@ -328,8 +328,10 @@ fp_status fp_plan_query(fp_plan_t plan, int64_t M, int32_t* path,
  * plan may store fp32 outputs (FP_F32): the fp32 sums are stored without
  * rounding, as the router GEMV of PR #20502 (dense-MLP/router commits: bf16
  * operands, fp32 logits, checked against an FP64 reference) needs.  Such a
- * plan runs the vector-ALU kernel for 1 <= M <= 16 (M above 16 is
- * FP_ERR_UNSUPPORTED), takes fp32 output buffers in every forward call, and
+ * plan runs the vector-ALU kernel for 1 <= M <= 16 (9..16 tokens on rows
+ * of more than 8192 elements split K across workgroups, added in the same
+ * launch; M above 16 is FP_ERR_UNSUPPORTED), takes fp32 output buffers in
+ * every forward call, and
  * has no epilogue forms.  An fp32 plan accepts only FP_F32.  Host-only; call
  * it before the plan's forward calls. */
 fp_status fp_plan_set_out_dtype(fp_plan_t plan, int32_t out_dtype);

@@ -185,6 +185,17 @@ int skinny_var(const fp_plan_s* p) {
 // served up to 8 tokens by the vector-ALU and small-M matrix-core kernels.
 bool is_mx(int32_t dtype) { return dtype == FP_MXFP8 || dtype == FP_MXFP4 || dtype == FP_NVFP4; }
 
+// The vector-ALU kernel a tiling launches, nullptr where none is compiled
+// (fp32 outputs: 1, 2, 4 and, up to 8 tokens, 8 rows per wave; gate/up
+// pairs: even rows; long chunk runs: one or two rows).  The row search and
+// the validity check ask this, so neither can pick a missing kernel.
+const void* skinny_fn(const fp_plan_s* p, const Tiling& t, bool pairs) {
+  return pairs ? fpk::skinny_pairs(t.mt, t.chunks, t.rows)
+         : p->out_f32 ? fpk::skinny_f32out(t.mt, t.chunks, t.rows)
+         : is_mx(p->dtype) ? fpk::skinny_mx(skinny_var(p), t.mt, t.chunks, t.rows)
+                           : fpk::skinny(p->dtype == FP_BF16, t.mt, t.chunks, t.rows);
+}
+
 bool dtype_known(int32_t dtype) {
   return dtype == FP_BF16 || dtype == FP_F32 || dtype == FP_MXFP8 || dtype == FP_MXFP4 ||
          dtype == FP_NVFP4;
@@ -227,10 +238,12 @@ void default_skinny_order(int32_t dtype, int64_t kc, int64_t n_total, int mt,
   // One workgroup covers a whole row whenever it can (16 waves * 64 lanes *
   // 2 chunks): finishing a K split across workgroups costs three dependent
   // memory round trips, more than the idle CUs of a short launch lose.
-  const int64_t S = ceil_div(kc, 16 * 64 * 2);
+  // The 16-token bucket (fp32 router outputs) holds twice the activations
+  // per chunk: two chunks per lane keep its workgroups within the register
+  // budget, and its thread bound (512) takes at most 8 K parts, so rows of
+  // more than 1024 chunks (bf16 K > 8192) split K across workgroups.
+  const int64_t S = ceil_div(kc, (mt >= 16 ? 8 : 16) * 64 * 2);
   const int64_t per = ceil_div(kc, S);
-  // the 16-token bucket holds twice the activations per chunk: two chunks
-  // per lane keep its workgroups within the register budget
   const int64_t CJ = std::max<int64_t>(ceil_div(per, 16 * 64), mt >= 16 ? 2 : 1);
   const int64_t P = ceil_div(per, 64 * CJ);
   t->path = S > 1 ? FP_PATH_SKINNY_SPLITK : FP_PATH_SKINNY;
@@ -508,7 +521,8 @@ bool default_smfma_order(int64_t kc, Tiling* t) {
 // ceil(ceil(n_rows / R) / CUs) * R (ties: the larger R, fewer workgroups);
 // RW <= min(8, 64 / MT) and G * P waves fit one workgroup.  Without a
 // one-round choice the largest R is taken.
-void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs, int var) {
+void resolve_skinny_rows(const fp_plan_s* p, int64_t n_rows, int mt, Tiling* t, bool pairs) {
+  const int var = skinny_var(p);
   const int rw_max = std::min(8, 64 / mt);
   const int64_t rows = n_rows * t->splits;  // work units: (row, K slice)
   if (t->rows > 0 && t->groups > 0) return;
@@ -516,6 +530,9 @@ void resolve_skinny_rows(int64_t n_rows, int mt, Tiling* t, bool pairs, int var)
   int64_t best_cost = INT64_MAX;
   for (int rw = pairs ? 2 : 1; rw <= rw_max; rw += pairs ? 2 : 1) {
     if (t->rows > 0 && rw != t->rows) continue;
+    Tiling built = *t;
+    built.rows = rw;
+    if (skinny_fn(p, built, pairs) == nullptr) continue;
     // only layouts whose workgroup fits the instantiation's thread bound
     // (long fp32 rows at 5..8 tokens: seven rows per workgroup would need
     // more registers than ten K parts leave)
@@ -716,7 +733,7 @@ WsView plan_ws(const fp_plan_s* p) {
 }
 
 bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t,
-                  const WsView& ws) {
+                  const WsView& ws, bool pairs) {
   if (t.splits < 1 || t.kparts < 1 || t.chunks < 1 || t.rows < 1) return false;
   // packed into 8- and 16-bit fields of the kernels' scalar arguments
   if (t.splits > 0x1fff || t.kparts > 0xff || t.rows > 0xff || t.groups > 0xff) return false;
@@ -778,6 +795,7 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
       return false;
     if ((int64_t)t.splits * t.kparts * 64 * t.chunks < p->kc) return false;
     if (skinny_lds(t) > kMaxLds) return false;
+    if (skinny_fn(p, t, pairs) == nullptr) return false;
   } else {
     return false;
   }
@@ -877,13 +895,13 @@ bool choose_tiling(const fp_plan_s* p, int64_t M, int64_t n_rows, Tiling* t,
   } else {
     t->mt = skinny_mt(M);
     if (t->kparts < 1) return false;
-    resolve_skinny_rows(n_rows, t->mt, t, pairs, skinny_var(p));
+    resolve_skinny_rows(p, n_rows, t->mt, t, pairs);
   }
   // a gate/up launch keeps both rows of a pair in one row group (and one
   // tile per wave)
   if (pairs && (t->rows % 2 != 0 || t->splits != 1)) return false;
   if (pairs && t->path == FP_PATH_MFMA_SMALL && smfma_tiles(*t) != 1) return false;
-  return tiling_valid(p, M, n_rows, *t, ws != nullptr ? *ws : plan_ws(p));
+  return tiling_valid(p, M, n_rows, *t, ws != nullptr ? *ws : plan_ws(p), pairs);
 }
 
 // A host-only stand-in plan with default settings and unlimited workspace,
@@ -922,11 +940,19 @@ size_t workspace_need(int32_t dtype, int64_t K, int64_t n_total, int64_t max_M) 
     most = std::max(most, partial_floats(t, n_total, M));
   }
   // the MFMA path at every M (a later fp_plan_set_mfma_min_m can move the
-  // crossover down) for bf16
+  // crossover down) and the fp32-output defaults (a later
+  // fp_plan_set_out_dtype) for bf16
   if (dtype == FP_BF16) {
     for (int64_t M = 1; M <= max_M; ++M) {
       Tiling t;
       if (!default_mfma_order(tmp.kc, M, n_total, &t)) continue;
+      most = std::max(most, partial_floats(t, n_total, M));
+    }
+    tmp.out_f32 = true;
+    tmp.osize = 4;
+    for (int64_t M = 1; M <= max_M; ++M) {
+      Tiling t;
+      if (!choose_tiling(&tmp, M, n_total, &t)) continue;
       most = std::max(most, partial_floats(t, n_total, M));
     }
   }
@@ -1052,11 +1078,8 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
   geo_a = t.kparts | (t.groups << 8) | (t.splits << 16);
   const int64_t R = (int64_t)t.groups * t.rows;
   const int64_t blocks = ceil_div(lr.n_rows, R) * t.splits;
-  const void* fn = pairs ? fpk::skinny_pairs(t.mt, t.chunks, t.rows)
-                   : p->out_f32 ? fpk::skinny_f32out(t.mt, t.chunks, t.rows)
-                   : is_mx(p->dtype) ? fpk::skinny_mx(skinny_var(p), t.mt, t.chunks, t.rows)
-                                     : fpk::skinny(p->dtype == FP_BF16, t.mt, t.chunks, t.rows);
-  return launch(fn, blocks, t.groups * t.kparts * 64, skinny_lds(t), args, stream);
+  return launch(skinny_fn(p, t, pairs), blocks, t.groups * t.kparts * 64, skinny_lds(t), args,
+                stream);
 }
 
 bool aligned(const void* p, uintptr_t a) {

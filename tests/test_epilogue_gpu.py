@@ -279,3 +279,42 @@ def test_epilogue_launch_counts():
         n_swiglu = _count_graph_nodes(lambda: fs.forward_swiglu(xsg, out=h, stream=s), s)
     torch.cuda.synchronize()
     assert (n_norm, n_swiglu) == (2, 1)
+
+
+def _random_epilogue_cases(n, seed, max_m, max_n):
+    """Seeded (K, N, M): K a multiple of 8 from 64 to 8192, N a multiple of 8
+    from 8 to max_n, at most 12M weight elements per projection pair."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        K = 8 * int(round(np.exp(rng.uniform(np.log(8.0), np.log(1024.0)))))
+        N = 8 * int(round(np.exp(rng.uniform(0.0, np.log(max_n / 8.0)))))
+        if 2 * N * K > 12_000_000:
+            continue
+        out.append((K, N, int(rng.integers(1, max_m + 1))))
+    return out
+
+
+@pytest.mark.parametrize("K,N,M", _random_epilogue_cases(16, 3, 8, 4096))
+def test_swiglu_on_random_shapes(K, N, M):
+    x, ws = si.make_case(K, (N, N), "bf16", M, seed=K + N + M)
+    fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=8)
+    xg = to_gpu(x)
+    h = fp.forward_swiglu(xg)
+    _check_swiglu(h, x, ws, "gate/up K=%d N=%d M=%d" % (K, N, M))
+    assert_bitwise_equal([h], [fp.forward_swiglu_separate(xg)], "fused vs unfused chain")
+
+
+@pytest.mark.parametrize("K,N,M", _random_epilogue_cases(16, 4, 16, 2048))
+def test_rmsnorm_on_random_shapes(K, N, M):
+    # two projections, the first normalised (at most 2048 wide, the widest
+    # normalised row), the second (N + 8 rows) plain
+    x, ws = si.make_case(K, (N, N + 8), "bf16", M, seed=K + N + M)
+    g = torch.Generator().manual_seed(K + N)
+    gammas = [(1.0 + 0.1 * torch.randn(N, generator=g)).to(torch.bfloat16), None]
+    fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=16)
+    xg = to_gpu(x)
+    gg = [to_gpu(gammas[0]), None]
+    outs = fp.forward_rmsnorm(xg, gg, EPS)
+    _check_norm(outs, x, ws, gammas, "K=%d N=%d M=%d" % (K, N, M))
+    assert_bitwise_equal(outs, fp.forward_rmsnorm_separate(xg, gg, EPS), "chain")

@@ -109,3 +109,78 @@ def test_router_refusals():
     assert P.fp_plan_set_out_dtype(f32.plan, P.FP_BF16) == P.FP_ERR_UNSUPPORTED
     assert P.fp_plan_set_out_dtype(f32.plan, P.FP_F32) == P.FP_OK
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("K", [10240, 16384])
+@pytest.mark.parametrize("M", [9, 16])
+def test_router_long_rows_split_k(K, M):
+    """Past 8192 elements a row's 9..16-token workgroup would need more than
+    8 K parts (its thread bound), so K is split across workgroups and the
+    last to arrive adds the slices in slice order: every logit against the
+    oracle under the fp32 rule, repeats, fused vs separate and graph replays
+    bitwise equal."""
+    x, ws = si.make_case(K, (256, 64), "bf16", M, seed=K + M)
+    fp = _router(ws)
+    assert fp.query(M)[0] == P.FP_PATH_SKINNY_SPLITK
+    xg = to_gpu(x)
+    ys = fp(xg)
+    _check(ys, x, ws, "router K=%d M=%d" % (K, M))
+    assert_bitwise_equal(ys, fp(xg), "repeat")
+    assert_bitwise_equal(ys, fp.forward_separate(xg), "fused vs separate")
+    outs = [torch.empty(M, n, dtype=torch.float32, device="cuda") for n in fp.N]
+    fp(xg, out=outs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp(xg, out=outs)
+    torch.cuda.synchronize()
+    for seed in (1, 2):
+        xn, _ = si.make_case(K, (256, 64), "bf16", M, seed=K + M + 100 * seed)
+        xg.copy_(to_gpu(xn))
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise_equal(outs, fp(xg), "replay %d" % seed)
+        _check(outs, xn, ws, "router K=%d M=%d replay" % (K, M))
+
+
+def _random_router_cases(n, seed):
+    """Seeded router shapes: K a multiple of 8 from 64 to 16384, one or two
+    projections of 1..4096 rows (at most 16M weight elements), M 1..16."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        K = 8 * int(round(np.exp(rng.uniform(np.log(8.0), np.log(2048.0)))))
+        N = tuple(int(round(np.exp(rng.uniform(0.0, np.log(4096.0)))))
+                  for _ in range(int(rng.integers(1, 3))))
+        if sum(N) * K > 16_000_000:
+            continue
+        out.append((K, N, int(rng.integers(1, 17))))
+    return out
+
+
+@pytest.mark.parametrize("K,N,M", _random_router_cases(24, 5))
+def test_router_on_random_shapes(K, N, M):
+    """Every router shape is served (no row layout without a compiled
+    kernel, no slice past the thread bound) and matches the oracle."""
+    x, ws = si.make_case(K, N, "bf16", M, seed=K + 7 * M)
+    fp = _router(ws)
+    xg = to_gpu(x)
+    assert fp.supported(xg), (K, N, M, fp.get_tiling(M))
+    ys = fp(xg)
+    _check(ys, x, ws, "router K=%d N=%s M=%d %s" % (K, N, M, fp.get_tiling(M)))
+    assert_bitwise_equal(ys, fp.forward_separate(xg), "fused vs separate")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_router_on_the_fused_wq_a_wkv_shape(M):
+    """fp32 outputs over [1280, 512] x 5120: the cheapest row layout (7 rows
+    per workgroup up to 8 tokens) has no compiled fp32-output kernel, so the
+    search keeps to those that exist (these calls were refused before)."""
+    x, ws = si.workload_case("crossover", M, 3)
+    fp = _router(ws)
+    xg = to_gpu(x)
+    assert fp.supported(xg)
+    assert fp.get_tiling(M)[4] in (1, 2, 4, 8)
+    ys = fp(xg)
+    _check(ys, x, ws, "router wq_a+wkv M=%d" % M)
+    assert_bitwise_equal(ys, fp.forward_separate(xg), "fused vs separate")
