@@ -732,6 +732,9 @@ WsView plan_ws(const fp_plan_s* p) {
   return w;
 }
 
+const void* mfma_fn(const Tiling& t);
+const void* smfma_fn(const Tiling& t, bool pairs, int32_t dtype, int64_t M);
+
 bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t,
                   const WsView& ws, bool pairs) {
   if (t.splits < 1 || t.kparts < 1 || t.chunks < 1 || t.rows < 1) return false;
@@ -795,10 +798,14 @@ bool tiling_valid(const fp_plan_s* p, int64_t M, int64_t n_rows, const Tiling& t
       return false;
     if ((int64_t)t.splits * t.kparts * 64 * t.chunks < p->kc) return false;
     if (skinny_lds(t) > kMaxLds) return false;
-    if (skinny_fn(p, t, pairs) == nullptr) return false;
   } else {
     return false;
   }
+  // only a tiling whose kernel is compiled
+  const void* fn = t.path == FP_PATH_MFMA         ? mfma_fn(t)
+                   : t.path == FP_PATH_MFMA_SMALL ? smfma_fn(t, pairs, p->dtype, M)
+                                                  : skinny_fn(p, t, pairs);
+  if (fn == nullptr) return false;
   // the tile kernels' in-launch finish addresses the partials with 32-bit
   // byte offsets
   const int64_t pbytes = partial_floats(t, n_rows, M) * 4;
