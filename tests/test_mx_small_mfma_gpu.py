@@ -207,3 +207,30 @@ def test_mx_two_token_halves_refused_past_k8192(fmt):
     assert fp.supported(xg[:8]) is True
     ys = fp(xg[:8])
     _check(ys, x[:8], ws, K, fmt, "%s K=8704 M=8" % fmt)
+
+
+def _random_mx_cases(n, seed):
+    """Seeded block-scaled shapes: K a multiple of 512 up to 8192, one or
+    two projections of 1..3000 rows, M 1..16."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        K = 512 * int(rng.integers(1, 17))
+        N = tuple(int(round(np.exp(rng.uniform(0.0, np.log(3000.0)))))
+                  for _ in range(int(rng.integers(1, 3))))
+        if sum(N) * K > 12_000_000:
+            continue
+        out.append((K, N, int(rng.integers(1, 17))))
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("K,N,M", _random_mx_cases(10, 8))
+def test_mx_default_routing_on_random_shapes(fmt, K, N, M):
+    x, ws = CASES[fmt][0](M, K + M, K=K, N=N)
+    fp = _plan(ws, fmt, max_M=16)
+    xg = to_gpu(x)
+    assert fp.supported(xg), (fmt, K, N, M)
+    ys = fp(xg)
+    _check(ys, x, ws, K, fmt, "%s K=%d N=%s M=%d %s" % (fmt, K, N, M, fp.get_tiling(M)))
+    assert_bitwise_equal(ys, fp.forward_separate(xg), "fused vs separate")

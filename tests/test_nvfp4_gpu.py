@@ -224,3 +224,22 @@ def test_nvfp4_two_token_halves_at_k7168(M):
     ys = fp(xg)
     _check(ys, x, ws, gs, K, "nvfp4 K=7168 M=%d" % M)
     assert_bitwise_equal(ys, fp.forward_separate(xg), "fused vs separate")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_nvfp4_default_routing_on_random_shapes(seed):
+    rng = np.random.default_rng(900 + seed)
+    while True:
+        K = 512 * int(rng.integers(1, 17))
+        N = tuple(int(round(np.exp(rng.uniform(0.0, np.log(3000.0)))))
+                  for _ in range(int(rng.integers(1, 3))))
+        if sum(N) * K <= 12_000_000:
+            break
+    M = int(rng.integers(1, 17))
+    x, ws, gs = si.nvfp4_case(M, 130 + seed, K=K, N=N)
+    fp = _plan(ws, gs, max_M=16)
+    xg = to_gpu(x)
+    assert fp.supported(xg), (K, N, M)
+    ys = fp(xg)
+    _check(ys, x, ws, gs, K, "nvfp4 K=%d N=%s M=%d %s" % (K, N, M, fp.get_tiling(M)))
+    assert_bitwise_equal(ys, fp.forward_separate(xg), "fused vs separate")
