@@ -1079,8 +1079,8 @@ fp_status run(const fp_plan_s* p, const Tiling& t, const LaunchRows& lr,
     const float* part_a = tail.partial;
     int32_t s_a = t.splits;
     void* rargs[] = {&part_a, &n_rows_a, &M_a, &s_a, &tail.out};
-    return launch(fpk::splitk_reduce(),
-                  ceil_div(M * ceil_div(lr.n_rows, 4), 256), 256, 0, rargs, stream);
+    return launch(fpk::splitk_reduce(), ceil_div(M * ceil_div(lr.n_rows, 4), fp::kReduceThreads),
+                  fp::kReduceThreads, 0, rargs, stream);
   }
   geo_a = t.kparts | (t.groups << 8) | (t.splits << 16);
   const int64_t R = (int64_t)t.groups * t.rows;

@@ -196,6 +196,8 @@ __device__ __forceinline__ void splitk_finish_vec(const float* partial, uint32_t
 // plus kGeoSecondFinish: the slices are added by splitk_reduce_kernel in a
 // second launch instead of by the last workgroup of each row block.
 constexpr int kGeoSecondFinish = 1 << 30;
+// Threads per workgroup of the second-launch finish.
+constexpr int kReduceThreads = 64;
 
 template <int MT16, int NW, int CS, int C>
 __global__ void __launch_bounds__(NW * 64)
@@ -339,11 +341,11 @@ tile_kernel(const unsigned char* __restrict__ w, const unsigned char* __restrict
 // * 16 * MT16 tokens); one workgroup per row block re-reading them (the
 // in-launch finish) is then slower than spreading the sum over the whole
 // GPU after a kernel boundary.
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kReduceThreads)
 splitk_reduce_kernel(const float* __restrict__ partial, int32_t n_rows, int32_t M, int32_t S,
                      const OutTable tab) {
   const int quads = (n_rows + 3) >> 2;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x;
   if (t >= (int64_t)M * quads) return;
   const int m = (int)(t / quads);
   const int row = 4 * (int)(t - (int64_t)m * quads);
