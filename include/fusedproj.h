@@ -169,7 +169,10 @@ fp_status fp_plan_destroy(fp_plan_t plan);
 /* Host-only predicate (no HIP call): FP_OK if fp_forward serves token count
  * M with x (device pointer, row stride ldx elements), FP_ERR_UNSUPPORTED if
  * the kernels do not (M > max_M, x or its row stride not 16-byte aligned,
- * fp32 with M > 8), FP_ERR_INVALID_ARG for invalid arguments (ldx < K,
+ * fp32 with M > 8, launches past 32-bit indexing: M * N_i outputs of one
+ * projection at or above 2^31, or on the matrix-core tile path more than
+ * 2^31 bytes of weights, activations or split-K partials per launch),
+ * FP_ERR_INVALID_ARG for invalid arguments (ldx < K,
  * M < 0, NULL x with M > 0, stale plan).  The pattern of the dense-MLP
  * commit of PR #20502: a host query, refusal otherwise. */
 fp_status fp_supported(fp_plan_t plan, int64_t M, const void* x, int64_t ldx);
