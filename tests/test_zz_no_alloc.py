@@ -101,3 +101,49 @@ def test_partials_beyond_the_scratch_are_refused_without_launch():
     for y in sentinel:
         assert bool((y == 3.0).all()), "a refused call wrote its outputs"
     fp.close()
+
+
+def _random_cases(n, seed):
+    """Seeded bf16 shapes (K a multiple of 8 from 64 to 8192, one to three
+    projections of 4..4096 rows, at most 12M weight elements) with a token
+    count around the kernels' boundaries."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        K = 8 * int(round(np.exp(rng.uniform(np.log(8.0), np.log(1024.0)))))
+        N = tuple(int(round(np.exp(rng.uniform(np.log(4.0), np.log(4096.0)))))
+                  for _ in range(int(rng.integers(1, 4))))
+        if sum(N) * K > 12_000_000:
+            continue
+        out.append((K, N, int(rng.choice([5, 9, 17, 25, 32, 48, 64, 100, 128]))))
+    return out
+
+
+@pytest.mark.parametrize("K,N,M", _random_cases(12, 17))
+def test_noalloc_on_random_shapes(K, N, M):
+    """The default tiling of shapes no other test names: fp_forward's bits,
+    or FP_ERR_WORKSPACE with the outputs untouched where the split-K
+    partials exceed the scratch."""
+    xc, ws = si.make_case(K, N, "bf16", M, seed=K + M)
+    fp = P.FusedProjection([to_gpu(w) for w in ws], max_M=max(8, M))
+    x = to_gpu(xc)
+    L = P._lib
+    ya = [torch.full((M, n), 7.0, dtype=torch.bfloat16, device="cuda") for n in fp.N]
+    yb = [torch.full((M, n), -7.0, dtype=torch.bfloat16, device="cuda") for n in fp.N]
+    h = torch.cuda.current_stream().cuda_stream
+    L.check(L.fp_forward(x.data_ptr(), M, x.stride(0), fp.plan, h, [y.data_ptr() for y in ya]),
+            "fp_forward")
+    st = L.fp_forward_noalloc(x.data_ptr(), M, x.stride(0), fp.plan, h,
+                              [y.data_ptr() for y in yb])
+    torch.cuda.synchronize()
+    label = "K=%d N=%s M=%d %s" % (K, N, M, fp.get_tiling(M))
+    if st == P.FP_ERR_WORKSPACE:
+        assert fp.get_tiling(M)[3] > 1, label
+        for y in yb:
+            assert bool((y == -7.0).all()), "a refused call wrote its outputs: " + label
+    else:
+        assert st == P.FP_OK, label
+        assert_bitwise_equal(ya, yb, label + " noalloc vs fp_forward")
+        assert_matches_oracle(yb, xc, ws, rows=_rows(M), label=label + " noalloc")
+    fp.close()
