@@ -625,8 +625,13 @@ def _random_routing_cases(n, seed):
 def test_default_routing_on_random_shapes(K, N, M):
     """Whatever kernel and layout the default routing picks for a shape no
     other test names: oracle parity (sampled token rows above 16), repeats
-    and fused vs one launch per projection bitwise equal."""
-    x, ws = si.make_case(K, N, "bf16", M, seed=K + M)
+    and fused vs one launch per projection bitwise equal, with contiguous
+    and strided activations."""
+    # two in three cases read x through a padded row stride (ldx = K + 8 or
+    # K + 16 elements, the pad filled with a sentinel)
+    ldx = K + 8 * ((K + M) % 3)
+    x, ws = si.make_case(K, N, "bf16", M, seed=K + M, ldx=ldx)
     fp = _plan(ws, max_M=max(8, M))
     rows = None if M <= 16 else sorted({0, 1, M // 2, M - 1} | set(range(3, M, 17)))
-    _check_case(fp, x, ws, "K=%d N=%s M=%d %s" % (K, N, M, fp.get_tiling(M)), rows=rows)
+    _check_case(fp, x, ws, "K=%d ldx=%d N=%s M=%d %s" % (K, ldx, N, M, fp.get_tiling(M)),
+                rows=rows)
