@@ -101,7 +101,8 @@ constexpr int kTileCounterStride = 32;
 // slice and slot).  Loads are issued in groups of GRP before the adds of
 // the group: one memory latency per group.  From a buffer resource (byte
 // offset `off` of slice 0, `sstride` bytes between slices; agent-coherent
-// loads) or from a plain pointer (slice stride `vstride` 16-byte vectors).
+// non-temporal loads: each partial is read once) or from a plain pointer
+// (slice stride `vstride` 16-byte vectors).
 template <int GRP>
 __device__ __forceinline__ f32x4 sum_slices_rsrc(__amdgpu_buffer_rsrc_t pr, uint32_t off,
                                                  uint32_t sstride, int S) {
@@ -111,7 +112,8 @@ __device__ __forceinline__ f32x4 sum_slices_rsrc(__amdgpu_buffer_rsrc_t pr, uint
 #pragma unroll
     for (int j = 0; j < GRP; ++j) {
       const uint32_t o = s0 + j < S ? off + (uint32_t)(s0 + j) * sstride : kOob;
-      v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, kAuxSc1));
+      v[j] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, kAuxSc1 | kAuxNt));
     }
 #pragma unroll
     for (int j = 0; j < GRP; ++j) {
